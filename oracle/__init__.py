@@ -1,0 +1,9 @@
+"""CPU oracle of the FSDP2 per-rank sharded step (test infrastructure only).
+
+Only tests/, the smoke check and the bench's CPU-baseline leg use this package.
+The product library never imports, links or runs it.
+"""
+from .fsdp import (  # noqa: F401
+    AdamWScalars, Entry, Plan, adamw, adamw_scalars, bf16_rne, bf16_to_f32,
+    chunk_rows, pack, plan, reduce, rows_of_rank, state_bytes, unpack,
+)

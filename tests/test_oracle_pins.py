@@ -1,0 +1,553 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each pin is independent of the oracle's own code: printed values from the
+pages (golden fixtures), library routines that define the same thing
+(torch.chunk, torch's bf16 cast, torch.optim.AdamW), closed forms, exact
+rounding by brute force, and invariants.  They are chosen so that a dropped
+term, a wrong index, sign or operand order in the oracle fails at least one.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import golden_kv, parse_shape, read_golden
+import oracle
+from oracle import fsdp as O
+from workloads import configs, synth
+
+F32 = np.float32
+
+
+# ---------------------------------------------------------------------------
+# Layout
+# ---------------------------------------------------------------------------
+
+def test_chunk_rows_match_torch_chunk_brute_force():
+    for rows in range(0, 65):
+        t = torch.empty(rows, 3)
+        for n in range(1, 17):
+            chunks = torch.chunk(t, n, 0)
+            begin = 0
+            for j in range(n):
+                b, lr = O.rows_of_rank(rows, n, j)
+                want = chunks[j].shape[0] if j < len(chunks) else 0
+                assert lr == want, (rows, n, j)
+                if want:
+                    assert b == begin
+                begin += want
+            assert sum(O.rows_of_rank(rows, n, j)[1] for j in range(n)) == rows
+            # every rank's piece is padded to chunk 0's rows
+            c0 = chunks[0].shape[0] if len(chunks) else 0
+            assert O.chunk_rows(rows, n) == c0
+
+
+def test_dtensor_local_view_4096():
+    world, rows, cols, lrows, lcols = map(int, read_golden("dtensor_local_view.txt")[0].split())
+    for r in range(world):
+        p = O.plan([(rows, cols)], world, r)
+        e = p.entries[0]
+        assert (e.local_rows, e.cols) == (lrows, lcols)
+        assert e.pad_numel == 0 and p.S == lrows * lcols
+
+
+def test_linear_probe_fsdp2_balanced_and_zero1_contrast():
+    g = golden_kv("zero1_probe.txt")
+    shapes = [parse_shape(t) for t in g["shapes"]]
+    world = int(g["world"][0])
+    want_zero1 = [int(x) for x in g["zero1_adam_state_elems"]]
+    numels = [int(np.prod(s)) for s in shapes]
+    assert shapes == [p.shape for p in configs.get(0).params]
+    # ZeroRedundancyOptimizer assigns whole parameters, largest first, to the
+    # least-loaded rank; Adam keeps two state elements per parameter element.
+    load = [0] * world
+    for n in sorted(numels, reverse=True):
+        load[load.index(min(load))] += n
+    assert [2 * x for x in load] == want_zero1
+    # FSDP2 splits every parameter on dim 0: both ranks hold half.
+    per_rank = []
+    for r in range(world):
+        p = O.plan(shapes, world, r)
+        assert [(e.local_rows, e.cols) for e in p.entries] == [(16, 16), (16, 1), (2, 32), (2, 1)]
+        per_rank.append(2 * p.V)
+    assert per_rank == [sum(want_zero1) // 2] * 2 == [676, 676]
+
+
+def test_lab_head_leaves_rank1_empty():
+    lines = read_golden("lab_head_split.txt")
+    world = int(lines[0].split(":")[1])
+    for ln in lines[1:]:
+        lhs, rhs = ln.split("->")
+        shape = parse_shape(lhs.strip())
+        want = [parse_shape(t) for t in rhs.split()]
+        for r in range(world):
+            e = O.plan([shape], world, r).entries[0]
+            local = (e.local_rows,) + tuple(shape[1:])
+            assert local == want[r]
+        # rank 1 still carries a padded piece of c*cols elements, all padding
+        e1 = O.plan([shape], world, 1).entries[0]
+        assert e1.valid_numel == 0 and e1.pad_numel == e1.shard_numel > 0
+
+
+@pytest.mark.parametrize("align", [1, 8])
+def test_plan_invariants_random_shapes(align):
+    rng = np.random.default_rng(7)
+    for _ in range(60):
+        n = int(rng.integers(1, 13))
+        shapes = []
+        for _ in range(int(rng.integers(1, 9))):
+            if rng.random() < 0.3:
+                shapes.append((int(rng.integers(0, 40)),))
+            else:
+                shapes.append((int(rng.integers(0, 40)), int(rng.integers(1, 9))))
+        plans = [O.plan(shapes, n, r, align) for r in range(n)]
+        S = plans[0].S
+        assert all(p.S == S for p in plans)
+        for i, shp in enumerate(shapes):
+            rows = shp[0]
+            es = [p.entries[i] for p in plans]
+            assert sum(e.local_rows for e in es) == rows
+            assert all(e.shard_offset == es[0].shard_offset for e in es)
+            assert es[0].shard_offset % align == 0
+            nxt = 0
+            for e in es:
+                if e.local_rows:
+                    assert e.row_begin == nxt
+                nxt += e.local_rows
+                assert e.valid_numel + e.pad_numel == e.shard_numel == e.chunk_rows * e.cols
+                assert e.seg_numel >= e.shard_numel
+        offs = [e.shard_offset for e in plans[0].entries]
+        segs = [e.seg_numel for e in plans[0].entries]
+        assert offs == list(np.cumsum([0] + segs[:-1]))
+        assert S == sum(segs)
+
+
+def test_plan_config_sizes():
+    """Segment sizes of the workloads (derived by hand from the shapes)."""
+    c1 = configs.get(1)
+    p = O.plan([q.shape for q in c1.groups[0].params], 8, 0)
+    assert p.S == p.V == 30_409_728 and p.F == 243_277_824
+    c3 = configs.get(3)
+    moe, root = ([q.shape for q in g.params] for g in c3.groups)
+    assert O.plan(moe, 6, 0).S == 92_469_293
+    assert O.plan(root, 6, 5).S == 10_924_374
+    r5 = O.plan(moe, 6, 5)
+    empty = sum(1 for e in r5.entries if e.local_rows == 0)
+    assert empty == 2  # the (1, 2048) head and its (1,) bias
+    c4 = configs.get(4)
+    blk = [q.shape for q in c4.groups[0].params]
+    assert O.plan(blk, 64, 0).S == 13_369_600
+    assert O.plan([q.shape for q in c4.groups[-1].params], 64, 0).S == 32_833_664
+
+
+def test_plan_rejects_bad_arguments():
+    with pytest.raises(ValueError):
+        O.plan([(4,)], 0, 0)
+    with pytest.raises(ValueError):
+        O.plan([(4,)], 2, 2)
+    with pytest.raises(ValueError):
+        O.plan([()], 2, 0)
+    with pytest.raises(ValueError):
+        O.plan([(4,)], 2, 0, align=4)
+
+
+# ---------------------------------------------------------------------------
+# State accounting
+# ---------------------------------------------------------------------------
+
+def test_state_bytes_pages_numbers():
+    g = golden_kv("state_bytes.txt")
+    P7 = float(g["params_7b"][0])
+    assert O.state_bytes(P7, 1, 0) == float(g["bytes_7b_ddp"][0])
+    assert round(O.state_bytes(P7, 1, 0) / 2**30, 1) == float(g["gib_7b_ddp"][0])
+    P70 = float(g["params_70b"][0])
+    parts = [float(x) * 1e9 for x in g["parts_70b_gb"]]
+    assert sum(parts) == float(g["bytes_70b_total"][0]) == O.state_bytes(P70, 1, 0)
+    # 2 + 2 + 8 + 4 bytes per parameter, split as the page lists them
+    assert parts == [2 * P70, 2 * P70, 8 * P70, 4 * P70]
+
+
+def test_state_bytes_fence1_relations():
+    P = 7e9
+    for n in (1, 8, 64):
+        row = [O.state_bytes(P, n, s) for s in range(4)]
+        assert all(a >= b for a, b in zip(row, row[1:]))
+        assert row[1] == 4 * P + 12 * P / n
+        assert row[2] == 2 * P + 14 * P / n
+        assert row[3] == 16 * P / n
+    assert O.state_bytes(P, 8, 3) == 16 * P / 8
+    assert O.state_bytes(P, 64, 0) == 112e9
+    with pytest.raises(ValueError):
+        O.state_bytes(P, 8, 4)
+
+
+# ---------------------------------------------------------------------------
+# bf16 conversion
+# ---------------------------------------------------------------------------
+
+def test_bf16_rne_golden_vectors():
+    for ln in read_golden("bf16_rne_cases.txt"):
+        f, b = ln.split()[:2]
+        x = np.array([int(f, 16)], dtype=np.uint32).view(F32)
+        got = int(O.bf16_rne(x)[0])
+        assert got == int(b, 16), (f, hex(got), b)
+
+
+def _nearest_bf16_brute(bits: np.ndarray) -> np.ndarray:
+    """Nearest bf16 by comparing the two neighbours in exact fp64 arithmetic."""
+    out = np.empty(bits.size, dtype=np.uint16)
+    for i, b in enumerate(bits.tolist()):
+        sign = b >> 31
+        mag = b & 0x7FFFFFFF
+        x = abs(float(np.array([mag], dtype=np.uint32).view(F32)[0]))
+        lo = mag >> 16
+        def val(k):
+            if k >= 0x7F80:  # one past the largest finite: 2^128, i.e. overflow
+                return 2.0 ** 128
+            return float(np.array([k << 16], dtype=np.uint32).view(F32)[0])
+        dlo, dhi = x - val(lo), val(lo + 1) - x
+        if dlo < dhi or (dlo == dhi and lo % 2 == 0):
+            k = lo
+        else:
+            k = lo + 1
+        out[i] = (sign << 15) | min(k, 0x7F80)
+    return out
+
+
+def test_bf16_rne_is_nearest_even_brute_force():
+    rng = np.random.default_rng(11)
+    bits = rng.integers(0, 2**32, size=4000, dtype=np.uint64).astype(np.uint32)
+    # add every tie and neighbours for a spread of exponents, incl. subnormals
+    base = rng.integers(0, 2**16, size=500, dtype=np.uint64).astype(np.uint32) << 16
+    extra = np.concatenate([base | 0x8000, base | 0x7FFF, base | 0x8001, base])
+    bits = np.concatenate([bits, extra]).astype(np.uint32)
+    x = bits.view(F32)
+    keep = ~np.isnan(x)
+    want = _nearest_bf16_brute(bits[keep])
+    got = O.bf16_rne(x[keep])
+    assert np.array_equal(got, want)
+
+
+def test_bf16_rne_matches_torch_library_cast():
+    rng = np.random.default_rng(3)
+    parts = [rng.standard_normal(1 << 20).astype(F32) * s for s in (1e-3, 0.02, 1.0, 1e30)]
+    parts.append((rng.standard_normal(1 << 16) * 1e-39).astype(F32))  # subnormals
+    parts.append(rng.integers(0, 2**32, size=1 << 18, dtype=np.uint64).astype(np.uint32).view(F32))
+    x = np.concatenate(parts)
+    x = x[~np.isnan(x)]
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.bf16_rne(x), want)
+    # widening back is exact and equals torch's
+    back = torch.from_numpy(want.view(np.int16)).view(torch.bfloat16).float().numpy()
+    w = O.bf16_to_f32(want)
+    assert np.array_equal(w.view(np.uint32), back.view(np.uint32))
+
+
+def test_bf16_nan_stays_nan_with_sign():
+    x = np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFFA12345], dtype=np.uint32).view(F32)
+    out = O.bf16_rne(x)
+    assert np.all(np.isnan(O.bf16_to_f32(out)))
+    assert [int(v) >> 15 for v in out] == [0, 1, 0, 1]
+
+
+# ---------------------------------------------------------------------------
+# pack / unpack
+# ---------------------------------------------------------------------------
+
+SMALL_CASES = [
+    ([(32, 16), (32,), (4, 32), (4,)], 2),               # the MLP probe
+    ([(1408 // 16, 2048 // 64), (2048 // 16,), (64, 32), (1, 32), (1,)], 6),
+    ([(5, 3), (0, 4), (7,), (1, 5), (13, 2)], 4),
+    ([(6, 3), (17,)], 8),                                # more ranks than rows
+    ([(9, 7)], 1),
+]
+
+
+def _chunks_of(W: torch.Tensor, n: int, j: int) -> torch.Tensor:
+    ch = torch.chunk(W, n, 0)
+    if j < len(ch):
+        return ch[j]
+    return W[W.shape[0]:]
+
+
+@pytest.mark.parametrize("align", [1, 8])
+@pytest.mark.parametrize("case", range(len(SMALL_CASES)))
+def test_pack_matches_torch_chunk_cast_pad_cat(case, align):
+    shapes, n = SMALL_CASES[case]
+    Ws = [synth.normal_f32(int(np.prod(s)) if s else 1, 0.02, ("pk", case, i)).reshape(s)
+          for i, s in enumerate(shapes)]
+    for r in range(n):
+        p = O.plan(shapes, n, r, align)
+        got = O.pack(p, [_chunks_of(W, n, r).numpy() for W in Ws])
+        parts = []
+        for W, e in zip(Ws, p.entries):
+            piece = _chunks_of(W, n, r).reshape(-1).to(torch.bfloat16).view(torch.int16)
+            pad = torch.zeros(e.seg_numel - piece.numel(), dtype=torch.int16)
+            parts.append(torch.cat([piece, pad]))
+        want = torch.cat(parts).numpy().view(np.uint16)
+        assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("align", [1, 8])
+@pytest.mark.parametrize("case", range(len(SMALL_CASES)))
+def test_unpack_of_packs_is_cast_of_full_params(case, align):
+    shapes, n = SMALL_CASES[case]
+    Ws = [synth.normal_f32(int(np.prod(s)), 0.02, ("rt", case, i)).reshape(s)
+          for i, s in enumerate(shapes)]
+    plans = [O.plan(shapes, n, r, align) for r in range(n)]
+    ag = np.stack([O.pack(plans[r], [_chunks_of(W, n, r).numpy() for W in Ws])
+                   for r in range(n)])
+    # padding never reaches an output: overwrite it with the sentinel NaN
+    for r in range(n):
+        mask = np.ones(plans[r].S, dtype=bool)
+        for e in plans[r].entries:
+            mask[e.shard_offset:e.shard_offset + e.valid_numel] = False
+        ag[r, mask] = synth.SENTINEL_BF16
+    for r in range(n):
+        fulls = O.unpack(plans[r], ag)
+        for W, full in zip(Ws, fulls):
+            want = W.reshape(W.shape[0], full.shape[1]).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            assert np.array_equal(full, want)
+
+
+def test_unpack_is_rank_concatenation_of_arbitrary_rows():
+    """Unpack reads row j's piece for rows of chunk j; checked on random bits."""
+    shapes, n = [(11, 3), (2,), (7, 5)], 4
+    p = O.plan(shapes, n, 0)
+    rng = np.random.default_rng(5)
+    ag = rng.integers(0, 2**16, size=(n, p.S), dtype=np.uint64).astype(np.uint16)
+    fulls = O.unpack(p, ag)
+    for i, (shp, e) in enumerate(zip(shapes, p.entries)):
+        pieces = []
+        for j in range(n):
+            t = torch.chunk(torch.arange(shp[0]), n)[j] if j < len(torch.chunk(torch.arange(shp[0]), n)) else torch.arange(0)
+            k = t.numel() * e.cols
+            pieces.append(ag[j, e.shard_offset:e.shard_offset + k])
+        assert np.array_equal(fulls[i].reshape(-1), np.concatenate(pieces))
+
+
+# ---------------------------------------------------------------------------
+# reduce
+# ---------------------------------------------------------------------------
+
+def _rs_buffer(p, n, key, fill_pad=True):
+    rs = np.empty((n, p.S), dtype=np.uint16)
+    for j in range(n):
+        rs[j] = synth.bf16_bits_to_u16(synth.normal_bf16_bits(p.S, 1e-3, key + (j,)))
+    if fill_pad:
+        mask = np.ones(p.S, dtype=bool)
+        for e in p.entries:
+            mask[e.shard_offset:e.shard_offset + e.valid_numel] = False
+        rs[:, mask] = synth.SENTINEL_BF16
+    return rs
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 6, 8, 64])
+def test_reduce_all_equal_contributions_is_exact(n):
+    """N equal bf16 gradients average to exactly that gradient (no 2x bug)."""
+    shapes = [(130, 3), (67,)]
+    p = O.plan(shapes, n, 0)
+    row = synth.bf16_bits_to_u16(synth.normal_bf16_bits(p.S, 1e-3, ("eq", n)))
+    rs = np.tile(row, (n, 1))
+    for e, g in zip(p.entries, O.reduce(p, rs)):
+        want = O.bf16_to_f32(row[e.shard_offset:e.shard_offset + e.valid_numel])
+        assert np.array_equal(g.view(np.uint32), want.view(np.uint32))
+
+
+def test_reduce_n1_is_exact_widening_and_keeps_negative_zero():
+    p = O.plan([(5, 2)], 1, 0)
+    rs = np.array([[0x8000, 0x0000, 0x3F80, 0xBF80, 0x0001, 0x8001, 0x7F80, 0xFF80, 0x4049, 0xC049]],
+                  dtype=np.uint16)
+    g = O.reduce(p, rs)[0].reshape(-1)
+    assert np.array_equal(g.view(np.uint32), rs[0].astype(np.uint32) << 16)
+    # all-(-0) contributions stay -0 at any N
+    p4 = O.plan([(4,)], 4, 0)
+    neg0 = np.full((4, p4.S), 0x8000, dtype=np.uint16)
+    assert O.reduce(p4, neg0)[0].view(np.uint32)[0] == 0x80000000
+
+
+@pytest.mark.parametrize("n", [2, 6, 8, 64])
+def test_reduce_within_fp32_error_bound_of_exact_sum(n):
+    shapes = [(3 * n + 1, 5), (2 * n - 1,)]
+    for r in (0, n - 1):
+        p = O.plan(shapes, n, r)
+        rs = _rs_buffer(p, n, ("eb", n, r))
+        grads = O.reduce(p, rs)
+        u = 2.0 ** -24
+        for e, g in zip(p.entries, grads):
+            cols = [O.bf16_to_f32(rs[j, e.shard_offset:e.shard_offset + e.valid_numel]).astype(np.float64)
+                    for j in range(n)]
+            for i in range(e.valid_numel):
+                xs = [c[i] for c in cols]
+                exact = math.fsum(xs) / n
+                bound = (n - 1) * u * sum(abs(x) for x in xs) / n + u * abs(exact) + 1e-45
+                assert abs(float(g[i]) - exact) <= bound * 1.0001
+
+
+def test_reduce_matches_torch_mean_and_never_reads_padding():
+    n = 6
+    shapes = [(1408 // 8, 16), (2048 // 8,), (1, 16), (1,)]
+    for r in range(n):
+        p = O.plan(shapes, n, r)
+        rs = _rs_buffer(p, n, ("tm", r), fill_pad=True)
+        t = torch.from_numpy(rs.view(np.int16)).view(torch.bfloat16).float()
+        for e, g in zip(p.entries, O.reduce(p, rs)):
+            assert np.all(np.isfinite(g))
+            want = (t[:, e.shard_offset:e.shard_offset + e.valid_numel].sum(0) / n).numpy()
+            np.testing.assert_allclose(g, want, rtol=2e-6, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# AdamW
+# ---------------------------------------------------------------------------
+
+HP = dict(lr=3e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+
+
+def _state(n, key):
+    p = synth.normal_f32(n, 0.02, key + ("p",)).numpy().copy()
+    return p, np.zeros(n, F32), np.zeros(n, F32)
+
+
+def test_adamw_zero_grad_only_decays():
+    p, m, v = _state(1000, ("z",))
+    p0 = p.astype(np.float64)
+    g = np.zeros_like(p)
+    for t in (1, 2, 3):
+        O.adamw(p, g, m, v, t, **HP)
+        assert not m.any() and not v.any()
+        want = p0 * (1 - HP["lr"] * HP["weight_decay"]) ** t
+        np.testing.assert_allclose(p, want, rtol=4 * 2**-24, atol=0)
+
+
+def test_adamw_first_step_closed_form():
+    p, m, v = _state(5000, ("s1",))
+    p0 = p.astype(np.float64)
+    g = synth.normal_f32(5000, 1e-3, ("s1", "g")).numpy()
+    O.adamw(p, g, m, v, 1, **HP)
+    g64 = g.astype(np.float64)
+    lr, wd, eps = HP["lr"], HP["weight_decay"], HP["eps"]
+    want = p0 * (1 - lr * wd) - lr * g64 / (np.abs(g64) + eps)
+    np.testing.assert_allclose(p, want, rtol=0, atol=8 * 2**-24 * np.abs(p0).max() + 1e-11)
+    np.testing.assert_allclose(m, (1 - HP["beta1"]) * g64, rtol=2**-22)
+    np.testing.assert_allclose(v, (1 - HP["beta2"]) * g64 * g64, rtol=2**-21)
+
+
+def test_adamw_constant_grad_three_steps_closed_form():
+    p, m, v = _state(4000, ("cg",))
+    p64 = p.astype(np.float64)
+    g = synth.normal_f32(4000, 1e-3, ("cg", "g")).numpy()
+    g64 = g.astype(np.float64)
+    lr, wd, eps, b1, b2 = HP["lr"], HP["weight_decay"], HP["eps"], HP["beta1"], HP["beta2"]
+    for t in (1, 2, 3):
+        O.adamw(p, g, m, v, t, **HP)
+        # bias-corrected moments of a constant gradient are g and g^2 exactly
+        p64 = p64 * (1 - lr * wd) - lr * g64 / (np.abs(g64) + eps)
+        np.testing.assert_allclose(m, (1 - b1 ** t) * g64, rtol=8 * 2**-24)
+        np.testing.assert_allclose(v, (1 - b2 ** t) * g64 * g64, rtol=16 * 2**-24)
+    np.testing.assert_allclose(p, p64, rtol=0, atol=32 * 2**-24 * np.abs(p64).max())
+
+
+def test_adamw_commutes_with_sharding_bit_exact():
+    """AdamW on each rank's chunk == chunk of AdamW on the whole tensor."""
+    shape, n = (37, 6), 4
+    W = synth.normal_f32(37 * 6, 0.02, ("sc", "W")).numpy().reshape(shape)
+    grads = [synth.normal_f32(37 * 6, 1e-3, ("sc", t)).numpy().reshape(shape) for t in (1, 2, 3)]
+    whole = [W.copy(), np.zeros(shape, F32), np.zeros(shape, F32)]
+    for t, g in enumerate(grads, 1):
+        O.adamw(whole[0], g, whole[1], whole[2], t, **HP)
+    for r in range(n):
+        b, lr_ = O.rows_of_rank(37, n, r)
+        sh = [W[b:b + lr_].copy(), np.zeros((lr_, 6), F32), np.zeros((lr_, 6), F32)]
+        for t, g in enumerate(grads, 1):
+            O.adamw(sh[0], np.ascontiguousarray(g[b:b + lr_]), sh[1], sh[2], t, **HP)
+        for a, w in zip(sh, whole):
+            assert np.array_equal(a.view(np.uint32), w[b:b + lr_].view(np.uint32))
+
+
+def test_adamw_matches_torch_optim_adamw_three_steps():
+    cfg = configs.get(0)
+    for i, prm in enumerate(cfg.params):
+        n = prm.numel
+        W = synth.normal_f32(n, 0.02, ("ta", i)).reshape(prm.shape)
+        tp = torch.nn.Parameter(W.clone())
+        opt = torch.optim.AdamW([tp], lr=HP["lr"], betas=(HP["beta1"], HP["beta2"]),
+                                eps=HP["eps"], weight_decay=HP["weight_decay"], foreach=False)
+        p = W.numpy().copy()
+        m, v = np.zeros_like(p), np.zeros_like(p)
+        for t in (1, 2, 3):
+            g = synth.normal_f32(n, 1e-3, ("ta", i, t)).reshape(prm.shape)
+            tp.grad = g.clone()
+            opt.step()
+            O.adamw(p, g.numpy(), m, v, t, **HP)
+        st = opt.state[tp]
+        for ours, ref in ((p, tp.detach()), (m, st["exp_avg"]), (v, st["exp_avg_sq"])):
+            ref = ref.numpy()
+            assert np.abs(ours - ref).max() <= 1e-6 * np.abs(ref).max()
+
+
+def test_adamw_nearly_scale_invariant_in_grad():
+    """Doubling every gradient barely moves AdamW (why a 2x reduce bug hid)."""
+    p1, m1, v1 = _state(2000, ("si",))
+    p2, m2, v2 = p1.copy(), m1.copy(), v1.copy()
+    p0 = p1.copy()
+    for t in (1, 2, 3):
+        g = synth.normal_f32(2000, 1e-3, ("si", t)).numpy()
+        O.adamw(p1, g, m1, v1, t, **HP)
+        O.adamw(p2, (g * 2).astype(F32), m2, v2, t, **HP)
+    moved = np.abs(p1 - p0).max()
+    # only the eps term (and nothing else) sees the scale: tiny gradients move
+    assert np.abs(p1 - p2).max() < 0.05 * moved
+    assert np.abs(p1 - p2).mean() < 0.002 * moved
+    assert not np.array_equal(m1, m2)
+
+
+def test_adamw_scalars_precision():
+    s = O.adamw_scalars(3e-4, 0.9, 0.999, 1e-8, 0.01, 2)
+    assert s.decay == F32(1 - 3e-6)
+    assert s.step_size == F32(3e-4 / (1 - 0.81))
+    assert s.bc2_sqrt == F32(math.sqrt(1 - 0.999 ** 2))
+    with pytest.raises(ValueError):
+        O.adamw_scalars(3e-4, 0.9, 0.999, 1e-8, 0.01, 0)
+
+
+# ---------------------------------------------------------------------------
+# One whole step on the MLP probe, against torch library building blocks
+# ---------------------------------------------------------------------------
+
+def test_whole_step_mlp_probe_against_torch_building_blocks():
+    cfg = configs.get(0)
+    n = cfg.world
+    shapes = [q.shape for q in cfg.params]
+    Ws = [synth.normal_f32(q.numel, 0.02, ("ws", i)).reshape(q.shape) for i, q in enumerate(cfg.params)]
+    plans = [O.plan(shapes, n, r) for r in range(n)]
+    for r in range(n):
+        p = plans[r]
+        masters = [_chunks_of(W, n, r).numpy().copy() for W in Ws]
+        ms = [np.zeros_like(x) for x in masters]
+        vs = [np.zeros_like(x) for x in masters]
+        tparams = [torch.nn.Parameter(torch.from_numpy(x.copy())) for x in masters]
+        opt = torch.optim.AdamW(tparams, lr=cfg.hp.lr, betas=(cfg.hp.beta1, cfg.hp.beta2),
+                                eps=cfg.hp.eps, weight_decay=cfg.hp.weight_decay, foreach=False)
+        for t in (1, 2, 3):
+            rs = _rs_buffer(p, n, ("ws", r, t))
+            grads = O.reduce(p, rs)
+            trs = torch.from_numpy(rs.view(np.int16)).view(torch.bfloat16).float()
+            for e, g, tp in zip(p.entries, grads, tparams):
+                tg = trs[:, e.shard_offset:e.shard_offset + e.valid_numel].sum(0) / n
+                np.testing.assert_allclose(g, tg.numpy(), rtol=2e-6, atol=1e-12)
+                tp.grad = tg.reshape(tp.shape).clone()
+            opt.step()
+            for x, g, m, v in zip(masters, grads, ms, vs):
+                O.adamw(x, g.reshape(x.shape), m, v, t, **vars(cfg.hp))
+        for x, tp in zip(masters, tparams):
+            ref = tp.detach().numpy()
+            assert np.abs(x - ref).max() <= 1e-6 * max(np.abs(ref).max(), 1e-30)
+        seg = O.pack(p, masters)
+        want = torch.cat([torch.cat([tp.detach().reshape(-1).to(torch.bfloat16).view(torch.int16),
+                                     torch.zeros(e.seg_numel - e.valid_numel, dtype=torch.int16)])
+                          for e, tp in zip(p.entries, tparams)]).numpy().view(np.uint16)
+        # the two AdamW orders may differ by an fp32 ulp, which can move a bf16 tie
+        diff = np.abs(seg.astype(np.int32) - want.astype(np.int32))
+        assert diff.max() <= 1
