@@ -1,0 +1,247 @@
+/*
+ * fsdp_shard.h -- C ABI of one rank's FSDP2 sharded step on MI355X (gfx950).
+ *
+ * The library implements the four per-rank data movements of fully sharded
+ * data parallel training with per-parameter Shard(0) sharding and a
+ * bf16-param / fp32-reduce mixed-precision policy:
+ *
+ *   copy-in   fsdp_pack_allgather    fp32 master shards -> bf16 [S] segment
+ *   copy-out  fsdp_unpack_allgather  bf16 [N, S] buffer  -> full bf16 params
+ *   reduce    fsdp_reduce_shard      bf16 [N, S] grads   -> fp32 grad shards
+ *   update    fsdp_adamw_shard       AdamW on fp32 master, m and v shards
+ *
+ * plus a host-side shard-layout planner.  The collectives between these steps
+ * (all-gather, reduce-scatter) are not part of the library: a caller runs them
+ * on the buffers these calls read and write.
+ *
+ * Pages cited (by title and section):
+ *   [ST] "Sharded Training: FSDP2, DTensor, Tensor and Pipeline Parallelism"
+ *   [MS] "Introduction to PyTorch FSDP2 Backend Features"
+ *   [AF] "PyTorch FSDP2 Guide: Distributed LLM Training with DTensor"
+ *
+ * Conventions for every function below.
+ *  - Every call returns an fsdp_status: FSDP_OK (0) or a negative error.  No
+ *    C++ exception crosses the ABI.  On error, fsdp_last_error() returns a
+ *    thread-local message naming the offending argument, and nothing has been
+ *    launched.
+ *  - Device pointers are plain addresses of device memory on the device that
+ *    was current when fsdp_bind ran; streams are hipStream_t values passed as
+ *    void* (NULL = the default stream).  Hot calls only enqueue work on the
+ *    stream: they never synchronize and never allocate.
+ *  - The caller owns every tensor.  The library owns the plan and the device
+ *    tables it uploads at bind time, and frees both in fsdp_plan_destroy.
+ *  - bf16 values travel as uint16_t bit patterns; fp32 as float.
+ *  - A shard's valid elements start at offset 0 of the pointer the caller
+ *    binds; nothing past local_rows * cols is read or written.
+ *  - Sizes and offsets are in elements unless a name says bytes.
+ */
+#ifndef FSDP_SHARD_H
+#define FSDP_SHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FSDP_ABI_VERSION 1
+
+typedef int32_t fsdp_status;
+enum {
+    FSDP_OK = 0,
+    FSDP_E_INVAL = -1,        /* null pointer, world < 1, rank out of range,
+                                 negative rows or cols, bad index           */
+    FSDP_E_UNSUPPORTED = -2,  /* align_elems not 1 or 8, zero_stage not 0..3 */
+    FSDP_E_ALIGN = -3,        /* fp32 pointer not 4-byte or bf16 pointer not
+                                 2-byte aligned                            */
+    FSDP_E_STATE = -4,        /* hot call before the roles it needs are bound,
+                                 or on a device other than the bound one    */
+    FSDP_E_HIP = -5,          /* HIP runtime error (launch, copy, async)    */
+    FSDP_E_NOMEM = -6         /* host or device allocation failed at plan or
+                                 bind time                                 */
+};
+
+/* Opaque per-(group, rank) plan. */
+typedef struct fsdp_plan fsdp_plan;
+
+/* Layout of one parameter of the group, as seen by this rank.
+ * [ST] fully_shard paragraph: rank r keeps chunk r of
+ * torch.chunk(param, world, dim=0), padded internally; chunk_rows is
+ * ceil(rows / world), so ranks past the last chunk hold empty pieces. */
+typedef struct fsdp_shard_entry_t {
+    int64_t rows;         /* dim 0 of the parameter                         */
+    int64_t cols;         /* product of the other dims (1 for 1-D)          */
+    int64_t chunk_rows;   /* c = ceil(rows / world), 0 when rows == 0       */
+    int64_t row_begin;    /* first row this rank owns: min(rank * c, rows)  */
+    int64_t local_rows;   /* rows this rank owns (0 = empty chunk)          */
+    int64_t shard_offset; /* element offset of the piece inside a segment   */
+    int64_t shard_numel;  /* padded piece: c * cols                         */
+    int64_t valid_numel;  /* local_rows * cols                              */
+    int64_t pad_numel;    /* shard_numel - valid_numel                      */
+    int64_t seg_numel;    /* shard_numel rounded up to align_elems          */
+} fsdp_shard_entry_t;
+
+typedef struct fsdp_plan_info_t {
+    int32_t n_params;
+    int32_t world;
+    int32_t rank;
+    int32_t align_elems;
+    int64_t S;            /* segment length: sum of seg_numel (any rank)    */
+    int64_t V;            /* valid elements this rank owns                  */
+    int64_t F;            /* elements of the full (unsharded) parameters    */
+    int64_t pad_total;    /* S - V                                          */
+    int32_t n_empty;      /* parameters whose piece on this rank is empty   */
+    int32_t bound;        /* bitmask of bound roles (FSDP_ROLE_*)           */
+    int64_t n_tiles[4];   /* work tiles of pack, unpack, reduce, adamw      */
+} fsdp_plan_info_t;
+
+/* torch.optim.AdamW hyperparameters ([ST] ZeroRedundancyOptimizer example
+ * and lab: lr = 3e-4; betas, eps and weight decay are AdamW's). */
+typedef struct fsdp_adamw_hparams_t {
+    double lr;
+    double beta1;
+    double beta2;
+    double eps;
+    double weight_decay;
+} fsdp_adamw_hparams_t;
+
+enum {
+    FSDP_ROLE_MASTER = 1,
+    FSDP_ROLE_GRAD = 2,
+    FSDP_ROLE_EXP_AVG = 4,
+    FSDP_ROLE_EXP_AVG_SQ = 8,
+    FSDP_ROLE_FULL = 16
+};
+
+/* ---- library ---------------------------------------------------------- */
+
+int32_t fsdp_abi_version(void);
+/* Static string for a status code; never NULL. */
+const char *fsdp_status_string(fsdp_status s);
+/* Thread-local detail of this thread's last failed call ("" if none). */
+const char *fsdp_last_error(void);
+
+/* ---- planner: host only, needs no GPU ---------------------------------- */
+
+/* Plan the communication segment of one parameter group for rank `rank`.
+ * [ST] fully_shard paragraph: every parameter is a Shard(0) DTensor built
+ * from torch.chunk with internal padding, and one fully_shard call makes one
+ * group, one unit of communication.  The group's pieces are laid out in
+ * registration order (rows[i], cols[i] for i < n_params), each padded to
+ * chunk_rows * cols elements and its start rounded up to a multiple of
+ * align_elems (1: no gap; 8: 16-byte starts).  S does not depend on rank.
+ *   rows, cols   host arrays of n_params entries; rows >= 0, cols >= 1
+ *                (cols = numel / dim 0; a 0-dim tensor cannot be sharded)
+ *   world        N >= 1; rank in [0, N)
+ *   out          receives a new plan; release with fsdp_plan_destroy
+ * Errors: FSDP_E_INVAL, FSDP_E_UNSUPPORTED (align_elems), FSDP_E_NOMEM. */
+fsdp_status fsdp_plan_create(const int64_t *rows, const int64_t *cols,
+                             int32_t n_params, int32_t world, int32_t rank,
+                             int32_t align_elems, fsdp_plan **out);
+
+fsdp_status fsdp_plan_info(const fsdp_plan *plan, fsdp_plan_info_t *out);
+
+/* Layout of parameter i on this rank.  Errors: FSDP_E_INVAL. */
+fsdp_status fsdp_plan_entry(const fsdp_plan *plan, int32_t i,
+                            fsdp_shard_entry_t *out);
+
+/* Rows of parameter i owned by rank j (any j in [0, N)): the copy-out reads
+ * them from row j of the all-gather buffer.  Errors: FSDP_E_INVAL. */
+fsdp_status fsdp_plan_rows_of_rank(const fsdp_plan *plan, int32_t i, int32_t j,
+                                   int64_t *row_begin, int64_t *local_rows);
+
+/* Bytes of training state per rank for n_params parameters under ZeRO stage
+ * 0..3 with 16 bytes per parameter (2 bf16 weights, 2 bf16 grads, 12 for the
+ * fp32 master and Adam's two moments): [ST] opening paragraph, ZeRO
+ * paragraph and Fence 1; [AF] "The Problem" (1,120 GB for 70B).
+ * Errors: FSDP_E_INVAL (world < 1, n_params < 0, null out),
+ *         FSDP_E_UNSUPPORTED (zero_stage). */
+fsdp_status fsdp_state_bytes(double n_params, int32_t world, int32_t zero_stage,
+                             double *per_rank_bytes);
+
+/* Frees the plan and its device tables.  Waits for the device to finish
+ * using them.  NULL is a no-op. */
+void fsdp_plan_destroy(fsdp_plan *plan);
+
+/* ---- bind: device tables, once per set of persistent tensors ------------ */
+
+/* Record the per-parameter device tensors of this rank and upload the plan's
+ * device tables (entries and work tiles) on `stream`, then wait for that
+ * upload.  Each array is a host array of n_params device pointers, or NULL to
+ * leave that role unbound:
+ *   master, grad, exp_avg, exp_avg_sq  fp32 shards, valid_numel elements each
+ *                                      (the sharded parameter, its reduced
+ *                                      gradient, AdamW's m and v: [ST] the
+ *                                      optimizer built after sharding sees
+ *                                      only shards, so its state is sharded)
+ *   full                               bf16 [rows, cols] unsharded params
+ * A pointer may be NULL where its tensor has no elements.  Binding again
+ * replaces the pointers (waiting for the stream first).  Allocates device
+ * memory on the current device the first time.
+ * Errors: FSDP_E_INVAL (null pointer for a non-empty tensor), FSDP_E_ALIGN,
+ *         FSDP_E_NOMEM, FSDP_E_HIP. */
+fsdp_status fsdp_bind(fsdp_plan *plan, float *const *master, float *const *grad,
+                      float *const *exp_avg, float *const *exp_avg_sq,
+                      uint16_t *const *full, void *stream);
+
+/* ---- hot path: enqueue on `stream`; no sync, no allocation ------------- */
+
+/* All-gather copy-in.  Writes all S elements of ag_in: for each parameter,
+ * ag_in[shard_offset + i] = bf16(master[i]) for i < valid_numel, rounded to
+ * nearest even (a NaN stays a quiet NaN with its sign), and 0 in the piece's
+ * padding and any alignment gap.  [ST] "Mixed precision": sharded parameters
+ * stay fp32 and bf16 copies are all-gathered (param_dtype, half the bytes);
+ * [MS] "Mixed Precision".  ag_in may be row `rank` of the [N, S] all-gather
+ * output (in-place all-gather).  Needs FSDP_ROLE_MASTER.
+ * Errors: FSDP_E_INVAL (null ag_in with S > 0), FSDP_E_ALIGN, FSDP_E_STATE,
+ *         FSDP_E_HIP. */
+fsdp_status fsdp_pack_allgather(const fsdp_plan *plan, uint16_t *ag_in,
+                                void *stream);
+
+/* All-gather copy-out.  ag_out is the [N, S] bf16 all-gather result, row j =
+ * rank j's segment.  For every parameter and every rank j, copies rank j's
+ * local_rows(j) * cols valid elements to rows [row_begin(j), ...) of the full
+ * [rows, cols] tensor; padding is never read.  [ST] fully_shard paragraph
+ * (chunks of torch.chunk, padded internally); [MS] "DTensor" (the logical
+ * tensor is the whole parameter).  Bit copy, no arithmetic.
+ * Needs FSDP_ROLE_FULL.  Errors: as fsdp_pack_allgather. */
+fsdp_status fsdp_unpack_allgather(const fsdp_plan *plan, const uint16_t *ag_out,
+                                  void *stream);
+
+/* Reduce-scatter's local reduction for this rank.  rs_in is [N, S] bf16: row
+ * j is rank j's gradient contribution laid out like a segment.  For each
+ * parameter and i < valid_numel:
+ *     grad[i] = ((x_0 + x_1) + ... + x_{N-1}) / N,   x_j = fp32(rs_in[j][off+i])
+ * with fp32 adds in rank order and one correctly rounded fp32 division.
+ * [ST] "Mixed precision" (reduce_dtype fp32), "Other controls" and "The bug
+ * Adam hid" (set_force_sum_reduction_for_comms: reduce with SUM and divide by
+ * the world size); [MS] "Mixed Precision".  Padding is never read.
+ * Needs FSDP_ROLE_GRAD.  Errors: as fsdp_pack_allgather. */
+fsdp_status fsdp_reduce_shard(const fsdp_plan *plan, const uint16_t *rs_in,
+                              void *stream);
+
+/* One AdamW step (decoupled weight decay, bias-corrected; amsgrad and
+ * maximize off) on every bound shard, in place.  `step` counts from 1; m and
+ * v must be zero before step 1.  Host scalars come from the hyperparameters
+ * in fp64 and are rounded once to fp32; per element, each operation is one
+ * fp32 rounding, no fused multiply-add:
+ *     p = p * (1 - lr*wd);  m = b1*m + (1-b1)*g;  v = b2*v + (1-b2)*(g*g)
+ *     p = p - (lr / (1 - b1^t)) * (m / (sqrt(v) / sqrt(1 - b2^t) + eps))
+ * [ST] ZeroRedundancyOptimizer example and lab (torch.optim.AdamW at
+ * lr 3e-4), fully_shard paragraph (optimizer state sharded with the
+ * parameters); [MS] "Working Principle" (Update State).
+ * Needs FSDP_ROLE_MASTER | GRAD | EXP_AVG | EXP_AVG_SQ.
+ * Errors: FSDP_E_INVAL (null hparams, step < 1), FSDP_E_STATE, FSDP_E_HIP. */
+fsdp_status fsdp_adamw_shard(const fsdp_plan *plan,
+                             const fsdp_adamw_hparams_t *hp, int64_t step,
+                             void *stream);
+
+/* Wait for `stream` and report any asynchronous HIP error as FSDP_E_HIP. */
+fsdp_status fsdp_check_stream(void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FSDP_SHARD_H */

@@ -1,0 +1,73 @@
+"""Build the sharded-step library for gfx950 in-tree.
+
+    python -m sharded_shard_amd.build          # writes sharded_shard_amd/lib/libfsdp_shard.so
+
+hipcc cross-compiles for gfx950 without a GPU.  Device code is built with
+fp-contraction off and correctly rounded fp32 divide and square root (the
+reduction and AdamW must round every operation once), and with packed-fp32
+instructions disabled.
+"""
+from __future__ import annotations
+
+import os
+import shlex
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "csrc")
+OUT_DIR = os.path.join(HERE, "lib")
+LIB = os.path.join(OUT_DIR, "libfsdp_shard.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.path.join(ROCM, "bin", "hipcc")
+ARCH = "gfx950"
+
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter"]
+DEVICE = [f"--offload-arch={ARCH}", "-ffp-contract=off",
+          "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",
+          "-fno-gpu-rdc", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+SOURCES = [
+    ("plan.cpp", ["-x", "c++"]),
+    ("capi.cpp", ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROCM, "include")]),
+    ("kernels.hip", ["-x", "hip"] + DEVICE),
+]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(shlex.quote(c) for c in cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError(f"build step failed: {cmd[0]} ... {cmd[-1]}")
+    return r
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile every source and link the shared library; returns its path."""
+    os.makedirs(OUT_DIR, exist_ok=True)
+    objs = []
+    for name, flags in SOURCES:
+        src = os.path.join(SRC, name)
+        obj = os.path.join(OUT_DIR, name + ".o")
+        _run([HIPCC, *COMMON, *flags, *extra_flags, "-c", src, "-o", obj], verbose)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    os.replace(tmp, LIB)
+    for o in objs:
+        os.remove(o)
+    return LIB
+
+
+def emit_asm(out_path: str) -> str:
+    """Write the gfx950 assembly of the kernels (for inspecting the ISA)."""
+    src = os.path.join(SRC, "kernels.hip")
+    _run([HIPCC, *COMMON, "-x", "hip", *DEVICE, "--cuda-device-only", "-S",
+          src, "-o", out_path], False)
+    return out_path
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

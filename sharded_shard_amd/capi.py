@@ -1,0 +1,224 @@
+"""ctypes binding of libfsdp_shard.so: the C ABI's functions under the same names.
+
+Argument marshalling only: Python lists become int64 arrays, tensors become
+their device addresses, torch streams become hipStream_t handles, and a
+negative status becomes an ``FsdpError``.  Every step of the sharded path runs
+in the HIP library; nothing here computes any part of it.  The library must be
+built (``python -m sharded_shard_amd.build``); importing this module without it
+raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libfsdp_shard.so")
+
+FSDP_OK = 0
+FSDP_E_INVAL = -1
+FSDP_E_UNSUPPORTED = -2
+FSDP_E_ALIGN = -3
+FSDP_E_STATE = -4
+FSDP_E_HIP = -5
+FSDP_E_NOMEM = -6
+
+FSDP_ROLE_MASTER = 1
+FSDP_ROLE_GRAD = 2
+FSDP_ROLE_EXP_AVG = 4
+FSDP_ROLE_EXP_AVG_SQ = 8
+FSDP_ROLE_FULL = 16
+
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+
+class ShardEntry(ctypes.Structure):
+    _fields_ = [(n, _i64) for n in (
+        "rows", "cols", "chunk_rows", "row_begin", "local_rows", "shard_offset",
+        "shard_numel", "valid_numel", "pad_numel", "seg_numel")]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("n_params", _i32), ("world", _i32), ("rank", _i32), ("align_elems", _i32),
+                ("S", _i64), ("V", _i64), ("F", _i64), ("pad_total", _i64),
+                ("n_empty", _i32), ("bound", _i32), ("n_tiles", _i64 * 4)]
+
+
+class AdamwHparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double)]
+
+
+class FsdpError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} [{status}]")
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run: python -m sharded_shard_amd.build")
+
+# The library must use the same HIP runtime as torch, which allocates the
+# tensors and owns the streams: torch ships its own libamdhip64 with the same
+# soname, and loading torch first makes the dynamic linker reuse it instead
+# of loading a second runtime from the system ROCm.
+import torch  # noqa: E402,F401
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_PP = ctypes.POINTER(ctypes.c_void_p)
+
+_SIGS = {
+    "fsdp_abi_version": (_i32, []),
+    "fsdp_status_string": (ctypes.c_char_p, [_i32]),
+    "fsdp_last_error": (ctypes.c_char_p, []),
+    "fsdp_plan_create": (_i32, [ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i32, _i32, _i32,
+                                _i32, ctypes.POINTER(_P)]),
+    "fsdp_plan_info": (_i32, [_P, ctypes.POINTER(PlanInfo)]),
+    "fsdp_plan_entry": (_i32, [_P, _i32, ctypes.POINTER(ShardEntry)]),
+    "fsdp_plan_rows_of_rank": (_i32, [_P, _i32, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
+    "fsdp_state_bytes": (_i32, [ctypes.c_double, _i32, _i32, ctypes.POINTER(ctypes.c_double)]),
+    "fsdp_plan_destroy": (None, [_P]),
+    "fsdp_bind": (_i32, [_P, _PP, _PP, _PP, _PP, _PP, _P]),
+    "fsdp_pack_allgather": (_i32, [_P, _P, _P]),
+    "fsdp_unpack_allgather": (_i32, [_P, _P, _P]),
+    "fsdp_reduce_shard": (_i32, [_P, _P, _P]),
+    "fsdp_adamw_shard": (_i32, [_P, ctypes.POINTER(AdamwHparams), _i64, _P]),
+    "fsdp_check_stream": (_i32, [_P]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+def _check(status: int, call: str) -> None:
+    if status != FSDP_OK:
+        raise FsdpError(status, f"{call}: {fsdp_last_error()}")
+
+
+def addr(x) -> int:
+    """Device address of a tensor (or an int passed through); 0 for None."""
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def stream_handle(stream=None) -> int:
+    """hipStream_t of a torch stream, an int handle, or torch's current stream."""
+    if isinstance(stream, int):
+        return stream
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    return int(stream.cuda_stream)
+
+
+def _ptr_array(items):
+    if items is None:
+        return None
+    arr = (ctypes.c_void_p * max(1, len(items)))()
+    for i, t in enumerate(items):
+        arr[i] = addr(t) or None
+    return ctypes.cast(arr, _PP)
+
+
+# ---- library ---------------------------------------------------------------
+
+def fsdp_abi_version() -> int:
+    return int(lib.fsdp_abi_version())
+
+
+def fsdp_status_string(status: int) -> str:
+    return lib.fsdp_status_string(status).decode()
+
+
+def fsdp_last_error() -> str:
+    return lib.fsdp_last_error().decode()
+
+
+# ---- planner -------------------------------------------------------------------
+
+def fsdp_plan_create(rows, cols, world: int, rank: int, align_elems: int = 1):
+    """Returns an opaque plan handle (ctypes.c_void_p)."""
+    n = len(rows)
+    if len(cols) != n:
+        raise ValueError("rows and cols differ in length")
+    r = (_i64 * max(1, n))(*rows)
+    c = (_i64 * max(1, n))(*cols)
+    out = _P()
+    _check(lib.fsdp_plan_create(r, c, n, world, rank, align_elems, ctypes.byref(out)),
+           "fsdp_plan_create")
+    return out
+
+
+def fsdp_plan_info(plan) -> PlanInfo:
+    info = PlanInfo()
+    _check(lib.fsdp_plan_info(plan, ctypes.byref(info)), "fsdp_plan_info")
+    return info
+
+
+def fsdp_plan_entry(plan, i: int) -> ShardEntry:
+    e = ShardEntry()
+    _check(lib.fsdp_plan_entry(plan, i, ctypes.byref(e)), "fsdp_plan_entry")
+    return e
+
+
+def fsdp_plan_rows_of_rank(plan, i: int, j: int):
+    b, lr = _i64(), _i64()
+    _check(lib.fsdp_plan_rows_of_rank(plan, i, j, ctypes.byref(b), ctypes.byref(lr)),
+           "fsdp_plan_rows_of_rank")
+    return b.value, lr.value
+
+
+def fsdp_state_bytes(n_params: float, world: int, zero_stage: int) -> float:
+    out = ctypes.c_double()
+    _check(lib.fsdp_state_bytes(float(n_params), world, zero_stage, ctypes.byref(out)),
+           "fsdp_state_bytes")
+    return out.value
+
+
+def fsdp_plan_destroy(plan) -> None:
+    lib.fsdp_plan_destroy(plan)
+
+
+# ---- bind and hot path -----------------------------------------------------------
+
+def fsdp_bind(plan, master=None, grad=None, exp_avg=None, exp_avg_sq=None, full=None,
+              stream=None) -> None:
+    """Each role is a list of tensors/addresses (one per parameter) or None."""
+    _check(lib.fsdp_bind(plan, _ptr_array(master), _ptr_array(grad), _ptr_array(exp_avg),
+                         _ptr_array(exp_avg_sq), _ptr_array(full), stream_handle(stream)),
+           "fsdp_bind")
+
+
+def fsdp_pack_allgather(plan, ag_in, stream=None) -> None:
+    _check(lib.fsdp_pack_allgather(plan, addr(ag_in), stream_handle(stream)),
+           "fsdp_pack_allgather")
+
+
+def fsdp_unpack_allgather(plan, ag_out, stream=None) -> None:
+    _check(lib.fsdp_unpack_allgather(plan, addr(ag_out), stream_handle(stream)),
+           "fsdp_unpack_allgather")
+
+
+def fsdp_reduce_shard(plan, rs_in, stream=None) -> None:
+    _check(lib.fsdp_reduce_shard(plan, addr(rs_in), stream_handle(stream)),
+           "fsdp_reduce_shard")
+
+
+def fsdp_adamw_shard(plan, lr: float, beta1: float, beta2: float, eps: float,
+                     weight_decay: float, step: int, stream=None) -> None:
+    hp = AdamwHparams(lr, beta1, beta2, eps, weight_decay)
+    _check(lib.fsdp_adamw_shard(plan, ctypes.byref(hp), step, stream_handle(stream)),
+           "fsdp_adamw_shard")
+
+
+def fsdp_check_stream(stream=None) -> None:
+    _check(lib.fsdp_check_stream(stream_handle(stream)), "fsdp_check_stream")
+
+
+EXPORTS = tuple(_SIGS)

@@ -1,0 +1,365 @@
+// C ABI of the sharded-step library: argument checks, device tables, launches.
+//
+// Every exported function validates its arguments on the host before any HIP
+// call, so the error paths can be exercised without a GPU.  Hot calls only
+// enqueue kernels on the caller's stream.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/fsdp_shard.h"
+#include "plan.hpp"
+
+namespace fsdp {
+hipError_t launch_pack(const PackTile *tiles, int64_t n, const DevEntry *ents,
+                       uint16_t *ag_in, hipStream_t st);
+hipError_t launch_unpack(const UnpackTile *tiles, int64_t n, const DevEntry *ents,
+                         const uint16_t *ag_out, hipStream_t st);
+hipError_t launch_reduce(const ReduceTile *tiles, int64_t n, const DevEntry *ents,
+                         const uint16_t *rs_in, int64_t S, int32_t N, hipStream_t st);
+hipError_t launch_adamw(const EwTile *tiles, int64_t n, const DevEntry *ents,
+                        const float scal[8], hipStream_t st);
+}  // namespace fsdp
+
+struct fsdp_plan {
+    fsdp::Layout L;
+    std::vector<fsdp::DevEntry> host_entries;
+    int32_t bound = 0;
+    int device = -1;
+    char *dmem = nullptr;  // one device block: entries, then the four tile tables
+    fsdp::DevEntry *d_entries = nullptr;
+    fsdp::PackTile *d_pack = nullptr;
+    fsdp::UnpackTile *d_unpack = nullptr;
+    fsdp::ReduceTile *d_reduce = nullptr;
+    fsdp::EwTile *d_adamw = nullptr;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fsdp_status fail(fsdp_status s, const std::string &msg) {
+    g_last_error = msg;
+    return s;
+}
+
+fsdp_status hip_fail(hipError_t e, const char *what) {
+    return fail(FSDP_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool misaligned(const void *p, uintptr_t a) {
+    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0;
+}
+
+size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+// Hot calls run on the device the tables live on.
+fsdp_status check_device(const fsdp_plan *p) {
+    int d = -1;
+    hipError_t e = hipGetDevice(&d);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (d != p->device)
+        return fail(FSDP_E_STATE, "current device " + std::to_string(d) +
+                                      " differs from the bound device " +
+                                      std::to_string(p->device));
+    return FSDP_OK;
+}
+
+fsdp_status need_roles(const fsdp_plan *p, int32_t roles, const char *call) {
+    if (p == nullptr) return fail(FSDP_E_INVAL, std::string(call) + ": null plan");
+    if ((p->bound & roles) != roles || p->dmem == nullptr)
+        return fail(FSDP_E_STATE, std::string(call) + ": the tensors it needs are not bound");
+    return FSDP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fsdp_abi_version(void) { return FSDP_ABI_VERSION; }
+
+const char *fsdp_status_string(fsdp_status s) {
+    switch (s) {
+        case FSDP_OK: return "ok";
+        case FSDP_E_INVAL: return "invalid argument";
+        case FSDP_E_UNSUPPORTED: return "unsupported option";
+        case FSDP_E_ALIGN: return "misaligned pointer";
+        case FSDP_E_STATE: return "plan not bound for this call or device";
+        case FSDP_E_HIP: return "HIP runtime error";
+        case FSDP_E_NOMEM: return "out of memory";
+        default: return "unknown status";
+    }
+}
+
+const char *fsdp_last_error(void) { return g_last_error.c_str(); }
+
+fsdp_status fsdp_plan_create(const int64_t *rows, const int64_t *cols,
+                             int32_t n_params, int32_t world, int32_t rank,
+                             int32_t align_elems, fsdp_plan **out) {
+    if (out == nullptr) return fail(FSDP_E_INVAL, "fsdp_plan_create: null out");
+    *out = nullptr;
+    try {
+        fsdp_plan *p = new fsdp_plan();
+        std::string err;
+        fsdp_status s = fsdp::build_layout(rows, cols, n_params, world, rank,
+                                           align_elems, &p->L, &err);
+        if (s != FSDP_OK) {
+            delete p;
+            return fail(s, "fsdp_plan_create: " + err);
+        }
+        p->host_entries.assign(static_cast<size_t>(n_params), fsdp::DevEntry{});
+        for (int32_t i = 0; i < n_params; ++i)
+            p->host_entries[i].valid_numel = p->L.entries[i].valid_numel;
+        *out = p;
+        return FSDP_OK;
+    } catch (const std::bad_alloc &) {
+        return fail(FSDP_E_NOMEM, "fsdp_plan_create: host allocation failed");
+    } catch (...) {
+        return fail(FSDP_E_INVAL, "fsdp_plan_create: unexpected failure");
+    }
+}
+
+fsdp_status fsdp_plan_info(const fsdp_plan *p, fsdp_plan_info_t *out) {
+    if (p == nullptr || out == nullptr) return fail(FSDP_E_INVAL, "fsdp_plan_info: null argument");
+    std::memset(out, 0, sizeof(*out));
+    out->n_params = static_cast<int32_t>(p->L.entries.size());
+    out->world = p->L.world;
+    out->rank = p->L.rank;
+    out->align_elems = p->L.align;
+    out->S = p->L.S;
+    out->V = p->L.V;
+    out->F = p->L.F;
+    out->pad_total = p->L.S - p->L.V;
+    out->n_empty = p->L.n_empty;
+    out->bound = p->bound;
+    out->n_tiles[0] = static_cast<int64_t>(p->L.pack.size());
+    out->n_tiles[1] = static_cast<int64_t>(p->L.unpack.size());
+    out->n_tiles[2] = static_cast<int64_t>(p->L.reduce.size());
+    out->n_tiles[3] = static_cast<int64_t>(p->L.adamw.size());
+    return FSDP_OK;
+}
+
+fsdp_status fsdp_plan_entry(const fsdp_plan *p, int32_t i, fsdp_shard_entry_t *out) {
+    if (p == nullptr || out == nullptr) return fail(FSDP_E_INVAL, "fsdp_plan_entry: null argument");
+    if (i < 0 || static_cast<size_t>(i) >= p->L.entries.size())
+        return fail(FSDP_E_INVAL, "fsdp_plan_entry: index out of range");
+    *out = p->L.entries[i];
+    return FSDP_OK;
+}
+
+fsdp_status fsdp_plan_rows_of_rank(const fsdp_plan *p, int32_t i, int32_t j,
+                                   int64_t *row_begin, int64_t *local_rows) {
+    if (p == nullptr || row_begin == nullptr || local_rows == nullptr)
+        return fail(FSDP_E_INVAL, "fsdp_plan_rows_of_rank: null argument");
+    if (i < 0 || static_cast<size_t>(i) >= p->L.entries.size())
+        return fail(FSDP_E_INVAL, "fsdp_plan_rows_of_rank: parameter index out of range");
+    if (j < 0 || j >= p->L.world)
+        return fail(FSDP_E_INVAL, "fsdp_plan_rows_of_rank: rank out of range");
+    fsdp::rows_of_rank(p->L.entries[i].rows, p->L.world, j, row_begin, local_rows);
+    return FSDP_OK;
+}
+
+fsdp_status fsdp_state_bytes(double n_params, int32_t world, int32_t zero_stage,
+                             double *per_rank_bytes) {
+    if (per_rank_bytes == nullptr || world < 1 || !(n_params >= 0.0))
+        return fail(FSDP_E_INVAL, "fsdp_state_bytes: need n_params >= 0, world >= 1, non-null out");
+    if (zero_stage < 0 || zero_stage > 3)
+        return fail(FSDP_E_UNSUPPORTED, "fsdp_state_bytes: zero_stage must be 0..3");
+    double params = 2.0 * n_params, grads = 2.0 * n_params, optim = 12.0 * n_params;
+    if (zero_stage >= 1) optim /= world;
+    if (zero_stage >= 2) grads /= world;
+    if (zero_stage >= 3) params /= world;
+    *per_rank_bytes = params + grads + optim;
+    return FSDP_OK;
+}
+
+void fsdp_plan_destroy(fsdp_plan *p) {
+    if (p == nullptr) return;
+    if (p->dmem != nullptr) {
+        int cur = -1;
+        (void)hipGetDevice(&cur);
+        (void)hipSetDevice(p->device);
+        (void)hipDeviceSynchronize();
+        (void)hipFree(p->dmem);
+        if (cur >= 0) (void)hipSetDevice(cur);
+    }
+    delete p;
+}
+
+fsdp_status fsdp_bind(fsdp_plan *p, float *const *master, float *const *grad,
+                      float *const *exp_avg, float *const *exp_avg_sq,
+                      uint16_t *const *full, void *stream) {
+    if (p == nullptr) return fail(FSDP_E_INVAL, "fsdp_bind: null plan");
+    const size_t n = p->L.entries.size();
+    std::vector<fsdp::DevEntry> ents = p->host_entries;
+    int32_t roles = 0;
+    struct RoleArr {
+        float *const *arr;
+        int32_t bit;
+        const char *name;
+    } fr[4] = {{master, FSDP_ROLE_MASTER, "master"},
+               {grad, FSDP_ROLE_GRAD, "grad"},
+               {exp_avg, FSDP_ROLE_EXP_AVG, "exp_avg"},
+               {exp_avg_sq, FSDP_ROLE_EXP_AVG_SQ, "exp_avg_sq"}};
+    for (const RoleArr &r : fr) {
+        if (r.arr == nullptr) continue;
+        roles |= r.bit;
+        for (size_t i = 0; i < n; ++i) {
+            float *q = r.arr[i];
+            if (q == nullptr && p->L.entries[i].valid_numel > 0)
+                return fail(FSDP_E_INVAL, std::string("fsdp_bind: null ") + r.name +
+                                              " pointer for parameter " + std::to_string(i));
+            if (misaligned(q, 4))
+                return fail(FSDP_E_ALIGN, std::string("fsdp_bind: ") + r.name +
+                                              " pointer of parameter " + std::to_string(i) +
+                                              " is not 4-byte aligned");
+            float **slot = r.bit == FSDP_ROLE_MASTER   ? &ents[i].master
+                           : r.bit == FSDP_ROLE_GRAD    ? &ents[i].grad
+                           : r.bit == FSDP_ROLE_EXP_AVG ? &ents[i].exp_avg
+                                                        : &ents[i].exp_avg_sq;
+            *slot = q;
+        }
+    }
+    if (full != nullptr) {
+        roles |= FSDP_ROLE_FULL;
+        for (size_t i = 0; i < n; ++i) {
+            const fsdp_shard_entry_t &e = p->L.entries[i];
+            if (full[i] == nullptr && e.rows * e.cols > 0)
+                return fail(FSDP_E_INVAL, "fsdp_bind: null full pointer for parameter " +
+                                              std::to_string(i));
+            if (misaligned(full[i], 2))
+                return fail(FSDP_E_ALIGN, "fsdp_bind: full pointer of parameter " +
+                                              std::to_string(i) + " is not 2-byte aligned");
+            ents[i].full = full[i];
+        }
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "fsdp_bind: hipGetDevice");
+    if (p->dmem != nullptr && dev != p->device)
+        return fail(FSDP_E_STATE, "fsdp_bind: plan already bound on another device");
+    const size_t b_ent = round256(n * sizeof(fsdp::DevEntry));
+    const size_t b_pack = round256(p->L.pack.size() * sizeof(fsdp::PackTile));
+    const size_t b_unpack = round256(p->L.unpack.size() * sizeof(fsdp::UnpackTile));
+    const size_t b_reduce = round256(p->L.reduce.size() * sizeof(fsdp::ReduceTile));
+    const size_t b_adamw = round256(p->L.adamw.size() * sizeof(fsdp::EwTile));
+    const bool first = p->dmem == nullptr;
+    if (first) {
+        void *mem = nullptr;
+        const size_t total = b_ent + b_pack + b_unpack + b_reduce + b_adamw + 256;
+        e = hipMalloc(&mem, total);
+        if (e != hipSuccess) return fail(FSDP_E_NOMEM, "fsdp_bind: hipMalloc of device tables failed");
+        p->dmem = static_cast<char *>(mem);
+        p->device = dev;
+        char *c = p->dmem;
+        p->d_entries = reinterpret_cast<fsdp::DevEntry *>(c);
+        c += b_ent;
+        p->d_pack = reinterpret_cast<fsdp::PackTile *>(c);
+        c += b_pack;
+        p->d_unpack = reinterpret_cast<fsdp::UnpackTile *>(c);
+        c += b_unpack;
+        p->d_reduce = reinterpret_cast<fsdp::ReduceTile *>(c);
+        c += b_reduce;
+        p->d_adamw = reinterpret_cast<fsdp::EwTile *>(c);
+    }
+    // Kernels of this plan still queued on the stream may read the tables.
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "fsdp_bind: hipStreamSynchronize");
+    struct Up {
+        void *dst;
+        const void *src;
+        size_t bytes;
+    } ups[5] = {
+        {p->d_entries, ents.data(), n * sizeof(fsdp::DevEntry)},
+        {p->d_pack, p->L.pack.data(), p->L.pack.size() * sizeof(fsdp::PackTile)},
+        {p->d_unpack, p->L.unpack.data(), p->L.unpack.size() * sizeof(fsdp::UnpackTile)},
+        {p->d_reduce, p->L.reduce.data(), p->L.reduce.size() * sizeof(fsdp::ReduceTile)},
+        {p->d_adamw, p->L.adamw.data(), p->L.adamw.size() * sizeof(fsdp::EwTile)},
+    };
+    for (int k = 0; k < (first ? 5 : 1); ++k) {
+        if (ups[k].bytes == 0) continue;
+        e = hipMemcpyAsync(ups[k].dst, ups[k].src, ups[k].bytes, hipMemcpyHostToDevice, st);
+        if (e != hipSuccess) return hip_fail(e, "fsdp_bind: hipMemcpyAsync");
+    }
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "fsdp_bind: upload");
+    p->host_entries = std::move(ents);
+    p->bound = first ? roles : (p->bound | roles);
+    return FSDP_OK;
+}
+
+fsdp_status fsdp_pack_allgather(const fsdp_plan *p, uint16_t *ag_in, void *stream) {
+    fsdp_status s = need_roles(p, FSDP_ROLE_MASTER, "fsdp_pack_allgather");
+    if (s != FSDP_OK) return s;
+    if (ag_in == nullptr && p->L.S > 0) return fail(FSDP_E_INVAL, "fsdp_pack_allgather: null ag_in");
+    if (misaligned(ag_in, 2)) return fail(FSDP_E_ALIGN, "fsdp_pack_allgather: ag_in not 2-byte aligned");
+    if ((s = check_device(p)) != FSDP_OK) return s;
+    hipError_t e = fsdp::launch_pack(p->d_pack, static_cast<int64_t>(p->L.pack.size()),
+                                     p->d_entries, ag_in, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FSDP_OK : hip_fail(e, "fsdp_pack_allgather: launch");
+}
+
+fsdp_status fsdp_unpack_allgather(const fsdp_plan *p, const uint16_t *ag_out, void *stream) {
+    fsdp_status s = need_roles(p, FSDP_ROLE_FULL, "fsdp_unpack_allgather");
+    if (s != FSDP_OK) return s;
+    if (ag_out == nullptr && p->L.S > 0) return fail(FSDP_E_INVAL, "fsdp_unpack_allgather: null ag_out");
+    if (misaligned(ag_out, 2)) return fail(FSDP_E_ALIGN, "fsdp_unpack_allgather: ag_out not 2-byte aligned");
+    if ((s = check_device(p)) != FSDP_OK) return s;
+    hipError_t e = fsdp::launch_unpack(p->d_unpack, static_cast<int64_t>(p->L.unpack.size()),
+                                       p->d_entries, ag_out, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FSDP_OK : hip_fail(e, "fsdp_unpack_allgather: launch");
+}
+
+fsdp_status fsdp_reduce_shard(const fsdp_plan *p, const uint16_t *rs_in, void *stream) {
+    fsdp_status s = need_roles(p, FSDP_ROLE_GRAD, "fsdp_reduce_shard");
+    if (s != FSDP_OK) return s;
+    if (rs_in == nullptr && p->L.S > 0) return fail(FSDP_E_INVAL, "fsdp_reduce_shard: null rs_in");
+    if (misaligned(rs_in, 2)) return fail(FSDP_E_ALIGN, "fsdp_reduce_shard: rs_in not 2-byte aligned");
+    if ((s = check_device(p)) != FSDP_OK) return s;
+    hipError_t e = fsdp::launch_reduce(p->d_reduce, static_cast<int64_t>(p->L.reduce.size()),
+                                       p->d_entries, rs_in, p->L.S, p->L.world,
+                                       static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FSDP_OK : hip_fail(e, "fsdp_reduce_shard: launch");
+}
+
+fsdp_status fsdp_adamw_shard(const fsdp_plan *p, const fsdp_adamw_hparams_t *hp,
+                             int64_t step, void *stream) {
+    const int32_t roles = FSDP_ROLE_MASTER | FSDP_ROLE_GRAD | FSDP_ROLE_EXP_AVG | FSDP_ROLE_EXP_AVG_SQ;
+    fsdp_status s = need_roles(p, roles, "fsdp_adamw_shard");
+    if (s != FSDP_OK) return s;
+    if (hp == nullptr) return fail(FSDP_E_INVAL, "fsdp_adamw_shard: null hyperparameters");
+    if (step < 1) return fail(FSDP_E_INVAL, "fsdp_adamw_shard: step counts from 1");
+    if ((s = check_device(p)) != FSDP_OK) return s;
+    // fp64 on the hyperparameters, each scalar rounded once to fp32
+    const double bc1 = 1.0 - std::pow(hp->beta1, static_cast<double>(step));
+    const double bc2 = 1.0 - std::pow(hp->beta2, static_cast<double>(step));
+    const float scal[8] = {
+        static_cast<float>(hp->beta1),
+        static_cast<float>(1.0 - hp->beta1),
+        static_cast<float>(hp->beta2),
+        static_cast<float>(1.0 - hp->beta2),
+        static_cast<float>(hp->eps),
+        static_cast<float>(1.0 - hp->lr * hp->weight_decay),
+        static_cast<float>(hp->lr / bc1),
+        static_cast<float>(std::pow(bc2, 0.5)),
+    };
+    hipError_t e = fsdp::launch_adamw(p->d_adamw, static_cast<int64_t>(p->L.adamw.size()),
+                                      p->d_entries, scal, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FSDP_OK : hip_fail(e, "fsdp_adamw_shard: launch");
+}
+
+fsdp_status fsdp_check_stream(void *stream) {
+    hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "fsdp_check_stream: hipStreamSynchronize");
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "fsdp_check_stream");
+    return FSDP_OK;
+}
+
+}  // extern "C"

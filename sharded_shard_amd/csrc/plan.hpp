@@ -1,0 +1,104 @@
+// Internal structures of the shard-layout planner and the device work tables.
+//
+// Shard(0) layout ("Sharded Training: FSDP2, DTensor, Tensor and Pipeline
+// Parallelism", fully_shard paragraph): rank r keeps chunk r of
+// torch.chunk(param, N, dim=0), each rank's piece padded to c = ceil(rows/N)
+// rows; one group's pieces sit back to back in registration order and form
+// one communication segment of S elements per rank.
+//
+// The planner cuts every kernel's iteration space into tiles of at most
+// kTile* elements, so that workgroups get balanced work no matter how ragged
+// the parameter sizes are (1 element to tens of millions) and no kernel ever
+// searches for its parameter: a workgroup reads one 16- or 32-byte tile
+// record and one entry record.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/fsdp_shard.h"
+
+namespace fsdp {
+
+// Tile lengths in elements.  Multiples of 8 so every tile of a run starts at
+// the same offset modulo 16 bytes as the run itself.
+constexpr int64_t kTilePack = 16384;
+constexpr int64_t kTileUnpack = 32768;
+constexpr int64_t kTileReduce = 4096;
+constexpr int64_t kTileAdamw = 8192;
+
+// Device-side per-parameter record (64 bytes): the bound tensors.
+struct DevEntry {
+    float *master;
+    float *grad;
+    float *exp_avg;
+    float *exp_avg_sq;
+    uint16_t *full;
+    int64_t valid_numel;
+    int64_t rsv0;
+    int64_t rsv1;
+};
+static_assert(sizeof(DevEntry) == 64, "DevEntry layout");
+
+// copy-in: ag_in[dst .. dst+len) <- bf16(master[src .. src+valid)), then zeros.
+struct PackTile {
+    int64_t dst;
+    int64_t src;
+    int32_t entry;
+    int32_t len;
+    int32_t valid;
+    int32_t rsv;
+};
+static_assert(sizeof(PackTile) == 32, "PackTile layout");
+
+// copy-out: full[dst .. dst+len) <- ag_out[src .. src+len) (src counts rows*S).
+struct UnpackTile {
+    int64_t src;
+    int64_t dst;
+    int32_t entry;
+    int32_t len;
+    int64_t rsv;
+};
+static_assert(sizeof(UnpackTile) == 32, "UnpackTile layout");
+
+// reduce: grad[dst .. dst+len) <- mean over rows j of rs_in[j*S + src ...].
+struct ReduceTile {
+    int64_t src;
+    int64_t dst;
+    int32_t entry;
+    int32_t len;
+    int64_t rsv;
+};
+static_assert(sizeof(ReduceTile) == 32, "ReduceTile layout");
+
+// AdamW: elements [off .. off+len) of one parameter's shards.
+struct EwTile {
+    int64_t off;
+    int32_t entry;
+    int32_t len;
+};
+static_assert(sizeof(EwTile) == 16, "EwTile layout");
+
+struct Layout {
+    int32_t world = 0, rank = 0, align = 1;
+    std::vector<fsdp_shard_entry_t> entries;
+    int64_t S = 0, V = 0, F = 0;
+    int32_t n_empty = 0;
+    std::vector<PackTile> pack;
+    std::vector<UnpackTile> unpack;
+    std::vector<ReduceTile> reduce;
+    std::vector<EwTile> adamw;
+};
+
+// ceil(rows / world) and rank j's [row_begin, row_begin + local_rows).
+int64_t chunk_rows(int64_t rows, int32_t world);
+void rows_of_rank(int64_t rows, int32_t world, int32_t j, int64_t *begin,
+                  int64_t *local);
+
+// Builds entries and tiles.  Returns FSDP_OK or an error with `err` set.
+fsdp_status build_layout(const int64_t *rows, const int64_t *cols, int32_t n,
+                         int32_t world, int32_t rank, int32_t align, Layout *out,
+                         std::string *err);
+
+}  // namespace fsdp

@@ -1,0 +1,186 @@
+"""Host-side checks of the C ABI library (no GPU needed).
+
+* the shared library loads and exports every function include/fsdp_shard.h
+  declares;
+* the C++ planner agrees with the oracle's layout bit for bit on every
+  workload, every rank and both alignments;
+* argument errors are reported with the documented codes before any HIP call.
+"""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from conftest import ROOT
+from oracle import fsdp as O
+from workloads import configs
+
+capi = pytest.importorskip("sharded_shard_amd.capi")
+
+HEADER = os.path.join(ROOT, "include", "fsdp_shard.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fsdp_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for want in ("fsdp_plan_create", "fsdp_pack_allgather", "fsdp_unpack_allgather",
+                 "fsdp_reduce_shard", "fsdp_adamw_shard", "fsdp_bind", "fsdp_state_bytes"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", capi.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fsdp_\w+)", out))
+    missing = [n for n in header_functions() if n not in exported]
+    assert not missing, missing
+    for n in header_functions():
+        assert hasattr(capi.lib, n)
+        assert n in capi.EXPORTS
+
+
+def test_abi_version_and_status_strings():
+    assert capi.fsdp_abi_version() == 1
+    for s in (0, -1, -2, -3, -4, -5, -6, 7):
+        assert capi.fsdp_status_string(s)
+
+
+def _check_plan(shapes, world, rank, align):
+    rows = [s[0] for s in shapes]
+    cols = [int(np.prod(s[1:])) if len(s) > 1 else 1 for s in shapes]
+    ref = O.plan(shapes, world, rank, align)
+    p = capi.fsdp_plan_create(rows, cols, world, rank, align)
+    try:
+        info = capi.fsdp_plan_info(p)
+        assert (info.S, info.V, info.F) == (ref.S, ref.V, ref.F)
+        assert info.n_params == len(shapes) and info.pad_total == ref.S - ref.V
+        assert info.n_empty == sum(1 for e in ref.entries if e.local_rows == 0)
+        for i, e in enumerate(ref.entries):
+            g = capi.fsdp_plan_entry(p, i)
+            for f in ("rows", "cols", "chunk_rows", "row_begin", "local_rows", "shard_offset",
+                      "shard_numel", "valid_numel", "pad_numel", "seg_numel"):
+                assert getattr(g, f) == getattr(e, f), (f, i, rank)
+        for i, s in enumerate(shapes):
+            for j in range(world):
+                assert capi.fsdp_plan_rows_of_rank(p, i, j) == O.rows_of_rank(s[0], world, j)
+        return info
+    finally:
+        capi.fsdp_plan_destroy(p)
+
+
+@pytest.mark.parametrize("align", [1, 8])
+@pytest.mark.parametrize("cfg", configs.ALL)
+def test_planner_matches_oracle_on_every_workload(cfg, align):
+    c = configs.get(cfg)
+    seen = set()
+    for g in c.groups:
+        shapes = tuple(p.shape for p in g.params)
+        if shapes in seen:      # the repeated decoder blocks share one layout
+            continue
+        seen.add(shapes)
+        ranks = range(c.world) if c.world <= 8 else (0, 1, 31, 62, 63)
+        for r in ranks:
+            _check_plan(list(shapes), c.world, r, align)
+
+
+@pytest.mark.parametrize("align", [1, 8])
+def test_planner_matches_oracle_random_ragged(align):
+    rng = np.random.default_rng(17)
+    for _ in range(40):
+        n = int(rng.integers(1, 70))
+        shapes = []
+        for _ in range(int(rng.integers(1, 12))):
+            if rng.random() < 0.3:
+                shapes.append((int(rng.integers(0, 200)),))
+            else:
+                shapes.append((int(rng.integers(0, 200)), int(rng.integers(1, 50)), 2))
+        for r in {0, n - 1, int(rng.integers(0, n))}:
+            _check_plan(shapes, n, r, align)
+
+
+def test_tiles_cover_the_work_exactly():
+    """Tile counts: every run split into pieces of at most the tile length."""
+    c = configs.get(3)
+    shapes = [p.shape for p in c.groups[0].params]
+    info = _check_plan(shapes, 6, 5, 1)
+    ref = O.plan(shapes, 6, 5)
+    cdiv = lambda a, b: -(-a // b)
+    want_pack = sum(cdiv(e.seg_numel, 16384) for e in ref.entries)
+    want_unpack = sum(cdiv(O.rows_of_rank(e.rows, 6, j)[1] * e.cols, 32768)
+                      for e in ref.entries for j in range(6))
+    want_reduce = sum(cdiv(e.valid_numel, 4096) for e in ref.entries)
+    want_adamw = sum(cdiv(e.valid_numel, 8192) for e in ref.entries)
+    assert list(info.n_tiles) == [want_pack, want_unpack, want_reduce, want_adamw]
+
+
+def test_state_bytes_matches_pages_and_oracle():
+    assert capi.fsdp_state_bytes(7e9, 1, 0) == 112e9
+    assert capi.fsdp_state_bytes(70e9, 1, 0) == 1120e9
+    for n in (1, 8, 64):
+        for s in range(4):
+            assert capi.fsdp_state_bytes(7e9, n, s) == O.state_bytes(7e9, n, s)
+    with pytest.raises(capi.FsdpError) as ei:
+        capi.fsdp_state_bytes(7e9, 8, 4)
+    assert ei.value.status == capi.FSDP_E_UNSUPPORTED
+    with pytest.raises(capi.FsdpError) as ei:
+        capi.fsdp_state_bytes(7e9, 0, 1)
+    assert ei.value.status == capi.FSDP_E_INVAL
+
+
+@pytest.mark.parametrize("args,code", [
+    (([4], [1], 0, 0, 1), capi.FSDP_E_INVAL),       # world 0
+    (([4], [1], 2, 2, 1), capi.FSDP_E_INVAL),       # rank out of range
+    (([4], [1], 2, -1, 1), capi.FSDP_E_INVAL),
+    (([-1], [1], 2, 0, 1), capi.FSDP_E_INVAL),      # negative rows
+    (([4], [0], 2, 0, 1), capi.FSDP_E_INVAL),       # cols < 1
+    (([4], [1], 2, 0, 4), capi.FSDP_E_UNSUPPORTED),  # align
+    (([1 << 62], [1 << 10], 2, 0, 1), capi.FSDP_E_INVAL),  # overflow
+])
+def test_plan_create_errors(args, code):
+    with pytest.raises(capi.FsdpError) as ei:
+        capi.fsdp_plan_create(*args)
+    assert ei.value.status == code
+    assert capi.fsdp_last_error()
+
+
+def test_empty_group_and_rows_zero_are_legal():
+    info = _check_plan([(0, 5), (0,)], 4, 3, 1)
+    assert info.S == 0 and info.V == 0
+    info = _check_plan([], 2, 0, 1)
+    assert info.S == 0 and info.n_params == 0
+
+
+def test_hot_calls_reject_unbound_and_bad_arguments_without_gpu():
+    p = capi.fsdp_plan_create([4, 3], [2, 1], 2, 0, 1)
+    try:
+        for call in (lambda: capi.fsdp_pack_allgather(p, 0x1000, 0),
+                     lambda: capi.fsdp_unpack_allgather(p, 0x1000, 0),
+                     lambda: capi.fsdp_reduce_shard(p, 0x1000, 0),
+                     lambda: capi.fsdp_adamw_shard(p, 3e-4, 0.9, 0.999, 1e-8, 0.01, 1, 0)):
+            with pytest.raises(capi.FsdpError) as ei:
+                call()
+            assert ei.value.status == capi.FSDP_E_STATE
+        # bind validation happens before any device call
+        with pytest.raises(capi.FsdpError) as ei:
+            capi.fsdp_bind(p, master=[0, 0x1000], stream=0)
+        assert ei.value.status == capi.FSDP_E_INVAL
+        with pytest.raises(capi.FsdpError) as ei:
+            capi.fsdp_bind(p, master=[0x1002, 0x1000], stream=0)
+        assert ei.value.status == capi.FSDP_E_ALIGN
+        with pytest.raises(capi.FsdpError) as ei:
+            capi.fsdp_bind(p, full=[0x1001, 0x1000], stream=0)
+        assert ei.value.status == capi.FSDP_E_ALIGN
+        for fn in (capi.fsdp_pack_allgather, capi.fsdp_unpack_allgather, capi.fsdp_reduce_shard):
+            with pytest.raises(capi.FsdpError) as ei:
+                fn(None, 0x1000, 0)
+            assert ei.value.status == capi.FSDP_E_INVAL
+    finally:
+        capi.fsdp_plan_destroy(p)
+    capi.fsdp_plan_destroy(None)

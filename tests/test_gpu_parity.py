@@ -1,0 +1,432 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: layout, pack and unpack bit-exact; casts within 1 bf16 ulp (bit-exact
+expected); fp32 reductions and AdamW's master, m and v after 3 steps within a
+normwise relative error of 1e-6 (bit-exact expected: both sides round every
+fp32 operation once in the same order; the count of differing elements is
+reported and must be 0).
+
+Inputs are seeded synthetic draws (workloads.synth) and never come from the
+HIP path.  Small and medium cases are compared whole; full-size groups of the
+7B- and 70B-shaped workloads run in the same launch configuration the bench
+times and are checked on sampled outputs and by exact properties that hold at
+any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import fsdp as O
+from workloads import configs, synth
+
+pytestmark = pytest.mark.gpu
+
+capi = pytest.importorskip("sharded_shard_amd.capi")
+from sharded_shard_amd.group import ShardedGroup  # noqa: E402
+
+DEV = "cuda"
+HP = dict(lr=3e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+GUARD = 4096
+GUARD_VAL = 0x5A5A
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.synchronize()
+    yield
+    torch.cuda.synchronize()
+
+
+def u16(t):
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def f32(t):
+    return t.detach().cpu().contiguous().numpy()
+
+
+def normwise(a, b):
+    den = max(float(np.abs(b).max()) if b.size else 0.0, 1e-30)
+    return float(np.abs(a.astype(np.float64) - b.astype(np.float64)).max()) / den if a.size else 0.0
+
+
+def guarded_i16(n, fill=GUARD_VAL):
+    """int16 device buffer with GUARD elements of guard value on each side."""
+    buf = torch.full((n + 2 * GUARD,), fill - 65536 if fill > 32767 else fill,
+                     dtype=torch.int16, device=DEV)
+    return buf, buf[GUARD:GUARD + n]
+
+
+def assert_guards(buf, n, fill=GUARD_VAL):
+    h = u16(buf)
+    assert (h[:GUARD] == fill).all() and (h[GUARD + n:] == fill).all(), "write outside the buffer"
+
+
+def shapes_cols(shapes):
+    return [int(np.prod(s[1:])) if len(s) > 1 else 1 for s in shapes]
+
+
+CASES = [
+    ("mlp-probe", [(32, 16), (32,), (4, 32), (4,)], 2),
+    ("ragged-n6", [(1000, 70), (333,), (77, 129), (1, 2048), (1,), (64, 2048)], 6),
+    ("empty-rows", [(5, 3), (0, 4), (7,), (1, 5), (13, 2)], 4),
+    ("more-ranks", [(6, 3), (17,)], 8),
+    ("n1", [(9, 7), (4097,)], 1),
+    ("tiles", [(300, 1000), (4096, 33), (70001,)], 8),
+]
+
+
+def _case_ids():
+    return [c[0] for c in CASES]
+
+
+def _fill_masters(g, key):
+    for i, e in enumerate(g.entries):
+        if e.valid_numel:
+            g.shard_view(g.master_flat, i).copy_(synth.normal_f32(e.valid_numel, 0.02, key + (i,)))
+
+
+# ---------------------------------------------------------------------------
+# copy-in
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("align", [1, 8])
+@pytest.mark.parametrize("case", range(len(CASES)), ids=_case_ids())
+def test_pack_bit_exact(case, align):
+    name, shapes, n = CASES[case]
+    for r in range(n):
+        g = ShardedGroup(shapes, n, r, align)
+        _fill_masters(g, ("pack", name, r))
+        buf, ag = guarded_i16(n * g.S)
+        row = ag[r * g.S:(r + 1) * g.S]
+        g.pack(row)
+        torch.cuda.synchronize()
+        ref = O.pack(O.plan(shapes, n, r, align),
+                     [f32(g.shard_view(g.master_flat, i)) for i in range(len(shapes))])
+        got = u16(ag).reshape(n, g.S) if g.S else np.zeros((n, 0), np.uint16)
+        assert np.array_equal(got[r], ref)
+        others = np.delete(got, r, axis=0)
+        assert (others == GUARD_VAL).all(), "pack wrote outside its row"
+        assert_guards(buf, n * g.S)
+        g.close()
+
+
+def test_pack_special_values_and_misaligned_sources():
+    """NaN, infinities, ties, subnormals; shards at every 4-byte offset mod 16."""
+    specials = np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0x7FA00000, 0x7F800000, 0xFF800000,
+                         0x7F7FFFFF, 0xFF7FFFFF, 0x7F7F7FFF, 0x3F808000, 0x3F818000, 0xBF818000,
+                         0x00000001, 0x00008000, 0x00018000, 0x007FFFFF, 0x80000000, 0x00000000],
+                        dtype=np.uint32).view(np.float32)
+    rng = np.random.default_rng(0)
+    shapes = [(97, 13), (1031,), (5, 8)]
+    n, r = 3, 1
+    plan = O.plan(shapes, n, r)
+    for shift in range(4):
+        g = ShardedGroup(shapes, n, r, bind=False)
+        g.allocate()
+        masters = []
+        views = []
+        base = torch.zeros(sum(e.valid_numel + 8 for e in g.entries) + 64, dtype=torch.float32, device=DEV)
+        o = shift
+        for e in g.entries:
+            vals = rng.standard_normal(e.valid_numel).astype(np.float32) * 0.02
+            k = min(len(specials), e.valid_numel)
+            vals[:k] = specials[:k]
+            vals[-k:] = specials[:k][::-1]
+            v = base[o:o + e.valid_numel]
+            v.copy_(torch.from_numpy(vals))
+            masters.append(vals)
+            views.append(v)
+            o += e.valid_numel + 1   # consecutive shards at different alignments
+        capi.fsdp_bind(g.plan, master=[v.data_ptr() for v in views], stream=None)
+        for off in (0, 1, 3):      # ag_in at 2-byte offsets 0, 2, 6 mod 16
+            buf = torch.zeros(g.S + 16, dtype=torch.int16, device=DEV)
+            g.pack(buf[off:off + g.S])
+            torch.cuda.synchronize()
+            assert np.array_equal(u16(buf)[off:off + g.S], O.pack(plan, masters))
+        g.close()
+
+
+# ---------------------------------------------------------------------------
+# copy-out
+# ---------------------------------------------------------------------------
+
+def _rand_ag(n, S, key, sentinel_mask=None):
+    ag = np.empty((n, S), dtype=np.uint16)
+    rng = np.random.default_rng(synth.seed_for(*key) % (2**32))
+    ag[:] = rng.integers(0, 2**16, size=(n, S), dtype=np.uint16)
+    if sentinel_mask is not None:
+        ag[:, sentinel_mask] = synth.SENTINEL_BF16
+    return ag
+
+
+def _pad_mask(plan):
+    m = np.ones(plan.S, dtype=bool)
+    for e in plan.entries:
+        m[e.shard_offset:e.shard_offset + e.valid_numel] = False
+    return m
+
+
+@pytest.mark.parametrize("align", [1, 8])
+@pytest.mark.parametrize("case", range(len(CASES)), ids=_case_ids())
+def test_unpack_bit_exact_with_guards(case, align):
+    name, shapes, n = CASES[case]
+    for r in sorted({0, n - 1}):
+        plan = O.plan(shapes, n, r, align)
+        # padding of every row holds the sentinel (any rank's padding: rank 0's
+        # pieces are the longest, so mark what rank j leaves unused per row)
+        ag = _rand_ag(n, plan.S, ("unpack", name, r, align))
+        for j in range(n):
+            ag[j, _pad_mask(O.plan(shapes, n, j, align))] = synth.SENTINEL_BF16
+        g = ShardedGroup(shapes, n, r, align, bind=False)
+        g.allocate(full=False)
+        fbuf, full = guarded_i16(g.full_space)
+        full.fill_(0x1234)
+        g.full_flat = full
+        g.bind()
+        for off in (0, 3):   # ag_out 16-byte aligned, then at a 6-byte offset
+            src = torch.zeros(n * plan.S + 8, dtype=torch.int16, device=DEV)
+            src[off:off + n * plan.S].copy_(torch.from_numpy(ag.reshape(-1).view(np.int16)))
+            g.unpack(src[off:off + n * plan.S])
+            torch.cuda.synchronize()
+            ref = O.unpack(plan, ag)
+            for i, want in enumerate(ref):
+                assert np.array_equal(u16(g.full_view(i)), want), (name, r, i, off)
+            # the gaps between full views keep their fill
+            h = u16(full)
+            mask = np.ones(g.full_space, dtype=bool)
+            for i in range(len(shapes)):
+                o = g.full_offsets[i]
+                mask[o:o + g.rows[i] * g.cols[i]] = False
+            assert (h[mask] == 0x1234).all()
+            assert_guards(fbuf, g.full_space)
+        g.close()
+
+
+def test_unpack_misaligned_full_destinations():
+    """Full tensors at every 2-byte offset modulo 16."""
+    shapes, n = [(37, 11), (999,), (8, 64)], 5
+    plan = O.plan(shapes, n, 2)
+    ag = _rand_ag(n, plan.S, ("mis",))
+    src = torch.from_numpy(ag.reshape(-1).view(np.int16)).to(DEV)
+    ref = O.unpack(plan, ag)
+    for shift in range(8):
+        g = ShardedGroup(shapes, n, 2, bind=False)
+        arena = torch.zeros(sum(r * c + 9 for r, c in zip(g.rows, g.cols)) + 16,
+                            dtype=torch.int16, device=DEV)
+        views, o = [], shift
+        for r_, c_ in zip(g.rows, g.cols):
+            views.append(arena[o:o + r_ * c_])
+            o += r_ * c_ + 1
+        capi.fsdp_bind(g.plan, full=[v.data_ptr() for v in views], stream=None)
+        g.unpack(src)
+        torch.cuda.synchronize()
+        for v, want in zip(views, ref):
+            assert np.array_equal(u16(v), want.reshape(-1)), shift
+        g.close()
+
+
+# ---------------------------------------------------------------------------
+# reduce
+# ---------------------------------------------------------------------------
+
+def _rs_input(plan, n, key):
+    rs = np.empty((n, plan.S), dtype=np.uint16)
+    for j in range(n):
+        rs[j] = synth.bf16_bits_to_u16(synth.normal_bf16_bits(plan.S, 1e-3, key + (j,)))
+    rs[:, _pad_mask(plan)] = synth.SENTINEL_BF16
+    return rs
+
+
+def _cmp_f32(got, want, what):
+    assert got.shape == want.shape
+    if not got.size:
+        return
+    assert normwise(got, want) <= 1e-6, what
+    nbad = int((got.view(np.uint32) != want.view(np.uint32)).sum())
+    assert nbad == 0, f"{what}: {nbad} elements differ in bits (within tolerance)"
+
+
+@pytest.mark.parametrize("case", range(len(CASES)), ids=_case_ids())
+def test_reduce_matches_oracle(case):
+    name, shapes, n = CASES[case]
+    for r in sorted({0, n - 1, n // 2}):
+        plan = O.plan(shapes, n, r)
+        rs = _rs_input(plan, n, ("reduce", name, r))
+        g = ShardedGroup(shapes, n, r)
+        for off in (0, 1):
+            src = torch.zeros(n * plan.S + 8, dtype=torch.int16, device=DEV)
+            src[off:off + n * plan.S].copy_(torch.from_numpy(rs.reshape(-1).view(np.int16)))
+            g.grad_flat.fill_(float("nan"))
+            g.reduce(src[off:off + n * plan.S])
+            torch.cuda.synchronize()
+            for i, want in enumerate(O.reduce(plan, rs)):
+                _cmp_f32(f32(g.shard_view(g.grad_flat, i)), want, (name, r, i, off))
+        g.close()
+
+
+@pytest.mark.parametrize("n", [1, 2, 6, 8, 64])
+def test_reduce_all_equal_is_exact_and_odd_segments(n):
+    shapes = [(3 * n + 1, 5), (2 * n + 1,), (n * 40 + 3, 67)]
+    plan = O.plan(shapes, n, 0)
+    row = synth.bf16_bits_to_u16(synth.normal_bf16_bits(plan.S, 1e-3, ("eq", n)))
+    rs = np.tile(row, (n, 1))
+    g = ShardedGroup(shapes, n, 0)
+    g.reduce(torch.from_numpy(rs.reshape(-1).view(np.int16)).to(DEV))
+    torch.cuda.synchronize()
+    for i, e in enumerate(plan.entries):
+        want = O.bf16_to_f32(row[e.shard_offset:e.shard_offset + e.valid_numel])
+        got = f32(g.shard_view(g.grad_flat, i))
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    g.close()
+
+
+# ---------------------------------------------------------------------------
+# AdamW
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", range(len(CASES)), ids=_case_ids())
+def test_adamw_three_steps_matches_oracle(case):
+    name, shapes, n = CASES[case]
+    r = n - 1
+    g = ShardedGroup(shapes, n, r)
+    _fill_masters(g, ("adamw", name))
+    host = [[f32(g.shard_view(fl, i)) for i in range(len(shapes))]
+            for fl in (g.master_flat, g.m_flat, g.v_flat)]
+    for t in (1, 2, 3):
+        for i, e in enumerate(g.entries):
+            if e.valid_numel:
+                gr = synth.normal_f32(e.valid_numel, 1e-3, ("adamw-g", name, t, i))
+                g.shard_view(g.grad_flat, i).copy_(gr)
+                O.adamw(host[0][i], gr.numpy(), host[1][i], host[2][i], t, **HP)
+        g.adamw(t, **HP)
+    torch.cuda.synchronize()
+    for k, fl in enumerate((g.master_flat, g.m_flat, g.v_flat)):
+        for i in range(len(shapes)):
+            _cmp_f32(f32(g.shard_view(fl, i)), host[k][i], (name, k, i))
+    g.close()
+
+
+def test_adamw_misaligned_and_mixed_alignment_shards():
+    """Shards whose four pointers share an offset mod 16, and ones that do not."""
+    n_el = [1, 3, 4, 5, 8191, 8193, 20000]
+    for mixed in (False, True):
+        shapes = [(k,) for k in n_el]
+        g = ShardedGroup(shapes, 1, 0, bind=False)
+        bufs = [torch.zeros(sum(n_el) + 4 * len(n_el) + 16, dtype=torch.float32, device=DEV)
+                for _ in range(4)]
+        views = [[], [], [], []]
+        for role in range(4):
+            o = 1 + (role if mixed else 0)
+            for k in n_el:
+                views[role].append(bufs[role][o:o + k])
+                o += k + 3
+        host = [[], [], [], []]
+        for i, k in enumerate(n_el):
+            p0 = synth.normal_f32(k, 0.02, ("am", i))
+            views[0][i].copy_(p0)
+            host[0].append(p0.numpy().copy())
+            host[2].append(np.zeros(k, np.float32))
+            host[3].append(np.zeros(k, np.float32))
+        capi.fsdp_bind(g.plan, *[[v.data_ptr() for v in views[role]] for role in range(4)], None)
+        for t in (1, 2, 3):
+            for i, k in enumerate(n_el):
+                gr = synth.normal_f32(k, 1e-3, ("am-g", t, i))
+                views[1][i].copy_(gr)
+                O.adamw(host[0][i], gr.numpy(), host[2][i], host[3][i], t, **HP)
+            g.adamw(t, **HP)
+            torch.cuda.synchronize()
+        for role in (0, 2, 3):
+            for i in range(len(n_el)):
+                _cmp_f32(f32(views[role][i]), host[role][i], (mixed, role, i))
+        g.close()
+
+
+# ---------------------------------------------------------------------------
+# whole step on the MLP probe and the ragged MoE workload, every element
+# ---------------------------------------------------------------------------
+
+def _whole_step(cfg_index, ranks, steps=3, align=1):
+    cfg = configs.get(cfg_index)
+    n = cfg.world
+    hp = vars(cfg.hp)
+    for gi, grp in enumerate(cfg.groups):
+        shapes = [p.shape for p in grp.params]
+        for r in ranks:
+            plan = O.plan(shapes, n, r, align)
+            g = ShardedGroup(shapes, n, r, align)
+            _fill_masters(g, ("step", cfg_index, gi, r))
+            masters = [f32(g.shard_view(g.master_flat, i)) for i in range(len(shapes))]
+            ms = [np.zeros_like(x) for x in masters]
+            vs = [np.zeros_like(x) for x in masters]
+            ag = torch.empty(n * plan.S, dtype=torch.int16, device=DEV)
+            for t in range(1, steps + 1):
+                rs = _rs_input(plan, n, ("step-rs", cfg_index, gi, r, t))
+                g.reduce(torch.from_numpy(rs.reshape(-1).view(np.int16)).to(DEV))
+                g.adamw(t, **hp)
+                # other ranks' rows are synthetic; this rank packs its own row in place
+                other = _rand_ag(n, plan.S, ("step-ag", cfg_index, gi, r, t))
+                ag.copy_(torch.from_numpy(other.reshape(-1).view(np.int16)))
+                g.pack(ag[r * plan.S:(r + 1) * plan.S])
+                g.unpack(ag)
+                torch.cuda.synchronize()
+                grads = O.reduce(plan, rs)
+                for x, gr, m, v in zip(masters, grads, ms, vs):
+                    O.adamw(x, gr, m, v, t, **hp)
+                other[r] = O.pack(plan, masters)
+                for i, want in enumerate(grads):
+                    _cmp_f32(f32(g.shard_view(g.grad_flat, i)), want, ("grad", gi, r, t, i))
+                assert np.array_equal(u16(ag).reshape(n, plan.S)[r], other[r])
+                for i, want in enumerate(O.unpack(plan, other)):
+                    assert np.array_equal(u16(g.full_view(i)), want), ("full", gi, r, t, i)
+            for fl, host in ((g.master_flat, masters), (g.m_flat, ms), (g.v_flat, vs)):
+                for i in range(len(shapes)):
+                    _cmp_f32(f32(g.shard_view(fl, i)), host[i], ("state", gi, r, i))
+            g.close()
+            del ag
+            torch.cuda.empty_cache()
+
+
+def test_whole_step_mlp_probe_all_ranks():
+    _whole_step(0, ranks=(0, 1))
+
+
+@pytest.mark.parametrize("rank", [5, 0])
+def test_whole_step_moe_ragged(rank):
+    _whole_step(3, ranks=(rank,), steps=1)
+
+
+def test_whole_step_llama_block_rank0():
+    _whole_step(1, ranks=(0,), steps=1)
+
+
+def test_determinism_two_runs_identical():
+    shapes, n = [(1000, 70), (333,), (77, 129)], 6
+    outs = []
+    for _ in range(2):
+        g = ShardedGroup(shapes, n, 4)
+        _fill_masters(g, ("det",))
+        plan = O.plan(shapes, n, 4)
+        rs = torch.from_numpy(_rs_input(plan, n, ("det-rs",)).reshape(-1).view(np.int16)).to(DEV)
+        g.reduce(rs)
+        g.adamw(1, **HP)
+        ag = torch.zeros(n * plan.S, dtype=torch.int16, device=DEV)
+        g.pack(ag[4 * plan.S:5 * plan.S])
+        g.unpack(ag)
+        torch.cuda.synchronize()
+        outs.append([u16(ag), f32(g.master_flat), f32(g.grad_flat), u16(g.full_flat)])
+        g.close()
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_empty_group_calls_are_no_ops():
+    g = ShardedGroup([(0, 4), (0,)], 4, 1)
+    g.reduce(torch.zeros(1, dtype=torch.int16, device=DEV))
+    g.adamw(1, **HP)
+    g.pack(torch.zeros(1, dtype=torch.int16, device=DEV))
+    g.unpack(torch.zeros(1, dtype=torch.int16, device=DEV))
+    capi.fsdp_check_stream()
+    g.close()
