@@ -12,9 +12,13 @@ before the timed region starts.
 
 Prints one JSON line: params/s of this rank's shard (value), effective HBM
 GB/s (algorithmic bytes / time) and its fraction of the 8 TB/s HBM peak, the
-roofline of the dominant kernel (copy-out) measured with HIP events around its
-launches inside the timed region, and the CPU oracle timed on a bounded sample
-of the same workload.
+roofline of the dominant kernel (the one with the most algorithmic bytes)
+measured with HIP events around its launches inside the timed region, and the
+CPU oracle timed on a bounded sample of the same workload.
+
+By default reduce, AdamW and pack run as one fused launch per group
+(fsdp_step_shard, bit-identical to the three calls); --unfused runs them as
+three launches.
 """
 from __future__ import annotations
 
@@ -32,15 +36,23 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "sharded-step params/sec per GPU + effective HBM GB/s (% of MI355X peak)"
 
 
-def algorithmic_bytes(S, V, F, N):
-    """Bytes each kernel must move once per group (see the design notes).
+def algorithmic_bytes(S, V, F, N, fused):
+    """Bytes each kernel must move once per group.
 
-    pack: read 4V fp32, write 2S bf16; unpack: read 2F + write 2F;
-    reduce: read 2NV bf16 + write 4V fp32; AdamW: read p, g, m, v (16V) +
-    write p, m, v (12V).
+    reduce: read N bf16 contributions (2NV) + write the fp32 grad (4V);
+    adamw: read p, g, m, v (16V) + write p, m, v (12V); pack: read 4V fp32 +
+    write 2S bf16; unpack: read 2F + write 2F.  The fused step reads 2NV + 12V
+    and writes 12V + 2S: the gradient never goes to HBM.
     """
+    if fused:
+        return {"step": 2 * N * V + 24 * V + 2 * S, "unpack": 4 * F}
     return {"reduce": 2 * N * V + 4 * V, "adamw": 28 * V, "pack": 4 * V + 2 * S,
             "unpack": 4 * F}
+
+
+KERNEL_NAMES = {"step": "step_kernel (fused reduce+adamw+pack)", "reduce": "reduce_kernel",
+                "adamw": "adamw_kernel", "pack": "pack_kernel (copy-in)",
+                "unpack": "unpack_kernel (copy-out)"}
 
 
 def parse():
@@ -51,14 +63,42 @@ def parse():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
     ap.add_argument("--rank", type=int, default=None, help="simulated rank (default: the config's)")
     ap.add_argument("--align", type=int, default=1, choices=[1, 8])
+    ap.add_argument("--unfused", action="store_true",
+                    help="run reduce, adamw and pack as three launches instead of the fused step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown-steps", type=int, default=3,
                     help="extra untimed steps with events around every kernel")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain device-to-device copy of 2 GiB instead (the "
+                         "reference for HBM byte counters and the copy ceiling)")
     return ap.parse_args()
 
 
-def cpu_baseline(cfg, rank, budget_s=30.0):
-    """Time the CPU oracle on one block group plus the root group, one step."""
+def copy_calibration(reps=10):
+    """torch's own copy kernel on 2 GiB: known bytes read and written per launch."""
+    import torch
+    n = 1 << 29
+    src = torch.ones(n, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    nbytes = 4 * n
+    return {"copy_calibration": {"bytes_read_per_launch": nbytes, "bytes_written_per_launch": nbytes,
+                                 "avg_launch_ms": ms, "GBps": 2 * nbytes / (ms * 1e-3) / 1e9,
+                                 "hbm_frac": 2 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}}
+
+
+def cpu_baseline(cfg, rank, min_s=10.0, max_s=30.0):
+    """Time the CPU oracle on whole groups (first block, root, more blocks) for
+    one step each, until at least min_s of oracle time has accumulated."""
     import numpy as np
     import torch
 
@@ -67,7 +107,9 @@ def cpu_baseline(cfg, rank, budget_s=30.0):
 
     n = cfg.world
     hp = vars(cfg.hp)
-    sample = [cfg.groups[0]] + ([cfg.groups[-1]] if len(cfg.groups) > 1 else [])
+    order = [0] + ([len(cfg.groups) - 1] if len(cfg.groups) > 1 else []) + \
+        list(range(1, len(cfg.groups) - 1))
+    sample = [cfg.groups[i] for i in order]
     total_t, total_v = 0.0, 0
     names = []
     for gi, grp in enumerate(sample):
@@ -92,7 +134,7 @@ def cpu_baseline(cfg, rank, budget_s=30.0):
         total_v += plan.V
         names.append(grp.name)
         del rs, ag, grads
-        if total_t > budget_s:
+        if total_t >= min_s or total_t + total_t / len(names) > max_s:
             break
     return {
         "value": total_v / total_t,
@@ -112,6 +154,10 @@ def main():
                           "ranks are out of scope, so --gpus must be 1"}))
         sys.exit(2)
     import torch
+
+    if args.copy_calibration:
+        print(json.dumps(copy_calibration()), flush=True)
+        return
 
     from sharded_shard_amd.group import ShardedGroup
     from workloads import configs, synth
@@ -146,86 +192,83 @@ def main():
     print("bench: state resident", file=sys.stderr, flush=True)
 
     V = sum(g.V for g in groups)
-    byts = {k: 0 for k in ("reduce", "adamw", "pack", "unpack")}
+    fused = not args.unfused
+    kinds = ["step", "unpack"] if fused else ["reduce", "adamw", "pack", "unpack"]
+    byts = {k: 0 for k in kinds}
     for g in groups:
-        for k, b in algorithmic_bytes(g.S, g.V, g.F, n).items():
+        for k, b in algorithmic_bytes(g.S, g.V, g.F, n, fused).items():
             byts[k] += b
     step_bytes = sum(byts.values())
+    dominant = max(kinds, key=lambda k: byts[k])
 
     stream = torch.cuda.current_stream()
     step_counter = [0]
 
-    def step(events=None, all_events=None):
+    def calls(gi, g, t):
+        rs = rs_arena[gi & 1][:n * g.S]
+        ag = ag_arena[gi & 1][:n * g.S]
+        row = ag[rank * g.S:(rank + 1) * g.S]
+        if fused:
+            return [("step", lambda: g.step(rs, row, t, stream=stream, **hp)),
+                    ("unpack", lambda: g.unpack(ag, stream))]
+        return [("reduce", lambda: g.reduce(rs, stream)),
+                ("adamw", lambda: g.adamw(t, stream=stream, **hp)),
+                ("pack", lambda: g.pack(row, stream)),
+                ("unpack", lambda: g.unpack(ag, stream))]
+
+    def step(timed=None, every=None):
+        """One sharded step; events around `timed` kernels or around every kernel."""
         step_counter[0] += 1
         t = step_counter[0]
         for gi, g in enumerate(groups):
-            rs = rs_arena[gi & 1][:n * g.S]
-            ag = ag_arena[gi & 1][:n * g.S]
-            if all_events is not None:
-                e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-                e[0].record(stream)
-                g.reduce(rs, stream)
-                e[1].record(stream)
-                g.adamw(t, stream=stream, **hp)
-                e[2].record(stream)
-                g.pack(ag[rank * g.S:(rank + 1) * g.S], stream)
-                e[3].record(stream)
-                g.unpack(ag, stream)
-                e[4].record(stream)
-                all_events.append(e)
-                continue
-            g.reduce(rs, stream)
-            g.adamw(t, stream=stream, **hp)
-            g.pack(ag[rank * g.S:(rank + 1) * g.S], stream)
-            if events is not None:
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                g.unpack(ag, stream)
-                b.record(stream)
-                events.append((a, b))
-            else:
-                g.unpack(ag, stream)
+            for name, fn in calls(gi, g, t):
+                if (every is not None) or (timed is not None and name == dominant):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    fn()
+                    b.record(stream)
+                    (every if every is not None else timed).append((name, a, b))
+                else:
+                    fn()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     print(f"bench: {args.warmup} warmup steps done", file=sys.stderr, flush=True)
 
-    unpack_events = []
+    dom_events = []
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     start.record(stream)
     for _ in range(args.steps):
-        step(events=unpack_events)
+        step(timed=dom_events)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    ms_total = start.elapsed_time(end)
-    ms_step = ms_total / args.steps
+    ms_step = start.elapsed_time(end) / args.steps
     print(f"bench: {args.steps} timed steps, {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
-    unpack_ms = sum(a.elapsed_time(b) for a, b in unpack_events)
-    unpack_launches = len(unpack_events)
-    unpack_avg_ms = unpack_ms / max(1, unpack_launches)
-    unpack_bytes_per_launch = byts["unpack"] / len(groups)
-    achieved = unpack_bytes_per_launch / (unpack_avg_ms * 1e-3) / 1e9
+    dom_ms = sum(a.elapsed_time(b) for _, a, b in dom_events)
+    dom_launches = len(dom_events)
+    dom_avg_ms = dom_ms / max(1, dom_launches)
+    dom_bytes_per_launch = byts[dominant] / len(groups)
+    achieved = dom_bytes_per_launch / (dom_avg_ms * 1e-3) / 1e9
 
-    # per-kernel breakdown (untimed steps, events around every launch)
-    per = {k: 0.0 for k in ("reduce", "adamw", "pack", "unpack")}
+    # per-kernel breakdown (extra untimed steps, events around every launch)
+    per = {k: 0.0 for k in kinds}
     if args.breakdown_steps > 0:
         evs = []
         for _ in range(args.breakdown_steps):
-            step(all_events=evs)
+            step(every=evs)
         torch.cuda.synchronize()
-        for e in evs:
-            for k, (i, j) in zip(("reduce", "adamw", "pack", "unpack"), ((0, 1), (1, 2), (2, 3), (3, 4))):
-                per[k] += e[i].elapsed_time(e[j])
+        for name, a, b in evs:
+            per[name] += a.elapsed_time(b)
         per = {k: v / args.breakdown_steps for k, v in per.items()}
     kernels = {k: {"ms_per_step": round(per[k], 4),
                    "algorithmic_GB_per_step": round(byts[k] / 1e9, 4),
                    "GBps": round(byts[k] / (per[k] * 1e-3) / 1e9, 1) if per[k] else None,
                    "hbm_frac": round(byts[k] / (per[k] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4) if per[k] else None}
-               for k in per}
+               for k in kinds}
 
     eff_gbps = step_bytes / (ms_step * 1e-3) / 1e9
     out = {
@@ -243,17 +286,18 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "world": n, "rank": rank, "groups": len(groups),
                    "params_per_rank": V, "align_elems": args.align,
-                   "step": "per group: reduce -> adamw -> pack -> unpack",
-                   "io": "fp32 master/m/v/grad shards, bf16 [N,S] grads and all-gather buffers"},
+                   "step": ("per group: fused reduce+adamw+pack -> unpack" if fused else
+                            "per group: reduce -> adamw -> pack -> unpack"),
+                   "io": "fp32 master/m/v shards, bf16 [N,S] grads and all-gather buffers"},
         "effective_GBps": eff_gbps,
         "hbm_frac": eff_gbps / HBM_PEAK_GBPS,
         "step_algorithmic_bytes": step_bytes,
         "wall_ms_per_step": wall * 1e3 / args.steps,
-        "roofline": {"bound": "hbm", "kernel": "unpack_kernel (copy-out)",
+        "roofline": {"bound": "hbm", "kernel": KERNEL_NAMES[dominant],
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
-                     "avg_launch_ms": unpack_avg_ms, "launches": unpack_launches,
-                     "algorithmic_bytes_per_launch": unpack_bytes_per_launch},
+                     "avg_launch_ms": dom_avg_ms, "launches": dom_launches,
+                     "algorithmic_bytes_per_launch": dom_bytes_per_launch},
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:

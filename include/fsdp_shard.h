@@ -9,6 +9,7 @@
  *   copy-out  fsdp_unpack_allgather  bf16 [N, S] buffer  -> full bf16 params
  *   reduce    fsdp_reduce_shard      bf16 [N, S] grads   -> fp32 grad shards
  *   update    fsdp_adamw_shard       AdamW on fp32 master, m and v shards
+ *   fused     fsdp_step_shard        reduce -> AdamW -> copy-in in one pass
  *
  * plus a host-side shard-layout planner.  The collectives between these steps
  * (all-gather, reduce-scatter) are not part of the library: a caller runs them
@@ -236,6 +237,30 @@ fsdp_status fsdp_reduce_shard(const fsdp_plan *plan, const uint16_t *rs_in,
 fsdp_status fsdp_adamw_shard(const fsdp_plan *plan,
                              const fsdp_adamw_hparams_t *hp, int64_t step,
                              void *stream);
+
+/* Flags of fsdp_step_shard. */
+enum { FSDP_STEP_WRITE_GRAD = 1 };
+
+/* Fused sharded step: reduce -> AdamW -> copy-in in one pass over this
+ * rank's pieces.  Per valid element it computes the reduced gradient exactly
+ * as fsdp_reduce_shard (fp32 sum in rank order, one division by N), applies
+ * the AdamW update of fsdp_adamw_shard with that gradient, and writes the
+ * bf16 cast of the new master into ag_in as fsdp_pack_allgather does (zeros
+ * in padding and gaps).  Results are bit-identical to the three calls in
+ * sequence; the gradient is written to the bound grad shards only with
+ * FSDP_STEP_WRITE_GRAD, saving its write and re-read otherwise.
+ * [MS] "Working Principle" (Reduce-Scatter state, then the Update state on the
+ * gradient slices; the next all-gather gathers the updated shards); [ST]
+ * fully_shard paragraph (optimizer on the shards) and "Mixed precision".
+ *   rs_in  [N, S] bf16 contributions, as for fsdp_reduce_shard
+ *   ag_in  [S] bf16 copy-in output (may be row `rank` of the all-gather
+ *          buffer); must not overlap rs_in
+ * Needs FSDP_ROLE_MASTER | EXP_AVG | EXP_AVG_SQ, plus GRAD with the flag.
+ * Errors: FSDP_E_INVAL (null buffer with S > 0, null hparams, step < 1,
+ *         unknown flag), FSDP_E_ALIGN, FSDP_E_STATE, FSDP_E_HIP. */
+fsdp_status fsdp_step_shard(const fsdp_plan *plan, const uint16_t *rs_in,
+                            uint16_t *ag_in, const fsdp_adamw_hparams_t *hp,
+                            int64_t step, uint32_t flags, void *stream);
 
 /* Wait for `stream` and report any asynchronous HIP error as FSDP_E_HIP. */
 fsdp_status fsdp_check_stream(void *stream);

@@ -44,21 +44,25 @@ def _run(cmd, verbose):
     return r
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(OUT_DIR, exist_ok=True)
+def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
+    """Compile every source and link the shared library; returns its path.
+
+    extra_flags (e.g. -DFSDP_TILE_UNPACK=65536) and out select a variant build.
+    """
+    out_dir = os.path.dirname(os.path.abspath(out))
+    os.makedirs(out_dir, exist_ok=True)
     objs = []
     for name, flags in SOURCES:
         src = os.path.join(SRC, name)
-        obj = os.path.join(OUT_DIR, name + ".o")
+        obj = os.path.join(out_dir, name + ".o")
         _run([HIPCC, *COMMON, *flags, *extra_flags, "-c", src, "-o", obj], verbose)
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     for o in objs:
         os.remove(o)
-    return LIB
+    return out
 
 
 def emit_asm(out_path: str) -> str:

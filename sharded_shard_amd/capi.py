@@ -5,14 +5,16 @@ their device addresses, torch streams become hipStream_t handles, and a
 negative status becomes an ``FsdpError``.  Every step of the sharded path runs
 in the HIP library; nothing here computes any part of it.  The library must be
 built (``python -m sharded_shard_amd.build``); importing this module without it
-raises ImportError.
+raises ImportError.  FSDP_SHARD_LIB in the environment selects another build
+of the same library (e.g. one compiled with different tile sizes).
 """
 from __future__ import annotations
 
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libfsdp_shard.so")
+LIB_PATH = os.environ.get("FSDP_SHARD_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "lib", "libfsdp_shard.so")
 
 FSDP_OK = 0
 FSDP_E_INVAL = -1
@@ -27,6 +29,8 @@ FSDP_ROLE_GRAD = 2
 FSDP_ROLE_EXP_AVG = 4
 FSDP_ROLE_EXP_AVG_SQ = 8
 FSDP_ROLE_FULL = 16
+
+FSDP_STEP_WRITE_GRAD = 1
 
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
@@ -85,6 +89,7 @@ _SIGS = {
     "fsdp_unpack_allgather": (_i32, [_P, _P, _P]),
     "fsdp_reduce_shard": (_i32, [_P, _P, _P]),
     "fsdp_adamw_shard": (_i32, [_P, ctypes.POINTER(AdamwHparams), _i64, _P]),
+    "fsdp_step_shard": (_i32, [_P, _P, _P, ctypes.POINTER(AdamwHparams), _i64, ctypes.c_uint32, _P]),
     "fsdp_check_stream": (_i32, [_P]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -215,6 +220,13 @@ def fsdp_adamw_shard(plan, lr: float, beta1: float, beta2: float, eps: float,
     hp = AdamwHparams(lr, beta1, beta2, eps, weight_decay)
     _check(lib.fsdp_adamw_shard(plan, ctypes.byref(hp), step, stream_handle(stream)),
            "fsdp_adamw_shard")
+
+
+def fsdp_step_shard(plan, rs_in, ag_in, lr: float, beta1: float, beta2: float, eps: float,
+                    weight_decay: float, step: int, flags: int = 0, stream=None) -> None:
+    hp = AdamwHparams(lr, beta1, beta2, eps, weight_decay)
+    _check(lib.fsdp_step_shard(plan, addr(rs_in), addr(ag_in), ctypes.byref(hp), step, flags,
+                               stream_handle(stream)), "fsdp_step_shard")
 
 
 def fsdp_check_stream(stream=None) -> None:

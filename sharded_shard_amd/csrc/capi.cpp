@@ -24,6 +24,9 @@ hipError_t launch_reduce(const ReduceTile *tiles, int64_t n, const DevEntry *ent
                          const uint16_t *rs_in, int64_t S, int32_t N, hipStream_t st);
 hipError_t launch_adamw(const EwTile *tiles, int64_t n, const DevEntry *ents,
                         const float scal[8], hipStream_t st);
+hipError_t launch_step(const PackTile *tiles, int64_t n, const DevEntry *ents,
+                       const uint16_t *rs_in, uint16_t *ag_in, int64_t S, int32_t N,
+                       const float scal[8], bool write_grad, hipStream_t st);
 }  // namespace fsdp
 
 struct fsdp_plan {
@@ -57,6 +60,22 @@ bool misaligned(const void *p, uintptr_t a) {
 }
 
 size_t round256(size_t b) { return (b + 255) & ~static_cast<size_t>(255); }
+
+// AdamW scalars: fp64 arithmetic on the hyperparameters, each rounded once
+// to fp32 (beta1, 1-beta1, beta2, 1-beta2, eps, 1-lr*wd, lr/(1-beta1^t),
+// sqrt(1-beta2^t)).
+void adamw_scalars(const fsdp_adamw_hparams_t *hp, int64_t step, float out[8]) {
+    const double bc1 = 1.0 - std::pow(hp->beta1, static_cast<double>(step));
+    const double bc2 = 1.0 - std::pow(hp->beta2, static_cast<double>(step));
+    out[0] = static_cast<float>(hp->beta1);
+    out[1] = static_cast<float>(1.0 - hp->beta1);
+    out[2] = static_cast<float>(hp->beta2);
+    out[3] = static_cast<float>(1.0 - hp->beta2);
+    out[4] = static_cast<float>(hp->eps);
+    out[5] = static_cast<float>(1.0 - hp->lr * hp->weight_decay);
+    out[6] = static_cast<float>(hp->lr / bc1);
+    out[7] = static_cast<float>(std::pow(bc2, 0.5));
+}
 
 // Hot calls run on the device the tables live on.
 fsdp_status check_device(const fsdp_plan *p) {
@@ -336,22 +355,36 @@ fsdp_status fsdp_adamw_shard(const fsdp_plan *p, const fsdp_adamw_hparams_t *hp,
     if (hp == nullptr) return fail(FSDP_E_INVAL, "fsdp_adamw_shard: null hyperparameters");
     if (step < 1) return fail(FSDP_E_INVAL, "fsdp_adamw_shard: step counts from 1");
     if ((s = check_device(p)) != FSDP_OK) return s;
-    // fp64 on the hyperparameters, each scalar rounded once to fp32
-    const double bc1 = 1.0 - std::pow(hp->beta1, static_cast<double>(step));
-    const double bc2 = 1.0 - std::pow(hp->beta2, static_cast<double>(step));
-    const float scal[8] = {
-        static_cast<float>(hp->beta1),
-        static_cast<float>(1.0 - hp->beta1),
-        static_cast<float>(hp->beta2),
-        static_cast<float>(1.0 - hp->beta2),
-        static_cast<float>(hp->eps),
-        static_cast<float>(1.0 - hp->lr * hp->weight_decay),
-        static_cast<float>(hp->lr / bc1),
-        static_cast<float>(std::pow(bc2, 0.5)),
-    };
+    float scal[8];
+    adamw_scalars(hp, step, scal);
     hipError_t e = fsdp::launch_adamw(p->d_adamw, static_cast<int64_t>(p->L.adamw.size()),
                                       p->d_entries, scal, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? FSDP_OK : hip_fail(e, "fsdp_adamw_shard: launch");
+}
+
+fsdp_status fsdp_step_shard(const fsdp_plan *p, const uint16_t *rs_in, uint16_t *ag_in,
+                            const fsdp_adamw_hparams_t *hp, int64_t step, uint32_t flags,
+                            void *stream) {
+    const bool write_grad = (flags & FSDP_STEP_WRITE_GRAD) != 0;
+    const int32_t roles = FSDP_ROLE_MASTER | FSDP_ROLE_EXP_AVG | FSDP_ROLE_EXP_AVG_SQ |
+                          (write_grad ? FSDP_ROLE_GRAD : 0);
+    fsdp_status s = need_roles(p, roles, "fsdp_step_shard");
+    if (s != FSDP_OK) return s;
+    if ((flags & ~static_cast<uint32_t>(FSDP_STEP_WRITE_GRAD)) != 0)
+        return fail(FSDP_E_INVAL, "fsdp_step_shard: unknown flag");
+    if (p->L.S > 0 && (rs_in == nullptr || ag_in == nullptr))
+        return fail(FSDP_E_INVAL, "fsdp_step_shard: null rs_in or ag_in");
+    if (misaligned(rs_in, 2) || misaligned(ag_in, 2))
+        return fail(FSDP_E_ALIGN, "fsdp_step_shard: rs_in or ag_in not 2-byte aligned");
+    if (hp == nullptr) return fail(FSDP_E_INVAL, "fsdp_step_shard: null hyperparameters");
+    if (step < 1) return fail(FSDP_E_INVAL, "fsdp_step_shard: step counts from 1");
+    if ((s = check_device(p)) != FSDP_OK) return s;
+    float scal[8];
+    adamw_scalars(hp, step, scal);
+    hipError_t e = fsdp::launch_step(p->d_pack, static_cast<int64_t>(p->L.pack.size()),
+                                     p->d_entries, rs_in, ag_in, p->L.S, p->L.world, scal,
+                                     write_grad, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FSDP_OK : hip_fail(e, "fsdp_step_shard: launch");
 }
 
 fsdp_status fsdp_check_stream(void *stream) {

@@ -1,30 +1,76 @@
 // HIP kernels of one rank's FSDP2 sharded step, written for CDNA4 (gfx950).
 //
-// All four kernels stream HBM and do (almost) no arithmetic, so the design
-// rules are the memory-bound ones: 16-byte (dwordx4) coalesced loads and
-// stores, several independent loads in flight per lane, non-temporal hints
-// on data that is touched once, and no LDS.  Work is a table of tiles built
-// on the host (plan.cpp): block b takes tiles b, b + grid, ...; each tile is
-// one contiguous run of one parameter, so a block reads one tile record and
-// one entry record with scalar loads and then streams.
+// All kernels stream HBM and do little arithmetic, so the design rules are the
+// memory-bound ones: 16-byte (dwordx4) coalesced loads and stores, several
+// independent loads in flight per lane, a cache policy chosen per stream
+// (non-temporal for data touched once, where it measured faster), no LDS.
+//
+// Work decomposition.  The host planner (plan.cpp) cuts every run of every
+// parameter into tiles of kTile* elements and uploads the tile table once.  A
+// launch has `split` blocks per tile: block b serves tile b / split,
+// sub-range b % split of kTile / split elements.  The table stays small (one 16- or
+// 32-byte record per tile) while each block moves only a few KB, which keeps
+// all 256 CUs busy to the end of the launch.  Blocks read their tile record
+// and one entry record with scalar loads, then stream.  Grids are
+// grid-strided, so any grid size is correct.
 //
 // Alignment.  Pieces of a group sit back to back with no gap by default, so a
 // run can start at any 2-byte (bf16) or 4-byte (fp32) address.  Destinations
-// are handled in 16-byte vectors after a short element-wise head; sources
+// are written in 16-byte vectors after a short element-wise head; sources
 // that are misaligned relative to the destination are read as aligned 16-byte
 // vectors and funnel-shifted in registers (v_alignbyte).  A 16-byte aligned
 // vector never crosses a page, and every vector loaded holds at least one byte
-// of the run, so the extra reads never touch unmapped memory.
+// of the run, so these reads never touch unmapped memory.
 //
 // Numerics (built with -ffp-contract=off and correctly rounded fp32 divide
 // and square root): reductions add rank contributions in rank order starting
 // from rank 0's value, then divide once by N; AdamW performs each operation
-// as one fp32 rounding in the order documented in the C header.
+// as one fp32 rounding in the order documented in the C header; bf16 casts
+// round to nearest even.  The fused step uses the same device functions in
+// the same order, so its results equal the three separate calls bit for bit.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
 #include "plan.hpp"
+
+// Cache policy per kernel: bit 0 = non-temporal loads, bit 1 = non-temporal
+// stores.  Elements per block (sub-range) per kernel; for the kernels that
+// read all N rows per element, the sub-range shrinks as N grows
+// (FSDP_ROWS_BUDGET row-elements per block, at least FSDP_MIN_SUB).
+#ifndef FSDP_UNPACK_POL
+#define FSDP_UNPACK_POL 3
+#endif
+#ifndef FSDP_REDUCE_POL
+#define FSDP_REDUCE_POL 3
+#endif
+#ifndef FSDP_ADAMW_POL
+#define FSDP_ADAMW_POL 0
+#endif
+#ifndef FSDP_PACK_POL
+#define FSDP_PACK_POL 3
+#endif
+#ifndef FSDP_STEP_POL
+#define FSDP_STEP_POL 0
+#endif
+#ifndef FSDP_UNPACK_SUB
+#define FSDP_UNPACK_SUB 2048
+#endif
+#ifndef FSDP_ADAMW_SUB
+#define FSDP_ADAMW_SUB 4096
+#endif
+#ifndef FSDP_PACK_SUB
+#define FSDP_PACK_SUB 8192
+#endif
+#ifndef FSDP_ROWS_BUDGET
+#define FSDP_ROWS_BUDGET 32768
+#endif
+#ifndef FSDP_MIN_SUB
+#define FSDP_MIN_SUB 512
+#endif
+#ifndef FSDP_ROW_BATCH
+#define FSDP_ROW_BATCH 8
+#endif
 
 namespace fsdp {
 
@@ -39,14 +85,20 @@ constexpr int kBlock = 256;
 // small helpers
 // ---------------------------------------------------------------------------
 
-template <typename T>
-__device__ __forceinline__ T ld_nt(const T *p) {
-    return __builtin_nontemporal_load(p);
+template <int NT, typename T>
+__device__ __forceinline__ T ldp(const T *p) {
+    if constexpr (NT != 0) return __builtin_nontemporal_load(p);
+    else return *p;
 }
 
-template <typename T>
-__device__ __forceinline__ void st_nt(T *p, T v) {
-    __builtin_nontemporal_store(v, p);
+template <int NT, typename T>
+__device__ __forceinline__ void stp(T *p, T v) {
+    if constexpr (NT != 0) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+__device__ __forceinline__ uint32_t lo32(const void *p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
 __device__ __forceinline__ uint32_t alignbyte2(uint32_t hi, uint32_t lo) {
@@ -81,27 +133,27 @@ __device__ __forceinline__ u32x4 funnel_bytes(u32x4 a, u32x4 b, uint32_t k) {
     return lo;
 }
 
-// 16 bytes at byte address `addr` (even).  k = addr & 15 must be uniform
-// across the wave for the branch to stay scalar.
+// 16 bytes starting at p; k = p's address & 15 (even), uniform across the
+// wave so the branch stays scalar.
+template <int NT>
 __device__ __forceinline__ u32x4 load16_at(const uint16_t *p, uint32_t k) {
-    if (k == 0) return ld_nt(reinterpret_cast<const u32x4 *>(p));
-    const u32x4 *al = reinterpret_cast<const u32x4 *>(
-        reinterpret_cast<uintptr_t>(p) - k);
-    const u32x4 a = ld_nt(al);
-    const u32x4 b = ld_nt(al + 1);
+    if (k == 0) return ldp<NT>(reinterpret_cast<const u32x4 *>(p));
+    const u32x4 *al = reinterpret_cast<const u32x4 *>(reinterpret_cast<uintptr_t>(p) - k);
+    const u32x4 a = ldp<NT>(al);
+    const u32x4 b = ldp<NT>(al + 1);
     return funnel_bytes(a, b, k);
 }
 
 // Eight fp32 starting at p, whose dword index modulo 4 is q (uniform).
-__device__ __forceinline__ void load8f_at(const float *p, uint32_t q, f32x4 &o0,
-                                          f32x4 &o1) {
+template <int NT>
+__device__ __forceinline__ void load8f_at(const float *p, uint32_t q, f32x4 &o0, f32x4 &o1) {
     const f32x4 *al = reinterpret_cast<const f32x4 *>(p - q);
     if (q == 0) {
-        o0 = ld_nt(al);
-        o1 = ld_nt(al + 1);
+        o0 = ldp<NT>(al);
+        o1 = ldp<NT>(al + 1);
         return;
     }
-    const f32x4 a = ld_nt(al), b = ld_nt(al + 1), c = ld_nt(al + 2);
+    const f32x4 a = ldp<NT>(al), b = ldp<NT>(al + 1), c = ldp<NT>(al + 2);
     switch (q) {
         case 1:
             o0 = f32x4{a.y, a.z, a.w, b.x};
@@ -115,6 +167,28 @@ __device__ __forceinline__ void load8f_at(const float *p, uint32_t q, f32x4 &o0,
             o0 = f32x4{a.w, b.x, b.y, b.z};
             o1 = f32x4{b.w, c.x, c.y, c.z};
             break;
+    }
+}
+
+// Store 8 bf16 (one u32x4) at p, whose address modulo 16 is ka (even,
+// uniform): one 16-byte store when aligned, else dword and short stores.
+template <int NT>
+__device__ __forceinline__ void store16_at(uint16_t *p, uint32_t ka, u32x4 w) {
+    if (ka == 0) {
+        stp<NT>(reinterpret_cast<u32x4 *>(p), w);
+    } else if ((ka & 3u) == 0) {
+        uint32_t *d = reinterpret_cast<uint32_t *>(p);
+        d[0] = w.x;
+        d[1] = w.y;
+        d[2] = w.z;
+        d[3] = w.w;
+    } else {
+        p[0] = static_cast<uint16_t>(w.x);
+        uint32_t *d = reinterpret_cast<uint32_t *>(p + 1);
+        d[0] = alignbyte2(w.y, w.x);
+        d[1] = alignbyte2(w.z, w.y);
+        d[2] = alignbyte2(w.w, w.z);
+        p[7] = static_cast<uint16_t>(w.w >> 16);
     }
 }
 
@@ -133,6 +207,10 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return bf16_rne(lo) | (bf16_rne(hi) << 16);
 }
 
+__device__ __forceinline__ u32x4 pack8(const float (&x)[8]) {
+    return u32x4{pack2(x[0], x[1]), pack2(x[2], x[3]), pack2(x[4], x[5]), pack2(x[6], x[7])};
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -140,60 +218,69 @@ __device__ __forceinline__ float widen(uint16_t h) {
     return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
+// Tile t and first element b of virtual tile vt: `split` blocks per tile,
+// `sub` elements each (a multiple of 8, so every sub-range keeps the tile's
+// phase modulo 16 bytes).
+__device__ __forceinline__ void sub_range(int64_t vt, int32_t split, int64_t sub, int64_t *t,
+                                          int64_t *b) {
+    *t = vt / split;
+    *b = (vt - *t * split) * sub;
+}
+
 // ---------------------------------------------------------------------------
 // copy-out: [N, S] bf16 -> full parameters
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ void copy_run_bf16(uint16_t *dst, const uint16_t *src,
-                                              int64_t len) {
+template <int POL>
+__device__ __forceinline__ void copy_run_bf16(uint16_t *__restrict__ dst,
+                                              const uint16_t *__restrict__ src, int64_t len) {
+    constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
     const int tid = threadIdx.x;
-    const uint32_t da = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst));
-    int64_t head = ((16u - (da & 15u)) & 15u) >> 1;
+    int64_t head = ((16u - (lo32(dst) & 15u)) & 15u) >> 1;
     if (head > len) head = len;
     if (tid < head) dst[tid] = src[tid];
-    const int64_t rem = len - head;
-    const int64_t nvec = rem >> 3;
+    const int64_t nvec = (len - head) >> 3;
     u32x4 *dv = reinterpret_cast<u32x4 *>(dst + head);
     const uint16_t *s = src + head;
-    const uint32_t k = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s)) & 15u;
+    const uint32_t k = lo32(s) & 15u;
     if (k == 0) {
         const u32x4 *sv = reinterpret_cast<const u32x4 *>(s);
         int64_t v = tid;
-        for (; v + 3 * kBlock < nvec; v += 4 * kBlock) {
-            const u32x4 x0 = ld_nt(sv + v);
-            const u32x4 x1 = ld_nt(sv + v + kBlock);
-            const u32x4 x2 = ld_nt(sv + v + 2 * kBlock);
-            const u32x4 x3 = ld_nt(sv + v + 3 * kBlock);
-            st_nt(dv + v, x0);
-            st_nt(dv + v + kBlock, x1);
-            st_nt(dv + v + 2 * kBlock, x2);
-            st_nt(dv + v + 3 * kBlock, x3);
+        for (; v + kBlock < nvec; v += 2 * kBlock) {
+            const u32x4 x0 = ldp<LN>(sv + v);
+            const u32x4 x1 = ldp<LN>(sv + v + kBlock);
+            stp<SN>(dv + v, x0);
+            stp<SN>(dv + v + kBlock, x1);
         }
-        for (; v < nvec; v += kBlock) st_nt(dv + v, ld_nt(sv + v));
+        if (v < nvec) stp<SN>(dv + v, ldp<LN>(sv + v));
     } else {
-        const u32x4 *sv = reinterpret_cast<const u32x4 *>(
-            reinterpret_cast<uintptr_t>(s) - k);
+        const u32x4 *sv = reinterpret_cast<const u32x4 *>(reinterpret_cast<uintptr_t>(s) - k);
         int64_t v = tid;
         for (; v + kBlock < nvec; v += 2 * kBlock) {
-            const u32x4 a0 = ld_nt(sv + v), b0 = ld_nt(sv + v + 1);
-            const u32x4 a1 = ld_nt(sv + v + kBlock), b1 = ld_nt(sv + v + kBlock + 1);
-            st_nt(dv + v, funnel_bytes(a0, b0, k));
-            st_nt(dv + v + kBlock, funnel_bytes(a1, b1, k));
+            const u32x4 a0 = ldp<LN>(sv + v), b0 = ldp<LN>(sv + v + 1);
+            const u32x4 a1 = ldp<LN>(sv + v + kBlock), b1 = ldp<LN>(sv + v + kBlock + 1);
+            stp<SN>(dv + v, funnel_bytes(a0, b0, k));
+            stp<SN>(dv + v + kBlock, funnel_bytes(a1, b1, k));
         }
-        for (; v < nvec; v += kBlock)
-            st_nt(dv + v, funnel_bytes(ld_nt(sv + v), ld_nt(sv + v + 1), k));
+        if (v < nvec) stp<SN>(dv + v, funnel_bytes(ldp<LN>(sv + v), ldp<LN>(sv + v + 1), k));
     }
     const int64_t done = head + (nvec << 3);
     if (tid < len - done) dst[done + tid] = src[done + tid];
 }
 
+template <int POL>
 __global__ __launch_bounds__(kBlock) void unpack_kernel(
-    const UnpackTile *__restrict__ tiles, int64_t n_tiles,
+    const UnpackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
     const DevEntry *__restrict__ ents, const uint16_t *__restrict__ ag_out) {
-    for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
         const UnpackTile tl = tiles[t];
-        uint16_t *dst = ents[tl.entry].full + tl.dst;
-        copy_run_bf16(dst, ag_out + tl.src, tl.len);
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        copy_run_bf16<POL>(ents[tl.entry].full + tl.dst + b, ag_out + tl.src + b, len);
     }
 }
 
@@ -201,60 +288,71 @@ __global__ __launch_bounds__(kBlock) void unpack_kernel(
 // copy-in: fp32 master shards -> bf16 segment (zeros in padding)
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(kBlock) void pack_kernel(
-    const PackTile *__restrict__ tiles, int64_t n_tiles,
-    const DevEntry *__restrict__ ents, uint16_t *__restrict__ ag_in) {
+// dst[e] = 0 for e in [from, len), 16-byte stores where aligned.
+template <int SN>
+__device__ __forceinline__ void zero_bf16(uint16_t *dst, int64_t from, int64_t len) {
     const int tid = threadIdx.x;
-    for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+    if (from >= len) return;
+    uint16_t *d = dst + from;
+    const int64_t n = len - from;
+    int64_t head = ((16u - (lo32(d) & 15u)) & 15u) >> 1;
+    if (head > n) head = n;
+    if (tid < head) d[tid] = 0;
+    const int64_t nvec = (n - head) >> 3;
+    u32x4 *dv = reinterpret_cast<u32x4 *>(d + head);
+    for (int64_t v = tid; v < nvec; v += kBlock) stp<SN>(dv + v, u32x4{0u, 0u, 0u, 0u});
+    const int64_t done = head + (nvec << 3);
+    if (tid < n - done) d[done + tid] = 0;
+}
+
+template <int POL>
+__device__ __forceinline__ void pack_run(uint16_t *__restrict__ dst, const float *__restrict__ src,
+                                         int64_t len, int64_t valid) {
+    constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
+    const int tid = threadIdx.x;
+    int64_t head = ((16u - (lo32(dst) & 15u)) & 15u) >> 1;
+    if (head > valid) head = valid;
+    if (tid < head) dst[tid] = static_cast<uint16_t>(bf16_rne(src[tid]));
+    const int64_t nvec = (valid - head) >> 3;
+    u32x4 *dv = reinterpret_cast<u32x4 *>(dst + head);
+    const float *s = src + head;
+    const uint32_t q = (lo32(s) >> 2) & 3u;
+    int64_t v = tid;
+    for (; v + kBlock < nvec; v += 2 * kBlock) {
+        f32x4 a0, a1, b0, b1;
+        load8f_at<LN>(s + (v << 3), q, a0, a1);
+        load8f_at<LN>(s + ((v + kBlock) << 3), q, b0, b1);
+        stp<SN>(dv + v, u32x4{pack2(a0.x, a0.y), pack2(a0.z, a0.w), pack2(a1.x, a1.y),
+                              pack2(a1.z, a1.w)});
+        stp<SN>(dv + v + kBlock, u32x4{pack2(b0.x, b0.y), pack2(b0.z, b0.w), pack2(b1.x, b1.y),
+                                       pack2(b1.z, b1.w)});
+    }
+    if (v < nvec) {
+        f32x4 a0, a1;
+        load8f_at<LN>(s + (v << 3), q, a0, a1);
+        stp<SN>(dv + v, u32x4{pack2(a0.x, a0.y), pack2(a0.z, a0.w), pack2(a1.x, a1.y),
+                              pack2(a1.z, a1.w)});
+    }
+    const int64_t done = head + (nvec << 3);
+    if (tid < valid - done) dst[done + tid] = static_cast<uint16_t>(bf16_rne(src[done + tid]));
+    zero_bf16<SN>(dst, valid, len);
+}
+
+template <int POL>
+__global__ __launch_bounds__(kBlock) void pack_kernel(
+    const PackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
+    const DevEntry *__restrict__ ents, uint16_t *__restrict__ ag_in) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
         const PackTile tl = tiles[t];
-        uint16_t *dst = ag_in + tl.dst;
-        const float *src = ents[tl.entry].master + tl.src;
-        const int64_t len = tl.len, valid = tl.valid;
-        const uint32_t da = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst));
-        int64_t head = ((16u - (da & 15u)) & 15u) >> 1;
-        if (head > len) head = len;
-        if (tid < head) dst[tid] = tid < valid ? static_cast<uint16_t>(bf16_rne(src[tid])) : 0;
-        const int64_t nvec = (len - head) >> 3;
-        u32x4 *dv = reinterpret_cast<u32x4 *>(dst + head);
-        const float *s = src + head;
-        const uint32_t q = (static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s)) >> 2) & 3u;
-        // vectors wholly inside the valid part, then the straddling one, then zeros
-        const int64_t vfull = valid > head ? (valid - head) >> 3 : 0;
-        int64_t v = tid;
-        for (; v + kBlock < vfull; v += 2 * kBlock) {
-            f32x4 a0, a1, b0, b1;
-            load8f_at(s + (v << 3), q, a0, a1);
-            load8f_at(s + ((v + kBlock) << 3), q, b0, b1);
-            st_nt(dv + v, u32x4{pack2(a0.x, a0.y), pack2(a0.z, a0.w),
-                                pack2(a1.x, a1.y), pack2(a1.z, a1.w)});
-            st_nt(dv + v + kBlock, u32x4{pack2(b0.x, b0.y), pack2(b0.z, b0.w),
-                                         pack2(b1.x, b1.y), pack2(b1.z, b1.w)});
-        }
-        for (; v < vfull; v += kBlock) {
-            f32x4 a0, a1;
-            load8f_at(s + (v << 3), q, a0, a1);
-            st_nt(dv + v, u32x4{pack2(a0.x, a0.y), pack2(a0.z, a0.w),
-                                pack2(a1.x, a1.y), pack2(a1.z, a1.w)});
-        }
-        for (v = vfull + tid; v < nvec; v += kBlock) {
-            const int64_t e0 = head + (v << 3);
-            if (e0 >= valid) {
-                st_nt(dv + v, u32x4{0u, 0u, 0u, 0u});
-            } else {
-                uint32_t w[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t e = e0 + 2 * i;
-                    const uint32_t lo = e < valid ? bf16_rne(src[e]) : 0u;
-                    const uint32_t hi = e + 1 < valid ? bf16_rne(src[e + 1]) : 0u;
-                    w[i] = lo | (hi << 16);
-                }
-                st_nt(dv + v, u32x4{w[0], w[1], w[2], w[3]});
-            }
-        }
-        const int64_t done = head + (nvec << 3);
-        const int64_t e = done + tid;
-        if (e < len) dst[e] = e < valid ? static_cast<uint16_t>(bf16_rne(src[e])) : 0;
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        int64_t valid = tl.valid - b;
+        valid = valid < 0 ? 0 : (valid > len ? len : valid);
+        pack_run<POL>(ag_in + tl.dst + b, ents[tl.entry].master + tl.src + b, len, valid);
     }
 }
 
@@ -263,8 +361,8 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(
 // ---------------------------------------------------------------------------
 
 // Sum of rows 0..N-1 at element offset `e` (from row 0's base), in order.
-__device__ __forceinline__ float sum_rows_scalar(const uint16_t *src0, int64_t S,
-                                                 int32_t N, int64_t e) {
+__device__ __forceinline__ float sum_rows_scalar(const uint16_t *src0, int64_t S, int32_t N,
+                                                 int64_t e) {
     float acc = widen(src0[e]);
     for (int32_t j = 1; j < N; ++j) acc = acc + widen(src0[static_cast<int64_t>(j) * S + e]);
     return acc;
@@ -292,57 +390,101 @@ __device__ __forceinline__ void init8(float (&acc)[8], u32x4 x) {
     acc[7] = bf16_hi(x.w);
 }
 
-template <bool kRowsAligned>
-__global__ __launch_bounds__(kBlock) void reduce_kernel(
-    const ReduceTile *__restrict__ tiles, int64_t n_tiles,
-    const DevEntry *__restrict__ ents, const uint16_t *__restrict__ rs_in,
-    int64_t S, int32_t N, float fN) {
+// Raw buffer load of 16 bytes at byte offset voff from a 16-byte aligned,
+// wave-uniform base.  The descriptor (base, nbytes) lives in SGPRs, so each
+// row of [N, S] costs one shared 32-bit lane offset instead of a 64-bit
+// address per row, which keeps VGPR use and occupancy where the row batch
+// needs them.  Reads at or past nbytes return zero instead of touching memory.
+// Descriptor word 3 is the gfx9-family raw-buffer format; aux bit 1 = nt.
+template <int NT>
+__device__ __forceinline__ u32x4 bload16(const char *al, uint32_t voff, uint32_t nbytes) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(al), 0, nbytes, 0x00020000);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, NT ? 2 : 0);
+}
+
+// 16 bytes at row + offb; k = (row + offb) & 15, uniform; nbytes bounds the
+// bytes this block reads past row - k.
+template <int NT>
+__device__ __forceinline__ u32x4 row_load16(const char *row, uint32_t offb, uint32_t k,
+                                            uint32_t nbytes) {
+    const char *al = row - k;
+    if (k == 0) return bload16<NT>(al, offb, nbytes);
+    const u32x4 a = bload16<NT>(al, offb, nbytes);
+    const u32x4 b = bload16<NT>(al, offb + 16, nbytes);
+    return funnel_bytes(a, b, k);
+}
+
+// Eight consecutive column sums of the N rows of [N, S] bf16 whose row 0
+// starts at base (uniform) plus this lane's byte offset offb, added in rank
+// order from row 0; k0 = (base + offb) & 15, kS = (2S) & 15; the block reads
+// fewer than nbytes bytes from each row base.
+template <int NT, bool kRowsAligned>
+__device__ __forceinline__ void sum_rows8(const uint16_t *base, uint32_t offb, uint32_t nbytes,
+                                          int64_t S, int32_t N, uint32_t k0, uint32_t kS,
+                                          float (&acc)[8]) {
+    const char *r = reinterpret_cast<const char *>(base);
+    const int64_t Sb = S * 2;
+    init8(acc, row_load16<NT>(r, offb, k0, nbytes));
+    if (kRowsAligned) {
+        constexpr int RB = FSDP_ROW_BATCH;
+        int32_t j = 1;
+        for (; j + RB - 1 < N; j += RB) {
+            u32x4 x[RB];
+#pragma unroll
+            for (int i = 0; i < RB; ++i) x[i] = row_load16<NT>(r + (j + i) * Sb, offb, k0, nbytes);
+#pragma unroll
+            for (int i = 0; i < RB; ++i) acc8(acc, x[i]);
+        }
+        for (; j < N; ++j) acc8(acc, row_load16<NT>(r + j * Sb, offb, k0, nbytes));
+    } else {
+        uint32_t k = k0;
+        for (int32_t j = 1; j < N; ++j) {
+            k = (k + kS) & 15u;
+            acc8(acc, row_load16<NT>(r + j * Sb, offb, k, nbytes));
+        }
+    }
+}
+
+template <int POL, bool kRowsAligned>
+__device__ __forceinline__ void reduce_run(float *__restrict__ dst, const uint16_t *__restrict__ src0,
+                                           int64_t len, int64_t S, int32_t N, float fN) {
+    constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
     const int tid = threadIdx.x;
     const uint32_t kS = static_cast<uint32_t>((S * 2) & 15);
-    for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+    int64_t head = ((16u - (lo32(dst) & 15u)) & 15u) >> 2;
+    if (head > len) head = len;
+    if (tid < head) dst[tid] = sum_rows_scalar(src0, S, N, tid) / fN;
+    const int64_t ngrp = (len - head) >> 3;
+    const uint16_t *s0 = src0 + head;
+    const uint32_t k0 = lo32(s0) & 15u;
+    const uint32_t nbytes = static_cast<uint32_t>(2 * (len - head) + 48);
+    f32x4 *dv = reinterpret_cast<f32x4 *>(dst + head);
+    for (int64_t g = tid; g < ngrp; g += kBlock) {
+        float acc[8];
+        sum_rows8<LN, kRowsAligned>(s0, static_cast<uint32_t>(g) << 4, nbytes, S, N, k0, kS, acc);
+        stp<SN>(dv + 2 * g, f32x4{acc[0] / fN, acc[1] / fN, acc[2] / fN, acc[3] / fN});
+        stp<SN>(dv + 2 * g + 1, f32x4{acc[4] / fN, acc[5] / fN, acc[6] / fN, acc[7] / fN});
+    }
+    const int64_t done = head + (ngrp << 3);
+    if (tid < len - done) dst[done + tid] = sum_rows_scalar(src0, S, N, done + tid) / fN;
+}
+
+template <int POL, bool kRowsAligned>
+__global__ __launch_bounds__(kBlock) void reduce_kernel(
+    const ReduceTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
+    const DevEntry *__restrict__ ents, const uint16_t *__restrict__ rs_in,
+    int64_t S, int32_t N, float fN) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
         const ReduceTile tl = tiles[t];
-        float *dst = ents[tl.entry].grad + tl.dst;
-        const uint16_t *src0 = rs_in + tl.src;
-        const int64_t len = tl.len;
-        const uint32_t da = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst));
-        int64_t head = ((16u - (da & 15u)) & 15u) >> 2;
-        if (head > len) head = len;
-        if (tid < head) dst[tid] = sum_rows_scalar(src0, S, N, tid) / fN;
-        const int64_t ngrp = (len - head) >> 3;
-        const uint16_t *s0 = src0 + head;
-        const uint32_t k0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s0)) & 15u;
-        f32x4 *dv = reinterpret_cast<f32x4 *>(dst + head);
-        for (int64_t g = tid; g < ngrp; g += kBlock) {
-            const uint16_t *p = s0 + (g << 3);
-            float acc[8];
-            if (kRowsAligned) {
-                // every row starts at the same offset modulo 16 bytes
-                init8(acc, load16_at(p, k0));
-                int32_t j = 1;
-                for (; j + 7 < N; j += 8) {
-                    u32x4 x[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) x[i] = load16_at(p + static_cast<int64_t>(j + i) * S, k0);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) acc8(acc, x[i]);
-                }
-                for (; j < N; ++j) acc8(acc, load16_at(p + static_cast<int64_t>(j) * S, k0));
-            } else {
-                init8(acc, load16_at(p, k0));
-                uint32_t k = k0;
-                for (int32_t j = 1; j < N; ++j) {
-                    k = (k + kS) & 15u;
-                    acc8(acc, load16_at(p + static_cast<int64_t>(j) * S, k));
-                }
-            }
-            const f32x4 o0{acc[0] / fN, acc[1] / fN, acc[2] / fN, acc[3] / fN};
-            const f32x4 o1{acc[4] / fN, acc[5] / fN, acc[6] / fN, acc[7] / fN};
-            st_nt(dv + 2 * g, o0);
-            st_nt(dv + 2 * g + 1, o1);
-        }
-        const int64_t done = head + (ngrp << 3);
-        const int64_t e = done + tid;
-        if (e < len) dst[e] = sum_rows_scalar(src0, S, N, e) / fN;
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        reduce_run<POL, kRowsAligned>(ents[tl.entry].grad + tl.dst + b, rs_in + tl.src + b, len,
+                                      S, N, fN);
     }
 }
 
@@ -351,8 +493,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(
 // ---------------------------------------------------------------------------
 
 struct AdamwScalars {
-    float beta1, one_minus_beta1, beta2, one_minus_beta2, eps, decay, step_size,
-        bc2_sqrt;
+    float beta1, one_minus_beta1, beta2, one_minus_beta2, eps, decay, step_size, bc2_sqrt;
 };
 
 __device__ __forceinline__ void adamw_elem(float &p, float g, float &m, float &v,
@@ -364,72 +505,222 @@ __device__ __forceinline__ void adamw_elem(float &p, float g, float &m, float &v
     p = p - c.step_size * (m / d);
 }
 
-__global__ __launch_bounds__(kBlock) void adamw_kernel(
-    const EwTile *__restrict__ tiles, int64_t n_tiles,
-    const DevEntry *__restrict__ ents, AdamwScalars c) {
-    const int tid = threadIdx.x;
-    for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
-        const EwTile tl = tiles[t];
-        const DevEntry en = ents[tl.entry];
-        float *P = en.master + tl.off;
-        const float *G = en.grad + tl.off;
-        float *M = en.exp_avg + tl.off;
-        float *Vv = en.exp_avg_sq + tl.off;
-        const int64_t len = tl.len;
-        const uint32_t ap = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(P)) & 15u;
-        const bool same = ap == (static_cast<uint32_t>(reinterpret_cast<uintptr_t>(G)) & 15u) &&
-                          ap == (static_cast<uint32_t>(reinterpret_cast<uintptr_t>(M)) & 15u) &&
-                          ap == (static_cast<uint32_t>(reinterpret_cast<uintptr_t>(Vv)) & 15u);
-        if (!same) {
-            for (int64_t i = tid; i < len; i += kBlock) {
-                float p = P[i], m = M[i], v = Vv[i];
-                adamw_elem(p, G[i], m, v, c);
-                P[i] = p;
-                M[i] = m;
-                Vv[i] = v;
-            }
-            continue;
-        }
-        int64_t head = ((16u - ap) & 15u) >> 2;
-        if (head > len) head = len;
-        if (tid < head) {
-            float p = P[tid], m = M[tid], v = Vv[tid];
-            adamw_elem(p, G[tid], m, v, c);
-            P[tid] = p;
-            M[tid] = m;
-            Vv[tid] = v;
-        }
-        const int64_t nvec = (len - head) >> 2;
-        f32x4 *pv = reinterpret_cast<f32x4 *>(P + head);
-        const f32x4 *gv = reinterpret_cast<const f32x4 *>(G + head);
-        f32x4 *mv = reinterpret_cast<f32x4 *>(M + head);
-        f32x4 *vv = reinterpret_cast<f32x4 *>(Vv + head);
-        for (int64_t i = tid; i < nvec; i += kBlock) {
-            const f32x4 g = ld_nt(gv + i);
-            f32x4 p = ld_nt(pv + i), m = ld_nt(mv + i), v = ld_nt(vv + i);
-            float pe[4] = {p.x, p.y, p.z, p.w}, me[4] = {m.x, m.y, m.z, m.w},
-                  ve[4] = {v.x, v.y, v.z, v.w};
-            const float ge[4] = {g.x, g.y, g.z, g.w};
+__device__ __forceinline__ void adamw_vec(f32x4 &p, f32x4 g, f32x4 &m, f32x4 &v,
+                                          const AdamwScalars &c) {
+    float pe[4] = {p.x, p.y, p.z, p.w}, me[4] = {m.x, m.y, m.z, m.w}, ve[4] = {v.x, v.y, v.z, v.w};
+    const float ge[4] = {g.x, g.y, g.z, g.w};
 #pragma unroll
-            for (int k = 0; k < 4; ++k) adamw_elem(pe[k], ge[k], me[k], ve[k], c);
-            st_nt(pv + i, f32x4{pe[0], pe[1], pe[2], pe[3]});
-            st_nt(mv + i, f32x4{me[0], me[1], me[2], me[3]});
-            st_nt(vv + i, f32x4{ve[0], ve[1], ve[2], ve[3]});
-        }
-        const int64_t e = head + (nvec << 2) + tid;
-        if (e < len) {
-            float p = P[e], m = M[e], v = Vv[e];
-            adamw_elem(p, G[e], m, v, c);
-            P[e] = p;
-            M[e] = m;
-            Vv[e] = v;
-        }
+    for (int k = 0; k < 4; ++k) adamw_elem(pe[k], ge[k], me[k], ve[k], c);
+    p = f32x4{pe[0], pe[1], pe[2], pe[3]};
+    m = f32x4{me[0], me[1], me[2], me[3]};
+    v = f32x4{ve[0], ve[1], ve[2], ve[3]};
+}
+
+__device__ __forceinline__ void adamw_scalar_at(float *P, const float *G, float *M, float *Vv,
+                                                int64_t i, const AdamwScalars &c) {
+    float p = P[i], m = M[i], v = Vv[i];
+    adamw_elem(p, G[i], m, v, c);
+    P[i] = p;
+    M[i] = m;
+    Vv[i] = v;
+}
+
+template <int POL>
+__device__ __forceinline__ void adamw_run(float *P, const float *G, float *M, float *Vv, int64_t len,
+                                          const AdamwScalars &c) {
+    constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
+    const int tid = threadIdx.x;
+    const uint32_t ap = lo32(P) & 15u;
+    const bool same = ap == (lo32(G) & 15u) && ap == (lo32(M) & 15u) && ap == (lo32(Vv) & 15u);
+    if (!same) {
+        for (int64_t i = tid; i < len; i += kBlock) adamw_scalar_at(P, G, M, Vv, i, c);
+        return;
+    }
+    int64_t head = ((16u - ap) & 15u) >> 2;
+    if (head > len) head = len;
+    if (tid < head) adamw_scalar_at(P, G, M, Vv, tid, c);
+    const int64_t nvec = (len - head) >> 2;
+    f32x4 *pv = reinterpret_cast<f32x4 *>(P + head);
+    const f32x4 *gv = reinterpret_cast<const f32x4 *>(G + head);
+    f32x4 *mv = reinterpret_cast<f32x4 *>(M + head);
+    f32x4 *vv = reinterpret_cast<f32x4 *>(Vv + head);
+    int64_t i = tid;
+    for (; i + kBlock < nvec; i += 2 * kBlock) {
+        const int64_t i1 = i + kBlock;
+        f32x4 p0 = ldp<LN>(pv + i), m0 = ldp<LN>(mv + i), v0 = ldp<LN>(vv + i);
+        f32x4 p1 = ldp<LN>(pv + i1), m1 = ldp<LN>(mv + i1), v1 = ldp<LN>(vv + i1);
+        const f32x4 g0 = ldp<LN>(gv + i), g1 = ldp<LN>(gv + i1);
+        adamw_vec(p0, g0, m0, v0, c);
+        adamw_vec(p1, g1, m1, v1, c);
+        stp<SN>(pv + i, p0);
+        stp<SN>(mv + i, m0);
+        stp<SN>(vv + i, v0);
+        stp<SN>(pv + i1, p1);
+        stp<SN>(mv + i1, m1);
+        stp<SN>(vv + i1, v1);
+    }
+    if (i < nvec) {
+        f32x4 p0 = ldp<LN>(pv + i), m0 = ldp<LN>(mv + i), v0 = ldp<LN>(vv + i);
+        const f32x4 g0 = ldp<LN>(gv + i);
+        adamw_vec(p0, g0, m0, v0, c);
+        stp<SN>(pv + i, p0);
+        stp<SN>(mv + i, m0);
+        stp<SN>(vv + i, v0);
+    }
+    const int64_t e = head + (nvec << 2) + tid;
+    if (e < len) adamw_scalar_at(P, G, M, Vv, e, c);
+}
+
+template <int POL>
+__global__ __launch_bounds__(kBlock) void adamw_kernel(
+    const EwTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
+    const DevEntry *__restrict__ ents, AdamwScalars c) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
+        const EwTile tl = tiles[t];
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        const DevEntry en = ents[tl.entry];
+        const int64_t o = tl.off + b;
+        adamw_run<POL>(en.master + o, en.grad + o, en.exp_avg + o, en.exp_avg_sq + o, len, c);
     }
 }
 
-inline unsigned grid_for(int64_t n_tiles) {
-    constexpr int64_t kMaxGrid = 1 << 20;
-    return static_cast<unsigned>(n_tiles < kMaxGrid ? n_tiles : kMaxGrid);
+// ---------------------------------------------------------------------------
+// fused step: reduce -> AdamW -> copy-in, one pass over this rank's pieces
+// ---------------------------------------------------------------------------
+
+// One element: the three steps exactly as the separate kernels compute them.
+template <bool kWriteGrad>
+__device__ __forceinline__ void step_scalar_at(const uint16_t *rs0, int64_t S, int32_t N, float fN,
+                                               float *P, float *M, float *Vv, float *G,
+                                               uint16_t *dst, int64_t e, const AdamwScalars &c) {
+    const float g = sum_rows_scalar(rs0, S, N, e) / fN;
+    if (kWriteGrad) G[e] = g;
+    float p = P[e], m = M[e], v = Vv[e];
+    adamw_elem(p, g, m, v, c);
+    P[e] = p;
+    M[e] = m;
+    Vv[e] = v;
+    dst[e] = static_cast<uint16_t>(bf16_rne(p));
+}
+
+// Valid elements [0, valid) then zeros up to len.  rs0 is row 0 of the
+// gradient contributions at this run's first segment position; dst is ag_in
+// at the same position; P, M, Vv, G are the shards at this run's first
+// element.  The vector path aligns on the fp32 shards (the bulk of the
+// bytes); contributions are funnel-shifted per row and the bf16 output is
+// stored whole, by dwords or by halves, as its address allows.
+template <int POL, bool kRowsAligned, bool kWriteGrad>
+__device__ __forceinline__ void step_run(const uint16_t *__restrict__ rs0, int64_t S, int32_t N,
+                                         float fN, float *P, float *M, float *Vv, float *G,
+                                         uint16_t *dst, int64_t len, int64_t valid,
+                                         const AdamwScalars &c) {
+    constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
+    const int tid = threadIdx.x;
+    const uint32_t ap = lo32(P) & 15u;
+    const bool same = ap == (lo32(M) & 15u) && ap == (lo32(Vv) & 15u) &&
+                      (!kWriteGrad || ap == (lo32(G) & 15u));
+    if (!same) {
+        for (int64_t e = tid; e < valid; e += kBlock)
+            step_scalar_at<kWriteGrad>(rs0, S, N, fN, P, M, Vv, G, dst, e, c);
+    } else {
+        int64_t head = ((16u - ap) & 15u) >> 2;
+        if (head > valid) head = valid;
+        if (tid < head) step_scalar_at<kWriteGrad>(rs0, S, N, fN, P, M, Vv, G, dst, tid, c);
+        const int64_t ngrp = (valid - head) >> 3;
+        const uint32_t kS = static_cast<uint32_t>((S * 2) & 15);
+        const uint32_t k0 = lo32(rs0 + head) & 15u;
+        const uint32_t ka = lo32(dst + head) & 15u;
+        const uint32_t nbytes = static_cast<uint32_t>(2 * (valid - head) + 48);
+        for (int64_t g8 = tid; g8 < ngrp; g8 += kBlock) {
+            const int64_t e0 = head + (g8 << 3);
+            float acc[8];
+            sum_rows8<1, kRowsAligned>(rs0 + head, static_cast<uint32_t>(g8) << 4, nbytes, S, N,
+                                       k0, kS, acc);
+            f32x4 *pv = reinterpret_cast<f32x4 *>(P + e0);
+            f32x4 *mv = reinterpret_cast<f32x4 *>(M + e0);
+            f32x4 *vv = reinterpret_cast<f32x4 *>(Vv + e0);
+            f32x4 p0 = ldp<LN>(pv), p1 = ldp<LN>(pv + 1);
+            f32x4 m0 = ldp<LN>(mv), m1 = ldp<LN>(mv + 1);
+            f32x4 v0 = ldp<LN>(vv), v1 = ldp<LN>(vv + 1);
+            const f32x4 g0{acc[0] / fN, acc[1] / fN, acc[2] / fN, acc[3] / fN};
+            const f32x4 g1{acc[4] / fN, acc[5] / fN, acc[6] / fN, acc[7] / fN};
+            if (kWriteGrad) {
+                f32x4 *gv = reinterpret_cast<f32x4 *>(G + e0);
+                stp<SN>(gv, g0);
+                stp<SN>(gv + 1, g1);
+            }
+            adamw_vec(p0, g0, m0, v0, c);
+            adamw_vec(p1, g1, m1, v1, c);
+            stp<SN>(pv, p0);
+            stp<SN>(pv + 1, p1);
+            stp<SN>(mv, m0);
+            stp<SN>(mv + 1, m1);
+            stp<SN>(vv, v0);
+            stp<SN>(vv + 1, v1);
+            const float pb[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+            store16_at<1>(dst + e0, ka, pack8(pb));
+        }
+        const int64_t done = head + (ngrp << 3);
+        if (tid < valid - done)
+            step_scalar_at<kWriteGrad>(rs0, S, N, fN, P, M, Vv, G, dst, done + tid, c);
+    }
+    zero_bf16<1>(dst, valid, len);
+}
+
+template <int POL, bool kRowsAligned, bool kWriteGrad>
+__global__ __launch_bounds__(kBlock) void step_kernel(
+    const PackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
+    const DevEntry *__restrict__ ents,
+    const uint16_t *__restrict__ rs_in, uint16_t *__restrict__ ag_in, int64_t S, int32_t N,
+    float fN, AdamwScalars c) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
+        const PackTile tl = tiles[t];
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        int64_t valid = tl.valid - b;
+        valid = valid < 0 ? 0 : (valid > len ? len : valid);
+        const DevEntry en = ents[tl.entry];
+        const int64_t o = tl.src + b;
+        step_run<POL, kRowsAligned, kWriteGrad>(rs_in + tl.dst + b, S, N, fN, en.master + o,
+                                                en.exp_avg + o, en.exp_avg_sq + o,
+                                                kWriteGrad ? en.grad + o : nullptr,
+                                                ag_in + tl.dst + b, len, valid, c);
+    }
+}
+
+inline unsigned grid_for(int64_t n_tiles, int32_t split) {
+    constexpr int64_t kMaxGrid = 1 << 22;
+    const int64_t n = n_tiles * split;
+    return static_cast<unsigned>(n < kMaxGrid ? n : kMaxGrid);
+}
+
+// Blocks per tile for a wanted sub-range: the largest power of two not above
+// `want`, within [8, kTile]; tiles are powers of two, so it divides them.
+inline int32_t split_for(int64_t tile, int64_t want) {
+    int64_t sub = 8;
+    while (sub * 2 <= want && sub * 2 <= tile) sub *= 2;
+    return static_cast<int32_t>(tile / sub);
+}
+
+// Sub-range for kernels that read all N rows per element (reduce, fused step):
+// about FSDP_ROWS_BUDGET row-elements per block.
+inline int32_t split_rows(int64_t tile, int32_t N, int32_t extra_rows) {
+    int64_t want = FSDP_ROWS_BUDGET / (N + extra_rows);
+    if (want < FSDP_MIN_SUB) want = FSDP_MIN_SUB;
+    return split_for(tile, want);
+}
+
+AdamwScalars to_scalars(const float s[8]) {
+    return AdamwScalars{s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7]};
 }
 
 }  // namespace
@@ -438,17 +729,21 @@ inline unsigned grid_for(int64_t n_tiles) {
 // launchers (called by the C ABI after validation)
 // ---------------------------------------------------------------------------
 
-hipError_t launch_pack(const PackTile *tiles, int64_t n, const DevEntry *ents,
-                       uint16_t *ag_in, hipStream_t st) {
+hipError_t launch_pack(const PackTile *tiles, int64_t n, const DevEntry *ents, uint16_t *ag_in,
+                       hipStream_t st) {
     if (n == 0) return hipSuccess;
-    pack_kernel<<<grid_for(n), kBlock, 0, st>>>(tiles, n, ents, ag_in);
+    const int32_t sp = split_for(kTilePack, FSDP_PACK_SUB);
+    pack_kernel<FSDP_PACK_POL>
+        <<<grid_for(n, sp), kBlock, 0, st>>>(tiles, n, sp, kTilePack / sp, ents, ag_in);
     return hipGetLastError();
 }
 
 hipError_t launch_unpack(const UnpackTile *tiles, int64_t n, const DevEntry *ents,
                          const uint16_t *ag_out, hipStream_t st) {
     if (n == 0) return hipSuccess;
-    unpack_kernel<<<grid_for(n), kBlock, 0, st>>>(tiles, n, ents, ag_out);
+    const int32_t sp = split_for(kTileUnpack, FSDP_UNPACK_SUB);
+    unpack_kernel<FSDP_UNPACK_POL>
+        <<<grid_for(n, sp), kBlock, 0, st>>>(tiles, n, sp, kTileUnpack / sp, ents, ag_out);
     return hipGetLastError();
 }
 
@@ -456,18 +751,46 @@ hipError_t launch_reduce(const ReduceTile *tiles, int64_t n, const DevEntry *ent
                          const uint16_t *rs_in, int64_t S, int32_t N, hipStream_t st) {
     if (n == 0) return hipSuccess;
     const float fN = static_cast<float>(N);
+    const int32_t sp = split_rows(kTileReduce, N, 0);
+    const unsigned grid = grid_for(n, sp);
     if (((S * 2) & 15) == 0)
-        reduce_kernel<true><<<grid_for(n), kBlock, 0, st>>>(tiles, n, ents, rs_in, S, N, fN);
+        reduce_kernel<FSDP_REDUCE_POL, true>
+            <<<grid, kBlock, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
     else
-        reduce_kernel<false><<<grid_for(n), kBlock, 0, st>>>(tiles, n, ents, rs_in, S, N, fN);
+        reduce_kernel<FSDP_REDUCE_POL, false>
+            <<<grid, kBlock, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
     return hipGetLastError();
 }
 
 hipError_t launch_adamw(const EwTile *tiles, int64_t n, const DevEntry *ents,
                         const float scal[8], hipStream_t st) {
     if (n == 0) return hipSuccess;
-    AdamwScalars c{scal[0], scal[1], scal[2], scal[3], scal[4], scal[5], scal[6], scal[7]};
-    adamw_kernel<<<grid_for(n), kBlock, 0, st>>>(tiles, n, ents, c);
+    const int32_t sp = split_for(kTileAdamw, FSDP_ADAMW_SUB);
+    adamw_kernel<FSDP_ADAMW_POL><<<grid_for(n, sp), kBlock, 0, st>>>(
+        tiles, n, sp, kTileAdamw / sp, ents, to_scalars(scal));
+    return hipGetLastError();
+}
+
+hipError_t launch_step(const PackTile *tiles, int64_t n, const DevEntry *ents,
+                       const uint16_t *rs_in, uint16_t *ag_in, int64_t S, int32_t N,
+                       const float scal[8], bool write_grad, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const float fN = static_cast<float>(N);
+    const AdamwScalars c = to_scalars(scal);
+    // p, m, v read and written: six more streams per element besides the N rows
+    const int32_t sp = split_rows(kTilePack, N, 6);
+    const int64_t sub = kTilePack / sp;
+    const unsigned grid = grid_for(n, sp);
+    const bool aligned = ((S * 2) & 15) == 0;
+    constexpr int P = FSDP_STEP_POL;
+    if (aligned && write_grad)
+        step_kernel<P, true, true><<<grid, kBlock, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N, fN, c);
+    else if (aligned)
+        step_kernel<P, true, false><<<grid, kBlock, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N, fN, c);
+    else if (write_grad)
+        step_kernel<P, false, true><<<grid, kBlock, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N, fN, c);
+    else
+        step_kernel<P, false, false><<<grid, kBlock, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N, fN, c);
     return hipGetLastError();
 }
 

@@ -23,10 +23,22 @@ namespace fsdp {
 
 // Tile lengths in elements.  Multiples of 8 so every tile of a run starts at
 // the same offset modulo 16 bytes as the run itself.
-constexpr int64_t kTilePack = 16384;
-constexpr int64_t kTileUnpack = 32768;
-constexpr int64_t kTileReduce = 4096;
-constexpr int64_t kTileAdamw = 8192;
+#ifndef FSDP_TILE_PACK
+#define FSDP_TILE_PACK 16384
+#endif
+#ifndef FSDP_TILE_UNPACK
+#define FSDP_TILE_UNPACK 32768
+#endif
+#ifndef FSDP_TILE_REDUCE
+#define FSDP_TILE_REDUCE 4096
+#endif
+#ifndef FSDP_TILE_ADAMW
+#define FSDP_TILE_ADAMW 8192
+#endif
+constexpr int64_t kTilePack = FSDP_TILE_PACK;
+constexpr int64_t kTileUnpack = FSDP_TILE_UNPACK;
+constexpr int64_t kTileReduce = FSDP_TILE_REDUCE;
+constexpr int64_t kTileAdamw = FSDP_TILE_ADAMW;
 
 // Device-side per-parameter record (64 bytes): the bound tensors.
 struct DevEntry {

@@ -120,6 +120,12 @@ class ShardedGroup:
               weight_decay: float, stream=None) -> None:
         capi.fsdp_adamw_shard(self.plan, lr, beta1, beta2, eps, weight_decay, step, stream)
 
+    def step(self, rs_in, ag_in, step: int, lr: float, beta1: float, beta2: float, eps: float,
+             weight_decay: float, write_grad: bool = False, stream=None) -> None:
+        """Fused reduce -> AdamW -> pack (bit-identical to the three calls)."""
+        capi.fsdp_step_shard(self.plan, rs_in, ag_in, lr, beta1, beta2, eps, weight_decay, step,
+                             capi.FSDP_STEP_WRITE_GRAD if write_grad else 0, stream)
+
     def close(self) -> None:
         if self.plan is not None:
             capi.fsdp_plan_destroy(self.plan)

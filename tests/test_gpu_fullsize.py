@@ -102,14 +102,15 @@ def test_roundtrip_pack_unpack_every_element(cfg_index, which):
     g0.close()
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
 @pytest.mark.parametrize("cfg_index,which", CASES, ids=[f"c{c}-{w}" for c, w in CASES])
-def test_step_sampled_against_oracle(cfg_index, which):
+def test_step_sampled_against_oracle(cfg_index, which, fused):
     cfg, gs = _groups(cfg_index)
     gi, grp = gs[0] if which == "block" else gs[1]
     shapes = [p.shape for p in grp.params]
     n, r = cfg.world, cfg.timing_rank
     hp = vars(cfg.hp)
-    print(f"[fullsize] step cfg={cfg_index} group={gi} n={n} r={r}", flush=True)
+    print(f"[fullsize] step cfg={cfg_index} group={gi} n={n} r={r} fused={fused}", flush=True)
     g = ShardedGroup(shapes, n, r)
     S = g.S
     for i, e in enumerate(g.entries):
@@ -124,7 +125,10 @@ def test_step_sampled_against_oracle(cfg_index, which):
     for t in (1, 2, 3):
         synth.fill_normal_bf16_bits_(rs, 1e-3, ("fs-rs", cfg_index, gi, t))
         synth.fill_normal_bf16_bits_(ag, 0.02, ("fs-ag", cfg_index, gi, t))
-        g.reduce(rs)
+        if fused:
+            g.step(rs, ag[r * S:(r + 1) * S], t, write_grad=True, **hp)
+        else:
+            g.reduce(rs)
         torch.cuda.synchronize()
         rs2 = rs.view(n, S)
         for i, e in enumerate(g.entries):
@@ -135,8 +139,9 @@ def test_step_sampled_against_oracle(cfg_index, which):
             got = g.shard_view(g.grad_flat, i)[tidx[i]].cpu().numpy()
             assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), ("grad", i, t)
             O.adamw(host_p[i], want, host_m[i], host_v[i], t, **hp)
-        g.adamw(t, **hp)
-        g.pack(ag[r * S:(r + 1) * S])
+        if not fused:
+            g.adamw(t, **hp)
+            g.pack(ag[r * S:(r + 1) * S])
         g.unpack(ag)
         torch.cuda.synchronize()
         row = ag.view(n, S)[r]

@@ -430,3 +430,101 @@ def test_empty_group_calls_are_no_ops():
     g.unpack(torch.zeros(1, dtype=torch.int16, device=DEV))
     capi.fsdp_check_stream()
     g.close()
+
+
+# ---------------------------------------------------------------------------
+# fused step: reduce -> AdamW -> pack in one pass
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("write_grad", [False, True], ids=["nograd", "grad"])
+@pytest.mark.parametrize("case", range(len(CASES)), ids=_case_ids())
+def test_fused_step_equals_separate_calls_and_oracle(case, write_grad):
+    name, shapes, n = CASES[case]
+    hp = HP
+    for r in sorted({0, n - 1}):
+        plan = O.plan(shapes, n, r)
+        ga, gb = ShardedGroup(shapes, n, r), ShardedGroup(shapes, n, r)
+        _fill_masters(ga, ("fused", name, r))
+        gb.master_flat.copy_(ga.master_flat)
+        masters = [f32(ga.shard_view(ga.master_flat, i)) for i in range(len(shapes))]
+        ms = [np.zeros_like(x) for x in masters]
+        vs = [np.zeros_like(x) for x in masters]
+        for t in (1, 2, 3):
+            rs = _rs_input(plan, n, ("fused-rs", name, r, t))
+            d_rs = torch.from_numpy(rs.reshape(-1).view(np.int16)).to(DEV)
+            off = t - 1            # ag_in at 0, 2 and 4 bytes past a 16-byte boundary
+            aga = torch.full((plan.S + 16,), 7, dtype=torch.int16, device=DEV)
+            agb = torch.full((plan.S + 16,), 7, dtype=torch.int16, device=DEV)
+            ga.reduce(d_rs)
+            ga.adamw(t, **hp)
+            ga.pack(aga[off:off + plan.S])
+            gb.grad_flat.fill_(-1.0)
+            gb.step(d_rs, agb[off:off + plan.S], t, write_grad=write_grad, **hp)
+            torch.cuda.synchronize()
+            assert torch.equal(aga, agb), (name, r, t)
+            for fl in ("master_flat", "m_flat", "v_flat"):
+                assert torch.equal(getattr(ga, fl).view(torch.int32), getattr(gb, fl).view(torch.int32))
+            grads = O.reduce(plan, rs)
+            for x, gr, m, v in zip(masters, grads, ms, vs):
+                O.adamw(x, gr, m, v, t, **hp)
+            assert np.array_equal(u16(agb)[off:off + plan.S], O.pack(plan, masters))
+            for i in range(len(shapes)):
+                _cmp_f32(f32(gb.shard_view(gb.master_flat, i)), masters[i], ("p", name, r, t, i))
+                got_g = f32(gb.shard_view(gb.grad_flat, i))
+                if write_grad:
+                    _cmp_f32(got_g, grads[i], ("g", name, r, t, i))
+                else:
+                    assert (got_g == -1.0).all(), "grad written without the flag"
+        ga.close()
+        gb.close()
+
+
+def test_fused_step_mixed_alignment_shards():
+    """Shards whose pointers differ modulo 16 take the element-wise path."""
+    shapes, n, r = [(41, 9), (777,), (3, 5)], 3, 1
+    plan = O.plan(shapes, n, r)
+    g = ShardedGroup(shapes, n, r, bind=False)
+    bufs = [torch.zeros(plan.V + 64, dtype=torch.float32, device=DEV) for _ in range(4)]
+    views = [[], [], [], []]
+    for role in range(4):
+        o = 1 + role
+        for e in g.entries:
+            views[role].append(bufs[role][o:o + e.valid_numel])
+            o += e.valid_numel + 5
+    host = []
+    for i, e in enumerate(g.entries):
+        p0 = synth.normal_f32(e.valid_numel, 0.02, ("fm", i))
+        views[0][i].copy_(p0)
+        host.append(p0.numpy().copy())
+    capi.fsdp_bind(g.plan, *[[v.data_ptr() for v in views[role]] for role in range(4)], None)
+    ms = [np.zeros_like(x) for x in host]
+    vs = [np.zeros_like(x) for x in host]
+    for t in (1, 2):
+        rs = _rs_input(plan, n, ("fm-rs", t))
+        ag = torch.zeros(plan.S + 8, dtype=torch.int16, device=DEV)
+        g.step(torch.from_numpy(rs.reshape(-1).view(np.int16)).to(DEV), ag[3:3 + plan.S], t,
+               write_grad=True, **HP)
+        torch.cuda.synchronize()
+        grads = O.reduce(plan, rs)
+        for x, gr, m, v in zip(host, grads, ms, vs):
+            O.adamw(x, gr, m, v, t, **HP)
+        assert np.array_equal(u16(ag)[3:3 + plan.S], O.pack(plan, host))
+        for i in range(len(shapes)):
+            _cmp_f32(f32(views[0][i]), host[i], ("p", t, i))
+            _cmp_f32(f32(views[1][i]), grads[i], ("g", t, i))
+            _cmp_f32(f32(views[2][i]), ms[i], ("m", t, i))
+            _cmp_f32(f32(views[3][i]), vs[i], ("v", t, i))
+    g.close()
+
+
+def test_fused_step_rejects_unbound_and_bad_flags():
+    g = ShardedGroup([(8, 4)], 2, 0)
+    rs = torch.zeros(2 * g.S, dtype=torch.int16, device=DEV)
+    ag = torch.zeros(g.S, dtype=torch.int16, device=DEV)
+    with pytest.raises(capi.FsdpError) as ei:
+        capi.fsdp_step_shard(g.plan, rs, ag, 3e-4, 0.9, 0.999, 1e-8, 0.01, 1, flags=2)
+    assert ei.value.status == capi.FSDP_E_INVAL
+    with pytest.raises(capi.FsdpError) as ei:
+        capi.fsdp_step_shard(g.plan, rs, ag, 3e-4, 0.9, 0.999, 1e-8, 0.01, 0)
+    assert ei.value.status == capi.FSDP_E_INVAL
+    g.close()
