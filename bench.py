@@ -23,6 +23,7 @@ three launches.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -48,6 +49,30 @@ def algorithmic_bytes(S, V, F, N, fused):
         return {"step": 2 * N * V + 24 * V + 2 * S, "unpack": 4 * F}
     return {"reduce": 2 * N * V + 4 * V, "adamw": 28 * V, "pack": 4 * V + 2 * S,
             "unpack": 4 * F}
+
+
+KERNEL_SYMBOLS = {"step": "step_kernel", "reduce": "reduce_kernel", "adamw": "adamw_kernel",
+                  "pack": "pack_kernel", "unpack": "unpack_kernel"}
+
+
+def measured_traffic(workload, rank, align, kind):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (profiles/pmc_traffic.json), or None when there is none for this kernel
+    and workload or the kernel source has changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    src = os.path.join(ROOT, "sharded_shard_amd", "csrc", "kernels.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernels_source_sha256") != sha:
+        return None
+    wl = rec.get("workloads", {}).get(workload)
+    if not wl or wl.get("rank") != rank or wl.get("align_elems") != align:
+        return None
+    k = wl.get("kernels", {}).get(KERNEL_SYMBOLS[kind])
+    return None if k is None else k["traffic_bytes_per_launch"]
 
 
 KERNEL_NAMES = {"step": "step_kernel (fused reduce+adamw+pack)", "reduce": "reduce_kernel",
@@ -141,7 +166,8 @@ def cpu_baseline(cfg, rank, min_s=10.0, max_s=30.0):
         "unit": "params/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"one step of groups {names} of {cfg.name}, rank {rank}: {total_v} params "
+        "sample": (f"one step of {len(names)} groups ({names[0]}, {names[-1]}, ...) of {cfg.name}, "
+                   f"rank {rank}: {total_v} params "
                    f"in {total_t:.2f} s (NumPy, single thread; host has {os.cpu_count()} cpus, "
                    f"affinity {len(os.sched_getaffinity(0))})"),
     }
@@ -295,7 +321,8 @@ def main():
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "roofline": {"bound": "hbm", "kernel": KERNEL_NAMES[dominant],
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(cfg.name, rank, args.align, dominant),
                      "avg_launch_ms": dom_avg_ms, "launches": dom_launches,
                      "algorithmic_bytes_per_launch": dom_bytes_per_launch},
         "kernels": kernels,
