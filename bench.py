@@ -92,7 +92,7 @@ def parse():
                     help="run reduce, adamw and pack as three launches instead of the fused step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown-steps", type=int, default=3,
-                    help="extra untimed steps with events around every kernel")
+                    help="extra untimed steps per kernel kind, with events around its launches")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device-to-device copy of 2 GiB instead (the "
                          "reference for HBM byte counters and the copy ceiling)")
@@ -185,6 +185,7 @@ def main():
         print(json.dumps(copy_calibration()), flush=True)
         return
 
+    from sharded_shard_amd import capi
     from sharded_shard_amd.group import ShardedGroup
     from workloads import configs, synth
 
@@ -229,67 +230,68 @@ def main():
 
     stream = torch.cuda.current_stream()
     step_counter = [0]
+    # One native call per step runs every group's launches (no per-launch
+    # Python on the critical path); HIP events around one kernel kind per
+    # group are recorded by the library on the same stream.
+    execute = capi.StepGroupsCall(
+        [g.plan for g in groups],
+        [rs_arena[gi & 1][:n * g.S] for gi, g in enumerate(groups)],
+        [ag_arena[gi & 1][rank * g.S:(rank + 1) * g.S] for gi, g in enumerate(groups)],
+        [ag_arena[gi & 1][:n * g.S] for gi, g in enumerate(groups)],
+        flags=0 if fused else capi.FSDP_STEP_UNFUSED, stream=stream, **hp)
+    kernel_id = {"step": capi.FSDP_KERNEL_STEP, "reduce": capi.FSDP_KERNEL_REDUCE,
+                 "adamw": capi.FSDP_KERNEL_ADAMW, "pack": capi.FSDP_KERNEL_PACK,
+                 "unpack": capi.FSDP_KERNEL_UNPACK}
 
-    def calls(gi, g, t):
-        rs = rs_arena[gi & 1][:n * g.S]
-        ag = ag_arena[gi & 1][:n * g.S]
-        row = ag[rank * g.S:(rank + 1) * g.S]
-        if fused:
-            return [("step", lambda: g.step(rs, row, t, stream=stream, **hp)),
-                    ("unpack", lambda: g.unpack(ag, stream))]
-        return [("reduce", lambda: g.reduce(rs, stream)),
-                ("adamw", lambda: g.adamw(t, stream=stream, **hp)),
-                ("pack", lambda: g.pack(row, stream)),
-                ("unpack", lambda: g.unpack(ag, stream))]
+    def new_events():
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(groups))]
+        for e in evs:          # create the underlying hipEvents now
+            e.record(stream)
+        return evs
 
-    def step(timed=None, every=None):
-        """One sharded step; events around `timed` kernels or around every kernel."""
+    def step(kind=None, evs=None):
         step_counter[0] += 1
-        t = step_counter[0]
-        for gi, g in enumerate(groups):
-            for name, fn in calls(gi, g, t):
-                if (every is not None) or (timed is not None and name == dominant):
-                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    a.record(stream)
-                    fn()
-                    b.record(stream)
-                    (every if every is not None else timed).append((name, a, b))
-                else:
-                    fn()
+        if kind is None:
+            execute(step_counter[0])
+        else:
+            execute(step_counter[0], kernel_id[kind], evs)
+
+    def elapsed(evs):
+        return [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(len(groups))]
 
     for _ in range(args.warmup):
         step()
+    timed_events = [new_events() for _ in range(args.steps)]
     torch.cuda.synchronize()
     print(f"bench: {args.warmup} warmup steps done", file=sys.stderr, flush=True)
 
-    dom_events = []
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     start.record(stream)
-    for _ in range(args.steps):
-        step(timed=dom_events)
+    for k in range(args.steps):
+        step(dominant, timed_events[k])
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_step = start.elapsed_time(end) / args.steps
     print(f"bench: {args.steps} timed steps, {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
-    dom_ms = sum(a.elapsed_time(b) for _, a, b in dom_events)
-    dom_launches = len(dom_events)
-    dom_avg_ms = dom_ms / max(1, dom_launches)
+    dom = [x for evs in timed_events for x in elapsed(evs)]
+    dom_launches = len(dom)
+    dom_avg_ms = sum(dom) / max(1, dom_launches)
     dom_bytes_per_launch = byts[dominant] / len(groups)
     achieved = dom_bytes_per_launch / (dom_avg_ms * 1e-3) / 1e9
 
-    # per-kernel breakdown (extra untimed steps, events around every launch)
+    # per-kernel breakdown: extra untimed steps, each timing one kernel kind
     per = {k: 0.0 for k in kinds}
     if args.breakdown_steps > 0:
-        evs = []
-        for _ in range(args.breakdown_steps):
-            step(every=evs)
+        runs = {k: [new_events() for _ in range(args.breakdown_steps)] for k in kinds}
         torch.cuda.synchronize()
-        for name, a, b in evs:
-            per[name] += a.elapsed_time(b)
-        per = {k: v / args.breakdown_steps for k, v in per.items()}
+        for k in kinds:
+            for evs in runs[k]:
+                step(k, evs)
+        torch.cuda.synchronize()
+        per = {k: sum(sum(elapsed(evs)) for evs in runs[k]) / args.breakdown_steps for k in kinds}
     kernels = {k: {"ms_per_step": round(per[k], 4),
                    "algorithmic_GB_per_step": round(byts[k] / 1e9, 4),
                    "GBps": round(byts[k] / (per[k] * 1e-3) / 1e9, 1) if per[k] else None,

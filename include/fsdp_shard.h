@@ -238,8 +238,17 @@ fsdp_status fsdp_adamw_shard(const fsdp_plan *plan,
                              const fsdp_adamw_hparams_t *hp, int64_t step,
                              void *stream);
 
-/* Flags of fsdp_step_shard. */
-enum { FSDP_STEP_WRITE_GRAD = 1 };
+/* Flags of fsdp_step_shard and fsdp_step_groups. */
+enum { FSDP_STEP_WRITE_GRAD = 1, FSDP_STEP_UNFUSED = 2 };
+
+/* Kernel selectors for the timing hooks of fsdp_step_groups. */
+enum {
+    FSDP_KERNEL_STEP = 0,
+    FSDP_KERNEL_REDUCE = 1,
+    FSDP_KERNEL_ADAMW = 2,
+    FSDP_KERNEL_PACK = 3,
+    FSDP_KERNEL_UNPACK = 4
+};
 
 /* Fused sharded step: reduce -> AdamW -> copy-in in one pass over this
  * rank's pieces.  Per valid element it computes the reduced gradient exactly
@@ -261,6 +270,32 @@ enum { FSDP_STEP_WRITE_GRAD = 1 };
 fsdp_status fsdp_step_shard(const fsdp_plan *plan, const uint16_t *rs_in,
                             uint16_t *ag_in, const fsdp_adamw_hparams_t *hp,
                             int64_t step, uint32_t flags, void *stream);
+
+/* One rank's whole sharded step over n_groups parameter groups, launched
+ * from native code in group order on one stream (one call instead of two to
+ * four per group, so host launch overhead cannot starve the GPU).  For group
+ * g: fsdp_step_shard(plans[g], rs_in[g], ag_in[g], ...) -- or, with
+ * FSDP_STEP_UNFUSED, fsdp_reduce_shard, fsdp_adamw_shard and
+ * fsdp_pack_allgather -- then, unless ag_out is NULL,
+ * fsdp_unpack_allgather(plans[g], ag_out[g]).  Results equal those calls
+ * made one by one.  [MS] "Working Principle" (per-group reduce-scatter,
+ * sharded update, all-gather before the next use); [ST] fully_shard
+ * paragraph (one group = one communication unit).
+ *   plans, rs_in, ag_in, ag_out  host arrays of n_groups entries (device
+ *                                buffers as in the single-group calls)
+ *   timing_events  NULL, or 2*n_groups hipEvent_t (as void*): events 2g and
+ *                  2g+1 are recorded on `stream` just before and after group
+ *                  g's launch of kernel `timed_kernel` (FSDP_KERNEL_*), which
+ *                  must be one this call runs
+ * Every group is checked before anything is launched.  Errors: as the
+ * single-group calls, plus FSDP_E_INVAL for null arrays, unknown flags or a
+ * timed kernel the call does not run. */
+fsdp_status fsdp_step_groups(fsdp_plan *const *plans, int32_t n_groups,
+                             const uint16_t *const *rs_in, uint16_t *const *ag_in,
+                             const uint16_t *const *ag_out,
+                             const fsdp_adamw_hparams_t *hp, int64_t step,
+                             uint32_t flags, int32_t timed_kernel,
+                             void *const *timing_events, void *stream);
 
 /* Wait for `stream` and report any asynchronous HIP error as FSDP_E_HIP. */
 fsdp_status fsdp_check_stream(void *stream);

@@ -31,6 +31,13 @@ FSDP_ROLE_EXP_AVG_SQ = 8
 FSDP_ROLE_FULL = 16
 
 FSDP_STEP_WRITE_GRAD = 1
+FSDP_STEP_UNFUSED = 2
+
+FSDP_KERNEL_STEP = 0
+FSDP_KERNEL_REDUCE = 1
+FSDP_KERNEL_ADAMW = 2
+FSDP_KERNEL_PACK = 3
+FSDP_KERNEL_UNPACK = 4
 
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
@@ -90,6 +97,8 @@ _SIGS = {
     "fsdp_reduce_shard": (_i32, [_P, _P, _P]),
     "fsdp_adamw_shard": (_i32, [_P, ctypes.POINTER(AdamwHparams), _i64, _P]),
     "fsdp_step_shard": (_i32, [_P, _P, _P, ctypes.POINTER(AdamwHparams), _i64, ctypes.c_uint32, _P]),
+    "fsdp_step_groups": (_i32, [_PP, _i32, _PP, _PP, _PP, ctypes.POINTER(AdamwHparams), _i64,
+                                ctypes.c_uint32, _i32, _PP, _P]),
     "fsdp_check_stream": (_i32, [_P]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -227,6 +236,44 @@ def fsdp_step_shard(plan, rs_in, ag_in, lr: float, beta1: float, beta2: float, e
     hp = AdamwHparams(lr, beta1, beta2, eps, weight_decay)
     _check(lib.fsdp_step_shard(plan, addr(rs_in), addr(ag_in), ctypes.byref(hp), step, flags,
                                stream_handle(stream)), "fsdp_step_shard")
+
+
+class StepGroupsCall:
+    """fsdp_step_groups with its pointer arrays marshalled once.
+
+    plans: plan handles; rs_in, ag_in, ag_out: tensors/addresses per group
+    (ag_out may be None to skip the copy-out).  Each call() passes only the
+    step index, so the per-step host cost is one ctypes call.
+    """
+
+    def __init__(self, plans, rs_in, ag_in, ag_out, lr, beta1, beta2, eps, weight_decay,
+                 flags=0, stream=None):
+        n = len(plans)
+        self.n = n
+        self._plans = (ctypes.c_void_p * max(1, n))(*[p.value for p in plans])
+        self._rs = _ptr_array(rs_in)
+        self._ag_in = _ptr_array(ag_in)
+        self._ag_out = _ptr_array(ag_out) if ag_out is not None else None
+        self._keep = (rs_in, ag_in, ag_out)
+        self._hp = AdamwHparams(lr, beta1, beta2, eps, weight_decay)
+        self.flags = flags
+        self._stream = stream_handle(stream)
+
+    def __call__(self, step: int, timed_kernel: int = 0, events=None) -> None:
+        ev = None
+        if events is not None:
+            ev = (ctypes.c_void_p * len(events))(*[int(e.cuda_event) for e in events])
+            ev = ctypes.cast(ev, _PP)
+        _check(lib.fsdp_step_groups(ctypes.cast(self._plans, _PP), self.n, self._rs, self._ag_in,
+                                    self._ag_out, ctypes.byref(self._hp), step, self.flags,
+                                    timed_kernel, ev, self._stream), "fsdp_step_groups")
+
+
+def fsdp_step_groups(plans, rs_in, ag_in, ag_out, lr: float, beta1: float, beta2: float,
+                     eps: float, weight_decay: float, step: int, flags: int = 0,
+                     timed_kernel: int = 0, timing_events=None, stream=None) -> None:
+    StepGroupsCall(plans, rs_in, ag_in, ag_out, lr, beta1, beta2, eps, weight_decay, flags,
+                   stream)(step, timed_kernel, timing_events)
 
 
 def fsdp_check_stream(stream=None) -> None:

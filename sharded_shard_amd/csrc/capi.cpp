@@ -313,78 +313,210 @@ fsdp_status fsdp_bind(fsdp_plan *p, float *const *master, float *const *grad,
     return FSDP_OK;
 }
 
-fsdp_status fsdp_pack_allgather(const fsdp_plan *p, uint16_t *ag_in, void *stream) {
-    fsdp_status s = need_roles(p, FSDP_ROLE_MASTER, "fsdp_pack_allgather");
+}  // extern "C"
+
+// ---- hot path: host-side checks (no HIP call), then launches ----------------
+
+namespace {
+
+constexpr int32_t kAdamwRoles =
+    FSDP_ROLE_MASTER | FSDP_ROLE_GRAD | FSDP_ROLE_EXP_AVG | FSDP_ROLE_EXP_AVG_SQ;
+
+fsdp_status check_buf(const fsdp_plan *p, const void *buf, const char *call, const char *name) {
+    if (buf == nullptr && p->L.S > 0)
+        return fail(FSDP_E_INVAL, std::string(call) + ": null " + name);
+    if (misaligned(buf, 2))
+        return fail(FSDP_E_ALIGN, std::string(call) + ": " + name + " not 2-byte aligned");
+    return FSDP_OK;
+}
+
+fsdp_status check_pack(const fsdp_plan *p, const uint16_t *ag_in, const char *call) {
+    fsdp_status s = need_roles(p, FSDP_ROLE_MASTER, call);
+    return s != FSDP_OK ? s : check_buf(p, ag_in, call, "ag_in");
+}
+
+fsdp_status check_unpack(const fsdp_plan *p, const uint16_t *ag_out, const char *call) {
+    fsdp_status s = need_roles(p, FSDP_ROLE_FULL, call);
+    return s != FSDP_OK ? s : check_buf(p, ag_out, call, "ag_out");
+}
+
+fsdp_status check_reduce(const fsdp_plan *p, const uint16_t *rs_in, const char *call) {
+    fsdp_status s = need_roles(p, FSDP_ROLE_GRAD, call);
+    return s != FSDP_OK ? s : check_buf(p, rs_in, call, "rs_in");
+}
+
+fsdp_status check_hparams(const fsdp_adamw_hparams_t *hp, int64_t step, const char *call) {
+    if (hp == nullptr) return fail(FSDP_E_INVAL, std::string(call) + ": null hyperparameters");
+    if (step < 1) return fail(FSDP_E_INVAL, std::string(call) + ": step counts from 1");
+    return FSDP_OK;
+}
+
+fsdp_status check_step(const fsdp_plan *p, const uint16_t *rs_in, const uint16_t *ag_in,
+                       bool write_grad, const char *call) {
+    const int32_t roles = FSDP_ROLE_MASTER | FSDP_ROLE_EXP_AVG | FSDP_ROLE_EXP_AVG_SQ |
+                          (write_grad ? FSDP_ROLE_GRAD : 0);
+    fsdp_status s = need_roles(p, roles, call);
     if (s != FSDP_OK) return s;
-    if (ag_in == nullptr && p->L.S > 0) return fail(FSDP_E_INVAL, "fsdp_pack_allgather: null ag_in");
-    if (misaligned(ag_in, 2)) return fail(FSDP_E_ALIGN, "fsdp_pack_allgather: ag_in not 2-byte aligned");
-    if ((s = check_device(p)) != FSDP_OK) return s;
-    hipError_t e = fsdp::launch_pack(p->d_pack, static_cast<int64_t>(p->L.pack.size()),
-                                     p->d_entries, ag_in, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? FSDP_OK : hip_fail(e, "fsdp_pack_allgather: launch");
+    if ((s = check_buf(p, rs_in, call, "rs_in")) != FSDP_OK) return s;
+    return check_buf(p, ag_in, call, "ag_in");
+}
+
+hipError_t do_pack(const fsdp_plan *p, uint16_t *ag_in, hipStream_t st) {
+    return fsdp::launch_pack(p->d_pack, static_cast<int64_t>(p->L.pack.size()), p->d_entries,
+                             ag_in, st);
+}
+
+hipError_t do_unpack(const fsdp_plan *p, const uint16_t *ag_out, hipStream_t st) {
+    return fsdp::launch_unpack(p->d_unpack, static_cast<int64_t>(p->L.unpack.size()),
+                               p->d_entries, ag_out, st);
+}
+
+hipError_t do_reduce(const fsdp_plan *p, const uint16_t *rs_in, hipStream_t st) {
+    return fsdp::launch_reduce(p->d_reduce, static_cast<int64_t>(p->L.reduce.size()),
+                               p->d_entries, rs_in, p->L.S, p->L.world, st);
+}
+
+hipError_t do_adamw(const fsdp_plan *p, const float scal[8], hipStream_t st) {
+    return fsdp::launch_adamw(p->d_adamw, static_cast<int64_t>(p->L.adamw.size()), p->d_entries,
+                              scal, st);
+}
+
+hipError_t do_step(const fsdp_plan *p, const uint16_t *rs_in, uint16_t *ag_in,
+                   const float scal[8], bool write_grad, hipStream_t st) {
+    return fsdp::launch_step(p->d_pack, static_cast<int64_t>(p->L.pack.size()), p->d_entries,
+                             rs_in, ag_in, p->L.S, p->L.world, scal, write_grad, st);
+}
+
+fsdp_status launched(hipError_t e, const char *call) {
+    return e == hipSuccess ? FSDP_OK : hip_fail(e, call);
+}
+
+}  // namespace
+
+extern "C" {
+
+fsdp_status fsdp_pack_allgather(const fsdp_plan *p, uint16_t *ag_in, void *stream) {
+    fsdp_status s = check_pack(p, ag_in, "fsdp_pack_allgather");
+    if (s != FSDP_OK || (s = check_device(p)) != FSDP_OK) return s;
+    return launched(do_pack(p, ag_in, static_cast<hipStream_t>(stream)),
+                    "fsdp_pack_allgather: launch");
 }
 
 fsdp_status fsdp_unpack_allgather(const fsdp_plan *p, const uint16_t *ag_out, void *stream) {
-    fsdp_status s = need_roles(p, FSDP_ROLE_FULL, "fsdp_unpack_allgather");
-    if (s != FSDP_OK) return s;
-    if (ag_out == nullptr && p->L.S > 0) return fail(FSDP_E_INVAL, "fsdp_unpack_allgather: null ag_out");
-    if (misaligned(ag_out, 2)) return fail(FSDP_E_ALIGN, "fsdp_unpack_allgather: ag_out not 2-byte aligned");
-    if ((s = check_device(p)) != FSDP_OK) return s;
-    hipError_t e = fsdp::launch_unpack(p->d_unpack, static_cast<int64_t>(p->L.unpack.size()),
-                                       p->d_entries, ag_out, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? FSDP_OK : hip_fail(e, "fsdp_unpack_allgather: launch");
+    fsdp_status s = check_unpack(p, ag_out, "fsdp_unpack_allgather");
+    if (s != FSDP_OK || (s = check_device(p)) != FSDP_OK) return s;
+    return launched(do_unpack(p, ag_out, static_cast<hipStream_t>(stream)),
+                    "fsdp_unpack_allgather: launch");
 }
 
 fsdp_status fsdp_reduce_shard(const fsdp_plan *p, const uint16_t *rs_in, void *stream) {
-    fsdp_status s = need_roles(p, FSDP_ROLE_GRAD, "fsdp_reduce_shard");
-    if (s != FSDP_OK) return s;
-    if (rs_in == nullptr && p->L.S > 0) return fail(FSDP_E_INVAL, "fsdp_reduce_shard: null rs_in");
-    if (misaligned(rs_in, 2)) return fail(FSDP_E_ALIGN, "fsdp_reduce_shard: rs_in not 2-byte aligned");
-    if ((s = check_device(p)) != FSDP_OK) return s;
-    hipError_t e = fsdp::launch_reduce(p->d_reduce, static_cast<int64_t>(p->L.reduce.size()),
-                                       p->d_entries, rs_in, p->L.S, p->L.world,
-                                       static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? FSDP_OK : hip_fail(e, "fsdp_reduce_shard: launch");
+    fsdp_status s = check_reduce(p, rs_in, "fsdp_reduce_shard");
+    if (s != FSDP_OK || (s = check_device(p)) != FSDP_OK) return s;
+    return launched(do_reduce(p, rs_in, static_cast<hipStream_t>(stream)),
+                    "fsdp_reduce_shard: launch");
 }
 
 fsdp_status fsdp_adamw_shard(const fsdp_plan *p, const fsdp_adamw_hparams_t *hp,
                              int64_t step, void *stream) {
-    const int32_t roles = FSDP_ROLE_MASTER | FSDP_ROLE_GRAD | FSDP_ROLE_EXP_AVG | FSDP_ROLE_EXP_AVG_SQ;
-    fsdp_status s = need_roles(p, roles, "fsdp_adamw_shard");
-    if (s != FSDP_OK) return s;
-    if (hp == nullptr) return fail(FSDP_E_INVAL, "fsdp_adamw_shard: null hyperparameters");
-    if (step < 1) return fail(FSDP_E_INVAL, "fsdp_adamw_shard: step counts from 1");
-    if ((s = check_device(p)) != FSDP_OK) return s;
+    fsdp_status s = need_roles(p, kAdamwRoles, "fsdp_adamw_shard");
+    if (s != FSDP_OK || (s = check_hparams(hp, step, "fsdp_adamw_shard")) != FSDP_OK ||
+        (s = check_device(p)) != FSDP_OK)
+        return s;
     float scal[8];
     adamw_scalars(hp, step, scal);
-    hipError_t e = fsdp::launch_adamw(p->d_adamw, static_cast<int64_t>(p->L.adamw.size()),
-                                      p->d_entries, scal, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? FSDP_OK : hip_fail(e, "fsdp_adamw_shard: launch");
+    return launched(do_adamw(p, scal, static_cast<hipStream_t>(stream)),
+                    "fsdp_adamw_shard: launch");
 }
 
 fsdp_status fsdp_step_shard(const fsdp_plan *p, const uint16_t *rs_in, uint16_t *ag_in,
                             const fsdp_adamw_hparams_t *hp, int64_t step, uint32_t flags,
                             void *stream) {
+    const char *call = "fsdp_step_shard";
     const bool write_grad = (flags & FSDP_STEP_WRITE_GRAD) != 0;
-    const int32_t roles = FSDP_ROLE_MASTER | FSDP_ROLE_EXP_AVG | FSDP_ROLE_EXP_AVG_SQ |
-                          (write_grad ? FSDP_ROLE_GRAD : 0);
-    fsdp_status s = need_roles(p, roles, "fsdp_step_shard");
+    fsdp_status s = check_step(p, rs_in, ag_in, write_grad, call);
     if (s != FSDP_OK) return s;
     if ((flags & ~static_cast<uint32_t>(FSDP_STEP_WRITE_GRAD)) != 0)
         return fail(FSDP_E_INVAL, "fsdp_step_shard: unknown flag");
-    if (p->L.S > 0 && (rs_in == nullptr || ag_in == nullptr))
-        return fail(FSDP_E_INVAL, "fsdp_step_shard: null rs_in or ag_in");
-    if (misaligned(rs_in, 2) || misaligned(ag_in, 2))
-        return fail(FSDP_E_ALIGN, "fsdp_step_shard: rs_in or ag_in not 2-byte aligned");
-    if (hp == nullptr) return fail(FSDP_E_INVAL, "fsdp_step_shard: null hyperparameters");
-    if (step < 1) return fail(FSDP_E_INVAL, "fsdp_step_shard: step counts from 1");
-    if ((s = check_device(p)) != FSDP_OK) return s;
+    if ((s = check_hparams(hp, step, call)) != FSDP_OK || (s = check_device(p)) != FSDP_OK)
+        return s;
     float scal[8];
     adamw_scalars(hp, step, scal);
-    hipError_t e = fsdp::launch_step(p->d_pack, static_cast<int64_t>(p->L.pack.size()),
-                                     p->d_entries, rs_in, ag_in, p->L.S, p->L.world, scal,
-                                     write_grad, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? FSDP_OK : hip_fail(e, "fsdp_step_shard: launch");
+    return launched(do_step(p, rs_in, ag_in, scal, write_grad, static_cast<hipStream_t>(stream)),
+                    "fsdp_step_shard: launch");
+}
+
+fsdp_status fsdp_step_groups(fsdp_plan *const *plans, int32_t n_groups,
+                             const uint16_t *const *rs_in, uint16_t *const *ag_in,
+                             const uint16_t *const *ag_out, const fsdp_adamw_hparams_t *hp,
+                             int64_t step, uint32_t flags, int32_t timed_kernel,
+                             void *const *timing_events, void *stream) {
+    const char *call = "fsdp_step_groups";
+    if (n_groups < 0 || (n_groups > 0 && (plans == nullptr || rs_in == nullptr ||
+                                          ag_in == nullptr)))
+        return fail(FSDP_E_INVAL, "fsdp_step_groups: null array or negative n_groups");
+    const uint32_t known = FSDP_STEP_WRITE_GRAD | FSDP_STEP_UNFUSED;
+    if ((flags & ~known) != 0) return fail(FSDP_E_INVAL, "fsdp_step_groups: unknown flag");
+    const bool write_grad = (flags & FSDP_STEP_WRITE_GRAD) != 0;
+    const bool unfused = (flags & FSDP_STEP_UNFUSED) != 0;
+    if (timing_events != nullptr) {
+        const bool ok = timed_kernel == FSDP_KERNEL_UNPACK ||
+                        (unfused ? (timed_kernel == FSDP_KERNEL_REDUCE ||
+                                    timed_kernel == FSDP_KERNEL_ADAMW ||
+                                    timed_kernel == FSDP_KERNEL_PACK)
+                                 : timed_kernel == FSDP_KERNEL_STEP);
+        if (!ok || (timed_kernel == FSDP_KERNEL_UNPACK && ag_out == nullptr))
+            return fail(FSDP_E_INVAL, "fsdp_step_groups: timed_kernel is not run by this call");
+        for (int32_t g = 0; g < 2 * n_groups; ++g)
+            if (timing_events[g] == nullptr)
+                return fail(FSDP_E_INVAL, "fsdp_step_groups: null timing event");
+    }
+    fsdp_status s = check_hparams(hp, step, call);
+    if (s != FSDP_OK) return s;
+    for (int32_t g = 0; g < n_groups; ++g) {
+        const fsdp_plan *p = plans[g];
+        if (unfused) {
+            if ((s = check_reduce(p, rs_in[g], call)) != FSDP_OK ||
+                (s = need_roles(p, kAdamwRoles, call)) != FSDP_OK ||
+                (s = check_pack(p, ag_in[g], call)) != FSDP_OK)
+                return s;
+        } else if ((s = check_step(p, rs_in[g], ag_in[g], write_grad, call)) != FSDP_OK) {
+            return s;
+        }
+        if (ag_out != nullptr && (s = check_unpack(p, ag_out[g], call)) != FSDP_OK) return s;
+        if ((s = check_device(p)) != FSDP_OK) return s;
+    }
+    float scal[8];
+    adamw_scalars(hp, step, scal);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    auto mark = [&](int32_t g, int32_t kernel, int which) -> hipError_t {
+        if (timing_events == nullptr || kernel != timed_kernel) return hipSuccess;
+        return hipEventRecord(static_cast<hipEvent_t>(timing_events[2 * g + which]), st);
+    };
+    for (int32_t g = 0; g < n_groups; ++g) {
+        const fsdp_plan *p = plans[g];
+        hipError_t e = hipSuccess;
+        if (unfused) {
+            if ((e = mark(g, FSDP_KERNEL_REDUCE, 0)) == hipSuccess &&
+                (e = do_reduce(p, rs_in[g], st)) == hipSuccess &&
+                (e = mark(g, FSDP_KERNEL_REDUCE, 1)) == hipSuccess &&
+                (e = mark(g, FSDP_KERNEL_ADAMW, 0)) == hipSuccess &&
+                (e = do_adamw(p, scal, st)) == hipSuccess &&
+                (e = mark(g, FSDP_KERNEL_ADAMW, 1)) == hipSuccess &&
+                (e = mark(g, FSDP_KERNEL_PACK, 0)) == hipSuccess &&
+                (e = do_pack(p, ag_in[g], st)) == hipSuccess)
+                e = mark(g, FSDP_KERNEL_PACK, 1);
+        } else if ((e = mark(g, FSDP_KERNEL_STEP, 0)) == hipSuccess &&
+                   (e = do_step(p, rs_in[g], ag_in[g], scal, write_grad, st)) == hipSuccess) {
+            e = mark(g, FSDP_KERNEL_STEP, 1);
+        }
+        if (e == hipSuccess && ag_out != nullptr &&
+            (e = mark(g, FSDP_KERNEL_UNPACK, 0)) == hipSuccess &&
+            (e = do_unpack(p, ag_out[g], st)) == hipSuccess)
+            e = mark(g, FSDP_KERNEL_UNPACK, 1);
+        if (e != hipSuccess)
+            return hip_fail(e, ("fsdp_step_groups: group " + std::to_string(g)).c_str());
+    }
+    return FSDP_OK;
 }
 
 fsdp_status fsdp_check_stream(void *stream) {

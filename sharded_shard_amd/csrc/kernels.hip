@@ -71,6 +71,12 @@
 #ifndef FSDP_ROW_BATCH
 #define FSDP_ROW_BATCH 8
 #endif
+#ifndef FSDP_STEP_PREFETCH
+#define FSDP_STEP_PREFETCH 0
+#endif
+#ifndef FSDP_ROW_BLOCK_FIT
+#define FSDP_ROW_BLOCK_FIT 0
+#endif
 
 namespace fsdp {
 
@@ -300,7 +306,8 @@ __device__ __forceinline__ void zero_bf16(uint16_t *dst, int64_t from, int64_t l
     if (tid < head) d[tid] = 0;
     const int64_t nvec = (n - head) >> 3;
     u32x4 *dv = reinterpret_cast<u32x4 *>(d + head);
-    for (int64_t v = tid; v < nvec; v += kBlock) stp<SN>(dv + v, u32x4{0u, 0u, 0u, 0u});
+    const int nthr = blockDim.x;
+    for (int64_t v = tid; v < nvec; v += nthr) stp<SN>(dv + v, u32x4{0u, 0u, 0u, 0u});
     const int64_t done = head + (nvec << 3);
     if (tid < n - done) d[done + tid] = 0;
 }
@@ -460,7 +467,8 @@ __device__ __forceinline__ void reduce_run(float *__restrict__ dst, const uint16
     const uint32_t k0 = lo32(s0) & 15u;
     const uint32_t nbytes = static_cast<uint32_t>(2 * (len - head) + 48);
     f32x4 *dv = reinterpret_cast<f32x4 *>(dst + head);
-    for (int64_t g = tid; g < ngrp; g += kBlock) {
+    const int nthr = blockDim.x;
+    for (int64_t g = tid; g < ngrp; g += nthr) {
         float acc[8];
         sum_rows8<LN, kRowsAligned>(s0, static_cast<uint32_t>(g) << 4, nbytes, S, N, k0, kS, acc);
         stp<SN>(dv + 2 * g, f32x4{acc[0] / fN, acc[1] / fN, acc[2] / fN, acc[3] / fN});
@@ -625,7 +633,7 @@ __device__ __forceinline__ void step_run(const uint16_t *__restrict__ rs0, int64
     const bool same = ap == (lo32(M) & 15u) && ap == (lo32(Vv) & 15u) &&
                       (!kWriteGrad || ap == (lo32(G) & 15u));
     if (!same) {
-        for (int64_t e = tid; e < valid; e += kBlock)
+        for (int64_t e = tid; e < valid; e += static_cast<int64_t>(blockDim.x))
             step_scalar_at<kWriteGrad>(rs0, S, N, fN, P, M, Vv, G, dst, e, c);
     } else {
         int64_t head = ((16u - ap) & 15u) >> 2;
@@ -636,17 +644,28 @@ __device__ __forceinline__ void step_run(const uint16_t *__restrict__ rs0, int64
         const uint32_t k0 = lo32(rs0 + head) & 15u;
         const uint32_t ka = lo32(dst + head) & 15u;
         const uint32_t nbytes = static_cast<uint32_t>(2 * (valid - head) + 48);
-        for (int64_t g8 = tid; g8 < ngrp; g8 += kBlock) {
+        const int nthr = blockDim.x;
+        for (int64_t g8 = tid; g8 < ngrp; g8 += nthr) {
             const int64_t e0 = head + (g8 << 3);
-            float acc[8];
-            sum_rows8<1, kRowsAligned>(rs0 + head, static_cast<uint32_t>(g8) << 4, nbytes, S, N,
-                                       k0, kS, acc);
             f32x4 *pv = reinterpret_cast<f32x4 *>(P + e0);
             f32x4 *mv = reinterpret_cast<f32x4 *>(M + e0);
             f32x4 *vv = reinterpret_cast<f32x4 *>(Vv + e0);
+#if FSDP_STEP_PREFETCH
+            // the optimizer state streams in while the N rows are summed
             f32x4 p0 = ldp<LN>(pv), p1 = ldp<LN>(pv + 1);
             f32x4 m0 = ldp<LN>(mv), m1 = ldp<LN>(mv + 1);
             f32x4 v0 = ldp<LN>(vv), v1 = ldp<LN>(vv + 1);
+            float acc[8];
+            sum_rows8<1, kRowsAligned>(rs0 + head, static_cast<uint32_t>(g8) << 4, nbytes, S, N,
+                                       k0, kS, acc);
+#else
+            float acc[8];
+            sum_rows8<1, kRowsAligned>(rs0 + head, static_cast<uint32_t>(g8) << 4, nbytes, S, N,
+                                       k0, kS, acc);
+            f32x4 p0 = ldp<LN>(pv), p1 = ldp<LN>(pv + 1);
+            f32x4 m0 = ldp<LN>(mv), m1 = ldp<LN>(mv + 1);
+            f32x4 v0 = ldp<LN>(vv), v1 = ldp<LN>(vv + 1);
+#endif
             const f32x4 g0{acc[0] / fN, acc[1] / fN, acc[2] / fN, acc[3] / fN};
             const f32x4 g1{acc[4] / fN, acc[5] / fN, acc[6] / fN, acc[7] / fN};
             if (kWriteGrad) {
@@ -719,6 +738,18 @@ inline int32_t split_rows(int64_t tile, int32_t N, int32_t extra_rows) {
     return split_for(tile, want);
 }
 
+// Threads for the row kernels: one 8-element group per lane, whole waves,
+// at most kBlock (so a small sub-range does not leave idle waves).
+inline unsigned row_threads(int64_t sub) {
+#if FSDP_ROW_BLOCK_FIT
+    int64_t t = (sub / 8 + 63) / 64 * 64;
+    return static_cast<unsigned>(t < 64 ? 64 : (t > kBlock ? kBlock : t));
+#else
+    (void)sub;
+    return kBlock;
+#endif
+}
+
 AdamwScalars to_scalars(const float s[8]) {
     return AdamwScalars{s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7]};
 }
@@ -753,12 +784,13 @@ hipError_t launch_reduce(const ReduceTile *tiles, int64_t n, const DevEntry *ent
     const float fN = static_cast<float>(N);
     const int32_t sp = split_rows(kTileReduce, N, 0);
     const unsigned grid = grid_for(n, sp);
+    const unsigned thr = row_threads(kTileReduce / sp);
     if (((S * 2) & 15) == 0)
         reduce_kernel<FSDP_REDUCE_POL, true>
-            <<<grid, kBlock, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
+            <<<grid, thr, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
     else
         reduce_kernel<FSDP_REDUCE_POL, false>
-            <<<grid, kBlock, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
+            <<<grid, thr, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
     return hipGetLastError();
 }
 
@@ -781,16 +813,17 @@ hipError_t launch_step(const PackTile *tiles, int64_t n, const DevEntry *ents,
     const int32_t sp = split_rows(kTilePack, N, 6);
     const int64_t sub = kTilePack / sp;
     const unsigned grid = grid_for(n, sp);
+    const unsigned thr = row_threads(sub);
     const bool aligned = ((S * 2) & 15) == 0;
     constexpr int P = FSDP_STEP_POL;
     if (aligned && write_grad)
-        step_kernel<P, true, true><<<grid, kBlock, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N, fN, c);
+        step_kernel<P, true, true><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N, fN, c);
     else if (aligned)
-        step_kernel<P, true, false><<<grid, kBlock, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N, fN, c);
+        step_kernel<P, true, false><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N, fN, c);
     else if (write_grad)
-        step_kernel<P, false, true><<<grid, kBlock, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N, fN, c);
+        step_kernel<P, false, true><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N, fN, c);
     else
-        step_kernel<P, false, false><<<grid, kBlock, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N, fN, c);
+        step_kernel<P, false, false><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N, fN, c);
     return hipGetLastError();
 }
 

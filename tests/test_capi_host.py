@@ -184,3 +184,23 @@ def test_hot_calls_reject_unbound_and_bad_arguments_without_gpu():
     finally:
         capi.fsdp_plan_destroy(p)
     capi.fsdp_plan_destroy(None)
+
+
+def test_step_groups_rejects_bad_arguments_without_gpu():
+    p = capi.fsdp_plan_create([8, 3], [4, 1], 2, 0, 1)
+    try:
+        call = capi.StepGroupsCall([p], [0x1000], [0x2000], [0x3000], 3e-4, 0.9, 0.999, 1e-8,
+                                   0.01, stream=0)
+        with pytest.raises(capi.FsdpError) as ei:      # not bound
+            call(1)
+        assert ei.value.status == capi.FSDP_E_STATE
+        bad = capi.StepGroupsCall([p], [0x1000], [0x2000], [0x3000], 3e-4, 0.9, 0.999, 1e-8,
+                                  0.01, flags=8, stream=0)
+        with pytest.raises(capi.FsdpError) as ei:      # unknown flag
+            bad(1)
+        assert ei.value.status == capi.FSDP_E_INVAL
+        with pytest.raises(capi.FsdpError) as ei:      # step counts from 1
+            call(0)
+        assert ei.value.status == capi.FSDP_E_INVAL
+    finally:
+        capi.fsdp_plan_destroy(p)

@@ -528,3 +528,82 @@ def test_fused_step_rejects_unbound_and_bad_flags():
         capi.fsdp_step_shard(g.plan, rs, ag, 3e-4, 0.9, 0.999, 1e-8, 0.01, 0)
     assert ei.value.status == capi.FSDP_E_INVAL
     g.close()
+
+
+# ---------------------------------------------------------------------------
+# native multi-group executor
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("unfused", [False, True], ids=["fused", "unfused"])
+def test_step_groups_equals_per_group_calls(unfused):
+    n, r = 6, 5
+    group_shapes = [CASES[1][1], CASES[2][1], [(70001,), (300, 33)]]
+    A, B, rs_bufs, ag_a, ag_b = [], [], [], [], []
+    for gi, shapes in enumerate(group_shapes):
+        ga, gb = ShardedGroup(shapes, n, r), ShardedGroup(shapes, n, r)
+        _fill_masters(ga, ("exec", gi))
+        gb.master_flat.copy_(ga.master_flat)
+        plan = O.plan(shapes, n, r)
+        rs = _rs_input(plan, n, ("exec-rs", gi))
+        rs_bufs.append(torch.from_numpy(rs.reshape(-1).view(np.int16)).to(DEV))
+        other = torch.from_numpy(_rand_ag(n, plan.S, ("exec-ag", gi)).reshape(-1).view(np.int16)).to(DEV)
+        ag_a.append(other.clone())
+        ag_b.append(other.clone())
+        A.append(ga)
+        B.append(gb)
+    for t in (1, 2):
+        for gi, ga in enumerate(A):
+            S = ga.S
+            if unfused:
+                ga.reduce(rs_bufs[gi])
+                ga.adamw(t, **HP)
+                ga.pack(ag_a[gi][r * S:(r + 1) * S])
+            else:
+                ga.step(rs_bufs[gi], ag_a[gi][r * S:(r + 1) * S], t, **HP)
+            ga.unpack(ag_a[gi])
+        call = capi.StepGroupsCall([g.plan for g in B], rs_bufs,
+                                   [ag_b[gi][r * g.S:(r + 1) * g.S] for gi, g in enumerate(B)],
+                                   ag_b, flags=capi.FSDP_STEP_UNFUSED if unfused else 0, **HP)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(B))]
+        for e in evs:
+            e.record()
+        call(t, capi.FSDP_KERNEL_UNPACK, evs)
+        torch.cuda.synchronize()
+        assert all(evs[2 * i].elapsed_time(evs[2 * i + 1]) >= 0 for i in range(len(B)))
+        for ga, gb, aa, ab in zip(A, B, ag_a, ag_b):
+            assert torch.equal(aa, ab)
+            for fl in ("master_flat", "m_flat", "v_flat", "full_flat"):
+                x, y = getattr(ga, fl), getattr(gb, fl)
+                assert torch.equal(x.view(torch.int16), y.view(torch.int16)), fl
+            if unfused:
+                assert torch.equal(ga.grad_flat, gb.grad_flat)
+    for g in A + B:
+        g.close()
+
+
+def test_step_groups_checks_every_group_before_launching():
+    n, r = 4, 0
+    g1 = ShardedGroup([(64, 8)], n, r)
+    g2 = ShardedGroup([(32,)], n, r, bind=False)     # not bound
+    _fill_masters(g1, ("chk",))
+    before = g1.master_flat.clone()
+    rs = [torch.zeros(n * g.S, dtype=torch.int16, device=DEV) for g in (g1, g2)]
+    ag = [torch.zeros(n * g.S, dtype=torch.int16, device=DEV) for g in (g1, g2)]
+    call = capi.StepGroupsCall([g1.plan, g2.plan], rs, [a[:g.S] for a, g in zip(ag, (g1, g2))], ag, **HP)
+    with pytest.raises(capi.FsdpError) as ei:
+        call(1)
+    assert ei.value.status == capi.FSDP_E_STATE
+    torch.cuda.synchronize()
+    assert torch.equal(before, g1.master_flat), "a group ran although a later one was invalid"
+    call1 = capi.StepGroupsCall([g1.plan], rs[:1], [ag[0][:g1.S]], None, **HP)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for e in evs:
+        e.record()
+    with pytest.raises(capi.FsdpError) as ei:      # copy-out not run without ag_out
+        call1(1, capi.FSDP_KERNEL_UNPACK, evs)
+    assert ei.value.status == capi.FSDP_E_INVAL
+    with pytest.raises(capi.FsdpError) as ei:      # reduce is not a kernel of the fused path
+        call1(1, capi.FSDP_KERNEL_REDUCE, evs)
+    assert ei.value.status == capi.FSDP_E_INVAL
+    g1.close()
+    g2.close()
