@@ -93,6 +93,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown-steps", type=int, default=3,
                     help="extra untimed steps per kernel kind, with events around its launches")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip timing the reduce-scatter copy-in and fp32-contribution kernels")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device-to-device copy of 2 GiB instead (the "
                          "reference for HBM byte counters and the copy ceiling)")
@@ -171,6 +173,47 @@ def cpu_baseline(cfg, rank, min_s=10.0, max_s=30.0):
                    f"in {total_t:.2f} s (NumPy, single thread; host has {os.cpu_count()} cpus, "
                    f"affinity {len(os.sched_getaffinity(0))})"),
     }
+
+
+def measure_next(groups, n, rs_bf16, full_arena, stream, reps):
+    """Per-kernel rates of the kernels beyond the step, on the same groups:
+    the reduce-scatter copy-in (full bf16 grads -> [N, S] bf16, and widened
+    to fp32) and the reduction of fp32 contributions.  The full-parameter
+    arena stands in for the unsharded gradients."""
+    import torch
+    from sharded_shard_amd import capi
+
+    max_ns = max(n * g.S for g in groups)
+    rs_f32 = torch.empty(max_ns, dtype=torch.float32, device=full_arena.device)
+    for g in groups:
+        g.bind_full_grad(full_arena, stream)
+    kinds = {
+        "rs_copy_in_bf16": (lambda g: g.pack_reduce_scatter(rs_bf16[:n * g.S], capi.FSDP_DTYPE_BF16, stream),
+                            lambda g: 2 * g.F + 2 * n * g.S),
+        "rs_copy_in_f32": (lambda g: g.pack_reduce_scatter(rs_f32[:n * g.S], capi.FSDP_DTYPE_F32, stream),
+                           lambda g: 2 * g.F + 4 * n * g.S),
+        "reduce_f32": (lambda g: g.reduce_f32(rs_f32[:n * g.S], stream),
+                       lambda g: 4 * n * g.V + 4 * g.V),
+    }
+    res = {}
+    for name, (fn, nbytes) in kinds.items():
+        evs = []
+        for _ in range(reps + 1):
+            for g in groups:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn(g)
+                b.record(stream)
+                evs.append((a, b))
+        torch.cuda.synchronize()
+        evs = evs[len(groups):]                     # first pass warms up
+        ms = sum(a.elapsed_time(b) for a, b in evs) / reps
+        byts = sum(nbytes(g) for g in groups)
+        gbps = byts / (ms * 1e-3) / 1e9
+        res[name] = {"ms_per_step": round(ms, 4), "algorithmic_GB_per_step": round(byts / 1e9, 4),
+                     "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    del rs_f32
+    return res
 
 
 def main():
@@ -329,6 +372,9 @@ def main():
                      "algorithmic_bytes_per_launch": dom_bytes_per_launch},
         "kernels": kernels,
     }
+    if not args.no_next:
+        out["next_kernels"] = measure_next(groups, n, rs_arena[0], full_arena, stream,
+                                           max(1, args.breakdown_steps))
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(cfg, rank)

@@ -112,8 +112,12 @@ enum {
     FSDP_ROLE_GRAD = 2,
     FSDP_ROLE_EXP_AVG = 4,
     FSDP_ROLE_EXP_AVG_SQ = 8,
-    FSDP_ROLE_FULL = 16
+    FSDP_ROLE_FULL = 16,
+    FSDP_ROLE_FULL_GRAD = 32
 };
+
+/* Element types of the reduce-scatter buffers. */
+enum { FSDP_DTYPE_BF16 = 0, FSDP_DTYPE_F32 = 1 };
 
 /* ---- library ---------------------------------------------------------- */
 
@@ -186,6 +190,13 @@ fsdp_status fsdp_bind(fsdp_plan *plan, float *const *master, float *const *grad,
                       float *const *exp_avg, float *const *exp_avg_sq,
                       uint16_t *const *full, void *stream);
 
+/* Bind each parameter's unsharded bf16 gradient [rows, cols] (the input of
+ * the reduce-scatter copy-in).  full_grad is a host array of n_params device
+ * pointers; NULL only where the parameter has no elements.  Uploads the
+ * entry table like fsdp_bind (allocating the device tables on first use).
+ * Errors: FSDP_E_INVAL, FSDP_E_ALIGN, FSDP_E_NOMEM, FSDP_E_HIP. */
+fsdp_status fsdp_bind_full_grad(fsdp_plan *plan, uint16_t *const *full_grad, void *stream);
+
 /* ---- hot path: enqueue on `stream`; no sync, no allocation ------------- */
 
 /* All-gather copy-in.  Writes all S elements of ag_in: for each parameter,
@@ -221,6 +232,29 @@ fsdp_status fsdp_unpack_allgather(const fsdp_plan *plan, const uint16_t *ag_out,
  * Needs FSDP_ROLE_GRAD.  Errors: as fsdp_pack_allgather. */
 fsdp_status fsdp_reduce_shard(const fsdp_plan *plan, const uint16_t *rs_in,
                               void *stream);
+
+/* Reduce-scatter copy-in: writes the whole [N, S] input of the
+ * reduce-scatter from this rank's unsharded gradients.  Row j gets chunk j of
+ * every parameter (rows [row_begin(j), row_begin(j) + local_rows(j))) at its
+ * shard offset, then zeros up to the next piece, so row j has the layout of
+ * rank j's segment; the collective then hands rank j the sum of everyone's
+ * row j.  [MS] "Working Principle" (Reduce-Scatter state) and "Mixed
+ * Precision" (BF16 gradients cast to FP32 for the reduction); [ST] ZeRO
+ * paragraph.  dtype FSDP_DTYPE_BF16 copies the bits; FSDP_DTYPE_F32 widens
+ * each value exactly (reduce_dtype = fp32 on the wire); padding is 0 / +0.0.
+ *   rs_out  [N, S] of the chosen dtype (2- or 4-byte aligned)
+ * Needs FSDP_ROLE_FULL_GRAD.  Errors: FSDP_E_INVAL, FSDP_E_UNSUPPORTED
+ * (dtype), FSDP_E_ALIGN, FSDP_E_STATE, FSDP_E_HIP. */
+fsdp_status fsdp_pack_reduce_scatter(const fsdp_plan *plan, void *rs_out, int32_t dtype,
+                                     void *stream);
+
+/* fsdp_reduce_shard for fp32 contributions (reduce_dtype = fp32 on the
+ * wire): grad[i] = ((x_0 + x_1) + ... + x_{N-1}) / N with x_j = rs_in[j][off+i]
+ * read as fp32, adds in rank order, one correctly rounded division.
+ * [ST] "Mixed precision" and "Other controls"; [MS] "Mixed Precision".
+ *   rs_in  [N, S] fp32, 4-byte aligned
+ * Needs FSDP_ROLE_GRAD.  Errors: as fsdp_reduce_shard. */
+fsdp_status fsdp_reduce_shard_f32(const fsdp_plan *plan, const float *rs_in, void *stream);
 
 /* One AdamW step (decoupled weight decay, bias-corrected; amsgrad and
  * maximize off) on every bound shard, in place.  `step` counts from 1; m and

@@ -232,6 +232,50 @@ def reduce(p: Plan, rs_in: np.ndarray) -> List[np.ndarray]:
     return grads
 
 
+def pack_reduce_scatter(p: Plan, full_grads: Sequence[np.ndarray]) -> np.ndarray:
+    """Reduce-scatter copy-in: this rank's full bf16 gradients -> [N, S].
+
+    Before the reduce-scatter each rank holds the unsharded gradient of every
+    parameter; the collective gives rank j the sum of everyone's chunk j
+    ([MS] "Working Principle", Reduce-Scatter state; [ST] ZeRO paragraph).  Its
+    input therefore has the all-gather's layout: row j holds chunk j of every
+    parameter at its shard offset, each piece padded to c*cols with zeros.
+    """
+    out = np.zeros((p.world, p.S), dtype=np.uint16)
+    for e, g in zip(p.entries, full_grads):
+        flat = np.asarray(g, dtype=np.uint16).reshape(-1)
+        if flat.size != e.rows * e.cols:
+            raise ValueError("full gradient has the wrong size")
+        for j in range(p.world):
+            b, lr = rows_of_rank(e.rows, p.world, j)
+            n = lr * e.cols
+            out[j, e.shard_offset:e.shard_offset + n] = flat[b * e.cols:b * e.cols + n]
+    return out
+
+
+def pack_reduce_scatter_f32(p: Plan, full_grads: Sequence[np.ndarray]) -> np.ndarray:
+    """The same copy-in with reduce_dtype = fp32: the bf16 gradients are cast
+    to fp32 before the collective ([MS] "Mixed Precision": BF16 gradients are
+    cast to FP32 for the reduction).  The cast is exact; padding is +0.0."""
+    return bf16_to_f32(pack_reduce_scatter(p, full_grads))
+
+
+def reduce_f32(p: Plan, rs_in: np.ndarray) -> List[np.ndarray]:
+    """Local reduction of fp32 contributions (reduce_dtype = fp32 on the wire):
+    fp32 sum in rank order from rank 0's value, then one division by N, as
+    ``reduce`` does after widening bf16 contributions."""
+    rs = np.asarray(rs_in, dtype=F32).reshape(p.world, p.S)
+    n_div = F32(p.world)
+    grads = []
+    for e in p.entries:
+        sl = slice(e.shard_offset, e.shard_offset + e.valid_numel)
+        acc = rs[0, sl].copy()
+        for j in range(1, p.world):
+            acc = acc + rs[j, sl]
+        grads.append((acc / n_div).astype(F32))
+    return grads
+
+
 @dataclass(frozen=True)
 class AdamWScalars:
     beta1: np.float32

@@ -29,6 +29,10 @@ FSDP_ROLE_GRAD = 2
 FSDP_ROLE_EXP_AVG = 4
 FSDP_ROLE_EXP_AVG_SQ = 8
 FSDP_ROLE_FULL = 16
+FSDP_ROLE_FULL_GRAD = 32
+
+FSDP_DTYPE_BF16 = 0
+FSDP_DTYPE_F32 = 1
 
 FSDP_STEP_WRITE_GRAD = 1
 FSDP_STEP_UNFUSED = 2
@@ -97,6 +101,9 @@ _SIGS = {
     "fsdp_reduce_shard": (_i32, [_P, _P, _P]),
     "fsdp_adamw_shard": (_i32, [_P, ctypes.POINTER(AdamwHparams), _i64, _P]),
     "fsdp_step_shard": (_i32, [_P, _P, _P, ctypes.POINTER(AdamwHparams), _i64, ctypes.c_uint32, _P]),
+    "fsdp_bind_full_grad": (_i32, [_P, _PP, _P]),
+    "fsdp_pack_reduce_scatter": (_i32, [_P, _P, _i32, _P]),
+    "fsdp_reduce_shard_f32": (_i32, [_P, _P, _P]),
     "fsdp_step_groups": (_i32, [_PP, _i32, _PP, _PP, _PP, ctypes.POINTER(AdamwHparams), _i64,
                                 ctypes.c_uint32, _i32, _PP, _P]),
     "fsdp_check_stream": (_i32, [_P]),
@@ -207,6 +214,21 @@ def fsdp_bind(plan, master=None, grad=None, exp_avg=None, exp_avg_sq=None, full=
     _check(lib.fsdp_bind(plan, _ptr_array(master), _ptr_array(grad), _ptr_array(exp_avg),
                          _ptr_array(exp_avg_sq), _ptr_array(full), stream_handle(stream)),
            "fsdp_bind")
+
+
+def fsdp_bind_full_grad(plan, full_grad, stream=None) -> None:
+    _check(lib.fsdp_bind_full_grad(plan, _ptr_array(full_grad), stream_handle(stream)),
+           "fsdp_bind_full_grad")
+
+
+def fsdp_pack_reduce_scatter(plan, rs_out, dtype: int = FSDP_DTYPE_BF16, stream=None) -> None:
+    _check(lib.fsdp_pack_reduce_scatter(plan, addr(rs_out), dtype, stream_handle(stream)),
+           "fsdp_pack_reduce_scatter")
+
+
+def fsdp_reduce_shard_f32(plan, rs_in, stream=None) -> None:
+    _check(lib.fsdp_reduce_shard_f32(plan, addr(rs_in), stream_handle(stream)),
+           "fsdp_reduce_shard_f32")
 
 
 def fsdp_pack_allgather(plan, ag_in, stream=None) -> None:

@@ -27,6 +27,10 @@ hipError_t launch_adamw(const EwTile *tiles, int64_t n, const DevEntry *ents,
 hipError_t launch_step(const PackTile *tiles, int64_t n, const DevEntry *ents,
                        const uint16_t *rs_in, uint16_t *ag_in, int64_t S, int32_t N,
                        const float scal[8], bool write_grad, hipStream_t st);
+hipError_t launch_rspack(const PackTile *tiles, int64_t n, const DevEntry *ents, void *out,
+                         bool f32, hipStream_t st);
+hipError_t launch_reduce_f32(const ReduceTile *tiles, int64_t n, const DevEntry *ents,
+                             const float *rs_in, int64_t S, int32_t N, hipStream_t st);
 }  // namespace fsdp
 
 struct fsdp_plan {
@@ -34,9 +38,10 @@ struct fsdp_plan {
     std::vector<fsdp::DevEntry> host_entries;
     int32_t bound = 0;
     int device = -1;
-    char *dmem = nullptr;  // one device block: entries, then the four tile tables
+    char *dmem = nullptr;  // one device block: entries, then the tile tables
     fsdp::DevEntry *d_entries = nullptr;
     fsdp::PackTile *d_pack = nullptr;
+    fsdp::PackTile *d_rspack = nullptr;
     fsdp::UnpackTile *d_unpack = nullptr;
     fsdp::ReduceTile *d_reduce = nullptr;
     fsdp::EwTile *d_adamw = nullptr;
@@ -93,6 +98,65 @@ fsdp_status need_roles(const fsdp_plan *p, int32_t roles, const char *call) {
     if (p == nullptr) return fail(FSDP_E_INVAL, std::string(call) + ": null plan");
     if ((p->bound & roles) != roles || p->dmem == nullptr)
         return fail(FSDP_E_STATE, std::string(call) + ": the tensors it needs are not bound");
+    return FSDP_OK;
+}
+
+// Upload the entry table (and, the first time, allocate the device block and
+// upload every tile table) on `st`, then record the newly bound roles.
+fsdp_status commit_entries(fsdp_plan *p, std::vector<fsdp::DevEntry> ents, int32_t roles,
+                           hipStream_t st, const char *call) {
+    const std::string c(call);
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, (c + ": hipGetDevice").c_str());
+    if (p->dmem != nullptr && dev != p->device)
+        return fail(FSDP_E_STATE, c + ": plan already bound on another device");
+    const size_t n = p->L.entries.size();
+    struct Table {
+        void **dst;
+        const void *src;
+        size_t bytes;
+    } tabs[6] = {
+        {reinterpret_cast<void **>(&p->d_entries), nullptr, n * sizeof(fsdp::DevEntry)},
+        {reinterpret_cast<void **>(&p->d_pack), p->L.pack.data(),
+         p->L.pack.size() * sizeof(fsdp::PackTile)},
+        {reinterpret_cast<void **>(&p->d_rspack), p->L.rspack.data(),
+         p->L.rspack.size() * sizeof(fsdp::PackTile)},
+        {reinterpret_cast<void **>(&p->d_unpack), p->L.unpack.data(),
+         p->L.unpack.size() * sizeof(fsdp::UnpackTile)},
+        {reinterpret_cast<void **>(&p->d_reduce), p->L.reduce.data(),
+         p->L.reduce.size() * sizeof(fsdp::ReduceTile)},
+        {reinterpret_cast<void **>(&p->d_adamw), p->L.adamw.data(),
+         p->L.adamw.size() * sizeof(fsdp::EwTile)},
+    };
+    const bool first = p->dmem == nullptr;
+    if (first) {
+        size_t total = 256;
+        for (const Table &t : tabs) total += round256(t.bytes);
+        void *mem = nullptr;
+        e = hipMalloc(&mem, total);
+        if (e != hipSuccess) return fail(FSDP_E_NOMEM, c + ": hipMalloc of device tables failed");
+        p->dmem = static_cast<char *>(mem);
+        p->device = dev;
+        char *cur = p->dmem;
+        for (const Table &t : tabs) {
+            *t.dst = cur;
+            cur += round256(t.bytes);
+        }
+    }
+    // Kernels of this plan still queued on the stream may read the tables.
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, (c + ": hipStreamSynchronize").c_str());
+    for (int k = 0; k < (first ? 6 : 1); ++k) {
+        if (tabs[k].bytes == 0) continue;
+        const void *src = k == 0 ? static_cast<const void *>(ents.data()) : tabs[k].src;
+        e = hipMemcpyAsync(*tabs[k].dst, src, tabs[k].bytes, hipMemcpyHostToDevice, st);
+        if (e != hipSuccess) return hip_fail(e, (c + ": hipMemcpyAsync").c_str());
+    }
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, (c + ": upload").c_str());
+    p->host_entries = std::move(ents);
+    p->bound = first ? roles : (p->bound | roles);
     return FSDP_OK;
 }
 
@@ -257,60 +321,26 @@ fsdp_status fsdp_bind(fsdp_plan *p, float *const *master, float *const *grad,
             ents[i].full = full[i];
         }
     }
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    int dev = -1;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e, "fsdp_bind: hipGetDevice");
-    if (p->dmem != nullptr && dev != p->device)
-        return fail(FSDP_E_STATE, "fsdp_bind: plan already bound on another device");
-    const size_t b_ent = round256(n * sizeof(fsdp::DevEntry));
-    const size_t b_pack = round256(p->L.pack.size() * sizeof(fsdp::PackTile));
-    const size_t b_unpack = round256(p->L.unpack.size() * sizeof(fsdp::UnpackTile));
-    const size_t b_reduce = round256(p->L.reduce.size() * sizeof(fsdp::ReduceTile));
-    const size_t b_adamw = round256(p->L.adamw.size() * sizeof(fsdp::EwTile));
-    const bool first = p->dmem == nullptr;
-    if (first) {
-        void *mem = nullptr;
-        const size_t total = b_ent + b_pack + b_unpack + b_reduce + b_adamw + 256;
-        e = hipMalloc(&mem, total);
-        if (e != hipSuccess) return fail(FSDP_E_NOMEM, "fsdp_bind: hipMalloc of device tables failed");
-        p->dmem = static_cast<char *>(mem);
-        p->device = dev;
-        char *c = p->dmem;
-        p->d_entries = reinterpret_cast<fsdp::DevEntry *>(c);
-        c += b_ent;
-        p->d_pack = reinterpret_cast<fsdp::PackTile *>(c);
-        c += b_pack;
-        p->d_unpack = reinterpret_cast<fsdp::UnpackTile *>(c);
-        c += b_unpack;
-        p->d_reduce = reinterpret_cast<fsdp::ReduceTile *>(c);
-        c += b_reduce;
-        p->d_adamw = reinterpret_cast<fsdp::EwTile *>(c);
+    return commit_entries(p, std::move(ents), roles, static_cast<hipStream_t>(stream),
+                          "fsdp_bind");
+}
+
+fsdp_status fsdp_bind_full_grad(fsdp_plan *p, uint16_t *const *full_grad, void *stream) {
+    if (p == nullptr || full_grad == nullptr)
+        return fail(FSDP_E_INVAL, "fsdp_bind_full_grad: null plan or array");
+    std::vector<fsdp::DevEntry> ents = p->host_entries;
+    for (size_t i = 0; i < ents.size(); ++i) {
+        const fsdp_shard_entry_t &e = p->L.entries[i];
+        if (full_grad[i] == nullptr && e.rows * e.cols > 0)
+            return fail(FSDP_E_INVAL, "fsdp_bind_full_grad: null pointer for parameter " +
+                                          std::to_string(i));
+        if (misaligned(full_grad[i], 2))
+            return fail(FSDP_E_ALIGN, "fsdp_bind_full_grad: pointer of parameter " +
+                                          std::to_string(i) + " is not 2-byte aligned");
+        ents[i].full_grad = full_grad[i];
     }
-    // Kernels of this plan still queued on the stream may read the tables.
-    e = hipStreamSynchronize(st);
-    if (e != hipSuccess) return hip_fail(e, "fsdp_bind: hipStreamSynchronize");
-    struct Up {
-        void *dst;
-        const void *src;
-        size_t bytes;
-    } ups[5] = {
-        {p->d_entries, ents.data(), n * sizeof(fsdp::DevEntry)},
-        {p->d_pack, p->L.pack.data(), p->L.pack.size() * sizeof(fsdp::PackTile)},
-        {p->d_unpack, p->L.unpack.data(), p->L.unpack.size() * sizeof(fsdp::UnpackTile)},
-        {p->d_reduce, p->L.reduce.data(), p->L.reduce.size() * sizeof(fsdp::ReduceTile)},
-        {p->d_adamw, p->L.adamw.data(), p->L.adamw.size() * sizeof(fsdp::EwTile)},
-    };
-    for (int k = 0; k < (first ? 5 : 1); ++k) {
-        if (ups[k].bytes == 0) continue;
-        e = hipMemcpyAsync(ups[k].dst, ups[k].src, ups[k].bytes, hipMemcpyHostToDevice, st);
-        if (e != hipSuccess) return hip_fail(e, "fsdp_bind: hipMemcpyAsync");
-    }
-    e = hipStreamSynchronize(st);
-    if (e != hipSuccess) return hip_fail(e, "fsdp_bind: upload");
-    p->host_entries = std::move(ents);
-    p->bound = first ? roles : (p->bound | roles);
-    return FSDP_OK;
+    return commit_entries(p, std::move(ents), FSDP_ROLE_FULL_GRAD,
+                          static_cast<hipStream_t>(stream), "fsdp_bind_full_grad");
 }
 
 }  // extern "C"
@@ -443,6 +473,38 @@ fsdp_status fsdp_step_shard(const fsdp_plan *p, const uint16_t *rs_in, uint16_t 
     adamw_scalars(hp, step, scal);
     return launched(do_step(p, rs_in, ag_in, scal, write_grad, static_cast<hipStream_t>(stream)),
                     "fsdp_step_shard: launch");
+}
+
+fsdp_status fsdp_pack_reduce_scatter(const fsdp_plan *p, void *rs_out, int32_t dtype,
+                                     void *stream) {
+    const char *call = "fsdp_pack_reduce_scatter";
+    fsdp_status s = need_roles(p, FSDP_ROLE_FULL_GRAD, call);
+    if (s != FSDP_OK) return s;
+    if (dtype != FSDP_DTYPE_BF16 && dtype != FSDP_DTYPE_F32)
+        return fail(FSDP_E_UNSUPPORTED, "fsdp_pack_reduce_scatter: dtype must be BF16 or F32");
+    if (rs_out == nullptr && p->L.S > 0)
+        return fail(FSDP_E_INVAL, "fsdp_pack_reduce_scatter: null rs_out");
+    if (misaligned(rs_out, dtype == FSDP_DTYPE_F32 ? 4 : 2))
+        return fail(FSDP_E_ALIGN, "fsdp_pack_reduce_scatter: rs_out misaligned for its dtype");
+    if ((s = check_device(p)) != FSDP_OK) return s;
+    return launched(fsdp::launch_rspack(p->d_rspack, static_cast<int64_t>(p->L.rspack.size()),
+                                        p->d_entries, rs_out, dtype == FSDP_DTYPE_F32,
+                                        static_cast<hipStream_t>(stream)),
+                    "fsdp_pack_reduce_scatter: launch");
+}
+
+fsdp_status fsdp_reduce_shard_f32(const fsdp_plan *p, const float *rs_in, void *stream) {
+    const char *call = "fsdp_reduce_shard_f32";
+    fsdp_status s = need_roles(p, FSDP_ROLE_GRAD, call);
+    if (s != FSDP_OK) return s;
+    if (rs_in == nullptr && p->L.S > 0) return fail(FSDP_E_INVAL, "fsdp_reduce_shard_f32: null rs_in");
+    if (misaligned(rs_in, 4))
+        return fail(FSDP_E_ALIGN, "fsdp_reduce_shard_f32: rs_in not 4-byte aligned");
+    if ((s = check_device(p)) != FSDP_OK) return s;
+    return launched(fsdp::launch_reduce_f32(p->d_reduce, static_cast<int64_t>(p->L.reduce.size()),
+                                            p->d_entries, rs_in, p->L.S, p->L.world,
+                                            static_cast<hipStream_t>(stream)),
+                    "fsdp_reduce_shard_f32: launch");
 }
 
 fsdp_status fsdp_step_groups(fsdp_plan *const *plans, int32_t n_groups,

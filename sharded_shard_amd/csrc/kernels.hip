@@ -598,6 +598,193 @@ __global__ __launch_bounds__(kBlock) void adamw_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// reduce-scatter copy-in: full bf16 gradients -> [N, S] (bf16 or fp32)
+// ---------------------------------------------------------------------------
+
+template <int POL>
+__global__ __launch_bounds__(kBlock) void rspack_bf16_kernel(
+    const PackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
+    const DevEntry *__restrict__ ents, uint16_t *__restrict__ out) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
+        const PackTile tl = tiles[t];
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        int64_t valid = tl.valid - b;
+        valid = valid < 0 ? 0 : (valid > len ? len : valid);
+        uint16_t *dst = out + tl.dst + b;
+        if (valid > 0) copy_run_bf16<POL>(dst, ents[tl.entry].full_grad + tl.src + b, valid);
+        zero_bf16<(POL >> 1) & 1>(dst, valid, len);
+    }
+}
+
+// dst[e] = 0.0f for e in [from, len), 16-byte stores where aligned.
+template <int SN>
+__device__ __forceinline__ void zero_f32(float *dst, int64_t from, int64_t len) {
+    const int tid = threadIdx.x;
+    if (from >= len) return;
+    float *d = dst + from;
+    const int64_t n = len - from;
+    int64_t head = ((16u - (lo32(d) & 15u)) & 15u) >> 2;
+    if (head > n) head = n;
+    if (tid < head) d[tid] = 0.0f;
+    const int64_t nvec = (n - head) >> 2;
+    f32x4 *dv = reinterpret_cast<f32x4 *>(d + head);
+    for (int64_t v = tid; v < nvec; v += kBlock) stp<SN>(dv + v, f32x4{0.f, 0.f, 0.f, 0.f});
+    const int64_t done = head + (nvec << 2);
+    if (tid < n - done) d[done + tid] = 0.0f;
+}
+
+// dst[i] = fp32(src[i]) for i < valid (exact widening), zeros up to len.
+template <int POL>
+__device__ __forceinline__ void widen_run(float *__restrict__ dst, const uint16_t *__restrict__ src,
+                                          int64_t len, int64_t valid) {
+    constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
+    const int tid = threadIdx.x;
+    int64_t head = ((16u - (lo32(dst) & 15u)) & 15u) >> 2;
+    if (head > valid) head = valid;
+    if (tid < head) dst[tid] = widen(src[tid]);
+    const int64_t ngrp = (valid - head) >> 3;
+    const uint16_t *s = src + head;
+    const uint32_t k = lo32(s) & 15u;
+    f32x4 *dv = reinterpret_cast<f32x4 *>(dst + head);
+    for (int64_t g = tid; g < ngrp; g += kBlock) {
+        float x[8];
+        init8(x, load16_at<LN>(s + (g << 3), k));
+        stp<SN>(dv + 2 * g, f32x4{x[0], x[1], x[2], x[3]});
+        stp<SN>(dv + 2 * g + 1, f32x4{x[4], x[5], x[6], x[7]});
+    }
+    const int64_t done = head + (ngrp << 3);
+    if (tid < valid - done) dst[done + tid] = widen(src[done + tid]);
+    zero_f32<SN>(dst, valid, len);
+}
+
+template <int POL>
+__global__ __launch_bounds__(kBlock) void rspack_f32_kernel(
+    const PackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
+    const DevEntry *__restrict__ ents, float *__restrict__ out) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
+        const PackTile tl = tiles[t];
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        int64_t valid = tl.valid - b;
+        valid = valid < 0 ? 0 : (valid > len ? len : valid);
+        widen_run<POL>(out + tl.dst + b, ents[tl.entry].full_grad + tl.src + b, len, valid);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// reduce of fp32 contributions: [N, S] fp32 -> fp32 mean, this rank's pieces
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float sum_rows_scalar_f32(const float *src0, int64_t S, int32_t N,
+                                                     int64_t e) {
+    float acc = src0[e];
+    for (int32_t j = 1; j < N; ++j) acc = acc + src0[static_cast<int64_t>(j) * S + e];
+    return acc;
+}
+
+// Eight fp32 at row + offb (row uniform, offb this lane's byte offset); q is
+// the dword index of (row + offb) modulo 4, uniform.  Aligned 16-byte buffer
+// loads, then a dword select.
+template <int NT>
+__device__ __forceinline__ void row_load8f(const char *row, uint32_t offb, uint32_t q,
+                                           uint32_t nbytes, float (&x)[8]) {
+    const char *al = row - 4 * q;
+    const u32x4 a = bload16<NT>(al, offb, nbytes);
+    const u32x4 b = bload16<NT>(al, offb + 16, nbytes);
+    u32x4 lo, hi;
+    if (q == 0) {
+        lo = a;
+        hi = b;
+    } else {
+        const u32x4 c = bload16<NT>(al, offb + 32, nbytes);
+        switch (q) {
+            case 1:
+                lo = u32x4{a.y, a.z, a.w, b.x};
+                hi = u32x4{b.y, b.z, b.w, c.x};
+                break;
+            case 2:
+                lo = u32x4{a.z, a.w, b.x, b.y};
+                hi = u32x4{b.z, b.w, c.x, c.y};
+                break;
+            default:
+                lo = u32x4{a.w, b.x, b.y, b.z};
+                hi = u32x4{b.w, c.x, c.y, c.z};
+                break;
+        }
+    }
+    x[0] = __uint_as_float(lo.x);
+    x[1] = __uint_as_float(lo.y);
+    x[2] = __uint_as_float(lo.z);
+    x[3] = __uint_as_float(lo.w);
+    x[4] = __uint_as_float(hi.x);
+    x[5] = __uint_as_float(hi.y);
+    x[6] = __uint_as_float(hi.z);
+    x[7] = __uint_as_float(hi.w);
+}
+
+template <int POL, bool kRowsAligned>
+__device__ __forceinline__ void reduce_f32_run(float *__restrict__ dst,
+                                               const float *__restrict__ src0, int64_t len,
+                                               int64_t S, int32_t N, float fN) {
+    constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
+    const int tid = threadIdx.x;
+    int64_t head = ((16u - (lo32(dst) & 15u)) & 15u) >> 2;
+    if (head > len) head = len;
+    if (tid < head) dst[tid] = sum_rows_scalar_f32(src0, S, N, tid) / fN;
+    const int64_t ngrp = (len - head) >> 3;
+    const char *r0 = reinterpret_cast<const char *>(src0 + head);
+    const uint32_t q0 = (lo32(r0) >> 2) & 3u;
+    const uint32_t qS = static_cast<uint32_t>(S & 3);
+    const int64_t Sb = S * 4;
+    const uint32_t nbytes = static_cast<uint32_t>(4 * (len - head) + 64);
+    f32x4 *dv = reinterpret_cast<f32x4 *>(dst + head);
+    const int nthr = blockDim.x;
+    for (int64_t g = tid; g < ngrp; g += nthr) {
+        const uint32_t offb = static_cast<uint32_t>(g) << 5;
+        float acc[8], x[8];
+        row_load8f<LN>(r0, offb, q0, nbytes, acc);
+        uint32_t q = q0;
+        for (int32_t j = 1; j < N; ++j) {
+            if (!kRowsAligned) q = (q + qS) & 3u;
+            row_load8f<LN>(r0 + j * Sb, offb, q, nbytes, x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = acc[i] + x[i];
+        }
+        stp<SN>(dv + 2 * g, f32x4{acc[0] / fN, acc[1] / fN, acc[2] / fN, acc[3] / fN});
+        stp<SN>(dv + 2 * g + 1, f32x4{acc[4] / fN, acc[5] / fN, acc[6] / fN, acc[7] / fN});
+    }
+    const int64_t done = head + (ngrp << 3);
+    if (tid < len - done) dst[done + tid] = sum_rows_scalar_f32(src0, S, N, done + tid) / fN;
+}
+
+template <int POL, bool kRowsAligned>
+__global__ __launch_bounds__(kBlock) void reduce_f32_kernel(
+    const ReduceTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
+    const DevEntry *__restrict__ ents, const float *__restrict__ rs_in, int64_t S, int32_t N,
+    float fN) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
+        const ReduceTile tl = tiles[t];
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        reduce_f32_run<POL, kRowsAligned>(ents[tl.entry].grad + tl.dst + b, rs_in + tl.src + b,
+                                          len, S, N, fN);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // fused step: reduce -> AdamW -> copy-in, one pass over this rank's pieces
 // ---------------------------------------------------------------------------
 
@@ -800,6 +987,37 @@ hipError_t launch_adamw(const EwTile *tiles, int64_t n, const DevEntry *ents,
     const int32_t sp = split_for(kTileAdamw, FSDP_ADAMW_SUB);
     adamw_kernel<FSDP_ADAMW_POL><<<grid_for(n, sp), kBlock, 0, st>>>(
         tiles, n, sp, kTileAdamw / sp, ents, to_scalars(scal));
+    return hipGetLastError();
+}
+
+hipError_t launch_rspack(const PackTile *tiles, int64_t n, const DevEntry *ents, void *out,
+                         bool f32, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const int32_t sp = split_for(kTileUnpack, FSDP_UNPACK_SUB);
+    const unsigned grid = grid_for(n, sp);
+    if (f32)
+        rspack_f32_kernel<FSDP_UNPACK_POL><<<grid, kBlock, 0, st>>>(
+            tiles, n, sp, kTileUnpack / sp, ents, static_cast<float *>(out));
+    else
+        rspack_bf16_kernel<FSDP_UNPACK_POL><<<grid, kBlock, 0, st>>>(
+            tiles, n, sp, kTileUnpack / sp, ents, static_cast<uint16_t *>(out));
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce_f32(const ReduceTile *tiles, int64_t n, const DevEntry *ents,
+                             const float *rs_in, int64_t S, int32_t N, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const float fN = static_cast<float>(N);
+    // fp32 rows carry twice the bytes of bf16 rows per element
+    const int32_t sp = split_rows(kTileReduce, 2 * N, 0);
+    const unsigned grid = grid_for(n, sp);
+    const unsigned thr = row_threads(kTileReduce / sp);
+    if ((S & 3) == 0)
+        reduce_f32_kernel<FSDP_REDUCE_POL, true>
+            <<<grid, thr, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
+    else
+        reduce_f32_kernel<FSDP_REDUCE_POL, false>
+            <<<grid, thr, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
     return hipGetLastError();
 }
 

@@ -112,6 +112,23 @@ fsdp_status build_layout(const int64_t *rows, const int64_t *cols, int32_t n,
                 std::max<int64_t>(0, std::min<int64_t>(pt.len, e.valid_numel - t)));
             L.pack.push_back(pt);
         }
+        // reduce-scatter copy-in: rank j's segment slot of this parameter in
+        // row j, chunk j's rows first, then zeros (the mirror of copy-out).
+        for (int32_t j = 0; j < world; ++j) {
+            int64_t b = 0, lr = 0;
+            rows_of_rank(e.rows, world, j, &b, &lr);
+            const int64_t valid = lr * e.cols;
+            for (int64_t t = 0; t < e.seg_numel; t += kTileUnpack) {
+                PackTile rt{};
+                rt.dst = static_cast<int64_t>(j) * L.S + e.shard_offset + t;
+                rt.src = b * e.cols + t;
+                rt.entry = i;
+                rt.len = static_cast<int32_t>(std::min(kTileUnpack, e.seg_numel - t));
+                rt.valid = static_cast<int32_t>(
+                    std::max<int64_t>(0, std::min<int64_t>(rt.len, valid - t)));
+                L.rspack.push_back(rt);
+            }
+        }
         // copy-out: one run per source rank j, rows of chunk j.
         for (int32_t j = 0; j < world; ++j) {
             int64_t b = 0, lr = 0;

@@ -48,8 +48,8 @@ struct DevEntry {
     float *exp_avg_sq;
     uint16_t *full;
     int64_t valid_numel;
-    int64_t rsv0;
-    int64_t rsv1;
+    uint16_t *full_grad;   // unsharded bf16 gradient (reduce-scatter copy-in)
+    int64_t rsv;
 };
 static_assert(sizeof(DevEntry) == 64, "DevEntry layout");
 
@@ -98,6 +98,7 @@ struct Layout {
     int64_t S = 0, V = 0, F = 0;
     int32_t n_empty = 0;
     std::vector<PackTile> pack;
+    std::vector<PackTile> rspack;     // reduce-scatter copy-in: dst counts rows*S
     std::vector<UnpackTile> unpack;
     std::vector<ReduceTile> reduce;
     std::vector<EwTile> adamw;

@@ -105,7 +105,29 @@ class ShardedGroup:
         capi.fsdp_bind(self.plan, self._ptrs(self.master_flat), self._ptrs(self.grad_flat),
                        self._ptrs(self.m_flat), self._ptrs(self.v_flat), full, stream)
 
+    def bind_full_grad(self, arena: Optional[torch.Tensor] = None, stream=None) -> None:
+        """Bind unsharded bf16 gradients, laid out like the full parameters
+        (views of ``arena``, allocated here when not given)."""
+        if arena is None:
+            arena = torch.zeros(self.full_space, dtype=torch.int16, device=self.device)
+        if arena.numel() < self.full_space:
+            raise ValueError("full-gradient arena is too small for this group")
+        self.full_grad_flat = arena
+        ptrs = [arena[o:o + r * c].data_ptr() if r * c else 0
+                for o, r, c in zip(self.full_offsets, self.rows, self.cols)]
+        capi.fsdp_bind_full_grad(self.plan, ptrs, stream)
+
+    def full_grad_view(self, i: int) -> torch.Tensor:
+        o = self.full_offsets[i]
+        return self.full_grad_flat[o:o + self.rows[i] * self.cols[i]].view(self.rows[i], self.cols[i])
+
     # ---- hot path -----------------------------------------------------------------
+
+    def pack_reduce_scatter(self, rs_out, dtype: int = capi.FSDP_DTYPE_BF16, stream=None) -> None:
+        capi.fsdp_pack_reduce_scatter(self.plan, rs_out, dtype, stream)
+
+    def reduce_f32(self, rs_in, stream=None) -> None:
+        capi.fsdp_reduce_shard_f32(self.plan, rs_in, stream)
 
     def pack(self, ag_in, stream=None) -> None:
         capi.fsdp_pack_allgather(self.plan, ag_in, stream)

@@ -607,3 +607,116 @@ def test_step_groups_checks_every_group_before_launching():
     assert ei.value.status == capi.FSDP_E_INVAL
     g1.close()
     g2.close()
+
+
+# ---------------------------------------------------------------------------
+# reduce-scatter copy-in and fp32 contributions
+# ---------------------------------------------------------------------------
+
+def _fill_full_grads(g, key):
+    for i in range(len(g.shapes)):
+        n = g.rows[i] * g.cols[i]
+        if n:
+            g.full_grad_view(i).view(-1).copy_(synth.normal_bf16_bits(n, 1e-3, key + (i,)))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("align", [1, 8])
+@pytest.mark.parametrize("case", range(len(CASES)), ids=_case_ids())
+def test_pack_reduce_scatter_bit_exact(case, align, dtype):
+    name, shapes, n = CASES[case]
+    r = n - 1
+    plan = O.plan(shapes, n, r, align)
+    g = ShardedGroup(shapes, n, r, align)
+    g.bind_full_grad()
+    _fill_full_grads(g, ("rsp", name))
+    grads = [u16(g.full_grad_view(i)) for i in range(len(shapes))]
+    if dtype == "bf16":
+        want = O.pack_reduce_scatter(plan, grads).reshape(-1)
+        for off in (0, 1, 3):
+            buf, out = guarded_i16(n * plan.S + off)
+            out = out[off:]
+            g.pack_reduce_scatter(out, capi.FSDP_DTYPE_BF16)
+            torch.cuda.synchronize()
+            assert np.array_equal(u16(out), want), (name, off)
+            h = u16(buf)
+            assert (h[:GUARD + off] == GUARD_VAL).all() and (h[GUARD + off + n * plan.S:] == GUARD_VAL).all()
+    else:
+        want = O.pack_reduce_scatter_f32(plan, grads).reshape(-1)
+        for off in (0, 1, 2, 3):
+            buf = torch.full((n * plan.S + off + 2 * GUARD,), 7.5, dtype=torch.float32, device=DEV)
+            out = buf[GUARD + off:GUARD + off + n * plan.S]
+            g.pack_reduce_scatter(out, capi.FSDP_DTYPE_F32)
+            torch.cuda.synchronize()
+            assert np.array_equal(f32(out).view(np.uint32), want.view(np.uint32)), (name, off)
+            h = f32(buf)
+            assert (h[:GUARD + off] == 7.5).all() and (h[GUARD + off + n * plan.S:] == 7.5).all()
+    g.close()
+
+
+def test_pack_reduce_scatter_misaligned_full_grads_and_roundtrip():
+    shapes, n = [(37, 11), (999,), (8, 64), (1, 5)], 5
+    plan = O.plan(shapes, n, 2)
+    for shift in range(8):
+        g = ShardedGroup(shapes, n, 2)
+        arena = torch.zeros(sum(r * c + 9 for r, c in zip(g.rows, g.cols)) + 16, dtype=torch.int16, device=DEV)
+        views, o = [], shift
+        for i, (r_, c_) in enumerate(zip(g.rows, g.cols)):
+            v = arena[o:o + r_ * c_]
+            v.copy_(synth.normal_bf16_bits(r_ * c_, 1e-3, ("rspm", shift, i)))
+            views.append(v)
+            o += r_ * c_ + 1
+        capi.fsdp_bind_full_grad(g.plan, [v.data_ptr() for v in views], None)
+        out = torch.zeros(n * plan.S, dtype=torch.int16, device=DEV)
+        g.pack_reduce_scatter(out)
+        torch.cuda.synchronize()
+        want = O.pack_reduce_scatter(plan, [u16(v) for v in views])
+        assert np.array_equal(u16(out).reshape(n, plan.S), want), shift
+        # the reduce-scatter input has the all-gather layout: copy-out restores it
+        g.unpack(out)
+        torch.cuda.synchronize()
+        for i, v in enumerate(views):
+            assert torch.equal(g.full_view(i).reshape(-1), v)
+        g.close()
+
+
+@pytest.mark.parametrize("case", range(len(CASES)), ids=_case_ids())
+def test_reduce_f32_matches_oracle(case):
+    name, shapes, n = CASES[case]
+    for r in sorted({0, n - 1}):
+        plan = O.plan(shapes, n, r)
+        rng = np.random.default_rng(synth.seed_for("r32", name, r) % (2**32))
+        rs = (rng.standard_normal((n, plan.S)) * 1e-3).astype(np.float32)
+        rs[:, _pad_mask(plan)] = np.float32("nan")
+        g = ShardedGroup(shapes, n, r)
+        for off in (0, 1, 2, 3):
+            buf = torch.zeros(n * plan.S + 4, dtype=torch.float32, device=DEV)
+            buf[off:off + n * plan.S].copy_(torch.from_numpy(rs.reshape(-1)))
+            g.grad_flat.fill_(-7.0)
+            g.reduce_f32(buf[off:off + n * plan.S])
+            torch.cuda.synchronize()
+            for i, want in enumerate(O.reduce_f32(plan, rs)):
+                _cmp_f32(f32(g.shard_view(g.grad_flat, i)), want, (name, r, i, off))
+        g.close()
+
+
+@pytest.mark.parametrize("n", [2, 6, 8, 64])
+def test_reduce_f32_of_widened_copy_in_equals_bf16_reduce(n):
+    """reduce_f32(pack_rs_f32(G)) == reduce(pack_rs_bf16(G)), every element."""
+    shapes = [(n * 40 + 3, 67), (2 * n + 1,), (3 * n - 1, 9)]
+    r = n // 2
+    g = ShardedGroup(shapes, n, r)
+    g.bind_full_grad()
+    _fill_full_grads(g, ("wid", n))
+    b = torch.zeros(n * g.S, dtype=torch.int16, device=DEV)
+    f = torch.zeros(n * g.S, dtype=torch.float32, device=DEV)
+    g.pack_reduce_scatter(b, capi.FSDP_DTYPE_BF16)
+    g.pack_reduce_scatter(f, capi.FSDP_DTYPE_F32)
+    g.reduce(b)
+    torch.cuda.synchronize()
+    ref = g.grad_flat.clone()
+    g.grad_flat.zero_()
+    g.reduce_f32(f)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.view(torch.int32), g.grad_flat.view(torch.int32))
+    g.close()

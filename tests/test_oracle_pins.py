@@ -551,3 +551,91 @@ def test_whole_step_mlp_probe_against_torch_building_blocks():
         # the two AdamW orders may differ by an fp32 ulp, which can move a bf16 tie
         diff = np.abs(seg.astype(np.int32) - want.astype(np.int32))
         assert diff.max() <= 1
+
+
+# ---------------------------------------------------------------------------
+# reduce-scatter copy-in and fp32 contributions
+# ---------------------------------------------------------------------------
+
+def _bf16_grads(shapes, key):
+    out = []
+    for i, s in enumerate(shapes):
+        cols = int(np.prod(s[1:])) if len(s) > 1 else 1
+        g = synth.bf16_bits_to_u16(synth.normal_bf16_bits(int(np.prod(s)), 1e-3, key + (i,)))
+        out.append(g.reshape(s[0], cols))
+    return out
+
+
+@pytest.mark.parametrize("align", [1, 8])
+@pytest.mark.parametrize("case", range(len(SMALL_CASES)))
+def test_pack_reduce_scatter_matches_torch_chunk_pad_cat(case, align):
+    shapes, n = SMALL_CASES[case]
+    grads = _bf16_grads(shapes, ("rsp", case))
+    p = O.plan(shapes, n, 0, align)
+    got = O.pack_reduce_scatter(p, grads)
+    for j in range(n):
+        parts = []
+        for g, e in zip(grads, p.entries):
+            piece = _chunks_of(torch.from_numpy(g.view(np.int16)), n, j).reshape(-1)
+            parts.append(torch.cat([piece, torch.zeros(e.seg_numel - piece.numel(), dtype=torch.int16)]))
+        want = torch.cat(parts).numpy().view(np.uint16) if parts else np.zeros(0, np.uint16)
+        assert np.array_equal(got[j], want), (case, j)
+    # the layout is the all-gather's: copy-out of it gives the gradients back
+    for g, full in zip(grads, O.unpack(p, got)):
+        assert np.array_equal(full, g)
+    # row j equals rank j's own piece: pack of the fp32 widening of its chunk
+    for j in range(n):
+        pj = O.plan(shapes, n, j, align)
+        masters = [O.bf16_to_f32(_chunks_of(torch.from_numpy(g.view(np.int16)), n, j).numpy().view(np.uint16))
+                   for g in grads]
+        assert np.array_equal(O.pack(pj, masters), got[j])
+
+
+def test_pack_reduce_scatter_f32_is_exact_widening_with_zero_padding():
+    shapes, n = SMALL_CASES[1]
+    grads = _bf16_grads(shapes, ("rsp32",))
+    p = O.plan(shapes, n, 2)
+    f = O.pack_reduce_scatter_f32(p, grads)
+    b = O.pack_reduce_scatter(p, grads)
+    assert f.dtype == np.float32 and f.shape == b.shape
+    want = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert np.array_equal(f.view(np.uint32), want.view(np.uint32))
+    pad = np.ones(p.S, bool)
+    for e in p.entries:
+        pad[e.shard_offset:e.shard_offset + e.valid_numel] = False
+    rank2_pad = f[2][pad]
+    assert (rank2_pad.view(np.uint32) == 0).all()
+
+
+@pytest.mark.parametrize("n", [1, 2, 6, 8, 64])
+def test_reduce_f32_error_bound_and_torch(n):
+    shapes = [(3 * n + 1, 5), (2 * n - 1 if n > 1 else 3,)]
+    p = O.plan(shapes, n, n - 1)
+    rng = np.random.default_rng(n)
+    rs = (rng.standard_normal((n, p.S)) * 1e-3).astype(F32)
+    grads = O.reduce_f32(p, rs)
+    u = 2.0 ** -24
+    t = torch.from_numpy(rs)
+    for e, g in zip(p.entries, grads):
+        sl = slice(e.shard_offset, e.shard_offset + e.valid_numel)
+        for i in range(e.valid_numel):
+            xs = [float(rs[j, e.shard_offset + i]) for j in range(n)]
+            exact = math.fsum(xs) / n
+            bound = (n - 1) * u * sum(abs(x) for x in xs) / n + u * abs(exact) + 1e-45
+            assert abs(float(g[i]) - exact) <= bound * 1.0001
+        # torch sums in another order: both are within the summation bound
+        sumabs = t[:, sl].abs().sum(0).numpy().astype(np.float64) / n
+        diff = np.abs(g.astype(np.float64) - (t[:, sl].sum(0) / n).numpy())
+        assert (diff <= 2 * n * u * sumabs + 1e-30).all()
+
+
+def test_reduce_f32_special_cases():
+    # N = 1 is the identity; equal bf16-representable values average exactly
+    p1 = O.plan([(5, 3)], 1, 0)
+    x = np.random.default_rng(0).standard_normal((1, p1.S)).astype(F32)
+    assert np.array_equal(O.reduce_f32(p1, x)[0].reshape(-1).view(np.uint32), x[0].view(np.uint32))
+    p6 = O.plan([(12, 2)], 6, 3)
+    row = O.bf16_to_f32(synth.bf16_bits_to_u16(synth.normal_bf16_bits(p6.S, 1e-3, ("r32eq",))))
+    g = O.reduce_f32(p6, np.tile(row, (6, 1)))[0]
+    e = p6.entries[0]
+    assert np.array_equal(g.view(np.uint32), row[e.shard_offset:e.shard_offset + e.valid_numel].view(np.uint32))
