@@ -331,6 +331,51 @@ fsdp_status fsdp_step_groups(fsdp_plan *const *plans, int32_t n_groups,
                              uint32_t flags, int32_t timed_kernel,
                              void *const *timing_events, void *stream);
 
+/* ---- resharding a checkpoint to another world size --------------------- */
+
+/* [ST] distributed checkpoint paragraph: every rank's Shard(0) chunks are
+ * saved with their place in the global tensor; a loading rank reads only the
+ * chunks that overlap its new placement, so loading into another world size
+ * (2 ranks to 1, N to M) is planning, not conversion.  The reshard plan lists,
+ * for target rank rank_dst of world_dst, the overlap of its rows with every
+ * source rank's rows under world_src (both torch.chunk layouts), as runs of
+ * elements; the executor copies them on the GPU. */
+typedef struct fsdp_reshard_plan fsdp_reshard_plan;
+
+typedef struct fsdp_reshard_run_t {
+    int32_t param;       /* parameter index                                    */
+    int32_t src_rank;    /* source shard the run comes from                    */
+    int64_t src_offset;  /* elements from the start of that source shard       */
+    int64_t dst_offset;  /* elements from the start of the target shard        */
+    int64_t numel;       /* elements in the run (whole rows)                    */
+} fsdp_reshard_run_t;
+
+/* Host only.  rows/cols as in fsdp_plan_create.  Runs come in parameter
+ * order, then row order, and cover the target shard exactly once.
+ * Errors: FSDP_E_INVAL, FSDP_E_NOMEM. */
+fsdp_status fsdp_reshard_plan_create(const int64_t *rows, const int64_t *cols, int32_t n_params,
+                                     int32_t world_src, int32_t world_dst, int32_t rank_dst,
+                                     fsdp_reshard_plan **out);
+/* Number of runs and elements of the target shard (all parameters). */
+fsdp_status fsdp_reshard_plan_runs(const fsdp_reshard_plan *plan, int64_t *n_runs,
+                                   int64_t *dst_numel);
+fsdp_status fsdp_reshard_plan_run(const fsdp_reshard_plan *plan, int64_t i,
+                                  fsdp_reshard_run_t *out);
+/* src: host array of n_params * world_src device pointers, parameter-major
+ * (src[p * world_src + s] = source rank s's shard of parameter p, valid
+ * elements from offset 0); dst: n_params device pointers to the target
+ * shards.  elem_bytes is 2 (bf16) or 4 (fp32); pointers must be aligned to
+ * it and non-NULL wherever a run reads or writes.  Builds and uploads the
+ * copy table on `stream` (allocating device memory); rebinding replaces it.
+ * Errors: FSDP_E_INVAL, FSDP_E_UNSUPPORTED, FSDP_E_ALIGN, FSDP_E_NOMEM,
+ * FSDP_E_HIP. */
+fsdp_status fsdp_reshard_bind(fsdp_reshard_plan *plan, const void *const *src, void *const *dst,
+                              int32_t elem_bytes, void *stream);
+/* Enqueue the copies (one launch).  Errors: FSDP_E_INVAL, FSDP_E_STATE (not
+ * bound, or another device), FSDP_E_HIP. */
+fsdp_status fsdp_reshard_execute(const fsdp_reshard_plan *plan, void *stream);
+void fsdp_reshard_plan_destroy(fsdp_reshard_plan *plan);
+
 /* Wait for `stream` and report any asynchronous HIP error as FSDP_E_HIP. */
 fsdp_status fsdp_check_stream(void *stream);
 

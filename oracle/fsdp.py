@@ -334,6 +334,41 @@ def adamw(param: np.ndarray, grad: np.ndarray, exp_avg: np.ndarray,
 
 
 # ---------------------------------------------------------------------------
+# Resharding (distributed checkpoint load into another world size)
+# ---------------------------------------------------------------------------
+
+def reshard_runs(rows: int, cols: int, world_src: int, world_dst: int, rank_dst: int):
+    """Row overlaps rank ``rank_dst`` of ``world_dst`` reads from each source rank.
+
+    A checkpoint saved by world_src ranks holds chunk s of every parameter in
+    shard s; loading into world_dst ranks, each target rank reads only the
+    chunks that overlap its own rows, so resharding is planning, not
+    conversion ([ST] distributed checkpoint paragraph: 2 ranks to 1, FSDP to
+    FSDP+TP).  Returns (src_rank, src_offset, dst_offset, numel) in elements,
+    offsets relative to the start of each shard, in row order.
+    """
+    b2, l2 = rows_of_rank(rows, world_dst, rank_dst)
+    runs = []
+    for s in range(world_src):
+        b1, l1 = rows_of_rank(rows, world_src, s)
+        lo, hi = max(b1, b2), min(b1 + l1, b2 + l2)
+        if hi > lo:
+            runs.append((s, (lo - b1) * cols, (lo - b2) * cols, (hi - lo) * cols))
+    return runs
+
+
+def reshard(src_shards: Sequence[np.ndarray], rows: int, cols: int, world_dst: int,
+            rank_dst: int) -> np.ndarray:
+    """Target rank's shard: the unsharded rows (concatenation of the source
+    shards in rank order) cut by torch.chunk for the new world size."""
+    full = np.concatenate([np.asarray(x).reshape(-1) for x in src_shards])
+    if full.size != rows * cols:
+        raise ValueError("source shards do not add up to the parameter")
+    b, lr = rows_of_rank(rows, world_dst, rank_dst)
+    return full[b * cols:(b + lr) * cols].copy()
+
+
+# ---------------------------------------------------------------------------
 # State accounting
 # ---------------------------------------------------------------------------
 

@@ -30,6 +30,7 @@ DEVICE = [f"--offload-arch={ARCH}", "-ffp-contract=off",
 SOURCES = [
     ("plan.cpp", ["-x", "c++"]),
     ("capi.cpp", ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROCM, "include")]),
+    ("reshard.cpp", ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROCM, "include")]),
     ("kernels.hip", ["-x", "hip"] + DEVICE),
 ]
 

@@ -59,6 +59,11 @@ class PlanInfo(ctypes.Structure):
                 ("n_empty", _i32), ("bound", _i32), ("n_tiles", _i64 * 4)]
 
 
+class ReshardRun(ctypes.Structure):
+    _fields_ = [("param", _i32), ("src_rank", _i32), ("src_offset", _i64), ("dst_offset", _i64),
+                ("numel", _i64)]
+
+
 class AdamwHparams(ctypes.Structure):
     _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
                 ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double)]
@@ -104,6 +109,13 @@ _SIGS = {
     "fsdp_bind_full_grad": (_i32, [_P, _PP, _P]),
     "fsdp_pack_reduce_scatter": (_i32, [_P, _P, _i32, _P]),
     "fsdp_reduce_shard_f32": (_i32, [_P, _P, _P]),
+    "fsdp_reshard_plan_create": (_i32, [ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i32, _i32,
+                                        _i32, _i32, ctypes.POINTER(_P)]),
+    "fsdp_reshard_plan_runs": (_i32, [_P, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
+    "fsdp_reshard_plan_run": (_i32, [_P, _i64, ctypes.POINTER(ReshardRun)]),
+    "fsdp_reshard_bind": (_i32, [_P, _PP, _PP, _i32, _P]),
+    "fsdp_reshard_execute": (_i32, [_P, _P]),
+    "fsdp_reshard_plan_destroy": (None, [_P]),
     "fsdp_step_groups": (_i32, [_PP, _i32, _PP, _PP, _PP, ctypes.POINTER(AdamwHparams), _i64,
                                 ctypes.c_uint32, _i32, _PP, _P]),
     "fsdp_check_stream": (_i32, [_P]),
@@ -258,6 +270,42 @@ def fsdp_step_shard(plan, rs_in, ag_in, lr: float, beta1: float, beta2: float, e
     hp = AdamwHparams(lr, beta1, beta2, eps, weight_decay)
     _check(lib.fsdp_step_shard(plan, addr(rs_in), addr(ag_in), ctypes.byref(hp), step, flags,
                                stream_handle(stream)), "fsdp_step_shard")
+
+
+def fsdp_reshard_plan_create(rows, cols, world_src: int, world_dst: int, rank_dst: int):
+    n = len(rows)
+    r = (_i64 * max(1, n))(*rows)
+    c = (_i64 * max(1, n))(*cols)
+    out = _P()
+    _check(lib.fsdp_reshard_plan_create(r, c, n, world_src, world_dst, rank_dst, ctypes.byref(out)),
+           "fsdp_reshard_plan_create")
+    return out
+
+
+def fsdp_reshard_plan_runs(plan):
+    n, d = _i64(), _i64()
+    _check(lib.fsdp_reshard_plan_runs(plan, ctypes.byref(n), ctypes.byref(d)), "fsdp_reshard_plan_runs")
+    return n.value, d.value
+
+
+def fsdp_reshard_plan_run(plan, i: int) -> ReshardRun:
+    r = ReshardRun()
+    _check(lib.fsdp_reshard_plan_run(plan, i, ctypes.byref(r)), "fsdp_reshard_plan_run")
+    return r
+
+
+def fsdp_reshard_bind(plan, src, dst, elem_bytes: int, stream=None) -> None:
+    """src: flat list, parameter-major (param p, source rank s at p*world_src+s)."""
+    _check(lib.fsdp_reshard_bind(plan, _ptr_array(src), _ptr_array(dst), elem_bytes,
+                                 stream_handle(stream)), "fsdp_reshard_bind")
+
+
+def fsdp_reshard_execute(plan, stream=None) -> None:
+    _check(lib.fsdp_reshard_execute(plan, stream_handle(stream)), "fsdp_reshard_execute")
+
+
+def fsdp_reshard_plan_destroy(plan) -> None:
+    lib.fsdp_reshard_plan_destroy(plan)
 
 
 class StepGroupsCall:

@@ -162,6 +162,11 @@ fsdp_status commit_entries(fsdp_plan *p, std::vector<fsdp::DevEntry> ents, int32
 
 }  // namespace
 
+namespace fsdp {
+// Error reporting shared with the other translation units of the library.
+fsdp_status set_error(fsdp_status s, const std::string &msg) { return fail(s, msg); }
+}  // namespace fsdp
+
 extern "C" {
 
 int32_t fsdp_abi_version(void) { return FSDP_ABI_VERSION; }

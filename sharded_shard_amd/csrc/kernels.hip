@@ -290,6 +290,23 @@ __global__ __launch_bounds__(kBlock) void unpack_kernel(
     }
 }
 
+// Resharding: runs of 2-byte units between absolute addresses.
+template <int POL>
+__global__ __launch_bounds__(kBlock) void copy_runs_kernel(const CopyTile *__restrict__ tiles,
+                                                           int64_t n_tiles, int32_t split,
+                                                           int64_t sub) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
+        const CopyTile tl = tiles[t];
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        copy_run_bf16<POL>(tl.dst + b, tl.src + b, len);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // copy-in: fp32 master shards -> bf16 segment (zeros in padding)
 // ---------------------------------------------------------------------------
@@ -987,6 +1004,14 @@ hipError_t launch_adamw(const EwTile *tiles, int64_t n, const DevEntry *ents,
     const int32_t sp = split_for(kTileAdamw, FSDP_ADAMW_SUB);
     adamw_kernel<FSDP_ADAMW_POL><<<grid_for(n, sp), kBlock, 0, st>>>(
         tiles, n, sp, kTileAdamw / sp, ents, to_scalars(scal));
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_runs(const CopyTile *tiles, int64_t n, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const int32_t sp = split_for(kTileUnpack, FSDP_UNPACK_SUB);
+    copy_runs_kernel<FSDP_UNPACK_POL>
+        <<<grid_for(n, sp), kBlock, 0, st>>>(tiles, n, sp, kTileUnpack / sp);
     return hipGetLastError();
 }
 

@@ -84,6 +84,15 @@ struct ReduceTile {
 };
 static_assert(sizeof(ReduceTile) == 32, "ReduceTile layout");
 
+// Generic copy of 2-byte units between absolute device addresses (resharding).
+struct CopyTile {
+    const uint16_t *src;
+    uint16_t *dst;
+    int64_t len;
+    int64_t rsv;
+};
+static_assert(sizeof(CopyTile) == 32, "CopyTile layout");
+
 // AdamW: elements [off .. off+len) of one parameter's shards.
 struct EwTile {
     int64_t off;

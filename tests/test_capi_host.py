@@ -204,3 +204,47 @@ def test_step_groups_rejects_bad_arguments_without_gpu():
         assert ei.value.status == capi.FSDP_E_INVAL
     finally:
         capi.fsdp_plan_destroy(p)
+
+
+@pytest.mark.parametrize("n1,n2", [(2, 1), (1, 2), (3, 2), (8, 64), (64, 8), (6, 4), (5, 5)])
+def test_reshard_planner_matches_oracle(n1, n2):
+    shapes = [(37, 3), (1, 5), (0, 4), (130, 1), (128256 // 64, 2), (64, 7)]
+    rows = [s[0] for s in shapes]
+    cols = [s[1] for s in shapes]
+    for d in range(n2):
+        p = capi.fsdp_reshard_plan_create(rows, cols, n1, n2, d)
+        try:
+            want = [(i,) + r for i, (rr, cc) in enumerate(shapes)
+                    for r in O.reshard_runs(rr, cc, n1, n2, d)]
+            n_runs, dst_numel = capi.fsdp_reshard_plan_runs(p)
+            assert n_runs == len(want)
+            assert dst_numel == sum(O.rows_of_rank(rr, n2, d)[1] * cc for rr, cc in shapes)
+            for k, w in enumerate(want):
+                r = capi.fsdp_reshard_plan_run(p, k)
+                assert (r.param, r.src_rank, r.src_offset, r.dst_offset, r.numel) == w
+        finally:
+            capi.fsdp_reshard_plan_destroy(p)
+
+
+def test_reshard_plan_errors():
+    for args in (([4], [1], 0, 1, 0), ([4], [1], 1, 0, 0), ([4], [1], 2, 2, 2), ([-1], [1], 2, 2, 0),
+                 ([4], [0], 2, 2, 0)):
+        with pytest.raises(capi.FsdpError) as ei:
+            capi.fsdp_reshard_plan_create(*args)
+        assert ei.value.status == capi.FSDP_E_INVAL
+    p = capi.fsdp_reshard_plan_create([4], [2], 2, 1, 0)
+    try:
+        with pytest.raises(capi.FsdpError) as ei:
+            capi.fsdp_reshard_execute(p, 0)
+        assert ei.value.status == capi.FSDP_E_STATE
+        with pytest.raises(capi.FsdpError) as ei:
+            capi.fsdp_reshard_bind(p, [0x1000, 0x2000], [0x3000], 8, 0)
+        assert ei.value.status == capi.FSDP_E_UNSUPPORTED
+        with pytest.raises(capi.FsdpError) as ei:
+            capi.fsdp_reshard_bind(p, [0x1000, 0x2002], [0x3000], 4, 0)
+        assert ei.value.status == capi.FSDP_E_ALIGN
+        with pytest.raises(capi.FsdpError) as ei:
+            capi.fsdp_reshard_bind(p, [0x1000, 0], [0x3000], 4, 0)
+        assert ei.value.status == capi.FSDP_E_INVAL
+    finally:
+        capi.fsdp_reshard_plan_destroy(p)

@@ -720,3 +720,57 @@ def test_reduce_f32_of_widened_copy_in_equals_bf16_reduce(n):
     torch.cuda.synchronize()
     assert torch.equal(ref.view(torch.int32), g.grad_flat.view(torch.int32))
     g.close()
+
+
+# ---------------------------------------------------------------------------
+# resharding to another world size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("elem", [2, 4], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("n1,n2", [(2, 1), (1, 3), (8, 64), (64, 8), (6, 4), (3, 5)])
+def test_reshard_execute_matches_oracle(n1, n2, elem):
+    shapes = [(37, 3), (1, 5), (0, 4), (1031,), (200, 67), (64, 7)]
+    rows = [s[0] for s in shapes]
+    cols = [int(np.prod(s[1:])) if len(s) > 1 else 1 for s in shapes]
+    dt = torch.int16 if elem == 2 else torch.int32
+    rng = np.random.default_rng(n1 * 100 + n2)
+    fulls = [rng.integers(-2**15, 2**15 - 1 if elem == 2 else 2**15, size=r * c).astype(
+        np.int16 if elem == 2 else np.int32) for r, c in zip(rows, cols)]
+    for shift in (0, 1):
+        # source shards, each at its own (possibly misaligned) offset in one buffer
+        total = sum(f.size for f in fulls) + 64 * len(fulls) * n1
+        src_buf = torch.zeros(total, dtype=dt, device=DEV)
+        src_ptrs, o = [], shift
+        for f, r, c in zip(fulls, rows, cols):
+            for s in range(n1):
+                b, lr = O.rows_of_rank(r, n1, s)
+                piece = f[b * c:(b + lr) * c]
+                src_buf[o:o + piece.size].copy_(torch.from_numpy(piece))
+                src_ptrs.append(src_buf[o:].data_ptr() if piece.size else 0)
+                o += piece.size + 3
+        for d in sorted({0, n2 - 1, n2 // 2}):
+            p = capi.fsdp_reshard_plan_create(rows, cols, n1, n2, d)
+            dst_buf = torch.full((sum(f.size for f in fulls) + 64 * len(fulls),), -5, dtype=dt, device=DEV)
+            dst_views, o = [], shift
+            for r, c in zip(rows, cols):
+                k = O.rows_of_rank(r, n2, d)[1] * c
+                dst_views.append(dst_buf[o:o + k])
+                o += k + 5
+            capi.fsdp_reshard_bind(p, src_ptrs, [v.data_ptr() if v.numel() else 0 for v in dst_views],
+                                   elem, None)
+            capi.fsdp_reshard_execute(p)
+            torch.cuda.synchronize()
+            for f, r, c, v in zip(fulls, rows, cols, dst_views):
+                src = [f[O.rows_of_rank(r, n1, s)[0] * c:(O.rows_of_rank(r, n1, s)[0] + O.rows_of_rank(r, n1, s)[1]) * c]
+                       for s in range(n1)]
+                want = O.reshard(src, r, c, n2, d)
+                assert np.array_equal(v.cpu().numpy(), want), (n1, n2, d, r, shift)
+            # nothing outside the target views was touched
+            h = dst_buf.cpu().numpy()
+            mask = np.ones(h.size, bool)
+            o = shift
+            for v in dst_views:
+                mask[o:o + v.numel()] = False
+                o += v.numel() + 5
+            assert (h[mask] == -5).all()
+            capi.fsdp_reshard_plan_destroy(p)

@@ -639,3 +639,43 @@ def test_reduce_f32_special_cases():
     g = O.reduce_f32(p6, np.tile(row, (6, 1)))[0]
     e = p6.entries[0]
     assert np.array_equal(g.view(np.uint32), row[e.shard_offset:e.shard_offset + e.valid_numel].view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# resharding a checkpoint to another world size
+# ---------------------------------------------------------------------------
+
+def _torch_shards(W, n):
+    return [_chunks_of(W, n, j).contiguous() for j in range(n)]
+
+
+@pytest.mark.parametrize("n1,n2", [(2, 1), (1, 2), (2, 3), (3, 2), (4, 6), (6, 4), (8, 64), (64, 8), (5, 5)])
+def test_reshard_matches_torch_rechunk(n1, n2):
+    for rows, cols in [(37, 3), (1, 5), (0, 4), (130, 1), (64, 2)]:
+        W = torch.arange(rows * cols, dtype=torch.int32).reshape(rows, cols)
+        src = [t.numpy() for t in _torch_shards(W, n1)]
+        for d in range(n2):
+            got = O.reshard(src, rows, cols, n2, d)
+            want = _chunks_of(W, n2, d).reshape(-1).numpy()
+            assert np.array_equal(got, want), (rows, n1, n2, d)
+            # the runs say where every target element comes from, once
+            runs = O.reshard_runs(rows, cols, n1, n2, d)
+            cover = np.zeros(want.size, dtype=int)
+            for s, so, do, k in runs:
+                assert np.array_equal(src[s].reshape(-1)[so:so + k], want[do:do + k])
+                cover[do:do + k] += 1
+            assert (cover == 1).all()
+            assert [r[2] for r in runs] == sorted(r[2] for r in runs)
+
+
+def test_reshard_two_ranks_to_one_is_the_full_tensor_and_round_trips():
+    # the checkpoint page's example: two shards reloaded into a plain model
+    W = np.random.default_rng(1).standard_normal((33, 7)).astype(F32)
+    src = [x.numpy() for x in _torch_shards(torch.from_numpy(W), 2)]
+    assert np.array_equal(O.reshard(src, 33, 7, 1, 0).reshape(33, 7), W)
+    for n1, n2 in [(2, 5), (8, 3), (6, 64)]:
+        s1 = [x.numpy() for x in _torch_shards(torch.from_numpy(W), n1)]
+        s2 = [O.reshard(s1, 33, 7, n2, d) for d in range(n2)]
+        back = [O.reshard(s2, 33, 7, n1, d) for d in range(n1)]
+        for a, b in zip(back, s1):
+            assert np.array_equal(a, b.reshape(-1))
