@@ -232,7 +232,29 @@ def measure_next(groups, n, rs_bf16, full_arena, stream, reps):
                      "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
     capi.fsdp_reshard_plan_destroy(rplan)
     del rs_f32, dst
+    res["adamw_host_cpu_offload"] = measure_host_adamw()
     return res
+
+
+def measure_host_adamw(n=1 << 25, reps=3):
+    """CPU-offload AdamW on 32M host fp32 elements (28 B each per step): the
+    rate of host memory, on every hardware thread the process may use."""
+    import numpy as np
+    from sharded_shard_amd import capi
+    rng = np.random.default_rng(0)
+    p = rng.standard_normal(n, dtype=np.float32) * np.float32(0.02)
+    g = rng.standard_normal(n, dtype=np.float32) * np.float32(1e-3)
+    m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    threads = len(os.sched_getaffinity(0))
+    best = None
+    for t in range(1, reps + 2):
+        t0 = time.perf_counter()
+        capi.fsdp_adamw_host(p, g, m, v, 3e-4, 0.9, 0.999, 1e-8, 0.01, step=t, n_threads=threads)
+        dt = time.perf_counter() - t0
+        if t > 1:
+            best = dt if best is None else min(best, dt)
+    return {"ms": round(best * 1e3, 3), "elements": n, "threads": threads,
+            "host_GBps": round(28 * n / best / 1e9, 1), "note": "host DRAM, not HBM"}
 
 
 def main():

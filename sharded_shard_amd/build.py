@@ -30,6 +30,7 @@ DEVICE = [f"--offload-arch={ARCH}", "-ffp-contract=off",
 SOURCES = [
     ("plan.cpp", ["-x", "c++"]),
     ("capi.cpp", ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROCM, "include")]),
+    ("host_adamw.cpp", ["-x", "c++", "-ffp-contract=off", "-fno-fast-math", "-pthread"]),
     ("reshard.cpp", ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROCM, "include")]),
     ("kernels.hip", ["-x", "hip"] + DEVICE),
 ]
@@ -59,7 +60,7 @@ def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
         _run([HIPCC, *COMMON, *flags, *extra_flags, "-c", src, "-o", obj], verbose)
         objs.append(obj)
     tmp = out + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *objs, "-o", tmp], verbose)
     os.replace(tmp, out)
     for o in objs:
         os.remove(o)

@@ -116,6 +116,7 @@ _SIGS = {
     "fsdp_reshard_bind": (_i32, [_P, _PP, _PP, _i32, _P]),
     "fsdp_reshard_execute": (_i32, [_P, _P]),
     "fsdp_reshard_plan_destroy": (None, [_P]),
+    "fsdp_adamw_host": (_i32, [_P, _P, _P, _P, _i64, ctypes.POINTER(AdamwHparams), _i64, _i32]),
     "fsdp_step_groups": (_i32, [_PP, _i32, _PP, _PP, _PP, ctypes.POINTER(AdamwHparams), _i64,
                                 ctypes.c_uint32, _i32, _PP, _P]),
     "fsdp_check_stream": (_i32, [_P]),
@@ -137,7 +138,9 @@ def addr(x) -> int:
         return 0
     if isinstance(x, int):
         return x
-    return int(x.data_ptr())
+    if hasattr(x, "data_ptr"):
+        return int(x.data_ptr())
+    return int(x.ctypes.data)          # a NumPy array
 
 
 def stream_handle(stream=None) -> int:
@@ -270,6 +273,19 @@ def fsdp_step_shard(plan, rs_in, ag_in, lr: float, beta1: float, beta2: float, e
     hp = AdamwHparams(lr, beta1, beta2, eps, weight_decay)
     _check(lib.fsdp_step_shard(plan, addr(rs_in), addr(ag_in), ctypes.byref(hp), step, flags,
                                stream_handle(stream)), "fsdp_step_shard")
+
+
+def fsdp_adamw_host(p, g, m, v, lr: float, beta1: float, beta2: float, eps: float,
+                    weight_decay: float, step: int, n_threads: int = 0) -> None:
+    """p, g, m, v: contiguous fp32 host arrays (NumPy or CPU tensors) of equal size."""
+    n = int(p.numel() if hasattr(p, "numel") and callable(p.numel) else p.size)
+    for a in (g, m, v):
+        k = int(a.numel() if hasattr(a, "numel") and callable(a.numel) else a.size)
+        if k != n:
+            raise ValueError("p, g, m and v must have the same size")
+    hp = AdamwHparams(lr, beta1, beta2, eps, weight_decay)
+    _check(lib.fsdp_adamw_host(addr(p), addr(g), addr(m), addr(v), n, ctypes.byref(hp), step,
+                               n_threads), "fsdp_adamw_host")
 
 
 def fsdp_reshard_plan_create(rows, cols, world_src: int, world_dst: int, rank_dst: int):

@@ -163,8 +163,11 @@ fsdp_status commit_entries(fsdp_plan *p, std::vector<fsdp::DevEntry> ents, int32
 }  // namespace
 
 namespace fsdp {
-// Error reporting shared with the other translation units of the library.
+// Error reporting and AdamW scalars shared with the other translation units.
 fsdp_status set_error(fsdp_status s, const std::string &msg) { return fail(s, msg); }
+void adamw_scalars_host(const fsdp_adamw_hparams_t *hp, int64_t step, float out[8]) {
+    adamw_scalars(hp, step, out);
+}
 }  // namespace fsdp
 
 extern "C" {

@@ -248,3 +248,28 @@ def test_reshard_plan_errors():
         assert ei.value.status == capi.FSDP_E_INVAL
     finally:
         capi.fsdp_reshard_plan_destroy(p)
+
+
+@pytest.mark.parametrize("n_threads", [1, 3, 0])
+def test_host_adamw_bit_exact_with_oracle(n_threads):
+    from workloads import synth
+    HP = dict(lr=3e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    for n in (0, 1, 7, 65537, 300001):
+        p = synth.normal_f32(n, 0.02, ("hostadam", n)).numpy().copy()
+        m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
+        ref = [p.copy(), m.copy(), v.copy()]
+        for t in (1, 2, 3):
+            g = synth.normal_f32(n, 1e-3, ("hostadam-g", n, t)).numpy()
+            capi.fsdp_adamw_host(p, g, m, v, step=t, n_threads=n_threads, **HP)
+            O.adamw(ref[0], g, ref[1], ref[2], t, **HP)
+        for a, b in zip((p, m, v), ref):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), (n, n_threads)
+
+
+def test_host_adamw_errors():
+    x = np.zeros(4, np.float32)
+    with pytest.raises(capi.FsdpError) as ei:
+        capi.fsdp_adamw_host(x, x, x, x, 3e-4, 0.9, 0.999, 1e-8, 0.01, step=0)
+    assert ei.value.status == capi.FSDP_E_INVAL
+    with pytest.raises(ValueError):
+        capi.fsdp_adamw_host(x, x[:3], x, x, 3e-4, 0.9, 0.999, 1e-8, 0.01, step=1)
