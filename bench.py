@@ -185,8 +185,11 @@ def measure_next(groups, n, rs_bf16, full_arena, stream, reps):
 
     max_ns = max(n * g.S for g in groups)
     rs_f32 = torch.empty(max_ns, dtype=torch.float32, device=full_arena.device)
+    acc_arena = torch.zeros(max(g.full_space for g in groups), dtype=torch.float32,
+                            device=full_arena.device)
     for g in groups:
         g.bind_full_grad(full_arena, stream)
+        g.bind_grad_acc(acc_arena, stream)
     kinds = {
         "rs_copy_in_bf16": (lambda g: g.pack_reduce_scatter(rs_bf16[:n * g.S], capi.FSDP_DTYPE_BF16, stream),
                             lambda g: 2 * g.F + 2 * n * g.S),
@@ -194,6 +197,9 @@ def measure_next(groups, n, rs_bf16, full_arena, stream, reps):
                            lambda g: 2 * g.F + 4 * n * g.S),
         "reduce_f32": (lambda g: g.reduce_f32(rs_f32[:n * g.S], stream),
                        lambda g: 4 * n * g.V + 4 * g.V),
+        "grad_accumulate": (lambda g: g.accumulate_grad(False, stream), lambda g: 10 * g.F),
+        "rs_copy_in_from_acc": (lambda g: g.pack_reduce_scatter_acc(rs_f32[:n * g.S], stream),
+                                lambda g: 4 * g.F + 4 * n * g.S),
     }
     # resharding: load the first group's fp32 shards, saved by N ranks (the
     # rows of rs_f32 as [N, S] segments), into rank 0 of N/2 ranks
@@ -231,7 +237,7 @@ def measure_next(groups, n, rs_bf16, full_arena, stream, reps):
         res[name] = {"ms_per_step": round(ms, 4), "algorithmic_GB_per_step": round(byts / 1e9, 4),
                      "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
     capi.fsdp_reshard_plan_destroy(rplan)
-    del rs_f32, dst
+    del rs_f32, dst, acc_arena
     res["adamw_host_cpu_offload"] = measure_host_adamw()
     return res
 

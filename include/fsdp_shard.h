@@ -113,7 +113,8 @@ enum {
     FSDP_ROLE_EXP_AVG = 4,
     FSDP_ROLE_EXP_AVG_SQ = 8,
     FSDP_ROLE_FULL = 16,
-    FSDP_ROLE_FULL_GRAD = 32
+    FSDP_ROLE_FULL_GRAD = 32,
+    FSDP_ROLE_GRAD_ACC = 64
 };
 
 /* Element types of the reduce-scatter buffers. */
@@ -197,6 +198,11 @@ fsdp_status fsdp_bind(fsdp_plan *plan, float *const *master, float *const *grad,
  * Errors: FSDP_E_INVAL, FSDP_E_ALIGN, FSDP_E_NOMEM, FSDP_E_HIP. */
 fsdp_status fsdp_bind_full_grad(fsdp_plan *plan, uint16_t *const *full_grad, void *stream);
 
+/* Bind each parameter's unsharded fp32 gradient accumulator [rows, cols]
+ * (gradient accumulation without sync).  Same rules as
+ * fsdp_bind_full_grad, 4-byte aligned pointers. */
+fsdp_status fsdp_bind_grad_acc(fsdp_plan *plan, float *const *grad_acc, void *stream);
+
 /* ---- hot path: enqueue on `stream`; no sync, no allocation ------------- */
 
 /* All-gather copy-in.  Writes all S elements of ag_in: for each parameter,
@@ -247,6 +253,23 @@ fsdp_status fsdp_reduce_shard(const fsdp_plan *plan, const uint16_t *rs_in,
  * (dtype), FSDP_E_ALIGN, FSDP_E_STATE, FSDP_E_HIP. */
 fsdp_status fsdp_pack_reduce_scatter(const fsdp_plan *plan, void *rs_out, int32_t dtype,
                                      void *stream);
+
+/* Gradient accumulation without sync ([ST] "Other controls":
+ * set_requires_gradient_sync(False) accumulates unsharded gradients and
+ * skips the reduce-scatter): for every element of every parameter,
+ *     acc = reset ? fp32(g) : acc + fp32(g)
+ * with g the bound bf16 unsharded gradient and acc the bound fp32
+ * accumulator (reduce_dtype), one fp32 rounding per add.
+ * Needs FSDP_ROLE_FULL_GRAD | FSDP_ROLE_GRAD_ACC.
+ * Errors: FSDP_E_INVAL, FSDP_E_STATE, FSDP_E_HIP. */
+fsdp_status fsdp_accumulate_grad(const fsdp_plan *plan, int32_t reset, void *stream);
+
+/* Reduce-scatter copy-in of the synchronizing microbatch from the fp32
+ * accumulators: the [N, S] fp32 layout of fsdp_pack_reduce_scatter (row j =
+ * chunk j of every parameter, +0.0 padding), values copied from acc.
+ * Needs FSDP_ROLE_GRAD_ACC.  Errors: FSDP_E_INVAL, FSDP_E_ALIGN (4 bytes),
+ * FSDP_E_STATE, FSDP_E_HIP. */
+fsdp_status fsdp_pack_reduce_scatter_acc(const fsdp_plan *plan, float *rs_out, void *stream);
 
 /* fsdp_reduce_shard for fp32 contributions (reduce_dtype = fp32 on the
  * wire): grad[i] = ((x_0 + x_1) + ... + x_{N-1}) / N with x_j = rs_in[j][off+i]

@@ -260,6 +260,40 @@ def pack_reduce_scatter_f32(p: Plan, full_grads: Sequence[np.ndarray]) -> np.nda
     return bf16_to_f32(pack_reduce_scatter(p, full_grads))
 
 
+def accumulate_grad(acc, full_grads, reset: bool) -> List[np.ndarray]:
+    """Gradient accumulation without sync: fp32 acc <- acc + fp32(g).
+
+    With set_requires_gradient_sync(False) the unsharded gradients of
+    successive microbatches accumulate and no reduce-scatter runs ([ST] "Other
+    controls").  The sum is kept in reduce_dtype = fp32; the first microbatch
+    (reset) stores the exact widening of its gradient.
+    """
+    out = []
+    for i, g in enumerate(full_grads):
+        x = bf16_to_f32(np.asarray(g, dtype=np.uint16).reshape(-1))
+        if reset:
+            out.append(x.copy())
+        else:
+            out.append((np.asarray(acc[i], dtype=F32).reshape(-1) + x).astype(F32))
+    return out
+
+
+def pack_reduce_scatter_acc(p: Plan, acc: Sequence[np.ndarray]) -> np.ndarray:
+    """Reduce-scatter copy-in from the fp32 accumulators (the synchronizing
+    microbatch): the layout of ``pack_reduce_scatter`` with fp32 values and
+    +0.0 padding."""
+    out = np.zeros((p.world, p.S), dtype=F32)
+    for e, a in zip(p.entries, acc):
+        flat = np.asarray(a, dtype=F32).reshape(-1)
+        if flat.size != e.rows * e.cols:
+            raise ValueError("accumulator has the wrong size")
+        for j in range(p.world):
+            b, lr = rows_of_rank(e.rows, p.world, j)
+            n = lr * e.cols
+            out[j, e.shard_offset:e.shard_offset + n] = flat[b * e.cols:b * e.cols + n]
+    return out
+
+
 def reduce_f32(p: Plan, rs_in: np.ndarray) -> List[np.ndarray]:
     """Local reduction of fp32 contributions (reduce_dtype = fp32 on the wire):
     fp32 sum in rank order from rank 0's value, then one division by N, as

@@ -30,6 +30,7 @@ FSDP_ROLE_EXP_AVG = 4
 FSDP_ROLE_EXP_AVG_SQ = 8
 FSDP_ROLE_FULL = 16
 FSDP_ROLE_FULL_GRAD = 32
+FSDP_ROLE_GRAD_ACC = 64
 
 FSDP_DTYPE_BF16 = 0
 FSDP_DTYPE_F32 = 1
@@ -108,6 +109,9 @@ _SIGS = {
     "fsdp_step_shard": (_i32, [_P, _P, _P, ctypes.POINTER(AdamwHparams), _i64, ctypes.c_uint32, _P]),
     "fsdp_bind_full_grad": (_i32, [_P, _PP, _P]),
     "fsdp_pack_reduce_scatter": (_i32, [_P, _P, _i32, _P]),
+    "fsdp_bind_grad_acc": (_i32, [_P, _PP, _P]),
+    "fsdp_accumulate_grad": (_i32, [_P, _i32, _P]),
+    "fsdp_pack_reduce_scatter_acc": (_i32, [_P, _P, _P]),
     "fsdp_reduce_shard_f32": (_i32, [_P, _P, _P]),
     "fsdp_reshard_plan_create": (_i32, [ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i32, _i32,
                                         _i32, _i32, ctypes.POINTER(_P)]),
@@ -239,6 +243,21 @@ def fsdp_bind_full_grad(plan, full_grad, stream=None) -> None:
 def fsdp_pack_reduce_scatter(plan, rs_out, dtype: int = FSDP_DTYPE_BF16, stream=None) -> None:
     _check(lib.fsdp_pack_reduce_scatter(plan, addr(rs_out), dtype, stream_handle(stream)),
            "fsdp_pack_reduce_scatter")
+
+
+def fsdp_bind_grad_acc(plan, grad_acc, stream=None) -> None:
+    _check(lib.fsdp_bind_grad_acc(plan, _ptr_array(grad_acc), stream_handle(stream)),
+           "fsdp_bind_grad_acc")
+
+
+def fsdp_accumulate_grad(plan, reset: bool, stream=None) -> None:
+    _check(lib.fsdp_accumulate_grad(plan, 1 if reset else 0, stream_handle(stream)),
+           "fsdp_accumulate_grad")
+
+
+def fsdp_pack_reduce_scatter_acc(plan, rs_out, stream=None) -> None:
+    _check(lib.fsdp_pack_reduce_scatter_acc(plan, addr(rs_out), stream_handle(stream)),
+           "fsdp_pack_reduce_scatter_acc")
 
 
 def fsdp_reduce_shard_f32(plan, rs_in, stream=None) -> None:

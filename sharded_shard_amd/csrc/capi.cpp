@@ -31,6 +31,10 @@ hipError_t launch_rspack(const PackTile *tiles, int64_t n, const DevEntry *ents,
                          bool f32, hipStream_t st);
 hipError_t launch_reduce_f32(const ReduceTile *tiles, int64_t n, const DevEntry *ents,
                              const float *rs_in, int64_t S, int32_t N, hipStream_t st);
+hipError_t launch_accumulate(const EwTile *tiles, int64_t n, const DevEntry *ents, bool reset,
+                             hipStream_t st);
+hipError_t launch_rspack_acc(const PackTile *tiles, int64_t n, const DevEntry *ents, float *out,
+                             hipStream_t st);
 }  // namespace fsdp
 
 struct fsdp_plan {
@@ -45,6 +49,7 @@ struct fsdp_plan {
     fsdp::UnpackTile *d_unpack = nullptr;
     fsdp::ReduceTile *d_reduce = nullptr;
     fsdp::EwTile *d_adamw = nullptr;
+    fsdp::EwTile *d_full = nullptr;
 };
 
 namespace {
@@ -116,7 +121,7 @@ fsdp_status commit_entries(fsdp_plan *p, std::vector<fsdp::DevEntry> ents, int32
         void **dst;
         const void *src;
         size_t bytes;
-    } tabs[6] = {
+    } tabs[7] = {
         {reinterpret_cast<void **>(&p->d_entries), nullptr, n * sizeof(fsdp::DevEntry)},
         {reinterpret_cast<void **>(&p->d_pack), p->L.pack.data(),
          p->L.pack.size() * sizeof(fsdp::PackTile)},
@@ -128,6 +133,8 @@ fsdp_status commit_entries(fsdp_plan *p, std::vector<fsdp::DevEntry> ents, int32
          p->L.reduce.size() * sizeof(fsdp::ReduceTile)},
         {reinterpret_cast<void **>(&p->d_adamw), p->L.adamw.data(),
          p->L.adamw.size() * sizeof(fsdp::EwTile)},
+        {reinterpret_cast<void **>(&p->d_full), p->L.full.data(),
+         p->L.full.size() * sizeof(fsdp::EwTile)},
     };
     const bool first = p->dmem == nullptr;
     if (first) {
@@ -147,7 +154,7 @@ fsdp_status commit_entries(fsdp_plan *p, std::vector<fsdp::DevEntry> ents, int32
     // Kernels of this plan still queued on the stream may read the tables.
     e = hipStreamSynchronize(st);
     if (e != hipSuccess) return hip_fail(e, (c + ": hipStreamSynchronize").c_str());
-    for (int k = 0; k < (first ? 6 : 1); ++k) {
+    for (int k = 0; k < (first ? 7 : 1); ++k) {
         if (tabs[k].bytes == 0) continue;
         const void *src = k == 0 ? static_cast<const void *>(ents.data()) : tabs[k].src;
         e = hipMemcpyAsync(*tabs[k].dst, src, tabs[k].bytes, hipMemcpyHostToDevice, st);
@@ -333,6 +340,24 @@ fsdp_status fsdp_bind(fsdp_plan *p, float *const *master, float *const *grad,
                           "fsdp_bind");
 }
 
+fsdp_status fsdp_bind_grad_acc(fsdp_plan *p, float *const *grad_acc, void *stream) {
+    if (p == nullptr || grad_acc == nullptr)
+        return fail(FSDP_E_INVAL, "fsdp_bind_grad_acc: null plan or array");
+    std::vector<fsdp::DevEntry> ents = p->host_entries;
+    for (size_t i = 0; i < ents.size(); ++i) {
+        const fsdp_shard_entry_t &e = p->L.entries[i];
+        if (grad_acc[i] == nullptr && e.rows * e.cols > 0)
+            return fail(FSDP_E_INVAL, "fsdp_bind_grad_acc: null pointer for parameter " +
+                                          std::to_string(i));
+        if (misaligned(grad_acc[i], 4))
+            return fail(FSDP_E_ALIGN, "fsdp_bind_grad_acc: pointer of parameter " +
+                                          std::to_string(i) + " is not 4-byte aligned");
+        ents[i].grad_acc = grad_acc[i];
+    }
+    return commit_entries(p, std::move(ents), FSDP_ROLE_GRAD_ACC,
+                          static_cast<hipStream_t>(stream), "fsdp_bind_grad_acc");
+}
+
 fsdp_status fsdp_bind_full_grad(fsdp_plan *p, uint16_t *const *full_grad, void *stream) {
     if (p == nullptr || full_grad == nullptr)
         return fail(FSDP_E_INVAL, "fsdp_bind_full_grad: null plan or array");
@@ -481,6 +506,28 @@ fsdp_status fsdp_step_shard(const fsdp_plan *p, const uint16_t *rs_in, uint16_t 
     adamw_scalars(hp, step, scal);
     return launched(do_step(p, rs_in, ag_in, scal, write_grad, static_cast<hipStream_t>(stream)),
                     "fsdp_step_shard: launch");
+}
+
+fsdp_status fsdp_accumulate_grad(const fsdp_plan *p, int32_t reset, void *stream) {
+    fsdp_status s = need_roles(p, FSDP_ROLE_FULL_GRAD | FSDP_ROLE_GRAD_ACC, "fsdp_accumulate_grad");
+    if (s != FSDP_OK || (s = check_device(p)) != FSDP_OK) return s;
+    return launched(fsdp::launch_accumulate(p->d_full, static_cast<int64_t>(p->L.full.size()),
+                                            p->d_entries, reset != 0,
+                                            static_cast<hipStream_t>(stream)),
+                    "fsdp_accumulate_grad: launch");
+}
+
+fsdp_status fsdp_pack_reduce_scatter_acc(const fsdp_plan *p, float *rs_out, void *stream) {
+    fsdp_status s = need_roles(p, FSDP_ROLE_GRAD_ACC, "fsdp_pack_reduce_scatter_acc");
+    if (s != FSDP_OK) return s;
+    if (rs_out == nullptr && p->L.S > 0)
+        return fail(FSDP_E_INVAL, "fsdp_pack_reduce_scatter_acc: null rs_out");
+    if (misaligned(rs_out, 4))
+        return fail(FSDP_E_ALIGN, "fsdp_pack_reduce_scatter_acc: rs_out not 4-byte aligned");
+    if ((s = check_device(p)) != FSDP_OK) return s;
+    return launched(fsdp::launch_rspack_acc(p->d_rspack, static_cast<int64_t>(p->L.rspack.size()),
+                                            p->d_entries, rs_out, static_cast<hipStream_t>(stream)),
+                    "fsdp_pack_reduce_scatter_acc: launch");
 }
 
 fsdp_status fsdp_pack_reduce_scatter(const fsdp_plan *p, void *rs_out, int32_t dtype,

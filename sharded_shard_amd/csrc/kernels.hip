@@ -698,6 +698,101 @@ __global__ __launch_bounds__(kBlock) void rspack_f32_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// gradient accumulation without sync: fp32 acc <- acc + fp32(bf16 grad)
+// ---------------------------------------------------------------------------
+
+template <int POL, bool kReset>
+__device__ __forceinline__ void accumulate_run(float *__restrict__ acc, const uint16_t *__restrict__ g,
+                                               int64_t len) {
+    constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
+    const int tid = threadIdx.x;
+    int64_t head = ((16u - (lo32(acc) & 15u)) & 15u) >> 2;
+    if (head > len) head = len;
+    const bool vec = (lo32(g + head) & 7u) == 0;   // 4 bf16 per 16 fp32 bytes
+    if (!vec) head = len;
+    for (int64_t i = tid; i < head; i += kBlock) acc[i] = kReset ? widen(g[i]) : acc[i] + widen(g[i]);
+    if (!vec) return;
+    const int64_t nvec = (len - head) >> 2;
+    f32x4 *av = reinterpret_cast<f32x4 *>(acc + head);
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 *gv = reinterpret_cast<const u32x2 *>(g + head);
+    for (int64_t v = tid; v < nvec; v += kBlock) {
+        const u32x2 w = ldp<LN>(gv + v);
+        const f32x4 x{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+        if (kReset) {
+            stp<SN>(av + v, x);
+        } else {
+            const f32x4 a = ldp<LN>(av + v);
+            stp<SN>(av + v, f32x4{a.x + x.x, a.y + x.y, a.z + x.z, a.w + x.w});
+        }
+    }
+    const int64_t e = head + (nvec << 2) + tid;
+    if (e < len) acc[e] = kReset ? widen(g[e]) : acc[e] + widen(g[e]);
+}
+
+template <int POL, bool kReset>
+__global__ __launch_bounds__(kBlock) void accumulate_kernel(const EwTile *__restrict__ tiles,
+                                                            int64_t n_tiles, int32_t split,
+                                                            int64_t sub,
+                                                            const DevEntry *__restrict__ ents) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
+        const EwTile tl = tiles[t];
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        const DevEntry en = ents[tl.entry];
+        accumulate_run<POL, kReset>(en.grad_acc + tl.off + b, en.full_grad + tl.off + b, len);
+    }
+}
+
+// Reduce-scatter copy-in from the fp32 accumulators: copy fp32 runs, zeros
+// in padding.  dst is aligned to 16 bytes after a short head; the source is
+// read as aligned vectors and dword-selected.
+template <int POL>
+__device__ __forceinline__ void copy_f32_run(float *__restrict__ dst, const float *__restrict__ src,
+                                             int64_t len, int64_t valid) {
+    constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
+    const int tid = threadIdx.x;
+    int64_t head = ((16u - (lo32(dst) & 15u)) & 15u) >> 2;
+    if (head > valid) head = valid;
+    if (tid < head) dst[tid] = src[tid];
+    const int64_t ngrp = (valid - head) >> 3;
+    const float *s = src + head;
+    const uint32_t q = (lo32(s) >> 2) & 3u;
+    f32x4 *dv = reinterpret_cast<f32x4 *>(dst + head);
+    for (int64_t g = tid; g < ngrp; g += kBlock) {
+        f32x4 a, b;
+        load8f_at<LN>(s + (g << 3), q, a, b);
+        stp<SN>(dv + 2 * g, a);
+        stp<SN>(dv + 2 * g + 1, b);
+    }
+    const int64_t done = head + (ngrp << 3);
+    if (tid < valid - done) dst[done + tid] = src[done + tid];
+    zero_f32<SN>(dst, valid, len);
+}
+
+template <int POL>
+__global__ __launch_bounds__(kBlock) void rspack_acc_kernel(
+    const PackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
+    const DevEntry *__restrict__ ents, float *__restrict__ out) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
+        const PackTile tl = tiles[t];
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        int64_t valid = tl.valid - b;
+        valid = valid < 0 ? 0 : (valid > len ? len : valid);
+        copy_f32_run<POL>(out + tl.dst + b, ents[tl.entry].grad_acc + tl.src + b, len, valid);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // reduce of fp32 contributions: [N, S] fp32 -> fp32 mean, this rank's pieces
 // ---------------------------------------------------------------------------
 
@@ -1012,6 +1107,27 @@ hipError_t launch_copy_runs(const CopyTile *tiles, int64_t n, hipStream_t st) {
     const int32_t sp = split_for(kTileUnpack, FSDP_UNPACK_SUB);
     copy_runs_kernel<FSDP_UNPACK_POL>
         <<<grid_for(n, sp), kBlock, 0, st>>>(tiles, n, sp, kTileUnpack / sp);
+    return hipGetLastError();
+}
+
+hipError_t launch_accumulate(const EwTile *tiles, int64_t n, const DevEntry *ents, bool reset,
+                             hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const int32_t sp = split_for(kTileAdamw, FSDP_ADAMW_SUB);
+    const unsigned grid = grid_for(n, sp);
+    if (reset)
+        accumulate_kernel<FSDP_ADAMW_POL, true><<<grid, kBlock, 0, st>>>(tiles, n, sp, kTileAdamw / sp, ents);
+    else
+        accumulate_kernel<FSDP_ADAMW_POL, false><<<grid, kBlock, 0, st>>>(tiles, n, sp, kTileAdamw / sp, ents);
+    return hipGetLastError();
+}
+
+hipError_t launch_rspack_acc(const PackTile *tiles, int64_t n, const DevEntry *ents, float *out,
+                             hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const int32_t sp = split_for(kTileUnpack, FSDP_UNPACK_SUB);
+    rspack_acc_kernel<FSDP_UNPACK_POL><<<grid_for(n, sp), kBlock, 0, st>>>(
+        tiles, n, sp, kTileUnpack / sp, ents, out);
     return hipGetLastError();
 }
 

@@ -160,6 +160,15 @@ fsdp_status build_layout(const int64_t *rows, const int64_t *cols, int32_t n,
             at.len = static_cast<int32_t>(std::min(kTileAdamw, e.valid_numel - t));
             L.adamw.push_back(at);
         }
+        // gradient accumulation: every element of the unsharded parameter
+        const int64_t numel = e.rows * e.cols;
+        for (int64_t t = 0; t < numel; t += kTileAdamw) {
+            EwTile ft{};
+            ft.off = t;
+            ft.entry = i;
+            ft.len = static_cast<int32_t>(std::min(kTileAdamw, numel - t));
+            L.full.push_back(ft);
+        }
     }
     *out = std::move(L);
     return FSDP_OK;

@@ -49,7 +49,7 @@ struct DevEntry {
     uint16_t *full;
     int64_t valid_numel;
     uint16_t *full_grad;   // unsharded bf16 gradient (reduce-scatter copy-in)
-    int64_t rsv;
+    float *grad_acc;       // unsharded fp32 gradient accumulator
 };
 static_assert(sizeof(DevEntry) == 64, "DevEntry layout");
 
@@ -111,6 +111,7 @@ struct Layout {
     std::vector<UnpackTile> unpack;
     std::vector<ReduceTile> reduce;
     std::vector<EwTile> adamw;
+    std::vector<EwTile> full;         // every element of the unsharded parameters
 };
 
 // ceil(rows / world) and rank j's [row_begin, row_begin + local_rows).

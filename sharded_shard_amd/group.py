@@ -117,6 +117,22 @@ class ShardedGroup:
                 for o, r, c in zip(self.full_offsets, self.rows, self.cols)]
         capi.fsdp_bind_full_grad(self.plan, ptrs, stream)
 
+    def bind_grad_acc(self, arena: Optional[torch.Tensor] = None, stream=None) -> None:
+        """Bind fp32 unsharded gradient accumulators, laid out like the full
+        parameters (views of ``arena``, allocated here when not given)."""
+        if arena is None:
+            arena = torch.zeros(self.full_space, dtype=torch.float32, device=self.device)
+        if arena.numel() < self.full_space:
+            raise ValueError("accumulator arena is too small for this group")
+        self.grad_acc_flat = arena
+        ptrs = [arena[o:o + r * c].data_ptr() if r * c else 0
+                for o, r, c in zip(self.full_offsets, self.rows, self.cols)]
+        capi.fsdp_bind_grad_acc(self.plan, ptrs, stream)
+
+    def grad_acc_view(self, i: int) -> torch.Tensor:
+        o = self.full_offsets[i]
+        return self.grad_acc_flat[o:o + self.rows[i] * self.cols[i]].view(self.rows[i], self.cols[i])
+
     def full_grad_view(self, i: int) -> torch.Tensor:
         o = self.full_offsets[i]
         return self.full_grad_flat[o:o + self.rows[i] * self.cols[i]].view(self.rows[i], self.cols[i])
@@ -125,6 +141,12 @@ class ShardedGroup:
 
     def pack_reduce_scatter(self, rs_out, dtype: int = capi.FSDP_DTYPE_BF16, stream=None) -> None:
         capi.fsdp_pack_reduce_scatter(self.plan, rs_out, dtype, stream)
+
+    def accumulate_grad(self, reset: bool, stream=None) -> None:
+        capi.fsdp_accumulate_grad(self.plan, reset, stream)
+
+    def pack_reduce_scatter_acc(self, rs_out, stream=None) -> None:
+        capi.fsdp_pack_reduce_scatter_acc(self.plan, rs_out, stream)
 
     def reduce_f32(self, rs_in, stream=None) -> None:
         capi.fsdp_reduce_shard_f32(self.plan, rs_in, stream)

@@ -774,3 +774,68 @@ def test_reshard_execute_matches_oracle(n1, n2, elem):
                 o += v.numel() + 5
             assert (h[mask] == -5).all()
             capi.fsdp_reshard_plan_destroy(p)
+
+
+# ---------------------------------------------------------------------------
+# gradient accumulation without sync
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", range(len(CASES)), ids=_case_ids())
+def test_accumulate_then_copy_in_matches_oracle(case):
+    name, shapes, n = CASES[case]
+    r = n - 1
+    plan = O.plan(shapes, n, r)
+    g = ShardedGroup(shapes, n, r)
+    g.bind_full_grad()
+    g.bind_grad_acc()
+    g.grad_acc_flat.fill_(123.0)           # reset must overwrite whatever is there
+    acc = None
+    for k in range(3):
+        _fill_full_grads(g, ("accg", name, k))
+        grads = [u16(g.full_grad_view(i)) for i in range(len(shapes))]
+        g.accumulate_grad(reset=(k == 0))
+        acc = O.accumulate_grad(acc, grads, reset=(k == 0))
+    torch.cuda.synchronize()
+    for i, want in enumerate(acc):
+        got = f32(g.grad_acc_view(i)).reshape(-1)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (name, i)
+    want_rs = O.pack_reduce_scatter_acc(plan, acc).reshape(-1)
+    for off in (0, 1, 3):
+        buf = torch.full((n * plan.S + off + 8,), 9.0, dtype=torch.float32, device=DEV)
+        g.pack_reduce_scatter_acc(buf[off:off + n * plan.S])
+        torch.cuda.synchronize()
+        h = f32(buf)
+        assert np.array_equal(h[off:off + n * plan.S].view(np.uint32), want_rs.view(np.uint32))
+        assert (h[:off] == 9.0).all() and (h[off + n * plan.S:] == 9.0).all()
+    # the synchronizing microbatch: fp32 reduction of the accumulated copy-in
+    rs = torch.from_numpy(want_rs).to(DEV)
+    g.reduce_f32(rs)
+    torch.cuda.synchronize()
+    for i, want in enumerate(O.reduce_f32(plan, want_rs.reshape(n, plan.S))):
+        _cmp_f32(f32(g.shard_view(g.grad_flat, i)), want, (name, i))
+    g.close()
+
+
+def test_accumulate_misaligned_pointers_take_the_scalar_path():
+    shapes = [(37, 11), (999,), (8, 64)]
+    g = ShardedGroup(shapes, 2, 0, bind=True)
+    gbuf = torch.zeros(sum(r * c + 5 for r, c in zip(g.rows, g.cols)) + 16, dtype=torch.int16, device=DEV)
+    abuf = torch.zeros(sum(r * c + 5 for r, c in zip(g.rows, g.cols)) + 16, dtype=torch.float32, device=DEV)
+    gv, av, og, oa = [], [], 1, 2
+    for i, (r_, c_) in enumerate(zip(g.rows, g.cols)):
+        gv.append(gbuf[og:og + r_ * c_])
+        av.append(abuf[oa:oa + r_ * c_])
+        og += r_ * c_ + 3
+        oa += r_ * c_ + 1
+    capi.fsdp_bind_full_grad(g.plan, [v.data_ptr() for v in gv], None)
+    capi.fsdp_bind_grad_acc(g.plan, [v.data_ptr() for v in av], None)
+    acc = None
+    for k in range(2):
+        for i, v in enumerate(gv):
+            v.copy_(synth.normal_bf16_bits(v.numel(), 1e-3, ("accm", k, i)))
+        capi.fsdp_accumulate_grad(g.plan, k == 0)
+        acc = O.accumulate_grad(acc, [u16(v) for v in gv], reset=(k == 0))
+    torch.cuda.synchronize()
+    for v, want in zip(av, acc):
+        assert np.array_equal(f32(v).view(np.uint32), want.view(np.uint32))
+    g.close()

@@ -679,3 +679,53 @@ def test_reshard_two_ranks_to_one_is_the_full_tensor_and_round_trips():
         back = [O.reshard(s2, 33, 7, n1, d) for d in range(n1)]
         for a, b in zip(back, s1):
             assert np.array_equal(a, b.reshape(-1))
+
+
+# ---------------------------------------------------------------------------
+# gradient accumulation without sync
+# ---------------------------------------------------------------------------
+
+def test_accumulate_grad_sum_and_reset():
+    shapes = [(37, 3), (129,)]
+    micro = [_bf16_grads(shapes, ("acc", k)) for k in range(5)]
+    acc = O.accumulate_grad(None, micro[0], reset=True)
+    for a, g in zip(acc, micro[0]):                     # reset: exact widening
+        assert np.array_equal(a.view(np.uint32), O.bf16_to_f32(g.reshape(-1)).view(np.uint32))
+    for k in range(1, 5):
+        acc = O.accumulate_grad(acc, micro[k], reset=False)
+    u = 2.0 ** -24
+    for i, a in enumerate(acc):
+        xs = np.stack([O.bf16_to_f32(m[i].reshape(-1)).astype(np.float64) for m in micro])
+        for e in range(a.size):
+            exact = math.fsum(xs[:, e])
+            assert abs(float(a[e]) - exact) <= 4 * u * np.abs(xs[:, e]).sum() + 1e-45
+        # torch's sequential fp32 adds in the same order give the same bits
+        t = torch.zeros(a.size)
+        t += torch.from_numpy(xs[0].astype(np.float32))
+        for k in range(1, 5):
+            t = t + torch.from_numpy(xs[k].astype(np.float32))
+        assert np.array_equal(t.numpy().view(np.uint32), a.view(np.uint32))
+    # -0 survives a reset, and the sum is bit-stable when rerun
+    neg0 = [np.full((2, 2), 0x8000, np.uint16)]
+    assert O.accumulate_grad(None, neg0, True)[0].view(np.uint32)[0] == 0x80000000
+
+
+@pytest.mark.parametrize("case", range(len(SMALL_CASES)))
+def test_pack_reduce_scatter_acc_layout(case):
+    shapes, n = SMALL_CASES[case]
+    grads = _bf16_grads(shapes, ("rspa", case))
+    p = O.plan(shapes, n, 0)
+    acc = O.accumulate_grad(None, grads, reset=True)
+    # from a single microbatch it is the fp32 copy-in of that gradient
+    assert np.array_equal(O.pack_reduce_scatter_acc(p, acc).view(np.uint32),
+                          O.pack_reduce_scatter_f32(p, grads).view(np.uint32))
+    # and against torch.chunk / pad / cat on fp32 values
+    got = O.pack_reduce_scatter_acc(p, [a * np.float32(3) for a in acc])
+    for j in range(n):
+        parts = []
+        for a, e, s in zip(acc, p.entries, shapes):
+            rows, cols = s[0], (int(np.prod(s[1:])) if len(s) > 1 else 1)
+            piece = _chunks_of(torch.from_numpy(a * np.float32(3)).reshape(rows, cols), n, j).reshape(-1)
+            parts.append(torch.cat([piece, torch.zeros(e.seg_numel - piece.numel())]))
+        want = torch.cat(parts).numpy() if parts else np.zeros(0, np.float32)
+        assert np.array_equal(got[j].view(np.uint32), want.view(np.uint32))
