@@ -187,9 +187,13 @@ def measure_next(groups, n, rs_bf16, full_arena, stream, reps):
     rs_f32 = torch.empty(max_ns, dtype=torch.float32, device=full_arena.device)
     acc_arena = torch.zeros(max(g.full_space for g in groups), dtype=torch.float32,
                             device=full_arena.device)
+    ag_u8 = rs_bf16.view(torch.uint8)               # [N, S] bytes fit in the bf16 arena
+    fp8_scales = torch.full((max(len(g.rows) for g in groups),), 448.0 / 0.1,
+                            dtype=torch.float32, device=full_arena.device)
     for g in groups:
         g.bind_full_grad(full_arena, stream)
         g.bind_grad_acc(acc_arena, stream)
+        g.bind_full_fp8(full_arena.view(torch.uint8), stream)
     kinds = {
         "rs_copy_in_bf16": (lambda g: g.pack_reduce_scatter(rs_bf16[:n * g.S], capi.FSDP_DTYPE_BF16, stream),
                             lambda g: 2 * g.F + 2 * n * g.S),
@@ -197,6 +201,9 @@ def measure_next(groups, n, rs_bf16, full_arena, stream, reps):
                            lambda g: 2 * g.F + 4 * n * g.S),
         "reduce_f32": (lambda g: g.reduce_f32(rs_f32[:n * g.S], stream),
                        lambda g: 4 * n * g.V + 4 * g.V),
+        "fp8_copy_in": (lambda g: g.pack_fp8(ag_u8[:g.S], fp8_scales, stream),
+                        lambda g: 4 * g.V + g.S),
+        "fp8_copy_out": (lambda g: g.unpack_fp8(ag_u8[:n * g.S], stream), lambda g: 2 * g.F),
         "grad_accumulate": (lambda g: g.accumulate_grad(False, stream), lambda g: 10 * g.F),
         "rs_copy_in_from_acc": (lambda g: g.pack_reduce_scatter_acc(rs_f32[:n * g.S], stream),
                                 lambda g: 4 * g.F + 4 * n * g.S),
@@ -237,7 +244,7 @@ def measure_next(groups, n, rs_bf16, full_arena, stream, reps):
         res[name] = {"ms_per_step": round(ms, 4), "algorithmic_GB_per_step": round(byts / 1e9, 4),
                      "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
     capi.fsdp_reshard_plan_destroy(rplan)
-    del rs_f32, dst, acc_arena
+    del rs_f32, dst, acc_arena, fp8_scales
     res["adamw_host_cpu_offload"] = measure_host_adamw()
     return res
 

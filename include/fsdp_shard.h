@@ -114,7 +114,8 @@ enum {
     FSDP_ROLE_EXP_AVG_SQ = 8,
     FSDP_ROLE_FULL = 16,
     FSDP_ROLE_FULL_GRAD = 32,
-    FSDP_ROLE_GRAD_ACC = 64
+    FSDP_ROLE_GRAD_ACC = 64,
+    FSDP_ROLE_FULL_FP8 = 128
 };
 
 /* Element types of the reduce-scatter buffers. */
@@ -203,6 +204,11 @@ fsdp_status fsdp_bind_full_grad(fsdp_plan *plan, uint16_t *const *full_grad, voi
  * fsdp_bind_full_grad, 4-byte aligned pointers. */
 fsdp_status fsdp_bind_grad_acc(fsdp_plan *plan, float *const *grad_acc, void *stream);
 
+/* Bind each parameter's unsharded FP8 E4M3 tensor [rows, cols] (one byte per
+ * element; the FP8 copy-out's destination).  Same rules as
+ * fsdp_bind_full_grad, any byte alignment. */
+fsdp_status fsdp_bind_full_fp8(fsdp_plan *plan, uint8_t *const *full_fp8, void *stream);
+
 /* ---- hot path: enqueue on `stream`; no sync, no allocation ------------- */
 
 /* All-gather copy-in.  Writes all S elements of ag_in: for each parameter,
@@ -253,6 +259,34 @@ fsdp_status fsdp_reduce_shard(const fsdp_plan *plan, const uint16_t *rs_in,
  * (dtype), FSDP_E_ALIGN, FSDP_E_STATE, FSDP_E_HIP. */
 fsdp_status fsdp_pack_reduce_scatter(const fsdp_plan *plan, void *rs_out, int32_t dtype,
                                      void *stream);
+
+/* FP8 all-gather copy-in ([AF] "Native FP8 Training with Float8Tensor":
+ * parameters held in FP8 E4M3 and all-gathered as raw FP8 bytes, half the
+ * traffic of bf16).  Writes all S bytes of ag_in: for each parameter p,
+ * ag_in[shard_offset + i] = e4m3(fp32(master[i] * scales[p])) for
+ * i < valid_numel, zero elsewhere.  e4m3 is the OCP e4m3fn format, round to
+ * nearest even, magnitudes >= 448 and infinities saturated to +-448, NaN
+ * kept as the NaN code with its sign.
+ *   scales  device array of n_params fp32 per-tensor scales (e.g. 448 / amax
+ *           with amax the maximum over ranks of fsdp_amax_shard's output)
+ * Needs FSDP_ROLE_MASTER.  Errors: FSDP_E_INVAL, FSDP_E_ALIGN (scales),
+ * FSDP_E_STATE, FSDP_E_HIP. */
+fsdp_status fsdp_pack_allgather_fp8(const fsdp_plan *plan, uint8_t *ag_in, const float *scales,
+                                    void *stream);
+
+/* FP8 copy-out: [N, S] E4M3 bytes -> every parameter's bound FP8 [rows, cols]
+ * tensor (bytes copied, kept FP8 for FP8 GEMMs), row mapping as
+ * fsdp_unpack_allgather.  Needs FSDP_ROLE_FULL_FP8.
+ * Errors: FSDP_E_INVAL, FSDP_E_STATE, FSDP_E_HIP. */
+fsdp_status fsdp_unpack_allgather_fp8(const fsdp_plan *plan, const uint8_t *ag_out, void *stream);
+
+/* Per-parameter largest |master| over this rank's shard into amax (device,
+ * n_params fp32; 0 for an empty shard; a NaN propagates).  The maximum
+ * across ranks (a collective, outside this library) gives tensor-wise FP8
+ * scaling.  Launches a clear of amax and a reduction; amax is complete when
+ * the stream reaches it.  Needs FSDP_ROLE_MASTER.
+ * Errors: FSDP_E_INVAL, FSDP_E_ALIGN, FSDP_E_STATE, FSDP_E_HIP. */
+fsdp_status fsdp_amax_shard(const fsdp_plan *plan, float *amax, void *stream);
 
 /* Gradient accumulation without sync ([ST] "Other controls":
  * set_requires_gradient_sync(False) accumulates unsharded gradients and

@@ -170,6 +170,92 @@ def bf16_to_f32(u16) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# FP8 E4M3 (OCP e4m3fn: bias 7, 3 mantissa bits, no infinities)
+# ---------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_to_f32(u8) -> np.ndarray:
+    """Exact value of e4m3fn codes: S.EEEE.MMM, bias 7; exponent 0 holds
+    subnormals m/8 * 2^-6; S.1111.111 is NaN (there is no infinity)."""
+    b = np.asarray(u8, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    e = (b >> 3) & 0xF
+    m = b & 7
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return (sign * val).astype(F32)
+
+
+def e4m3_sat(x) -> np.ndarray:
+    """fp32 -> e4m3fn code, round to nearest even, saturating.
+
+    Magnitudes at or beyond 448 (the largest finite code), infinities
+    included, become +-448, as FP8 training casts clamp before converting; a
+    NaN becomes the NaN code with its sign.  Below 2^-6 the code is a
+    subnormal m/8 * 2^-6 rounded to nearest even (m = 8 is the smallest
+    normal code).  Written on the fp32 bit pattern.
+    """
+    a = np.ascontiguousarray(np.asarray(x, dtype=F32))
+    u = a.view(np.uint32).astype(np.int64)
+    sign = (u >> 24) & 0x80
+    mag = u & 0x7FFFFFFF
+    # normal range: keep 3 of the 23 mantissa bits, ties to even, rebias 127 -> 7
+    r = (mag + 0x7FFFF + ((mag >> 20) & 1)) >> 20
+    normal = np.minimum(r - (120 << 3), 0x7E)
+    # subnormal range: m = round_half_even(|x| * 2^9) from the 24-bit significand
+    E = mag >> 23
+    M = (mag & 0x7FFFFF) | 0x800000
+    shift = 141 - E
+    sh = np.clip(shift, 1, 40)
+    sub = np.where(shift >= 40, 0, (M + (1 << (sh - 1)) - 1 + ((M >> sh) & 1)) >> sh)
+    code = np.where(mag >= 0x3C800000, normal, sub)
+    code = np.where(mag >= 0x43E00000, 0x7E, code)          # |x| >= 448, inf too
+    code = np.where(mag > 0x7F800000, 0x7F, code)           # NaN
+    return (sign | code).astype(np.uint8)
+
+
+def pack_fp8(p: Plan, master_shards: Sequence[np.ndarray], scales: Sequence[float]) -> np.ndarray:
+    """FP8 all-gather copy-in: bytes e4m3(fp32(master * scale_p)) at each
+    shard offset of a [S] byte segment, zeros in padding.  Parameters stored
+    and all-gathered as raw FP8 bytes ([AF] "Native FP8 Training with
+    Float8Tensor"); the per-parameter scale comes from the caller (tensor-wise
+    scaling, e.g. 448 / amax)."""
+    out = np.zeros(p.S, dtype=np.uint8)
+    for e, m, sc in zip(p.entries, master_shards, scales):
+        flat = np.asarray(m, dtype=F32).reshape(-1)
+        out[e.shard_offset:e.shard_offset + e.valid_numel] = e4m3_sat(flat * F32(sc))
+    return out
+
+
+def unpack_fp8(p: Plan, ag_out: np.ndarray) -> List[np.ndarray]:
+    """FP8 copy-out: [N, S] bytes -> full [rows, cols] FP8 parameters (the
+    bytes stay FP8 for FP8 GEMMs); same row mapping as ``unpack``."""
+    ag = np.asarray(ag_out, dtype=np.uint8).reshape(p.world, p.S)
+    fulls = []
+    for e in p.entries:
+        full = np.empty(e.rows * e.cols, dtype=np.uint8)
+        for j in range(p.world):
+            b, lr = rows_of_rank(e.rows, p.world, j)
+            n = lr * e.cols
+            full[b * e.cols:b * e.cols + n] = ag[j, e.shard_offset:e.shard_offset + n]
+        fulls.append(full.reshape(e.rows, e.cols))
+    return fulls
+
+
+def amax(master_shards: Sequence[np.ndarray]) -> np.ndarray:
+    """Per parameter, the largest |x| of this rank's shard (0 when empty): the
+    input of tensor-wise FP8 scaling after a max across ranks.  Taken on the
+    bit patterns of |x|, so a NaN yields NaN."""
+    out = np.zeros(len(master_shards), dtype=F32)
+    for i, m in enumerate(master_shards):
+        b = np.asarray(m, dtype=F32).reshape(-1).view(np.uint32) & np.uint32(0x7FFFFFFF)
+        out[i] = np.array([b.max() if b.size else 0], dtype=np.uint32).view(F32)[0]
+    return out
+
+
+# ---------------------------------------------------------------------------
 # The four steps
 # ---------------------------------------------------------------------------
 

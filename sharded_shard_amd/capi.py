@@ -31,6 +31,7 @@ FSDP_ROLE_EXP_AVG_SQ = 8
 FSDP_ROLE_FULL = 16
 FSDP_ROLE_FULL_GRAD = 32
 FSDP_ROLE_GRAD_ACC = 64
+FSDP_ROLE_FULL_FP8 = 128
 
 FSDP_DTYPE_BF16 = 0
 FSDP_DTYPE_F32 = 1
@@ -110,6 +111,10 @@ _SIGS = {
     "fsdp_bind_full_grad": (_i32, [_P, _PP, _P]),
     "fsdp_pack_reduce_scatter": (_i32, [_P, _P, _i32, _P]),
     "fsdp_bind_grad_acc": (_i32, [_P, _PP, _P]),
+    "fsdp_bind_full_fp8": (_i32, [_P, _PP, _P]),
+    "fsdp_pack_allgather_fp8": (_i32, [_P, _P, _P, _P]),
+    "fsdp_unpack_allgather_fp8": (_i32, [_P, _P, _P]),
+    "fsdp_amax_shard": (_i32, [_P, _P, _P]),
     "fsdp_accumulate_grad": (_i32, [_P, _i32, _P]),
     "fsdp_pack_reduce_scatter_acc": (_i32, [_P, _P, _P]),
     "fsdp_reduce_shard_f32": (_i32, [_P, _P, _P]),
@@ -243,6 +248,25 @@ def fsdp_bind_full_grad(plan, full_grad, stream=None) -> None:
 def fsdp_pack_reduce_scatter(plan, rs_out, dtype: int = FSDP_DTYPE_BF16, stream=None) -> None:
     _check(lib.fsdp_pack_reduce_scatter(plan, addr(rs_out), dtype, stream_handle(stream)),
            "fsdp_pack_reduce_scatter")
+
+
+def fsdp_bind_full_fp8(plan, full_fp8, stream=None) -> None:
+    _check(lib.fsdp_bind_full_fp8(plan, _ptr_array(full_fp8), stream_handle(stream)),
+           "fsdp_bind_full_fp8")
+
+
+def fsdp_pack_allgather_fp8(plan, ag_in, scales, stream=None) -> None:
+    _check(lib.fsdp_pack_allgather_fp8(plan, addr(ag_in), addr(scales), stream_handle(stream)),
+           "fsdp_pack_allgather_fp8")
+
+
+def fsdp_unpack_allgather_fp8(plan, ag_out, stream=None) -> None:
+    _check(lib.fsdp_unpack_allgather_fp8(plan, addr(ag_out), stream_handle(stream)),
+           "fsdp_unpack_allgather_fp8")
+
+
+def fsdp_amax_shard(plan, amax, stream=None) -> None:
+    _check(lib.fsdp_amax_shard(plan, addr(amax), stream_handle(stream)), "fsdp_amax_shard")
 
 
 def fsdp_bind_grad_acc(plan, grad_acc, stream=None) -> None:

@@ -33,6 +33,12 @@ hipError_t launch_reduce_f32(const ReduceTile *tiles, int64_t n, const DevEntry 
                              const float *rs_in, int64_t S, int32_t N, hipStream_t st);
 hipError_t launch_accumulate(const EwTile *tiles, int64_t n, const DevEntry *ents, bool reset,
                              hipStream_t st);
+hipError_t launch_pack_fp8(const PackTile *tiles, int64_t n, const DevEntry *ents, uint8_t *ag_in,
+                           const float *scales, hipStream_t st);
+hipError_t launch_unpack_fp8(const UnpackTile *tiles, int64_t n, const DevEntry *ents,
+                             const uint8_t *ag_out, hipStream_t st);
+hipError_t launch_amax(const EwTile *tiles, int64_t n, const DevEntry *ents, float *amax,
+                       int32_t n_params, hipStream_t st);
 hipError_t launch_rspack_acc(const PackTile *tiles, int64_t n, const DevEntry *ents, float *out,
                              hipStream_t st);
 }  // namespace fsdp
@@ -211,8 +217,6 @@ fsdp_status fsdp_plan_create(const int64_t *rows, const int64_t *cols,
             return fail(s, "fsdp_plan_create: " + err);
         }
         p->host_entries.assign(static_cast<size_t>(n_params), fsdp::DevEntry{});
-        for (int32_t i = 0; i < n_params; ++i)
-            p->host_entries[i].valid_numel = p->L.entries[i].valid_numel;
         *out = p;
         return FSDP_OK;
     } catch (const std::bad_alloc &) {
@@ -338,6 +342,21 @@ fsdp_status fsdp_bind(fsdp_plan *p, float *const *master, float *const *grad,
     }
     return commit_entries(p, std::move(ents), roles, static_cast<hipStream_t>(stream),
                           "fsdp_bind");
+}
+
+fsdp_status fsdp_bind_full_fp8(fsdp_plan *p, uint8_t *const *full_fp8, void *stream) {
+    if (p == nullptr || full_fp8 == nullptr)
+        return fail(FSDP_E_INVAL, "fsdp_bind_full_fp8: null plan or array");
+    std::vector<fsdp::DevEntry> ents = p->host_entries;
+    for (size_t i = 0; i < ents.size(); ++i) {
+        const fsdp_shard_entry_t &e = p->L.entries[i];
+        if (full_fp8[i] == nullptr && e.rows * e.cols > 0)
+            return fail(FSDP_E_INVAL, "fsdp_bind_full_fp8: null pointer for parameter " +
+                                          std::to_string(i));
+        ents[i].full_fp8 = full_fp8[i];
+    }
+    return commit_entries(p, std::move(ents), FSDP_ROLE_FULL_FP8,
+                          static_cast<hipStream_t>(stream), "fsdp_bind_full_fp8");
 }
 
 fsdp_status fsdp_bind_grad_acc(fsdp_plan *p, float *const *grad_acc, void *stream) {
@@ -506,6 +525,47 @@ fsdp_status fsdp_step_shard(const fsdp_plan *p, const uint16_t *rs_in, uint16_t 
     adamw_scalars(hp, step, scal);
     return launched(do_step(p, rs_in, ag_in, scal, write_grad, static_cast<hipStream_t>(stream)),
                     "fsdp_step_shard: launch");
+}
+
+fsdp_status fsdp_pack_allgather_fp8(const fsdp_plan *p, uint8_t *ag_in, const float *scales,
+                                    void *stream) {
+    fsdp_status s = need_roles(p, FSDP_ROLE_MASTER, "fsdp_pack_allgather_fp8");
+    if (s != FSDP_OK) return s;
+    if (ag_in == nullptr && p->L.S > 0)
+        return fail(FSDP_E_INVAL, "fsdp_pack_allgather_fp8: null ag_in");
+    if (scales == nullptr && !p->L.entries.empty())
+        return fail(FSDP_E_INVAL, "fsdp_pack_allgather_fp8: null scales");
+    if (misaligned(scales, 4)) return fail(FSDP_E_ALIGN, "fsdp_pack_allgather_fp8: scales not 4-byte aligned");
+    if ((s = check_device(p)) != FSDP_OK) return s;
+    return launched(fsdp::launch_pack_fp8(p->d_pack, static_cast<int64_t>(p->L.pack.size()),
+                                          p->d_entries, ag_in, scales,
+                                          static_cast<hipStream_t>(stream)),
+                    "fsdp_pack_allgather_fp8: launch");
+}
+
+fsdp_status fsdp_unpack_allgather_fp8(const fsdp_plan *p, const uint8_t *ag_out, void *stream) {
+    fsdp_status s = need_roles(p, FSDP_ROLE_FULL_FP8, "fsdp_unpack_allgather_fp8");
+    if (s != FSDP_OK) return s;
+    if (ag_out == nullptr && p->L.S > 0)
+        return fail(FSDP_E_INVAL, "fsdp_unpack_allgather_fp8: null ag_out");
+    if ((s = check_device(p)) != FSDP_OK) return s;
+    return launched(fsdp::launch_unpack_fp8(p->d_unpack, static_cast<int64_t>(p->L.unpack.size()),
+                                            p->d_entries, ag_out, static_cast<hipStream_t>(stream)),
+                    "fsdp_unpack_allgather_fp8: launch");
+}
+
+fsdp_status fsdp_amax_shard(const fsdp_plan *p, float *amax, void *stream) {
+    fsdp_status s = need_roles(p, FSDP_ROLE_MASTER, "fsdp_amax_shard");
+    if (s != FSDP_OK) return s;
+    if (amax == nullptr && !p->L.entries.empty())
+        return fail(FSDP_E_INVAL, "fsdp_amax_shard: null amax");
+    if (misaligned(amax, 4)) return fail(FSDP_E_ALIGN, "fsdp_amax_shard: amax not 4-byte aligned");
+    if ((s = check_device(p)) != FSDP_OK) return s;
+    return launched(fsdp::launch_amax(p->d_adamw, static_cast<int64_t>(p->L.adamw.size()),
+                                      p->d_entries, amax,
+                                      static_cast<int32_t>(p->L.entries.size()),
+                                      static_cast<hipStream_t>(stream)),
+                    "fsdp_amax_shard: launch");
 }
 
 fsdp_status fsdp_accumulate_grad(const fsdp_plan *p, int32_t reset, void *stream) {

@@ -698,6 +698,202 @@ __global__ __launch_bounds__(kBlock) void rspack_f32_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// FP8 E4M3 all-gather: scaled saturating copy-in, byte copy-out, amax
+// ---------------------------------------------------------------------------
+
+// fp32 -> OCP e4m3fn code, round to nearest even, magnitudes >= 448 (and
+// infinities) saturate to +-448, NaN -> NaN code with its sign.  Normal
+// codes keep 3 of the 23 mantissa bits of the fp32 pattern (ties to even,
+// exponent rebiased from 127 to 7); below 2^-6 the code is the subnormal
+// m/8 * 2^-6 with m the significand shifted to 2^-9 units, ties to even.
+__device__ __forceinline__ uint32_t e4m3_sat(float f) {
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t mag = u & 0x7FFFFFFFu;
+    if (mag > 0x7F800000u) return sign | 0x7Fu;
+    if (mag >= 0x43E00000u) return sign | 0x7Eu;
+    if (mag >= 0x3C800000u) {
+        const uint32_t r = (mag + 0x7FFFFu + ((mag >> 20) & 1u)) >> 20;
+        const uint32_t c = r - (120u << 3);
+        return sign | (c > 0x7Eu ? 0x7Eu : c);
+    }
+    const uint32_t E = mag >> 23;
+    const uint32_t shift = 141u - E;          // >= 21 here
+    if (shift >= 32u) return sign;
+    const uint32_t M = (mag & 0x7FFFFFu) | 0x800000u;
+    return sign | ((M + (1u << (shift - 1u)) - 1u + ((M >> shift) & 1u)) >> shift);
+}
+
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d, float s) {
+    return e4m3_sat(a * s) | (e4m3_sat(b * s) << 8) | (e4m3_sat(c * s) << 16) |
+           (e4m3_sat(d * s) << 24);
+}
+
+// dst[e] = 0 for e in [from, len) bytes, 16-byte stores where aligned.
+__device__ __forceinline__ void zero_u8(uint8_t *dst, int64_t from, int64_t len) {
+    const int tid = threadIdx.x;
+    if (from >= len) return;
+    uint8_t *d = dst + from;
+    const int64_t n = len - from;
+    int64_t head = (16u - (lo32(d) & 15u)) & 15u;
+    if (head > n) head = n;
+    if (tid < head) d[tid] = 0;
+    const int64_t nvec = (n - head) >> 4;
+    u32x4 *dv = reinterpret_cast<u32x4 *>(d + head);
+    for (int64_t v = tid; v < nvec; v += kBlock) stp<1>(dv + v, u32x4{0u, 0u, 0u, 0u});
+    const int64_t done = head + (nvec << 4);
+    if (tid < n - done) d[done + tid] = 0;
+}
+
+template <int POL>
+__device__ __forceinline__ void pack_fp8_run(uint8_t *__restrict__ dst, const float *__restrict__ src,
+                                             int64_t len, int64_t valid, float scale) {
+    constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
+    const int tid = threadIdx.x;
+    int64_t head = (16u - (lo32(dst) & 15u)) & 15u;
+    if (head > valid) head = valid;
+    if (tid < head) dst[tid] = static_cast<uint8_t>(e4m3_sat(src[tid] * scale));
+    const int64_t ngrp = (valid - head) >> 4;
+    const float *s = src + head;
+    const uint32_t q = (lo32(s) >> 2) & 3u;
+    u32x4 *dv = reinterpret_cast<u32x4 *>(dst + head);
+    for (int64_t g = tid; g < ngrp; g += kBlock) {
+        f32x4 a0, a1, b0, b1;
+        load8f_at<LN>(s + (g << 4), q, a0, a1);
+        load8f_at<LN>(s + (g << 4) + 8, q, b0, b1);
+        stp<SN>(dv + g, u32x4{pack4_e4m3(a0.x, a0.y, a0.z, a0.w, scale),
+                              pack4_e4m3(a1.x, a1.y, a1.z, a1.w, scale),
+                              pack4_e4m3(b0.x, b0.y, b0.z, b0.w, scale),
+                              pack4_e4m3(b1.x, b1.y, b1.z, b1.w, scale)});
+    }
+    const int64_t done = head + (ngrp << 4);
+    if (tid < valid - done)
+        dst[done + tid] = static_cast<uint8_t>(e4m3_sat(src[done + tid] * scale));
+    zero_u8(dst, valid, len);
+}
+
+template <int POL>
+__global__ __launch_bounds__(kBlock) void pack_fp8_kernel(
+    const PackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
+    const DevEntry *__restrict__ ents, uint8_t *__restrict__ ag_in,
+    const float *__restrict__ scales) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
+        const PackTile tl = tiles[t];
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        int64_t valid = tl.valid - b;
+        valid = valid < 0 ? 0 : (valid > len ? len : valid);
+        pack_fp8_run<POL>(ag_in + tl.dst + b, ents[tl.entry].master + tl.src + b, len, valid,
+                          scales[tl.entry]);
+    }
+}
+
+// Bytes [k, k + 16) of the 32-byte little-endian concatenation a:b, any k.
+__device__ __forceinline__ u32x4 funnel_any(u32x4 a, u32x4 b, uint32_t k) {
+    u32x4 lo, hi;
+    switch (k >> 2) {
+        case 0:
+            lo = a;
+            hi = u32x4{a.y, a.z, a.w, b.x};
+            break;
+        case 1:
+            lo = u32x4{a.y, a.z, a.w, b.x};
+            hi = u32x4{a.z, a.w, b.x, b.y};
+            break;
+        case 2:
+            lo = u32x4{a.z, a.w, b.x, b.y};
+            hi = u32x4{a.w, b.x, b.y, b.z};
+            break;
+        default:
+            lo = u32x4{a.w, b.x, b.y, b.z};
+            hi = u32x4{b.x, b.y, b.z, b.w};
+            break;
+    }
+    const uint32_t r = k & 3u;
+    if (r == 0) return lo;
+    return u32x4{__builtin_amdgcn_alignbyte(hi.x, lo.x, r), __builtin_amdgcn_alignbyte(hi.y, lo.y, r),
+                 __builtin_amdgcn_alignbyte(hi.z, lo.z, r), __builtin_amdgcn_alignbyte(hi.w, lo.w, r)};
+}
+
+template <int POL>
+__device__ __forceinline__ void copy_run_u8(uint8_t *__restrict__ dst, const uint8_t *__restrict__ src,
+                                            int64_t len) {
+    constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
+    const int tid = threadIdx.x;
+    int64_t head = (16u - (lo32(dst) & 15u)) & 15u;
+    if (head > len) head = len;
+    if (tid < head) dst[tid] = src[tid];
+    const int64_t nvec = (len - head) >> 4;
+    u32x4 *dv = reinterpret_cast<u32x4 *>(dst + head);
+    const uint8_t *s = src + head;
+    const uint32_t k = lo32(s) & 15u;
+    const u32x4 *sv = reinterpret_cast<const u32x4 *>(reinterpret_cast<uintptr_t>(s) - k);
+    if (k == 0) {
+        for (int64_t v = tid; v < nvec; v += kBlock) stp<SN>(dv + v, ldp<LN>(sv + v));
+    } else {
+        for (int64_t v = tid; v < nvec; v += kBlock)
+            stp<SN>(dv + v, funnel_any(ldp<LN>(sv + v), ldp<LN>(sv + v + 1), k));
+    }
+    const int64_t done = head + (nvec << 4);
+    if (tid < len - done) dst[done + tid] = src[done + tid];
+}
+
+template <int POL>
+__global__ __launch_bounds__(kBlock) void unpack_fp8_kernel(
+    const UnpackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
+    const DevEntry *__restrict__ ents, const uint8_t *__restrict__ ag_out) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
+        const UnpackTile tl = tiles[t];
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        copy_run_u8<POL>(ents[tl.entry].full_fp8 + tl.dst + b, ag_out + tl.src + b, len);
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void zero_floats_kernel(float *p, int32_t n) {
+    const int i = blockIdx.x * kBlock + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+}
+
+// Largest |x| per parameter as the maximum of the bit patterns of |x|
+// (monotone for non-negative floats; a NaN wins), merged across blocks with
+// an unsigned atomic max on the result's bits.
+__global__ __launch_bounds__(kBlock) void amax_kernel(const EwTile *__restrict__ tiles,
+                                                      int64_t n_tiles, int32_t split, int64_t sub,
+                                                      const DevEntry *__restrict__ ents,
+                                                      uint32_t *__restrict__ amax_bits) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    const int tid = threadIdx.x;
+    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
+        const EwTile tl = tiles[t];
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        const float *P = ents[tl.entry].master + tl.off + b;
+        uint32_t m = 0;
+        for (int64_t i = tid; i < len; i += kBlock) {
+            const uint32_t x = __float_as_uint(P[i]) & 0x7FFFFFFFu;
+            m = x > m ? x : m;
+        }
+        for (int off = 32; off > 0; off >>= 1) {
+            const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off, 64));
+            m = o > m ? o : m;
+        }
+        if ((tid & 63) == 0 && m != 0) atomicMax(amax_bits + tl.entry, m);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // gradient accumulation without sync: fp32 acc <- acc + fp32(bf16 grad)
 // ---------------------------------------------------------------------------
 
@@ -1107,6 +1303,37 @@ hipError_t launch_copy_runs(const CopyTile *tiles, int64_t n, hipStream_t st) {
     const int32_t sp = split_for(kTileUnpack, FSDP_UNPACK_SUB);
     copy_runs_kernel<FSDP_UNPACK_POL>
         <<<grid_for(n, sp), kBlock, 0, st>>>(tiles, n, sp, kTileUnpack / sp);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_fp8(const PackTile *tiles, int64_t n, const DevEntry *ents, uint8_t *ag_in,
+                           const float *scales, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const int32_t sp = split_for(kTilePack, FSDP_PACK_SUB);
+    pack_fp8_kernel<FSDP_PACK_POL><<<grid_for(n, sp), kBlock, 0, st>>>(
+        tiles, n, sp, kTilePack / sp, ents, ag_in, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack_fp8(const UnpackTile *tiles, int64_t n, const DevEntry *ents,
+                             const uint8_t *ag_out, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    // 16 bytes per lane move 16 elements: twice the elements per block of bf16
+    const int32_t sp = split_for(kTileUnpack, 2 * FSDP_UNPACK_SUB);
+    unpack_fp8_kernel<FSDP_UNPACK_POL><<<grid_for(n, sp), kBlock, 0, st>>>(
+        tiles, n, sp, kTileUnpack / sp, ents, ag_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_amax(const EwTile *tiles, int64_t n, const DevEntry *ents, float *amax,
+                       int32_t n_params, hipStream_t st) {
+    if (n_params == 0) return hipSuccess;
+    zero_floats_kernel<<<(n_params + kBlock - 1) / kBlock, kBlock, 0, st>>>(amax, n_params);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || n == 0) return e;
+    const int32_t sp = split_for(kTileAdamw, FSDP_ADAMW_SUB);
+    amax_kernel<<<grid_for(n, sp), kBlock, 0, st>>>(tiles, n, sp, kTileAdamw / sp, ents,
+                                                    reinterpret_cast<uint32_t *>(amax));
     return hipGetLastError();
 }
 

@@ -47,7 +47,7 @@ struct DevEntry {
     float *exp_avg;
     float *exp_avg_sq;
     uint16_t *full;
-    int64_t valid_numel;
+    uint8_t *full_fp8;     // unsharded FP8 E4M3 parameter (FP8 copy-out)
     uint16_t *full_grad;   // unsharded bf16 gradient (reduce-scatter copy-in)
     float *grad_acc;       // unsharded fp32 gradient accumulator
 };

@@ -129,6 +129,22 @@ class ShardedGroup:
                 for o, r, c in zip(self.full_offsets, self.rows, self.cols)]
         capi.fsdp_bind_grad_acc(self.plan, ptrs, stream)
 
+    def bind_full_fp8(self, arena: Optional[torch.Tensor] = None, stream=None) -> None:
+        """Bind unsharded FP8 parameters (uint8 views of ``arena``, laid out
+        like the full parameters; allocated here when not given)."""
+        if arena is None:
+            arena = torch.zeros(self.full_space, dtype=torch.uint8, device=self.device)
+        if arena.numel() < self.full_space:
+            raise ValueError("FP8 arena is too small for this group")
+        self.full_fp8_flat = arena
+        ptrs = [arena[o:o + r * c].data_ptr() if r * c else 0
+                for o, r, c in zip(self.full_offsets, self.rows, self.cols)]
+        capi.fsdp_bind_full_fp8(self.plan, ptrs, stream)
+
+    def full_fp8_view(self, i: int) -> torch.Tensor:
+        o = self.full_offsets[i]
+        return self.full_fp8_flat[o:o + self.rows[i] * self.cols[i]].view(self.rows[i], self.cols[i])
+
     def grad_acc_view(self, i: int) -> torch.Tensor:
         o = self.full_offsets[i]
         return self.grad_acc_flat[o:o + self.rows[i] * self.cols[i]].view(self.rows[i], self.cols[i])
@@ -141,6 +157,15 @@ class ShardedGroup:
 
     def pack_reduce_scatter(self, rs_out, dtype: int = capi.FSDP_DTYPE_BF16, stream=None) -> None:
         capi.fsdp_pack_reduce_scatter(self.plan, rs_out, dtype, stream)
+
+    def pack_fp8(self, ag_in, scales, stream=None) -> None:
+        capi.fsdp_pack_allgather_fp8(self.plan, ag_in, scales, stream)
+
+    def unpack_fp8(self, ag_out, stream=None) -> None:
+        capi.fsdp_unpack_allgather_fp8(self.plan, ag_out, stream)
+
+    def amax(self, out, stream=None) -> None:
+        capi.fsdp_amax_shard(self.plan, out, stream)
 
     def accumulate_grad(self, reset: bool, stream=None) -> None:
         capi.fsdp_accumulate_grad(self.plan, reset, stream)

@@ -839,3 +839,123 @@ def test_accumulate_misaligned_pointers_take_the_scalar_path():
     for v, want in zip(av, acc):
         assert np.array_equal(f32(v).view(np.uint32), want.view(np.uint32))
     g.close()
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 all-gather
+# ---------------------------------------------------------------------------
+
+def u8(t):
+    return t.detach().cpu().contiguous().numpy().view(np.uint8)
+
+
+@pytest.mark.parametrize("case", range(len(CASES)), ids=_case_ids())
+def test_pack_fp8_bit_exact(case):
+    name, shapes, n = CASES[case]
+    specials = np.array([0x7FC00000, 0xFFC00000, 0x7F800000, 0xFF800000, 0x43E80000, 0x3A800000,
+                         0x3AC00000, 0x3F880000, 0x3F980000, 0x80000000, 0x00000001],
+                        dtype=np.uint32).view(np.float32)
+    for r in sorted({0, n - 1}):
+        plan = O.plan(shapes, n, r)
+        g = ShardedGroup(shapes, n, r)
+        _fill_masters(g, ("fp8", name, r))
+        for i, e in enumerate(g.entries):
+            k = min(e.valid_numel, len(specials))
+            if k:
+                g.shard_view(g.master_flat, i)[:k].copy_(torch.from_numpy(specials[:k] / np.float32(20.0)))
+        masters = [f32(g.shard_view(g.master_flat, i)) for i in range(len(shapes))]
+        scales_h = np.array([20.0 + i for i in range(len(shapes))], dtype=np.float32)
+        scales = torch.from_numpy(scales_h).to(DEV)
+        want = O.pack_fp8(plan, masters, scales_h)
+        for off in (0, 1, 5, 13):
+            buf = torch.full((plan.S + off + 64,), 0xA5, dtype=torch.uint8, device=DEV)
+            g.pack_fp8(buf[off:off + plan.S], scales)
+            torch.cuda.synchronize()
+            h = u8(buf)
+            assert np.array_equal(h[off:off + plan.S], want), (name, r, off)
+            assert (h[:off] == 0xA5).all() and (h[off + plan.S:] == 0xA5).all()
+        g.close()
+
+
+@pytest.mark.parametrize("case", range(len(CASES)), ids=_case_ids())
+def test_unpack_fp8_bit_exact_misaligned(case):
+    name, shapes, n = CASES[case]
+    r = 0
+    plan = O.plan(shapes, n, r)
+    rng = np.random.default_rng(synth.seed_for("u8", name) % (2**32))
+    ag = rng.integers(0, 256, size=(n, plan.S), dtype=np.uint8)
+    for j in range(n):
+        ag[j, _pad_mask(O.plan(shapes, n, j))] = 0x7F
+    ref = O.unpack_fp8(plan, ag)
+    g = ShardedGroup(shapes, n, r, bind=False)
+    for shift in (0, 3, 9):
+        arena = torch.full((sum(rr * cc + 7 for rr, cc in zip(g.rows, g.cols)) + 32,), 0x5A,
+                           dtype=torch.uint8, device=DEV)
+        views, o = [], shift
+        for rr, cc in zip(g.rows, g.cols):
+            views.append(arena[o:o + rr * cc])
+            o += rr * cc + 7
+        capi.fsdp_bind_full_fp8(g.plan, [v.data_ptr() if v.numel() else 0 for v in views], None)
+        src = torch.zeros(n * plan.S + 32, dtype=torch.uint8, device=DEV)
+        src[shift + 1:shift + 1 + n * plan.S].copy_(torch.from_numpy(ag.reshape(-1)))
+        g.unpack_fp8(src[shift + 1:shift + 1 + n * plan.S])
+        torch.cuda.synchronize()
+        h = u8(arena)
+        mask = np.ones(h.size, bool)
+        o = shift
+        for v, want in zip(views, ref):
+            assert np.array_equal(u8(v), want.reshape(-1)), (name, shift)
+            mask[o:o + v.numel()] = False
+            o += v.numel() + 7
+        assert (h[mask] == 0x5A).all()
+    g.close()
+
+
+def test_amax_matches_oracle_and_propagates_nan():
+    shapes, n = [(1000, 70), (333,), (77, 129), (1, 2048), (1,)], 6
+    for r in (0, 5):
+        g = ShardedGroup(shapes, n, r)
+        _fill_masters(g, ("amax", r))
+        out = torch.full((len(shapes),), -1.0, device=DEV)
+        g.amax(out)
+        torch.cuda.synchronize()
+        want = O.amax([f32(g.shard_view(g.master_flat, i)) for i in range(len(shapes))])
+        assert np.array_equal(f32(out).view(np.uint32), want.view(np.uint32))
+        if g.entries[0].valid_numel:
+            g.shard_view(g.master_flat, 0)[5] = float("nan")
+            g.amax(out)
+            torch.cuda.synchronize()
+            assert torch.isnan(out[0]).item()
+        g.close()
+
+
+@pytest.mark.parametrize("cfg_index", [2, 4])
+def test_fp8_roundtrip_full_size_block(cfg_index):
+    """Every rank's FP8 copy-in, then copy-out, equals torch's saturating cast."""
+    cfg = configs.get(cfg_index)
+    shapes = [p.shape for p in cfg.groups[0].params]
+    n = cfg.world
+    Ws = []
+    for i, s in enumerate(shapes):
+        W = torch.empty(s, dtype=torch.float32, device=DEV)
+        synth.fill_normal_f32_(W, 0.02, ("fp8rt", cfg_index, i))
+        Ws.append(W)
+    scales = torch.stack([448.0 / W.abs().max() for W in Ws]).float()
+    g0 = ShardedGroup(shapes, n, 0, bind=False)
+    S = g0.S
+    ag = torch.empty(n * S, dtype=torch.uint8, device=DEV)
+    for j in range(n):
+        gj = ShardedGroup(shapes, n, j, bind=False)
+        masters = [W.view(-1)[e.row_begin * e.cols:].data_ptr() if e.valid_numel else 0
+                   for W, e in zip(Ws, gj.entries)]
+        capi.fsdp_bind(gj.plan, master=masters, stream=None)
+        gj.pack_fp8(ag[j * S:(j + 1) * S], scales)
+        torch.cuda.synchronize()
+        gj.close()
+    g0.bind_full_fp8()
+    g0.unpack_fp8(ag)
+    torch.cuda.synchronize()
+    for i, W in enumerate(Ws):
+        want = (W.reshape(W.shape[0], -1) * scales[i]).clamp(-448, 448).to(torch.float8_e4m3fn)
+        assert torch.equal(g0.full_fp8_view(i), want.view(torch.uint8)), i
+    g0.close()

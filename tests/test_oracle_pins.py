@@ -729,3 +729,82 @@ def test_pack_reduce_scatter_acc_layout(case):
             parts.append(torch.cat([piece, torch.zeros(e.seg_numel - piece.numel())]))
         want = torch.cat(parts).numpy() if parts else np.zeros(0, np.float32)
         assert np.array_equal(got[j].view(np.uint32), want.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3 all-gather
+# ---------------------------------------------------------------------------
+
+def test_e4m3_golden_vectors():
+    for ln in read_golden("e4m3_cases.txt"):
+        f, b = ln.split()[:2]
+        x = np.array([int(f, 16)], dtype=np.uint32).view(F32)
+        assert int(O.e4m3_sat(x)[0]) == int(b, 16), (f, b)
+
+
+def test_e4m3_decode_matches_torch_for_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    dec = O.e4m3_to_f32(codes)
+    t = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    assert np.array_equal(np.isnan(dec), np.isnan(t))
+    assert np.array_equal(dec[~np.isnan(dec)].view(np.uint32), t[~np.isnan(t)].view(np.uint32))
+
+
+def test_e4m3_encode_is_nearest_even_brute_force_and_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = O.e4m3_to_f32(codes).astype(np.float64)
+    finite = ~np.isnan(vals)
+    rng = np.random.default_rng(4)
+    x = np.concatenate([(rng.standard_normal(20000) * s).astype(F32) for s in (1e-3, 0.02, 1.0, 50.0, 600.0)])
+    # every midpoint between neighbouring codes and its neighbours
+    pos = np.sort(np.unique(vals[finite & (vals >= 0)]))
+    mids = ((pos[1:] + pos[:-1]) / 2).astype(F32)
+    x = np.concatenate([x, mids, -mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9))])
+    got = O.e4m3_sat(x)
+    # brute force: nearest finite code in exact arithmetic, ties to even mantissa
+    for xi, gi in zip(x.astype(np.float64), got):
+        c = np.clip(xi, -448.0, 448.0)
+        d = np.abs(vals - c)
+        d[~finite] = np.inf
+        best = np.flatnonzero(d == d.min())
+        if len(best) > 1:
+            best = [b for b in best if (b & 1) == 0]
+        want = best[0]
+        if c == 0.0:
+            want = 0x80 if np.signbit(xi) else 0x00
+        assert gi == want or (vals[gi] == vals[want]), (xi, gi, want)
+    t = torch.from_numpy(x).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(t, got)
+
+
+@pytest.mark.parametrize("case", range(len(SMALL_CASES)))
+def test_pack_fp8_matches_torch_and_unpack_round_trips(case):
+    shapes, n = SMALL_CASES[case]
+    Ws = [synth.normal_f32(int(np.prod(s)), 0.02, ("fp8", case, i)).reshape(s) for i, s in enumerate(shapes)]
+    scales = [float(448.0 / max(float(W.abs().max()) if W.numel() else 1.0, 1e-12)) for W in Ws]
+    plans = [O.plan(shapes, n, r) for r in range(n)]
+    ag = np.stack([O.pack_fp8(plans[r], [_chunks_of(W, n, r).numpy() for W in Ws], scales)
+                   for r in range(n)])
+    for r in range(n):
+        parts = []
+        for W, e, sc in zip(Ws, plans[r].entries, scales):
+            piece = (_chunks_of(W, n, r).reshape(-1) * np.float32(sc)).clamp(-448, 448)
+            q = piece.to(torch.float8_e4m3fn).view(torch.uint8)
+            parts.append(torch.cat([q, torch.zeros(e.seg_numel - q.numel(), dtype=torch.uint8)]))
+        want = torch.cat(parts).numpy() if parts else np.zeros(0, np.uint8)
+        assert np.array_equal(ag[r], want)
+    for W, full, sc in zip(Ws, O.unpack_fp8(plans[0], ag), scales):
+        want = O.e4m3_sat(W.reshape(-1).numpy() * np.float32(sc))
+        assert np.array_equal(full.reshape(-1), want)
+    # the scale maps each tensor's largest magnitude onto 448
+    for W, full, sc in zip(Ws, O.unpack_fp8(plans[0], ag), scales):
+        if W.numel():
+            assert np.nanmax(np.abs(O.e4m3_to_f32(full))) == 448.0
+
+
+def test_amax_matches_torch():
+    shards = [synth.normal_f32(k, 0.02, ("amax", k)).numpy() for k in (1, 17, 4097)] + [np.zeros(0, F32)]
+    got = O.amax(shards)
+    for g, s in zip(got, shards):
+        assert g == (np.abs(s).max() if s.size else 0.0)
+    assert np.isnan(O.amax([np.array([1.0, np.nan, -3.0], F32)])[0])
