@@ -21,12 +21,14 @@ hipError_t launch_pack(const PackTile *tiles, int64_t n, const DevEntry *ents,
 hipError_t launch_unpack(const UnpackTile *tiles, int64_t n, const DevEntry *ents,
                          const uint16_t *ag_out, hipStream_t st);
 hipError_t launch_reduce(const ReduceTile *tiles, int64_t n, const DevEntry *ents,
-                         const uint16_t *rs_in, int64_t S, int32_t N, hipStream_t st);
+                         const uint16_t *rs_in, int64_t S, int32_t N, bool chunk_aligned,
+                         hipStream_t st);
 hipError_t launch_adamw(const EwTile *tiles, int64_t n, const DevEntry *ents,
                         const float scal[8], hipStream_t st);
 hipError_t launch_step(const PackTile *tiles, int64_t n, const DevEntry *ents,
                        const uint16_t *rs_in, uint16_t *ag_in, int64_t S, int32_t N,
-                       const float scal[8], bool write_grad, hipStream_t st);
+                       const float scal[8], bool write_grad, bool chunk_aligned,
+                       hipStream_t st);
 hipError_t launch_rspack(const PackTile *tiles, int64_t n, const DevEntry *ents, void *out,
                          bool f32, hipStream_t st);
 hipError_t launch_reduce_f32(const ReduceTile *tiles, int64_t n, const DevEntry *ents,
@@ -453,9 +455,16 @@ hipError_t do_unpack(const fsdp_plan *p, const uint16_t *ag_out, hipStream_t st)
                                p->d_entries, ag_out, st);
 }
 
+// Every row piece starts 16-byte aligned: the offsets allow it and the
+// [N, S] buffer itself is 16-byte aligned.
+bool chunk_aligned(const fsdp_plan *p, const void *rows) {
+    return p->L.offsets8 && (reinterpret_cast<uintptr_t>(rows) & 15u) == 0;
+}
+
 hipError_t do_reduce(const fsdp_plan *p, const uint16_t *rs_in, hipStream_t st) {
     return fsdp::launch_reduce(p->d_reduce, static_cast<int64_t>(p->L.reduce.size()),
-                               p->d_entries, rs_in, p->L.S, p->L.world, st);
+                               p->d_entries, rs_in, p->L.S, p->L.world,
+                               chunk_aligned(p, rs_in), st);
 }
 
 hipError_t do_adamw(const fsdp_plan *p, const float scal[8], hipStream_t st) {
@@ -466,7 +475,8 @@ hipError_t do_adamw(const fsdp_plan *p, const float scal[8], hipStream_t st) {
 hipError_t do_step(const fsdp_plan *p, const uint16_t *rs_in, uint16_t *ag_in,
                    const float scal[8], bool write_grad, hipStream_t st) {
     return fsdp::launch_step(p->d_pack, static_cast<int64_t>(p->L.pack.size()), p->d_entries,
-                             rs_in, ag_in, p->L.S, p->L.world, scal, write_grad, st);
+                             rs_in, ag_in, p->L.S, p->L.world, scal, write_grad,
+                             chunk_aligned(p, rs_in), st);
 }
 
 fsdp_status launched(hipError_t e, const char *call) {

@@ -71,9 +71,6 @@
 #ifndef FSDP_ROW_BATCH
 #define FSDP_ROW_BATCH 8
 #endif
-#ifndef FSDP_STEP_PREFETCH
-#define FSDP_STEP_PREFETCH 0
-#endif
 #ifndef FSDP_ROW_BLOCK_FIT
 #define FSDP_ROW_BLOCK_FIT 0
 #endif
@@ -439,38 +436,105 @@ __device__ __forceinline__ u32x4 row_load16(const char *row, uint32_t offb, uint
     return funnel_bytes(a, b, k);
 }
 
+// Bytes [k, k + 16) of the 32-byte little-endian concatenation a:b, k even
+// and wave-uniform, without branches: an 8-byte and a 4-byte select step,
+// then a byte align of the remaining 0..3 bytes.
+__device__ __forceinline__ u32x4 funnel_sel(u32x4 a, u32x4 b, uint32_t k) {
+    const bool s8 = (k & 8u) != 0, s4 = (k & 4u) != 0;
+    const uint32_t u0 = s8 ? a.z : a.x, u1 = s8 ? a.w : a.y, u2 = s8 ? b.x : a.z;
+    const uint32_t u3 = s8 ? b.y : a.w, u4 = s8 ? b.z : b.x, u5 = s8 ? b.w : b.y;
+    const uint32_t v0 = s4 ? u1 : u0, v1 = s4 ? u2 : u1, v2 = s4 ? u3 : u2;
+    const uint32_t v3 = s4 ? u4 : u3, v4 = s4 ? u5 : u4;
+    const uint32_t sh = k & 3u;
+    return u32x4{__builtin_amdgcn_alignbyte(v1, v0, sh), __builtin_amdgcn_alignbyte(v2, v1, sh),
+                 __builtin_amdgcn_alignbyte(v3, v2, sh), __builtin_amdgcn_alignbyte(v4, v3, sh)};
+}
+
+// The same register of the next lane of the wave (wave_shl:1 DPP); the last
+// lane gets 0.
+__device__ __forceinline__ uint32_t next_lane(uint32_t x) {
+    return __builtin_amdgcn_update_dpp(0u, x, 0x130, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ u32x4 next_lane16(u32x4 a) {
+    return u32x4{next_lane(a.x), next_lane(a.y), next_lane(a.z), next_lane(a.w)};
+}
+
 // Eight consecutive column sums of the N rows of [N, S] bf16 whose row 0
 // starts at base (uniform) plus this lane's byte offset offb, added in rank
-// order from row 0; k0 = (base + offb) & 15, kS = (2S) & 15; the block reads
-// fewer than nbytes bytes from each row base.
-template <int NT, bool kRowsAligned>
-__device__ __forceinline__ void sum_rows8(const uint16_t *base, uint32_t offb, uint32_t nbytes,
+// order from row 0; k0 = (base + offb) & 15, kS = (2S) & 15.  Each row's
+// buffer range covers exactly the 16-byte chunks that hold its dbytes data
+// bytes, so a lane past the end of the data reads zeros and never touches
+// memory beyond the last chunk.  Rows are loaded FSDP_ROW_BATCH at a time so
+// that many loads are in flight per lane.
+//
+// kChunkAligned: every row starts 16-byte aligned here (k0 = 0, kS = 0), so
+// each row is one aligned 16-byte load.  Otherwise a row is read as aligned
+// 16-byte chunks and funnel-shifted; the caller gives the lanes of a wave
+// consecutive chunks (offb = 16 * (lane + const)), so a lane's second chunk
+// is the next lane's first, and lane 63's sums are not valid.
+template <int NT, bool kChunkAligned>
+__device__ __forceinline__ void sum_rows8(const uint16_t *base, uint32_t offb, uint32_t dbytes,
                                           int64_t S, int32_t N, uint32_t k0, uint32_t kS,
                                           float (&acc)[8]) {
     const char *r = reinterpret_cast<const char *>(base);
     const int64_t Sb = S * 2;
-    init8(acc, row_load16<NT>(r, offb, k0, nbytes));
-    if (kRowsAligned) {
-        constexpr int RB = FSDP_ROW_BATCH;
-        int32_t j = 1;
-        for (; j + RB - 1 < N; j += RB) {
-            u32x4 x[RB];
+    constexpr int RB = FSDP_ROW_BATCH;
+    for (int32_t j = 0; j < N; j += RB) {
+        // rows past N get an empty range: their loads read zero and are
+        // never added
+        u32x4 x[RB];
+        if (kChunkAligned) {
+            const uint32_t nb = (dbytes + 15u) & ~15u;
 #pragma unroll
-            for (int i = 0; i < RB; ++i) x[i] = row_load16<NT>(r + (j + i) * Sb, offb, k0, nbytes);
+            for (int i = 0; i < RB; ++i)
+                x[i] = bload16<NT>(r + (j + i) * Sb, offb, j + i < N ? nb : 0u);
+        } else {
+            uint32_t kk[RB];
 #pragma unroll
-            for (int i = 0; i < RB; ++i) acc8(acc, x[i]);
+            for (int i = 0; i < RB; ++i) {
+                kk[i] = (k0 + static_cast<uint32_t>(j + i) * kS) & 15u;
+                x[i] = bload16<NT>(r + (j + i) * Sb - kk[i], offb,
+                                   j + i < N ? (kk[i] + dbytes + 15u) & ~15u : 0u);
+            }
+#pragma unroll
+            for (int i = 0; i < RB; ++i) x[i] = funnel_sel(x[i], next_lane16(x[i]), kk[i]);
         }
-        for (; j < N; ++j) acc8(acc, row_load16<NT>(r + j * Sb, offb, k0, nbytes));
-    } else {
-        uint32_t k = k0;
-        for (int32_t j = 1; j < N; ++j) {
-            k = (k + kS) & 15u;
-            acc8(acc, row_load16<NT>(r + j * Sb, offb, k, nbytes));
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            if (j + i < N) {
+                if (j + i == 0) init8(acc, x[i]);
+                else acc8(acc, x[i]);
+            }
         }
     }
 }
 
-template <int POL, bool kRowsAligned>
+// Group schedule of the row kernels: 8-element groups [0, ngrp), one per
+// lane.  Aligned rows: lane l of wave w takes groups w*64 + l, then steps by
+// the block.  Misaligned rows: a wave covers 63 groups and its lane 63 only
+// loads the chunk after lane 62's (see sum_rows8); every lane runs the same
+// number of iterations, and `own` says whether its group is to be written.
+template <bool kChunkAligned>
+struct GroupWalk {
+    int64_t g, step;
+    __device__ GroupWalk() {
+        const int64_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        constexpr int64_t per = kChunkAligned ? 64 : 63;
+        g = wave * per + lane;
+        step = static_cast<int64_t>(blockDim.x >> 6) * per;
+    }
+    // the wave still has work
+    __device__ bool more(int64_t ngrp) const {
+        return g - static_cast<int64_t>(threadIdx.x & 63) < ngrp;
+    }
+    __device__ bool own(int64_t ngrp) const {
+        return g < ngrp && (kChunkAligned || (threadIdx.x & 63) != 63);
+    }
+    __device__ void next() { g += step; }
+};
+
+template <int POL, bool kChunkAligned>
 __device__ __forceinline__ void reduce_run(float *__restrict__ dst, const uint16_t *__restrict__ src0,
                                            int64_t len, int64_t S, int32_t N, float fN) {
     constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
@@ -478,24 +542,33 @@ __device__ __forceinline__ void reduce_run(float *__restrict__ dst, const uint16
     const uint32_t kS = static_cast<uint32_t>((S * 2) & 15);
     int64_t head = ((16u - (lo32(dst) & 15u)) & 15u) >> 2;
     if (head > len) head = len;
-    if (tid < head) dst[tid] = sum_rows_scalar(src0, S, N, tid) / fN;
-    const int64_t ngrp = (len - head) >> 3;
     const uint16_t *s0 = src0 + head;
     const uint32_t k0 = lo32(s0) & 15u;
-    const uint32_t nbytes = static_cast<uint32_t>(2 * (len - head) + 48);
+    if (kChunkAligned && (k0 | kS) != 0) {
+        // the launch assumed aligned rows; this run is not: element by element
+        for (int64_t e = tid; e < len; e += static_cast<int64_t>(blockDim.x))
+            dst[e] = sum_rows_scalar(src0, S, N, e) / fN;
+        return;
+    }
+    if (tid < head) dst[tid] = sum_rows_scalar(src0, S, N, tid) / fN;
+    const int64_t ngrp = (len - head) >> 3;
+    const uint32_t dbytes = static_cast<uint32_t>(2 * (len - head));
     f32x4 *dv = reinterpret_cast<f32x4 *>(dst + head);
-    const int nthr = blockDim.x;
-    for (int64_t g = tid; g < ngrp; g += nthr) {
+    for (GroupWalk<kChunkAligned> w; w.more(ngrp); w.next()) {
         float acc[8];
-        sum_rows8<LN, kRowsAligned>(s0, static_cast<uint32_t>(g) << 4, nbytes, S, N, k0, kS, acc);
-        stp<SN>(dv + 2 * g, f32x4{acc[0] / fN, acc[1] / fN, acc[2] / fN, acc[3] / fN});
-        stp<SN>(dv + 2 * g + 1, f32x4{acc[4] / fN, acc[5] / fN, acc[6] / fN, acc[7] / fN});
+        sum_rows8<LN, kChunkAligned>(s0, static_cast<uint32_t>(w.g) << 4, dbytes, S, N, k0, kS,
+                                     acc);
+        if (w.own(ngrp)) {
+            const int64_t g = w.g;
+            stp<SN>(dv + 2 * g, f32x4{acc[0] / fN, acc[1] / fN, acc[2] / fN, acc[3] / fN});
+            stp<SN>(dv + 2 * g + 1, f32x4{acc[4] / fN, acc[5] / fN, acc[6] / fN, acc[7] / fN});
+        }
     }
     const int64_t done = head + (ngrp << 3);
     if (tid < len - done) dst[done + tid] = sum_rows_scalar(src0, S, N, done + tid) / fN;
 }
 
-template <int POL, bool kRowsAligned>
+template <int POL, bool kChunkAligned>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(
     const ReduceTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
     const DevEntry *__restrict__ ents, const uint16_t *__restrict__ rs_in,
@@ -508,8 +581,8 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(
         const ReduceTile tl = tiles[t];
         if (b >= tl.len) continue;
         const int64_t len = tl.len - b < L ? tl.len - b : L;
-        reduce_run<POL, kRowsAligned>(ents[tl.entry].grad + tl.dst + b, rs_in + tl.src + b, len,
-                                      S, N, fN);
+        reduce_run<POL, kChunkAligned>(ents[tl.entry].grad + tl.dst + b, rs_in + tl.src + b, len,
+                                       S, N, fN);
     }
 }
 
@@ -707,21 +780,24 @@ __global__ __launch_bounds__(kBlock) void rspack_f32_kernel(
 // exponent rebiased from 127 to 7); below 2^-6 the code is the subnormal
 // m/8 * 2^-6 with m the significand shifted to 2^-9 units, ties to even.
 __device__ __forceinline__ uint32_t e4m3_sat(float f) {
+    // Every case is computed and the right one selected, so a wave never
+    // diverges on the value class.
     const uint32_t u = __float_as_uint(f);
     const uint32_t sign = (u >> 24) & 0x80u;
     const uint32_t mag = u & 0x7FFFFFFFu;
-    if (mag > 0x7F800000u) return sign | 0x7Fu;
-    if (mag >= 0x43E00000u) return sign | 0x7Eu;
-    if (mag >= 0x3C800000u) {
-        const uint32_t r = (mag + 0x7FFFFu + ((mag >> 20) & 1u)) >> 20;
-        const uint32_t c = r - (120u << 3);
-        return sign | (c > 0x7Eu ? 0x7Eu : c);
-    }
+    // normal: round the fp32 pattern to 3 mantissa bits, rebias 127 -> 7
+    uint32_t cn = ((mag + 0x7FFFFu + ((mag >> 20) & 1u)) >> 20) - (120u << 3);
+    cn = cn > 0x7Eu ? 0x7Eu : cn;
+    // subnormal (exponent field 120 or less): shifts of 32 or more leave 0,
+    // and so does 31 for a 24-bit significand, so the shift is capped there
     const uint32_t E = mag >> 23;
-    const uint32_t shift = 141u - E;          // >= 21 here
-    if (shift >= 32u) return sign;
+    const uint32_t shift = E - 110u <= 10u ? 141u - E : 31u;
     const uint32_t M = (mag & 0x7FFFFFu) | 0x800000u;
-    return sign | ((M + (1u << (shift - 1u)) - 1u + ((M >> shift) & 1u)) >> shift);
+    const uint32_t cs = (M + (1u << (shift - 1u)) - 1u + ((M >> shift) & 1u)) >> shift;
+    uint32_t r = mag >= 0x3C800000u ? cn : cs;
+    r = mag >= 0x43E00000u ? 0x7Eu : r;
+    r = mag > 0x7F800000u ? 0x7Fu : r;
+    return sign | r;
 }
 
 __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d, float s) {
@@ -1117,7 +1193,7 @@ __device__ __forceinline__ void step_scalar_at(const uint16_t *rs0, int64_t S, i
 // element.  The vector path aligns on the fp32 shards (the bulk of the
 // bytes); contributions are funnel-shifted per row and the bf16 output is
 // stored whole, by dwords or by halves, as its address allows.
-template <int POL, bool kRowsAligned, bool kWriteGrad>
+template <int POL, bool kChunkAligned, bool kWriteGrad>
 __device__ __forceinline__ void step_run(const uint16_t *__restrict__ rs0, int64_t S, int32_t N,
                                          float fN, float *P, float *M, float *Vv, float *G,
                                          uint16_t *dst, int64_t len, int64_t valid,
@@ -1125,42 +1201,35 @@ __device__ __forceinline__ void step_run(const uint16_t *__restrict__ rs0, int64
     constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
     const int tid = threadIdx.x;
     const uint32_t ap = lo32(P) & 15u;
+    int64_t head = ((16u - ap) & 15u) >> 2;
+    if (head > valid) head = valid;
+    const uint32_t kS = static_cast<uint32_t>((S * 2) & 15);
+    const uint32_t k0 = lo32(rs0 + head) & 15u;
+    // the vector path needs the shards equally aligned, and with
+    // kChunkAligned the rows 16-byte aligned at the first vector element
     const bool same = ap == (lo32(M) & 15u) && ap == (lo32(Vv) & 15u) &&
-                      (!kWriteGrad || ap == (lo32(G) & 15u));
+                      (!kWriteGrad || ap == (lo32(G) & 15u)) &&
+                      (!kChunkAligned || (k0 | kS) == 0);
     if (!same) {
         for (int64_t e = tid; e < valid; e += static_cast<int64_t>(blockDim.x))
             step_scalar_at<kWriteGrad>(rs0, S, N, fN, P, M, Vv, G, dst, e, c);
     } else {
-        int64_t head = ((16u - ap) & 15u) >> 2;
-        if (head > valid) head = valid;
         if (tid < head) step_scalar_at<kWriteGrad>(rs0, S, N, fN, P, M, Vv, G, dst, tid, c);
         const int64_t ngrp = (valid - head) >> 3;
-        const uint32_t kS = static_cast<uint32_t>((S * 2) & 15);
-        const uint32_t k0 = lo32(rs0 + head) & 15u;
         const uint32_t ka = lo32(dst + head) & 15u;
-        const uint32_t nbytes = static_cast<uint32_t>(2 * (valid - head) + 48);
-        const int nthr = blockDim.x;
-        for (int64_t g8 = tid; g8 < ngrp; g8 += nthr) {
-            const int64_t e0 = head + (g8 << 3);
+        const uint32_t dbytes = static_cast<uint32_t>(2 * (valid - head));
+        for (GroupWalk<kChunkAligned> w; w.more(ngrp); w.next()) {
+            float acc[8];
+            sum_rows8<1, kChunkAligned>(rs0 + head, static_cast<uint32_t>(w.g) << 4, dbytes, S, N,
+                                        k0, kS, acc);
+            if (!w.own(ngrp)) continue;
+            const int64_t e0 = head + (w.g << 3);
             f32x4 *pv = reinterpret_cast<f32x4 *>(P + e0);
             f32x4 *mv = reinterpret_cast<f32x4 *>(M + e0);
             f32x4 *vv = reinterpret_cast<f32x4 *>(Vv + e0);
-#if FSDP_STEP_PREFETCH
-            // the optimizer state streams in while the N rows are summed
             f32x4 p0 = ldp<LN>(pv), p1 = ldp<LN>(pv + 1);
             f32x4 m0 = ldp<LN>(mv), m1 = ldp<LN>(mv + 1);
             f32x4 v0 = ldp<LN>(vv), v1 = ldp<LN>(vv + 1);
-            float acc[8];
-            sum_rows8<1, kRowsAligned>(rs0 + head, static_cast<uint32_t>(g8) << 4, nbytes, S, N,
-                                       k0, kS, acc);
-#else
-            float acc[8];
-            sum_rows8<1, kRowsAligned>(rs0 + head, static_cast<uint32_t>(g8) << 4, nbytes, S, N,
-                                       k0, kS, acc);
-            f32x4 p0 = ldp<LN>(pv), p1 = ldp<LN>(pv + 1);
-            f32x4 m0 = ldp<LN>(mv), m1 = ldp<LN>(mv + 1);
-            f32x4 v0 = ldp<LN>(vv), v1 = ldp<LN>(vv + 1);
-#endif
             const f32x4 g0{acc[0] / fN, acc[1] / fN, acc[2] / fN, acc[3] / fN};
             const f32x4 g1{acc[4] / fN, acc[5] / fN, acc[6] / fN, acc[7] / fN};
             if (kWriteGrad) {
@@ -1186,7 +1255,7 @@ __device__ __forceinline__ void step_run(const uint16_t *__restrict__ rs0, int64
     zero_bf16<1>(dst, valid, len);
 }
 
-template <int POL, bool kRowsAligned, bool kWriteGrad>
+template <int POL, bool kChunkAligned, bool kWriteGrad>
 __global__ __launch_bounds__(kBlock) void step_kernel(
     const PackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
     const DevEntry *__restrict__ ents,
@@ -1204,7 +1273,7 @@ __global__ __launch_bounds__(kBlock) void step_kernel(
         valid = valid < 0 ? 0 : (valid > len ? len : valid);
         const DevEntry en = ents[tl.entry];
         const int64_t o = tl.src + b;
-        step_run<POL, kRowsAligned, kWriteGrad>(rs_in + tl.dst + b, S, N, fN, en.master + o,
+        step_run<POL, kChunkAligned, kWriteGrad>(rs_in + tl.dst + b, S, N, fN, en.master + o,
                                                 en.exp_avg + o, en.exp_avg_sq + o,
                                                 kWriteGrad ? en.grad + o : nullptr,
                                                 ag_in + tl.dst + b, len, valid, c);
@@ -1274,13 +1343,14 @@ hipError_t launch_unpack(const UnpackTile *tiles, int64_t n, const DevEntry *ent
 }
 
 hipError_t launch_reduce(const ReduceTile *tiles, int64_t n, const DevEntry *ents,
-                         const uint16_t *rs_in, int64_t S, int32_t N, hipStream_t st) {
+                         const uint16_t *rs_in, int64_t S, int32_t N, bool chunk_aligned,
+                         hipStream_t st) {
     if (n == 0) return hipSuccess;
     const float fN = static_cast<float>(N);
     const int32_t sp = split_rows(kTileReduce, N, 0);
     const unsigned grid = grid_for(n, sp);
     const unsigned thr = row_threads(kTileReduce / sp);
-    if (((S * 2) & 15) == 0)
+    if (chunk_aligned)
         reduce_kernel<FSDP_REDUCE_POL, true>
             <<<grid, thr, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
     else
@@ -1391,7 +1461,8 @@ hipError_t launch_reduce_f32(const ReduceTile *tiles, int64_t n, const DevEntry 
 
 hipError_t launch_step(const PackTile *tiles, int64_t n, const DevEntry *ents,
                        const uint16_t *rs_in, uint16_t *ag_in, int64_t S, int32_t N,
-                       const float scal[8], bool write_grad, hipStream_t st) {
+                       const float scal[8], bool write_grad, bool chunk_aligned,
+                       hipStream_t st) {
     if (n == 0) return hipSuccess;
     const float fN = static_cast<float>(N);
     const AdamwScalars c = to_scalars(scal);
@@ -1400,7 +1471,7 @@ hipError_t launch_step(const PackTile *tiles, int64_t n, const DevEntry *ents,
     const int64_t sub = kTilePack / sp;
     const unsigned grid = grid_for(n, sp);
     const unsigned thr = row_threads(sub);
-    const bool aligned = ((S * 2) & 15) == 0;
+    const bool aligned = chunk_aligned;
     constexpr int P = FSDP_STEP_POL;
     if (aligned && write_grad)
         step_kernel<P, true, true><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N, fN, c);

@@ -97,6 +97,9 @@ fsdp_status build_layout(const int64_t *rows, const int64_t *cols, int32_t n,
         if (e.local_rows == 0) ++L.n_empty;
     }
     L.S = off;
+    L.offsets8 = (L.S % 8) == 0;
+    for (const fsdp_shard_entry_t &e : L.entries)
+        if (e.shard_offset % 8 != 0) L.offsets8 = false;
 
     // Tiles.  Every run below is split into pieces of at most kTile* elements.
     for (int32_t i = 0; i < n; ++i) {

@@ -106,6 +106,9 @@ struct Layout {
     std::vector<fsdp_shard_entry_t> entries;
     int64_t S = 0, V = 0, F = 0;
     int32_t n_empty = 0;
+    // S and every shard_offset are multiples of 8 elements: with a 16-byte
+    // aligned [N, S] buffer every piece of every row starts 16-byte aligned
+    bool offsets8 = true;
     std::vector<PackTile> pack;
     std::vector<PackTile> rspack;     // reduce-scatter copy-in: dst counts rows*S
     std::vector<UnpackTile> unpack;

@@ -75,6 +75,9 @@ CASES = [
     ("more-ranks", [(6, 3), (17,)], 8),
     ("n1", [(9, 7), (4097,)], 1),
     ("tiles", [(300, 1000), (4096, 33), (70001,)], 8),
+    # odd pieces over several row batches (12 = 8 + 4, 64 = 8 x 8)
+    ("odd-n12", [(1000, 37), (4097,), (129, 3), (25, 8)], 12),
+    ("odd-n64", [(700, 9), (129,), (64, 33)], 64),
 ]
 
 
