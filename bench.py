@@ -51,8 +51,10 @@ def algorithmic_bytes(S, V, F, N, fused):
             "unpack": 4 * F}
 
 
-KERNEL_SYMBOLS = {"step": "step_kernel", "reduce": "reduce_kernel", "adamw": "adamw_kernel",
-                  "pack": "pack_kernel", "unpack": "unpack_kernel"}
+# rocprofv3 kernel names; the fused step has a variant for 16-byte aligned rows
+KERNEL_SYMBOLS = {"step": ("step_kernel_aligned", "step_kernel"), "reduce": ("reduce_kernel",),
+                  "adamw": ("adamw_kernel",), "pack": ("pack_kernel",),
+                  "unpack": ("unpack_kernel",)}
 
 
 def measured_traffic(workload, rank, align, kind):
@@ -71,8 +73,11 @@ def measured_traffic(workload, rank, align, kind):
     wl = rec.get("workloads", {}).get(workload)
     if not wl or wl.get("rank") != rank or wl.get("align_elems") != align:
         return None
-    k = wl.get("kernels", {}).get(KERNEL_SYMBOLS[kind])
-    return None if k is None else k["traffic_bytes_per_launch"]
+    for sym in KERNEL_SYMBOLS[kind]:
+        k = wl.get("kernels", {}).get(sym)
+        if k is not None:
+            return k["traffic_bytes_per_launch"]
+    return None
 
 
 KERNEL_NAMES = {"step": "step_kernel (fused reduce+adamw+pack)", "reduce": "reduce_kernel",
@@ -396,6 +401,11 @@ def main():
                for k in kinds}
 
     eff_gbps = step_bytes / (ms_step * 1e-3) / 1e9
+    # the method's own bytes per step, counted kernel by kernel as if unfused
+    # (reduce 2NV+4V, AdamW 28V, copy-in 4V+2S, copy-out 4F): what a step
+    # has to move when each stage is its own pass over HBM
+    method_bytes = sum(sum(algorithmic_bytes(g.S, g.V, g.F, n, False).values()) for g in groups)
+    method_gbps = method_bytes / (ms_step * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": V / (ms_step * 1e-3),
@@ -418,6 +428,9 @@ def main():
         "hbm_frac": eff_gbps / HBM_PEAK_GBPS,
         "step_algorithmic_bytes": step_bytes,
         "wall_ms_per_step": wall * 1e3 / args.steps,
+        "method_bytes_per_step": method_bytes,
+        "method_effective_GBps": method_gbps,
+        "method_hbm_frac": method_gbps / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "kernel": KERNEL_NAMES[dominant],
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,

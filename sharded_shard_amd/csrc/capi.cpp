@@ -32,7 +32,8 @@ hipError_t launch_step(const PackTile *tiles, int64_t n, const DevEntry *ents,
 hipError_t launch_rspack(const PackTile *tiles, int64_t n, const DevEntry *ents, void *out,
                          bool f32, hipStream_t st);
 hipError_t launch_reduce_f32(const ReduceTile *tiles, int64_t n, const DevEntry *ents,
-                             const float *rs_in, int64_t S, int32_t N, hipStream_t st);
+                             const float *rs_in, int64_t S, int32_t N, bool chunk_aligned,
+                             hipStream_t st);
 hipError_t launch_accumulate(const EwTile *tiles, int64_t n, const DevEntry *ents, bool reset,
                              hipStream_t st);
 hipError_t launch_pack_fp8(const PackTile *tiles, int64_t n, const DevEntry *ents, uint8_t *ag_in,
@@ -628,6 +629,7 @@ fsdp_status fsdp_reduce_shard_f32(const fsdp_plan *p, const float *rs_in, void *
     if ((s = check_device(p)) != FSDP_OK) return s;
     return launched(fsdp::launch_reduce_f32(p->d_reduce, static_cast<int64_t>(p->L.reduce.size()),
                                             p->d_entries, rs_in, p->L.S, p->L.world,
+                                            chunk_aligned(p, rs_in),
                                             static_cast<hipStream_t>(stream)),
                     "fsdp_reduce_shard_f32: launch");
 }
