@@ -39,9 +39,9 @@
 // read all N rows per element, the sub-range shrinks as N grows
 // (FSDP_ROWS_BUDGET row-elements per block, at least FSDP_MIN_SUB).  Rows in
 // flight per lane: the fused step keeps FSDP_STEP_ROW_BATCH row loads
-// outstanding, the plain reductions FSDP_REDUCE_ROW_BATCH (measured on
-// MI355X: more rows in flight per wave cost the reductions bandwidth, fewer
-// cost the step).
+// outstanding up to 8 ranks and FSDP_STEP_ROW_BATCH_WIDE beyond, the plain
+// reductions FSDP_REDUCE_ROW_BATCH (measured on MI355X: more rows in flight
+// per wave cost the reductions bandwidth, fewer cost the step at 6-8 ranks).
 #ifndef FSDP_UNPACK_POL
 #define FSDP_UNPACK_POL 3
 #endif
@@ -80,6 +80,9 @@
 #endif
 #ifndef FSDP_STEP_ROW_BATCH
 #define FSDP_STEP_ROW_BATCH 8
+#endif
+#ifndef FSDP_STEP_ROW_BATCH_WIDE
+#define FSDP_STEP_ROW_BATCH_WIDE 4
 #endif
 #ifndef FSDP_REDUCE_ROW_BATCH
 #define FSDP_REDUCE_ROW_BATCH 2
@@ -1227,7 +1230,7 @@ __device__ __forceinline__ void step_scalar_at(const uint16_t *rs0, int64_t S, i
 // element.  The vector path aligns on the fp32 shards (the bulk of the
 // bytes); contributions are funnel-shifted per row and the bf16 output is
 // stored whole, by dwords or by halves, as its address allows.
-template <int POL, bool kChunkAligned, bool kWriteGrad>
+template <int POL, int RB, bool kChunkAligned, bool kWriteGrad>
 __device__ __forceinline__ void step_run(const uint16_t *__restrict__ rs0, int64_t S, int32_t N,
                                          float fN, float *P, float *M, float *Vv, float *G,
                                          uint16_t *dst, int64_t len, int64_t valid,
@@ -1254,7 +1257,7 @@ __device__ __forceinline__ void step_run(const uint16_t *__restrict__ rs0, int64
         const uint32_t dbytes = static_cast<uint32_t>(2 * (valid - head));
         for (GroupWalk<kChunkAligned> w; w.more(ngrp); w.next()) {
             float acc[8];
-            sum_rows8<1, FSDP_STEP_ROW_BATCH, kChunkAligned>(
+            sum_rows8<1, RB, kChunkAligned>(
                 rs0 + head, static_cast<uint32_t>(w.g) << 4, dbytes, S, N, k0, kS, acc);
             if (!w.own(ngrp)) continue;
             const int64_t e0 = head + (w.g << 3);
@@ -1289,7 +1292,7 @@ __device__ __forceinline__ void step_run(const uint16_t *__restrict__ rs0, int64
     zero_bf16<1>(dst, valid, len);
 }
 
-template <int POL, bool kChunkAligned, bool kWriteGrad>
+template <int POL, int RB, bool kChunkAligned, bool kWriteGrad>
 __device__ __forceinline__ void step_tiles(const PackTile *__restrict__ tiles, int64_t n_tiles,
                                            int32_t split, int64_t sub,
                                            const DevEntry *__restrict__ ents,
@@ -1308,7 +1311,7 @@ __device__ __forceinline__ void step_tiles(const PackTile *__restrict__ tiles, i
         valid = valid < 0 ? 0 : (valid > len ? len : valid);
         const DevEntry en = ents[tl.entry];
         const int64_t o = tl.src + b;
-        step_run<POL, kChunkAligned, kWriteGrad>(rs_in + tl.dst + b, S, N, fN, en.master + o,
+        step_run<POL, RB, kChunkAligned, kWriteGrad>(rs_in + tl.dst + b, S, N, fN, en.master + o,
                                                 en.exp_avg + o, en.exp_avg_sq + o,
                                                 kWriteGrad ? en.grad + o : nullptr,
                                                 ag_in + tl.dst + b, len, valid, c);
@@ -1317,22 +1320,24 @@ __device__ __forceinline__ void step_tiles(const PackTile *__restrict__ tiles, i
 
 // Aligned rows: scheduled for 6 waves per SIMD (measured faster on MI355X
 // than the default target or 7 or 8 waves).
-template <int POL, bool kWriteGrad>
+template <int POL, int RB, bool kWriteGrad>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(FSDP_STEP_WAVES)))
 void step_kernel_aligned(const PackTile *__restrict__ tiles, int64_t n_tiles, int32_t split,
                          int64_t sub, const DevEntry *__restrict__ ents,
                          const uint16_t *__restrict__ rs_in, uint16_t *__restrict__ ag_in,
                          int64_t S, int32_t N, float fN, AdamwScalars c) {
-    step_tiles<POL, true, kWriteGrad>(tiles, n_tiles, split, sub, ents, rs_in, ag_in, S, N, fN, c);
+    step_tiles<POL, RB, true, kWriteGrad>(tiles, n_tiles, split, sub, ents, rs_in, ag_in, S, N, fN,
+                                          c);
 }
 
-template <int POL, bool kWriteGrad>
+template <int POL, int RB, bool kWriteGrad>
 __global__ __launch_bounds__(kBlock) void step_kernel(
     const PackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
     const DevEntry *__restrict__ ents,
     const uint16_t *__restrict__ rs_in, uint16_t *__restrict__ ag_in, int64_t S, int32_t N,
     float fN, AdamwScalars c) {
-    step_tiles<POL, false, kWriteGrad>(tiles, n_tiles, split, sub, ents, rs_in, ag_in, S, N, fN, c);
+    step_tiles<POL, RB, false, kWriteGrad>(tiles, n_tiles, split, sub, ents, rs_in, ag_in, S, N, fN,
+                                           c);
 }
 
 inline unsigned grid_for(int64_t n_tiles, int32_t split) {
@@ -1515,6 +1520,25 @@ hipError_t launch_reduce_f32(const ReduceTile *tiles, int64_t n, const DevEntry 
     return hipGetLastError();
 }
 
+template <int P, int RB>
+void launch_step_rb(bool aligned, bool write_grad, unsigned grid, unsigned thr, hipStream_t st,
+                    const PackTile *tiles, int64_t n, int32_t sp, int64_t sub, const DevEntry *ents,
+                    const uint16_t *rs_in, uint16_t *ag_in, int64_t S, int32_t N, float fN,
+                    const AdamwScalars &c) {
+    if (aligned && write_grad)
+        step_kernel_aligned<P, RB, true><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in,
+                                                              S, N, fN, c);
+    else if (aligned)
+        step_kernel_aligned<P, RB, false><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in,
+                                                               ag_in, S, N, fN, c);
+    else if (write_grad)
+        step_kernel<P, RB, true><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N,
+                                                      fN, c);
+    else
+        step_kernel<P, RB, false><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N,
+                                                       fN, c);
+}
+
 hipError_t launch_step(const PackTile *tiles, int64_t n, const DevEntry *ents,
                        const uint16_t *rs_in, uint16_t *ag_in, int64_t S, int32_t N,
                        const float scal[8], bool write_grad, bool chunk_aligned,
@@ -1529,14 +1553,12 @@ hipError_t launch_step(const PackTile *tiles, int64_t n, const DevEntry *ents,
     const unsigned thr = row_threads(sub);
     const bool aligned = chunk_aligned;
     constexpr int P = FSDP_STEP_POL;
-    if (aligned && write_grad)
-        step_kernel_aligned<P, true><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N, fN, c);
-    else if (aligned)
-        step_kernel_aligned<P, false><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N, fN, c);
-    else if (write_grad)
-        step_kernel<P, true><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N, fN, c);
+    if (N <= 8)
+        launch_step_rb<P, FSDP_STEP_ROW_BATCH>(aligned, write_grad, grid, thr, st, tiles, n, sp, sub,
+                                               ents, rs_in, ag_in, S, N, fN, c);
     else
-        step_kernel<P, false><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N, fN, c);
+        launch_step_rb<P, FSDP_STEP_ROW_BATCH_WIDE>(aligned, write_grad, grid, thr, st, tiles, n, sp,
+                                                    sub, ents, rs_in, ag_in, S, N, fN, c);
     return hipGetLastError();
 }
 
