@@ -103,7 +103,10 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device-to-device copy of 2 GiB instead (the "
                          "reference for HBM byte counters and the copy ceiling)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be at least 1 and --warmup at least 0")
+    return args
 
 
 def copy_calibration(reps=10):
@@ -361,9 +364,21 @@ def main():
     def elapsed(evs):
         return [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(len(groups))]
 
+    def elapsed_sampled(evs):
+        return [(i, evs[2 * i].elapsed_time(evs[2 * i + 1])) for i in range(len(groups))
+                if evs[2 * i] is not None]
+
     for _ in range(args.warmup):
         step()
-    timed_events = [new_events() for _ in range(args.steps)]
+    # Each group's launch of the dominant kernel is timed once over the timed
+    # steps (group g in step g mod K): a recorded event pair costs the two
+    # launches around it their back-to-back dispatch (about 6 us per pair on
+    # MI355X), so timing every launch of every step would slow the steps the
+    # same region measures.
+    timed_events = []
+    for k in range(args.steps):
+        evs = new_events()
+        timed_events.append([e if (i // 2) % args.steps == k else None for i, e in enumerate(evs)])
     torch.cuda.synchronize()
     print(f"bench: {args.warmup} warmup steps done", file=sys.stderr, flush=True)
 
@@ -378,10 +393,11 @@ def main():
     wall = time.perf_counter() - w0
     ms_step = start.elapsed_time(end) / args.steps
     print(f"bench: {args.steps} timed steps, {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
-    dom = [x for evs in timed_events for x in elapsed(evs)]
+    dom = [x for evs in timed_events for x in elapsed_sampled(evs)]
     dom_launches = len(dom)
-    dom_avg_ms = sum(dom) / max(1, dom_launches)
-    dom_bytes_per_launch = byts[dominant] / len(groups)
+    dom_avg_ms = sum(ms for _, ms in dom) / max(1, dom_launches)
+    dom_bytes_per_launch = sum(algorithmic_bytes(groups[i].S, groups[i].V, groups[i].F, n, fused)[dominant]
+                               for i, _ in dom) / max(1, dom_launches)
     achieved = dom_bytes_per_launch / (dom_avg_ms * 1e-3) / 1e9
 
     # per-kernel breakdown: extra untimed steps, each timing one kernel kind

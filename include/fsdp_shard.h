@@ -377,7 +377,10 @@ fsdp_status fsdp_step_shard(const fsdp_plan *plan, const uint16_t *rs_in,
  *   timing_events  NULL, or 2*n_groups hipEvent_t (as void*): events 2g and
  *                  2g+1 are recorded on `stream` just before and after group
  *                  g's launch of kernel `timed_kernel` (FSDP_KERNEL_*), which
- *                  must be one this call runs
+ *                  must be one this call runs.  A NULL pair leaves group g
+ *                  untimed (each recorded pair breaks the back-to-back
+ *                  dispatch of two launches, so a caller may time a few
+ *                  groups per step); a pair with one NULL is an error
  * Every group is checked before anything is launched.  Errors: as the
  * single-group calls, plus FSDP_E_INVAL for null arrays, unknown flags or a
  * timed kernel the call does not run. */

@@ -390,8 +390,9 @@ class StepGroupsCall:
 
     def __call__(self, step: int, timed_kernel: int = 0, events=None) -> None:
         ev = None
-        if events is not None:
-            ev = (ctypes.c_void_p * len(events))(*[int(e.cuda_event) for e in events])
+        if events is not None:     # None entries leave that group untimed
+            ev = (ctypes.c_void_p * len(events))(
+                *[int(e.cuda_event) if e is not None else None for e in events])
             ev = ctypes.cast(ev, _PP)
         _check(lib.fsdp_step_groups(ctypes.cast(self._plans, _PP), self.n, self._rs, self._ag_in,
                                     self._ag_out, ctypes.byref(self._hp), step, self.flags,

@@ -655,9 +655,10 @@ fsdp_status fsdp_step_groups(fsdp_plan *const *plans, int32_t n_groups,
                                  : timed_kernel == FSDP_KERNEL_STEP);
         if (!ok || (timed_kernel == FSDP_KERNEL_UNPACK && ag_out == nullptr))
             return fail(FSDP_E_INVAL, "fsdp_step_groups: timed_kernel is not run by this call");
-        for (int32_t g = 0; g < 2 * n_groups; ++g)
-            if (timing_events[g] == nullptr)
-                return fail(FSDP_E_INVAL, "fsdp_step_groups: null timing event");
+        for (int32_t g = 0; g < n_groups; ++g)
+            if ((timing_events[2 * g] == nullptr) != (timing_events[2 * g + 1] == nullptr))
+                return fail(FSDP_E_INVAL, "fsdp_step_groups: timing events of a group must both be "
+                                          "set or both be null");
     }
     fsdp_status s = check_hparams(hp, step, call);
     if (s != FSDP_OK) return s;
@@ -678,7 +679,9 @@ fsdp_status fsdp_step_groups(fsdp_plan *const *plans, int32_t n_groups,
     adamw_scalars(hp, step, scal);
     hipStream_t st = static_cast<hipStream_t>(stream);
     auto mark = [&](int32_t g, int32_t kernel, int which) -> hipError_t {
-        if (timing_events == nullptr || kernel != timed_kernel) return hipSuccess;
+        if (timing_events == nullptr || kernel != timed_kernel ||
+            timing_events[2 * g + which] == nullptr)
+            return hipSuccess;
         return hipEventRecord(static_cast<hipEvent_t>(timing_events[2 * g + which]), st);
     };
     for (int32_t g = 0; g < n_groups; ++g) {

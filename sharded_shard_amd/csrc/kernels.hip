@@ -46,7 +46,19 @@
 #define FSDP_UNPACK_POL 3
 #endif
 #ifndef FSDP_REDUCE_POL
-#define FSDP_REDUCE_POL 3
+#define FSDP_REDUCE_POL 1
+#endif
+// Lanes of these kernels store two 16-byte halves of a 32-byte span per
+// group: non-temporal stores of that pattern cost extra HBM writes (measured
+// 1.1-1.7x the algorithmic bytes), plain stores do not.
+#ifndef FSDP_REDUCE_F32_POL
+#define FSDP_REDUCE_F32_POL 0
+#endif
+#ifndef FSDP_RSPACK_F32_POL
+#define FSDP_RSPACK_F32_POL 1
+#endif
+#ifndef FSDP_RSPACK_ACC_POL
+#define FSDP_RSPACK_ACC_POL 0
 #endif
 #ifndef FSDP_ADAMW_POL
 #define FSDP_ADAMW_POL 0
@@ -89,6 +101,24 @@
 #endif
 #ifndef FSDP_STEP_WAVES
 #define FSDP_STEP_WAVES 6
+#endif
+// occupancy target of the fused step on misaligned rows (0: the default)
+#ifndef FSDP_STEP_GEN_WAVES
+#define FSDP_STEP_GEN_WAVES 0
+#endif
+#if FSDP_STEP_GEN_WAVES > 0
+#define FSDP_STEP_GEN_ATTR __attribute__((amdgpu_waves_per_eu(FSDP_STEP_GEN_WAVES)))
+#else
+#define FSDP_STEP_GEN_ATTR
+#endif
+// occupancy target of the AdamW kernel (0: the compiler's default)
+#ifndef FSDP_ADAMW_WAVES
+#define FSDP_ADAMW_WAVES 0
+#endif
+#if FSDP_ADAMW_WAVES > 0
+#define FSDP_ADAMW_ATTR __attribute__((amdgpu_waves_per_eu(FSDP_ADAMW_WAVES)))
+#else
+#define FSDP_ADAMW_ATTR
 #endif
 #ifndef FSDP_ROW_BLOCK_FIT
 #define FSDP_ROW_BLOCK_FIT 0
@@ -657,7 +687,7 @@ __device__ __forceinline__ void adamw_run(float *P, const float *G, float *M, fl
 }
 
 template <int POL>
-__global__ __launch_bounds__(kBlock) void adamw_kernel(
+__global__ __launch_bounds__(kBlock) FSDP_ADAMW_ATTR void adamw_kernel(
     const EwTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
     const DevEntry *__restrict__ ents, AdamwScalars c) {
     const int64_t L = sub;
@@ -1331,7 +1361,7 @@ void step_kernel_aligned(const PackTile *__restrict__ tiles, int64_t n_tiles, in
 }
 
 template <int POL, int RB, bool kWriteGrad>
-__global__ __launch_bounds__(kBlock) void step_kernel(
+__global__ __launch_bounds__(kBlock) FSDP_STEP_GEN_ATTR void step_kernel(
     const PackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
     const DevEntry *__restrict__ ents,
     const uint16_t *__restrict__ rs_in, uint16_t *__restrict__ ag_in, int64_t S, int32_t N,
@@ -1483,7 +1513,7 @@ hipError_t launch_rspack_acc(const PackTile *tiles, int64_t n, const DevEntry *e
                              hipStream_t st) {
     if (n == 0) return hipSuccess;
     const int32_t sp = split_for(kTileUnpack, FSDP_UNPACK_SUB);
-    rspack_acc_kernel<FSDP_UNPACK_POL><<<grid_for(n, sp), kBlock, 0, st>>>(
+    rspack_acc_kernel<FSDP_RSPACK_ACC_POL><<<grid_for(n, sp), kBlock, 0, st>>>(
         tiles, n, sp, kTileUnpack / sp, ents, out);
     return hipGetLastError();
 }
@@ -1494,7 +1524,7 @@ hipError_t launch_rspack(const PackTile *tiles, int64_t n, const DevEntry *ents,
     const int32_t sp = split_for(kTileUnpack, FSDP_UNPACK_SUB);
     const unsigned grid = grid_for(n, sp);
     if (f32)
-        rspack_f32_kernel<FSDP_UNPACK_POL><<<grid, kBlock, 0, st>>>(
+        rspack_f32_kernel<FSDP_RSPACK_F32_POL><<<grid, kBlock, 0, st>>>(
             tiles, n, sp, kTileUnpack / sp, ents, static_cast<float *>(out));
     else
         rspack_bf16_kernel<FSDP_UNPACK_POL><<<grid, kBlock, 0, st>>>(
@@ -1512,10 +1542,10 @@ hipError_t launch_reduce_f32(const ReduceTile *tiles, int64_t n, const DevEntry 
     const unsigned grid = grid_for(n, sp);
     const unsigned thr = row_threads(kTileReduce / sp);
     if (chunk_aligned)
-        reduce_f32_kernel<FSDP_REDUCE_POL, true>
+        reduce_f32_kernel<FSDP_REDUCE_F32_POL, true>
             <<<grid, thr, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
     else
-        reduce_f32_kernel<FSDP_REDUCE_POL, false>
+        reduce_f32_kernel<FSDP_REDUCE_F32_POL, false>
             <<<grid, thr, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
     return hipGetLastError();
 }

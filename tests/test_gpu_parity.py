@@ -570,9 +570,12 @@ def test_step_groups_equals_per_group_calls(unfused):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(B))]
         for e in evs:
             e.record()
+        if t == 2:                # a null pair leaves the middle group untimed
+            evs[2] = evs[3] = None
         call(t, capi.FSDP_KERNEL_UNPACK, evs)
         torch.cuda.synchronize()
-        assert all(evs[2 * i].elapsed_time(evs[2 * i + 1]) >= 0 for i in range(len(B)))
+        assert all(evs[2 * i].elapsed_time(evs[2 * i + 1]) >= 0 for i in range(len(B))
+                   if evs[2 * i] is not None)
         for ga, gb, aa, ab in zip(A, B, ag_a, ag_b):
             assert torch.equal(aa, ab)
             for fl in ("master_flat", "m_flat", "v_flat", "full_flat"):
@@ -608,6 +611,11 @@ def test_step_groups_checks_every_group_before_launching():
     with pytest.raises(capi.FsdpError) as ei:      # reduce is not a kernel of the fused path
         call1(1, capi.FSDP_KERNEL_REDUCE, evs)
     assert ei.value.status == capi.FSDP_E_INVAL
+    with pytest.raises(capi.FsdpError) as ei:      # half a pair
+        call1(1, capi.FSDP_KERNEL_STEP, [evs[0], None])
+    assert ei.value.status == capi.FSDP_E_INVAL
+    torch.cuda.synchronize()
+    assert torch.equal(before, g1.master_flat), "a rejected call launched something"
     g1.close()
     g2.close()
 
