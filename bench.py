@@ -13,8 +13,8 @@ before the timed region starts.
 Prints one JSON line: params/s of this rank's shard (value), effective HBM
 GB/s (algorithmic bytes / time) and its fraction of the 8 TB/s HBM peak, the
 roofline of the dominant kernel (the one with the most algorithmic bytes)
-measured with HIP events around its launches inside the timed region, and the
-CPU oracle timed on a bounded sample of the same workload.
+measured with HIP events around one launch per group inside the timed region,
+and the CPU oracle timed on a bounded sample of the same workload.
 
 By default reduce, AdamW and pack run as one fused launch per group
 (fsdp_step_shard, bit-identical to the three calls); --unfused runs them as
@@ -281,8 +281,8 @@ def measure_host_adamw(n=1 << 25, reps=3):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the collectives between "
-                          "ranks are out of scope, so --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU only: the collectives between "
+                          "ranks are not part of it, so --gpus must be 1"}))
         sys.exit(2)
     import torch
 
