@@ -98,6 +98,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown-steps", type=int, default=3,
                     help="extra untimed steps per kernel kind, with events around its launches")
+    ap.add_argument("--isolated", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time every kernel kind alone per group after flushing the "
+                         "last-level cache (per-kernel roofline protocol)")
     ap.add_argument("--no-next", action="store_true",
                     help="skip timing the reduce-scatter copy-in and fp32-contribution kernels")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -257,6 +260,47 @@ def measure_next(groups, n, rs_bf16, full_arena, stream, reps):
     return res
 
 
+def _pct(sorted_vals, q):
+    """Nearest-rank percentile of an ascending list."""
+    i = max(0, min(len(sorted_vals) - 1, -(-q * len(sorted_vals) // 100) - 1))
+    return round(sorted_vals[i], 4)
+
+
+def measure_isolated(groups, kinds, n, rank, hp, rs_arena, ag_arena, fused, stream):
+    """Each kernel kind launched alone per group, after a 1 GiB write that
+    flushes the 256 MB MALL, so no input can come from the last-level cache:
+    the per-kernel roofline protocol.  Sum of algorithmic bytes / sum of
+    event-timed launch durations over the groups."""
+    import torch
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=rs_arena[0].device)
+    res = {}
+    t = 10_000
+    for k in kinds:
+        tot_b = tot_ms = 0.0
+        for gi, g in enumerate(groups):
+            rs = rs_arena[gi & 1][:n * g.S]
+            ag_in = ag_arena[gi & 1][rank * g.S:(rank + 1) * g.S]
+            ag_out = ag_arena[gi & 1][:n * g.S]
+            launch = {"step": lambda: g.step(rs, ag_in, t, **hp, stream=stream),
+                      "reduce": lambda: g.reduce(rs, stream),
+                      "adamw": lambda: g.adamw(t, **hp, stream=stream),
+                      "pack": lambda: g.pack(ag_in, stream),
+                      "unpack": lambda: g.unpack(ag_out, stream)}[k]
+            flush.fill_(gi & 0xFF)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            launch()
+            b.record(stream)
+            b.synchronize()
+            tot_ms += a.elapsed_time(b)
+            tot_b += algorithmic_bytes(g.S, g.V, g.F, n, fused)[k]
+            t += 1
+        gbps = tot_b / (tot_ms * 1e-3) / 1e9
+        res[k] = {"isolated_GBps": round(gbps, 1), "isolated_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    del flush
+    return res
+
+
 def measure_host_adamw(n=1 << 25, reps=3):
     """CPU-offload AdamW on 32M host fp32 elements (28 B each per step): the
     rate of host memory, on every hardware thread the process may use."""
@@ -382,16 +426,19 @@ def main():
     torch.cuda.synchronize()
     print(f"bench: {args.warmup} warmup steps done", file=sys.stderr, flush=True)
 
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event at every step boundary: the distribution of step times
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    start, end = bounds[0], bounds[-1]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     start.record(stream)
     for k in range(args.steps):
         step(dominant, timed_events[k])
-    end.record(stream)
+        bounds[k + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_step = start.elapsed_time(end) / args.steps
+    step_ms = sorted(bounds[k].elapsed_time(bounds[k + 1]) for k in range(args.steps))
     print(f"bench: {args.steps} timed steps, {ms_step:.3f} ms/step", file=sys.stderr, flush=True)
     dom = [x for evs in timed_events for x in elapsed_sampled(evs)]
     dom_launches = len(dom)
@@ -415,6 +462,10 @@ def main():
                    "GBps": round(byts[k] / (per[k] * 1e-3) / 1e9, 1) if per[k] else None,
                    "hbm_frac": round(byts[k] / (per[k] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4) if per[k] else None}
                for k in kinds}
+    if args.isolated:
+        iso = measure_isolated(groups, kinds, n, rank, hp, rs_arena, ag_arena, fused, stream)
+        for k in kinds:
+            kernels[k].update(iso[k])
 
     eff_gbps = step_bytes / (ms_step * 1e-3) / 1e9
     # the method's own bytes per step, counted kernel by kernel as if unfused
@@ -444,6 +495,7 @@ def main():
         "hbm_frac": eff_gbps / HBM_PEAK_GBPS,
         "step_algorithmic_bytes": step_bytes,
         "wall_ms_per_step": wall * 1e3 / args.steps,
+        "step_ms": {"median": _pct(step_ms, 50), "p10": _pct(step_ms, 10), "p90": _pct(step_ms, 90)},
         "method_bytes_per_step": method_bytes,
         "method_effective_GBps": method_gbps,
         "method_hbm_frac": method_gbps / HBM_PEAK_GBPS,
