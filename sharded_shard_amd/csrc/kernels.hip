@@ -187,6 +187,29 @@ __device__ __forceinline__ void select8f(f32x4 a, f32x4 b, f32x4 c, uint32_t q, 
     (void)u9;
 }
 
+// Raw buffer load of 16 bytes at byte offset voff from a 16-byte aligned,
+// wave-uniform base.  The descriptor (base, nbytes) lives in SGPRs, so each
+// row of [N, S] costs one shared 32-bit lane offset instead of a 64-bit
+// address per row, which keeps VGPR use and occupancy where the row batch
+// needs them.  Reads at or past nbytes return zero instead of touching memory.
+// Descriptor word 3 is the gfx9-family raw-buffer format; aux bit 1 = nt.
+template <int NT>
+__device__ __forceinline__ u32x4 bload16(const char *al, uint32_t voff, uint32_t nbytes) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(al), 0, nbytes, 0x00020000);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, NT ? 2 : 0);
+}
+
+// The same register of the next lane of the wave (wave_shl:1 DPP); the last
+// lane gets 0.
+__device__ __forceinline__ uint32_t next_lane(uint32_t x) {
+    return __builtin_amdgcn_update_dpp(0u, x, 0x130, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ u32x4 next_lane16(u32x4 a) {
+    return u32x4{next_lane(a.x), next_lane(a.y), next_lane(a.z), next_lane(a.w)};
+}
+
 // 16 bytes starting at p; k = p's address & 15, wave-uniform.  kAl: k == 0.
 // Callers pick the variant once per run, so the loop holds no branch.
 template <int NT, bool kAl>
@@ -284,25 +307,42 @@ __device__ __forceinline__ void copy_run_bf16(uint16_t *__restrict__ dst,
     const uint16_t *s = src + head;
     const uint32_t k = lo32(s) & 15u;
     if (k == 0) {
-        const u32x4 *sv = reinterpret_cast<const u32x4 *>(s);
+        // raw buffer loads from one SGPR descriptor per run (measured faster
+        // than per-lane 64-bit addresses on MI355X)
+        const char *sb = reinterpret_cast<const char *>(s);
+        const uint32_t nb = static_cast<uint32_t>(nvec) << 4;
         int64_t v = tid;
         for (; v + kBlock < nvec; v += 2 * kBlock) {
-            const u32x4 x0 = ldp<LN>(sv + v);
-            const u32x4 x1 = ldp<LN>(sv + v + kBlock);
+            const u32x4 x0 = bload16<LN>(sb, static_cast<uint32_t>(v) << 4, nb);
+            const u32x4 x1 = bload16<LN>(sb, static_cast<uint32_t>(v + kBlock) << 4, nb);
             stp<SN>(dv + v, x0);
             stp<SN>(dv + v + kBlock, x1);
         }
-        if (v < nvec) stp<SN>(dv + v, ldp<LN>(sv + v));
+        if (v < nvec) stp<SN>(dv + v, bload16<LN>(sb, static_cast<uint32_t>(v) << 4, nb));
     } else {
-        const u32x4 *sv = reinterpret_cast<const u32x4 *>(reinterpret_cast<uintptr_t>(s) - k);
-        int64_t v = tid;
-        for (; v + kBlock < nvec; v += 2 * kBlock) {
-            const u32x4 a0 = ldp<LN>(sv + v), b0 = ldp<LN>(sv + v + 1);
-            const u32x4 a1 = ldp<LN>(sv + v + kBlock), b1 = ldp<LN>(sv + v + kBlock + 1);
-            stp<SN>(dv + v, funnel(a0, b0, k));
-            stp<SN>(dv + v + kBlock, funnel(a1, b1, k));
+        // Every aligned 16-byte source chunk is read once: a lane's second
+        // chunk is the next lane's first (DPP), and lane 63 of each wave
+        // loads its own with a load whose other lanes sit at the end of the
+        // buffer range (they read zero and touch no memory).  The range is
+        // exactly the chunks holding data, and whole waves iterate together.
+        const char *al = reinterpret_cast<const char *>(s) - k;
+        const uint32_t nb = (k + 2 * static_cast<uint32_t>(len - head) + 15u) & ~15u;
+        const uint32_t lane = tid & 63;
+        const bool last = lane == 63;
+        for (int64_t w0 = tid - lane; w0 < nvec; w0 += 2 * kBlock) {
+            const int64_t v0 = w0 + lane, v1 = v0 + kBlock;
+            const uint32_t o0 = static_cast<uint32_t>(v0) << 4, o1 = static_cast<uint32_t>(v1) << 4;
+            const u32x4 a0 = bload16<LN>(al, o0, nb), a1 = bload16<LN>(al, o1, nb);
+            const u32x4 h0 = bload16<LN>(al, last ? o0 + 16 : nb, nb);
+            const u32x4 h1 = bload16<LN>(al, last ? o1 + 16 : nb, nb);
+            u32x4 b0 = next_lane16(a0), b1 = next_lane16(a1);
+            if (last) {
+                b0 = h0;
+                b1 = h1;
+            }
+            if (v0 < nvec) stp<SN>(dv + v0, funnel(a0, b0, k));
+            if (v1 < nvec) stp<SN>(dv + v1, funnel(a1, b1, k));
         }
-        if (v < nvec) stp<SN>(dv + v, funnel(ldp<LN>(sv + v), ldp<LN>(sv + v + 1), k));
     }
     const int64_t done = head + (nvec << 3);
     if (tid < len - done) dst[done + tid] = src[done + tid];
@@ -454,29 +494,6 @@ __device__ __forceinline__ void init8(float (&acc)[8], u32x4 x) {
     acc[5] = bf16_hi(x.z);
     acc[6] = bf16_lo(x.w);
     acc[7] = bf16_hi(x.w);
-}
-
-// Raw buffer load of 16 bytes at byte offset voff from a 16-byte aligned,
-// wave-uniform base.  The descriptor (base, nbytes) lives in SGPRs, so each
-// row of [N, S] costs one shared 32-bit lane offset instead of a 64-bit
-// address per row, which keeps VGPR use and occupancy where the row batch
-// needs them.  Reads at or past nbytes return zero instead of touching memory.
-// Descriptor word 3 is the gfx9-family raw-buffer format; aux bit 1 = nt.
-template <int NT>
-__device__ __forceinline__ u32x4 bload16(const char *al, uint32_t voff, uint32_t nbytes) {
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(al), 0, nbytes, 0x00020000);
-    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, NT ? 2 : 0);
-}
-
-// The same register of the next lane of the wave (wave_shl:1 DPP); the last
-// lane gets 0.
-__device__ __forceinline__ uint32_t next_lane(uint32_t x) {
-    return __builtin_amdgcn_update_dpp(0u, x, 0x130, 0xF, 0xF, false);
-}
-
-__device__ __forceinline__ u32x4 next_lane16(u32x4 a) {
-    return u32x4{next_lane(a.x), next_lane(a.y), next_lane(a.z), next_lane(a.w)};
 }
 
 // Eight consecutive column sums of the N rows of [N, S] bf16 whose row 0
@@ -948,12 +965,26 @@ __device__ __forceinline__ void copy_run_u8(uint8_t *__restrict__ dst, const uin
     u32x4 *dv = reinterpret_cast<u32x4 *>(dst + head);
     const uint8_t *s = src + head;
     const uint32_t k = lo32(s) & 15u;
-    const u32x4 *sv = reinterpret_cast<const u32x4 *>(reinterpret_cast<uintptr_t>(s) - k);
+    // raw buffer loads over exactly the 16-byte chunks holding the run; a
+    // misaligned run reads every chunk once, a lane's second chunk coming
+    // from the next lane (lane 63 loads its own), as in copy_run_bf16
+    const char *al = reinterpret_cast<const char *>(s) - k;
+    const uint32_t nb = (k + static_cast<uint32_t>(len - head) + 15u) & ~15u;
     if (k == 0) {
-        for (int64_t v = tid; v < nvec; v += kBlock) stp<SN>(dv + v, ldp<LN>(sv + v));
-    } else {
         for (int64_t v = tid; v < nvec; v += kBlock)
-            stp<SN>(dv + v, funnel(ldp<LN>(sv + v), ldp<LN>(sv + v + 1), k));
+            stp<SN>(dv + v, bload16<LN>(al, static_cast<uint32_t>(v) << 4, nb));
+    } else {
+        const uint32_t lane = tid & 63;
+        const bool last = lane == 63;
+        for (int64_t w0 = tid - lane; w0 < nvec; w0 += kBlock) {
+            const int64_t v = w0 + lane;
+            const uint32_t o = static_cast<uint32_t>(v) << 4;
+            const u32x4 a = bload16<LN>(al, o, nb);
+            const u32x4 h = bload16<LN>(al, last ? o + 16 : nb, nb);
+            u32x4 b = next_lane16(a);
+            if (last) b = h;
+            if (v < nvec) stp<SN>(dv + v, funnel(a, b, k));
+        }
     }
     const int64_t done = head + (nvec << 4);
     if (tid < len - done) dst[done + tid] = src[done + tid];
