@@ -102,6 +102,10 @@
 #ifndef FSDP_STEP_WAVES
 #define FSDP_STEP_WAVES 6
 #endif
+// the fused step reads its N gradient rows with non-temporal loads
+#ifndef FSDP_STEP_ROW_NT
+#define FSDP_STEP_ROW_NT 1
+#endif
 // occupancy target of the fused step on misaligned rows (0: the default)
 #ifndef FSDP_STEP_GEN_WAVES
 #define FSDP_STEP_GEN_WAVES 0
@@ -1318,7 +1322,7 @@ __device__ __forceinline__ void step_run(const uint16_t *__restrict__ rs0, int64
         const uint32_t dbytes = static_cast<uint32_t>(2 * (valid - head));
         for (GroupWalk<kChunkAligned> w; w.more(ngrp); w.next()) {
             float acc[8];
-            sum_rows8<1, RB, kChunkAligned>(
+            sum_rows8<FSDP_STEP_ROW_NT, RB, kChunkAligned>(
                 rs0 + head, static_cast<uint32_t>(w.g) << 4, dbytes, S, N, k0, kS, acc);
             if (!w.own(ngrp)) continue;
             const int64_t e0 = head + (w.g << 3);
