@@ -10,10 +10,17 @@
  *   reduce    fsdp_reduce_shard      bf16 [N, S] grads   -> fp32 grad shards
  *   update    fsdp_adamw_shard       AdamW on fp32 master, m and v shards
  *   fused     fsdp_step_shard        reduce -> AdamW -> copy-in in one pass
+ *   executor  fsdp_step_groups       a whole step over many groups, one call
  *
- * plus a host-side shard-layout planner.  The collectives between these steps
- * (all-gather, reduce-scatter) are not part of the library: a caller runs them
- * on the buffers these calls read and write.
+ * and around them: the reduce-scatter copy-in (fsdp_pack_reduce_scatter),
+ * fp32 contributions (fsdp_reduce_shard_f32), the FP8 E4M3 all-gather
+ * (fsdp_pack_allgather_fp8, fsdp_unpack_allgather_fp8, fsdp_amax_shard),
+ * gradient accumulation without sync (fsdp_accumulate_grad,
+ * fsdp_pack_reduce_scatter_acc), AdamW on host shards (fsdp_adamw_host) and
+ * resharding saved shards to another world size (fsdp_reshard_*); plus a
+ * host-side shard-layout planner.  The collectives between these steps
+ * (all-gather, reduce-scatter) are not part of the library: a caller runs
+ * them on the buffers these calls read and write.
  *
  * Pages cited (by title and section):
  *   [ST] "Sharded Training: FSDP2, DTensor, Tensor and Pipeline Parallelism"
