@@ -192,7 +192,9 @@ void fsdp_plan_destroy(fsdp_plan *plan);
  *   full                               bf16 [rows, cols] unsharded params
  * A pointer may be NULL where its tensor has no elements.  Binding again
  * replaces the pointers (waiting for the stream first).  Allocates device
- * memory on the current device the first time.
+ * memory on the current device the first time.  A rejected call (bad
+ * argument) keeps the previous binding; a HIP failure during the upload
+ * leaves the plan unbound until a bind succeeds.
  * Errors: FSDP_E_INVAL (null pointer for a non-empty tensor), FSDP_E_ALIGN,
  *         FSDP_E_NOMEM, FSDP_E_HIP. */
 fsdp_status fsdp_bind(fsdp_plan *plan, float *const *master, float *const *grad,
@@ -446,6 +448,8 @@ fsdp_status fsdp_reshard_plan_run(const fsdp_reshard_plan *plan, int64_t i,
  * shards.  elem_bytes is 2 (bf16) or 4 (fp32); pointers must be aligned to
  * it and non-NULL wherever a run reads or writes.  Builds and uploads the
  * copy table on `stream` (allocating device memory); rebinding replaces it.
+ * A rejected call keeps the previous binding; a HIP or allocation failure
+ * while the table is replaced leaves the plan unbound.
  * Errors: FSDP_E_INVAL, FSDP_E_UNSUPPORTED, FSDP_E_ALIGN, FSDP_E_NOMEM,
  * FSDP_E_HIP. */
 fsdp_status fsdp_reshard_bind(fsdp_reshard_plan *plan, const void *const *src, void *const *dst,

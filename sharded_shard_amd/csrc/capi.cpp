@@ -51,6 +51,7 @@ struct fsdp_plan {
     std::vector<fsdp::DevEntry> host_entries;
     int32_t bound = 0;
     int device = -1;
+    bool tiles_uploaded = false;  // the tile tables below hold the plan's tiles
     char *dmem = nullptr;  // one device block: entries, then the tile tables
     fsdp::DevEntry *d_entries = nullptr;
     fsdp::PackTile *d_pack = nullptr;
@@ -115,8 +116,9 @@ fsdp_status need_roles(const fsdp_plan *p, int32_t roles, const char *call) {
     return FSDP_OK;
 }
 
-// Upload the entry table (and, the first time, allocate the device block and
-// upload every tile table) on `st`, then record the newly bound roles.
+// Upload the entry table (and, until one upload has succeeded, the tile
+// tables; the device block is allocated the first time) on `st`, then record
+// the newly bound roles.
 fsdp_status commit_entries(fsdp_plan *p, std::vector<fsdp::DevEntry> ents, int32_t roles,
                            hipStream_t st, const char *call) {
     const std::string c(call);
@@ -163,7 +165,12 @@ fsdp_status commit_entries(fsdp_plan *p, std::vector<fsdp::DevEntry> ents, int32
     // Kernels of this plan still queued on the stream may read the tables.
     e = hipStreamSynchronize(st);
     if (e != hipSuccess) return hip_fail(e, (c + ": hipStreamSynchronize").c_str());
-    for (int k = 0; k < (first ? 7 : 1); ++k) {
+    // From here the device tables change: a failure leaves the plan unbound
+    // (hot calls then fail with FSDP_E_STATE) rather than half-updated.
+    const int32_t prev = p->bound;
+    p->bound = 0;
+    const int n_tabs = p->tiles_uploaded ? 1 : 7;
+    for (int k = 0; k < n_tabs; ++k) {
         if (tabs[k].bytes == 0) continue;
         const void *src = k == 0 ? static_cast<const void *>(ents.data()) : tabs[k].src;
         e = hipMemcpyAsync(*tabs[k].dst, src, tabs[k].bytes, hipMemcpyHostToDevice, st);
@@ -171,8 +178,9 @@ fsdp_status commit_entries(fsdp_plan *p, std::vector<fsdp::DevEntry> ents, int32
     }
     e = hipStreamSynchronize(st);
     if (e != hipSuccess) return hip_fail(e, (c + ": upload").c_str());
+    p->tiles_uploaded = true;
     p->host_entries = std::move(ents);
-    p->bound = first ? roles : (p->bound | roles);
+    p->bound = prev | roles;
     return FSDP_OK;
 }
 

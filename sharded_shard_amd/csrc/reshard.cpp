@@ -142,6 +142,11 @@ fsdp_status fsdp_reshard_bind(fsdp_reshard_plan *p, const void *const *src, void
     e = hipStreamSynchronize(st);   // queued executions may still read the old table
     if (e != hipSuccess) return set_error(FSDP_E_HIP, std::string("fsdp_reshard_bind: ") + hipGetErrorString(e));
     const size_t bytes = tiles.size() * sizeof(fsdp::CopyTile);
+    // From here the device table is being replaced: until the upload below
+    // succeeds the plan is unbound, so a failed bind cannot leave a stale or
+    // freed table behind for fsdp_reshard_execute.
+    p->bound = false;
+    p->tiles.clear();
     if (p->d_tiles != nullptr && (bytes > p->d_cap || dev != p->device)) {
         (void)hipFree(p->d_tiles);
         p->d_tiles = nullptr;

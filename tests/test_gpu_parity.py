@@ -587,6 +587,41 @@ def test_step_groups_equals_per_group_calls(unfused):
         g.close()
 
 
+def test_rejected_bind_keeps_the_previous_binding():
+    """A bind that fails argument checks changes nothing: the plan stays bound
+    to its previous tensors and the hot calls still produce the oracle's
+    results."""
+    shapes, n, r = [(33, 5), (17,)], 4, 1
+    g = ShardedGroup(shapes, n, r)
+    _fill_masters(g, ("rebind",))
+    plan = O.plan(shapes, n, r)
+    bad = [x + 2 if x else 0 for x in g._ptrs(g.master_flat)]      # not 4-byte aligned
+    with pytest.raises(capi.FsdpError) as ei:
+        capi.fsdp_bind(g.plan, master=bad)
+    assert ei.value.status == capi.FSDP_E_ALIGN
+    ag = torch.zeros(plan.S, dtype=torch.int16, device=DEV)
+    g.pack(ag)
+    torch.cuda.synchronize()
+    want = O.pack(plan, [f32(g.shard_view(g.master_flat, i)) for i in range(len(shapes))])
+    assert np.array_equal(u16(ag), want)
+    # the reshard plan: a rejected rebind keeps the previous copy table
+    rows, cols = [10, 7], [3, 1]
+    rp = capi.fsdp_reshard_plan_create(rows, cols, 2, 1, 0)
+    src = torch.arange(37, dtype=torch.int32, device=DEV)
+    dst = torch.full((37,), -1, dtype=torch.int32, device=DEV)
+    s_ptrs = [src.data_ptr(), src[15:].data_ptr(), src[30:].data_ptr(), src[34:].data_ptr()]
+    d_ptrs = [dst.data_ptr(), dst[30:].data_ptr()]
+    capi.fsdp_reshard_bind(rp, s_ptrs, d_ptrs, 4, None)
+    with pytest.raises(capi.FsdpError) as ei:
+        capi.fsdp_reshard_bind(rp, s_ptrs, d_ptrs, 3, None)
+    assert ei.value.status == capi.FSDP_E_UNSUPPORTED
+    capi.fsdp_reshard_execute(rp)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    capi.fsdp_reshard_plan_destroy(rp)
+    g.close()
+
+
 def test_step_groups_checks_every_group_before_launching():
     n, r = 4, 0
     g1 = ShardedGroup([(64, 8)], n, r)
