@@ -407,8 +407,9 @@ fsdp_status fsdp_step_groups(fsdp_plan *const *plans, int32_t n_groups,
  * optimizer step on the CPU).  Same update, element for element, as
  * fsdp_adamw_shard (bit-identical results); n elements of p, g, m, v (host
  * pointers); n_threads <= 0 uses every hardware thread.  Synchronous; needs
- * no GPU.  Errors: FSDP_E_INVAL (null arrays, n < 0, null hparams,
- * step < 1), FSDP_E_NOMEM (threads). */
+ * no GPU; a range whose thread cannot be started runs on the calling
+ * thread.  Errors: FSDP_E_INVAL (null arrays, n < 0, null hparams,
+ * step < 1). */
 fsdp_status fsdp_adamw_host(float *p, const float *g, float *m, float *v, int64_t n,
                             const fsdp_adamw_hparams_t *hp, int64_t step, int32_t n_threads);
 

@@ -59,17 +59,26 @@ extern "C" fsdp_status fsdp_adamw_host(float *p, const float *g, float *m, float
         adamw_range(p, g, m, v, 0, n, c);
         return FSDP_OK;
     }
+    // A range whose thread cannot be started runs on this thread instead;
+    // every started thread is joined before returning.
+    const int64_t per = (n + t - 1) / t;
+    std::vector<std::thread> pool;
+    int64_t k = 0;
     try {
-        std::vector<std::thread> pool;
-        const int64_t per = (n + t - 1) / t;
-        for (int64_t k = 0; k < t; ++k) {
+        pool.reserve(static_cast<size_t>(t));
+        for (; k < t; ++k) {
             const int64_t b = k * per, e = std::min(n, b + per);
             if (b >= e) break;
             pool.emplace_back(adamw_range, p, g, m, v, b, e, c);
         }
-        for (std::thread &th : pool) th.join();
     } catch (...) {
-        return fsdp::set_error(FSDP_E_NOMEM, "fsdp_adamw_host: could not start threads");
+        // fall through: ranges k.. are done below
     }
+    for (; k < t; ++k) {
+        const int64_t b = k * per, e = std::min(n, b + per);
+        if (b >= e) break;
+        adamw_range(p, g, m, v, b, e, c);
+    }
+    for (std::thread &th : pool) th.join();
     return FSDP_OK;
 }
