@@ -72,8 +72,12 @@ class ShardedGroup:
         self.master_flat = self.grad_flat = self.m_flat = self.v_flat = None
         self.full_flat = full_arena
         if bind:
-            self.allocate()
-            self.bind(stream)
+            try:
+                self.allocate()
+                self.bind(stream)
+            except Exception:
+                self.close()
+                raise
 
     # ---- memory ---------------------------------------------------------------
 
@@ -199,6 +203,12 @@ class ShardedGroup:
         if self.plan is not None:
             capi.fsdp_plan_destroy(self.plan)
             self.plan = None
+
+    def __enter__(self) -> "ShardedGroup":
+        return self
+
+    def __exit__(self, *exc) -> None:
+        self.close()
 
     def __del__(self):
         try:
