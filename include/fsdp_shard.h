@@ -365,8 +365,9 @@ enum {
  *   ag_in  [S] bf16 copy-in output (may be row `rank` of the all-gather
  *          buffer); must not overlap rs_in
  * Needs FSDP_ROLE_MASTER | EXP_AVG | EXP_AVG_SQ, plus GRAD with the flag.
- * Errors: FSDP_E_INVAL (null buffer with S > 0, null hparams, step < 1,
- *         unknown flag), FSDP_E_ALIGN, FSDP_E_STATE, FSDP_E_HIP. */
+ * Errors: FSDP_E_INVAL (null buffer with S > 0, ag_in overlapping rs_in,
+ *         null hparams, step < 1, unknown flag), FSDP_E_ALIGN, FSDP_E_STATE,
+ *         FSDP_E_HIP. */
 fsdp_status fsdp_step_shard(const fsdp_plan *plan, const uint16_t *rs_in,
                             uint16_t *ag_in, const fsdp_adamw_hparams_t *hp,
                             int64_t step, uint32_t flags, void *stream);

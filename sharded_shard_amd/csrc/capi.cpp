@@ -451,7 +451,15 @@ fsdp_status check_step(const fsdp_plan *p, const uint16_t *rs_in, const uint16_t
     fsdp_status s = need_roles(p, roles, call);
     if (s != FSDP_OK) return s;
     if ((s = check_buf(p, rs_in, call, "rs_in")) != FSDP_OK) return s;
-    return check_buf(p, ag_in, call, "ag_in");
+    if ((s = check_buf(p, ag_in, call, "ag_in")) != FSDP_OK) return s;
+    // ag_in is written while rs_in is read: the two must not share bytes
+    const uintptr_t r0 = reinterpret_cast<uintptr_t>(rs_in);
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(ag_in);
+    const uintptr_t rb = static_cast<uintptr_t>(p->L.world) * static_cast<uintptr_t>(p->L.S) * 2;
+    const uintptr_t ab = static_cast<uintptr_t>(p->L.S) * 2;
+    if (p->L.S > 0 && a0 < r0 + rb && r0 < a0 + ab)
+        return fail(FSDP_E_INVAL, std::string(call) + ": ag_in overlaps rs_in");
+    return FSDP_OK;
 }
 
 hipError_t do_pack(const fsdp_plan *p, uint16_t *ag_in, hipStream_t st) {

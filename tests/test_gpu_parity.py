@@ -530,6 +530,14 @@ def test_fused_step_rejects_unbound_and_bad_flags():
     with pytest.raises(capi.FsdpError) as ei:
         capi.fsdp_step_shard(g.plan, rs, ag, 3e-4, 0.9, 0.999, 1e-8, 0.01, 0)
     assert ei.value.status == capi.FSDP_E_INVAL
+    # ag_in may not share bytes with rs_in (it is written while rs_in is read)
+    both = torch.zeros(3 * g.S, dtype=torch.int16, device=DEV)
+    for a in (both[g.S - 1:2 * g.S - 1], both[2 * g.S - 1:3 * g.S - 1], both[:g.S]):
+        with pytest.raises(capi.FsdpError) as ei:
+            capi.fsdp_step_shard(g.plan, both[:2 * g.S], a, 3e-4, 0.9, 0.999, 1e-8, 0.01, 1)
+        assert ei.value.status == capi.FSDP_E_INVAL
+    capi.fsdp_step_shard(g.plan, both[:2 * g.S], both[2 * g.S:], 3e-4, 0.9, 0.999, 1e-8, 0.01, 1)
+    torch.cuda.synchronize()
     g.close()
 
 
