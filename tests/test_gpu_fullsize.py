@@ -190,3 +190,83 @@ def test_reduce_all_equal_every_element(cfg_index):
         got = g.shard_view(g.grad_flat, i)
         assert torch.equal(got.view(torch.int32), want.view(torch.int32)), i
     g.close()
+
+
+@pytest.mark.parametrize("cfg_index", [2, 4])
+def test_next_rows_full_block_group(cfg_index):
+    """The reduce-scatter copy-ins (bf16 and fp32), the fp32 reduction and
+    gradient accumulation on a full block group, in the bench's launch
+    configuration.  Every element against constructions from torch's own
+    ops (chunk, zero padding, exact widening, fp32 add); the fp32 reduction
+    against the oracle on sampled columns and, over every element, against
+    the bf16 reduction of the same values."""
+    cfg, gs = _groups(cfg_index)
+    gi, grp = gs[0]
+    shapes = [p.shape for p in grp.params]
+    n, r = cfg.world, cfg.timing_rank
+    print(f"[fullsize] next rows cfg={cfg_index} group={gi} n={n}", flush=True)
+    g = ShardedGroup(shapes, n, r)
+    S = g.S
+    g.bind_full_grad()
+    g.bind_grad_acc()
+    micro = []
+    for k in range(2):
+        arena = torch.empty(g.full_space, dtype=torch.int16, device=DEV)
+        synth.fill_normal_bf16_bits_(arena, 1e-3, ("nx-g", cfg_index, k))
+        micro.append(arena)
+    # accumulation: reset with microbatch 0, then add microbatch 1
+    g.full_grad_flat.copy_(micro[0])
+    g.accumulate_grad(True)
+    g.full_grad_flat.copy_(micro[1])
+    g.accumulate_grad(False)
+    rs_b = torch.empty(n * S, dtype=torch.int16, device=DEV)
+    rs_f = torch.empty(n * S, dtype=torch.float32, device=DEV)
+    rs_a = torch.empty(n * S, dtype=torch.float32, device=DEV)
+    g.pack_reduce_scatter(rs_b, capi.FSDP_DTYPE_BF16)
+    g.pack_reduce_scatter(rs_f, capi.FSDP_DTYPE_F32)
+    g.pack_reduce_scatter_acc(rs_a)
+    torch.cuda.synchronize()
+    rb, rf, ra = rs_b.view(n, S), rs_f.view(n, S), rs_a.view(n, S)
+    for i, e in enumerate(g.entries):
+        numel = e.rows * e.cols
+        o = g.full_offsets[i]
+        g0 = micro[0][o:o + numel].view(torch.bfloat16).float()
+        g1 = micro[1][o:o + numel].view(torch.bfloat16).float()
+        acc_want = g0 + g1                                  # one fp32 add per element
+        acc = g.grad_acc_flat[o:o + numel]
+        assert torch.equal(acc.view(torch.int32), acc_want.view(torch.int32)), ("acc", i)
+        grad1 = micro[1][o:o + numel].view(e.rows, e.cols)
+        acc2 = acc_want.view(e.rows, e.cols)
+        for j in range(n):
+            b, lr = O.rows_of_rank(e.rows, n, j)
+            k = lr * e.cols
+            sl = slice(e.shard_offset, e.shard_offset + e.seg_numel)
+            want_b = torch.zeros(e.seg_numel, dtype=torch.int16, device=DEV)
+            want_b[:k] = grad1[b:b + lr].reshape(-1)
+            assert torch.equal(rb[j, sl], want_b), ("rs bf16", i, j)
+            want_f = want_b.view(torch.bfloat16).float()
+            want_f[k:] = 0.0
+            assert torch.equal(rf[j, sl].view(torch.int32), want_f.view(torch.int32)), ("rs f32", i, j)
+            want_a = torch.zeros(e.seg_numel, dtype=torch.float32, device=DEV)
+            want_a[:k] = acc2[b:b + lr].reshape(-1)
+            assert torch.equal(ra[j, sl].view(torch.int32), want_a.view(torch.int32)), ("rs acc", i, j)
+    # fp32 reduction of the widened copy-in == bf16 reduction, every element
+    g.reduce(rs_b)
+    torch.cuda.synchronize()
+    ref = g.grad_flat.clone()
+    g.grad_flat.zero_()
+    g.reduce_f32(rs_f)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.view(torch.int32), g.grad_flat.view(torch.int32))
+    # the fp32 reduction of the accumulators, sampled against the oracle
+    g.reduce_f32(rs_a)
+    torch.cuda.synchronize()
+    for i, e in enumerate(g.entries):
+        if not e.valid_numel:
+            continue
+        ix = torch.from_numpy(_sample_idx(e.valid_numel, ("nx-idx", cfg_index, i))).to(DEV)
+        cols = ra[:, e.shard_offset + ix].cpu().numpy()
+        want = O.reduce_f32(_col_plan(n, cols.shape[1]), cols)[0]
+        got = g.shard_view(g.grad_flat, i)[ix].cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), ("reduce f32", i)
+    g.close()
