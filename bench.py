@@ -51,8 +51,10 @@ def algorithmic_bytes(S, V, F, N, fused):
             "unpack": 4 * F}
 
 
-# rocprofv3 kernel names; the fused step has a variant for 16-byte aligned rows
-KERNEL_SYMBOLS = {"step": ("step_kernel_aligned", "step_kernel"), "reduce": ("reduce_kernel",),
+# rocprofv3 kernel names; the fused step has variants for 16-byte aligned rows
+# (the wide one from 16 ranks)
+KERNEL_SYMBOLS = {"step": ("step_kernel_wide", "step_kernel_aligned", "step_kernel"),
+                  "reduce": ("reduce_kernel",),
                   "adamw": ("adamw_kernel",), "pack": ("pack_kernel",),
                   "unpack": ("unpack_kernel",)}
 

@@ -78,6 +78,10 @@ CASES = [
     # odd pieces over several row batches (12 = 8 + 4, 64 = 8 x 8)
     ("odd-n12", [(1000, 37), (4097,), (129, 3), (25, 8)], 12),
     ("odd-n64", [(700, 9), (129,), (64, 33)], 64),
+    # every piece a multiple of 8 elements: 16-byte aligned rows, the fused
+    # step's wide kernel from 16 ranks (several tiles, empty chunks)
+    ("wide-n16", [(2048, 160), (4096,), (96, 40), (17, 8)], 16),
+    ("wide-n64", [(5000, 24), (64, 72), (129, 8), (1, 8)], 64),
 ]
 
 

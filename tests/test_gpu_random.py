@@ -1,9 +1,10 @@
 """GPU parity on seeded random parameter groups: every kernel against the oracle.
 
 Each case draws a ragged group (1-6 parameters, 0-400 rows, 1-70 columns, some
-1-D), a world size of 1-13, a rank, the alignment option and element offsets
-of the [N, S] buffers, so layouts the fixed cases do not name (misaligned rows
-at every offset, partial row batches, empty chunks, tiny runs) are covered.
+1-D), a world size of 1-13 (16-64 for every fourth case), a rank, the
+alignment option and element offsets of the [N, S] buffers, so layouts the
+fixed cases do not name (misaligned rows at every offset, partial row
+batches, empty chunks, tiny runs) are covered.
 Bit-exact bars as in the fixed-case tests.
 """
 import numpy as np
@@ -42,10 +43,12 @@ def _case(seed):
             shapes.append((rows, int(rng.integers(1, 71))))
     if seed % 5 == 4:  # an empty parameter somewhere in the group
         shapes.insert(int(rng.integers(0, len(shapes) + 1)), (0, int(rng.integers(1, 71))))
-    n =int(rng.integers(1, 14))
+    n = int(rng.integers(1, 14)) if seed % 4 else int(rng.choice([16, 17, 24, 32, 64]))
     r = int(rng.integers(0, n))
     align = int(rng.choice([1, 8]))
     offs = [int(x) for x in rng.integers(0, 8, size=4)]
+    if seed % 8 == 0:  # 16-byte aligned rows: the fused step's wide kernel from 16 ranks
+        align, offs[0] = 8, 0
     return shapes, n, r, align, offs
 
 
