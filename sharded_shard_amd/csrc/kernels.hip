@@ -48,17 +48,24 @@
 #ifndef FSDP_REDUCE_POL
 #define FSDP_REDUCE_POL 1
 #endif
-// Lanes of these kernels store two 16-byte halves of a 32-byte span per
+// Lanes of the fp32 reduction store two 16-byte halves of a 32-byte span per
 // group: non-temporal stores of that pattern cost extra HBM writes (measured
-// 1.1-1.7x the algorithmic bytes), plain stores do not.
+// 1.1-1.7x the algorithmic bytes), plain stores do not.  The fp32 copy-ins
+// and the accumulation move four elements per lane on their aligned paths,
+// so every store instruction of a wave writes 1 KB contiguously, and take
+// non-temporal loads and stores there (their misaligned paths keep plain
+// stores).
 #ifndef FSDP_REDUCE_F32_POL
 #define FSDP_REDUCE_F32_POL 0
 #endif
 #ifndef FSDP_RSPACK_F32_POL
-#define FSDP_RSPACK_F32_POL 1
+#define FSDP_RSPACK_F32_POL 3
 #endif
 #ifndef FSDP_RSPACK_ACC_POL
-#define FSDP_RSPACK_ACC_POL 0
+#define FSDP_RSPACK_ACC_POL 3
+#endif
+#ifndef FSDP_ACC_POL
+#define FSDP_ACC_POL 3
 #endif
 #ifndef FSDP_ADAMW_POL
 #define FSDP_ADAMW_POL 0
@@ -108,6 +115,14 @@
 #ifndef FSDP_STEP_WIDE_MIN_N
 #define FSDP_STEP_WIDE_MIN_N 16
 #endif
+// The same for the plain reduction of bf16 contributions (fp32
+// contributions measured slower read this way: 5.65 vs 5.87 TB/s at N = 64).
+#ifndef FSDP_REDUCE_WIDE
+#define FSDP_REDUCE_WIDE 4
+#endif
+#ifndef FSDP_REDUCE_WIDE_MIN_N
+#define FSDP_REDUCE_WIDE_MIN_N 16
+#endif
 #ifndef FSDP_STEP_WAVES
 #define FSDP_STEP_WAVES 6
 #endif
@@ -142,6 +157,7 @@ namespace fsdp {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 256;
@@ -613,7 +629,7 @@ struct GroupWalk {
     __device__ void next() { g += step; }
 };
 
-template <int POL, bool kChunkAligned>
+template <int POL, int C, bool kChunkAligned>
 __device__ __forceinline__ void reduce_run(float *__restrict__ dst, const uint16_t *__restrict__ src0,
                                            int64_t len, int64_t S, int32_t N, float fN) {
     constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
@@ -633,21 +649,27 @@ __device__ __forceinline__ void reduce_run(float *__restrict__ dst, const uint16
     const int64_t ngrp = (len - head) >> 3;
     const uint32_t dbytes = static_cast<uint32_t>(2 * (len - head));
     f32x4 *dv = reinterpret_cast<f32x4 *>(dst + head);
-    for (GroupWalk<kChunkAligned> w; w.more(ngrp); w.next()) {
-        float acc[8];
-        sum_rows8<LN, FSDP_REDUCE_ROW_BATCH, kChunkAligned>(
-            s0, static_cast<uint32_t>(w.g) << 4, dbytes, S, N, k0, kS, acc);
-        if (w.own(ngrp)) {
-            const int64_t g = w.g;
-            stp<SN>(dv + 2 * g, f32x4{acc[0] / fN, acc[1] / fN, acc[2] / fN, acc[3] / fN});
-            stp<SN>(dv + 2 * g + 1, f32x4{acc[4] / fN, acc[5] / fN, acc[6] / fN, acc[7] / fN});
+    for (GroupWalk<kChunkAligned, C> w; w.more(ngrp); w.next()) {
+        float acc[C][8];
+        if constexpr (C == 1)
+            sum_rows8<LN, FSDP_REDUCE_ROW_BATCH, kChunkAligned>(
+                s0, static_cast<uint32_t>(w.g) << 4, dbytes, S, N, k0, kS, acc[0]);
+        else
+            sum_rows_wide<LN, C>(s0, static_cast<uint32_t>(w.g) << 4, dbytes, S, N, acc);
+#pragma unroll
+        for (int q = 0; q < C; ++q) {
+            if (!w.own(ngrp, q)) continue;
+            const int64_t g = w.at(q);
+            const float *a = acc[q];
+            stp<SN>(dv + 2 * g, f32x4{a[0] / fN, a[1] / fN, a[2] / fN, a[3] / fN});
+            stp<SN>(dv + 2 * g + 1, f32x4{a[4] / fN, a[5] / fN, a[6] / fN, a[7] / fN});
         }
     }
     const int64_t done = head + (ngrp << 3);
     if (tid < len - done) dst[done + tid] = sum_rows_scalar(src0, S, N, done + tid) / fN;
 }
 
-template <int POL, bool kChunkAligned>
+template <int POL, int C, bool kChunkAligned>
 __global__ __launch_bounds__(kBlock) void reduce_kernel(
     const ReduceTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
     const DevEntry *__restrict__ ents, const uint16_t *__restrict__ rs_in,
@@ -660,8 +682,8 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(
         const ReduceTile tl = tiles[t];
         if (b >= tl.len) continue;
         const int64_t len = tl.len - b < L ? tl.len - b : L;
-        reduce_run<POL, kChunkAligned>(ents[tl.entry].grad + tl.dst + b, rs_in + tl.src + b, len,
-                                       S, N, fN);
+        reduce_run<POL, C, kChunkAligned>(ents[tl.entry].grad + tl.dst + b, rs_in + tl.src + b,
+                                          len, S, N, fN);
     }
 }
 
@@ -820,6 +842,10 @@ __device__ __forceinline__ void widen_vec(f32x4 *__restrict__ dv, const uint16_t
 }
 
 // dst[i] = fp32(src[i]) for i < valid (exact widening), zeros up to len.
+// dst is aligned to 16 bytes after a short head.  An 8-byte aligned source
+// moves four elements per lane (8-byte loads, 16-byte stores: each wave
+// instruction is contiguous); otherwise eight per lane from funnel-shifted
+// 16-byte chunks, with plain stores (a lane writes two halves of 32 bytes).
 template <int POL>
 __device__ __forceinline__ void widen_run(float *__restrict__ dst, const uint16_t *__restrict__ src,
                                           int64_t len, int64_t valid) {
@@ -828,13 +854,23 @@ __device__ __forceinline__ void widen_run(float *__restrict__ dst, const uint16_
     int64_t head = ((16u - (lo32(dst) & 15u)) & 15u) >> 2;
     if (head > valid) head = valid;
     if (tid < head) dst[tid] = widen(src[tid]);
-    const int64_t ngrp = (valid - head) >> 3;
     const uint16_t *s = src + head;
     const uint32_t k = lo32(s) & 15u;
     f32x4 *dv = reinterpret_cast<f32x4 *>(dst + head);
-    if (k == 0) widen_vec<LN, SN, true>(dv, s, ngrp, 0u);
-    else widen_vec<LN, SN, false>(dv, s, ngrp, k);
-    const int64_t done = head + (ngrp << 3);
+    int64_t done;
+    if ((k & 7u) == 0) {
+        const int64_t nq = (valid - head) >> 2;
+        const u32x2 *sv = reinterpret_cast<const u32x2 *>(s);
+        for (int64_t q = tid; q < nq; q += kBlock) {
+            const u32x2 w = ldp<LN>(sv + q);
+            stp<SN>(dv + q, f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)});
+        }
+        done = head + (nq << 2);
+    } else {
+        const int64_t ngrp = (valid - head) >> 3;
+        widen_vec<LN, 0, false>(dv, s, ngrp, k);
+        done = head + (ngrp << 3);
+    }
     if (tid < valid - done) dst[done + tid] = widen(src[done + tid]);
     zero_f32<SN>(dst, valid, len);
 }
@@ -1103,7 +1139,6 @@ __device__ __forceinline__ void accumulate_run(float *__restrict__ acc, const ui
     if (!vec) return;
     const int64_t nvec = (len - head) >> 2;
     f32x4 *av = reinterpret_cast<f32x4 *>(acc + head);
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     const u32x2 *gv = reinterpret_cast<const u32x2 *>(g + head);
     for (int64_t v = tid; v < nvec; v += kBlock) {
         const u32x2 w = ldp<LN>(gv + v);
@@ -1150,8 +1185,10 @@ __device__ __forceinline__ void copy_f32_vec(f32x4 *__restrict__ dv, const float
 }
 
 // Reduce-scatter copy-in from the fp32 accumulators: copy fp32 runs, zeros
-// in padding.  dst is aligned to 16 bytes after a short head; the source is
-// read as aligned vectors and dword-selected.
+// in padding.  dst is aligned to 16 bytes after a short head.  An aligned
+// source is copied one 16-byte vector per lane (each wave instruction
+// contiguous); otherwise eight elements per lane from aligned vectors,
+// dword-selected, with plain stores (a lane writes two halves of 32 bytes).
 template <int POL>
 __device__ __forceinline__ void copy_f32_run(float *__restrict__ dst, const float *__restrict__ src,
                                              int64_t len, int64_t valid) {
@@ -1160,13 +1197,20 @@ __device__ __forceinline__ void copy_f32_run(float *__restrict__ dst, const floa
     int64_t head = ((16u - (lo32(dst) & 15u)) & 15u) >> 2;
     if (head > valid) head = valid;
     if (tid < head) dst[tid] = src[tid];
-    const int64_t ngrp = (valid - head) >> 3;
     const float *s = src + head;
     const uint32_t q = (lo32(s) >> 2) & 3u;
     f32x4 *dv = reinterpret_cast<f32x4 *>(dst + head);
-    if (q == 0) copy_f32_vec<LN, SN, true>(dv, s, ngrp, 0u);
-    else copy_f32_vec<LN, SN, false>(dv, s, ngrp, q);
-    const int64_t done = head + (ngrp << 3);
+    int64_t done;
+    if (q == 0) {
+        const int64_t nq = (valid - head) >> 2;
+        const f32x4 *sv = reinterpret_cast<const f32x4 *>(s);
+        for (int64_t v = tid; v < nq; v += kBlock) stp<SN>(dv + v, ldp<LN>(sv + v));
+        done = head + (nq << 2);
+    } else {
+        const int64_t ngrp = (valid - head) >> 3;
+        copy_f32_vec<LN, 0, false>(dv, s, ngrp, q);
+        done = head + (ngrp << 3);
+    }
     if (tid < valid - done) dst[done + tid] = src[done + tid];
     zero_f32<SN>(dst, valid, len);
 }
@@ -1532,14 +1576,23 @@ hipError_t launch_reduce(const ReduceTile *tiles, int64_t n, const DevEntry *ent
                          hipStream_t st) {
     if (n == 0) return hipSuccess;
     const float fN = static_cast<float>(N);
+    if (chunk_aligned && N >= FSDP_REDUCE_WIDE_MIN_N) {
+        // one wave per block, each block one sub-range of 64 * 8 * FSDP_REDUCE_WIDE elements
+        constexpr int64_t wsub = 64 * 8 * FSDP_REDUCE_WIDE;
+        static_assert(kTileReduce % wsub == 0, "wide sub-range must divide the tile");
+        const int32_t wsp = static_cast<int32_t>(kTileReduce / wsub);
+        reduce_kernel<FSDP_REDUCE_POL, FSDP_REDUCE_WIDE, true>
+            <<<grid_for(n, wsp), 64, 0, st>>>(tiles, n, wsp, wsub, ents, rs_in, S, N, fN);
+        return hipGetLastError();
+    }
     const int32_t sp = split_rows(kTileReduce, N, 0);
     const unsigned grid = grid_for(n, sp);
     const unsigned thr = row_threads(kTileReduce / sp);
     if (chunk_aligned)
-        reduce_kernel<FSDP_REDUCE_POL, true>
+        reduce_kernel<FSDP_REDUCE_POL, 1, true>
             <<<grid, thr, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
     else
-        reduce_kernel<FSDP_REDUCE_POL, false>
+        reduce_kernel<FSDP_REDUCE_POL, 1, false>
             <<<grid, thr, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
     return hipGetLastError();
 }
@@ -1598,9 +1651,9 @@ hipError_t launch_accumulate(const EwTile *tiles, int64_t n, const DevEntry *ent
     const int32_t sp = split_for(kTileAdamw, FSDP_ADAMW_SUB);
     const unsigned grid = grid_for(n, sp);
     if (reset)
-        accumulate_kernel<FSDP_ADAMW_POL, true><<<grid, kBlock, 0, st>>>(tiles, n, sp, kTileAdamw / sp, ents);
+        accumulate_kernel<FSDP_ACC_POL, true><<<grid, kBlock, 0, st>>>(tiles, n, sp, kTileAdamw / sp, ents);
     else
-        accumulate_kernel<FSDP_ADAMW_POL, false><<<grid, kBlock, 0, st>>>(tiles, n, sp, kTileAdamw / sp, ents);
+        accumulate_kernel<FSDP_ACC_POL, false><<<grid, kBlock, 0, st>>>(tiles, n, sp, kTileAdamw / sp, ents);
     return hipGetLastError();
 }
 

@@ -47,8 +47,8 @@ def _case(seed):
     r = int(rng.integers(0, n))
     align = int(rng.choice([1, 8]))
     offs = [int(x) for x in rng.integers(0, 8, size=4)]
-    if seed % 8 == 0:  # 16-byte aligned rows: the fused step's wide kernel from 16 ranks
-        align, offs[0] = 8, 0
+    if seed % 8 == 0:  # 16-byte aligned rows: the wide row kernels from 16 ranks
+        align, offs[0], offs[2] = 8, 0, 0
     return shapes, n, r, align, offs
 
 
