@@ -103,6 +103,10 @@
 #ifndef FSDP_STEP_ROW_BATCH_WIDE
 #define FSDP_STEP_ROW_BATCH_WIDE 4
 #endif
+// rows in flight of the fused step on misaligned rows up to 8 ranks
+#ifndef FSDP_STEP_GEN_ROW_BATCH
+#define FSDP_STEP_GEN_ROW_BATCH 2
+#endif
 #ifndef FSDP_REDUCE_ROW_BATCH
 #define FSDP_REDUCE_ROW_BATCH 2
 #endif
@@ -1543,6 +1547,20 @@ inline unsigned row_threads(int64_t sub) {
 #endif
 }
 
+// Misaligned rows: a wave covers 63 groups (504 elements), so sub-ranges are
+// cut in whole such waves; a power-of-two sub-range would leave one wave a
+// second pass through all N rows for a handful of groups.
+struct RowSplit {
+    int32_t split;
+    int64_t sub;
+};
+inline RowSplit row_split(int64_t tile, int32_t sp, bool aligned) {
+    const int64_t sub = tile / sp;
+    if (aligned) return RowSplit{sp, sub};
+    const int64_t msub = sub / 512 * 504;
+    return RowSplit{static_cast<int32_t>((tile + msub - 1) / msub), msub};
+}
+
 AdamwScalars to_scalars(const float s[8]) {
     return AdamwScalars{s[0], s[1], s[2], s[3], s[4], s[5], s[6], s[7]};
 }
@@ -1585,15 +1603,15 @@ hipError_t launch_reduce(const ReduceTile *tiles, int64_t n, const DevEntry *ent
             <<<grid_for(n, wsp), 64, 0, st>>>(tiles, n, wsp, wsub, ents, rs_in, S, N, fN);
         return hipGetLastError();
     }
-    const int32_t sp = split_rows(kTileReduce, N, 0);
-    const unsigned grid = grid_for(n, sp);
-    const unsigned thr = row_threads(kTileReduce / sp);
+    const RowSplit rsp = row_split(kTileReduce, split_rows(kTileReduce, N, 0), chunk_aligned);
+    const unsigned grid = grid_for(n, rsp.split);
+    const unsigned thr = row_threads(rsp.sub);
     if (chunk_aligned)
         reduce_kernel<FSDP_REDUCE_POL, 1, true>
-            <<<grid, thr, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
+            <<<grid, thr, 0, st>>>(tiles, n, rsp.split, rsp.sub, ents, rs_in, S, N, fN);
     else
         reduce_kernel<FSDP_REDUCE_POL, 1, false>
-            <<<grid, thr, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
+            <<<grid, thr, 0, st>>>(tiles, n, rsp.split, rsp.sub, ents, rs_in, S, N, fN);
     return hipGetLastError();
 }
 
@@ -1686,19 +1704,19 @@ hipError_t launch_reduce_f32(const ReduceTile *tiles, int64_t n, const DevEntry 
     if (n == 0) return hipSuccess;
     const float fN = static_cast<float>(N);
     // fp32 rows carry twice the bytes of bf16 rows per element
-    const int32_t sp = split_rows(kTileReduce, 2 * N, 0);
-    const unsigned grid = grid_for(n, sp);
-    const unsigned thr = row_threads(kTileReduce / sp);
+    const RowSplit rsp = row_split(kTileReduce, split_rows(kTileReduce, 2 * N, 0), chunk_aligned);
+    const unsigned grid = grid_for(n, rsp.split);
+    const unsigned thr = row_threads(rsp.sub);
     if (chunk_aligned)
         reduce_f32_kernel<FSDP_REDUCE_F32_POL, true>
-            <<<grid, thr, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
+            <<<grid, thr, 0, st>>>(tiles, n, rsp.split, rsp.sub, ents, rs_in, S, N, fN);
     else
         reduce_f32_kernel<FSDP_REDUCE_F32_POL, false>
-            <<<grid, thr, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
+            <<<grid, thr, 0, st>>>(tiles, n, rsp.split, rsp.sub, ents, rs_in, S, N, fN);
     return hipGetLastError();
 }
 
-template <int P, int RB>
+template <int P, int RB, int RBG>
 void launch_step_rb(bool aligned, bool write_grad, unsigned grid, unsigned thr, hipStream_t st,
                     const PackTile *tiles, int64_t n, int32_t sp, int64_t sub, const DevEntry *ents,
                     const uint16_t *rs_in, uint16_t *ag_in, int64_t S, int32_t N, float fN,
@@ -1710,11 +1728,11 @@ void launch_step_rb(bool aligned, bool write_grad, unsigned grid, unsigned thr, 
         step_kernel_aligned<P, RB, false><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in,
                                                                ag_in, S, N, fN, c);
     else if (write_grad)
-        step_kernel<P, RB, true><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N,
-                                                      fN, c);
-    else
-        step_kernel<P, RB, false><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N,
+        step_kernel<P, RBG, true><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N,
                                                        fN, c);
+    else
+        step_kernel<P, RBG, false><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S,
+                                                        N, fN, c);
 }
 
 hipError_t launch_step(const PackTile *tiles, int64_t n, const DevEntry *ents,
@@ -1725,8 +1743,9 @@ hipError_t launch_step(const PackTile *tiles, int64_t n, const DevEntry *ents,
     const float fN = static_cast<float>(N);
     const AdamwScalars c = to_scalars(scal);
     // p, m, v read and written: six more streams per element besides the N rows
-    const int32_t sp = split_rows(kTilePack, N, 6);
-    const int64_t sub = kTilePack / sp;
+    const RowSplit rsp = row_split(kTilePack, split_rows(kTilePack, N, 6), chunk_aligned);
+    const int32_t sp = rsp.split;
+    const int64_t sub = rsp.sub;
     const unsigned grid = grid_for(n, sp);
     const unsigned thr = row_threads(sub);
     const bool aligned = chunk_aligned;
@@ -1746,11 +1765,11 @@ hipError_t launch_step(const PackTile *tiles, int64_t n, const DevEntry *ents,
         return hipGetLastError();
     }
     if (N <= 8)
-        launch_step_rb<P, FSDP_STEP_ROW_BATCH>(aligned, write_grad, grid, thr, st, tiles, n, sp, sub,
-                                               ents, rs_in, ag_in, S, N, fN, c);
+        launch_step_rb<P, FSDP_STEP_ROW_BATCH, FSDP_STEP_GEN_ROW_BATCH>(
+            aligned, write_grad, grid, thr, st, tiles, n, sp, sub, ents, rs_in, ag_in, S, N, fN, c);
     else
-        launch_step_rb<P, FSDP_STEP_ROW_BATCH_WIDE>(aligned, write_grad, grid, thr, st, tiles, n, sp,
-                                                    sub, ents, rs_in, ag_in, S, N, fN, c);
+        launch_step_rb<P, FSDP_STEP_ROW_BATCH_WIDE, FSDP_STEP_ROW_BATCH_WIDE>(
+            aligned, write_grad, grid, thr, st, tiles, n, sp, sub, ents, rs_in, ag_in, S, N, fN, c);
     return hipGetLastError();
 }
 
