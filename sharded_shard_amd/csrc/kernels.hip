@@ -51,10 +51,9 @@
 // Lanes of the fp32 reduction store two 16-byte halves of a 32-byte span per
 // group: non-temporal stores of that pattern cost extra HBM writes (measured
 // 1.1-1.7x the algorithmic bytes), plain stores do not.  The fp32 copy-ins
-// and the accumulation move four elements per lane on their aligned paths,
-// so every store instruction of a wave writes 1 KB contiguously, and take
-// non-temporal loads and stores there (their misaligned paths keep plain
-// stores).
+// and the accumulation move four elements per lane, so every store
+// instruction of a wave writes 1 KB contiguously, and take non-temporal
+// loads and stores.
 #ifndef FSDP_REDUCE_F32_POL
 #define FSDP_REDUCE_F32_POL 0
 #endif
@@ -233,6 +232,14 @@ __device__ __forceinline__ u32x4 bload16(const char *al, uint32_t voff, uint32_t
     return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, NT ? 2 : 0);
 }
 
+// The same for 8 bytes from an 8-byte aligned, wave-uniform base.
+template <int NT>
+__device__ __forceinline__ u32x2 bload8(const char *al, uint32_t voff, uint32_t nbytes) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(al), 0, nbytes, 0x00020000);
+    return __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, NT ? 2 : 0);
+}
+
 // The same register of the next lane of the wave (wave_shl:1 DPP); the last
 // lane gets 0.
 __device__ __forceinline__ uint32_t next_lane(uint32_t x) {
@@ -241,15 +248,6 @@ __device__ __forceinline__ uint32_t next_lane(uint32_t x) {
 
 __device__ __forceinline__ u32x4 next_lane16(u32x4 a) {
     return u32x4{next_lane(a.x), next_lane(a.y), next_lane(a.z), next_lane(a.w)};
-}
-
-// 16 bytes starting at p; k = p's address & 15, wave-uniform.  kAl: k == 0.
-// Callers pick the variant once per run, so the loop holds no branch.
-template <int NT, bool kAl>
-__device__ __forceinline__ u32x4 load16(const void *p, uint32_t k) {
-    if (kAl) return ldp<NT>(reinterpret_cast<const u32x4 *>(p));
-    const u32x4 *al = reinterpret_cast<const u32x4 *>(reinterpret_cast<uintptr_t>(p) - k);
-    return funnel(ldp<NT>(al), ldp<NT>(al + 1), k);
 }
 
 // Eight fp32 starting at p, whose dword index modulo 4 is q (wave-uniform).
@@ -833,23 +831,14 @@ __device__ __forceinline__ void zero_f32(float *dst, int64_t from, int64_t len) 
     if (tid < n - done) d[done + tid] = 0.0f;
 }
 
-// dv[2g], dv[2g + 1] = fp32 of s[8g .. 8g + 8) for g < ngrp.
-template <int LN, int SN, bool kAl>
-__device__ __forceinline__ void widen_vec(f32x4 *__restrict__ dv, const uint16_t *__restrict__ s,
-                                          int64_t ngrp, uint32_t k) {
-    for (int64_t g = threadIdx.x; g < ngrp; g += kBlock) {
-        float x[8];
-        init8(x, load16<LN, kAl>(s + (g << 3), k));
-        stp<SN>(dv + 2 * g, f32x4{x[0], x[1], x[2], x[3]});
-        stp<SN>(dv + 2 * g + 1, f32x4{x[4], x[5], x[6], x[7]});
-    }
-}
-
 // dst[i] = fp32(src[i]) for i < valid (exact widening), zeros up to len.
-// dst is aligned to 16 bytes after a short head.  An 8-byte aligned source
-// moves four elements per lane (8-byte loads, 16-byte stores: each wave
-// instruction is contiguous); otherwise eight per lane from funnel-shifted
-// 16-byte chunks, with plain stores (a lane writes two halves of 32 bytes).
+// dst is aligned to 16 bytes after a short head; every lane then widens four
+// elements into one 16-byte store, so each wave instruction is contiguous.
+// An 8-byte aligned source is one 8-byte load per lane.  Otherwise lane l
+// loads the 8-byte word holding its first element, takes the next word from
+// lane l + 1 (DPP; lane 63 loads its own from a load whose other lanes sit
+// at the end of the buffer range), and funnel-shifts: every source word is
+// read once, and whole waves iterate together.
 template <int POL>
 __device__ __forceinline__ void widen_run(float *__restrict__ dst, const uint16_t *__restrict__ src,
                                           int64_t len, int64_t valid) {
@@ -871,9 +860,27 @@ __device__ __forceinline__ void widen_run(float *__restrict__ dst, const uint16_
         }
         done = head + (nq << 2);
     } else {
-        const int64_t ngrp = (valid - head) >> 3;
-        widen_vec<LN, 0, false>(dv, s, ngrp, k);
-        done = head + (ngrp << 3);
+        const uint32_t k8 = k & 7u;                     // 2, 4 or 6
+        const char *al = reinterpret_cast<const char *>(s) - k8;
+        const int64_t nq = (valid - head) >> 2;
+        const uint32_t nb = (k8 + 2 * static_cast<uint32_t>(valid - head) + 7u) & ~7u;
+        const uint32_t lane = tid & 63;
+        const bool last = lane == 63, s4 = k8 >= 4u;
+        const uint32_t sh = k8 & 3u;
+        for (int64_t w0 = tid - lane; w0 < nq; w0 += kBlock) {
+            const int64_t q = w0 + lane;
+            const uint32_t o = static_cast<uint32_t>(q) << 3;
+            const u32x2 a = bload8<LN>(al, o, nb);
+            const u32x2 h = bload8<LN>(al, last ? o + 8 : nb, nb);
+            u32x2 b{next_lane(a.x), next_lane(a.y)};
+            if (last) b = h;
+            // bytes [k8, k8 + 8) of a:b
+            const uint32_t u0 = s4 ? a.y : a.x, u1 = s4 ? b.x : a.y, u2 = s4 ? b.y : b.x;
+            const uint32_t r0 = __builtin_amdgcn_alignbyte(u1, u0, sh);
+            const uint32_t r1 = __builtin_amdgcn_alignbyte(u2, u1, sh);
+            if (q < nq) stp<SN>(dv + q, f32x4{bf16_lo(r0), bf16_hi(r0), bf16_lo(r1), bf16_hi(r1)});
+        }
+        done = head + (nq << 2);
     }
     if (tid < valid - done) dst[done + tid] = widen(src[done + tid]);
     zero_f32<SN>(dst, valid, len);
@@ -1176,23 +1183,12 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(const EwTile *__rest
     }
 }
 
-// dv[2g], dv[2g + 1] = s[8g .. 8g + 8) for g < ngrp.
-template <int LN, int SN, bool kAl>
-__device__ __forceinline__ void copy_f32_vec(f32x4 *__restrict__ dv, const float *__restrict__ s,
-                                             int64_t ngrp, uint32_t q) {
-    for (int64_t g = threadIdx.x; g < ngrp; g += kBlock) {
-        f32x4 a, b;
-        load8f<LN, kAl>(s + (g << 3), q, a, b);
-        stp<SN>(dv + 2 * g, a);
-        stp<SN>(dv + 2 * g + 1, b);
-    }
-}
-
 // Reduce-scatter copy-in from the fp32 accumulators: copy fp32 runs, zeros
-// in padding.  dst is aligned to 16 bytes after a short head.  An aligned
-// source is copied one 16-byte vector per lane (each wave instruction
-// contiguous); otherwise eight elements per lane from aligned vectors,
-// dword-selected, with plain stores (a lane writes two halves of 32 bytes).
+// in padding.  dst is aligned to 16 bytes after a short head; every lane then
+// stores one 16-byte vector, so each wave instruction is contiguous.  An
+// aligned source is one load per lane; otherwise lane l loads the aligned
+// chunk holding its first element, takes the next chunk from lane l + 1
+// (DPP; lane 63 loads its own) and shifts by whole dwords.
 template <int POL>
 __device__ __forceinline__ void copy_f32_run(float *__restrict__ dst, const float *__restrict__ src,
                                              int64_t len, int64_t valid) {
@@ -1211,9 +1207,21 @@ __device__ __forceinline__ void copy_f32_run(float *__restrict__ dst, const floa
         for (int64_t v = tid; v < nq; v += kBlock) stp<SN>(dv + v, ldp<LN>(sv + v));
         done = head + (nq << 2);
     } else {
-        const int64_t ngrp = (valid - head) >> 3;
-        copy_f32_vec<LN, 0, false>(dv, s, ngrp, q);
-        done = head + (ngrp << 3);
+        const char *al = reinterpret_cast<const char *>(s) - 4 * q;
+        const int64_t nv = (valid - head) >> 2;
+        const uint32_t nb = (4 * q + 4 * static_cast<uint32_t>(valid - head) + 15u) & ~15u;
+        const uint32_t lane = tid & 63;
+        const bool last = lane == 63;
+        for (int64_t w0 = tid - lane; w0 < nv; w0 += kBlock) {
+            const int64_t v = w0 + lane;
+            const uint32_t o = static_cast<uint32_t>(v) << 4;
+            const u32x4 a = bload16<LN>(al, o, nb);
+            const u32x4 h = bload16<LN>(al, last ? o + 16 : nb, nb);
+            u32x4 b = next_lane16(a);
+            if (last) b = h;
+            if (v < nv) stp<SN>(dv + v, __builtin_bit_cast(f32x4, funnel(a, b, 4 * q)));
+        }
+        done = head + (nv << 2);
     }
     if (tid < valid - done) dst[done + tid] = src[done + tid];
     zero_f32<SN>(dst, valid, len);
