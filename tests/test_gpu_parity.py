@@ -550,9 +550,14 @@ def test_fused_step_rejects_unbound_and_bad_flags():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("unfused", [False, True], ids=["fused", "unfused"])
-def test_step_groups_equals_per_group_calls(unfused):
-    n, r = 6, 5
-    group_shapes = [CASES[1][1], CASES[2][1], [(70001,), (300, 33)]]
+@pytest.mark.parametrize("n,r", [(6, 5), (64, 0)], ids=["n6", "n64"])
+def test_step_groups_equals_per_group_calls(unfused, n, r):
+    if n == 6:
+        group_shapes = [CASES[1][1], CASES[2][1], [(70001,), (300, 33)]]
+    else:
+        # 16-byte aligned rows (the wide row kernels) beside misaligned ones
+        named = {c[0]: c[1] for c in CASES}
+        group_shapes = [named["wide-n64"], named["odd-n64"], [(64 * 300, 24), (8192,)]]
     A, B, rs_bufs, ag_a, ag_b = [], [], [], [], []
     for gi, shapes in enumerate(group_shapes):
         ga, gb = ShardedGroup(shapes, n, r), ShardedGroup(shapes, n, r)
