@@ -38,10 +38,11 @@
 // stores.  Elements per block (sub-range) per kernel; for the kernels that
 // read all N rows per element, the sub-range shrinks as N grows
 // (FSDP_ROWS_BUDGET row-elements per block, at least FSDP_MIN_SUB).  Rows in
-// flight per lane: the fused step keeps FSDP_STEP_ROW_BATCH row loads
-// outstanding up to 8 ranks and FSDP_STEP_ROW_BATCH_WIDE beyond, the plain
-// reductions FSDP_REDUCE_ROW_BATCH (measured on MI355X: more rows in flight
-// per wave cost the reductions bandwidth, fewer cost the step at 6-8 ranks).
+// flight per lane: the fused step keeps FSDP_STEP_ROW_BATCH rows (aligned)
+// or FSDP_STEP_GEN_ROW_BATCH rows (misaligned) outstanding up to 8 ranks and
+// FSDP_STEP_ROW_BATCH_WIDE beyond, the plain reductions
+// FSDP_REDUCE_ROW_BATCH (measured on MI355X: more rows in flight per wave
+// spread each wave over more DRAM pages).
 #ifndef FSDP_UNPACK_POL
 #define FSDP_UNPACK_POL 3
 #endif
@@ -75,6 +76,16 @@
 #ifndef FSDP_STEP_POL
 #define FSDP_STEP_POL 0
 #endif
+// shard policy of the aligned fused step (a quad per lane: every wave
+// instruction contiguous, so non-temporal stores write whole lines)
+#ifndef FSDP_STEP_QUAD_POL
+#define FSDP_STEP_QUAD_POL 3
+#endif
+// the aligned fused step's bf16 output: plain stores (the copy-out that
+// follows reads that row)
+#ifndef FSDP_STEP_OUT_NT
+#define FSDP_STEP_OUT_NT 0
+#endif
 #ifndef FSDP_UNPACK_SUB
 #define FSDP_UNPACK_SUB 4096
 #endif
@@ -97,7 +108,7 @@
 #define FSDP_MIN_SUB 512
 #endif
 #ifndef FSDP_STEP_ROW_BATCH
-#define FSDP_STEP_ROW_BATCH 8
+#define FSDP_STEP_ROW_BATCH 2
 #endif
 #ifndef FSDP_STEP_ROW_BATCH_WIDE
 #define FSDP_STEP_ROW_BATCH_WIDE 4
@@ -1462,7 +1473,118 @@ __device__ __forceinline__ void step_run(const uint16_t *__restrict__ rs0, int64
     zero_bf16<1>(dst, valid, len);
 }
 
-template <int POL, int RB, int C, bool kChunkAligned, bool kWriteGrad>
+
+// Column sums of four consecutive elements (a quad) at two places per lane,
+// byte offsets offb and offb + 512 from row 0 at base (16-byte aligned rows,
+// uniform), over the N rows of [N, S] bf16, in rank order from row 0; rows
+// RB at a time, each row two 8-byte loads per lane.  Buffer ranges as in
+// sum_rows8.
+template <int NT, int RB>
+__device__ __forceinline__ void sum_rows_quad(const uint16_t *base, uint32_t offb, uint32_t dbytes,
+                                              int64_t S, int32_t N, float (&acc)[2][4]) {
+    const char *r = reinterpret_cast<const char *>(base);
+    const int64_t Sb = S * 2;
+    const uint32_t nb = (dbytes + 7u) & ~7u;
+    for (int32_t j = 0; j < N; j += RB) {
+        u32x2 x[RB][2];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            const char *row = r + (j + i) * Sb;
+            const uint32_t n = j + i < N ? nb : 0u;
+            x[i][0] = bload8<NT>(row, offb, n);
+            x[i][1] = bload8<NT>(row, offb + 512u, n);
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            if (j + i >= N) continue;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const float y[4] = {bf16_lo(x[i][h].x), bf16_hi(x[i][h].x), bf16_lo(x[i][h].y),
+                                    bf16_hi(x[i][h].y)};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[h][e] = j + i == 0 ? y[e] : acc[h][e] + y[e];
+            }
+        }
+    }
+}
+
+// Store 4 bf16 (one u32x2) at p, whose address modulo 8 is k (even, uniform):
+// one 8-byte store when aligned, else dword and short stores.
+template <int NT>
+__device__ __forceinline__ void store8_at(uint16_t *p, uint32_t k, u32x2 w) {
+    if (k == 0) {
+        stp<NT>(reinterpret_cast<u32x2 *>(p), w);
+    } else if (k == 4) {
+        uint32_t *d = reinterpret_cast<uint32_t *>(p);
+        d[0] = w.x;
+        d[1] = w.y;
+    } else {
+        p[0] = static_cast<uint16_t>(w.x);
+        *reinterpret_cast<uint32_t *>(p + 1) = alignbyte2(w.y, w.x);
+        p[3] = static_cast<uint16_t>(w.y >> 16);
+    }
+}
+
+// The fused step on 16-byte aligned rows, a quad per lane and pass: lane l of
+// a wave takes quads l and l + 64 of the wave's 128, so every load and store
+// instruction of the wave is contiguous (rows 512 bytes, shards 1 KB, the
+// bf16 output 512 bytes).  That lets the shards use non-temporal loads and
+// stores without partial writes (a lane storing two halves of 32 bytes
+// splits them).  Same arithmetic, in the same order, as step_run.
+template <int POL, int RB, bool kWriteGrad>
+__device__ __forceinline__ void step_run_quad(const uint16_t *__restrict__ rs0, int64_t S,
+                                              int32_t N, float fN, float *P, float *M, float *Vv,
+                                              float *G, uint16_t *dst, int64_t len, int64_t valid,
+                                              const AdamwScalars &c) {
+    constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
+    const int tid = threadIdx.x;
+    const uint32_t ap = lo32(P) & 15u;
+    int64_t head = ((16u - ap) & 15u) >> 2;
+    if (head > valid) head = valid;
+    const uint32_t kS = static_cast<uint32_t>((S * 2) & 15);
+    const uint32_t k0 = lo32(rs0 + head) & 15u;
+    const bool same = ap == (lo32(M) & 15u) && ap == (lo32(Vv) & 15u) &&
+                      (!kWriteGrad || ap == (lo32(G) & 15u)) && (k0 | kS) == 0;
+    if (!same) {
+        for (int64_t e = tid; e < valid; e += static_cast<int64_t>(blockDim.x))
+            step_scalar_at<kWriteGrad>(rs0, S, N, fN, P, M, Vv, G, dst, e, c);
+    } else {
+        if (tid < head) step_scalar_at<kWriteGrad>(rs0, S, N, fN, P, M, Vv, G, dst, tid, c);
+        const int64_t nq = (valid - head) >> 2;
+        const uint32_t k8 = lo32(dst + head) & 7u;
+        const uint32_t dbytes = static_cast<uint32_t>(2 * (valid - head));
+        const int64_t lane = tid & 63;
+        const int64_t qstep = static_cast<int64_t>(blockDim.x >> 6) * 128;
+        for (int64_t qb = (tid >> 6) * 128; qb < nq; qb += qstep) {
+            float acc[2][4];
+            sum_rows_quad<FSDP_STEP_ROW_NT, RB>(rs0 + head, static_cast<uint32_t>(qb + lane) << 3,
+                                                dbytes, S, N, acc);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int64_t q = qb + lane + 64 * h;
+                if (q >= nq) continue;
+                const int64_t e0 = head + (q << 2);
+                f32x4 *pv = reinterpret_cast<f32x4 *>(P + e0);
+                f32x4 *mv = reinterpret_cast<f32x4 *>(M + e0);
+                f32x4 *vv = reinterpret_cast<f32x4 *>(Vv + e0);
+                f32x4 pq = ldp<LN>(pv), mq = ldp<LN>(mv), vq = ldp<LN>(vv);
+                const f32x4 g{acc[h][0] / fN, acc[h][1] / fN, acc[h][2] / fN, acc[h][3] / fN};
+                if (kWriteGrad) stp<SN>(reinterpret_cast<f32x4 *>(G + e0), g);
+                adamw_vec(pq, g, mq, vq, c);
+                stp<SN>(pv, pq);
+                stp<SN>(mv, mq);
+                stp<SN>(vv, vq);
+                store8_at<FSDP_STEP_OUT_NT>(dst + e0, k8, u32x2{pack2(pq.x, pq.y), pack2(pq.z, pq.w)});
+            }
+        }
+        const int64_t done = head + (nq << 2);
+        if (tid < valid - done)
+            step_scalar_at<kWriteGrad>(rs0, S, N, fN, P, M, Vv, G, dst, done + tid, c);
+    }
+    zero_bf16<1>(dst, valid, len);
+}
+
+template <int POL, int RB, int C, bool kChunkAligned, bool kWriteGrad, bool kQuad = false>
 __device__ __forceinline__ void step_tiles(const PackTile *__restrict__ tiles, int64_t n_tiles,
                                            int32_t split, int64_t sub,
                                            const DevEntry *__restrict__ ents,
@@ -1481,23 +1603,29 @@ __device__ __forceinline__ void step_tiles(const PackTile *__restrict__ tiles, i
         valid = valid < 0 ? 0 : (valid > len ? len : valid);
         const DevEntry en = ents[tl.entry];
         const int64_t o = tl.src + b;
-        step_run<POL, RB, C, kChunkAligned, kWriteGrad>(rs_in + tl.dst + b, S, N, fN, en.master + o,
-                                                en.exp_avg + o, en.exp_avg_sq + o,
-                                                kWriteGrad ? en.grad + o : nullptr,
-                                                ag_in + tl.dst + b, len, valid, c);
+        if constexpr (kQuad)
+            step_run_quad<POL, RB, kWriteGrad>(rs_in + tl.dst + b, S, N, fN, en.master + o,
+                                               en.exp_avg + o, en.exp_avg_sq + o,
+                                               kWriteGrad ? en.grad + o : nullptr,
+                                               ag_in + tl.dst + b, len, valid, c);
+        else
+            step_run<POL, RB, C, kChunkAligned, kWriteGrad>(
+                rs_in + tl.dst + b, S, N, fN, en.master + o, en.exp_avg + o, en.exp_avg_sq + o,
+                kWriteGrad ? en.grad + o : nullptr, ag_in + tl.dst + b, len, valid, c);
     }
 }
 
-// Aligned rows: scheduled for 6 waves per SIMD (measured faster on MI355X
-// than the default target or 7 or 8 waves).
-template <int POL, int RB, bool kWriteGrad>
+// Aligned rows, a quad per lane and pass (step_run_quad) with the shard
+// policy FSDP_STEP_QUAD_POL, scheduled for FSDP_STEP_WAVES waves per SIMD.
+template <int RB, bool kWriteGrad>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(FSDP_STEP_WAVES)))
 void step_kernel_aligned(const PackTile *__restrict__ tiles, int64_t n_tiles, int32_t split,
                          int64_t sub, const DevEntry *__restrict__ ents,
                          const uint16_t *__restrict__ rs_in, uint16_t *__restrict__ ag_in,
                          int64_t S, int32_t N, float fN, AdamwScalars c) {
-    step_tiles<POL, RB, 1, true, kWriteGrad>(tiles, n_tiles, split, sub, ents, rs_in, ag_in, S, N,
-                                             fN, c);
+    step_tiles<FSDP_STEP_QUAD_POL, RB, 1, true, kWriteGrad, true>(tiles, n_tiles, split, sub,
+                                                                   ents, rs_in, ag_in, S, N, fN,
+                                                                   c);
 }
 
 // Aligned rows at many ranks: one wave per block, FSDP_STEP_WIDE groups per
@@ -1730,11 +1858,11 @@ void launch_step_rb(bool aligned, bool write_grad, unsigned grid, unsigned thr, 
                     const uint16_t *rs_in, uint16_t *ag_in, int64_t S, int32_t N, float fN,
                     const AdamwScalars &c) {
     if (aligned && write_grad)
-        step_kernel_aligned<P, RB, true><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in,
-                                                              S, N, fN, c);
+        step_kernel_aligned<RB, true><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in,
+                                                           S, N, fN, c);
     else if (aligned)
-        step_kernel_aligned<P, RB, false><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in,
-                                                               ag_in, S, N, fN, c);
+        step_kernel_aligned<RB, false><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in,
+                                                            ag_in, S, N, fN, c);
     else if (write_grad)
         step_kernel<P, RBG, true><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N,
                                                        fN, c);
