@@ -49,6 +49,11 @@
 #ifndef FSDP_REDUCE_POL
 #define FSDP_REDUCE_POL 1
 #endif
+// the bf16 reduction on aligned rows below the wide threshold: a quad per
+// lane, non-temporal loads and stores
+#ifndef FSDP_REDUCE_QUAD_POL
+#define FSDP_REDUCE_QUAD_POL 3
+#endif
 // Lanes of the fp32 reduction store two 16-byte halves of a 32-byte span per
 // group: non-temporal stores of that pattern cost extra HBM writes (measured
 // 1.1-1.7x the algorithmic bytes), plain stores do not.  The fp32 copy-ins
@@ -67,8 +72,10 @@
 #ifndef FSDP_ACC_POL
 #define FSDP_ACC_POL 3
 #endif
+// AdamW moves one 16-byte vector per lane and array (contiguous wave
+// instructions): non-temporal loads and stores
 #ifndef FSDP_ADAMW_POL
-#define FSDP_ADAMW_POL 0
+#define FSDP_ADAMW_POL 3
 #endif
 #ifndef FSDP_PACK_POL
 #define FSDP_PACK_POL 3
@@ -614,6 +621,40 @@ __device__ __forceinline__ void sum_rows_wide(const uint16_t *base, uint32_t off
     }
 }
 
+// Column sums of four consecutive elements (a quad) at QP places per lane,
+// byte offsets offb + 512 h (h < QP) from row 0 at base (16-byte aligned
+// rows, uniform), over the N rows of [N, S] bf16, in rank order from row 0;
+// rows RB at a time, each row QP 8-byte loads per lane.  Buffer ranges as in
+// sum_rows8.
+template <int NT, int RB, int QP>
+__device__ __forceinline__ void sum_rows_quad(const uint16_t *base, uint32_t offb, uint32_t dbytes,
+                                              int64_t S, int32_t N, float (&acc)[QP][4]) {
+    const char *r = reinterpret_cast<const char *>(base);
+    const int64_t Sb = S * 2;
+    const uint32_t nb = (dbytes + 7u) & ~7u;
+    for (int32_t j = 0; j < N; j += RB) {
+        u32x2 x[RB][QP];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            const char *row = r + (j + i) * Sb;
+            const uint32_t n = j + i < N ? nb : 0u;
+#pragma unroll
+            for (int h = 0; h < QP; ++h) x[i][h] = bload8<NT>(row, offb + 512u * h, n);
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            if (j + i >= N) continue;
+#pragma unroll
+            for (int h = 0; h < QP; ++h) {
+                const float y[4] = {bf16_lo(x[i][h].x), bf16_hi(x[i][h].x), bf16_lo(x[i][h].y),
+                                    bf16_hi(x[i][h].y)};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[h][e] = j + i == 0 ? y[e] : acc[h][e] + y[e];
+            }
+        }
+    }
+}
+
 // Group schedule of the row kernels: 8-element groups [0, ngrp), C per lane
 // per pass, a wave's lanes on consecutive groups.  Aligned rows: pass c of
 // lane l of wave w takes group (w*C + c)*64 + l, then all step by the block.
@@ -659,9 +700,32 @@ __device__ __forceinline__ void reduce_run(float *__restrict__ dst, const uint16
         return;
     }
     if (tid < head) dst[tid] = sum_rows_scalar(src0, S, N, tid) / fN;
-    const int64_t ngrp = (len - head) >> 3;
     const uint32_t dbytes = static_cast<uint32_t>(2 * (len - head));
     f32x4 *dv = reinterpret_cast<f32x4 *>(dst + head);
+    if constexpr (kChunkAligned && C == 1) {
+        // a quad per lane and pass, two passes 64 quads apart: every wave
+        // instruction contiguous, so the stores take FSDP_REDUCE_QUAD_POL
+        constexpr int QS = (FSDP_REDUCE_QUAD_POL >> 1) & 1;
+        const int64_t nq = (len - head) >> 2;
+        const int64_t lane = tid & 63;
+        const int64_t qstep = static_cast<int64_t>(blockDim.x >> 6) * 128;
+        for (int64_t qb = (tid >> 6) * 128; qb < nq; qb += qstep) {
+            float acc[2][4];
+            sum_rows_quad<FSDP_REDUCE_QUAD_POL & 1, FSDP_REDUCE_ROW_BATCH, 2>(
+                s0, static_cast<uint32_t>(qb + lane) << 3, dbytes, S, N, acc);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int64_t q = qb + lane + 64 * h;
+                if (q < nq)
+                    stp<QS>(dv + q, f32x4{acc[h][0] / fN, acc[h][1] / fN, acc[h][2] / fN,
+                                          acc[h][3] / fN});
+            }
+        }
+        const int64_t done = head + (nq << 2);
+        if (tid < len - done) dst[done + tid] = sum_rows_scalar(src0, S, N, done + tid) / fN;
+        return;
+    }
+    const int64_t ngrp = (len - head) >> 3;
     for (GroupWalk<kChunkAligned, C> w; w.more(ngrp); w.next()) {
         float acc[C][8];
         if constexpr (C == 1)
@@ -1474,40 +1538,6 @@ __device__ __forceinline__ void step_run(const uint16_t *__restrict__ rs0, int64
 }
 
 
-// Column sums of four consecutive elements (a quad) at two places per lane,
-// byte offsets offb and offb + 512 from row 0 at base (16-byte aligned rows,
-// uniform), over the N rows of [N, S] bf16, in rank order from row 0; rows
-// RB at a time, each row two 8-byte loads per lane.  Buffer ranges as in
-// sum_rows8.
-template <int NT, int RB>
-__device__ __forceinline__ void sum_rows_quad(const uint16_t *base, uint32_t offb, uint32_t dbytes,
-                                              int64_t S, int32_t N, float (&acc)[2][4]) {
-    const char *r = reinterpret_cast<const char *>(base);
-    const int64_t Sb = S * 2;
-    const uint32_t nb = (dbytes + 7u) & ~7u;
-    for (int32_t j = 0; j < N; j += RB) {
-        u32x2 x[RB][2];
-#pragma unroll
-        for (int i = 0; i < RB; ++i) {
-            const char *row = r + (j + i) * Sb;
-            const uint32_t n = j + i < N ? nb : 0u;
-            x[i][0] = bload8<NT>(row, offb, n);
-            x[i][1] = bload8<NT>(row, offb + 512u, n);
-        }
-#pragma unroll
-        for (int i = 0; i < RB; ++i) {
-            if (j + i >= N) continue;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const float y[4] = {bf16_lo(x[i][h].x), bf16_hi(x[i][h].x), bf16_lo(x[i][h].y),
-                                    bf16_hi(x[i][h].y)};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[h][e] = j + i == 0 ? y[e] : acc[h][e] + y[e];
-            }
-        }
-    }
-}
-
 // Store 4 bf16 (one u32x2) at p, whose address modulo 8 is k (even, uniform):
 // one 8-byte store when aligned, else dword and short stores.
 template <int NT>
@@ -1526,12 +1556,12 @@ __device__ __forceinline__ void store8_at(uint16_t *p, uint32_t k, u32x2 w) {
 }
 
 // The fused step on 16-byte aligned rows, a quad per lane and pass: lane l of
-// a wave takes quads l and l + 64 of the wave's 128, so every load and store
-// instruction of the wave is contiguous (rows 512 bytes, shards 1 KB, the
-// bf16 output 512 bytes).  That lets the shards use non-temporal loads and
-// stores without partial writes (a lane storing two halves of 32 bytes
+// a wave takes quads l + 64 h (h < QP) of the wave's 64 QP, so every load and
+// store instruction of the wave is contiguous (rows 512 bytes, shards 1 KB,
+// the bf16 output 512 bytes).  That lets the shards use non-temporal loads
+// and stores without partial writes (a lane storing two halves of 32 bytes
 // splits them).  Same arithmetic, in the same order, as step_run.
-template <int POL, int RB, bool kWriteGrad>
+template <int POL, int RB, int QP, bool kWriteGrad>
 __device__ __forceinline__ void step_run_quad(const uint16_t *__restrict__ rs0, int64_t S,
                                               int32_t N, float fN, float *P, float *M, float *Vv,
                                               float *G, uint16_t *dst, int64_t len, int64_t valid,
@@ -1554,13 +1584,13 @@ __device__ __forceinline__ void step_run_quad(const uint16_t *__restrict__ rs0, 
         const uint32_t k8 = lo32(dst + head) & 7u;
         const uint32_t dbytes = static_cast<uint32_t>(2 * (valid - head));
         const int64_t lane = tid & 63;
-        const int64_t qstep = static_cast<int64_t>(blockDim.x >> 6) * 128;
-        for (int64_t qb = (tid >> 6) * 128; qb < nq; qb += qstep) {
-            float acc[2][4];
-            sum_rows_quad<FSDP_STEP_ROW_NT, RB>(rs0 + head, static_cast<uint32_t>(qb + lane) << 3,
-                                                dbytes, S, N, acc);
+        const int64_t qstep = static_cast<int64_t>(blockDim.x >> 6) * 64 * QP;
+        for (int64_t qb = (tid >> 6) * 64 * QP; qb < nq; qb += qstep) {
+            float acc[QP][4];
+            sum_rows_quad<FSDP_STEP_ROW_NT, RB, QP>(
+                rs0 + head, static_cast<uint32_t>(qb + lane) << 3, dbytes, S, N, acc);
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int h = 0; h < QP; ++h) {
                 const int64_t q = qb + lane + 64 * h;
                 if (q >= nq) continue;
                 const int64_t e0 = head + (q << 2);
@@ -1584,7 +1614,7 @@ __device__ __forceinline__ void step_run_quad(const uint16_t *__restrict__ rs0, 
     zero_bf16<1>(dst, valid, len);
 }
 
-template <int POL, int RB, int C, bool kChunkAligned, bool kWriteGrad, bool kQuad = false>
+template <int POL, int RB, int C, bool kChunkAligned, bool kWriteGrad, int QP = 0>
 __device__ __forceinline__ void step_tiles(const PackTile *__restrict__ tiles, int64_t n_tiles,
                                            int32_t split, int64_t sub,
                                            const DevEntry *__restrict__ ents,
@@ -1603,8 +1633,8 @@ __device__ __forceinline__ void step_tiles(const PackTile *__restrict__ tiles, i
         valid = valid < 0 ? 0 : (valid > len ? len : valid);
         const DevEntry en = ents[tl.entry];
         const int64_t o = tl.src + b;
-        if constexpr (kQuad)
-            step_run_quad<POL, RB, kWriteGrad>(rs_in + tl.dst + b, S, N, fN, en.master + o,
+        if constexpr (QP > 0)
+            step_run_quad<POL, RB, QP, kWriteGrad>(rs_in + tl.dst + b, S, N, fN, en.master + o,
                                                en.exp_avg + o, en.exp_avg_sq + o,
                                                kWriteGrad ? en.grad + o : nullptr,
                                                ag_in + tl.dst + b, len, valid, c);
@@ -1623,9 +1653,8 @@ void step_kernel_aligned(const PackTile *__restrict__ tiles, int64_t n_tiles, in
                          int64_t sub, const DevEntry *__restrict__ ents,
                          const uint16_t *__restrict__ rs_in, uint16_t *__restrict__ ag_in,
                          int64_t S, int32_t N, float fN, AdamwScalars c) {
-    step_tiles<FSDP_STEP_QUAD_POL, RB, 1, true, kWriteGrad, true>(tiles, n_tiles, split, sub,
-                                                                   ents, rs_in, ag_in, S, N, fN,
-                                                                   c);
+    step_tiles<FSDP_STEP_QUAD_POL, RB, 1, true, kWriteGrad, 2>(tiles, n_tiles, split, sub, ents,
+                                                                rs_in, ag_in, S, N, fN, c);
 }
 
 // Aligned rows at many ranks: one wave per block, FSDP_STEP_WIDE groups per
