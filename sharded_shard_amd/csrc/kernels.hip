@@ -63,6 +63,11 @@
 #ifndef FSDP_REDUCE_F32_POL
 #define FSDP_REDUCE_F32_POL 0
 #endif
+// the fp32 reduction on aligned rows: a vector per lane, non-temporal loads
+// and stores
+#ifndef FSDP_REDUCE_F32_QUAD_POL
+#define FSDP_REDUCE_F32_QUAD_POL 3
+#endif
 #ifndef FSDP_RSPACK_F32_POL
 #define FSDP_RSPACK_F32_POL 3
 #endif
@@ -1407,9 +1412,56 @@ __device__ __forceinline__ void reduce_f32_run(float *__restrict__ dst,
         return;
     }
     if (tid < head) dst[tid] = sum_rows_scalar_f32(src0, S, N, tid) / fN;
-    const int64_t ngrp = (len - head) >> 3;
     const uint32_t dbytes = static_cast<uint32_t>(4 * (len - head));
     f32x4 *dv = reinterpret_cast<f32x4 *>(dst + head);
+    if constexpr (kChunkAligned) {
+        // four elements (one vector) per lane and pass, two passes 64
+        // vectors apart: every wave instruction contiguous, so loads and
+        // stores take FSDP_REDUCE_F32_QUAD_POL
+        constexpr int QL = FSDP_REDUCE_F32_QUAD_POL & 1, QS = (FSDP_REDUCE_F32_QUAD_POL >> 1) & 1;
+        const char *r = reinterpret_cast<const char *>(s0);
+        const int64_t Sb = S * 4;
+        const uint32_t nb = (dbytes + 15u) & ~15u;
+        const int64_t nq = (len - head) >> 2;
+        const int64_t lane = tid & 63;
+        const int64_t qstep = static_cast<int64_t>(blockDim.x >> 6) * 128;
+        for (int64_t qb = (tid >> 6) * 128; qb < nq; qb += qstep) {
+            const uint32_t off = static_cast<uint32_t>(qb + lane) << 4;
+            f32x4 acc[2];
+            for (int32_t j = 0; j < N; j += FSDP_REDUCE_ROW_BATCH) {
+                f32x4 x[FSDP_REDUCE_ROW_BATCH][2];
+#pragma unroll
+                for (int i = 0; i < FSDP_REDUCE_ROW_BATCH; ++i) {
+                    const char *row = r + (j + i) * Sb;
+                    const uint32_t n = j + i < N ? nb : 0u;
+                    x[i][0] = __builtin_bit_cast(f32x4, bload16<QL>(row, off, n));
+                    x[i][1] = __builtin_bit_cast(f32x4, bload16<QL>(row, off + 1024u, n));
+                }
+#pragma unroll
+                for (int i = 0; i < FSDP_REDUCE_ROW_BATCH; ++i) {
+                    if (j + i >= N) continue;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const f32x4 y = x[i][h];
+                        acc[h] = j + i == 0 ? y
+                                            : f32x4{acc[h].x + y.x, acc[h].y + y.y,
+                                                    acc[h].z + y.z, acc[h].w + y.w};
+                    }
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int64_t q = qb + lane + 64 * h;
+                if (q < nq)
+                    stp<QS>(dv + q, f32x4{acc[h].x / fN, acc[h].y / fN, acc[h].z / fN,
+                                          acc[h].w / fN});
+            }
+        }
+        const int64_t done = head + (nq << 2);
+        if (tid < len - done) dst[done + tid] = sum_rows_scalar_f32(src0, S, N, done + tid) / fN;
+        return;
+    }
+    const int64_t ngrp = (len - head) >> 3;
     for (GroupWalk<kChunkAligned> w; w.more(ngrp); w.next()) {
         float acc[8];
         sum_rows8f<LN, FSDP_REDUCE_ROW_BATCH, kChunkAligned>(
