@@ -77,10 +77,10 @@
 #ifndef FSDP_ACC_POL
 #define FSDP_ACC_POL 3
 #endif
-// AdamW moves one 16-byte vector per lane and array (contiguous wave
-// instructions): non-temporal loads and stores
+// AdamW: plain loads and stores (non-temporal ones measured faster for the
+// kernel itself but slowed the copy-in and copy-out after it by more)
 #ifndef FSDP_ADAMW_POL
-#define FSDP_ADAMW_POL 3
+#define FSDP_ADAMW_POL 0
 #endif
 #ifndef FSDP_PACK_POL
 #define FSDP_PACK_POL 3
