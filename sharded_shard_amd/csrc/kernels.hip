@@ -127,7 +127,7 @@
 #endif
 // rows in flight of the fused step on misaligned rows up to 8 ranks
 #ifndef FSDP_STEP_GEN_ROW_BATCH
-#define FSDP_STEP_GEN_ROW_BATCH 2
+#define FSDP_STEP_GEN_ROW_BATCH 1
 #endif
 #ifndef FSDP_REDUCE_ROW_BATCH
 #define FSDP_REDUCE_ROW_BATCH 2
@@ -655,6 +655,56 @@ __device__ __forceinline__ void sum_rows_quad(const uint16_t *base, uint32_t off
                                     bf16_hi(x[i][h].y)};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[h][e] = j + i == 0 ? y[e] : acc[h][e] + y[e];
+            }
+        }
+    }
+}
+
+// The same sums over misaligned rows: row j starts k_j = (k0 + j kS) & 7
+// bytes past an 8-byte boundary.  Lane l loads the 8-byte word holding the
+// start of its quad, takes the next word from lane l + 1 (DPP; lane 63 loads
+// its own, from a load whose other lanes sit at the end of the buffer
+// range), and funnel-shifts by k_j: every word of a row is read once.  The
+// whole wave must run this (the DPP reads every lane).
+template <int NT, int RB>
+__device__ __forceinline__ void sum_rows_quad_mis(const uint16_t *base, uint32_t offb,
+                                                  uint32_t dbytes, int64_t S, int32_t N,
+                                                  uint32_t k0, uint32_t kS, float (&acc)[2][4]) {
+    const char *r = reinterpret_cast<const char *>(base);
+    const int64_t Sb = S * 2;
+    const bool last = (threadIdx.x & 63) == 63;
+    for (int32_t j = 0; j < N; j += RB) {
+        u32x2 a[RB][2], e[RB][2];
+        uint32_t kk[RB];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            kk[i] = (k0 + static_cast<uint32_t>(j + i) * kS) & 7u;
+            const char *al = r + (j + i) * Sb - kk[i];
+            const uint32_t n = j + i < N ? (kk[i] + dbytes + 7u) & ~7u : 0u;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t o = offb + 512u * h;
+                a[i][h] = bload8<NT>(al, o, n);
+                e[i][h] = bload8<NT>(al, last ? o + 8u : n, n);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            const bool s4 = kk[i] >= 4u;
+            const uint32_t sh = kk[i] & 3u;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                u32x2 b{next_lane(a[i][h].x), next_lane(a[i][h].y)};
+                if (last) b = e[i][h];
+                // bytes [k, k + 8) of a:b
+                const uint32_t u0 = s4 ? a[i][h].y : a[i][h].x, u1 = s4 ? b.x : a[i][h].y;
+                const uint32_t u2 = s4 ? b.y : b.x;
+                const uint32_t w0 = __builtin_amdgcn_alignbyte(u1, u0, sh);
+                const uint32_t w1 = __builtin_amdgcn_alignbyte(u2, u1, sh);
+                if (j + i >= N) continue;
+                const float y[4] = {bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[h][q] = j + i == 0 ? y[q] : acc[h][q] + y[q];
             }
         }
     }
@@ -1607,13 +1657,14 @@ __device__ __forceinline__ void store8_at(uint16_t *p, uint32_t k, u32x2 w) {
     }
 }
 
-// The fused step on 16-byte aligned rows, a quad per lane and pass: lane l of
-// a wave takes quads l + 64 h (h < QP) of the wave's 64 QP, so every load and
-// store instruction of the wave is contiguous (rows 512 bytes, shards 1 KB,
-// the bf16 output 512 bytes).  That lets the shards use non-temporal loads
-// and stores without partial writes (a lane storing two halves of 32 bytes
-// splits them).  Same arithmetic, in the same order, as step_run.
-template <int POL, int RB, int QP, bool kWriteGrad>
+// The fused step, a quad per lane and pass: lane l of a wave takes quads
+// l + 64 h (h < QP) of the wave's 64 QP, so every load and store instruction
+// of the wave is contiguous (rows 512 bytes, shards 1 KB, the bf16 output 512
+// bytes).  That lets the shards use non-temporal loads and stores without
+// partial writes (a lane storing two halves of 32 bytes splits them).  Rows
+// 16-byte aligned, or with kMis at any even byte phase (sum_rows_quad_mis,
+// QP = 2).  Same arithmetic, in the same order, as step_run.
+template <int POL, int RB, int QP, bool kWriteGrad, bool kMis = false>
 __device__ __forceinline__ void step_run_quad(const uint16_t *__restrict__ rs0, int64_t S,
                                               int32_t N, float fN, float *P, float *M, float *Vv,
                                               float *G, uint16_t *dst, int64_t len, int64_t valid,
@@ -1626,11 +1677,12 @@ __device__ __forceinline__ void step_run_quad(const uint16_t *__restrict__ rs0, 
     const uint32_t kS = static_cast<uint32_t>((S * 2) & 15);
     const uint32_t k0 = lo32(rs0 + head) & 15u;
     const bool same = ap == (lo32(M) & 15u) && ap == (lo32(Vv) & 15u) &&
-                      (!kWriteGrad || ap == (lo32(G) & 15u)) && (k0 | kS) == 0;
+                      (!kWriteGrad || ap == (lo32(G) & 15u)) && (kMis || (k0 | kS) == 0);
     if (!same) {
         for (int64_t e = tid; e < valid; e += static_cast<int64_t>(blockDim.x))
             step_scalar_at<kWriteGrad>(rs0, S, N, fN, P, M, Vv, G, dst, e, c);
     } else {
+        static_assert(!kMis || QP == 2, "misaligned rows: two quads per lane");
         if (tid < head) step_scalar_at<kWriteGrad>(rs0, S, N, fN, P, M, Vv, G, dst, tid, c);
         const int64_t nq = (valid - head) >> 2;
         const uint32_t k8 = lo32(dst + head) & 7u;
@@ -1639,8 +1691,13 @@ __device__ __forceinline__ void step_run_quad(const uint16_t *__restrict__ rs0, 
         const int64_t qstep = static_cast<int64_t>(blockDim.x >> 6) * 64 * QP;
         for (int64_t qb = (tid >> 6) * 64 * QP; qb < nq; qb += qstep) {
             float acc[QP][4];
-            sum_rows_quad<FSDP_STEP_ROW_NT, RB, QP>(
-                rs0 + head, static_cast<uint32_t>(qb + lane) << 3, dbytes, S, N, acc);
+            if constexpr (kMis)
+                sum_rows_quad_mis<FSDP_STEP_ROW_NT, RB>(rs0 + head,
+                                                        static_cast<uint32_t>(qb + lane) << 3,
+                                                        dbytes, S, N, k0 & 7u, kS & 7u, acc);
+            else
+                sum_rows_quad<FSDP_STEP_ROW_NT, RB, QP>(
+                    rs0 + head, static_cast<uint32_t>(qb + lane) << 3, dbytes, S, N, acc);
 #pragma unroll
             for (int h = 0; h < QP; ++h) {
                 const int64_t q = qb + lane + 64 * h;
@@ -1686,7 +1743,7 @@ __device__ __forceinline__ void step_tiles(const PackTile *__restrict__ tiles, i
         const DevEntry en = ents[tl.entry];
         const int64_t o = tl.src + b;
         if constexpr (QP > 0)
-            step_run_quad<POL, RB, QP, kWriteGrad>(rs_in + tl.dst + b, S, N, fN, en.master + o,
+            step_run_quad<POL, RB, QP, kWriteGrad, !kChunkAligned>(rs_in + tl.dst + b, S, N, fN, en.master + o,
                                                en.exp_avg + o, en.exp_avg_sq + o,
                                                kWriteGrad ? en.grad + o : nullptr,
                                                ag_in + tl.dst + b, len, valid, c);
@@ -1720,14 +1777,16 @@ __global__ __launch_bounds__(64) void step_kernel_wide(
                                                          ag_in, S, N, fN, c);
 }
 
-template <int POL, int RB, bool kWriteGrad>
+// Misaligned rows: a quad per lane and pass as the aligned kernel, each row
+// funnel-shifted by its own phase (sum_rows_quad_mis).
+template <int RB, bool kWriteGrad>
 __global__ __launch_bounds__(kBlock) FSDP_STEP_GEN_ATTR void step_kernel(
     const PackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
     const DevEntry *__restrict__ ents,
     const uint16_t *__restrict__ rs_in, uint16_t *__restrict__ ag_in, int64_t S, int32_t N,
     float fN, AdamwScalars c) {
-    step_tiles<POL, RB, 1, false, kWriteGrad>(tiles, n_tiles, split, sub, ents, rs_in, ag_in, S, N,
-                                              fN, c);
+    step_tiles<FSDP_STEP_QUAD_POL, RB, 1, false, kWriteGrad, 2>(tiles, n_tiles, split, sub, ents,
+                                                                 rs_in, ag_in, S, N, fN, c);
 }
 
 inline unsigned grid_for(int64_t n_tiles, int32_t split) {
@@ -1933,7 +1992,7 @@ hipError_t launch_reduce_f32(const ReduceTile *tiles, int64_t n, const DevEntry 
     return hipGetLastError();
 }
 
-template <int P, int RB, int RBG>
+template <int RB, int RBG>
 void launch_step_rb(bool aligned, bool write_grad, unsigned grid, unsigned thr, hipStream_t st,
                     const PackTile *tiles, int64_t n, int32_t sp, int64_t sub, const DevEntry *ents,
                     const uint16_t *rs_in, uint16_t *ag_in, int64_t S, int32_t N, float fN,
@@ -1945,11 +2004,11 @@ void launch_step_rb(bool aligned, bool write_grad, unsigned grid, unsigned thr, 
         step_kernel_aligned<RB, false><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in,
                                                             ag_in, S, N, fN, c);
     else if (write_grad)
-        step_kernel<P, RBG, true><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N,
-                                                       fN, c);
+        step_kernel<RBG, true><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N,
+                                                    fN, c);
     else
-        step_kernel<P, RBG, false><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S,
-                                                        N, fN, c);
+        step_kernel<RBG, false><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N,
+                                                     fN, c);
 }
 
 hipError_t launch_step(const PackTile *tiles, int64_t n, const DevEntry *ents,
@@ -1959,8 +2018,9 @@ hipError_t launch_step(const PackTile *tiles, int64_t n, const DevEntry *ents,
     if (n == 0) return hipSuccess;
     const float fN = static_cast<float>(N);
     const AdamwScalars c = to_scalars(scal);
-    // p, m, v read and written: six more streams per element besides the N rows
-    const RowSplit rsp = row_split(kTilePack, split_rows(kTilePack, N, 6), chunk_aligned);
+    // p, m, v read and written: six more streams per element besides the N rows;
+    // both variants run whole waves of 128 quads, so sub-ranges are powers of two
+    const RowSplit rsp = row_split(kTilePack, split_rows(kTilePack, N, 6), true);
     const int32_t sp = rsp.split;
     const int64_t sub = rsp.sub;
     const unsigned grid = grid_for(n, sp);
@@ -1982,10 +2042,10 @@ hipError_t launch_step(const PackTile *tiles, int64_t n, const DevEntry *ents,
         return hipGetLastError();
     }
     if (N <= 8)
-        launch_step_rb<P, FSDP_STEP_ROW_BATCH, FSDP_STEP_GEN_ROW_BATCH>(
+        launch_step_rb<FSDP_STEP_ROW_BATCH, FSDP_STEP_GEN_ROW_BATCH>(
             aligned, write_grad, grid, thr, st, tiles, n, sp, sub, ents, rs_in, ag_in, S, N, fN, c);
     else
-        launch_step_rb<P, FSDP_STEP_ROW_BATCH_WIDE, FSDP_STEP_ROW_BATCH_WIDE>(
+        launch_step_rb<FSDP_STEP_ROW_BATCH_WIDE, FSDP_STEP_ROW_BATCH_WIDE>(
             aligned, write_grad, grid, thr, st, tiles, n, sp, sub, ents, rs_in, ag_in, S, N, fN, c);
     return hipGetLastError();
 }
