@@ -19,7 +19,7 @@ namespace fsdp {
 hipError_t launch_pack(const PackTile *tiles, int64_t n, const DevEntry *ents,
                        uint16_t *ag_in, hipStream_t st);
 hipError_t launch_unpack(const UnpackTile *tiles, int64_t n, const DevEntry *ents,
-                         const uint16_t *ag_out, hipStream_t st);
+                         const uint16_t *ag_out, bool chunk_aligned, hipStream_t st);
 hipError_t launch_reduce(const ReduceTile *tiles, int64_t n, const DevEntry *ents,
                          const uint16_t *rs_in, int64_t S, int32_t N, bool chunk_aligned,
                          hipStream_t st);
@@ -467,15 +467,15 @@ hipError_t do_pack(const fsdp_plan *p, uint16_t *ag_in, hipStream_t st) {
                              ag_in, st);
 }
 
-hipError_t do_unpack(const fsdp_plan *p, const uint16_t *ag_out, hipStream_t st) {
-    return fsdp::launch_unpack(p->d_unpack, static_cast<int64_t>(p->L.unpack.size()),
-                               p->d_entries, ag_out, st);
-}
-
 // Every row piece starts 16-byte aligned: the offsets allow it and the
 // [N, S] buffer itself is 16-byte aligned.
 bool chunk_aligned(const fsdp_plan *p, const void *rows) {
     return p->L.offsets8 && (reinterpret_cast<uintptr_t>(rows) & 15u) == 0;
+}
+
+hipError_t do_unpack(const fsdp_plan *p, const uint16_t *ag_out, hipStream_t st) {
+    return fsdp::launch_unpack(p->d_unpack, static_cast<int64_t>(p->L.unpack.size()),
+                               p->d_entries, ag_out, chunk_aligned(p, ag_out), st);
 }
 
 hipError_t do_reduce(const fsdp_plan *p, const uint16_t *rs_in, hipStream_t st) {

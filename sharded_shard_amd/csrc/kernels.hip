@@ -98,8 +98,26 @@
 #ifndef FSDP_STEP_OUT_NT
 #define FSDP_STEP_OUT_NT 0
 #endif
+// copy-out blocks: 2048 elements over 128 threads when every row piece is
+// 16-byte aligned, 4096 over 256 otherwise (7B shape: 128 threads 6.33-6.60
+// TB/s, 64 threads 6.18-6.52, 256 threads 6.05-6.42, 512 threads 6.12-6.36;
+// misaligned ragged rows: 256 threads 5.77, 128 threads 5.62-5.68)
 #ifndef FSDP_UNPACK_SUB
-#define FSDP_UNPACK_SUB 4096
+#define FSDP_UNPACK_SUB 2048
+#endif
+#ifndef FSDP_UNPACK_THREADS
+#define FSDP_UNPACK_THREADS 128
+#endif
+#ifndef FSDP_UNPACK_MIS_SUB
+#define FSDP_UNPACK_MIS_SUB 4096
+#endif
+#ifndef FSDP_UNPACK_MIS_THREADS
+#define FSDP_UNPACK_MIS_THREADS 256
+#endif
+// 16-byte chunks each lane of an aligned copy loads before storing them (4
+// or 8 with correspondingly larger blocks measured 9-16% slower)
+#ifndef FSDP_UNPACK_UNROLL
+#define FSDP_UNPACK_UNROLL 2
 #endif
 #ifndef FSDP_ADAMW_SUB
 #define FSDP_ADAMW_SUB 4096
@@ -148,6 +166,10 @@
 #endif
 #ifndef FSDP_REDUCE_WIDE_MIN_N
 #define FSDP_REDUCE_WIDE_MIN_N 16
+#endif
+// threads per block of the fused step below the wide kernel (at most kBlock)
+#ifndef FSDP_STEP_THREADS
+#define FSDP_STEP_THREADS 256
 #endif
 #ifndef FSDP_STEP_WAVES
 #define FSDP_STEP_WAVES 6
@@ -348,7 +370,8 @@ __device__ __forceinline__ void sub_range(int64_t vt, int32_t split, int64_t sub
 // copy-out: [N, S] bf16 -> full parameters
 // ---------------------------------------------------------------------------
 
-template <int POL>
+// TB threads per block (whole waves).
+template <int POL, int TB = kBlock>
 __device__ __forceinline__ void copy_run_bf16(uint16_t *__restrict__ dst,
                                               const uint16_t *__restrict__ src, int64_t len) {
     constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
@@ -363,16 +386,21 @@ __device__ __forceinline__ void copy_run_bf16(uint16_t *__restrict__ dst,
     if (k == 0) {
         // raw buffer loads from one SGPR descriptor per run (measured faster
         // than per-lane 64-bit addresses on MI355X)
+        // FSDP_UNPACK_UNROLL chunks in flight per lane before their stores
+        constexpr int U = FSDP_UNPACK_UNROLL;
         const char *sb = reinterpret_cast<const char *>(s);
         const uint32_t nb = static_cast<uint32_t>(nvec) << 4;
         int64_t v = tid;
-        for (; v + kBlock < nvec; v += 2 * kBlock) {
-            const u32x4 x0 = bload16<LN>(sb, static_cast<uint32_t>(v) << 4, nb);
-            const u32x4 x1 = bload16<LN>(sb, static_cast<uint32_t>(v + kBlock) << 4, nb);
-            stp<SN>(dv + v, x0);
-            stp<SN>(dv + v + kBlock, x1);
+        for (; v + (U - 1) * TB < nvec; v += U * TB) {
+            u32x4 x[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                x[u] = bload16<LN>(sb, static_cast<uint32_t>(v + u * TB) << 4, nb);
+#pragma unroll
+            for (int u = 0; u < U; ++u) stp<SN>(dv + v + u * TB, x[u]);
         }
-        if (v < nvec) stp<SN>(dv + v, bload16<LN>(sb, static_cast<uint32_t>(v) << 4, nb));
+        for (; v < nvec; v += TB)
+            stp<SN>(dv + v, bload16<LN>(sb, static_cast<uint32_t>(v) << 4, nb));
     } else {
         // Every aligned 16-byte source chunk is read once: a lane's second
         // chunk is the next lane's first (DPP), and lane 63 of each wave
@@ -383,8 +411,8 @@ __device__ __forceinline__ void copy_run_bf16(uint16_t *__restrict__ dst,
         const uint32_t nb = (k + 2 * static_cast<uint32_t>(len - head) + 15u) & ~15u;
         const uint32_t lane = tid & 63;
         const bool last = lane == 63;
-        for (int64_t w0 = tid - lane; w0 < nvec; w0 += 2 * kBlock) {
-            const int64_t v0 = w0 + lane, v1 = v0 + kBlock;
+        for (int64_t w0 = tid - lane; w0 < nvec; w0 += 2 * TB) {
+            const int64_t v0 = w0 + lane, v1 = v0 + TB;
             const uint32_t o0 = static_cast<uint32_t>(v0) << 4, o1 = static_cast<uint32_t>(v1) << 4;
             const u32x4 a0 = bload16<LN>(al, o0, nb), a1 = bload16<LN>(al, o1, nb);
             const u32x4 h0 = bload16<LN>(al, last ? o0 + 16 : nb, nb);
@@ -402,8 +430,8 @@ __device__ __forceinline__ void copy_run_bf16(uint16_t *__restrict__ dst,
     if (tid < len - done) dst[done + tid] = src[done + tid];
 }
 
-template <int POL>
-__global__ __launch_bounds__(kBlock) void unpack_kernel(
+template <int POL, int TB>
+__global__ __launch_bounds__(TB) void unpack_kernel(
     const UnpackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
     const DevEntry *__restrict__ ents, const uint16_t *__restrict__ ag_out) {
     const int64_t L = sub;
@@ -414,7 +442,7 @@ __global__ __launch_bounds__(kBlock) void unpack_kernel(
         const UnpackTile tl = tiles[t];
         if (b >= tl.len) continue;
         const int64_t len = tl.len - b < L ? tl.len - b : L;
-        copy_run_bf16<POL>(ents[tl.entry].full + tl.dst + b, ag_out + tl.src + b, len);
+        copy_run_bf16<POL, TB>(ents[tl.entry].full + tl.dst + b, ag_out + tl.src + b, len);
     }
 }
 
@@ -1856,12 +1884,23 @@ hipError_t launch_pack(const PackTile *tiles, int64_t n, const DevEntry *ents, u
     return hipGetLastError();
 }
 
+// Row pieces 16-byte aligned: FSDP_UNPACK_THREADS threads per block over
+// FSDP_UNPACK_SUB elements; otherwise FSDP_UNPACK_MIS_THREADS over
+// FSDP_UNPACK_MIS_SUB (both correct for any alignment; measured per case).
 hipError_t launch_unpack(const UnpackTile *tiles, int64_t n, const DevEntry *ents,
-                         const uint16_t *ag_out, hipStream_t st) {
+                         const uint16_t *ag_out, bool chunk_aligned, hipStream_t st) {
     if (n == 0) return hipSuccess;
-    const int32_t sp = split_for(kTileUnpack, FSDP_UNPACK_SUB);
-    unpack_kernel<FSDP_UNPACK_POL>
-        <<<grid_for(n, sp), kBlock, 0, st>>>(tiles, n, sp, kTileUnpack / sp, ents, ag_out);
+    if (chunk_aligned) {
+        const int32_t sp = split_for(kTileUnpack, FSDP_UNPACK_SUB);
+        unpack_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_THREADS>
+            <<<grid_for(n, sp), FSDP_UNPACK_THREADS, 0, st>>>(tiles, n, sp, kTileUnpack / sp,
+                                                              ents, ag_out);
+    } else {
+        const int32_t sp = split_for(kTileUnpack, FSDP_UNPACK_MIS_SUB);
+        unpack_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_MIS_THREADS>
+            <<<grid_for(n, sp), FSDP_UNPACK_MIS_THREADS, 0, st>>>(tiles, n, sp, kTileUnpack / sp,
+                                                                  ents, ag_out);
+    }
     return hipGetLastError();
 }
 
@@ -2024,7 +2063,7 @@ hipError_t launch_step(const PackTile *tiles, int64_t n, const DevEntry *ents,
     const int32_t sp = rsp.split;
     const int64_t sub = rsp.sub;
     const unsigned grid = grid_for(n, sp);
-    const unsigned thr = row_threads(sub);
+    const unsigned thr = row_threads(sub) < FSDP_STEP_THREADS ? row_threads(sub) : FSDP_STEP_THREADS;
     const bool aligned = chunk_aligned;
     constexpr int P = FSDP_STEP_POL;
     if (aligned && N >= FSDP_STEP_WIDE_MIN_N) {
