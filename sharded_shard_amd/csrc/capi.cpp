@@ -30,7 +30,7 @@ hipError_t launch_step(const PackTile *tiles, int64_t n, const DevEntry *ents,
                        const float scal[8], bool write_grad, bool chunk_aligned,
                        hipStream_t st);
 hipError_t launch_rspack(const PackTile *tiles, int64_t n, const DevEntry *ents, void *out,
-                         bool f32, hipStream_t st);
+                         bool f32, bool chunk_aligned, hipStream_t st);
 hipError_t launch_reduce_f32(const ReduceTile *tiles, int64_t n, const DevEntry *ents,
                              const float *rs_in, int64_t S, int32_t N, bool chunk_aligned,
                              hipStream_t st);
@@ -631,7 +631,7 @@ fsdp_status fsdp_pack_reduce_scatter(const fsdp_plan *p, void *rs_out, int32_t d
     if ((s = check_device(p)) != FSDP_OK) return s;
     return launched(fsdp::launch_rspack(p->d_rspack, static_cast<int64_t>(p->L.rspack.size()),
                                         p->d_entries, rs_out, dtype == FSDP_DTYPE_F32,
-                                        static_cast<hipStream_t>(stream)),
+                                        chunk_aligned(p, rs_out), static_cast<hipStream_t>(stream)),
                     "fsdp_pack_reduce_scatter: launch");
 }
 

@@ -99,7 +99,9 @@
 #define FSDP_STEP_OUT_NT 0
 #endif
 // copy-out blocks: 2048 elements over 128 threads when every row piece is
-// 16-byte aligned, 4096 over 256 otherwise (7B shape: 128 threads 6.33-6.60
+// 16-byte aligned, 4096 over 256 otherwise; the other two-byte copies (bf16
+// reduce-scatter copy-in, resharding) and the FP8 copy-out (4096 bytes) take
+// the 128-thread shape (7B shape: 128 threads 6.33-6.60
 // TB/s, 64 threads 6.18-6.52, 256 threads 6.05-6.42, 512 threads 6.12-6.36;
 // misaligned ragged rows: 256 threads 5.77, 128 threads 5.62-5.68)
 #ifndef FSDP_UNPACK_SUB
@@ -208,7 +210,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBlock = 256;
+#ifndef FSDP_BLOCK
+#define FSDP_BLOCK 256
+#endif
+constexpr int kBlock = FSDP_BLOCK;
 
 // ---------------------------------------------------------------------------
 // small helpers
@@ -447,8 +452,8 @@ __global__ __launch_bounds__(TB) void unpack_kernel(
 }
 
 // Resharding: runs of 2-byte units between absolute addresses.
-template <int POL>
-__global__ __launch_bounds__(kBlock) void copy_runs_kernel(const CopyTile *__restrict__ tiles,
+template <int POL, int TB>
+__global__ __launch_bounds__(TB) void copy_runs_kernel(const CopyTile *__restrict__ tiles,
                                                            int64_t n_tiles, int32_t split,
                                                            int64_t sub) {
     const int64_t L = sub;
@@ -459,7 +464,7 @@ __global__ __launch_bounds__(kBlock) void copy_runs_kernel(const CopyTile *__res
         const CopyTile tl = tiles[t];
         if (b >= tl.len) continue;
         const int64_t len = tl.len - b < L ? tl.len - b : L;
-        copy_run_bf16<POL>(tl.dst + b, tl.src + b, len);
+        copy_run_bf16<POL, TB>(tl.dst + b, tl.src + b, len);
     }
 }
 
@@ -952,8 +957,8 @@ __global__ __launch_bounds__(kBlock) FSDP_ADAMW_ATTR void adamw_kernel(
 // reduce-scatter copy-in: full bf16 gradients -> [N, S] (bf16 or fp32)
 // ---------------------------------------------------------------------------
 
-template <int POL>
-__global__ __launch_bounds__(kBlock) void rspack_bf16_kernel(
+template <int POL, int TB>
+__global__ __launch_bounds__(TB) void rspack_bf16_kernel(
     const PackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
     const DevEntry *__restrict__ ents, uint16_t *__restrict__ out) {
     const int64_t L = sub;
@@ -967,7 +972,7 @@ __global__ __launch_bounds__(kBlock) void rspack_bf16_kernel(
         int64_t valid = tl.valid - b;
         valid = valid < 0 ? 0 : (valid > len ? len : valid);
         uint16_t *dst = out + tl.dst + b;
-        if (valid > 0) copy_run_bf16<POL>(dst, ents[tl.entry].full_grad + tl.src + b, valid);
+        if (valid > 0) copy_run_bf16<POL, TB>(dst, ents[tl.entry].full_grad + tl.src + b, valid);
         zero_bf16<(POL >> 1) & 1>(dst, valid, len);
     }
 }
@@ -1203,7 +1208,7 @@ __global__ __launch_bounds__(kBlock) void pack_fp8_kernel(
     }
 }
 
-template <int POL>
+template <int POL, int TB = kBlock>
 __device__ __forceinline__ void copy_run_u8(uint8_t *__restrict__ dst, const uint8_t *__restrict__ src,
                                             int64_t len) {
     constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
@@ -1221,12 +1226,12 @@ __device__ __forceinline__ void copy_run_u8(uint8_t *__restrict__ dst, const uin
     const char *al = reinterpret_cast<const char *>(s) - k;
     const uint32_t nb = (k + static_cast<uint32_t>(len - head) + 15u) & ~15u;
     if (k == 0) {
-        for (int64_t v = tid; v < nvec; v += kBlock)
+        for (int64_t v = tid; v < nvec; v += TB)
             stp<SN>(dv + v, bload16<LN>(al, static_cast<uint32_t>(v) << 4, nb));
     } else {
         const uint32_t lane = tid & 63;
         const bool last = lane == 63;
-        for (int64_t w0 = tid - lane; w0 < nvec; w0 += kBlock) {
+        for (int64_t w0 = tid - lane; w0 < nvec; w0 += TB) {
             const int64_t v = w0 + lane;
             const uint32_t o = static_cast<uint32_t>(v) << 4;
             const u32x4 a = bload16<LN>(al, o, nb);
@@ -1240,8 +1245,8 @@ __device__ __forceinline__ void copy_run_u8(uint8_t *__restrict__ dst, const uin
     if (tid < len - done) dst[done + tid] = src[done + tid];
 }
 
-template <int POL>
-__global__ __launch_bounds__(kBlock) void unpack_fp8_kernel(
+template <int POL, int TB>
+__global__ __launch_bounds__(TB) void unpack_fp8_kernel(
     const UnpackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
     const DevEntry *__restrict__ ents, const uint8_t *__restrict__ ag_out) {
     const int64_t L = sub;
@@ -1252,7 +1257,7 @@ __global__ __launch_bounds__(kBlock) void unpack_fp8_kernel(
         const UnpackTile tl = tiles[t];
         if (b >= tl.len) continue;
         const int64_t len = tl.len - b < L ? tl.len - b : L;
-        copy_run_u8<POL>(ents[tl.entry].full_fp8 + tl.dst + b, ag_out + tl.src + b, len);
+        copy_run_u8<POL, TB>(ents[tl.entry].full_fp8 + tl.dst + b, ag_out + tl.src + b, len);
     }
 }
 
@@ -1942,8 +1947,8 @@ hipError_t launch_adamw(const EwTile *tiles, int64_t n, const DevEntry *ents,
 hipError_t launch_copy_runs(const CopyTile *tiles, int64_t n, hipStream_t st) {
     if (n == 0) return hipSuccess;
     const int32_t sp = split_for(kTileUnpack, FSDP_UNPACK_SUB);
-    copy_runs_kernel<FSDP_UNPACK_POL>
-        <<<grid_for(n, sp), kBlock, 0, st>>>(tiles, n, sp, kTileUnpack / sp);
+    copy_runs_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_THREADS>
+        <<<grid_for(n, sp), FSDP_UNPACK_THREADS, 0, st>>>(tiles, n, sp, kTileUnpack / sp);
     return hipGetLastError();
 }
 
@@ -1961,8 +1966,9 @@ hipError_t launch_unpack_fp8(const UnpackTile *tiles, int64_t n, const DevEntry 
     if (n == 0) return hipSuccess;
     // 16 bytes per lane move 16 elements: twice the elements per block of bf16
     const int32_t sp = split_for(kTileUnpack, 2 * FSDP_UNPACK_SUB);
-    unpack_fp8_kernel<FSDP_UNPACK_POL><<<grid_for(n, sp), kBlock, 0, st>>>(
-        tiles, n, sp, kTileUnpack / sp, ents, ag_out);
+    unpack_fp8_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_THREADS>
+        <<<grid_for(n, sp), FSDP_UNPACK_THREADS, 0, st>>>(tiles, n, sp, kTileUnpack / sp, ents,
+                                                          ag_out);
     return hipGetLastError();
 }
 
@@ -1999,17 +2005,23 @@ hipError_t launch_rspack_acc(const PackTile *tiles, int64_t n, const DevEntry *e
     return hipGetLastError();
 }
 
+// Block shapes as the copy-out's, chosen by whether every row piece of the
+// output is 16-byte aligned.
 hipError_t launch_rspack(const PackTile *tiles, int64_t n, const DevEntry *ents, void *out,
-                         bool f32, hipStream_t st) {
+                         bool f32, bool chunk_aligned, hipStream_t st) {
     if (n == 0) return hipSuccess;
-    const int32_t sp = split_for(kTileUnpack, FSDP_UNPACK_SUB);
+    const int32_t sp = split_for(kTileUnpack, chunk_aligned ? FSDP_UNPACK_SUB : FSDP_UNPACK_MIS_SUB);
     const unsigned grid = grid_for(n, sp);
     if (f32)
         rspack_f32_kernel<FSDP_RSPACK_F32_POL><<<grid, kBlock, 0, st>>>(
             tiles, n, sp, kTileUnpack / sp, ents, static_cast<float *>(out));
-    else
-        rspack_bf16_kernel<FSDP_UNPACK_POL><<<grid, kBlock, 0, st>>>(
+    else if (chunk_aligned)
+        rspack_bf16_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_THREADS><<<grid, FSDP_UNPACK_THREADS, 0, st>>>(
             tiles, n, sp, kTileUnpack / sp, ents, static_cast<uint16_t *>(out));
+    else
+        rspack_bf16_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_MIS_THREADS>
+            <<<grid, FSDP_UNPACK_MIS_THREADS, 0, st>>>(tiles, n, sp, kTileUnpack / sp, ents,
+                                                       static_cast<uint16_t *>(out));
     return hipGetLastError();
 }
 
