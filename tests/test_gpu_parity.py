@@ -212,15 +212,17 @@ def test_unpack_bit_exact_with_guards(case, align):
         g.close()
 
 
-def test_unpack_misaligned_full_destinations():
-    """Full tensors at every 2-byte offset modulo 16."""
+@pytest.mark.parametrize("align", [1, 8])
+def test_unpack_misaligned_full_destinations(align):
+    """Full tensors at every 2-byte offset modulo 16; with align 8 every row
+    piece of the source is 16-byte aligned (the copy-out's other block shape)."""
     shapes, n = [(37, 11), (999,), (8, 64)], 5
-    plan = O.plan(shapes, n, 2)
-    ag = _rand_ag(n, plan.S, ("mis",))
+    plan = O.plan(shapes, n, 2, align)
+    ag = _rand_ag(n, plan.S, ("mis", align))
     src = torch.from_numpy(ag.reshape(-1).view(np.int16)).to(DEV)
     ref = O.unpack(plan, ag)
     for shift in range(8):
-        g = ShardedGroup(shapes, n, 2, bind=False)
+        g = ShardedGroup(shapes, n, 2, align, bind=False)
         arena = torch.zeros(sum(r * c + 9 for r, c in zip(g.rows, g.cols)) + 16,
                             dtype=torch.int16, device=DEV)
         views, o = [], shift
@@ -717,11 +719,12 @@ def test_pack_reduce_scatter_bit_exact(case, align, dtype):
     g.close()
 
 
-def test_pack_reduce_scatter_misaligned_full_grads_and_roundtrip():
+@pytest.mark.parametrize("align", [1, 8])
+def test_pack_reduce_scatter_misaligned_full_grads_and_roundtrip(align):
     shapes, n = [(37, 11), (999,), (8, 64), (1, 5)], 5
-    plan = O.plan(shapes, n, 2)
+    plan = O.plan(shapes, n, 2, align)
     for shift in range(8):
-        g = ShardedGroup(shapes, n, 2)
+        g = ShardedGroup(shapes, n, 2, align)
         arena = torch.zeros(sum(r * c + 9 for r, c in zip(g.rows, g.cols)) + 16, dtype=torch.int16, device=DEV)
         views, o = [], shift
         for i, (r_, c_) in enumerate(zip(g.rows, g.cols)):
