@@ -509,6 +509,15 @@ def main():
                      "algorithmic_bytes_per_launch": dom_bytes_per_launch},
         "kernels": kernels,
     }
+    if per.get("unpack"):
+        # derived, not timed: with reshard-after-forward a step all-gathers
+        # every group twice (forward and backward), so one more copy-out per
+        # group is added at its measured per-step time
+        t2 = ms_step + per["unpack"]
+        out["two_allgather_variant"] = {
+            "derived": True, "ms_per_step": t2, "params_per_s": V / (t2 * 1e-3),
+            "effective_GBps": (step_bytes + byts["unpack"]) / (t2 * 1e-3) / 1e9,
+            "hbm_frac": (step_bytes + byts["unpack"]) / (t2 * 1e-3) / 1e9 / HBM_PEAK_GBPS}
     if not args.no_next:
         out["next_kernels"] = measure_next(groups, n, rs_arena[0], full_arena, stream,
                                            max(1, args.breakdown_steps))
