@@ -9,6 +9,15 @@ if ROOT not in sys.path:
 
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 
+# tests/test_oracle_mutations.py runs the oracle's pins in child processes
+# with one planted mistake each, named by this variable; it is never set in
+# an ordinary run
+_MUTATION = os.environ.get("FSDP_ORACLE_MUTATION")
+if _MUTATION:
+    import oracle_mutations
+
+    oracle_mutations.apply(_MUTATION)
+
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
