@@ -84,7 +84,7 @@ def _unpack_from_row0(p, ag_out):
     return fulls
 
 
-def _reduce_variant(drop_last=False, divide=True):
+def _reduce_variant(drop_last=False, divide=True, reciprocal=False):
     def reduce(p, rs_in):
         rs = np.asarray(rs_in, dtype=np.uint16).reshape(p.world, p.S)
         grads = []
@@ -93,9 +93,25 @@ def _reduce_variant(drop_last=False, divide=True):
             acc = O.bf16_to_f32(rs[0, sl]).copy()
             for j in range(1, p.world - (1 if drop_last else 0)):
                 acc = acc + O.bf16_to_f32(rs[j, sl])
-            grads.append((acc / F32(p.world) if divide else acc).astype(F32))
+            if reciprocal:
+                acc = acc * (F32(1.0) / F32(p.world))
+            elif divide:
+                acc = acc / F32(p.world)
+            grads.append(acc.astype(F32))
         return grads
     return reduce
+
+
+def _reduce_f32_times_reciprocal(p, rs_in):
+    rs = np.asarray(rs_in, dtype=F32).reshape(p.world, p.S)
+    grads = []
+    for e in p.entries:
+        sl = slice(e.shard_offset, e.shard_offset + e.valid_numel)
+        acc = rs[0, sl].copy()
+        for j in range(1, p.world):
+            acc = acc + rs[j, sl]
+        grads.append((acc * (F32(1.0) / F32(p.world))).astype(F32))
+    return grads
 
 
 _orig_scalars = O.adamw_scalars
@@ -183,6 +199,8 @@ MUTATIONS = {
     "unpack_from_row0": ("unpack", _unpack_from_row0),
     "reduce_drop_last_rank": ("reduce", _reduce_variant(drop_last=True)),
     "reduce_no_divide": ("reduce", _reduce_variant(divide=False)),
+    "reduce_times_reciprocal": ("reduce", _reduce_variant(reciprocal=True)),
+    "reduce_f32_times_reciprocal": ("reduce_f32", _reduce_f32_times_reciprocal),
     "adamw_no_weight_decay": ("adamw_scalars", _scalars_variant(no_decay=True)),
     "adamw_no_bias_correction1": ("adamw_scalars", _scalars_variant(no_bc1=True)),
     "adamw_no_sqrt_bias_correction2": ("adamw_scalars", _scalars_variant(no_sqrt_bc2=True)),

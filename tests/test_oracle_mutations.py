@@ -6,7 +6,8 @@ run must end with failed tests, not with an error of the harness).  The
 mutations are plausible mistakes in writing the oracle from the pages: a
 wrong chunk rule, a lost row, alignment ignored, rounding half up or by
 truncation, padding left unset, every piece read from row 0, a rank's
-contribution dropped, no division by N, each AdamW term dropped or swapped,
+contribution dropped, no division by N or a multiply by a rounded 1/N (bf16
+and fp32 contributions), each AdamW term dropped or swapped,
 the update's sign flipped, eps inside the square root, optimizer state not
 sharded in the accounting, FP8 overflow to NaN, resharding offsets taken
 from the wrong side.  CPU only.

@@ -385,6 +385,40 @@ def test_reduce_within_fp32_error_bound_of_exact_sum(n):
                 assert abs(float(g[i]) - exact) <= bound * 1.0001
 
 
+def _nearest_f32(fr):
+    """The fp32 nearest to an exact rational, ties to the even bit pattern
+    (normal range), by comparing exact distances of the candidates."""
+    from fractions import Fraction
+    c = np.float32(float(fr))
+    cands = [np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))]
+    return min(cands, key=lambda y: (abs(Fraction(float(y)) - fr),
+                                     int(np.array([y], dtype=F32).view(np.uint32)[0]) & 1))
+
+
+@pytest.mark.parametrize("n", [3, 6, 7, 12])
+def test_reduce_divides_once_correctly_rounded(n):
+    """With contributions whose fp32 sums are exact (small integers times a
+    power of two), the only rounding left is the division by N: the result
+    must be the correctly rounded quotient of the exact sum, which a multiply
+    by a rounded 1/N misses for some sums.  The same holds for fp32
+    contributions."""
+    from fractions import Fraction
+    p = O.plan([(4096,)], n, 0)
+    rng = np.random.default_rng(1000 + n)
+    k = rng.integers(-256, 257, size=(n, p.S)).astype(np.float32)
+    scale = np.float32(2.0 ** -7)
+    vals = torch.from_numpy(k * scale)
+    rs = vals.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert torch.equal(vals.to(torch.bfloat16).float(), vals)       # bf16-exact inputs
+    g = O.reduce(p, rs)[0]
+    g32 = O.reduce_f32(p, k * scale)[0]
+    for i in range(p.S):
+        exact = Fraction(int(k[:, i].sum())) * Fraction(1, 128) / n
+        want = _nearest_f32(exact) if exact != 0 else np.float32(0.0)
+        assert g[i] == want, (n, i, float(exact))
+        assert g32[i] == want, (n, i, float(exact))
+
+
 def test_reduce_matches_torch_mean_and_never_reads_padding():
     n = 6
     shapes = [(1408 // 8, 16), (2048 // 8,), (1, 16), (1,)]
