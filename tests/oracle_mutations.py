@@ -188,6 +188,90 @@ def _reshard_runs_dst_offset_zero(rows, cols, world_src, world_dst, rank_dst):
     return runs
 
 
+def _bf16_no_nan_case(x):
+    # rounding applied to NaNs too: a NaN with only low payload bits becomes inf
+    a = np.ascontiguousarray(np.asarray(x, dtype=F32))
+    b = a.view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _accumulate_reset_adds_zero(acc, full_grads, reset):
+    # the first microbatch adds to +0.0 instead of storing the widening
+    out = []
+    for i, g in enumerate(full_grads):
+        x = O.bf16_to_f32(np.asarray(g, dtype=np.uint16).reshape(-1))
+        base = np.zeros_like(x) if reset else np.asarray(acc[i], dtype=F32).reshape(-1)
+        out.append((base + x).astype(F32))
+    return out
+
+
+def _rspack_rows_reversed(p, full_grads):
+    # chunk j written to row N-1-j
+    out = np.zeros((p.world, p.S), dtype=np.uint16)
+    for e, g in zip(p.entries, full_grads):
+        flat = np.asarray(g, dtype=np.uint16).reshape(-1)
+        for j in range(p.world):
+            b, lr = O.rows_of_rank(e.rows, p.world, j)
+            n = lr * e.cols
+            out[p.world - 1 - j, e.shard_offset:e.shard_offset + n] = flat[b * e.cols:b * e.cols + n]
+    return out
+
+
+def _adamw_v_without_square(param, grad, exp_avg, exp_avg_sq, step, lr, beta1, beta2, eps,
+                            weight_decay):
+    s = O.adamw_scalars(lr, beta1, beta2, eps, weight_decay, step)
+    g = grad
+    p = param * s.decay
+    m = exp_avg * s.beta1 + s.one_minus_beta1 * g
+    v = exp_avg_sq * s.beta2 + s.one_minus_beta2 * np.abs(g)
+    d = np.sqrt(v) / s.bc2_sqrt + s.eps
+    param[...] = p - s.step_size * (m / d)
+    exp_avg[...] = m
+    exp_avg_sq[...] = v
+
+
+def _amax_signed(master_shards):
+    # largest signed value instead of the largest magnitude
+    out = np.zeros(len(master_shards), dtype=F32)
+    for i, m in enumerate(master_shards):
+        b = np.asarray(m, dtype=F32).reshape(-1)
+        out[i] = b.max() if b.size else 0
+    return out
+
+
+def _e4m3_ties_away(x):
+    # ties rounded away from zero instead of to even (normal range)
+    a = np.ascontiguousarray(np.asarray(x, dtype=F32))
+    code = _orig_e4m3(a)
+    u = a.view(np.uint32).astype(np.int64)
+    mag = u & 0x7FFFFFFF
+    tie = ((mag & 0xFFFFF) == 0x80000) & (mag >= 0x3C800000) & (mag < 0x43E00000)
+    up = ((mag >> 20) & 1) == 0      # ties-to-even rounded these down
+    return np.where(tie & up, code + 1, code).astype(np.uint8)
+
+
+_orig_reshard_runs = O.reshard_runs
+
+
+def _reshard_runs_skip_last_source(rows, cols, world_src, world_dst, rank_dst):
+    # the last source rank's rows never read (a loop bound one short)
+    return [r for r in _orig_reshard_runs(rows, cols, world_src, world_dst, rank_dst)
+            if r[0] != world_src - 1 or world_src == 1]
+
+
+def _state_grads_unsharded(n_params, world, zero_stage):
+    # stage 2 forgets to shard the gradients
+    if zero_stage not in (0, 1, 2, 3) or world < 1:
+        raise ValueError("stage in 0..3, world >= 1")
+    params, grads, optim = 2.0 * n_params, 2.0 * n_params, 12.0 * n_params
+    if zero_stage >= 1:
+        optim /= world
+    if zero_stage >= 3:
+        params /= world
+        grads /= world
+    return params + grads + optim
+
+
 MUTATIONS = {
     "chunk_floor_plus_one": ("chunk_rows", _chunk_floor_plus_one),
     "rows_even_split": ("rows_of_rank", _rows_even_split),
@@ -210,6 +294,14 @@ MUTATIONS = {
     "state_optimizer_unsharded": ("state_bytes", _state_optimizer_unsharded),
     "e4m3_overflow_to_nan": ("e4m3_sat", _e4m3_overflow_to_nan),
     "reshard_dst_offset_wrong": ("reshard_runs", _reshard_runs_dst_offset_zero),
+    "bf16_no_nan_case": ("bf16_rne", _bf16_no_nan_case),
+    "accumulate_reset_adds_zero": ("accumulate_grad", _accumulate_reset_adds_zero),
+    "rspack_rows_reversed": ("pack_reduce_scatter", _rspack_rows_reversed),
+    "adamw_v_without_square": ("adamw", _adamw_v_without_square),
+    "amax_signed": ("amax", _amax_signed),
+    "e4m3_ties_away": ("e4m3_sat", _e4m3_ties_away),
+    "reshard_skip_last_source": ("reshard_runs", _reshard_runs_skip_last_source),
+    "state_grads_unsharded": ("state_bytes", _state_grads_unsharded),
 }
 
 

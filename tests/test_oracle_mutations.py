@@ -9,8 +9,11 @@ truncation, padding left unset, every piece read from row 0, a rank's
 contribution dropped, no division by N or a multiply by a rounded 1/N (bf16
 and fp32 contributions), each AdamW term dropped or swapped,
 the update's sign flipped, eps inside the square root, optimizer state not
-sharded in the accounting, FP8 overflow to NaN, resharding offsets taken
-from the wrong side.  CPU only.
+sharded in the accounting (optimizer state, gradients), FP8 overflow to
+NaN or ties away from zero, resharding offsets taken from the wrong side or
+the last source rank skipped, NaNs rounded like numbers in the bf16 cast,
+accumulation restarted by adding to +0, the reduce-scatter rows reversed,
+the second moment without the square, amax of signed values.  CPU only.
 """
 import os
 import subprocess

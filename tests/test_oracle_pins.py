@@ -842,3 +842,10 @@ def test_amax_matches_torch():
     for g, s in zip(got, shards):
         assert g == (np.abs(s).max() if s.size else 0.0)
     assert np.isnan(O.amax([np.array([1.0, np.nan, -3.0], F32)])[0])
+    # the largest magnitude can be negative; -0 has magnitude +0
+    hand = [np.array([3.0, -7.5, 2.0], F32), np.array([-1e-30], F32), np.array([-0.0, 0.0], F32),
+            np.array([-np.inf, 1.0], F32)]
+    got = O.amax(hand)
+    assert got.view(np.uint32).tolist() == np.array([7.5, 1e-30, 0.0, np.inf], F32).view(np.uint32).tolist()
+    for g, s in zip(got, hand):
+        assert g == torch.from_numpy(s).abs().max().item()
