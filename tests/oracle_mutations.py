@@ -272,6 +272,47 @@ def _state_grads_unsharded(n_params, world, zero_stage):
     return params + grads + optim
 
 
+def _pack_fp8_divides_by_scale(p, master_shards, scales):
+    # the tensor-wise scale divided instead of multiplied
+    out = np.zeros(p.S, dtype=np.uint8)
+    for e, m, sc in zip(p.entries, master_shards, scales):
+        flat = np.asarray(m, dtype=F32).reshape(-1)
+        out[e.shard_offset:e.shard_offset + e.valid_numel] = O.e4m3_sat(flat / F32(sc))
+    return out
+
+
+_orig_e4m3_to_f32 = O.e4m3_to_f32
+
+
+def _e4m3_decode_bias8(u8):
+    # exponent bias 8 instead of 7: every value halved
+    return (_orig_e4m3_to_f32(u8) * F32(0.5)).astype(F32)
+
+
+def _plan_reverse_order(shapes, world, rank, align=1):
+    # pieces laid out in reverse registration order
+    pl = _orig_plan(list(shapes)[::-1], world, rank, align)
+    pl.entries = pl.entries[::-1]
+    return pl
+
+
+def _decay_without_lr(lr, beta1, beta2, eps, weight_decay, step):
+    # decoupled decay written as 1 - wd instead of 1 - lr * wd
+    s = _orig_scalars(lr, beta1, beta2, eps, weight_decay, step)
+    vals = dict(s.__dict__)
+    vals["decay"] = F32(1.0 - weight_decay)
+    return O.AdamWScalars(**vals)
+
+
+def _rows_begin_off_by_one(rows, world, j):
+    # every rank after the first starts one row late
+    b, lr = _orig_rows_of_rank(rows, world, j)
+    return (b + 1 if lr and j > 0 else b), lr
+
+
+_orig_rows_of_rank = O.rows_of_rank
+
+
 MUTATIONS = {
     "chunk_floor_plus_one": ("chunk_rows", _chunk_floor_plus_one),
     "rows_even_split": ("rows_of_rank", _rows_even_split),
@@ -302,6 +343,11 @@ MUTATIONS = {
     "e4m3_ties_away": ("e4m3_sat", _e4m3_ties_away),
     "reshard_skip_last_source": ("reshard_runs", _reshard_runs_skip_last_source),
     "state_grads_unsharded": ("state_bytes", _state_grads_unsharded),
+    "pack_fp8_divides_by_scale": ("pack_fp8", _pack_fp8_divides_by_scale),
+    "e4m3_decode_bias8": ("e4m3_to_f32", _e4m3_decode_bias8),
+    "plan_reverse_order": ("plan", _plan_reverse_order),
+    "adamw_decay_without_lr": ("adamw_scalars", _decay_without_lr),
+    "rows_begin_off_by_one": ("rows_of_rank", _rows_begin_off_by_one),
 }
 
 

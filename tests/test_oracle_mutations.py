@@ -13,7 +13,10 @@ sharded in the accounting (optimizer state, gradients), FP8 overflow to
 NaN or ties away from zero, resharding offsets taken from the wrong side or
 the last source rank skipped, NaNs rounded like numbers in the bf16 cast,
 accumulation restarted by adding to +0, the reduce-scatter rows reversed,
-the second moment without the square, amax of signed values.  CPU only.
+the second moment without the square, amax of signed values, the FP8
+scale divided, e4m3 decoded with bias 8, pieces in reverse registration
+order, decay without the learning rate, pieces starting a row late.  CPU
+only.
 """
 import os
 import subprocess
