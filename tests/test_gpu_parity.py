@@ -488,6 +488,92 @@ def test_fused_step_equals_separate_calls_and_oracle(case, write_grad):
         gb.close()
 
 
+# bf16 specials injected into gradient contributions: +-inf, NaN, +-max
+# finite (sums overflow), smallest and largest subnormals, -0, smallest normal
+_BF16_SPECIALS = [0x7F80, 0xFF80, 0x7FC0, 0x7F7F, 0xFF7F, 0x0001, 0x8001, 0x007F, 0x8000, 0x0080]
+# fp32 masters: zeros, near overflow, subnormals, infinities, NaN
+_F32_SPECIALS = [0.0, -0.0, 3.0e38, -3.0e38, 1e-45, -1e-40, 1e-30, float("inf"), float("-inf"),
+                 float("nan")]
+
+
+def _bf16_is_nan(u):
+    return ((u & 0x7F80) == 0x7F80) & ((u & 0x7F) != 0)
+
+
+def _same_f32_nan_ok(got, want, what):
+    """Bit-exact, except that any NaN matches any NaN: IEEE 754 leaves the sign
+    and payload of a NaN that an invalid operation creates to the machine."""
+    gn, wn = np.isnan(got), np.isnan(want)
+    assert np.array_equal(gn, wn), (what, int((gn != wn).sum()))
+    assert np.array_equal(got[~gn].view(np.uint32), want[~wn].view(np.uint32)), what
+
+
+def _same_bf16_nan_ok(got, want, what):
+    gn, wn = _bf16_is_nan(got), _bf16_is_nan(want)
+    assert np.array_equal(gn, wn), (what, int((gn != wn).sum()))
+    assert np.array_equal(got[~gn], want[~wn]), what
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+@pytest.mark.parametrize("n,align", [(3, 1), (6, 1), (8, 8), (16, 8), (64, 8)])
+def test_step_special_values_match_oracle(n, align, fused):
+    """Infinities, NaNs, overflowing sums, subnormals and signed zeros through
+    reduce, AdamW and the copy-in for 3 steps, on the misaligned, aligned and
+    wide kernels: every output bit-exact with the oracle, NaNs matched as
+    NaNs."""
+    shapes = [(37, 5), (64,), (130, 3), (9, 129), (1024, 16)]
+    r = n // 2
+    plan = O.plan(shapes, n, r, align)
+    g = ShardedGroup(shapes, n, r, align)
+    rng = np.random.default_rng(7000 + n)
+    masters = []
+    for i, e in enumerate(g.entries):
+        x = synth.normal_f32(e.valid_numel, 0.02, ("spec-m", n, i)).numpy().copy()
+        if x.size:
+            pos = rng.choice(x.size, size=min(x.size, len(_F32_SPECIALS)), replace=False)
+            x[pos] = np.array(_F32_SPECIALS[:pos.size], dtype=np.float32)
+        g.shard_view(g.master_flat, i).copy_(torch.from_numpy(x))
+        masters.append(x)
+    ms = [np.zeros_like(x) for x in masters]
+    vs = [np.zeros_like(x) for x in masters]
+    seen = set()
+    for t in (1, 2, 3):
+        rs = _rs_input(plan, n, ("spec-rs", n, t))
+        mask = ~_pad_mask(plan)
+        hit = (rng.random(rs.shape) < 0.2) & mask[None, :]
+        rs[hit] = rng.choice(np.array(_BF16_SPECIALS, dtype=np.uint16), size=int(hit.sum()))
+        # a few columns of subnormals in every row: subnormal sums and means
+        cols = rng.choice(np.flatnonzero(mask), size=4, replace=False)
+        rs[:, cols[:2]] = 0x0001
+        rs[:, cols[2:]] = 0x807F
+        d_rs = torch.from_numpy(rs.reshape(-1).view(np.int16)).to(DEV)
+        ag = torch.zeros(plan.S, dtype=torch.int16, device=DEV)
+        if fused:
+            g.step(d_rs, ag, t, write_grad=True, **HP)
+        else:
+            g.reduce(d_rs)
+            g.adamw(t, **HP)
+            g.pack(ag)
+        torch.cuda.synchronize()
+        with np.errstate(all="ignore"):
+            grads = O.reduce(plan, rs)
+            for x, gr, m, v in zip(masters, grads, ms, vs):
+                O.adamw(x, gr, m, v, t, **HP)
+            want_ag = O.pack(plan, masters)
+        for gr in grads:
+            a = np.abs(gr)
+            seen.update(k for k, hit in (("nan", np.isnan(gr).any()), ("inf", np.isinf(gr).any()),
+                                         ("sub", ((a > 0) & (a < 2.0 ** -126)).any())) if hit)
+        _same_bf16_nan_ok(u16(ag), want_ag, ("ag", n, t))
+        for i in range(len(shapes)):
+            _same_f32_nan_ok(f32(g.shard_view(g.grad_flat, i)), grads[i], ("g", n, t, i))
+            _same_f32_nan_ok(f32(g.shard_view(g.master_flat, i)), masters[i], ("p", n, t, i))
+            _same_f32_nan_ok(f32(g.shard_view(g.m_flat, i)), ms[i], ("m", n, t, i))
+            _same_f32_nan_ok(f32(g.shard_view(g.v_flat, i)), vs[i], ("v", n, t, i))
+    g.close()
+    assert seen == {"nan", "inf", "sub"}, seen     # the specials reached the reduction
+
+
 def test_fused_step_mixed_alignment_shards():
     """Shards whose pointers differ modulo 16 take the element-wise path."""
     shapes, n, r = [(41, 9), (777,), (3, 5)], 3, 1
