@@ -968,6 +968,56 @@ def test_accumulate_then_copy_in_matches_oracle(case):
     g.close()
 
 
+@pytest.mark.parametrize("n,align", [(6, 1), (8, 8), (64, 8)])
+def test_accumulate_and_reduce_f32_special_values(n, align):
+    """Infinities, NaNs, overflow and subnormals through the fp32
+    accumulation (3 microbatches), its copy-in and the fp32 reduction: bit
+    for bit with the oracle, NaNs created by an operation matched as NaNs."""
+    shapes = [(37, 5), (130, 3), (1024, 16)]
+    r = n // 2
+    plan = O.plan(shapes, n, r, align)
+    g = ShardedGroup(shapes, n, r, align)
+    g.bind_full_grad()
+    g.bind_grad_acc()
+    rng = np.random.default_rng(8000 + n)
+    acc = None
+    for k in range(3):
+        grads = []
+        for i in range(len(shapes)):
+            v = g.full_grad_view(i).view(-1)
+            x = synth.bf16_bits_to_u16(synth.normal_bf16_bits(v.numel(), 1e-3, ("accs", n, k, i)))
+            hit = rng.random(x.size) < 0.1
+            x[hit] = rng.choice(np.array(_BF16_SPECIALS, dtype=np.uint16), size=int(hit.sum()))
+            x[:4] = [0x0001, 0x807F, 0x7F7F, 0x7F7F]     # subnormals; a sum that overflows
+            v.copy_(torch.from_numpy(x.view(np.int16)))
+            grads.append(x)
+        g.accumulate_grad(reset=(k == 0))
+        with np.errstate(all="ignore"):
+            acc = O.accumulate_grad(acc, grads, reset=(k == 0))
+    torch.cuda.synchronize()
+    for i, want in enumerate(acc):
+        _same_f32_nan_ok(f32(g.grad_acc_view(i)).reshape(-1), want, ("acc", n, i))
+    want_rs = O.pack_reduce_scatter_acc(plan, acc)
+    rs = torch.zeros(n * plan.S, dtype=torch.float32, device=DEV)
+    g.pack_reduce_scatter_acc(rs)
+    torch.cuda.synchronize()
+    _same_f32_nan_ok(f32(rs), want_rs.reshape(-1), ("rs", n))
+    # the fp32 reduction of contributions holding every special value
+    rsf = want_rs.copy()
+    valid = ~_pad_mask(plan)
+    specials = np.array([np.inf, -np.inf, np.nan, 3e38, -3e38, 1e-45, -1e-40, -0.0], np.float32)
+    hit = (rng.random(rsf.shape) < 0.2) & valid[None, :]
+    rsf[hit] = rng.choice(specials, size=int(hit.sum()))
+    rsf[:, ~valid] = np.float32("nan")                  # padding is never read
+    g.reduce_f32(torch.from_numpy(rsf.reshape(-1)).to(DEV))
+    torch.cuda.synchronize()
+    with np.errstate(all="ignore"):
+        want_g = O.reduce_f32(plan, rsf)
+    for i, want in enumerate(want_g):
+        _same_f32_nan_ok(f32(g.shard_view(g.grad_flat, i)), want, ("g32", n, i))
+    g.close()
+
+
 def test_accumulate_misaligned_pointers_take_the_scalar_path():
     shapes = [(37, 11), (999,), (8, 64)]
     g = ShardedGroup(shapes, 2, 0, bind=True)
