@@ -266,6 +266,36 @@ def test_host_adamw_bit_exact_with_oracle(n_threads):
             assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), (n, n_threads)
 
 
+def test_host_adamw_special_values():
+    """Infinities, NaNs, subnormals, zeros and near-overflow values in the
+    master and the gradient: the host update equals the oracle bit for bit,
+    a NaN created by an operation matching any NaN."""
+    HP = dict(lr=3e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    specials = np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 3e38, -3e38, 1e-45, -1e-40, 1e-30],
+                        np.float32)
+    rng = np.random.default_rng(11)
+    n = 4099
+    p = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    hit = rng.random(n) < 0.2
+    p[hit] = rng.choice(specials, size=int(hit.sum()))
+    p[:specials.size] = specials
+    m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    ref = [p.copy(), m.copy(), v.copy()]
+    for t in (1, 2, 3):
+        g = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        hit = rng.random(n) < 0.2
+        g[hit] = rng.choice(specials, size=int(hit.sum()))
+        g[-specials.size:] = specials
+        capi.fsdp_adamw_host(p, g, m, v, step=t, n_threads=3, **HP)
+        with np.errstate(all="ignore"):
+            O.adamw(ref[0], g, ref[1], ref[2], t, **HP)
+    for a, b in zip((p, m, v), ref):
+        an, bn = np.isnan(a), np.isnan(b)
+        assert np.array_equal(an, bn)
+        assert np.array_equal(a[~an].view(np.uint32), b[~bn].view(np.uint32))
+    assert np.isnan(ref[0]).any() and np.isinf(ref[2]).any()
+
+
 def test_host_adamw_errors():
     x = np.zeros(4, np.float32)
     with pytest.raises(capi.FsdpError) as ei:
