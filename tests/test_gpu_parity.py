@@ -1079,6 +1079,29 @@ def test_pack_fp8_bit_exact(case):
         g.close()
 
 
+def test_pack_fp8_every_rounding_boundary():
+    """The FP8 cast on every fp32 upper half (sign, exponent and the top 7
+    mantissa bits: every kept-bit and round-bit combination of the normal and
+    subnormal E4M3 ranges, saturation, infinities and NaNs) times low halves
+    0, 1, 0x7FFF, 0x8000, 0x8001 and 0xFFFF (sticky bits), scale 1: equal to
+    the oracle byte for byte."""
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    lo = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32)
+    x = (hi[:, None] | lo[None, :]).reshape(-1).view(np.float32)
+    plan = O.plan([(x.size,)], 1, 0)
+    g = ShardedGroup([(x.size,)], 1, 0)
+    g.shard_view(g.master_flat, 0).copy_(torch.from_numpy(x))
+    out = torch.zeros(plan.S, dtype=torch.uint8, device=DEV)
+    g.pack_fp8(out, torch.ones(1, dtype=torch.float32, device=DEV))
+    torch.cuda.synchronize()
+    with np.errstate(all="ignore"):
+        want = O.pack_fp8(plan, [x], np.ones(1, np.float32))
+    got = u8(out)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, [(hex(int(x.view(np.uint32)[i])), int(got[i]), int(want[i])) for i in bad[:8]]
+    g.close()
+
+
 @pytest.mark.parametrize("case", range(len(CASES)), ids=_case_ids())
 def test_unpack_fp8_bit_exact_misaligned(case):
     name, shapes, n = CASES[case]
