@@ -1079,6 +1079,28 @@ def test_pack_fp8_bit_exact(case):
         g.close()
 
 
+def test_pack_bf16_every_rounding_boundary():
+    """The bf16 copy-in on every fp32 upper half (every kept pattern, so every
+    exponent, both parities of the last kept bit, infinities and NaN
+    payloads) times low halves 0, 1, 0x7FFF, 0x8000 (the tie), 0x8001 and
+    0xFFFF: equal to the oracle bit for bit."""
+    hi = np.arange(1 << 16, dtype=np.uint32) << 16
+    lo = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], dtype=np.uint32)
+    x = (hi[:, None] | lo[None, :]).reshape(-1).view(np.float32)
+    plan = O.plan([(x.size,)], 1, 0)
+    g = ShardedGroup([(x.size,)], 1, 0)
+    g.shard_view(g.master_flat, 0).copy_(torch.from_numpy(x))
+    out = torch.zeros(plan.S, dtype=torch.int16, device=DEV)
+    g.pack(out)
+    torch.cuda.synchronize()
+    want = O.pack(plan, [x])
+    got = u16(out)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, [(hex(int(x.view(np.uint32)[i])), hex(int(got[i])), hex(int(want[i])))
+                           for i in bad[:8]]
+    g.close()
+
+
 def test_pack_fp8_every_rounding_boundary():
     """The FP8 cast on every fp32 upper half (sign, exponent and the top 7
     mantissa bits: every kept-bit and round-bit combination of the normal and
