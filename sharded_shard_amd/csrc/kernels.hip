@@ -101,9 +101,10 @@
 // copy-out blocks: 2048 elements over 128 threads when every row piece is
 // 16-byte aligned, 4096 over 256 otherwise; the other two-byte copies (bf16
 // reduce-scatter copy-in, resharding) and the FP8 copy-out (4096 bytes) take
-// the 128-thread shape (7B shape: 128 threads 6.33-6.60
-// TB/s, 64 threads 6.18-6.52, 256 threads 6.05-6.42, 512 threads 6.12-6.36;
-// misaligned ragged rows: 256 threads 5.77, 128 threads 5.62-5.68)
+// the 128-thread shape.  Copy-out measured on MI355X, two chunks per lane,
+// Llama 7B and 70B shapes: 128 threads 6.26 and 6.60 TB/s, 64 threads 6.18
+// and 6.52, 256 threads 6.05 and 6.41, 512 threads 6.12 and 6.36; misaligned
+// ragged rows: 256 threads 5.77-5.89, 128 threads 5.62-5.73.
 #ifndef FSDP_UNPACK_SUB
 #define FSDP_UNPACK_SUB 2048
 #endif
