@@ -1,11 +1,15 @@
 """Full-size parity on the 7B- and 70B-shaped groups, as the bench launches them.
 
 The groups are planned and bound exactly as bench.py does (ShardedGroup, same
-plans, tiles and grids).  The oracle cannot run whole at these sizes, so each
-output is checked two ways:
+plans, tiles and grids).  Outputs are checked three ways:
 
+* whole groups: the multi-group executor the bench times (fsdp_step_groups,
+  fused) runs 3 steps on whole groups of the one-block, ragged MoE and 70B
+  shapes, and every element of every output is compared with the oracle run
+  on the same inputs read back;
 * sampled: the oracle computes chosen outputs one by one from the same inputs
-  read back (first and last elements, tile edges, random picks);
+  read back (first and last elements, tile edges, random picks), for the
+  separate kernels and the single-group fused call;
 * exact properties over every element: unpack of every rank's pack of a full
   weight W gives bf16(W) back bit for bit, with torch's library cast as the
   reference; N equal gradient contributions reduce to exactly that gradient.
@@ -270,3 +274,82 @@ def test_next_rows_full_block_group(cfg_index):
         got = g.shard_view(g.grad_flat, i)[ix].cpu().numpy()
         assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), ("reduce f32", i)
     g.close()
+
+
+# Whole parameter groups (one group = one communication unit, [ST] fully_shard
+# paragraph) through the multi-group executor the bench times, 3 AdamW steps,
+# every element of every output against the oracle, bit for bit.  The groups:
+# the one-block Llama group (= a block of the 7B shape, N = 8, the aligned
+# fused kernel), the ragged MoE workload's two groups at ranks 5 and 0 (N = 6,
+# odd segment, misaligned fused kernel), and the 70B shape's first and last
+# block and its root group (N = 64, the wide fused kernel).
+WHOLE = [("llama-block-r0", 1, (0,), 0),
+         ("moe-r5", 3, (0, 1), 5),
+         ("moe-r0", 3, (0, 1), 0),
+         ("llama70b-r0", 4, (0, 79, 80), 0)]
+
+
+@pytest.mark.parametrize("write_grad", [False, True], ids=["nograd", "grad"])
+@pytest.mark.parametrize("name,cfg_index,group_ids,rank", WHOLE, ids=[w[0] for w in WHOLE])
+def test_step_groups_whole_groups_every_element(name, cfg_index, group_ids, rank, write_grad):
+    cfg = configs.get(cfg_index)
+    n, hp = cfg.world, vars(cfg.hp)
+    flags = capi.FSDP_STEP_WRITE_GRAD if write_grad else 0
+    groups, plans, rs, ag = [], [], [], []
+    hosts = []            # per group: oracle masters, m, v
+    for gi in group_ids:
+        shapes = [p.shape for p in cfg.groups[gi].params]
+        g = ShardedGroup(shapes, n, rank)
+        for i, e in enumerate(g.entries):
+            synth.fill_normal_f32_(g.shard_view(g.master_flat, i), cfg.master_std,
+                                   ("whole-m", cfg_index, gi, rank, i))
+        g.grad_flat.fill_(-1.0)
+        groups.append(g)
+        plans.append(O.plan(shapes, n, rank))
+        rs.append(torch.empty(n * g.S, dtype=torch.int16, device=DEV))
+        ag.append(torch.empty(n * g.S, dtype=torch.int16, device=DEV))
+        masters = [g.shard_view(g.master_flat, i).cpu().numpy() for i in range(len(shapes))]
+        hosts.append((masters, [np.zeros_like(x) for x in masters],
+                      [np.zeros_like(x) for x in masters]))
+    execute = capi.StepGroupsCall([g.plan for g in groups], rs,
+                                  [a[rank * g.S:(rank + 1) * g.S] for a, g in zip(ag, groups)],
+                                  ag, flags=flags, **hp)
+    for t in (1, 2, 3):
+        rs_h, ag_h = [], []
+        for k, (gi, g) in enumerate(zip(group_ids, groups)):
+            synth.fill_normal_bf16_bits_(rs[k], cfg.grad_std, ("whole-rs", cfg_index, gi, rank, t))
+            synth.fill_normal_bf16_bits_(ag[k], cfg.master_std, ("whole-ag", cfg_index, gi, rank, t))
+            # inputs as the oracle sees them, read back before the step runs
+            rs_h.append(rs[k].cpu().numpy().view(np.uint16).reshape(n, g.S))
+            ag_h.append(ag[k].cpu().numpy().view(np.uint16).reshape(n, g.S))
+        print(f"[fullsize] whole groups {name} step {t} flags={flags}", flush=True)
+        execute(t)
+        torch.cuda.synchronize()
+        for k, (gi, g, plan) in enumerate(zip(group_ids, groups, plans)):
+            masters, ms, vs = hosts[k]
+            grads = O.reduce(plan, rs_h[k])
+            for x, gr, m, v in zip(masters, grads, ms, vs):
+                O.adamw(x, gr, m, v, t, **hp)
+            want_ag = ag_h[k]
+            want_ag[rank] = O.pack(plan, masters)
+            got_row = ag[k].view(n, g.S)[rank].cpu().numpy().view(np.uint16)
+            assert np.array_equal(got_row, want_ag[rank]), (name, gi, t, "packed row")
+            for i, e in enumerate(g.entries):
+                for fl, host, what in ((g.master_flat, masters, "master"), (g.m_flat, ms, "m"),
+                                       (g.v_flat, vs, "v")):
+                    got = g.shard_view(fl, i).cpu().numpy()
+                    assert np.array_equal(got.view(np.uint32), host[i].view(np.uint32)), \
+                        (name, gi, t, what, i)
+                got_g = g.shard_view(g.grad_flat, i).cpu().numpy()
+                if write_grad:
+                    assert np.array_equal(got_g.view(np.uint32), grads[i].view(np.uint32)), \
+                        (name, gi, t, "grad", i)
+                else:
+                    assert (got_g == -1.0).all(), (name, gi, t, "grad written without the flag")
+            for i, want in enumerate(O.unpack(plan, want_ag)):
+                got = g.full_view(i).cpu().numpy().view(np.uint16)
+                assert np.array_equal(got, want), (name, gi, t, "full", i)
+            del grads, want_ag
+        del rs_h, ag_h
+    for g in groups:
+        g.close()
