@@ -445,14 +445,18 @@ def test_empty_group_calls_are_no_ops():
 # fused step: reduce -> AdamW -> pack in one pass
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("align", [1, 8])
 @pytest.mark.parametrize("write_grad", [False, True], ids=["nograd", "grad"])
 @pytest.mark.parametrize("case", range(len(CASES)), ids=_case_ids())
-def test_fused_step_equals_separate_calls_and_oracle(case, write_grad):
+def test_fused_step_equals_separate_calls_and_oracle(case, write_grad, align):
+    """align 1 puts most cases on misaligned rows (the misaligned fused
+    kernel); align 8 makes every row piece 16-byte aligned, so the aligned
+    kernel (below 16 ranks) and the wide one run on whole multi-tile groups."""
     name, shapes, n = CASES[case]
     hp = HP
     for r in sorted({0, n - 1}):
-        plan = O.plan(shapes, n, r)
-        ga, gb = ShardedGroup(shapes, n, r), ShardedGroup(shapes, n, r)
+        plan = O.plan(shapes, n, r, align)
+        ga, gb = ShardedGroup(shapes, n, r, align), ShardedGroup(shapes, n, r, align)
         _fill_masters(ga, ("fused", name, r))
         gb.master_flat.copy_(ga.master_flat)
         masters = [f32(ga.shard_view(ga.master_flat, i)) for i in range(len(shapes))]
@@ -479,6 +483,8 @@ def test_fused_step_equals_separate_calls_and_oracle(case, write_grad):
             assert np.array_equal(u16(agb)[off:off + plan.S], O.pack(plan, masters))
             for i in range(len(shapes)):
                 _cmp_f32(f32(gb.shard_view(gb.master_flat, i)), masters[i], ("p", name, r, t, i))
+                _cmp_f32(f32(gb.shard_view(gb.m_flat, i)), ms[i], ("m", name, r, t, i))
+                _cmp_f32(f32(gb.shard_view(gb.v_flat, i)), vs[i], ("v", name, r, t, i))
                 got_g = f32(gb.shard_view(gb.grad_flat, i))
                 if write_grad:
                     _cmp_f32(got_g, grads[i], ("g", name, r, t, i))
@@ -631,6 +637,52 @@ def test_fused_step_rejects_unbound_and_bad_flags():
     capi.fsdp_step_shard(g.plan, both[:2 * g.S], both[2 * g.S:], 3e-4, 0.9, 0.999, 1e-8, 0.01, 1)
     torch.cuda.synchronize()
     g.close()
+
+
+def test_injected_launch_fault_reaches_the_caller(monkeypatch):
+    """FSDP_FAULT=launch fails every launch before it is enqueued;
+    FSDP_FAULT=launch@K only the K-th.  The caller sees FSDP_E_HIP with the
+    call and group named, nothing after the fault runs, and the stream stays
+    usable once the variable is gone."""
+    n, r = 4, 1
+    shapes = [(64, 8), (17,)]
+    g = ShardedGroup(shapes, n, r)
+    h = ShardedGroup(shapes, n, r)
+    _fill_masters(g, ("fault", 0))
+    _fill_masters(h, ("fault", 1))
+    ag = torch.full((n * g.S,), 7, dtype=torch.int16, device=DEV)
+    agh = torch.full((n * h.S,), 7, dtype=torch.int16, device=DEV)
+    rs = torch.zeros(n * g.S, dtype=torch.int16, device=DEV)
+    before = [g.master_flat.clone(), h.master_flat.clone()]
+    monkeypatch.setenv("FSDP_FAULT", "launch")
+    for call in (lambda: g.pack(ag[r * g.S:(r + 1) * g.S]), lambda: g.unpack(ag),
+                 lambda: g.step(rs, ag[r * g.S:(r + 1) * g.S], 1, **HP)):
+        with pytest.raises(capi.FsdpError) as ei:
+            call()
+        assert ei.value.status == capi.FSDP_E_HIP and "injected" in str(ei.value)
+    torch.cuda.synchronize()
+    assert (ag == 7).all() and torch.equal(before[0], g.master_flat), "a faulted call launched"
+    # two groups: the third launch (group 1's fused step) fails; group 0's
+    # step and copy-out ran, group 1 is untouched
+    monkeypatch.setenv("FSDP_FAULT", "launch@3")
+    call = capi.StepGroupsCall([g.plan, h.plan], [rs, rs],
+                               [ag[r * g.S:(r + 1) * g.S], agh[r * h.S:(r + 1) * h.S]],
+                               [ag, agh], **HP)
+    with pytest.raises(capi.FsdpError) as ei:
+        call(1)
+    assert ei.value.status == capi.FSDP_E_HIP and "group 1" in str(ei.value)
+    torch.cuda.synchronize()
+    assert not torch.equal(before[0], g.master_flat), "group 0 did not run"
+    assert torch.equal(before[1], h.master_flat) and (agh == 7).all(), "group 1 ran"
+    monkeypatch.delenv("FSDP_FAULT")
+    capi.fsdp_check_stream()
+    g.pack(ag[r * g.S:(r + 1) * g.S])
+    torch.cuda.synchronize()
+    plan = O.plan(shapes, n, r)
+    want = O.pack(plan, [f32(g.shard_view(g.master_flat, i)) for i in range(len(shapes))])
+    assert np.array_equal(u16(ag).reshape(n, g.S)[r], want)
+    g.close()
+    h.close()
 
 
 # ---------------------------------------------------------------------------
