@@ -162,6 +162,41 @@ def stream_handle(stream=None) -> int:
     return int(stream.cuda_stream)
 
 
+def _dims(plan):
+    """(N, S, n_params) of a plan, or None for a null handle (the C call then
+    reports it)."""
+    if plan is None or getattr(plan, "value", 1) is None:
+        return None
+    info = fsdp_plan_info(plan)
+    return info.world, info.S, info.n_params
+
+
+def _dev(x, nbytes: int, what: str) -> int:
+    """Device address of a buffer argument of at least ``nbytes`` bytes.
+
+    The C ABI receives bare addresses and cannot see how large a buffer is, so
+    a torch tensor is checked here before any launch: it must hold nbytes, be
+    contiguous and live on the current GPU; otherwise ValueError.  An int is
+    taken as an address whose size the caller vouches for; None is 0.
+    """
+    if x is None or isinstance(x, int):
+        return addr(x)
+    if not hasattr(x, "data_ptr"):
+        raise TypeError(f"{what}: expected a torch tensor or an address")
+    have = x.numel() * x.element_size()
+    if have < nbytes:
+        raise ValueError(f"{what} holds {have} bytes; this call reads or writes {nbytes}")
+    if not x.is_cuda:
+        raise ValueError(f"{what} must be a GPU tensor (got device {x.device})")
+    if not x.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    import torch
+    if x.device.index != torch.cuda.current_device():
+        raise ValueError(f"{what} is on {x.device}, not on the current device "
+                         f"cuda:{torch.cuda.current_device()}")
+    return int(x.data_ptr())
+
+
 def _ptr_array(items):
     if items is None:
         return None
@@ -246,7 +281,10 @@ def fsdp_bind_full_grad(plan, full_grad, stream=None) -> None:
 
 
 def fsdp_pack_reduce_scatter(plan, rs_out, dtype: int = FSDP_DTYPE_BF16, stream=None) -> None:
-    _check(lib.fsdp_pack_reduce_scatter(plan, addr(rs_out), dtype, stream_handle(stream)),
+    d = _dims(plan)
+    esize = 4 if dtype == FSDP_DTYPE_F32 else 2
+    buf = _dev(rs_out, esize * d[0] * d[1], "rs_out") if d else addr(rs_out)
+    _check(lib.fsdp_pack_reduce_scatter(plan, buf, dtype, stream_handle(stream)),
            "fsdp_pack_reduce_scatter")
 
 
@@ -256,17 +294,24 @@ def fsdp_bind_full_fp8(plan, full_fp8, stream=None) -> None:
 
 
 def fsdp_pack_allgather_fp8(plan, ag_in, scales, stream=None) -> None:
-    _check(lib.fsdp_pack_allgather_fp8(plan, addr(ag_in), addr(scales), stream_handle(stream)),
+    d = _dims(plan)
+    a = _dev(ag_in, d[1], "ag_in") if d else addr(ag_in)
+    sc = _dev(scales, 4 * d[2], "scales") if d else addr(scales)
+    _check(lib.fsdp_pack_allgather_fp8(plan, a, sc, stream_handle(stream)),
            "fsdp_pack_allgather_fp8")
 
 
 def fsdp_unpack_allgather_fp8(plan, ag_out, stream=None) -> None:
-    _check(lib.fsdp_unpack_allgather_fp8(plan, addr(ag_out), stream_handle(stream)),
+    d = _dims(plan)
+    a = _dev(ag_out, d[0] * d[1], "ag_out") if d else addr(ag_out)
+    _check(lib.fsdp_unpack_allgather_fp8(plan, a, stream_handle(stream)),
            "fsdp_unpack_allgather_fp8")
 
 
 def fsdp_amax_shard(plan, amax, stream=None) -> None:
-    _check(lib.fsdp_amax_shard(plan, addr(amax), stream_handle(stream)), "fsdp_amax_shard")
+    d = _dims(plan)
+    a = _dev(amax, 4 * d[2], "amax") if d else addr(amax)
+    _check(lib.fsdp_amax_shard(plan, a, stream_handle(stream)), "fsdp_amax_shard")
 
 
 def fsdp_bind_grad_acc(plan, grad_acc, stream=None) -> None:
@@ -280,28 +325,35 @@ def fsdp_accumulate_grad(plan, reset: bool, stream=None) -> None:
 
 
 def fsdp_pack_reduce_scatter_acc(plan, rs_out, stream=None) -> None:
-    _check(lib.fsdp_pack_reduce_scatter_acc(plan, addr(rs_out), stream_handle(stream)),
+    d = _dims(plan)
+    a = _dev(rs_out, 4 * d[0] * d[1], "rs_out") if d else addr(rs_out)
+    _check(lib.fsdp_pack_reduce_scatter_acc(plan, a, stream_handle(stream)),
            "fsdp_pack_reduce_scatter_acc")
 
 
 def fsdp_reduce_shard_f32(plan, rs_in, stream=None) -> None:
-    _check(lib.fsdp_reduce_shard_f32(plan, addr(rs_in), stream_handle(stream)),
+    d = _dims(plan)
+    a = _dev(rs_in, 4 * d[0] * d[1], "rs_in") if d else addr(rs_in)
+    _check(lib.fsdp_reduce_shard_f32(plan, a, stream_handle(stream)),
            "fsdp_reduce_shard_f32")
 
 
 def fsdp_pack_allgather(plan, ag_in, stream=None) -> None:
-    _check(lib.fsdp_pack_allgather(plan, addr(ag_in), stream_handle(stream)),
-           "fsdp_pack_allgather")
+    d = _dims(plan)
+    a = _dev(ag_in, 2 * d[1], "ag_in") if d else addr(ag_in)
+    _check(lib.fsdp_pack_allgather(plan, a, stream_handle(stream)), "fsdp_pack_allgather")
 
 
 def fsdp_unpack_allgather(plan, ag_out, stream=None) -> None:
-    _check(lib.fsdp_unpack_allgather(plan, addr(ag_out), stream_handle(stream)),
-           "fsdp_unpack_allgather")
+    d = _dims(plan)
+    a = _dev(ag_out, 2 * d[0] * d[1], "ag_out") if d else addr(ag_out)
+    _check(lib.fsdp_unpack_allgather(plan, a, stream_handle(stream)), "fsdp_unpack_allgather")
 
 
 def fsdp_reduce_shard(plan, rs_in, stream=None) -> None:
-    _check(lib.fsdp_reduce_shard(plan, addr(rs_in), stream_handle(stream)),
-           "fsdp_reduce_shard")
+    d = _dims(plan)
+    a = _dev(rs_in, 2 * d[0] * d[1], "rs_in") if d else addr(rs_in)
+    _check(lib.fsdp_reduce_shard(plan, a, stream_handle(stream)), "fsdp_reduce_shard")
 
 
 def fsdp_adamw_shard(plan, lr: float, beta1: float, beta2: float, eps: float,
@@ -314,7 +366,10 @@ def fsdp_adamw_shard(plan, lr: float, beta1: float, beta2: float, eps: float,
 def fsdp_step_shard(plan, rs_in, ag_in, lr: float, beta1: float, beta2: float, eps: float,
                     weight_decay: float, step: int, flags: int = 0, stream=None) -> None:
     hp = AdamwHparams(lr, beta1, beta2, eps, weight_decay)
-    _check(lib.fsdp_step_shard(plan, addr(rs_in), addr(ag_in), ctypes.byref(hp), step, flags,
+    d = _dims(plan)
+    r = _dev(rs_in, 2 * d[0] * d[1], "rs_in") if d else addr(rs_in)
+    a = _dev(ag_in, 2 * d[1], "ag_in") if d else addr(ag_in)
+    _check(lib.fsdp_step_shard(plan, r, a, ctypes.byref(hp), step, flags,
                                stream_handle(stream)), "fsdp_step_shard")
 
 
@@ -378,11 +433,25 @@ class StepGroupsCall:
     def __init__(self, plans, rs_in, ag_in, ag_out, lr, beta1, beta2, eps, weight_decay,
                  flags=0, stream=None):
         n = len(plans)
+        if len(rs_in) != n or len(ag_in) != n or (ag_out is not None and len(ag_out) != n):
+            raise ValueError("plans, rs_in, ag_in and ag_out must have one entry per group")
         self.n = n
         self._plans = (ctypes.c_void_p * max(1, n))(*[p.value for p in plans])
-        self._rs = _ptr_array(rs_in)
-        self._ag_in = _ptr_array(ag_in)
-        self._ag_out = _ptr_array(ag_out) if ag_out is not None else None
+        rs_p, in_p, out_p = [], [], []
+        for g, p in enumerate(plans):      # tensors are size-checked once, here
+            d = _dims(p)
+            if d is None:
+                rs_p.append(addr(rs_in[g]))
+                in_p.append(addr(ag_in[g]))
+                out_p.append(addr(ag_out[g]) if ag_out is not None else 0)
+                continue
+            rs_p.append(_dev(rs_in[g], 2 * d[0] * d[1], f"rs_in[{g}]"))
+            in_p.append(_dev(ag_in[g], 2 * d[1], f"ag_in[{g}]"))
+            if ag_out is not None:
+                out_p.append(_dev(ag_out[g], 2 * d[0] * d[1], f"ag_out[{g}]"))
+        self._rs = _ptr_array(rs_p)
+        self._ag_in = _ptr_array(in_p)
+        self._ag_out = _ptr_array(out_p) if ag_out is not None else None
         self._keep = (rs_in, ag_in, ag_out)
         self._hp = AdamwHparams(lr, beta1, beta2, eps, weight_decay)
         self.flags = flags
@@ -391,6 +460,8 @@ class StepGroupsCall:
     def __call__(self, step: int, timed_kernel: int = 0, events=None) -> None:
         ev = None
         if events is not None:     # None entries leave that group untimed
+            if len(events) != 2 * self.n:
+                raise ValueError(f"events: need 2 per group ({2 * self.n}), got {len(events)}")
             ev = (ctypes.c_void_p * len(events))(
                 *[int(e.cuda_event) if e is not None else None for e in events])
             ev = ctypes.cast(ev, _PP)

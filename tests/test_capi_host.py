@@ -206,6 +206,71 @@ def test_step_groups_rejects_bad_arguments_without_gpu():
         capi.fsdp_plan_destroy(p)
 
 
+def test_check_stream_reports_hip_errors_as_fsdp_e_hip():
+    """fsdp_check_stream's error branch: on a machine without a GPU the HIP
+    runtime fails the stream wait, and the status and HIP's message reach the
+    caller (on a GPU the same branch reports an asynchronous kernel fault)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("needs a machine without a GPU")
+    with pytest.raises(capi.FsdpError) as ei:
+        capi.fsdp_check_stream(0)
+    assert ei.value.status == capi.FSDP_E_HIP
+    assert "hipStreamSynchronize" in str(ei.value) and capi.fsdp_last_error()
+
+
+def test_binding_rejects_undersized_and_host_tensors_before_launching():
+    """The C ABI cannot see buffer sizes; the binding checks torch tensors
+    (size for this plan, then GPU residence) before the C call, so an
+    undersized or host tensor never reaches a kernel."""
+    import torch
+    p = capi.fsdp_plan_create([8, 3], [4, 1], 2, 0, 1)
+    try:
+        info = capi.fsdp_plan_info(p)
+        n, S, k = info.world, info.S, info.n_params
+        assert S > 0
+        i16 = lambda m: torch.zeros(m, dtype=torch.int16)
+        f32 = lambda m: torch.zeros(m, dtype=torch.float32)
+        u8 = lambda m: torch.zeros(m, dtype=torch.uint8)
+        calls = [
+            (lambda b: capi.fsdp_pack_allgather(p, b, 0), i16, S),
+            (lambda b: capi.fsdp_unpack_allgather(p, b, 0), i16, n * S),
+            (lambda b: capi.fsdp_reduce_shard(p, b, 0), i16, n * S),
+            (lambda b: capi.fsdp_reduce_shard_f32(p, b, 0), f32, n * S),
+            (lambda b: capi.fsdp_pack_reduce_scatter(p, b, capi.FSDP_DTYPE_BF16, 0), i16, n * S),
+            (lambda b: capi.fsdp_pack_reduce_scatter(p, b, capi.FSDP_DTYPE_F32, 0), f32, n * S),
+            (lambda b: capi.fsdp_pack_reduce_scatter_acc(p, b, 0), f32, n * S),
+            (lambda b: capi.fsdp_unpack_allgather_fp8(p, b, 0), u8, n * S),
+            (lambda b: capi.fsdp_pack_allgather_fp8(p, b, 0x1000, 0), u8, S),
+            (lambda b: capi.fsdp_pack_allgather_fp8(p, 0x1000, b, 0), f32, k),
+            (lambda b: capi.fsdp_amax_shard(p, b, 0), f32, k),
+            (lambda b: capi.fsdp_step_shard(p, b, 0x1000, 3e-4, 0.9, 0.999, 1e-8, 0.01, 1,
+                                             stream=0), i16, n * S),
+            (lambda b: capi.fsdp_step_shard(p, 0x1000, b, 3e-4, 0.9, 0.999, 1e-8, 0.01, 1,
+                                             stream=0), i16, S),
+        ]
+        for call, make, need in calls:
+            with pytest.raises(ValueError, match="bytes"):
+                call(make(need - 1))
+            with pytest.raises(ValueError, match="GPU tensor"):
+                call(make(need))
+        for rs, ag_in, ag_out in ((i16(n * S - 1), 0x2000, 0x3000),
+                                  (0x1000, i16(S - 1), 0x3000),
+                                  (0x1000, 0x2000, i16(n * S - 1))):
+            with pytest.raises(ValueError, match="bytes"):
+                capi.StepGroupsCall([p], [rs], [ag_in], [ag_out], 3e-4, 0.9, 0.999, 1e-8, 0.01,
+                                    stream=0)
+        with pytest.raises(ValueError, match="one entry per group"):
+            capi.StepGroupsCall([p], [0x1000, 0x2000], [0x2000], None, 3e-4, 0.9, 0.999, 1e-8,
+                                0.01, stream=0)
+        call = capi.StepGroupsCall([p], [0x1000], [0x2000], [0x3000], 3e-4, 0.9, 0.999, 1e-8,
+                                   0.01, stream=0)
+        with pytest.raises(ValueError, match="2 per group"):      # 2 events per group
+            call(1, capi.FSDP_KERNEL_STEP, [None, None, None])
+    finally:
+        capi.fsdp_plan_destroy(p)
+
+
 @pytest.mark.parametrize("n1,n2", [(2, 1), (1, 2), (3, 2), (8, 64), (64, 8), (6, 4), (5, 5)])
 def test_reshard_planner_matches_oracle(n1, n2):
     shapes = [(37, 3), (1, 5), (0, 4), (130, 1), (128256 // 64, 2), (64, 7)]
