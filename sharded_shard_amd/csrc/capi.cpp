@@ -5,9 +5,12 @@
 // enqueue kernels on the caller's stream.
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -65,6 +68,7 @@ struct fsdp_plan {
 namespace {
 
 thread_local std::string g_last_error;
+thread_local bool g_fault_injected = false;
 
 fsdp_status fail(fsdp_status s, const std::string &msg) {
     g_last_error = msg;
@@ -72,7 +76,10 @@ fsdp_status fail(fsdp_status s, const std::string &msg) {
 }
 
 fsdp_status hip_fail(hipError_t e, const char *what) {
-    return fail(FSDP_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+    std::string msg = std::string(what) + ": " + hipGetErrorString(e);
+    if (g_fault_injected) msg += " (injected by FSDP_FAULT)";
+    g_fault_injected = false;
+    return fail(FSDP_E_HIP, msg);
 }
 
 bool misaligned(const void *p, uintptr_t a) {
@@ -189,6 +196,43 @@ fsdp_status commit_entries(fsdp_plan *p, std::vector<fsdp::DevEntry> ents, int32
 namespace fsdp {
 // Error reporting and AdamW scalars shared with the other translation units.
 fsdp_status set_error(fsdp_status s, const std::string &msg) { return fail(s, msg); }
+fsdp_status set_hip_error(hipError_t e, const char *what) { return hip_fail(e, what); }
+
+// Fault injection, to test how callers see a failed launch without breaking a
+// kernel.  With FSDP_FAULT=launch in the environment every library launch
+// (one per hot call, one per kernel of fsdp_step_groups) fails with
+// hipErrorLaunchFailure before anything is enqueued; FSDP_FAULT=launch@K
+// fails only the K-th launch counted from when a launch first sees that
+// value (a launch that sees the variable unset or changed restarts the
+// count).  Unset, it costs one getenv per launch.
+hipError_t injected_fault() {
+    static std::mutex mu;
+    static std::string seen;
+    static long count = 0;
+    static std::atomic<bool> counting{false};
+    const char *f = std::getenv("FSDP_FAULT");
+    const bool at = f != nullptr && std::strncmp(f, "launch@", 7) == 0;
+    if (!at) {
+        if (counting.load(std::memory_order_relaxed)) {
+            std::lock_guard<std::mutex> lock(mu);
+            seen.clear();
+            count = 0;
+            counting.store(false, std::memory_order_relaxed);
+        }
+        if (f == nullptr || std::strcmp(f, "launch") != 0) return hipSuccess;
+        g_fault_injected = true;
+        return hipErrorLaunchFailure;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    counting.store(true, std::memory_order_relaxed);
+    if (seen != f) {
+        seen = f;
+        count = 0;
+    }
+    if (++count != std::strtol(f + 7, nullptr, 10)) return hipSuccess;
+    g_fault_injected = true;
+    return hipErrorLaunchFailure;
+}
 void adamw_scalars_host(const fsdp_adamw_hparams_t *hp, int64_t step, float out[8]) {
     adamw_scalars(hp, step, out);
 }
@@ -462,9 +506,18 @@ fsdp_status check_step(const fsdp_plan *p, const uint16_t *rs_in, const uint16_t
     return FSDP_OK;
 }
 
+// Runs one library launch unless a fault is injected in its place.
+template <typename F>
+hipError_t guarded(F &&launch) {
+    const hipError_t e = fsdp::injected_fault();
+    return e != hipSuccess ? e : launch();
+}
+
 hipError_t do_pack(const fsdp_plan *p, uint16_t *ag_in, hipStream_t st) {
-    return fsdp::launch_pack(p->d_pack, static_cast<int64_t>(p->L.pack.size()), p->d_entries,
-                             ag_in, st);
+    return guarded([&] {
+        return fsdp::launch_pack(p->d_pack, static_cast<int64_t>(p->L.pack.size()), p->d_entries,
+                                 ag_in, st);
+    });
 }
 
 // Every row piece starts 16-byte aligned: the offsets allow it and the
@@ -474,26 +527,34 @@ bool chunk_aligned(const fsdp_plan *p, const void *rows) {
 }
 
 hipError_t do_unpack(const fsdp_plan *p, const uint16_t *ag_out, hipStream_t st) {
-    return fsdp::launch_unpack(p->d_unpack, static_cast<int64_t>(p->L.unpack.size()),
-                               p->d_entries, ag_out, chunk_aligned(p, ag_out), st);
+    return guarded([&] {
+        return fsdp::launch_unpack(p->d_unpack, static_cast<int64_t>(p->L.unpack.size()),
+                                   p->d_entries, ag_out, chunk_aligned(p, ag_out), st);
+    });
 }
 
 hipError_t do_reduce(const fsdp_plan *p, const uint16_t *rs_in, hipStream_t st) {
-    return fsdp::launch_reduce(p->d_reduce, static_cast<int64_t>(p->L.reduce.size()),
-                               p->d_entries, rs_in, p->L.S, p->L.world,
-                               chunk_aligned(p, rs_in), st);
+    return guarded([&] {
+        return fsdp::launch_reduce(p->d_reduce, static_cast<int64_t>(p->L.reduce.size()),
+                                   p->d_entries, rs_in, p->L.S, p->L.world,
+                                   chunk_aligned(p, rs_in), st);
+    });
 }
 
 hipError_t do_adamw(const fsdp_plan *p, const float scal[8], hipStream_t st) {
-    return fsdp::launch_adamw(p->d_adamw, static_cast<int64_t>(p->L.adamw.size()), p->d_entries,
-                              scal, st);
+    return guarded([&] {
+        return fsdp::launch_adamw(p->d_adamw, static_cast<int64_t>(p->L.adamw.size()),
+                                  p->d_entries, scal, st);
+    });
 }
 
 hipError_t do_step(const fsdp_plan *p, const uint16_t *rs_in, uint16_t *ag_in,
                    const float scal[8], bool write_grad, hipStream_t st) {
-    return fsdp::launch_step(p->d_pack, static_cast<int64_t>(p->L.pack.size()), p->d_entries,
-                             rs_in, ag_in, p->L.S, p->L.world, scal, write_grad,
-                             chunk_aligned(p, rs_in), st);
+    return guarded([&] {
+        return fsdp::launch_step(p->d_pack, static_cast<int64_t>(p->L.pack.size()), p->d_entries,
+                                 rs_in, ag_in, p->L.S, p->L.world, scal, write_grad,
+                                 chunk_aligned(p, rs_in), st);
+    });
 }
 
 fsdp_status launched(hipError_t e, const char *call) {
@@ -564,9 +625,11 @@ fsdp_status fsdp_pack_allgather_fp8(const fsdp_plan *p, uint8_t *ag_in, const fl
         return fail(FSDP_E_INVAL, "fsdp_pack_allgather_fp8: null scales");
     if (misaligned(scales, 4)) return fail(FSDP_E_ALIGN, "fsdp_pack_allgather_fp8: scales not 4-byte aligned");
     if ((s = check_device(p)) != FSDP_OK) return s;
-    return launched(fsdp::launch_pack_fp8(p->d_pack, static_cast<int64_t>(p->L.pack.size()),
-                                          p->d_entries, ag_in, scales,
-                                          static_cast<hipStream_t>(stream)),
+    return launched(guarded([&] {
+                        return fsdp::launch_pack_fp8(
+                            p->d_pack, static_cast<int64_t>(p->L.pack.size()), p->d_entries,
+                            ag_in, scales, static_cast<hipStream_t>(stream));
+                    }),
                     "fsdp_pack_allgather_fp8: launch");
 }
 
@@ -576,8 +639,11 @@ fsdp_status fsdp_unpack_allgather_fp8(const fsdp_plan *p, const uint8_t *ag_out,
     if (ag_out == nullptr && p->L.S > 0)
         return fail(FSDP_E_INVAL, "fsdp_unpack_allgather_fp8: null ag_out");
     if ((s = check_device(p)) != FSDP_OK) return s;
-    return launched(fsdp::launch_unpack_fp8(p->d_unpack, static_cast<int64_t>(p->L.unpack.size()),
-                                            p->d_entries, ag_out, static_cast<hipStream_t>(stream)),
+    return launched(guarded([&] {
+                        return fsdp::launch_unpack_fp8(
+                            p->d_unpack, static_cast<int64_t>(p->L.unpack.size()), p->d_entries,
+                            ag_out, static_cast<hipStream_t>(stream));
+                    }),
                     "fsdp_unpack_allgather_fp8: launch");
 }
 
@@ -588,19 +654,23 @@ fsdp_status fsdp_amax_shard(const fsdp_plan *p, float *amax, void *stream) {
         return fail(FSDP_E_INVAL, "fsdp_amax_shard: null amax");
     if (misaligned(amax, 4)) return fail(FSDP_E_ALIGN, "fsdp_amax_shard: amax not 4-byte aligned");
     if ((s = check_device(p)) != FSDP_OK) return s;
-    return launched(fsdp::launch_amax(p->d_adamw, static_cast<int64_t>(p->L.adamw.size()),
-                                      p->d_entries, amax,
-                                      static_cast<int32_t>(p->L.entries.size()),
-                                      static_cast<hipStream_t>(stream)),
+    return launched(guarded([&] {
+                        return fsdp::launch_amax(p->d_adamw, static_cast<int64_t>(p->L.adamw.size()),
+                                                 p->d_entries, amax,
+                                                 static_cast<int32_t>(p->L.entries.size()),
+                                                 static_cast<hipStream_t>(stream));
+                    }),
                     "fsdp_amax_shard: launch");
 }
 
 fsdp_status fsdp_accumulate_grad(const fsdp_plan *p, int32_t reset, void *stream) {
     fsdp_status s = need_roles(p, FSDP_ROLE_FULL_GRAD | FSDP_ROLE_GRAD_ACC, "fsdp_accumulate_grad");
     if (s != FSDP_OK || (s = check_device(p)) != FSDP_OK) return s;
-    return launched(fsdp::launch_accumulate(p->d_full, static_cast<int64_t>(p->L.full.size()),
-                                            p->d_entries, reset != 0,
-                                            static_cast<hipStream_t>(stream)),
+    return launched(guarded([&] {
+                        return fsdp::launch_accumulate(
+                            p->d_full, static_cast<int64_t>(p->L.full.size()), p->d_entries,
+                            reset != 0, static_cast<hipStream_t>(stream));
+                    }),
                     "fsdp_accumulate_grad: launch");
 }
 
@@ -612,8 +682,11 @@ fsdp_status fsdp_pack_reduce_scatter_acc(const fsdp_plan *p, float *rs_out, void
     if (misaligned(rs_out, 4))
         return fail(FSDP_E_ALIGN, "fsdp_pack_reduce_scatter_acc: rs_out not 4-byte aligned");
     if ((s = check_device(p)) != FSDP_OK) return s;
-    return launched(fsdp::launch_rspack_acc(p->d_rspack, static_cast<int64_t>(p->L.rspack.size()),
-                                            p->d_entries, rs_out, static_cast<hipStream_t>(stream)),
+    return launched(guarded([&] {
+                        return fsdp::launch_rspack_acc(
+                            p->d_rspack, static_cast<int64_t>(p->L.rspack.size()), p->d_entries,
+                            rs_out, static_cast<hipStream_t>(stream));
+                    }),
                     "fsdp_pack_reduce_scatter_acc: launch");
 }
 
@@ -629,9 +702,12 @@ fsdp_status fsdp_pack_reduce_scatter(const fsdp_plan *p, void *rs_out, int32_t d
     if (misaligned(rs_out, dtype == FSDP_DTYPE_F32 ? 4 : 2))
         return fail(FSDP_E_ALIGN, "fsdp_pack_reduce_scatter: rs_out misaligned for its dtype");
     if ((s = check_device(p)) != FSDP_OK) return s;
-    return launched(fsdp::launch_rspack(p->d_rspack, static_cast<int64_t>(p->L.rspack.size()),
-                                        p->d_entries, rs_out, dtype == FSDP_DTYPE_F32,
-                                        chunk_aligned(p, rs_out), static_cast<hipStream_t>(stream)),
+    return launched(guarded([&] {
+                        return fsdp::launch_rspack(
+                            p->d_rspack, static_cast<int64_t>(p->L.rspack.size()), p->d_entries,
+                            rs_out, dtype == FSDP_DTYPE_F32, chunk_aligned(p, rs_out),
+                            static_cast<hipStream_t>(stream));
+                    }),
                     "fsdp_pack_reduce_scatter: launch");
 }
 
@@ -643,10 +719,12 @@ fsdp_status fsdp_reduce_shard_f32(const fsdp_plan *p, const float *rs_in, void *
     if (misaligned(rs_in, 4))
         return fail(FSDP_E_ALIGN, "fsdp_reduce_shard_f32: rs_in not 4-byte aligned");
     if ((s = check_device(p)) != FSDP_OK) return s;
-    return launched(fsdp::launch_reduce_f32(p->d_reduce, static_cast<int64_t>(p->L.reduce.size()),
-                                            p->d_entries, rs_in, p->L.S, p->L.world,
-                                            chunk_aligned(p, rs_in),
-                                            static_cast<hipStream_t>(stream)),
+    return launched(guarded([&] {
+                        return fsdp::launch_reduce_f32(
+                            p->d_reduce, static_cast<int64_t>(p->L.reduce.size()), p->d_entries,
+                            rs_in, p->L.S, p->L.world, chunk_aligned(p, rs_in),
+                            static_cast<hipStream_t>(stream));
+                    }),
                     "fsdp_reduce_shard_f32: launch");
 }
 

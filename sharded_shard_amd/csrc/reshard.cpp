@@ -21,6 +21,8 @@
 namespace fsdp {
 hipError_t launch_copy_runs(const CopyTile *tiles, int64_t n, hipStream_t st);
 fsdp_status set_error(fsdp_status s, const std::string &msg);
+fsdp_status set_hip_error(hipError_t e, const char *what);
+hipError_t injected_fault();
 }  // namespace fsdp
 
 struct fsdp_reshard_plan {
@@ -177,9 +179,11 @@ fsdp_status fsdp_reshard_execute(const fsdp_reshard_plan *p, void *stream) {
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return set_error(FSDP_E_HIP, std::string("fsdp_reshard_execute: ") + hipGetErrorString(e));
     if (dev != p->device) return set_error(FSDP_E_STATE, "fsdp_reshard_execute: wrong device");
-    e = fsdp::launch_copy_runs(p->d_tiles, static_cast<int64_t>(p->tiles.size()),
-                               static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return set_error(FSDP_E_HIP, std::string("fsdp_reshard_execute: ") + hipGetErrorString(e));
+    e = fsdp::injected_fault();
+    if (e == hipSuccess)
+        e = fsdp::launch_copy_runs(p->d_tiles, static_cast<int64_t>(p->tiles.size()),
+                                   static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fsdp::set_hip_error(e, "fsdp_reshard_execute");
     return FSDP_OK;
 }
 
