@@ -1,6 +1,6 @@
 """Benchmark of one rank's FSDP2 sharded step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--also 4]
 
 A step is one pass of the whole per-rank hot path over every parameter group
 of the workload: for each group, reduce (bf16 [N, S] gradient contributions
@@ -10,11 +10,15 @@ full parameters).  Other ranks' rows are synthetic data already in HBM; the
 collectives themselves are not part of the step.  Inputs are resident in HBM
 before the timed region starts.
 
-Prints one JSON line: params/s of this rank's shard (value), effective HBM
-GB/s (algorithmic bytes / time) and its fraction of the 8 TB/s HBM peak, the
-roofline of the dominant kernel (the one with the most algorithmic bytes)
-measured with HIP events around one launch per group inside the timed region,
-and the CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line for the headline workload (the 7B-shaped per-rank share
+by default): params/s of this rank's shard (value), effective HBM GB/s (the
+bytes the step's kernels move / time) and its fraction of the 8 TB/s HBM
+peak and of a copy ceiling measured in the same run with the library's own
+copy kernel, the roofline of the dominant kernel (the one with the most
+algorithmic bytes) measured with HIP events around one launch per group
+inside the timed region, and the CPU oracle timed on a bounded sample of the
+same workload.  The same record for each workload named by --also (the
+70B-shaped per-rank share by default) sits under "also".
 
 By default reduce, AdamW and pack run as one fused launch per group
 (fsdp_step_shard, bit-identical to the three calls); --unfused runs them as
@@ -82,6 +86,10 @@ def measured_traffic(workload, rank, align, kind):
     return None
 
 
+TRAFFIC_SOURCE = ("committed rocprofv3 --pmc summary (profiles/pmc_traffic.json), valid only "
+                  "for the kernel source it was taken on (null otherwise)")
+
+
 KERNEL_NAMES = {"step": "step_kernel (fused reduce+adamw+pack)", "reduce": "reduce_kernel",
                 "adamw": "adamw_kernel", "pack": "pack_kernel (copy-in)",
                 "unpack": "unpack_kernel (copy-out)"}
@@ -93,6 +101,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4])
+    ap.add_argument("--also", default=None,
+                    help="comma-separated configs measured after the headline one and reported "
+                         "under 'also' (default: 4 with --config 2, none otherwise; 'none')")
     ap.add_argument("--rank", type=int, default=None, help="simulated rank (default: the config's)")
     ap.add_argument("--align", type=int, default=1, choices=[1, 8])
     ap.add_argument("--unfused", action="store_true",
@@ -111,6 +122,14 @@ def parse():
     args = ap.parse_args()
     if args.steps < 1 or args.warmup < 0:
         ap.error("--steps must be at least 1 and --warmup at least 0")
+    if args.also is None:
+        args.also = "4" if args.config == 2 else "none"
+    try:
+        args.also = [] if args.also == "none" else [int(c) for c in args.also.split(",") if c]
+    except ValueError:
+        ap.error("--also takes comma-separated config numbers or 'none'")
+    if any(c not in (1, 2, 3, 4) or c == args.config for c in args.also):
+        ap.error("--also configs must be among 1-4 and differ from --config")
     return args
 
 
@@ -176,16 +195,23 @@ def cpu_baseline(cfg, rank, min_s=10.0, max_s=30.0):
         del rs, ag, grads
         if total_t >= min_s or total_t + total_t / len(names) > max_s:
             break
-    return {
-        "value": total_v / total_t,
+    rate = total_v / total_t
+    all_v = sum(O.plan([p.shape for p in g.params], n, rank).V for g in cfg.groups)
+    out = {
+        "value": rate,
         "unit": "params/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": (f"one step of {len(names)} groups ({names[0]}, {names[-1]}, ...) of {cfg.name}, "
-                   f"rank {rank}: {total_v} params "
+        "sample": (f"one step of {len(names)} of {len(cfg.groups)} groups ({names[0]}, "
+                   f"{names[-1]}, ...) of {cfg.name}, rank {rank}: {total_v} params "
                    f"in {total_t:.2f} s (NumPy, single thread; host has {os.cpu_count()} cpus, "
                    f"affinity {len(os.sched_getaffinity(0))})"),
+        "extrapolated": len(names) < len(cfg.groups),
     }
+    if out["extrapolated"]:
+        out["extrapolation"] = (f"rate over the sampled groups applied to the whole step: "
+                                f"{all_v} params at this rate = {all_v / rate:.1f} s per step")
+    return out
 
 
 def measure_next(groups, n, rs_bf16, full_arena, stream, reps):
@@ -269,12 +295,15 @@ def _pct(sorted_vals, q):
 
 
 def measure_isolated(groups, kinds, n, rank, hp, rs_arena, ag_arena, fused, stream):
-    """Each kernel kind launched alone per group, after a 1 GiB write that
-    flushes the 256 MB MALL, so no input can come from the last-level cache:
-    the per-kernel roofline protocol.  Sum of algorithmic bytes / sum of
-    event-timed launch durations over the groups."""
+    """Each kernel kind launched alone per group after the 256 MB MALL has
+    been flushed, so no input can come from the last-level cache: the
+    per-kernel roofline protocol.  The flush writes 1 GiB and then reads
+    another 1 GiB, so the cache holds only clean lines when the timed launch
+    starts (no write-back of the flush lands in it).  Sum of algorithmic
+    bytes / sum of event-timed launch durations over the groups."""
     import torch
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=rs_arena[0].device)
+    sweep = torch.zeros(1 << 28, dtype=torch.int32, device=rs_arena[0].device)
     res = {}
     t = 10_000
     for k in kinds:
@@ -289,6 +318,7 @@ def measure_isolated(groups, kinds, n, rank, hp, rs_arena, ag_arena, fused, stre
                       "pack": lambda: g.pack(ag_in, stream),
                       "unpack": lambda: g.unpack(ag_out, stream)}[k]
             flush.fill_(gi & 0xFF)
+            sweep.max()                     # read-only pass over another 1 GiB
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             launch()
@@ -299,7 +329,7 @@ def measure_isolated(groups, kinds, n, rank, hp, rs_arena, ag_arena, fused, stre
             t += 1
         gbps = tot_b / (tot_ms * 1e-3) / 1e9
         res[k] = {"isolated_GBps": round(gbps, 1), "isolated_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
-    del flush
+    del flush, sweep
     return res
 
 
@@ -324,28 +354,52 @@ def measure_host_adamw(n=1 << 25, reps=3):
             "host_GBps": round(28 * n / best / 1e9, 1), "note": "host DRAM, not HBM"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "the benchmark runs on one GPU only: the collectives between "
-                          "ranks are not part of it, so --gpus must be 1"}))
-        sys.exit(2)
+def measure_copy_ceiling(dev, stream, nbytes=1 << 30, reps=10):
+    """A plain 1 GiB device copy through the library's own copy kernel (the
+    resharding executor at 1 -> 1 rank: one run, the copy-out's block shape
+    and cache policy), timed with HIP events over `reps` launches.  Source
+    and destination together are 8x the 256 MB MALL, so the launches stream
+    from HBM.  The ceiling of a 1:1 read/write stream on this GPU, measured
+    in the same run as the step."""
     import torch
+    from sharded_shard_amd import capi
+    rows = 8192
+    cols = nbytes // 2 // rows
+    src = torch.ones(rows * cols, dtype=torch.int16, device=dev)
+    dst = torch.empty_like(src)
+    rp = capi.fsdp_reshard_plan_create([rows], [cols], 1, 1, 0)
+    try:
+        capi.fsdp_reshard_bind(rp, [src.data_ptr()], [dst.data_ptr()], 2, stream)
+        for _ in range(3):
+            capi.fsdp_reshard_execute(rp, stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            capi.fsdp_reshard_execute(rp, stream)
+        b.record(stream)
+        b.synchronize()
+        ms = a.elapsed_time(b) / reps
+        if not torch.equal(dst, src):
+            raise RuntimeError("copy ceiling: the copy kernel did not reproduce its source")
+    finally:
+        capi.fsdp_reshard_plan_destroy(rp)
+    gbps = 2 * rows * cols * 2 / (ms * 1e-3) / 1e9
+    return {"kernel": "copy_runs_kernel via fsdp_reshard_execute (1 -> 1 rank, one 1 GiB bf16 run)",
+            "bytes_per_launch": 2 * rows * cols * 2, "avg_launch_ms": round(ms, 4),
+            "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
 
-    if args.copy_calibration:
-        print(json.dumps(copy_calibration()), flush=True)
-        return
 
+def run_workload(cfg_index, args, dev, copy_gbps):
+    """Build, time and describe one workload; returns its record."""
+    import torch
     from sharded_shard_amd import capi
     from sharded_shard_amd.group import ShardedGroup
     from workloads import configs, synth
 
-    cfg = configs.get(args.config)
+    cfg = configs.get(cfg_index)
     n = cfg.world
     rank = cfg.timing_rank if args.rank is None else args.rank
     hp = vars(cfg.hp)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     print(f"bench: {cfg.name} rank={rank} groups={len(cfg.groups)}", file=sys.stderr, flush=True)
 
     # ---- persistent state: per-group shards, shared double-buffered arenas --------
@@ -359,12 +413,12 @@ def main():
     rs_arena = [torch.empty(max_ns, dtype=torch.int16, device=dev) for _ in range(2)]
     ag_arena = [torch.empty(max_ns, dtype=torch.int16, device=dev) for _ in range(2)]
     for b in range(2):
-        synth.fill_normal_bf16_bits_(rs_arena[b], cfg.grad_std, ("bench-rs", args.config, b))
-        synth.fill_normal_bf16_bits_(ag_arena[b], cfg.master_std, ("bench-ag", args.config, b))
+        synth.fill_normal_bf16_bits_(rs_arena[b], cfg.grad_std, ("bench-rs", cfg_index, b))
+        synth.fill_normal_bf16_bits_(ag_arena[b], cfg.master_std, ("bench-ag", cfg_index, b))
     for gi, g in enumerate(groups):
         g.full_flat = full_arena
         g.allocate(full=False)
-        synth.fill_normal_f32_(g.master_flat, cfg.master_std, ("bench-master", args.config, gi))
+        synth.fill_normal_f32_(g.master_flat, cfg.master_std, ("bench-master", cfg_index, gi))
         g.bind()
     torch.cuda.synchronize()
     print("bench: state resident", file=sys.stderr, flush=True)
@@ -450,6 +504,7 @@ def main():
     achieved = dom_bytes_per_launch / (dom_avg_ms * 1e-3) / 1e9
 
     # per-kernel breakdown: extra untimed steps, each timing one kernel kind
+    # (events around every launch of that kind)
     per = {k: 0.0 for k in kinds}
     if args.breakdown_steps > 0:
         runs = {k: [new_events() for _ in range(args.breakdown_steps)] for k in kinds}
@@ -459,11 +514,19 @@ def main():
                 step(k, evs)
         torch.cuda.synchronize()
         per = {k: sum(sum(elapsed(evs)) for evs in runs[k]) / args.breakdown_steps for k in kinds}
-    kernels = {k: {"ms_per_step": round(per[k], 4),
-                   "algorithmic_GB_per_step": round(byts[k] / 1e9, 4),
-                   "GBps": round(byts[k] / (per[k] * 1e-3) / 1e9, 1) if per[k] else None,
-                   "hbm_frac": round(byts[k] / (per[k] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4) if per[k] else None}
-               for k in kinds}
+
+    def frac(gbps, ref):
+        return round(gbps / ref, 4) if gbps and ref else None
+
+    kernels = {}
+    for k in kinds:
+        gbps = byts[k] / (per[k] * 1e-3) / 1e9 if per[k] else None
+        kernels[k] = {"kernel": KERNEL_NAMES[k], "ms_per_step": round(per[k], 4),
+                      "algorithmic_GB_per_step": round(byts[k] / 1e9, 4),
+                      "GBps": round(gbps, 1) if gbps else None,
+                      "hbm_frac": frac(gbps, HBM_PEAK_GBPS),
+                      "frac_of_copy_ceiling": frac(gbps, copy_gbps),
+                      "traffic_bytes_per_launch": measured_traffic(cfg.name, rank, args.align, k)}
     if args.isolated:
         iso = measure_isolated(groups, kinds, n, rank, hp, rs_arena, ag_arena, fused, stream)
         for k in kinds:
@@ -472,22 +535,15 @@ def main():
     eff_gbps = step_bytes / (ms_step * 1e-3) / 1e9
     # the method's own bytes per step, counted kernel by kernel as if unfused
     # (reduce 2NV+4V, AdamW 28V, copy-in 4V+2S, copy-out 4F): what a step
-    # has to move when each stage is its own pass over HBM
+    # moves when each stage is its own pass over HBM.  Divided by the fused
+    # step's time it credits bytes the fused step never moves, so it is a
+    # method-equivalent rate, not an HBM rate.
     method_bytes = sum(sum(algorithmic_bytes(g.S, g.V, g.F, n, False).values()) for g in groups)
     method_gbps = method_bytes / (ms_step * 1e-3) / 1e9
-    out = {
-        "metric": METRIC,
+    rec = {
         "value": V / (ms_step * 1e-3),
         "unit": "params/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
         "config": {"workload": cfg.name, "world": n, "rank": rank, "groups": len(groups),
                    "params_per_rank": V, "align_elems": args.align,
                    "step": ("per group: fused reduce+adamw+pack -> unpack" if fused else
@@ -495,18 +551,29 @@ def main():
                    "io": "fp32 master/m/v shards, bf16 [N,S] grads and all-gather buffers"},
         "effective_GBps": eff_gbps,
         "hbm_frac": eff_gbps / HBM_PEAK_GBPS,
+        "frac_of_copy_ceiling": frac(eff_gbps, copy_gbps),
         "step_algorithmic_bytes": step_bytes,
+        "bytes_note": ("bytes the step's kernels must move once each (fused step "
+                       "(2N+24)V+2S, copy-out 4F per group); hbm_frac = these / time / 8 TB/s"
+                       if fused else "bytes of the four separate kernels (reduce (2N+4)V, AdamW "
+                       "28V, copy-in 4V+2S, copy-out 4F per group) / time / 8 TB/s"),
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "step_ms": {"median": _pct(step_ms, 50), "p10": _pct(step_ms, 10), "p90": _pct(step_ms, 90)},
-        "method_bytes_per_step": method_bytes,
-        "method_effective_GBps": method_gbps,
-        "method_hbm_frac": method_gbps / HBM_PEAK_GBPS,
+        "method_equivalent": {
+            "bytes_per_step": method_bytes, "GBps": method_gbps,
+            "frac_of_peak": method_gbps / HBM_PEAK_GBPS,
+            "note": "separate-pass bytes over this step's time; counts bytes a fused step never "
+                    "moves, so it is not an HBM rate"},
         "roofline": {"bound": "hbm", "kernel": KERNEL_NAMES[dominant],
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(cfg.name, rank, args.align, dominant),
+                     "traffic_source": TRAFFIC_SOURCE,
+                     "frac_of_copy_ceiling": frac(achieved, copy_gbps),
                      "avg_launch_ms": dom_avg_ms, "launches": dom_launches,
-                     "algorithmic_bytes_per_launch": dom_bytes_per_launch},
+                     "algorithmic_bytes_per_launch": dom_bytes_per_launch,
+                     "timing": "HIP events around one launch per group on the step's stream, "
+                               "inside the timed steps"},
         "kernels": kernels,
     }
     if per.get("unpack"):
@@ -514,18 +581,65 @@ def main():
         # every group twice (forward and backward), so one more copy-out per
         # group is added at its measured per-step time
         t2 = ms_step + per["unpack"]
-        out["two_allgather_variant"] = {
+        rec["two_allgather_variant"] = {
             "derived": True, "ms_per_step": t2, "params_per_s": V / (t2 * 1e-3),
             "effective_GBps": (step_bytes + byts["unpack"]) / (t2 * 1e-3) / 1e9,
             "hbm_frac": (step_bytes + byts["unpack"]) / (t2 * 1e-3) / 1e9 / HBM_PEAK_GBPS}
     if not args.no_next:
-        out["next_kernels"] = measure_next(groups, n, rs_arena[0], full_arena, stream,
+        rec["next_kernels"] = measure_next(groups, n, rs_arena[0], full_arena, stream,
                                            max(1, args.breakdown_steps))
-    if not args.no_cpu_baseline:
-        print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(cfg, rank)
     for g in groups:
         g.close()
+    del groups, full_arena, rs_arena, ag_arena, execute
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(cfg, rank)
+    return rec
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "the benchmark runs on one GPU only: the collectives between "
+                          "ranks are not part of it, so --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+
+    if args.copy_calibration:
+        print(json.dumps(copy_calibration()), flush=True)
+        return
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    ceiling = measure_copy_ceiling(dev, stream)
+    print(f"bench: copy ceiling {ceiling['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
+    torch.cuda.empty_cache()
+    head = run_workload(args.config, args, dev, ceiling["GBps"])
+    out = {
+        "metric": METRIC,
+        "value": head.pop("value"),
+        "unit": head.pop("unit"),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head.pop("ms_per_step"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": head.pop("config"),
+    }
+    out.update(head)
+    out["copy_ceiling"] = ceiling
+    also = []
+    for c in args.also:
+        also.append(run_workload(c, args, dev, ceiling["GBps"]))
+    if also:
+        out["also"] = also
     print(json.dumps(out), flush=True)
 
 

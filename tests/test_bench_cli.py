@@ -58,3 +58,19 @@ def test_byte_accounting_matches_the_shapes(ci):
         assert fused == FUSED_BYTES[ci]
     # fusing saves the gradient's write and re-read and the master's re-read
     assert sep - fused == sum(12 * O.plan([q.shape for q in g.params], n, r).V for g in cfg.groups)
+
+
+@pytest.mark.parametrize("args,want", [((), [4]), (("--config", "4"), []),
+                                       (("--also", "none"), []), (("--also", "3,4"), [3, 4]),
+                                       (("--config", "1", "--also", "2"), [2])])
+def test_also_workloads(monkeypatch, args, want):
+    """The 7B-shaped headline carries the 70B-shaped share by default."""
+    monkeypatch.setattr(sys, "argv", ["bench.py", *args])
+    assert bench.parse().also == want
+
+
+@pytest.mark.parametrize("args", [("--also", "2"), ("--also", "7"), ("--also", "x")])
+def test_bad_also_is_rejected(args):
+    r = _run(*args)
+    assert r.returncode == 2
+    assert "--also" in r.stderr
