@@ -354,39 +354,47 @@ def measure_host_adamw(n=1 << 25, reps=3):
             "host_GBps": round(28 * n / best / 1e9, 1), "note": "host DRAM, not HBM"}
 
 
-def measure_copy_ceiling(dev, stream, nbytes=1 << 30, reps=10):
-    """A plain 1 GiB device copy through the library's own copy kernel (the
+def measure_copy_ceiling(dev, stream, sizes=(1 << 29, 1 << 30, 1 << 31), reps=5):
+    """A plain device copy through the library's own copy kernel (the
     resharding executor at 1 -> 1 rank: one run, the copy-out's block shape
-    and cache policy), timed with HIP events over `reps` launches.  Source
-    and destination together are 8x the 256 MB MALL, so the launches stream
-    from HBM.  The ceiling of a 1:1 read/write stream on this GPU, measured
-    in the same run as the step."""
+    and cache policy), timed with HIP events over `reps` launches for each
+    size (source plus destination 4x to 16x the 256 MB MALL, so the launches
+    stream from HBM).  The fastest size is the ceiling of a 1:1 read/write
+    stream on this GPU, measured in the same run as the step; every size's
+    rate is listed (on MI355X a 1 GiB copy measured faster than a 4 GiB one)."""
     import torch
     from sharded_shard_amd import capi
+    rates = {}
     rows = 8192
-    cols = nbytes // 2 // rows
-    src = torch.ones(rows * cols, dtype=torch.int16, device=dev)
-    dst = torch.empty_like(src)
-    rp = capi.fsdp_reshard_plan_create([rows], [cols], 1, 1, 0)
-    try:
-        capi.fsdp_reshard_bind(rp, [src.data_ptr()], [dst.data_ptr()], 2, stream)
-        for _ in range(3):
-            capi.fsdp_reshard_execute(rp, stream)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
-            capi.fsdp_reshard_execute(rp, stream)
-        b.record(stream)
-        b.synchronize()
-        ms = a.elapsed_time(b) / reps
-        if not torch.equal(dst, src):
-            raise RuntimeError("copy ceiling: the copy kernel did not reproduce its source")
-    finally:
-        capi.fsdp_reshard_plan_destroy(rp)
-    gbps = 2 * rows * cols * 2 / (ms * 1e-3) / 1e9
-    return {"kernel": "copy_runs_kernel via fsdp_reshard_execute (1 -> 1 rank, one 1 GiB bf16 run)",
-            "bytes_per_launch": 2 * rows * cols * 2, "avg_launch_ms": round(ms, 4),
-            "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    for nbytes in sizes:
+        cols = nbytes // 2 // rows
+        src = torch.ones(rows * cols, dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        rp = capi.fsdp_reshard_plan_create([rows], [cols], 1, 1, 0)
+        try:
+            capi.fsdp_reshard_bind(rp, [src.data_ptr()], [dst.data_ptr()], 2, stream)
+            for _ in range(3):
+                capi.fsdp_reshard_execute(rp, stream)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                capi.fsdp_reshard_execute(rp, stream)
+            b.record(stream)
+            b.synchronize()
+            ms = a.elapsed_time(b) / reps
+            if not torch.equal(dst, src):
+                raise RuntimeError("copy ceiling: the copy kernel did not reproduce its source")
+        finally:
+            capi.fsdp_reshard_plan_destroy(rp)
+        rates[nbytes] = (ms, 2 * rows * cols * 2 / (ms * 1e-3) / 1e9)
+        del src, dst
+        torch.cuda.empty_cache()
+    best = max(rates, key=lambda k: rates[k][1])
+    ms, gbps = rates[best]
+    return {"kernel": "copy_runs_kernel via fsdp_reshard_execute (1 -> 1 rank, one bf16 run)",
+            "bytes_per_launch": 2 * best, "avg_launch_ms": round(ms, 4),
+            "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "by_size_GBps": {f"{k >> 20} MiB": round(v[1], 1) for k, v in rates.items()}}
 
 
 def run_workload(cfg_index, args, dev, copy_gbps):
