@@ -27,7 +27,6 @@ three launches.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -67,11 +66,11 @@ def measured_traffic(workload, rank, align, kind):
     """HBM bytes per launch from the committed rocprofv3 counter summary
     (profiles/pmc_traffic.json), or None when there is none for this kernel
     and workload or the kernel source has changed since it was taken."""
+    from sharded_shard_amd.build import kernel_sources_sha256
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
-    src = os.path.join(ROOT, "sharded_shard_amd", "csrc", "kernels.hip")
     try:
         rec = json.load(open(path))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        sha = kernel_sources_sha256()
     except (OSError, ValueError):
         return None
     if rec.get("kernels_source_sha256") != sha:
@@ -114,6 +113,9 @@ def parse():
     ap.add_argument("--isolated", action=argparse.BooleanOptionalAction, default=True,
                     help="also time every kernel kind alone per group after flushing the "
                          "last-level cache (per-kernel roofline protocol)")
+    ap.add_argument("--no-copy-ceiling", action="store_true",
+                    help="skip the copy-ceiling measurement (profiled runs: its copies use the "
+                         "resharding kernel)")
     ap.add_argument("--no-next", action="store_true",
                     help="skip timing the reduce-scatter copy-in and fp32-contribution kernels")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -622,10 +624,12 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
-    ceiling = measure_copy_ceiling(dev, stream)
-    print(f"bench: copy ceiling {ceiling['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
+    ceiling = None if args.no_copy_ceiling else measure_copy_ceiling(dev, stream)
+    if ceiling:
+        print(f"bench: copy ceiling {ceiling['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
     torch.cuda.empty_cache()
-    head = run_workload(args.config, args, dev, ceiling["GBps"])
+    copy_gbps = ceiling["GBps"] if ceiling else None
+    head = run_workload(args.config, args, dev, copy_gbps)
     out = {
         "metric": METRIC,
         "value": head.pop("value"),
@@ -645,7 +649,7 @@ def main():
     out["copy_ceiling"] = ceiling
     also = []
     for c in args.also:
-        also.append(run_workload(c, args, dev, ceiling["GBps"]))
+        also.append(run_workload(c, args, dev, copy_gbps))
     if also:
         out["also"] = also
     print(json.dumps(out), flush=True)

@@ -32,8 +32,25 @@ SOURCES = [
     ("capi.cpp", ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROCM, "include")]),
     ("host_adamw.cpp", ["-x", "c++", "-ffp-contract=off", "-fno-fast-math", "-pthread"]),
     ("reshard.cpp", ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROCM, "include")]),
-    ("kernels.hip", ["-x", "hip"] + DEVICE),
+    ("copy.hip", ["-x", "hip"] + DEVICE),
+    ("pack.hip", ["-x", "hip"] + DEVICE),
+    ("reduce.hip", ["-x", "hip"] + DEVICE),
+    ("step.hip", ["-x", "hip"] + DEVICE),
 ]
+KERNEL_SOURCES = [n for n, _ in SOURCES if n.endswith(".hip")]
+
+
+def kernel_sources_sha256() -> str:
+    """sha256 over the device sources (every .hip file and the headers they
+    include), in name order: identifies the kernels a measurement was taken
+    on."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(KERNEL_SOURCES + ["device.hpp", "rows.hpp", "launch.hpp", "plan.hpp"]):
+        h.update(name.encode() + b"\0")
+        with open(os.path.join(SRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def _run(cmd, verbose):
@@ -67,12 +84,17 @@ def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
     return out
 
 
-def emit_asm(out_path: str) -> str:
-    """Write the gfx950 assembly of the kernels (for inspecting the ISA)."""
-    src = os.path.join(SRC, "kernels.hip")
-    _run([HIPCC, *COMMON, "-x", "hip", *DEVICE, "--cuda-device-only", "-S",
-          src, "-o", out_path], False)
-    return out_path
+def emit_asm(out_dir: str) -> list:
+    """Write the gfx950 assembly of every kernel source into out_dir (for
+    inspecting the ISA); returns the paths."""
+    os.makedirs(out_dir, exist_ok=True)
+    paths = []
+    for name in KERNEL_SOURCES:
+        path = os.path.join(out_dir, name.replace(".hip", ".s"))
+        _run([HIPCC, *COMMON, "-x", "hip", *DEVICE, "--cuda-device-only", "-S",
+              os.path.join(SRC, name), "-o", path], False)
+        paths.append(path)
+    return paths
 
 
 if __name__ == "__main__":

@@ -16,38 +16,9 @@
 #include <vector>
 
 #include "../../include/fsdp_shard.h"
+#include "launch.hpp"
 #include "plan.hpp"
 
-namespace fsdp {
-hipError_t launch_pack(const PackTile *tiles, int64_t n, const DevEntry *ents,
-                       uint16_t *ag_in, hipStream_t st);
-hipError_t launch_unpack(const UnpackTile *tiles, int64_t n, const DevEntry *ents,
-                         const uint16_t *ag_out, bool chunk_aligned, hipStream_t st);
-hipError_t launch_reduce(const ReduceTile *tiles, int64_t n, const DevEntry *ents,
-                         const uint16_t *rs_in, int64_t S, int32_t N, bool chunk_aligned,
-                         hipStream_t st);
-hipError_t launch_adamw(const EwTile *tiles, int64_t n, const DevEntry *ents,
-                        const float scal[8], hipStream_t st);
-hipError_t launch_step(const PackTile *tiles, int64_t n, const DevEntry *ents,
-                       const uint16_t *rs_in, uint16_t *ag_in, int64_t S, int32_t N,
-                       const float scal[8], bool write_grad, bool chunk_aligned,
-                       hipStream_t st);
-hipError_t launch_rspack(const PackTile *tiles, int64_t n, const DevEntry *ents, void *out,
-                         bool f32, bool chunk_aligned, hipStream_t st);
-hipError_t launch_reduce_f32(const ReduceTile *tiles, int64_t n, const DevEntry *ents,
-                             const float *rs_in, int64_t S, int32_t N, bool chunk_aligned,
-                             hipStream_t st);
-hipError_t launch_accumulate(const EwTile *tiles, int64_t n, const DevEntry *ents, bool reset,
-                             hipStream_t st);
-hipError_t launch_pack_fp8(const PackTile *tiles, int64_t n, const DevEntry *ents, uint8_t *ag_in,
-                           const float *scales, hipStream_t st);
-hipError_t launch_unpack_fp8(const UnpackTile *tiles, int64_t n, const DevEntry *ents,
-                             const uint8_t *ag_out, hipStream_t st);
-hipError_t launch_amax(const EwTile *tiles, int64_t n, const DevEntry *ents, float *amax,
-                       int32_t n_params, hipStream_t st);
-hipError_t launch_rspack_acc(const PackTile *tiles, int64_t n, const DevEntry *ents, float *out,
-                             hipStream_t st);
-}  // namespace fsdp
 
 struct fsdp_plan {
     fsdp::Layout L;

@@ -1,0 +1,451 @@
+// Copies of the sharded step: the all-gather copy-out ([N, S] bf16 -> full
+// parameters), the reduce-scatter copy-ins (full gradients or fp32
+// accumulators -> [N, S]), the FP8 copy-out and the resharding executor.
+// Pure data movement at the HBM roofline: 16-byte vectors, raw buffer loads
+// from one descriptor per run, misaligned sources funnel-shifted in
+// registers with each chunk read once.
+#include "device.hpp"
+#include "launch.hpp"
+
+// copy-out and the two-byte copies: non-temporal loads and stores
+#ifndef FSDP_UNPACK_POL
+#define FSDP_UNPACK_POL 3
+#endif
+// copy-out blocks: 2048 elements over 128 threads when every row piece is
+// 16-byte aligned, 4096 over 256 otherwise; the other two-byte copies (bf16
+// reduce-scatter copy-in, resharding) and the FP8 copy-out (4096 bytes) take
+// the 128-thread shape.  Copy-out measured on MI355X, two chunks per lane,
+// Llama 7B and 70B shapes: 128 threads 6.26 and 6.60 TB/s, 64 threads 6.18
+// and 6.52, 256 threads 6.05 and 6.41, 512 threads 6.12 and 6.36; misaligned
+// ragged rows: 256 threads 5.77-5.89, 128 threads 5.62-5.73.
+#ifndef FSDP_UNPACK_SUB
+#define FSDP_UNPACK_SUB 2048
+#endif
+#ifndef FSDP_UNPACK_THREADS
+#define FSDP_UNPACK_THREADS 128
+#endif
+#ifndef FSDP_UNPACK_MIS_SUB
+#define FSDP_UNPACK_MIS_SUB 4096
+#endif
+#ifndef FSDP_UNPACK_MIS_THREADS
+#define FSDP_UNPACK_MIS_THREADS 256
+#endif
+// 16-byte chunks each lane of an aligned copy loads before storing them (4
+// or 8 with correspondingly larger blocks measured 9-16% slower)
+#ifndef FSDP_UNPACK_UNROLL
+#define FSDP_UNPACK_UNROLL 2
+#endif
+// reduce-scatter copy-ins widening to fp32 and from the fp32 accumulators,
+// and the accumulation itself: non-temporal loads and stores
+#ifndef FSDP_RSPACK_F32_POL
+#define FSDP_RSPACK_F32_POL 3
+#endif
+#ifndef FSDP_RSPACK_ACC_POL
+#define FSDP_RSPACK_ACC_POL 3
+#endif
+
+namespace fsdp {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// copy-out: [N, S] bf16 -> full parameters
+// ---------------------------------------------------------------------------
+
+// TB threads per block (whole waves).
+template <int POL, int TB = kBlock>
+__device__ __forceinline__ void copy_run_bf16(uint16_t *__restrict__ dst,
+                                              const uint16_t *__restrict__ src, int64_t len) {
+    constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
+    const int tid = threadIdx.x;
+    int64_t head = ((16u - (lo32(dst) & 15u)) & 15u) >> 1;
+    if (head > len) head = len;
+    if (tid < head) dst[tid] = src[tid];
+    const int64_t nvec = (len - head) >> 3;
+    u32x4 *dv = reinterpret_cast<u32x4 *>(dst + head);
+    const uint16_t *s = src + head;
+    const uint32_t k = lo32(s) & 15u;
+    if (k == 0) {
+        // raw buffer loads from one SGPR descriptor per run (measured faster
+        // than per-lane 64-bit addresses on MI355X)
+        // FSDP_UNPACK_UNROLL chunks in flight per lane before their stores
+        constexpr int U = FSDP_UNPACK_UNROLL;
+        const char *sb = reinterpret_cast<const char *>(s);
+        const uint32_t nb = static_cast<uint32_t>(nvec) << 4;
+        int64_t v = tid;
+        for (; v + (U - 1) * TB < nvec; v += U * TB) {
+            u32x4 x[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                x[u] = bload16<LN>(sb, static_cast<uint32_t>(v + u * TB) << 4, nb);
+#pragma unroll
+            for (int u = 0; u < U; ++u) stp<SN>(dv + v + u * TB, x[u]);
+        }
+        for (; v < nvec; v += TB)
+            stp<SN>(dv + v, bload16<LN>(sb, static_cast<uint32_t>(v) << 4, nb));
+    } else {
+        // Every aligned 16-byte source chunk is read once: a lane's second
+        // chunk is the next lane's first (DPP), and lane 63 of each wave
+        // loads its own with a load whose other lanes sit at the end of the
+        // buffer range (they read zero and touch no memory).  The range is
+        // exactly the chunks holding data, and whole waves iterate together.
+        const char *al = reinterpret_cast<const char *>(s) - k;
+        const uint32_t nb = (k + 2 * static_cast<uint32_t>(len - head) + 15u) & ~15u;
+        const uint32_t lane = tid & 63;
+        const bool last = lane == 63;
+        for (int64_t w0 = tid - lane; w0 < nvec; w0 += 2 * TB) {
+            const int64_t v0 = w0 + lane, v1 = v0 + TB;
+            const uint32_t o0 = static_cast<uint32_t>(v0) << 4, o1 = static_cast<uint32_t>(v1) << 4;
+            const u32x4 a0 = bload16<LN>(al, o0, nb), a1 = bload16<LN>(al, o1, nb);
+            const u32x4 h0 = bload16<LN>(al, last ? o0 + 16 : nb, nb);
+            const u32x4 h1 = bload16<LN>(al, last ? o1 + 16 : nb, nb);
+            u32x4 b0 = next_lane16(a0), b1 = next_lane16(a1);
+            if (last) {
+                b0 = h0;
+                b1 = h1;
+            }
+            if (v0 < nvec) stp<SN>(dv + v0, funnel(a0, b0, k));
+            if (v1 < nvec) stp<SN>(dv + v1, funnel(a1, b1, k));
+        }
+    }
+    const int64_t done = head + (nvec << 3);
+    if (tid < len - done) dst[done + tid] = src[done + tid];
+}
+
+template <int POL, int TB>
+__global__ __launch_bounds__(TB) void unpack_kernel(
+    const UnpackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
+    const DevEntry *__restrict__ ents, const uint16_t *__restrict__ ag_out) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
+        const UnpackTile tl = tiles[t];
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        copy_run_bf16<POL, TB>(ents[tl.entry].full + tl.dst + b, ag_out + tl.src + b, len);
+    }
+}
+
+// Resharding: runs of 2-byte units between absolute addresses.
+template <int POL, int TB>
+__global__ __launch_bounds__(TB) void copy_runs_kernel(const CopyTile *__restrict__ tiles,
+                                                           int64_t n_tiles, int32_t split,
+                                                           int64_t sub) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
+        const CopyTile tl = tiles[t];
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        copy_run_bf16<POL, TB>(tl.dst + b, tl.src + b, len);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// reduce-scatter copy-in: full bf16 gradients -> [N, S] (bf16 or fp32)
+// ---------------------------------------------------------------------------
+
+template <int POL, int TB>
+__global__ __launch_bounds__(TB) void rspack_bf16_kernel(
+    const PackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
+    const DevEntry *__restrict__ ents, uint16_t *__restrict__ out) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
+        const PackTile tl = tiles[t];
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        int64_t valid = tl.valid - b;
+        valid = valid < 0 ? 0 : (valid > len ? len : valid);
+        uint16_t *dst = out + tl.dst + b;
+        if (valid > 0) copy_run_bf16<POL, TB>(dst, ents[tl.entry].full_grad + tl.src + b, valid);
+        zero_bf16<(POL >> 1) & 1>(dst, valid, len);
+    }
+}
+
+// dst[e] = 0.0f for e in [from, len), 16-byte stores where aligned.
+template <int SN>
+__device__ __forceinline__ void zero_f32(float *dst, int64_t from, int64_t len) {
+    const int tid = threadIdx.x;
+    if (from >= len) return;
+    float *d = dst + from;
+    const int64_t n = len - from;
+    int64_t head = ((16u - (lo32(d) & 15u)) & 15u) >> 2;
+    if (head > n) head = n;
+    if (tid < head) d[tid] = 0.0f;
+    const int64_t nvec = (n - head) >> 2;
+    f32x4 *dv = reinterpret_cast<f32x4 *>(d + head);
+    for (int64_t v = tid; v < nvec; v += kBlock) stp<SN>(dv + v, f32x4{0.f, 0.f, 0.f, 0.f});
+    const int64_t done = head + (nvec << 2);
+    if (tid < n - done) d[done + tid] = 0.0f;
+}
+
+// dst[i] = fp32(src[i]) for i < valid (exact widening), zeros up to len.
+// dst is aligned to 16 bytes after a short head; every lane then widens four
+// elements into one 16-byte store, so each wave instruction is contiguous.
+// An 8-byte aligned source is one 8-byte load per lane.  Otherwise lane l
+// loads the 8-byte word holding its first element, takes the next word from
+// lane l + 1 (DPP; lane 63 loads its own from a load whose other lanes sit
+// at the end of the buffer range), and funnel-shifts: every source word is
+// read once, and whole waves iterate together.
+template <int POL>
+__device__ __forceinline__ void widen_run(float *__restrict__ dst, const uint16_t *__restrict__ src,
+                                          int64_t len, int64_t valid) {
+    constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
+    const int tid = threadIdx.x;
+    int64_t head = ((16u - (lo32(dst) & 15u)) & 15u) >> 2;
+    if (head > valid) head = valid;
+    if (tid < head) dst[tid] = widen(src[tid]);
+    const uint16_t *s = src + head;
+    const uint32_t k = lo32(s) & 15u;
+    f32x4 *dv = reinterpret_cast<f32x4 *>(dst + head);
+    int64_t done;
+    if ((k & 7u) == 0) {
+        const int64_t nq = (valid - head) >> 2;
+        const u32x2 *sv = reinterpret_cast<const u32x2 *>(s);
+        for (int64_t q = tid; q < nq; q += kBlock) {
+            const u32x2 w = ldp<LN>(sv + q);
+            stp<SN>(dv + q, f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)});
+        }
+        done = head + (nq << 2);
+    } else {
+        const uint32_t k8 = k & 7u;                     // 2, 4 or 6
+        const char *al = reinterpret_cast<const char *>(s) - k8;
+        const int64_t nq = (valid - head) >> 2;
+        const uint32_t nb = (k8 + 2 * static_cast<uint32_t>(valid - head) + 7u) & ~7u;
+        const uint32_t lane = tid & 63;
+        const bool last = lane == 63, s4 = k8 >= 4u;
+        const uint32_t sh = k8 & 3u;
+        for (int64_t w0 = tid - lane; w0 < nq; w0 += kBlock) {
+            const int64_t q = w0 + lane;
+            const uint32_t o = static_cast<uint32_t>(q) << 3;
+            const u32x2 a = bload8<LN>(al, o, nb);
+            const u32x2 h = bload8<LN>(al, last ? o + 8 : nb, nb);
+            u32x2 b{next_lane(a.x), next_lane(a.y)};
+            if (last) b = h;
+            // bytes [k8, k8 + 8) of a:b
+            const uint32_t u0 = s4 ? a.y : a.x, u1 = s4 ? b.x : a.y, u2 = s4 ? b.y : b.x;
+            const uint32_t r0 = __builtin_amdgcn_alignbyte(u1, u0, sh);
+            const uint32_t r1 = __builtin_amdgcn_alignbyte(u2, u1, sh);
+            if (q < nq) stp<SN>(dv + q, f32x4{bf16_lo(r0), bf16_hi(r0), bf16_lo(r1), bf16_hi(r1)});
+        }
+        done = head + (nq << 2);
+    }
+    if (tid < valid - done) dst[done + tid] = widen(src[done + tid]);
+    zero_f32<SN>(dst, valid, len);
+}
+
+template <int POL>
+__global__ __launch_bounds__(kBlock) void rspack_f32_kernel(
+    const PackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
+    const DevEntry *__restrict__ ents, float *__restrict__ out) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
+        const PackTile tl = tiles[t];
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        int64_t valid = tl.valid - b;
+        valid = valid < 0 ? 0 : (valid > len ? len : valid);
+        widen_run<POL>(out + tl.dst + b, ents[tl.entry].full_grad + tl.src + b, len, valid);
+    }
+}
+
+template <int POL, int TB = kBlock>
+__device__ __forceinline__ void copy_run_u8(uint8_t *__restrict__ dst, const uint8_t *__restrict__ src,
+                                            int64_t len) {
+    constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
+    const int tid = threadIdx.x;
+    int64_t head = (16u - (lo32(dst) & 15u)) & 15u;
+    if (head > len) head = len;
+    if (tid < head) dst[tid] = src[tid];
+    const int64_t nvec = (len - head) >> 4;
+    u32x4 *dv = reinterpret_cast<u32x4 *>(dst + head);
+    const uint8_t *s = src + head;
+    const uint32_t k = lo32(s) & 15u;
+    // raw buffer loads over exactly the 16-byte chunks holding the run; a
+    // misaligned run reads every chunk once, a lane's second chunk coming
+    // from the next lane (lane 63 loads its own), as in copy_run_bf16
+    const char *al = reinterpret_cast<const char *>(s) - k;
+    const uint32_t nb = (k + static_cast<uint32_t>(len - head) + 15u) & ~15u;
+    if (k == 0) {
+        for (int64_t v = tid; v < nvec; v += TB)
+            stp<SN>(dv + v, bload16<LN>(al, static_cast<uint32_t>(v) << 4, nb));
+    } else {
+        const uint32_t lane = tid & 63;
+        const bool last = lane == 63;
+        for (int64_t w0 = tid - lane; w0 < nvec; w0 += TB) {
+            const int64_t v = w0 + lane;
+            const uint32_t o = static_cast<uint32_t>(v) << 4;
+            const u32x4 a = bload16<LN>(al, o, nb);
+            const u32x4 h = bload16<LN>(al, last ? o + 16 : nb, nb);
+            u32x4 b = next_lane16(a);
+            if (last) b = h;
+            if (v < nvec) stp<SN>(dv + v, funnel(a, b, k));
+        }
+    }
+    const int64_t done = head + (nvec << 4);
+    if (tid < len - done) dst[done + tid] = src[done + tid];
+}
+
+template <int POL, int TB>
+__global__ __launch_bounds__(TB) void unpack_fp8_kernel(
+    const UnpackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
+    const DevEntry *__restrict__ ents, const uint8_t *__restrict__ ag_out) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
+        const UnpackTile tl = tiles[t];
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        copy_run_u8<POL, TB>(ents[tl.entry].full_fp8 + tl.dst + b, ag_out + tl.src + b, len);
+    }
+}
+
+// Reduce-scatter copy-in from the fp32 accumulators: copy fp32 runs, zeros
+// in padding.  dst is aligned to 16 bytes after a short head; every lane then
+// stores one 16-byte vector, so each wave instruction is contiguous.  An
+// aligned source is one load per lane; otherwise lane l loads the aligned
+// chunk holding its first element, takes the next chunk from lane l + 1
+// (DPP; lane 63 loads its own) and shifts by whole dwords.
+template <int POL>
+__device__ __forceinline__ void copy_f32_run(float *__restrict__ dst, const float *__restrict__ src,
+                                             int64_t len, int64_t valid) {
+    constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
+    const int tid = threadIdx.x;
+    int64_t head = ((16u - (lo32(dst) & 15u)) & 15u) >> 2;
+    if (head > valid) head = valid;
+    if (tid < head) dst[tid] = src[tid];
+    const float *s = src + head;
+    const uint32_t q = (lo32(s) >> 2) & 3u;
+    f32x4 *dv = reinterpret_cast<f32x4 *>(dst + head);
+    int64_t done;
+    if (q == 0) {
+        const int64_t nq = (valid - head) >> 2;
+        const f32x4 *sv = reinterpret_cast<const f32x4 *>(s);
+        for (int64_t v = tid; v < nq; v += kBlock) stp<SN>(dv + v, ldp<LN>(sv + v));
+        done = head + (nq << 2);
+    } else {
+        const char *al = reinterpret_cast<const char *>(s) - 4 * q;
+        const int64_t nv = (valid - head) >> 2;
+        const uint32_t nb = (4 * q + 4 * static_cast<uint32_t>(valid - head) + 15u) & ~15u;
+        const uint32_t lane = tid & 63;
+        const bool last = lane == 63;
+        for (int64_t w0 = tid - lane; w0 < nv; w0 += kBlock) {
+            const int64_t v = w0 + lane;
+            const uint32_t o = static_cast<uint32_t>(v) << 4;
+            const u32x4 a = bload16<LN>(al, o, nb);
+            const u32x4 h = bload16<LN>(al, last ? o + 16 : nb, nb);
+            u32x4 b = next_lane16(a);
+            if (last) b = h;
+            if (v < nv) stp<SN>(dv + v, __builtin_bit_cast(f32x4, funnel(a, b, 4 * q)));
+        }
+        done = head + (nv << 2);
+    }
+    if (tid < valid - done) dst[done + tid] = src[done + tid];
+    zero_f32<SN>(dst, valid, len);
+}
+
+template <int POL>
+__global__ __launch_bounds__(kBlock) void rspack_acc_kernel(
+    const PackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
+    const DevEntry *__restrict__ ents, float *__restrict__ out) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
+        const PackTile tl = tiles[t];
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        int64_t valid = tl.valid - b;
+        valid = valid < 0 ? 0 : (valid > len ? len : valid);
+        copy_f32_run<POL>(out + tl.dst + b, ents[tl.entry].grad_acc + tl.src + b, len, valid);
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// launchers (called by the C ABI after validation)
+// ---------------------------------------------------------------------------
+
+// Row pieces 16-byte aligned: FSDP_UNPACK_THREADS threads per block over
+// FSDP_UNPACK_SUB elements; otherwise FSDP_UNPACK_MIS_THREADS over
+// FSDP_UNPACK_MIS_SUB (both correct for any alignment; measured per case).
+hipError_t launch_unpack(const UnpackTile *tiles, int64_t n, const DevEntry *ents,
+                         const uint16_t *ag_out, bool chunk_aligned, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    if (chunk_aligned) {
+        const int32_t sp = split_for(kTileUnpack, FSDP_UNPACK_SUB);
+        unpack_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_THREADS>
+            <<<grid_for(n, sp), FSDP_UNPACK_THREADS, 0, st>>>(tiles, n, sp, kTileUnpack / sp,
+                                                              ents, ag_out);
+    } else {
+        const int32_t sp = split_for(kTileUnpack, FSDP_UNPACK_MIS_SUB);
+        unpack_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_MIS_THREADS>
+            <<<grid_for(n, sp), FSDP_UNPACK_MIS_THREADS, 0, st>>>(tiles, n, sp, kTileUnpack / sp,
+                                                                  ents, ag_out);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_runs(const CopyTile *tiles, int64_t n, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const int32_t sp = split_for(kTileUnpack, FSDP_UNPACK_SUB);
+    copy_runs_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_THREADS>
+        <<<grid_for(n, sp), FSDP_UNPACK_THREADS, 0, st>>>(tiles, n, sp, kTileUnpack / sp);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack_fp8(const UnpackTile *tiles, int64_t n, const DevEntry *ents,
+                             const uint8_t *ag_out, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    // 16 bytes per lane move 16 elements: twice the elements per block of bf16
+    const int32_t sp = split_for(kTileUnpack, 2 * FSDP_UNPACK_SUB);
+    unpack_fp8_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_THREADS>
+        <<<grid_for(n, sp), FSDP_UNPACK_THREADS, 0, st>>>(tiles, n, sp, kTileUnpack / sp, ents,
+                                                          ag_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_rspack_acc(const PackTile *tiles, int64_t n, const DevEntry *ents, float *out,
+                             hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const int32_t sp = split_for(kTileUnpack, FSDP_UNPACK_SUB);
+    rspack_acc_kernel<FSDP_RSPACK_ACC_POL><<<grid_for(n, sp), kBlock, 0, st>>>(
+        tiles, n, sp, kTileUnpack / sp, ents, out);
+    return hipGetLastError();
+}
+
+// Block shapes as the copy-out's, chosen by whether every row piece of the
+// output is 16-byte aligned.
+hipError_t launch_rspack(const PackTile *tiles, int64_t n, const DevEntry *ents, void *out,
+                         bool f32, bool chunk_aligned, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const int32_t sp = split_for(kTileUnpack, chunk_aligned ? FSDP_UNPACK_SUB : FSDP_UNPACK_MIS_SUB);
+    const unsigned grid = grid_for(n, sp);
+    if (f32)
+        rspack_f32_kernel<FSDP_RSPACK_F32_POL><<<grid, kBlock, 0, st>>>(
+            tiles, n, sp, kTileUnpack / sp, ents, static_cast<float *>(out));
+    else if (chunk_aligned)
+        rspack_bf16_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_THREADS><<<grid, FSDP_UNPACK_THREADS, 0, st>>>(
+            tiles, n, sp, kTileUnpack / sp, ents, static_cast<uint16_t *>(out));
+    else
+        rspack_bf16_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_MIS_THREADS>
+            <<<grid, FSDP_UNPACK_MIS_THREADS, 0, st>>>(tiles, n, sp, kTileUnpack / sp, ents,
+                                                       static_cast<uint16_t *>(out));
+    return hipGetLastError();
+}
+
+}  // namespace fsdp

@@ -1,0 +1,412 @@
+// Local reductions of the reduce-scatter: N bf16 or fp32 gradient
+// contributions summed in fp32 in rank order, then one correctly rounded
+// division by N; and gradient accumulation without sync (fp32 += bf16).
+#include "launch.hpp"
+#include "rows.hpp"
+
+// the bf16 reduction's row-batch and wide variants: non-temporal loads
+#ifndef FSDP_REDUCE_POL
+#define FSDP_REDUCE_POL 1
+#endif
+// the bf16 reduction on aligned rows below the wide threshold: a quad per
+// lane, non-temporal loads and stores
+#ifndef FSDP_REDUCE_QUAD_POL
+#define FSDP_REDUCE_QUAD_POL 3
+#endif
+// Lanes of the fp32 reduction store two 16-byte halves of a 32-byte span per
+// group: non-temporal stores of that pattern cost extra HBM writes (measured
+// 1.1-1.7x the algorithmic bytes), plain stores do not.  The fp32 copy-ins
+// and the accumulation move four elements per lane, so every store
+// instruction of a wave writes 1 KB contiguously, and take non-temporal
+// loads and stores.
+#ifndef FSDP_REDUCE_F32_POL
+#define FSDP_REDUCE_F32_POL 0
+#endif
+// the fp32 reduction on aligned rows: a vector per lane, non-temporal loads
+// and stores
+#ifndef FSDP_REDUCE_F32_QUAD_POL
+#define FSDP_REDUCE_F32_QUAD_POL 3
+#endif
+// gradient accumulation: non-temporal loads and stores
+#ifndef FSDP_ACC_POL
+#define FSDP_ACC_POL 3
+#endif
+// Groups per lane of the bf16 reduction's wide variant, used on aligned rows
+// from FSDP_REDUCE_WIDE_MIN_N ranks (fp32 contributions measured slower read
+// this way: 5.65 vs 5.87 TB/s at N = 64, so their reduction has none).
+#ifndef FSDP_REDUCE_WIDE
+#define FSDP_REDUCE_WIDE 4
+#endif
+#ifndef FSDP_REDUCE_WIDE_MIN_N
+#define FSDP_REDUCE_WIDE_MIN_N 16
+#endif
+
+namespace fsdp {
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// reduce: [N, S] bf16 contributions -> fp32 mean, this rank's pieces
+// ---------------------------------------------------------------------------
+
+template <int POL, int C, bool kChunkAligned>
+__device__ __forceinline__ void reduce_run(float *__restrict__ dst, const uint16_t *__restrict__ src0,
+                                           int64_t len, int64_t S, int32_t N, float fN) {
+    constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
+    const int tid = threadIdx.x;
+    const uint32_t kS = static_cast<uint32_t>((S * 2) & 15);
+    int64_t head = ((16u - (lo32(dst) & 15u)) & 15u) >> 2;
+    if (head > len) head = len;
+    const uint16_t *s0 = src0 + head;
+    const uint32_t k0 = lo32(s0) & 15u;
+    if (kChunkAligned && (k0 | kS) != 0) {
+        // the launch assumed aligned rows; this run is not: element by element
+        for (int64_t e = tid; e < len; e += static_cast<int64_t>(blockDim.x))
+            dst[e] = sum_rows_scalar(src0, S, N, e) / fN;
+        return;
+    }
+    if (tid < head) dst[tid] = sum_rows_scalar(src0, S, N, tid) / fN;
+    const uint32_t dbytes = static_cast<uint32_t>(2 * (len - head));
+    f32x4 *dv = reinterpret_cast<f32x4 *>(dst + head);
+    if constexpr (kChunkAligned && C == 1) {
+        // a quad per lane and pass, two passes 64 quads apart: every wave
+        // instruction contiguous, so the stores take FSDP_REDUCE_QUAD_POL
+        constexpr int QS = (FSDP_REDUCE_QUAD_POL >> 1) & 1;
+        const int64_t nq = (len - head) >> 2;
+        const int64_t lane = tid & 63;
+        const int64_t qstep = static_cast<int64_t>(blockDim.x >> 6) * 128;
+        for (int64_t qb = (tid >> 6) * 128; qb < nq; qb += qstep) {
+            float acc[2][4];
+            sum_rows_quad<FSDP_REDUCE_QUAD_POL & 1, FSDP_REDUCE_ROW_BATCH, 2>(
+                s0, static_cast<uint32_t>(qb + lane) << 3, dbytes, S, N, acc);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int64_t q = qb + lane + 64 * h;
+                if (q < nq)
+                    stp<QS>(dv + q, f32x4{acc[h][0] / fN, acc[h][1] / fN, acc[h][2] / fN,
+                                          acc[h][3] / fN});
+            }
+        }
+        const int64_t done = head + (nq << 2);
+        if (tid < len - done) dst[done + tid] = sum_rows_scalar(src0, S, N, done + tid) / fN;
+        return;
+    }
+    const int64_t ngrp = (len - head) >> 3;
+    for (GroupWalk<kChunkAligned, C> w; w.more(ngrp); w.next()) {
+        float acc[C][8];
+        if constexpr (C == 1)
+            sum_rows8<LN, FSDP_REDUCE_ROW_BATCH, kChunkAligned>(
+                s0, static_cast<uint32_t>(w.g) << 4, dbytes, S, N, k0, kS, acc[0]);
+        else
+            sum_rows_wide<LN, C>(s0, static_cast<uint32_t>(w.g) << 4, dbytes, S, N, acc);
+#pragma unroll
+        for (int q = 0; q < C; ++q) {
+            if (!w.own(ngrp, q)) continue;
+            const int64_t g = w.at(q);
+            const float *a = acc[q];
+            stp<SN>(dv + 2 * g, f32x4{a[0] / fN, a[1] / fN, a[2] / fN, a[3] / fN});
+            stp<SN>(dv + 2 * g + 1, f32x4{a[4] / fN, a[5] / fN, a[6] / fN, a[7] / fN});
+        }
+    }
+    const int64_t done = head + (ngrp << 3);
+    if (tid < len - done) dst[done + tid] = sum_rows_scalar(src0, S, N, done + tid) / fN;
+}
+
+template <int POL, int C, bool kChunkAligned>
+__global__ __launch_bounds__(kBlock) void reduce_kernel(
+    const ReduceTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
+    const DevEntry *__restrict__ ents, const uint16_t *__restrict__ rs_in,
+    int64_t S, int32_t N, float fN) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
+        const ReduceTile tl = tiles[t];
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        reduce_run<POL, C, kChunkAligned>(ents[tl.entry].grad + tl.dst + b, rs_in + tl.src + b,
+                                          len, S, N, fN);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// gradient accumulation without sync: fp32 acc <- acc + fp32(bf16 grad)
+// ---------------------------------------------------------------------------
+
+template <int POL, bool kReset>
+__device__ __forceinline__ void accumulate_run(float *__restrict__ acc, const uint16_t *__restrict__ g,
+                                               int64_t len) {
+    constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
+    const int tid = threadIdx.x;
+    int64_t head = ((16u - (lo32(acc) & 15u)) & 15u) >> 2;
+    if (head > len) head = len;
+    const bool vec = (lo32(g + head) & 7u) == 0;   // 4 bf16 per 16 fp32 bytes
+    if (!vec) head = len;
+    for (int64_t i = tid; i < head; i += kBlock) acc[i] = kReset ? widen(g[i]) : acc[i] + widen(g[i]);
+    if (!vec) return;
+    const int64_t nvec = (len - head) >> 2;
+    f32x4 *av = reinterpret_cast<f32x4 *>(acc + head);
+    const u32x2 *gv = reinterpret_cast<const u32x2 *>(g + head);
+    for (int64_t v = tid; v < nvec; v += kBlock) {
+        const u32x2 w = ldp<LN>(gv + v);
+        const f32x4 x{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
+        if (kReset) {
+            stp<SN>(av + v, x);
+        } else {
+            const f32x4 a = ldp<LN>(av + v);
+            stp<SN>(av + v, f32x4{a.x + x.x, a.y + x.y, a.z + x.z, a.w + x.w});
+        }
+    }
+    const int64_t e = head + (nvec << 2) + tid;
+    if (e < len) acc[e] = kReset ? widen(g[e]) : acc[e] + widen(g[e]);
+}
+
+template <int POL, bool kReset>
+__global__ __launch_bounds__(kBlock) void accumulate_kernel(const EwTile *__restrict__ tiles,
+                                                            int64_t n_tiles, int32_t split,
+                                                            int64_t sub,
+                                                            const DevEntry *__restrict__ ents) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
+        const EwTile tl = tiles[t];
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        const DevEntry en = ents[tl.entry];
+        accumulate_run<POL, kReset>(en.grad_acc + tl.off + b, en.full_grad + tl.off + b, len);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// reduce of fp32 contributions: [N, S] fp32 -> fp32 mean, this rank's pieces
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float sum_rows_scalar_f32(const float *src0, int64_t S, int32_t N,
+                                                     int64_t e) {
+    float acc = src0[e];
+    for (int32_t j = 1; j < N; ++j) acc = acc + src0[static_cast<int64_t>(j) * S + e];
+    return acc;
+}
+
+// Eight consecutive column sums of the N rows of [N, S] fp32 whose row 0
+// starts at base (uniform) plus this lane's byte offset offb (32 bytes per
+// group), added in rank order from row 0; q0 = dword index of base + offb
+// modulo 4, qS = S modulo 4.  Buffer ranges cover exactly the 16-byte chunks
+// holding each row's dbytes data bytes.  Same scheme as sum_rows8: with
+// kChunkAligned (q0 = qS = 0) each row is two aligned loads; otherwise a
+// lane's third chunk is the next lane's first (waves of 63 groups).
+template <int NT, int RB, bool kChunkAligned>
+__device__ __forceinline__ void sum_rows8f(const float *base, uint32_t offb, uint32_t dbytes,
+                                           int64_t S, int32_t N, uint32_t q0, uint32_t qS,
+                                           float (&acc)[8]) {
+    const char *r = reinterpret_cast<const char *>(base);
+    const int64_t Sb = S * 4;
+    for (int32_t j = 0; j < N; j += RB) {
+        f32x4 lo[RB], hi[RB];
+        if (kChunkAligned) {
+            const uint32_t nb = (dbytes + 15u) & ~15u;
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                const char *row = r + (j + i) * Sb;
+                const uint32_t n = j + i < N ? nb : 0u;
+                lo[i] = __builtin_bit_cast(f32x4, bload16<NT>(row, offb, n));
+                hi[i] = __builtin_bit_cast(f32x4, bload16<NT>(row, offb + 16, n));
+            }
+        } else {
+            uint32_t qq[RB];
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                qq[i] = (q0 + static_cast<uint32_t>(j + i) * qS) & 3u;
+                const char *al = r + (j + i) * Sb - 4 * qq[i];
+                const uint32_t n = j + i < N ? (4 * qq[i] + dbytes + 15u) & ~15u : 0u;
+                lo[i] = __builtin_bit_cast(f32x4, bload16<NT>(al, offb, n));
+                hi[i] = __builtin_bit_cast(f32x4, bload16<NT>(al, offb + 16, n));
+            }
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                const f32x4 c = __builtin_bit_cast(
+                    f32x4, next_lane16(__builtin_bit_cast(u32x4, lo[i])));
+                select8f(lo[i], hi[i], c, qq[i], lo[i], hi[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            if (j + i < N) {
+                const float x[8] = {lo[i].x, lo[i].y, lo[i].z, lo[i].w,
+                                    hi[i].x, hi[i].y, hi[i].z, hi[i].w};
+                if (j + i == 0) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[e] = x[e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[e] = acc[e] + x[e];
+                }
+            }
+        }
+    }
+}
+
+template <int POL, bool kChunkAligned>
+__device__ __forceinline__ void reduce_f32_run(float *__restrict__ dst,
+                                               const float *__restrict__ src0, int64_t len,
+                                               int64_t S, int32_t N, float fN) {
+    constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
+    const int tid = threadIdx.x;
+    int64_t head = ((16u - (lo32(dst) & 15u)) & 15u) >> 2;
+    if (head > len) head = len;
+    const float *s0 = src0 + head;
+    const uint32_t q0 = (lo32(s0) >> 2) & 3u;
+    const uint32_t qS = static_cast<uint32_t>(S & 3);
+    if (kChunkAligned && (q0 | qS) != 0) {
+        // the launch assumed aligned rows; this run is not: element by element
+        for (int64_t e = tid; e < len; e += static_cast<int64_t>(blockDim.x))
+            dst[e] = sum_rows_scalar_f32(src0, S, N, e) / fN;
+        return;
+    }
+    if (tid < head) dst[tid] = sum_rows_scalar_f32(src0, S, N, tid) / fN;
+    const uint32_t dbytes = static_cast<uint32_t>(4 * (len - head));
+    f32x4 *dv = reinterpret_cast<f32x4 *>(dst + head);
+    if constexpr (kChunkAligned) {
+        // four elements (one vector) per lane and pass, two passes 64
+        // vectors apart: every wave instruction contiguous, so loads and
+        // stores take FSDP_REDUCE_F32_QUAD_POL
+        constexpr int QL = FSDP_REDUCE_F32_QUAD_POL & 1, QS = (FSDP_REDUCE_F32_QUAD_POL >> 1) & 1;
+        const char *r = reinterpret_cast<const char *>(s0);
+        const int64_t Sb = S * 4;
+        const uint32_t nb = (dbytes + 15u) & ~15u;
+        const int64_t nq = (len - head) >> 2;
+        const int64_t lane = tid & 63;
+        const int64_t qstep = static_cast<int64_t>(blockDim.x >> 6) * 128;
+        for (int64_t qb = (tid >> 6) * 128; qb < nq; qb += qstep) {
+            const uint32_t off = static_cast<uint32_t>(qb + lane) << 4;
+            f32x4 acc[2];
+            for (int32_t j = 0; j < N; j += FSDP_REDUCE_ROW_BATCH) {
+                f32x4 x[FSDP_REDUCE_ROW_BATCH][2];
+#pragma unroll
+                for (int i = 0; i < FSDP_REDUCE_ROW_BATCH; ++i) {
+                    const char *row = r + (j + i) * Sb;
+                    const uint32_t n = j + i < N ? nb : 0u;
+                    x[i][0] = __builtin_bit_cast(f32x4, bload16<QL>(row, off, n));
+                    x[i][1] = __builtin_bit_cast(f32x4, bload16<QL>(row, off + 1024u, n));
+                }
+#pragma unroll
+                for (int i = 0; i < FSDP_REDUCE_ROW_BATCH; ++i) {
+                    if (j + i >= N) continue;
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const f32x4 y = x[i][h];
+                        acc[h] = j + i == 0 ? y
+                                            : f32x4{acc[h].x + y.x, acc[h].y + y.y,
+                                                    acc[h].z + y.z, acc[h].w + y.w};
+                    }
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int64_t q = qb + lane + 64 * h;
+                if (q < nq)
+                    stp<QS>(dv + q, f32x4{acc[h].x / fN, acc[h].y / fN, acc[h].z / fN,
+                                          acc[h].w / fN});
+            }
+        }
+        const int64_t done = head + (nq << 2);
+        if (tid < len - done) dst[done + tid] = sum_rows_scalar_f32(src0, S, N, done + tid) / fN;
+        return;
+    }
+    const int64_t ngrp = (len - head) >> 3;
+    for (GroupWalk<kChunkAligned> w; w.more(ngrp); w.next()) {
+        float acc[8];
+        sum_rows8f<LN, FSDP_REDUCE_ROW_BATCH, kChunkAligned>(
+            s0, static_cast<uint32_t>(w.g) << 5, dbytes, S, N, q0, qS, acc);
+        if (w.own(ngrp)) {
+            const int64_t g = w.g;
+            stp<SN>(dv + 2 * g, f32x4{acc[0] / fN, acc[1] / fN, acc[2] / fN, acc[3] / fN});
+            stp<SN>(dv + 2 * g + 1, f32x4{acc[4] / fN, acc[5] / fN, acc[6] / fN, acc[7] / fN});
+        }
+    }
+    const int64_t done = head + (ngrp << 3);
+    if (tid < len - done) dst[done + tid] = sum_rows_scalar_f32(src0, S, N, done + tid) / fN;
+}
+
+template <int POL, bool kChunkAligned>
+__global__ __launch_bounds__(kBlock) void reduce_f32_kernel(
+    const ReduceTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
+    const DevEntry *__restrict__ ents, const float *__restrict__ rs_in, int64_t S, int32_t N,
+    float fN) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
+        const ReduceTile tl = tiles[t];
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        reduce_f32_run<POL, kChunkAligned>(ents[tl.entry].grad + tl.dst + b, rs_in + tl.src + b,
+                                          len, S, N, fN);
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// launchers (called by the C ABI after validation)
+// ---------------------------------------------------------------------------
+
+hipError_t launch_reduce(const ReduceTile *tiles, int64_t n, const DevEntry *ents,
+                         const uint16_t *rs_in, int64_t S, int32_t N, bool chunk_aligned,
+                         hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const float fN = static_cast<float>(N);
+    if (chunk_aligned && N >= FSDP_REDUCE_WIDE_MIN_N) {
+        // one wave per block, each block one sub-range of 64 * 8 * FSDP_REDUCE_WIDE elements
+        constexpr int64_t wsub = 64 * 8 * FSDP_REDUCE_WIDE;
+        static_assert(kTileReduce % wsub == 0, "wide sub-range must divide the tile");
+        const int32_t wsp = static_cast<int32_t>(kTileReduce / wsub);
+        reduce_kernel<FSDP_REDUCE_POL, FSDP_REDUCE_WIDE, true>
+            <<<grid_for(n, wsp), 64, 0, st>>>(tiles, n, wsp, wsub, ents, rs_in, S, N, fN);
+        return hipGetLastError();
+    }
+    const RowSplit rsp = row_split(kTileReduce, split_rows(kTileReduce, N, 0), chunk_aligned);
+    const unsigned grid = grid_for(n, rsp.split);
+    if (chunk_aligned)
+        reduce_kernel<FSDP_REDUCE_POL, 1, true>
+            <<<grid, kBlock, 0, st>>>(tiles, n, rsp.split, rsp.sub, ents, rs_in, S, N, fN);
+    else
+        reduce_kernel<FSDP_REDUCE_POL, 1, false>
+            <<<grid, kBlock, 0, st>>>(tiles, n, rsp.split, rsp.sub, ents, rs_in, S, N, fN);
+    return hipGetLastError();
+}
+
+hipError_t launch_accumulate(const EwTile *tiles, int64_t n, const DevEntry *ents, bool reset,
+                             hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const int32_t sp = split_for(kTileAdamw, FSDP_ADAMW_SUB);
+    const unsigned grid = grid_for(n, sp);
+    if (reset)
+        accumulate_kernel<FSDP_ACC_POL, true><<<grid, kBlock, 0, st>>>(tiles, n, sp, kTileAdamw / sp, ents);
+    else
+        accumulate_kernel<FSDP_ACC_POL, false><<<grid, kBlock, 0, st>>>(tiles, n, sp, kTileAdamw / sp, ents);
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce_f32(const ReduceTile *tiles, int64_t n, const DevEntry *ents,
+                             const float *rs_in, int64_t S, int32_t N, bool chunk_aligned,
+                             hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const float fN = static_cast<float>(N);
+    // fp32 rows carry twice the bytes of bf16 rows per element
+    const RowSplit rsp = row_split(kTileReduce, split_rows(kTileReduce, 2 * N, 0), chunk_aligned);
+    const unsigned grid = grid_for(n, rsp.split);
+    if (chunk_aligned)
+        reduce_f32_kernel<FSDP_REDUCE_F32_POL, true>
+            <<<grid, kBlock, 0, st>>>(tiles, n, rsp.split, rsp.sub, ents, rs_in, S, N, fN);
+    else
+        reduce_f32_kernel<FSDP_REDUCE_F32_POL, false>
+            <<<grid, kBlock, 0, st>>>(tiles, n, rsp.split, rsp.sub, ents, rs_in, S, N, fN);
+    return hipGetLastError();
+}
+
+}  // namespace fsdp

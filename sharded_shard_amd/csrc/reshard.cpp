@@ -16,10 +16,10 @@
 #include <vector>
 
 #include "../../include/fsdp_shard.h"
+#include "launch.hpp"
 #include "plan.hpp"
 
 namespace fsdp {
-hipError_t launch_copy_runs(const CopyTile *tiles, int64_t n, hipStream_t st);
 fsdp_status set_error(fsdp_status s, const std::string &msg);
 fsdp_status set_hip_error(hipError_t e, const char *what);
 hipError_t injected_fault();

@@ -10,6 +10,7 @@
 #include <cstdint>
 #include <vector>
 
+#include "../../sharded_shard_amd/csrc/launch.hpp"
 #include "../../sharded_shard_amd/csrc/plan.hpp"
 #include "harness.hpp"
 
