@@ -85,8 +85,10 @@ def measured_traffic(workload, rank, align, kind):
     return None
 
 
-TRAFFIC_SOURCE = ("committed rocprofv3 --pmc summary (profiles/pmc_traffic.json), valid only "
-                  "for the kernel source it was taken on (null otherwise)")
+TRAFFIC_SOURCE = ("HBM bytes per launch from the rocprofv3 memory-request counters "
+                  "(TCC_EA0_RDREQ_32B/64B/128B, TCC_EA0_WRREQ/WRREQ_64B) in the committed "
+                  "profiles/pmc_traffic.json; valid only for the kernel sources it was taken on "
+                  "(null otherwise)")
 
 
 KERNEL_NAMES = {"step": "step_kernel (fused reduce+adamw+pack)", "reduce": "reduce_kernel",
