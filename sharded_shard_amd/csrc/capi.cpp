@@ -613,7 +613,7 @@ fsdp_status fsdp_unpack_allgather_fp8(const fsdp_plan *p, const uint8_t *ag_out,
     return launched(guarded([&] {
                         return fsdp::launch_unpack_fp8(
                             p->d_unpack, static_cast<int64_t>(p->L.unpack.size()), p->d_entries,
-                            ag_out, static_cast<hipStream_t>(stream));
+                            ag_out, chunk_aligned(p, ag_out), static_cast<hipStream_t>(stream));
                     }),
                     "fsdp_unpack_allgather_fp8: launch");
 }
@@ -656,7 +656,7 @@ fsdp_status fsdp_pack_reduce_scatter_acc(const fsdp_plan *p, float *rs_out, void
     return launched(guarded([&] {
                         return fsdp::launch_rspack_acc(
                             p->d_rspack, static_cast<int64_t>(p->L.rspack.size()), p->d_entries,
-                            rs_out, static_cast<hipStream_t>(stream));
+                            rs_out, chunk_aligned(p, rs_out), static_cast<hipStream_t>(stream));
                     }),
                     "fsdp_pack_reduce_scatter_acc: launch");
 }

@@ -112,13 +112,13 @@ __device__ __forceinline__ void copy_run_bf16(uint16_t *__restrict__ dst,
     if (tid < len - done) dst[done + tid] = src[done + tid];
 }
 
-template <int POL, int TB>
+template <int POL, int TB, bool kRemap>
 __global__ __launch_bounds__(TB) void unpack_kernel(
     const UnpackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
     const DevEntry *__restrict__ ents, const uint16_t *__restrict__ ag_out) {
     const int64_t L = sub;
     const int64_t nvt = n_tiles * split;
-    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+    for (int64_t vt = first_vt<kRemap>(); vt < nvt; vt += gridDim.x) {
         int64_t t, b;
         sub_range(vt, split, L, &t, &b);
         const UnpackTile tl = tiles[t];
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(TB) void copy_runs_kernel(const CopyTile *__restric
                                                            int64_t sub) {
     const int64_t L = sub;
     const int64_t nvt = n_tiles * split;
-    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+    for (int64_t vt = first_vt(); vt < nvt; vt += gridDim.x) {
         int64_t t, b;
         sub_range(vt, split, L, &t, &b);
         const CopyTile tl = tiles[t];
@@ -149,13 +149,13 @@ __global__ __launch_bounds__(TB) void copy_runs_kernel(const CopyTile *__restric
 // reduce-scatter copy-in: full bf16 gradients -> [N, S] (bf16 or fp32)
 // ---------------------------------------------------------------------------
 
-template <int POL, int TB>
+template <int POL, int TB, bool kRemap>
 __global__ __launch_bounds__(TB) void rspack_bf16_kernel(
     const PackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
     const DevEntry *__restrict__ ents, uint16_t *__restrict__ out) {
     const int64_t L = sub;
     const int64_t nvt = n_tiles * split;
-    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+    for (int64_t vt = first_vt<kRemap>(); vt < nvt; vt += gridDim.x) {
         int64_t t, b;
         sub_range(vt, split, L, &t, &b);
         const PackTile tl = tiles[t];
@@ -241,13 +241,13 @@ __device__ __forceinline__ void widen_run(float *__restrict__ dst, const uint16_
     zero_f32<SN>(dst, valid, len);
 }
 
-template <int POL>
+template <int POL, bool kRemap>
 __global__ __launch_bounds__(kBlock) void rspack_f32_kernel(
     const PackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
     const DevEntry *__restrict__ ents, float *__restrict__ out) {
     const int64_t L = sub;
     const int64_t nvt = n_tiles * split;
-    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+    for (int64_t vt = first_vt<kRemap>(); vt < nvt; vt += gridDim.x) {
         int64_t t, b;
         sub_range(vt, split, L, &t, &b);
         const PackTile tl = tiles[t];
@@ -296,13 +296,13 @@ __device__ __forceinline__ void copy_run_u8(uint8_t *__restrict__ dst, const uin
     if (tid < len - done) dst[done + tid] = src[done + tid];
 }
 
-template <int POL, int TB>
+template <int POL, int TB, bool kRemap>
 __global__ __launch_bounds__(TB) void unpack_fp8_kernel(
     const UnpackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
     const DevEntry *__restrict__ ents, const uint8_t *__restrict__ ag_out) {
     const int64_t L = sub;
     const int64_t nvt = n_tiles * split;
-    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+    for (int64_t vt = first_vt<kRemap>(); vt < nvt; vt += gridDim.x) {
         int64_t t, b;
         sub_range(vt, split, L, &t, &b);
         const UnpackTile tl = tiles[t];
@@ -356,13 +356,13 @@ __device__ __forceinline__ void copy_f32_run(float *__restrict__ dst, const floa
     zero_f32<SN>(dst, valid, len);
 }
 
-template <int POL>
+template <int POL, bool kRemap>
 __global__ __launch_bounds__(kBlock) void rspack_acc_kernel(
     const PackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
     const DevEntry *__restrict__ ents, float *__restrict__ out) {
     const int64_t L = sub;
     const int64_t nvt = n_tiles * split;
-    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+    for (int64_t vt = first_vt<kRemap>(); vt < nvt; vt += gridDim.x) {
         int64_t t, b;
         sub_range(vt, split, L, &t, &b);
         const PackTile tl = tiles[t];
@@ -388,12 +388,12 @@ hipError_t launch_unpack(const UnpackTile *tiles, int64_t n, const DevEntry *ent
     if (n == 0) return hipSuccess;
     if (chunk_aligned) {
         const int32_t sp = split_for(kTileUnpack, FSDP_UNPACK_SUB);
-        unpack_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_THREADS>
+        unpack_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_THREADS, false>
             <<<grid_for(n, sp), FSDP_UNPACK_THREADS, 0, st>>>(tiles, n, sp, kTileUnpack / sp,
                                                               ents, ag_out);
     } else {
         const int32_t sp = split_for(kTileUnpack, FSDP_UNPACK_MIS_SUB);
-        unpack_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_MIS_THREADS>
+        unpack_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_MIS_THREADS, true>
             <<<grid_for(n, sp), FSDP_UNPACK_MIS_THREADS, 0, st>>>(tiles, n, sp, kTileUnpack / sp,
                                                                   ents, ag_out);
     }
@@ -409,40 +409,53 @@ hipError_t launch_copy_runs(const CopyTile *tiles, int64_t n, hipStream_t st) {
 }
 
 hipError_t launch_unpack_fp8(const UnpackTile *tiles, int64_t n, const DevEntry *ents,
-                             const uint8_t *ag_out, hipStream_t st) {
+                             const uint8_t *ag_out, bool chunk_aligned, hipStream_t st) {
     if (n == 0) return hipSuccess;
     // 16 bytes per lane move 16 elements: twice the elements per block of bf16
     const int32_t sp = split_for(kTileUnpack, 2 * FSDP_UNPACK_SUB);
-    unpack_fp8_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_THREADS>
-        <<<grid_for(n, sp), FSDP_UNPACK_THREADS, 0, st>>>(tiles, n, sp, kTileUnpack / sp, ents,
-                                                          ag_out);
+    if (chunk_aligned)
+        unpack_fp8_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_THREADS, false>
+            <<<grid_for(n, sp), FSDP_UNPACK_THREADS, 0, st>>>(tiles, n, sp, kTileUnpack / sp,
+                                                              ents, ag_out);
+    else
+        unpack_fp8_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_THREADS, true>
+            <<<grid_for(n, sp), FSDP_UNPACK_THREADS, 0, st>>>(tiles, n, sp, kTileUnpack / sp,
+                                                              ents, ag_out);
     return hipGetLastError();
 }
 
 hipError_t launch_rspack_acc(const PackTile *tiles, int64_t n, const DevEntry *ents, float *out,
-                             hipStream_t st) {
+                             bool chunk_aligned, hipStream_t st) {
     if (n == 0) return hipSuccess;
     const int32_t sp = split_for(kTileUnpack, FSDP_UNPACK_SUB);
-    rspack_acc_kernel<FSDP_RSPACK_ACC_POL><<<grid_for(n, sp), kBlock, 0, st>>>(
-        tiles, n, sp, kTileUnpack / sp, ents, out);
+    if (chunk_aligned)
+        rspack_acc_kernel<FSDP_RSPACK_ACC_POL, false><<<grid_for(n, sp), kBlock, 0, st>>>(
+            tiles, n, sp, kTileUnpack / sp, ents, out);
+    else
+        rspack_acc_kernel<FSDP_RSPACK_ACC_POL, true><<<grid_for(n, sp), kBlock, 0, st>>>(
+            tiles, n, sp, kTileUnpack / sp, ents, out);
     return hipGetLastError();
 }
 
 // Block shapes as the copy-out's, chosen by whether every row piece of the
-// output is 16-byte aligned.
+// output is 16-byte aligned; misaligned rows take the XCD remap (first_vt).
 hipError_t launch_rspack(const PackTile *tiles, int64_t n, const DevEntry *ents, void *out,
                          bool f32, bool chunk_aligned, hipStream_t st) {
     if (n == 0) return hipSuccess;
     const int32_t sp = split_for(kTileUnpack, chunk_aligned ? FSDP_UNPACK_SUB : FSDP_UNPACK_MIS_SUB);
     const unsigned grid = grid_for(n, sp);
-    if (f32)
-        rspack_f32_kernel<FSDP_RSPACK_F32_POL><<<grid, kBlock, 0, st>>>(
+    if (f32 && chunk_aligned)
+        rspack_f32_kernel<FSDP_RSPACK_F32_POL, false><<<grid, kBlock, 0, st>>>(
+            tiles, n, sp, kTileUnpack / sp, ents, static_cast<float *>(out));
+    else if (f32)
+        rspack_f32_kernel<FSDP_RSPACK_F32_POL, true><<<grid, kBlock, 0, st>>>(
             tiles, n, sp, kTileUnpack / sp, ents, static_cast<float *>(out));
     else if (chunk_aligned)
-        rspack_bf16_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_THREADS><<<grid, FSDP_UNPACK_THREADS, 0, st>>>(
-            tiles, n, sp, kTileUnpack / sp, ents, static_cast<uint16_t *>(out));
+        rspack_bf16_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_THREADS, false>
+            <<<grid, FSDP_UNPACK_THREADS, 0, st>>>(tiles, n, sp, kTileUnpack / sp, ents,
+                                                   static_cast<uint16_t *>(out));
     else
-        rspack_bf16_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_MIS_THREADS>
+        rspack_bf16_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_MIS_THREADS, true>
             <<<grid, FSDP_UNPACK_MIS_THREADS, 0, st>>>(tiles, n, sp, kTileUnpack / sp, ents,
                                                        static_cast<uint16_t *>(out));
     return hipGetLastError();

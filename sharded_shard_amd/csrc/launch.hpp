@@ -46,13 +46,13 @@ hipError_t launch_accumulate(const EwTile *tiles, int64_t n, const DevEntry *ent
 hipError_t launch_pack_fp8(const PackTile *tiles, int64_t n, const DevEntry *ents, uint8_t *ag_in,
                            const float *scales, hipStream_t st);
 hipError_t launch_unpack_fp8(const UnpackTile *tiles, int64_t n, const DevEntry *ents,
-                             const uint8_t *ag_out, hipStream_t st);
+                             const uint8_t *ag_out, bool chunk_aligned, hipStream_t st);
 // per-parameter amax of the master shards into amax[0 .. n_params)
 hipError_t launch_amax(const EwTile *tiles, int64_t n, const DevEntry *ents, float *amax,
                        int32_t n_params, hipStream_t st);
 // reduce-scatter copy-in from the fp32 accumulators
 hipError_t launch_rspack_acc(const PackTile *tiles, int64_t n, const DevEntry *ents, float *out,
-                             hipStream_t st);
+                             bool chunk_aligned, hipStream_t st);
 // resharding: runs of 2-byte units between absolute addresses
 hipError_t launch_copy_runs(const CopyTile *tiles, int64_t n, hipStream_t st);
 

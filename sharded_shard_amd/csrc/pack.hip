@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kBlock) void pack_kernel(
     const DevEntry *__restrict__ ents, uint16_t *__restrict__ ag_in) {
     const int64_t L = sub;
     const int64_t nvt = n_tiles * split;
-    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+    for (int64_t vt = first_vt(); vt < nvt; vt += gridDim.x) {
         int64_t t, b;
         sub_range(vt, split, L, &t, &b);
         const PackTile tl = tiles[t];
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(kBlock) void pack_fp8_kernel(
     const float *__restrict__ scales) {
     const int64_t L = sub;
     const int64_t nvt = n_tiles * split;
-    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+    for (int64_t vt = first_vt(); vt < nvt; vt += gridDim.x) {
         int64_t t, b;
         sub_range(vt, split, L, &t, &b);
         const PackTile tl = tiles[t];
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kBlock) void amax_kernel(const EwTile *__restrict__
     const int64_t L = sub;
     const int64_t nvt = n_tiles * split;
     const int tid = threadIdx.x;
-    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+    for (int64_t vt = first_vt(); vt < nvt; vt += gridDim.x) {
         int64_t t, b;
         sub_range(vt, split, L, &t, &b);
         const EwTile tl = tiles[t];

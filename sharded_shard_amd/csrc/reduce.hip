@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kBlock) void reduce_kernel(
     int64_t S, int32_t N, float fN) {
     const int64_t L = sub;
     const int64_t nvt = n_tiles * split;
-    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+    for (int64_t vt = first_vt(); vt < nvt; vt += gridDim.x) {
         int64_t t, b;
         sub_range(vt, split, L, &t, &b);
         const ReduceTile tl = tiles[t];
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kBlock) void accumulate_kernel(const EwTile *__rest
                                                             const DevEntry *__restrict__ ents) {
     const int64_t L = sub;
     const int64_t nvt = n_tiles * split;
-    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+    for (int64_t vt = first_vt(); vt < nvt; vt += gridDim.x) {
         int64_t t, b;
         sub_range(vt, split, L, &t, &b);
         const EwTile tl = tiles[t];
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(kBlock) void reduce_f32_kernel(
     float fN) {
     const int64_t L = sub;
     const int64_t nvt = n_tiles * split;
-    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+    for (int64_t vt = first_vt(); vt < nvt; vt += gridDim.x) {
         int64_t t, b;
         sub_range(vt, split, L, &t, &b);
         const ReduceTile tl = tiles[t];

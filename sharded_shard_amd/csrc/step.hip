@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kBlock) void adamw_kernel(
     const DevEntry *__restrict__ ents, AdamwScalars c) {
     const int64_t L = sub;
     const int64_t nvt = n_tiles * split;
-    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+    for (int64_t vt = first_vt(); vt < nvt; vt += gridDim.x) {
         int64_t t, b;
         sub_range(vt, split, L, &t, &b);
         const EwTile tl = tiles[t];
@@ -354,7 +354,7 @@ __device__ __forceinline__ void step_tiles(const PackTile *__restrict__ tiles, i
                                            float fN, const AdamwScalars &c) {
     const int64_t L = sub;
     const int64_t nvt = n_tiles * split;
-    for (int64_t vt = blockIdx.x; vt < nvt; vt += gridDim.x) {
+    for (int64_t vt = first_vt(); vt < nvt; vt += gridDim.x) {
         int64_t t, b;
         sub_range(vt, split, L, &t, &b);
         const PackTile tl = tiles[t];

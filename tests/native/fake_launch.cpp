@@ -158,7 +158,7 @@ hipError_t launch_pack_fp8(const PackTile *tiles, int64_t n, const DevEntry *ent
 }
 
 hipError_t launch_unpack_fp8(const UnpackTile *tiles, int64_t n, const DevEntry *ents,
-                             const uint8_t *ag_out, hipStream_t) {
+                             const uint8_t *ag_out, bool, hipStream_t) {
     ++harness::launches;
     for (int64_t i = 0; i < n; ++i) {
         const UnpackTile &t = tiles[i];
@@ -177,7 +177,7 @@ hipError_t launch_amax(const EwTile *tiles, int64_t n, const DevEntry *ents, flo
 }
 
 hipError_t launch_rspack_acc(const PackTile *tiles, int64_t n, const DevEntry *ents, float *out,
-                             hipStream_t) {
+                             bool, hipStream_t) {
     ++harness::launches;
     for (int64_t i = 0; i < n; ++i) {
         const PackTile &t = tiles[i];
