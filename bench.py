@@ -22,7 +22,8 @@ same workload.  The same record for each workload named by --also (the
 
 By default reduce, AdamW and pack run as one fused launch per group
 (fsdp_step_shard, bit-identical to the three calls); --unfused runs them as
-three launches.
+separate kernels through a group set: a reduce per group, then one AdamW and
+one copy-in launch over every group.
 """
 from __future__ import annotations
 
@@ -94,6 +95,9 @@ TRAFFIC_SOURCE = ("HBM bytes per launch from the rocprofv3 memory-request counte
 KERNEL_NAMES = {"step": "step_kernel (fused reduce+adamw+pack)", "reduce": "reduce_kernel",
                 "adamw": "adamw_kernel", "pack": "pack_kernel (copy-in)",
                 "unpack": "unpack_kernel (copy-out)"}
+# kinds the separate-kernel path launches once per step over every group (a
+# group set); the others run once per group
+SET_KINDS = ("adamw", "pack")
 
 
 def parse():
@@ -108,7 +112,8 @@ def parse():
     ap.add_argument("--rank", type=int, default=None, help="simulated rank (default: the config's)")
     ap.add_argument("--align", type=int, default=1, choices=[1, 8])
     ap.add_argument("--unfused", action="store_true",
-                    help="run reduce, adamw and pack as three launches instead of the fused step")
+                    help="run reduce (per group), adamw and pack (one launch each over every "
+                         "group) instead of the fused step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown-steps", type=int, default=3,
                     help="extra untimed steps per kernel kind, with events around its launches")
@@ -298,20 +303,39 @@ def _pct(sorted_vals, q):
     return round(sorted_vals[i], 4)
 
 
-def measure_isolated(groups, kinds, n, rank, hp, rs_arena, ag_arena, fused, stream):
-    """Each kernel kind launched alone per group after the 256 MB MALL has
+def measure_isolated(groups, kinds, n, rank, hp, rs_arena, ag_arena, fused, stream,
+                     gset=None, arena=None):
+    """Each kernel kind launched alone per group (or, for the kinds a group
+    set runs in one launch, alone over every group) after the 256 MB MALL has
     been flushed, so no input can come from the last-level cache: the
     per-kernel roofline protocol.  The flush writes 1 GiB and then reads
     another 1 GiB, so the cache holds only clean lines when the timed launch
     starts (no write-back of the flush lands in it).  Sum of algorithmic
-    bytes / sum of event-timed launch durations over the groups."""
+    bytes / sum of event-timed launch durations over the launches."""
     import torch
+    from sharded_shard_amd import capi
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=rs_arena[0].device)
     sweep = torch.zeros(1 << 28, dtype=torch.int32, device=rs_arena[0].device)
     res = {}
     t = 10_000
     for k in kinds:
         tot_b = tot_ms = 0.0
+        if gset is not None and k in SET_KINDS:
+            launch = {"adamw": lambda: capi.fsdp_adamw_groups(gset, step=t, stream=stream, **hp),
+                      "pack": lambda: capi.fsdp_pack_allgather_groups(gset, arena, stream)}[k]
+            flush.fill_(1)
+            sweep.max()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            launch()
+            b.record(stream)
+            b.synchronize()
+            gbps = sum(algorithmic_bytes(g.S, g.V, g.F, n, fused)[k] for g in groups) \
+                / (a.elapsed_time(b) * 1e-3) / 1e9
+            t += 1
+            res[k] = {"isolated_GBps": round(gbps, 1),
+                      "isolated_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+            continue
         for gi, g in enumerate(groups):
             rs = rs_arena[gi & 1][:n * g.S]
             ag_in = ag_arena[gi & 1][rank * g.S:(rank + 1) * g.S]
@@ -449,13 +473,33 @@ def run_workload(cfg_index, args, dev, copy_gbps):
     step_counter = [0]
     # One native call per step runs every group's launches (no per-launch
     # Python on the critical path); HIP events around one kernel kind per
-    # group are recorded by the library on the same stream.
-    execute = capi.StepGroupsCall(
-        [g.plan for g in groups],
-        [rs_arena[gi & 1][:n * g.S] for gi, g in enumerate(groups)],
-        [ag_arena[gi & 1][rank * g.S:(rank + 1) * g.S] for gi, g in enumerate(groups)],
-        [ag_arena[gi & 1][:n * g.S] for gi, g in enumerate(groups)],
-        flags=0 if fused else capi.FSDP_STEP_UNFUSED, stream=stream, **hp)
+    # group are recorded by the library on the same stream.  The fused step
+    # runs per group; the separate kernels run as a group set: a reduce per
+    # group, one AdamW and one copy-in launch over every group (into an arena
+    # of every group's segment), a copy-out per group.
+    gset = arena = None
+    if fused:
+        execute = capi.StepGroupsCall(
+            [g.plan for g in groups],
+            [rs_arena[gi & 1][:n * g.S] for gi, g in enumerate(groups)],
+            [ag_arena[gi & 1][rank * g.S:(rank + 1) * g.S] for gi, g in enumerate(groups)],
+            [ag_arena[gi & 1][:n * g.S] for gi, g in enumerate(groups)],
+            stream=stream, **hp)
+    else:
+        gset = capi.fsdp_group_set_create([g.plan for g in groups], stream)
+        arena = torch.empty(max(1, capi.fsdp_group_set_segment(gset, 0)[1]), dtype=torch.int16,
+                            device=dev)
+        execute = capi.StepGroupSetCall(
+            gset, [g.plan for g in groups],
+            [rs_arena[gi & 1][:n * g.S] for gi, g in enumerate(groups)], arena,
+            [ag_arena[gi & 1][:n * g.S] for gi, g in enumerate(groups)], stream=stream, **hp)
+    one_launch = set() if fused else set(SET_KINDS)
+
+    def launch_bytes(kind, gi):
+        """Algorithmic bytes of the launch of `kind` timed by group gi's events."""
+        if kind in one_launch:
+            return byts[kind]
+        return algorithmic_bytes(groups[gi].S, groups[gi].V, groups[gi].F, n, fused)[kind]
     kernel_id = {"step": capi.FSDP_KERNEL_STEP, "reduce": capi.FSDP_KERNEL_REDUCE,
                  "adamw": capi.FSDP_KERNEL_ADAMW, "pack": capi.FSDP_KERNEL_PACK,
                  "unpack": capi.FSDP_KERNEL_UNPACK}
@@ -473,9 +517,6 @@ def run_workload(cfg_index, args, dev, copy_gbps):
         else:
             execute(step_counter[0], kernel_id[kind], evs)
 
-    def elapsed(evs):
-        return [evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(len(groups))]
-
     def elapsed_sampled(evs):
         return [(i, evs[2 * i].elapsed_time(evs[2 * i + 1])) for i in range(len(groups))
                 if evs[2 * i] is not None]
@@ -490,7 +531,11 @@ def run_workload(cfg_index, args, dev, copy_gbps):
     timed_events = []
     for k in range(args.steps):
         evs = new_events()
-        timed_events.append([e if (i // 2) % args.steps == k else None for i, e in enumerate(evs)])
+        if dominant in one_launch:      # its one launch per step, every step
+            timed_events.append([e if i < 2 else None for i, e in enumerate(evs)])
+        else:
+            timed_events.append([e if (i // 2) % args.steps == k else None
+                                 for i, e in enumerate(evs)])
     torch.cuda.synchronize()
     print(f"bench: {args.warmup} warmup steps done", file=sys.stderr, flush=True)
 
@@ -511,8 +556,7 @@ def run_workload(cfg_index, args, dev, copy_gbps):
     dom = [x for evs in timed_events for x in elapsed_sampled(evs)]
     dom_launches = len(dom)
     dom_avg_ms = sum(ms for _, ms in dom) / max(1, dom_launches)
-    dom_bytes_per_launch = sum(algorithmic_bytes(groups[i].S, groups[i].V, groups[i].F, n, fused)[dominant]
-                               for i, _ in dom) / max(1, dom_launches)
+    dom_bytes_per_launch = sum(launch_bytes(dominant, i) for i, _ in dom) / max(1, dom_launches)
     achieved = dom_bytes_per_launch / (dom_avg_ms * 1e-3) / 1e9
 
     # per-kernel breakdown: extra untimed steps, each timing one kernel kind
@@ -520,12 +564,15 @@ def run_workload(cfg_index, args, dev, copy_gbps):
     per = {k: 0.0 for k in kinds}
     if args.breakdown_steps > 0:
         runs = {k: [new_events() for _ in range(args.breakdown_steps)] for k in kinds}
+        for k in one_launch:
+            runs[k] = [[e if i < 2 else None for i, e in enumerate(evs)] for evs in runs[k]]
         torch.cuda.synchronize()
         for k in kinds:
             for evs in runs[k]:
                 step(k, evs)
         torch.cuda.synchronize()
-        per = {k: sum(sum(elapsed(evs)) for evs in runs[k]) / args.breakdown_steps for k in kinds}
+        per = {k: sum(sum(ms for _, ms in elapsed_sampled(evs)) for evs in runs[k])
+               / args.breakdown_steps for k in kinds}
 
     def frac(gbps, ref):
         return round(gbps / ref, 4) if gbps and ref else None
@@ -534,13 +581,15 @@ def run_workload(cfg_index, args, dev, copy_gbps):
     for k in kinds:
         gbps = byts[k] / (per[k] * 1e-3) / 1e9 if per[k] else None
         kernels[k] = {"kernel": KERNEL_NAMES[k], "ms_per_step": round(per[k], 4),
+                      "launches_per_step": 1 if k in one_launch else len(groups),
                       "algorithmic_GB_per_step": round(byts[k] / 1e9, 4),
                       "GBps": round(gbps, 1) if gbps else None,
                       "hbm_frac": frac(gbps, HBM_PEAK_GBPS),
                       "frac_of_copy_ceiling": frac(gbps, copy_gbps),
                       "traffic_bytes_per_launch": measured_traffic(cfg.name, rank, args.align, k)}
     if args.isolated:
-        iso = measure_isolated(groups, kinds, n, rank, hp, rs_arena, ag_arena, fused, stream)
+        iso = measure_isolated(groups, kinds, n, rank, hp, rs_arena, ag_arena, fused, stream,
+                               gset, arena)
         for k in kinds:
             kernels[k].update(iso[k])
 
@@ -559,7 +608,8 @@ def run_workload(cfg_index, args, dev, copy_gbps):
         "config": {"workload": cfg.name, "world": n, "rank": rank, "groups": len(groups),
                    "params_per_rank": V, "align_elems": args.align,
                    "step": ("per group: fused reduce+adamw+pack -> unpack" if fused else
-                            "per group: reduce -> adamw -> pack -> unpack"),
+                            "reduce per group -> one adamw launch over every group -> one "
+                            "copy-in launch over every group -> unpack per group"),
                    "io": "fp32 master/m/v shards, bf16 [N,S] grads and all-gather buffers"},
         "effective_GBps": eff_gbps,
         "hbm_frac": eff_gbps / HBM_PEAK_GBPS,
@@ -584,8 +634,10 @@ def run_workload(cfg_index, args, dev, copy_gbps):
                      "frac_of_copy_ceiling": frac(achieved, copy_gbps),
                      "avg_launch_ms": dom_avg_ms, "launches": dom_launches,
                      "algorithmic_bytes_per_launch": dom_bytes_per_launch,
-                     "timing": "HIP events around one launch per group on the step's stream, "
-                               "inside the timed steps"},
+                     "timing": ("HIP events around its one launch per step"
+                                if dominant in one_launch else
+                                "HIP events around one launch per group") +
+                               " on the step's stream, inside the timed steps"},
         "kernels": kernels,
     }
     if per.get("unpack"):
@@ -600,9 +652,11 @@ def run_workload(cfg_index, args, dev, copy_gbps):
     if not args.no_next:
         rec["next_kernels"] = measure_next(groups, n, rs_arena[0], full_arena, stream,
                                            max(1, args.breakdown_steps))
+    if gset is not None:
+        capi.fsdp_group_set_destroy(gset)
     for g in groups:
         g.close()
-    del groups, full_arena, rs_arena, ag_arena, execute
+    del groups, full_arena, rs_arena, ag_arena, execute, arena
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:

@@ -11,6 +11,8 @@
  *   update    fsdp_adamw_shard       AdamW on fp32 master, m and v shards
  *   fused     fsdp_step_shard        reduce -> AdamW -> copy-in in one pass
  *   executor  fsdp_step_groups       a whole step over many groups, one call
+ *   sets      fsdp_adamw_groups, fsdp_pack_allgather_groups, fsdp_step_group_set
+ *             AdamW and copy-in of many groups, one launch each
  *
  * and around them: the reduce-scatter copy-in (fsdp_pack_reduce_scatter),
  * fp32 contributions (fsdp_reduce_shard_f32), the FP8 E4M3 all-gather
@@ -400,6 +402,85 @@ fsdp_status fsdp_step_groups(fsdp_plan *const *plans, int32_t n_groups,
                              const fsdp_adamw_hparams_t *hp, int64_t step,
                              uint32_t flags, int32_t timed_kernel,
                              void *const *timing_events, void *stream);
+
+/* ---- group sets: one launch for the AdamW and the copy-in of many groups -- */
+
+/* The optimizer is built over the whole sharded model, so one optimizer step
+ * updates the shards of every group ([ST] fully_shard paragraph: build the
+ * optimizer after sharding, its state sharded with the parameters; [MS]
+ * "Working Principle", Update state).  A group set runs that step, and the
+ * copy-in of every group, as one multi-tensor launch each over a
+ * concatenated device table, instead of one launch per group.  It borrows
+ * its plans (destroy the set before them) and holds their AdamW tensors as
+ * bound when it was built: rebinding master, grad, exp_avg or exp_avg_sq of
+ * any group makes every call on the set fail with FSDP_E_STATE. */
+typedef struct fsdp_group_set fsdp_group_set;
+
+/* Builds a set over n_groups distinct plans, each bound at least once (its
+ * device tables exist), all on the current device.  Uploads the tables on
+ * `stream` and waits for it.  The copy-in arena of the set holds group g's
+ * S_g-element segment at an offset that fsdp_group_set_segment reports
+ * (each segment starts on a multiple of 8 elements; the up to 7 elements
+ * between segments are never written).
+ * Errors: FSDP_E_INVAL (null or repeated plan, n_groups < 1, bound shard
+ *         tensors that overlap where the AdamW update writes: a master,
+ *         exp_avg or exp_avg_sq element that is also part of another bound
+ *         shard of the set), FSDP_E_STATE (a plan never bound, plans on
+ *         different devices or not on the current one), FSDP_E_NOMEM,
+ *         FSDP_E_HIP. */
+fsdp_status fsdp_group_set_create(fsdp_plan *const *plans, int32_t n_groups,
+                                  void *stream, fsdp_group_set **out);
+
+/* Waits for the device and frees the set's tables; NULL is ignored. */
+void fsdp_group_set_destroy(fsdp_group_set *set);
+
+/* Group g's copy-in segment: elements [*offset, *offset + S_g) of the arena,
+ * which holds *arena_elems elements in all.  Errors: FSDP_E_INVAL. */
+fsdp_status fsdp_group_set_segment(const fsdp_group_set *set, int32_t g,
+                                   int64_t *offset, int64_t *arena_elems);
+
+/* fsdp_adamw_shard on every group of the set, in one launch; results are
+ * bit-identical to the per-group calls.  Needs FSDP_ROLE_MASTER | GRAD |
+ * EXP_AVG | EXP_AVG_SQ on every group.
+ * Errors: as fsdp_adamw_shard, plus FSDP_E_INVAL (null set) and
+ *         FSDP_E_STATE (a group rebound since the set was built). */
+fsdp_status fsdp_adamw_groups(const fsdp_group_set *set,
+                              const fsdp_adamw_hparams_t *hp, int64_t step,
+                              void *stream);
+
+/* fsdp_pack_allgather of every group of the set into its segment of
+ * `arena` (bf16, 2-byte aligned; 16-byte aligned for full-width stores), in
+ * one launch; each segment equals the per-group copy-in.  Needs
+ * FSDP_ROLE_MASTER on every group.
+ * Errors: FSDP_E_INVAL (null set, null arena), FSDP_E_ALIGN, FSDP_E_STATE,
+ *         FSDP_E_HIP. */
+fsdp_status fsdp_pack_allgather_groups(const fsdp_group_set *set, uint16_t *arena,
+                                       void *stream);
+
+/* The unfused sharded step of a set, from native code on one stream:
+ * fsdp_reduce_shard of every group in order (each group's reduce-scatter
+ * output arrives on its own), then fsdp_adamw_groups, then
+ * fsdp_pack_allgather_groups, then -- unless ag_out is NULL --
+ * fsdp_unpack_allgather of every group.  Master, grad, m, v, the arena
+ * segments and the full tensors equal those of fsdp_step_groups with
+ * FSDP_STEP_UNFUSED and ag_in[g] = the group's segment.
+ *   rs_in, ag_out  host arrays of one device buffer per group, as for
+ *                  fsdp_step_groups; the arena must not overlap any rs_in
+ *   timing_events  NULL, or 2*n_groups hipEvent_t: for the per-group
+ *                  kernels (FSDP_KERNEL_REDUCE, FSDP_KERNEL_UNPACK) events
+ *                  2g and 2g+1 bracket group g's launch; for the one-launch
+ *                  kernels (FSDP_KERNEL_ADAMW, FSDP_KERNEL_PACK) events 0
+ *                  and 1 bracket that launch.  A NULL pair is skipped; a
+ *                  pair with one NULL is an error
+ * Every argument is checked before anything is launched.  Errors: as the
+ * calls it makes, plus FSDP_E_INVAL for a null rs_in array, an arena
+ * overlapping an rs_in buffer or a timed kernel the call does not run. */
+fsdp_status fsdp_step_group_set(const fsdp_group_set *set,
+                                const uint16_t *const *rs_in, uint16_t *arena,
+                                const uint16_t *const *ag_out,
+                                const fsdp_adamw_hparams_t *hp, int64_t step,
+                                int32_t timed_kernel, void *const *timing_events,
+                                void *stream);
 
 /* ---- CPU offload --------------------------------------------------------- */
 

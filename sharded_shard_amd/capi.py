@@ -128,6 +128,13 @@ _SIGS = {
     "fsdp_adamw_host": (_i32, [_P, _P, _P, _P, _i64, ctypes.POINTER(AdamwHparams), _i64, _i32]),
     "fsdp_step_groups": (_i32, [_PP, _i32, _PP, _PP, _PP, ctypes.POINTER(AdamwHparams), _i64,
                                 ctypes.c_uint32, _i32, _PP, _P]),
+    "fsdp_group_set_create": (_i32, [_PP, _i32, _P, ctypes.POINTER(_P)]),
+    "fsdp_group_set_destroy": (None, [_P]),
+    "fsdp_group_set_segment": (_i32, [_P, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
+    "fsdp_adamw_groups": (_i32, [_P, ctypes.POINTER(AdamwHparams), _i64, _P]),
+    "fsdp_pack_allgather_groups": (_i32, [_P, _P, _P]),
+    "fsdp_step_group_set": (_i32, [_P, _PP, _P, _PP, ctypes.POINTER(AdamwHparams), _i64, _i32,
+                                   _PP, _P]),
     "fsdp_check_stream": (_i32, [_P]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -475,6 +482,92 @@ def fsdp_step_groups(plans, rs_in, ag_in, ag_out, lr: float, beta1: float, beta2
                      timed_kernel: int = 0, timing_events=None, stream=None) -> None:
     StepGroupsCall(plans, rs_in, ag_in, ag_out, lr, beta1, beta2, eps, weight_decay, flags,
                    stream)(step, timed_kernel, timing_events)
+
+
+# ---- group sets -------------------------------------------------------------------
+
+def fsdp_group_set_create(plans, stream=None):
+    """Returns an opaque group-set handle over the (bound) plans."""
+    arr = (ctypes.c_void_p * max(1, len(plans)))(*[p.value if p is not None else None
+                                                   for p in plans])
+    out = _P()
+    _check(lib.fsdp_group_set_create(ctypes.cast(arr, _PP), len(plans), stream_handle(stream),
+                                     ctypes.byref(out)), "fsdp_group_set_create")
+    return out
+
+
+def fsdp_group_set_destroy(gset) -> None:
+    lib.fsdp_group_set_destroy(gset)
+
+
+def fsdp_group_set_segment(gset, g: int):
+    """(offset, arena_elems): group g's copy-in segment starts at element offset
+    of an arena of arena_elems bf16 elements."""
+    off, tot = _i64(), _i64()
+    _check(lib.fsdp_group_set_segment(gset, g, ctypes.byref(off), ctypes.byref(tot)),
+           "fsdp_group_set_segment")
+    return off.value, tot.value
+
+
+def _arena_elems(gset):
+    if gset is None or getattr(gset, "value", 1) is None:
+        return None
+    return fsdp_group_set_segment(gset, 0)[1]
+
+
+def fsdp_adamw_groups(gset, lr: float, beta1: float, beta2: float, eps: float,
+                      weight_decay: float, step: int, stream=None) -> None:
+    hp = AdamwHparams(lr, beta1, beta2, eps, weight_decay)
+    _check(lib.fsdp_adamw_groups(gset, ctypes.byref(hp), step, stream_handle(stream)),
+           "fsdp_adamw_groups")
+
+
+def fsdp_pack_allgather_groups(gset, arena, stream=None) -> None:
+    n = _arena_elems(gset)
+    a = _dev(arena, 2 * n, "arena") if n is not None else addr(arena)
+    _check(lib.fsdp_pack_allgather_groups(gset, a, stream_handle(stream)),
+           "fsdp_pack_allgather_groups")
+
+
+class StepGroupSetCall:
+    """fsdp_step_group_set with its pointer arrays marshalled once.
+
+    plans: the set's plans, in its order (for the buffer size checks);
+    rs_in, ag_out: tensors/addresses per group (ag_out may be None);
+    arena: the copy-in arena of the set.
+    """
+
+    def __init__(self, gset, plans, rs_in, arena, ag_out, lr, beta1, beta2, eps,
+                 weight_decay, stream=None):
+        n = len(plans)
+        if len(rs_in) != n or (ag_out is not None and len(ag_out) != n):
+            raise ValueError("rs_in and ag_out must have one entry per group")
+        self.n = n
+        self._set = gset
+        rs_p, out_p = [], []
+        for g, p in enumerate(plans):
+            d = _dims(p)
+            rs_p.append(_dev(rs_in[g], 2 * d[0] * d[1], f"rs_in[{g}]"))
+            if ag_out is not None:
+                out_p.append(_dev(ag_out[g], 2 * d[0] * d[1], f"ag_out[{g}]"))
+        self._arena = _dev(arena, 2 * _arena_elems(gset), "arena")
+        self._rs = _ptr_array(rs_p)
+        self._ag_out = _ptr_array(out_p) if ag_out is not None else None
+        self._keep = (rs_in, arena, ag_out)
+        self._hp = AdamwHparams(lr, beta1, beta2, eps, weight_decay)
+        self._stream = stream_handle(stream)
+
+    def __call__(self, step: int, timed_kernel: int = 0, events=None) -> None:
+        ev = None
+        if events is not None:
+            if len(events) != 2 * self.n:
+                raise ValueError(f"events: need 2 per group ({2 * self.n}), got {len(events)}")
+            ev = (ctypes.c_void_p * len(events))(
+                *[int(e.cuda_event) if e is not None else None for e in events])
+            ev = ctypes.cast(ev, _PP)
+        _check(lib.fsdp_step_group_set(self._set, self._rs, self._arena, self._ag_out,
+                                       ctypes.byref(self._hp), step, timed_kernel, ev,
+                                       self._stream), "fsdp_step_group_set")
 
 
 def fsdp_check_stream(stream=None) -> None:

@@ -5,6 +5,7 @@
 // enqueue kernels on the caller's stream.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -34,6 +35,23 @@ struct fsdp_plan {
     fsdp::ReduceTile *d_reduce = nullptr;
     fsdp::EwTile *d_adamw = nullptr;
     fsdp::EwTile *d_full = nullptr;
+};
+
+// Bound plans whose AdamW and copy-in run as one launch each: the plans'
+// entry records concatenated (group g's entries from ent_off[g]) and their
+// AdamW and copy-in tiles re-indexed into that table and into one copy-in
+// arena (group g's segment from seg_off[g]).  Built once; it borrows the
+// plans and is valid while their AdamW tensors stay bound as they were.
+struct fsdp_group_set {
+    std::vector<fsdp_plan *> plans;
+    std::vector<int64_t> ent_off, seg_off;  // n_groups + 1 prefix offsets
+    std::vector<fsdp::DevEntry> snapshot;   // concatenated entries at creation
+    int device = -1;
+    char *dmem = nullptr;
+    fsdp::DevEntry *d_entries = nullptr;
+    fsdp::PackTile *d_pack = nullptr;
+    fsdp::EwTile *d_adamw = nullptr;
+    int64_t n_pack = 0, n_adamw = 0;
 };
 
 namespace {
@@ -772,6 +790,318 @@ fsdp_status fsdp_step_groups(fsdp_plan *const *plans, int32_t n_groups,
             e = mark(g, FSDP_KERNEL_UNPACK, 1);
         if (e != hipSuccess)
             return hip_fail(e, ("fsdp_step_groups: group " + std::to_string(g)).c_str());
+    }
+    return FSDP_OK;
+}
+
+}  // extern "C"
+
+// ---- group sets: AdamW and copy-in of many groups in one launch each --------
+
+namespace {
+
+// Copy-in segments of a set start 16-byte aligned in the arena.
+int64_t round8(int64_t n) { return (n + 7) & ~static_cast<int64_t>(7); }
+
+// No element of a written AdamW shard (master, exp_avg, exp_avg_sq) may
+// belong to any other bound shard of the set (those three or grad), in
+// this group or another: one launch updates them all at once.
+fsdp_status check_disjoint(const fsdp_group_set *set) {
+    struct Span {
+        uintptr_t lo, hi;
+        bool written;
+        int32_t g, i;
+    };
+    std::vector<Span> spans;
+    for (size_t g = 0; g < set->plans.size(); ++g) {
+        const fsdp_plan *p = set->plans[g];
+        for (size_t i = 0; i < p->L.entries.size(); ++i) {
+            const int64_t n = p->L.entries[i].valid_numel;
+            if (n <= 0) continue;
+            const fsdp::DevEntry &e = p->host_entries[i];
+            const float *role[4] = {e.master, e.exp_avg, e.exp_avg_sq, e.grad};
+            for (int r = 0; r < 4; ++r) {
+                if (role[r] == nullptr) continue;
+                const uintptr_t lo = reinterpret_cast<uintptr_t>(role[r]);
+                spans.push_back({lo, lo + static_cast<uintptr_t>(n) * 4, r < 3,
+                                 static_cast<int32_t>(g), static_cast<int32_t>(i)});
+            }
+        }
+    }
+    std::sort(spans.begin(), spans.end(),
+              [](const Span &a, const Span &b) { return a.lo < b.lo; });
+    // Every overlapping pair is seen when its later-starting span comes up:
+    // it meets an earlier written span, or it is written and meets any.
+    uintptr_t end_any = 0, end_written = 0;
+    const Span *last_any = nullptr, *last_written = nullptr;
+    for (const Span &sp : spans) {
+        const Span *hit = sp.lo < end_written ? last_written
+                          : (sp.written && sp.lo < end_any) ? last_any
+                                                            : nullptr;
+        if (hit != nullptr)
+            return fail(FSDP_E_INVAL,
+                        "fsdp_group_set_create: shard tensors overlap (group " +
+                            std::to_string(hit->g) + " parameter " + std::to_string(hit->i) +
+                            ", group " + std::to_string(sp.g) + " parameter " +
+                            std::to_string(sp.i) + ")");
+        if (sp.hi > end_any) end_any = sp.hi, last_any = &sp;
+        if (sp.written && sp.hi > end_written) end_written = sp.hi, last_written = &sp;
+    }
+    return FSDP_OK;
+}
+
+// The set's plans still hold the AdamW tensors it was built with, on the
+// current device.
+fsdp_status check_set(const fsdp_group_set *set, int32_t roles, const char *call) {
+    if (set == nullptr) return fail(FSDP_E_INVAL, std::string(call) + ": null set");
+    size_t k = 0;
+    for (const fsdp_plan *p : set->plans) {
+        fsdp_status s = need_roles(p, roles, call);
+        if (s != FSDP_OK) return s;
+        for (const fsdp::DevEntry &e : p->host_entries) {
+            const fsdp::DevEntry &o = set->snapshot[k++];
+            if (e.master != o.master || e.grad != o.grad || e.exp_avg != o.exp_avg ||
+                e.exp_avg_sq != o.exp_avg_sq)
+                return fail(FSDP_E_STATE, std::string(call) +
+                                              ": a group was rebound after the set was built");
+        }
+    }
+    if (set->plans.empty()) return FSDP_OK;
+    return check_device(set->plans[0]);
+}
+
+hipError_t do_adamw_set(const fsdp_group_set *set, const float scal[8], hipStream_t st) {
+    return guarded([&] {
+        return fsdp::launch_adamw(set->d_adamw, set->n_adamw, set->d_entries, scal, st);
+    });
+}
+
+hipError_t do_pack_set(const fsdp_group_set *set, uint16_t *arena, hipStream_t st) {
+    return guarded(
+        [&] { return fsdp::launch_pack(set->d_pack, set->n_pack, set->d_entries, arena, st); });
+}
+
+}  // namespace
+
+extern "C" {
+
+fsdp_status fsdp_group_set_create(fsdp_plan *const *plans, int32_t n_groups, void *stream,
+                                  fsdp_group_set **out) {
+    if (out == nullptr) return fail(FSDP_E_INVAL, "fsdp_group_set_create: null out");
+    *out = nullptr;
+    if (n_groups < 1 || plans == nullptr)
+        return fail(FSDP_E_INVAL, "fsdp_group_set_create: need n_groups >= 1 and a plan array");
+    for (int32_t g = 0; g < n_groups; ++g) {
+        if (plans[g] == nullptr) return fail(FSDP_E_INVAL, "fsdp_group_set_create: null plan");
+        for (int32_t h = 0; h < g; ++h)
+            if (plans[h] == plans[g])
+                return fail(FSDP_E_INVAL, "fsdp_group_set_create: plan of group " +
+                                              std::to_string(g) + " repeats group " +
+                                              std::to_string(h));
+    }
+    for (int32_t g = 0; g < n_groups; ++g) {
+        if (plans[g]->dmem == nullptr)
+            return fail(FSDP_E_STATE, "fsdp_group_set_create: plan of group " +
+                                          std::to_string(g) + " has never been bound");
+        if (plans[g]->device != plans[0]->device)
+            return fail(FSDP_E_STATE, "fsdp_group_set_create: groups bound on different devices");
+    }
+    fsdp_group_set *set = nullptr;
+    try {
+        set = new fsdp_group_set();
+        set->plans.assign(plans, plans + n_groups);
+        set->ent_off.assign(1, 0);
+        set->seg_off.assign(1, 0);
+        for (const fsdp_plan *p : set->plans) {
+            set->ent_off.push_back(set->ent_off.back() +
+                                   static_cast<int64_t>(p->L.entries.size()));
+            set->seg_off.push_back(set->seg_off.back() + round8(p->L.S));
+            set->snapshot.insert(set->snapshot.end(), p->host_entries.begin(),
+                                 p->host_entries.end());
+            set->n_pack += static_cast<int64_t>(p->L.pack.size());
+            set->n_adamw += static_cast<int64_t>(p->L.adamw.size());
+        }
+        fsdp_status s = check_disjoint(set);
+        if (s == FSDP_OK) s = check_device(set->plans[0]);
+        if (s != FSDP_OK) {
+            delete set;
+            return s;
+        }
+        // host copies of the tables, re-indexed into the set
+        std::vector<fsdp::PackTile> pack;
+        std::vector<fsdp::EwTile> adamw;
+        pack.reserve(static_cast<size_t>(set->n_pack));
+        adamw.reserve(static_cast<size_t>(set->n_adamw));
+        for (int32_t g = 0; g < n_groups; ++g) {
+            const fsdp::Layout &L = set->plans[g]->L;
+            const int32_t eo = static_cast<int32_t>(set->ent_off[g]);
+            for (fsdp::PackTile t : L.pack) {
+                t.dst += set->seg_off[g];
+                t.entry += eo;
+                pack.push_back(t);
+            }
+            for (fsdp::EwTile t : L.adamw) {
+                t.entry += eo;
+                adamw.push_back(t);
+            }
+        }
+        const size_t eb = set->snapshot.size() * sizeof(fsdp::DevEntry);
+        const size_t pb = pack.size() * sizeof(fsdp::PackTile);
+        const size_t ab = adamw.size() * sizeof(fsdp::EwTile);
+        void *mem = nullptr;
+        hipError_t e = hipMalloc(&mem, round256(eb) + round256(pb) + round256(ab) + 256);
+        if (e != hipSuccess) {
+            delete set;
+            return fail(FSDP_E_NOMEM, "fsdp_group_set_create: hipMalloc of device tables failed");
+        }
+        set->dmem = static_cast<char *>(mem);
+        set->device = set->plans[0]->device;
+        set->d_entries = reinterpret_cast<fsdp::DevEntry *>(set->dmem);
+        set->d_pack = reinterpret_cast<fsdp::PackTile *>(set->dmem + round256(eb));
+        set->d_adamw = reinterpret_cast<fsdp::EwTile *>(set->dmem + round256(eb) + round256(pb));
+        const hipStream_t st = static_cast<hipStream_t>(stream);
+        const struct {
+            void *dst;
+            const void *src;
+            size_t bytes;
+        } up[3] = {{set->d_entries, set->snapshot.data(), eb},
+                   {set->d_pack, pack.data(), pb},
+                   {set->d_adamw, adamw.data(), ab}};
+        for (const auto &u : up) {
+            if (u.bytes == 0) continue;
+            if ((e = hipMemcpyAsync(u.dst, u.src, u.bytes, hipMemcpyHostToDevice, st)) !=
+                hipSuccess)
+                break;
+        }
+        if (e == hipSuccess) e = hipStreamSynchronize(st);
+        if (e != hipSuccess) {
+            fsdp_group_set_destroy(set);
+            return hip_fail(e, "fsdp_group_set_create: upload");
+        }
+        *out = set;
+        return FSDP_OK;
+    } catch (const std::bad_alloc &) {
+        delete set;
+        return fail(FSDP_E_NOMEM, "fsdp_group_set_create: host allocation failed");
+    }
+}
+
+void fsdp_group_set_destroy(fsdp_group_set *set) {
+    if (set == nullptr) return;
+    if (set->dmem != nullptr) {
+        int cur = -1;
+        (void)hipGetDevice(&cur);
+        (void)hipSetDevice(set->device);
+        (void)hipDeviceSynchronize();
+        (void)hipFree(set->dmem);
+        if (cur >= 0) (void)hipSetDevice(cur);
+    }
+    delete set;
+}
+
+fsdp_status fsdp_group_set_segment(const fsdp_group_set *set, int32_t g, int64_t *offset,
+                                   int64_t *arena_elems) {
+    if (set == nullptr || offset == nullptr || arena_elems == nullptr)
+        return fail(FSDP_E_INVAL, "fsdp_group_set_segment: null argument");
+    if (g < 0 || static_cast<size_t>(g) >= set->plans.size())
+        return fail(FSDP_E_INVAL, "fsdp_group_set_segment: group out of range");
+    *offset = set->seg_off[g];
+    *arena_elems = set->seg_off.back();
+    return FSDP_OK;
+}
+
+fsdp_status fsdp_adamw_groups(const fsdp_group_set *set, const fsdp_adamw_hparams_t *hp,
+                              int64_t step, void *stream) {
+    const char *call = "fsdp_adamw_groups";
+    fsdp_status s = check_set(set, kAdamwRoles, call);
+    if (s != FSDP_OK || (s = check_hparams(hp, step, call)) != FSDP_OK) return s;
+    float scal[8];
+    adamw_scalars(hp, step, scal);
+    return launched(do_adamw_set(set, scal, static_cast<hipStream_t>(stream)),
+                    "fsdp_adamw_groups: launch");
+}
+
+fsdp_status fsdp_pack_allgather_groups(const fsdp_group_set *set, uint16_t *arena,
+                                       void *stream) {
+    const char *call = "fsdp_pack_allgather_groups";
+    fsdp_status s = check_set(set, FSDP_ROLE_MASTER, call);
+    if (s != FSDP_OK) return s;
+    if (arena == nullptr && set->seg_off.back() > 0)
+        return fail(FSDP_E_INVAL, "fsdp_pack_allgather_groups: null arena");
+    if (misaligned(arena, 2))
+        return fail(FSDP_E_ALIGN, "fsdp_pack_allgather_groups: arena not 2-byte aligned");
+    return launched(do_pack_set(set, arena, static_cast<hipStream_t>(stream)),
+                    "fsdp_pack_allgather_groups: launch");
+}
+
+fsdp_status fsdp_step_group_set(const fsdp_group_set *set, const uint16_t *const *rs_in,
+                                uint16_t *arena, const uint16_t *const *ag_out,
+                                const fsdp_adamw_hparams_t *hp, int64_t step,
+                                int32_t timed_kernel, void *const *timing_events,
+                                void *stream) {
+    const char *call = "fsdp_step_group_set";
+    fsdp_status s = check_set(set, kAdamwRoles, call);
+    if (s != FSDP_OK) return s;
+    const int32_t n = static_cast<int32_t>(set->plans.size());
+    if (rs_in == nullptr) return fail(FSDP_E_INVAL, "fsdp_step_group_set: null rs_in array");
+    if ((s = check_hparams(hp, step, call)) != FSDP_OK) return s;
+    if (arena == nullptr && set->seg_off.back() > 0)
+        return fail(FSDP_E_INVAL, "fsdp_step_group_set: null arena");
+    if (misaligned(arena, 2))
+        return fail(FSDP_E_ALIGN, "fsdp_step_group_set: arena not 2-byte aligned");
+    if (timing_events != nullptr) {
+        const bool ok = timed_kernel == FSDP_KERNEL_REDUCE || timed_kernel == FSDP_KERNEL_ADAMW ||
+                        timed_kernel == FSDP_KERNEL_PACK ||
+                        (timed_kernel == FSDP_KERNEL_UNPACK && ag_out != nullptr);
+        if (!ok) return fail(FSDP_E_INVAL, "fsdp_step_group_set: timed_kernel is not run by this call");
+        for (int32_t g = 0; g < n; ++g)
+            if ((timing_events[2 * g] == nullptr) != (timing_events[2 * g + 1] == nullptr))
+                return fail(FSDP_E_INVAL, "fsdp_step_group_set: timing events of a group must "
+                                          "both be set or both be null");
+    }
+    for (int32_t g = 0; g < n; ++g) {
+        const fsdp_plan *p = set->plans[g];
+        if ((s = check_reduce(p, rs_in[g], call)) != FSDP_OK) return s;
+        if (ag_out != nullptr && (s = check_unpack(p, ag_out[g], call)) != FSDP_OK) return s;
+        // the reduce reads rs_in while the copy-in writes the arena
+        const uintptr_t r0 = reinterpret_cast<uintptr_t>(rs_in[g]);
+        const uintptr_t rb = static_cast<uintptr_t>(p->L.world) * static_cast<uintptr_t>(p->L.S) * 2;
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(arena);
+        const uintptr_t ab = static_cast<uintptr_t>(set->seg_off.back()) * 2;
+        if (rb > 0 && ab > 0 && a0 < r0 + rb && r0 < a0 + ab)
+            return fail(FSDP_E_INVAL, "fsdp_step_group_set: arena overlaps rs_in of group " +
+                                          std::to_string(g));
+    }
+    float scal[8];
+    adamw_scalars(hp, step, scal);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    auto mark = [&](int32_t g, int32_t kernel, int which) -> hipError_t {
+        if (timing_events == nullptr || kernel != timed_kernel ||
+            timing_events[2 * g + which] == nullptr)
+            return hipSuccess;
+        return hipEventRecord(static_cast<hipEvent_t>(timing_events[2 * g + which]), st);
+    };
+    hipError_t e = hipSuccess;
+    for (int32_t g = 0; g < n && e == hipSuccess; ++g) {
+        if ((e = mark(g, FSDP_KERNEL_REDUCE, 0)) == hipSuccess &&
+            (e = do_reduce(set->plans[g], rs_in[g], st)) == hipSuccess)
+            e = mark(g, FSDP_KERNEL_REDUCE, 1);
+        if (e != hipSuccess)
+            return hip_fail(e, ("fsdp_step_group_set: reduce of group " + std::to_string(g)).c_str());
+    }
+    if ((e = mark(0, FSDP_KERNEL_ADAMW, 0)) == hipSuccess &&
+        (e = do_adamw_set(set, scal, st)) == hipSuccess &&
+        (e = mark(0, FSDP_KERNEL_ADAMW, 1)) == hipSuccess &&
+        (e = mark(0, FSDP_KERNEL_PACK, 0)) == hipSuccess &&
+        (e = do_pack_set(set, arena, st)) == hipSuccess)
+        e = mark(0, FSDP_KERNEL_PACK, 1);
+    if (e != hipSuccess) return hip_fail(e, "fsdp_step_group_set: AdamW or copy-in");
+    for (int32_t g = 0; ag_out != nullptr && g < n; ++g) {
+        if ((e = mark(g, FSDP_KERNEL_UNPACK, 0)) == hipSuccess &&
+            (e = do_unpack(set->plans[g], ag_out[g], st)) == hipSuccess)
+            e = mark(g, FSDP_KERNEL_UNPACK, 1);
+        if (e != hipSuccess)
+            return hip_fail(e, ("fsdp_step_group_set: copy-out of group " + std::to_string(g)).c_str());
     }
     return FSDP_OK;
 }

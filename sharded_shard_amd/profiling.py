@@ -47,6 +47,9 @@ WORKLOADS = {   # tag: (config, label, file stem)
     "c4": (4, "70B-shaped, 81 groups, N=64, rank 0", "llama70b_n64"),
 }
 SEPARATE = {"c2u": "c2", "c4u": "c4"}
+# kernels the separate-kernel path launches once per step over every group
+# (a group set): one launch moves the bytes of all groups
+SET_KERNELS = ("adamw_kernel", "pack_kernel")
 
 # kernel name -> algorithmic bytes of one launch for a group (S, V, F, N)
 ALG = {
@@ -224,12 +227,16 @@ def summarize(prof, out_dir, sha):
             sstats = kernel_stats(prof, sep_tag)
             lines += ["", "## Separate-kernel path (--unfused)", "", "```",
                       _trace_cmd(sep_tag, args + " --unfused"), "```", "",
+                      "A reduce and a copy-out per group; " + " and ".join(SET_KERNELS) +
+                      " run once per step over every group (a group set), so one launch "
+                      "moves the bytes of all groups.", "",
                       "| kernel | calls | avg us | algorithmic bytes | GB/s | % of 8 TB/s |",
                       "|---|---|---|---|---|---|"]
+            n_groups = len(group_sizes(ci)[1])
             for name, s in sorted(sstats.items(), key=lambda kv: -kv[1]["total_us"]):
                 if name not in ALG:
                     continue
-                alg = alg_bytes_per_launch(ci, name)
+                alg = alg_bytes_per_launch(ci, name) * (n_groups if name in SET_KERNELS else 1)
                 gbps = alg / (s["avg_us"] * 1e-6) / 1e9
                 lines.append(f"| {name} | {s['calls']} | {s['avg_us']:.1f} | {alg:.4g} | "
                              f"{gbps:.0f} | {100 * gbps / HBM_PEAK_GBPS:.1f} |")

@@ -9,9 +9,9 @@
 //     <name> <world> <rank> <align> <n_params> <rows_0> <cols_0> ... <rows_n-1> <cols_n-1>
 // Every buffer is its own exact-size allocation, so a tile reaching past its
 // tensor is an ASan report.  For each workload the harness binds every role,
-// runs every hot call and checks that each call writes every element of its
-// outputs exactly once; then it drives the error paths and the FSDP_FAULT
-// hook.  Prints "ALL OK" and exits 0 when every check passed.
+// runs every hot call (and the group-set calls over two groups) and checks
+// that each call writes every element of its outputs exactly once; then it
+// drives the error paths and the FSDP_FAULT hook.  Prints "ALL OK" and exits 0 when every check passed.
 #include <algorithm>
 #include <cstdint>
 #include <cstdio>
@@ -260,6 +260,152 @@ void executor(const Workload &w, Instance &a, Instance &b) {
                  FSDP_E_INVAL);
 }
 
+// Group sets: the one-launch AdamW and copy-in over two groups write every
+// shard and every segment exactly once (and nothing between segments); the
+// set executor matches the per-group unfused step's coverage; shards that
+// overlap where AdamW writes are refused, shared read-only grads are not;
+// rebinding a group invalidates the set until the old tensors are back.
+void group_sets(const Workload &w, Instance &a, Instance &b) {
+    fsdp_plan *plans[2] = {a.plan, b.plan};
+    fsdp_group_set *set = nullptr;
+    CHECK_STATUS(fsdp_group_set_create(plans, 2, nullptr, &set), FSDP_OK);
+    if (set == nullptr) return;
+    int64_t off[2] = {0, 0}, total = 0, t1 = 0;
+    CHECK_STATUS(fsdp_group_set_segment(set, 0, &off[0], &total), FSDP_OK);
+    CHECK_STATUS(fsdp_group_set_segment(set, 1, &off[1], &t1), FSDP_OK);
+    const int64_t S = a.info.S;
+    const int64_t S8 = (S + 7) / 8 * 8;
+    CHECK(off[0] == 0 && off[1] == S8 && total == 2 * S8 && t1 == total,
+          "%s: segments at %lld, %lld of %lld", w.name.c_str(), (long long)off[0],
+          (long long)off[1], (long long)total);
+    CHECK_STATUS(fsdp_group_set_segment(set, 2, &off[0], &total), FSDP_E_INVAL);
+    uint16_t *arena = alloc<uint16_t>(total);
+
+    harness::spans.clear();
+    CHECK_STATUS(fsdp_adamw_groups(set, &kHp, 1, nullptr), FSDP_OK);
+    for (Instance *in : {&a, &b}) check_shards(*in, in->master, "set AdamW", w.name);
+
+    auto check_arena = [&](const char *what) {
+        std::vector<uint8_t> hits(static_cast<size_t>(total), 0);
+        int64_t outside = 0, bad = 0;
+        for (const harness::Span &sp : harness::spans) {
+            if (sp.base != arena || sp.kind != harness::kSegment) continue;
+            if (sp.off < 0 || sp.off + sp.len > total) {
+                ++outside;
+                continue;
+            }
+            for (int64_t i = sp.off; i < sp.off + sp.len; ++i)
+                if (hits[i] < 2) ++hits[i];
+        }
+        for (int64_t i = 0; i < total; ++i) {
+            const bool in_seg = (i >= off[0] && i < off[0] + S) || (i >= off[1] && i < off[1] + S);
+            bad += hits[i] != (in_seg ? 1 : 0);
+        }
+        CHECK(outside == 0 && bad == 0, "%s / %s: %lld ranges outside, %lld elements wrong",
+              w.name.c_str(), what, (long long)outside, (long long)bad);
+    };
+    off[1] = S8;
+    harness::spans.clear();
+    CHECK_STATUS(fsdp_pack_allgather_groups(set, arena, nullptr), FSDP_OK);
+    check_arena("set copy-in");
+
+    const uint16_t *rs[2] = {a.rs, b.rs};
+    const uint16_t *ag_out[2] = {a.ag, b.ag};
+    harness::spans.clear();
+    CHECK_STATUS(fsdp_step_group_set(set, rs, arena, ag_out, &kHp, 2, 0, nullptr, nullptr),
+                 FSDP_OK);
+    check_arena("set executor copy-in");
+    for (Instance *in : {&a, &b}) {
+        check_shards(*in, in->grad, "set executor reduce", w.name);
+        check_shards(*in, in->master, "set executor AdamW", w.name);
+        check_full(*in, w, as_void(in->full), harness::kFull, "set executor copy-out");
+    }
+    int ev_storage[4];
+    void *evs[4] = {&ev_storage[0], &ev_storage[1], &ev_storage[2], &ev_storage[3]};
+    for (int32_t k : {FSDP_KERNEL_REDUCE, FSDP_KERNEL_ADAMW, FSDP_KERNEL_PACK, FSDP_KERNEL_UNPACK})
+        CHECK_STATUS(fsdp_step_group_set(set, rs, arena, ag_out, &kHp, 3, k, evs, nullptr),
+                     FSDP_OK);
+    CHECK_STATUS(fsdp_step_group_set(set, rs, arena, ag_out, &kHp, 3, FSDP_KERNEL_STEP, evs,
+                                     nullptr),
+                 FSDP_E_INVAL);
+    CHECK_STATUS(fsdp_step_group_set(set, rs, arena, nullptr, &kHp, 3, FSDP_KERNEL_UNPACK, evs,
+                                     nullptr),
+                 FSDP_E_INVAL);
+    evs[1] = nullptr;
+    CHECK_STATUS(fsdp_step_group_set(set, rs, arena, ag_out, &kHp, 3, FSDP_KERNEL_ADAMW, evs,
+                                     nullptr),
+                 FSDP_E_INVAL);
+    CHECK_STATUS(fsdp_step_group_set(set, nullptr, arena, ag_out, &kHp, 3, 0, nullptr, nullptr),
+                 FSDP_E_INVAL);
+    CHECK_STATUS(fsdp_step_group_set(set, rs, arena, ag_out, &kHp, 0, 0, nullptr, nullptr),
+                 FSDP_E_INVAL);
+    if (S > 0) {
+        CHECK_STATUS(fsdp_pack_allgather_groups(set, nullptr, nullptr), FSDP_E_INVAL);
+        CHECK_STATUS(fsdp_pack_allgather_groups(set, reinterpret_cast<uint16_t *>(
+                                                         reinterpret_cast<char *>(arena) + 1),
+                                                nullptr),
+                     FSDP_E_ALIGN);
+        // the arena may not cover a group's reduce-scatter input
+        CHECK_STATUS(fsdp_step_group_set(set, rs, const_cast<uint16_t *>(b.rs), ag_out, &kHp, 3, 0,
+                                         nullptr, nullptr),
+                     FSDP_E_INVAL);
+        setenv("FSDP_FAULT", "launch", 1);
+        const long l0 = harness::launches;
+        CHECK_STATUS(fsdp_adamw_groups(set, &kHp, 1, nullptr), FSDP_E_HIP);
+        CHECK(std::strstr(fsdp_last_error(), "injected") != nullptr, "message: %s",
+              fsdp_last_error());
+        CHECK(harness::launches == l0, "%s: a faulted set call launched", w.name.c_str());
+        unsetenv("FSDP_FAULT");
+    }
+
+    // rebinding a group's AdamW tensors invalidates the set; binding the old
+    // ones again makes it valid again
+    bool any_valid = false;
+    for (const fsdp_shard_entry_t &e : b.ents) any_valid = any_valid || e.valid_numel > 0;
+    if (any_valid) {
+        std::vector<float *> other;
+        for (const fsdp_shard_entry_t &e : b.ents) other.push_back(alloc<float>(e.valid_numel));
+        CHECK_STATUS(fsdp_bind(b.plan, other.data(), nullptr, nullptr, nullptr, nullptr, nullptr),
+                     FSDP_OK);
+        CHECK_STATUS(fsdp_adamw_groups(set, &kHp, 1, nullptr), FSDP_E_STATE);
+        CHECK_STATUS(fsdp_pack_allgather_groups(set, arena, nullptr), FSDP_E_STATE);
+        CHECK_STATUS(fsdp_bind(b.plan, b.master.data(), nullptr, nullptr, nullptr, nullptr,
+                               nullptr),
+                     FSDP_OK);
+        CHECK_STATUS(fsdp_adamw_groups(set, &kHp, 1, nullptr), FSDP_OK);
+    }
+    fsdp_group_set_destroy(set);
+
+    // a repeated plan, an unbound plan, overlapping written shards: refused
+    fsdp_plan *twice[2] = {a.plan, a.plan};
+    set = nullptr;
+    CHECK_STATUS(fsdp_group_set_create(twice, 2, nullptr, &set), FSDP_E_INVAL);
+    CHECK_STATUS(fsdp_group_set_create(plans, 0, nullptr, &set), FSDP_E_INVAL);
+    CHECK(set == nullptr, "a refused set was returned");
+    if (any_valid) {
+        Instance c;
+        if (!make(w, &c)) return;
+        fsdp_plan *ac[2] = {a.plan, c.plan};
+        CHECK_STATUS(fsdp_group_set_create(ac, 2, nullptr, &set), FSDP_E_STATE);
+        // c reads a's grads: reads may be shared
+        CHECK_STATUS(fsdp_bind(c.plan, c.master.data(), a.grad.data(), c.m.data(), c.v.data(),
+                               nullptr, nullptr),
+                     FSDP_OK);
+        CHECK_STATUS(fsdp_group_set_create(ac, 2, nullptr, &set), FSDP_OK);
+        fsdp_group_set_destroy(set);
+        set = nullptr;
+        // c's exp_avg is a's master: refused
+        CHECK_STATUS(fsdp_bind(c.plan, nullptr, nullptr, a.master.data(), nullptr, nullptr,
+                               nullptr),
+                     FSDP_OK);
+        CHECK_STATUS(fsdp_group_set_create(ac, 2, nullptr, &set), FSDP_E_INVAL);
+        CHECK(std::strstr(fsdp_last_error(), "overlap") != nullptr, "message: %s",
+              fsdp_last_error());
+        CHECK(set == nullptr, "a refused set was returned");
+        fsdp_plan_destroy(c.plan);
+    }
+}
+
 // FSDP_FAULT: every launch fails before anything is recorded, or only the
 // K-th one; the status and message reach the caller; unset, calls work.
 void faults(const Workload &w, Instance &a, Instance &b) {
@@ -471,6 +617,7 @@ int main() {
         bind_all(&b);
         hot_calls(w, a);
         executor(w, a, b);
+        group_sets(w, a, b);
         faults(w, a, b);
         error_paths(w, a);
         reshard(w);

@@ -206,6 +206,32 @@ def test_step_groups_rejects_bad_arguments_without_gpu():
         capi.fsdp_plan_destroy(p)
 
 
+def test_group_set_rejects_bad_arguments_without_gpu():
+    """fsdp_group_set_create refuses empty, null, repeated and never-bound
+    plans before any HIP call; the set calls refuse a null set."""
+    p = capi.fsdp_plan_create([8, 3], [4, 1], 2, 0, 1)
+    q = capi.fsdp_plan_create([5], [2], 2, 1, 1)
+    try:
+        for plans, code in (([], capi.FSDP_E_INVAL), ([p, None], capi.FSDP_E_INVAL),
+                            ([p, q, p], capi.FSDP_E_INVAL), ([p, q], capi.FSDP_E_STATE)):
+            with pytest.raises(capi.FsdpError) as ei:
+                capi.fsdp_group_set_create(plans, stream=0)
+            assert ei.value.status == code, plans
+        hp = capi.AdamwHparams(3e-4, 0.9, 0.999, 1e-8, 0.01)
+        assert capi.lib.fsdp_adamw_groups(None, capi.ctypes.byref(hp), 1, None) == \
+            capi.FSDP_E_INVAL
+        assert capi.lib.fsdp_pack_allgather_groups(None, 0x1000, None) == capi.FSDP_E_INVAL
+        assert capi.lib.fsdp_step_group_set(None, None, 0x1000, None, capi.ctypes.byref(hp), 1,
+                                            0, None, None) == capi.FSDP_E_INVAL
+        with pytest.raises(capi.FsdpError) as ei:
+            capi.fsdp_group_set_segment(None, 0)
+        assert ei.value.status == capi.FSDP_E_INVAL
+        capi.fsdp_group_set_destroy(None)
+    finally:
+        capi.fsdp_plan_destroy(p)
+        capi.fsdp_plan_destroy(q)
+
+
 def test_check_stream_reports_hip_errors_as_fsdp_e_hip():
     """fsdp_check_stream's error branch: on a machine without a GPU the HIP
     runtime fails the stream wait, and the status and HIP's message reach the

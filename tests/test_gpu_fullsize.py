@@ -10,6 +10,9 @@ plans, tiles and grids).  Outputs are checked three ways:
 * sampled: the oracle computes chosen outputs one by one from the same inputs
   read back (first and last elements, tile edges, random picks), for the
   separate kernels and the single-group fused call;
+* whole workloads through a group set: the separate-kernel path (a reduce per
+  group, one AdamW and one copy-in launch over all 33 or 81 groups) equals the
+  fused executor bit for bit in every shard and copy-in segment;
 * exact properties over every element: unpack of every rank's pack of a full
   weight W gives bf16(W) back bit for bit, with torch's library cast as the
   reference; N equal gradient contributions reduce to exactly that gradient.
@@ -352,4 +355,55 @@ def test_step_groups_whole_groups_every_element(name, cfg_index, group_ids, rank
             del grads, want_ag
         del rs_h, ag_h
     for g in groups:
+        g.close()
+
+
+# ---------------------------------------------------------------------------
+# group set at full size: the separate-kernel path the bench times with
+# --unfused (a reduce per group, one AdamW and one copy-in launch over every
+# group) against the fused executor on the same inputs, every group, every
+# element of the grad, master, m and v shards and of every copy-in segment
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg_index", [2, 4])
+def test_group_set_every_group_equals_fused_executor(cfg_index):
+    cfg = configs.get(cfg_index)
+    n, hp, rank = cfg.world, vars(cfg.hp), cfg.timing_rank
+    shapes = [[p.shape for p in grp.params] for grp in cfg.groups]
+
+    def shards_only(s):            # no full-parameter tensors: no copy-out here
+        g = ShardedGroup(s, n, rank, bind=False)
+        g.allocate(full=False)
+        g.bind()
+        return g
+
+    A = [shards_only(s) for s in shapes]
+    B = [shards_only(s) for s in shapes]
+    for gi, (ga, gb) in enumerate(zip(A, B)):
+        synth.fill_normal_f32_(ga.master_flat, cfg.master_std, ("set-full", cfg_index, gi))
+        gb.master_flat.copy_(ga.master_flat)
+    max_ns = max(n * g.S for g in A)
+    rs_arena = [torch.empty(max_ns, dtype=torch.int16, device=DEV) for _ in range(2)]
+    rs = [rs_arena[gi & 1][:n * g.S] for gi, g in enumerate(A)]
+    in_a = [torch.empty(g.S, dtype=torch.int16, device=DEV) for g in A]
+    fused = capi.StepGroupsCall([g.plan for g in A], rs, in_a, None,
+                                flags=capi.FSDP_STEP_WRITE_GRAD, **hp)
+    gset = capi.fsdp_group_set_create([g.plan for g in B])
+    offs = [capi.fsdp_group_set_segment(gset, gi)[0] for gi in range(len(B))]
+    arena = torch.empty(capi.fsdp_group_set_segment(gset, 0)[1], dtype=torch.int16, device=DEV)
+    separate = capi.StepGroupSetCall(gset, [g.plan for g in B], rs, arena, None, **hp)
+    for t in (1, 2):
+        for b in range(2):
+            synth.fill_normal_bf16_bits_(rs_arena[b], cfg.grad_std, ("set-full-rs", cfg_index, b, t))
+        print(f"[fullsize] group set c{cfg_index} step {t}", flush=True)
+        fused(t)
+        separate(t)
+        torch.cuda.synchronize()
+        for gi, (ga, gb) in enumerate(zip(A, B)):
+            for fl in ("master_flat", "grad_flat", "m_flat", "v_flat"):
+                assert torch.equal(getattr(ga, fl).view(torch.int32),
+                                   getattr(gb, fl).view(torch.int32)), (cfg_index, gi, t, fl)
+            assert torch.equal(arena[offs[gi]:offs[gi] + gb.S], in_a[gi]), (cfg_index, gi, t)
+    capi.fsdp_group_set_destroy(gset)
+    for g in A + B:
         g.close()

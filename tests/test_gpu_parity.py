@@ -744,6 +744,132 @@ def test_step_groups_equals_per_group_calls(unfused, n, r):
         g.close()
 
 
+def _set_groups(kind):
+    """(group shapes, N, rank) of the group-set cases: misaligned rows at 6
+    ranks, aligned beside misaligned at 64, and 40 small ragged groups."""
+    named = {c[0]: c[1] for c in CASES}
+    if kind == "n6":
+        return [CASES[1][1], CASES[2][1], [(70001,), (300, 33)], [(0, 4)]], 6, 5
+    if kind == "n64":
+        return [named["wide-n64"], named["odd-n64"], [(64 * 300, 24), (8192,)]], 64, 0
+    rng = np.random.default_rng(synth.seed_for("set-many") % (2**32))
+    groups = []
+    for _ in range(40):
+        k = int(rng.integers(1, 4))
+        groups.append([(int(rng.integers(0, 300)), int(rng.integers(1, 40))) for _ in range(k)])
+    return groups, 8, 3
+
+
+@pytest.mark.parametrize("kind", ["n6", "n64", "many"])
+def test_group_set_equals_per_group_unfused_step_and_oracle(kind):
+    """fsdp_step_group_set (one AdamW and one copy-in launch over every group)
+    against fsdp_step_groups with FSDP_STEP_UNFUSED (per-group launches) over
+    3 steps, every tensor bit for bit, and the first step against the oracle."""
+    group_shapes, n, r = _set_groups(kind)
+    A, B, rs_bufs, ag_a, ag_b, plans = [], [], [], [], [], []
+    for gi, shapes in enumerate(group_shapes):
+        ga, gb = ShardedGroup(shapes, n, r), ShardedGroup(shapes, n, r)
+        _fill_masters(ga, ("set", kind, gi))
+        gb.master_flat.copy_(ga.master_flat)
+        plan = O.plan(shapes, n, r)
+        plans.append(plan)
+        rs_bufs.append(torch.from_numpy(_rs_input(plan, n, ("set-rs", kind, gi)).reshape(-1)
+                                        .view(np.int16)).to(DEV))
+        other = torch.from_numpy(_rand_ag(n, plan.S, ("set-ag", kind, gi)).reshape(-1)
+                                 .view(np.int16)).to(DEV)
+        ag_a.append(other.clone())
+        ag_b.append(other.clone())
+        A.append(ga)
+        B.append(gb)
+    masters0 = [[f32(g.shard_view(g.master_flat, i)) for i in range(len(g.shapes))] for g in A]
+    gset = capi.fsdp_group_set_create([g.plan for g in B])
+    seg = [capi.fsdp_group_set_segment(gset, gi) for gi in range(len(B))]
+    total = seg[0][1]
+    assert [o for o, _ in seg] == list(np.cumsum([0] + [(g.S + 7) // 8 * 8 for g in B])[:-1])
+    arena_buf, arena = guarded_i16(total)
+    # A's copy-in goes to buffers of its own, so that both copy-outs read the
+    # same synthetic all-gather buffers
+    in_a = [torch.zeros(g.S, dtype=torch.int16, device=DEV) for g in A]
+    call_a = capi.StepGroupsCall([g.plan for g in A], rs_bufs, in_a, ag_a,
+                                 flags=capi.FSDP_STEP_UNFUSED, **HP)
+    call_b = capi.StepGroupSetCall(gset, [g.plan for g in B], rs_bufs, arena, ag_b, **HP)
+    gap = torch.ones(total, dtype=torch.bool, device=DEV)
+    for (o, _), g in zip(seg, B):
+        gap[o:o + g.S] = False
+    for t in (1, 2, 3):
+        call_a(t)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(B))]
+        for e in evs:
+            e.record()
+        call_b(t, [capi.FSDP_KERNEL_REDUCE, capi.FSDP_KERNEL_ADAMW, capi.FSDP_KERNEL_PACK][t - 1],
+               evs)
+        torch.cuda.synchronize()
+        assert evs[0].elapsed_time(evs[1]) >= 0
+        for gi, (ga, gb) in enumerate(zip(A, B)):
+            o = seg[gi][0]
+            assert torch.equal(arena[o:o + gb.S], in_a[gi]), ("segment", gi, t)
+            for fl in ("master_flat", "grad_flat", "m_flat", "v_flat", "full_flat"):
+                x, y = getattr(ga, fl), getattr(gb, fl)
+                assert torch.equal(x.view(torch.int16), y.view(torch.int16)), (fl, gi, t)
+        assert bool((arena[gap] == GUARD_VAL).all()), "a gap was written"
+        assert_guards(arena_buf, total)
+        if t == 1:               # the set's own results against the oracle
+            for gi, (gb, plan) in enumerate(zip(B, plans)):
+                rs = u16(rs_bufs[gi]).reshape(n, plan.S)
+                grads = O.reduce(plan, rs)
+                masters = [x.copy() for x in masters0[gi]]
+                ms = [np.zeros_like(x) for x in masters]
+                vs = [np.zeros_like(x) for x in masters]
+                for x, gr, m, v in zip(masters, grads, ms, vs):
+                    O.adamw(x, gr, m, v, 1, **HP)
+                for i in range(len(gb.shapes)):
+                    _cmp_f32(f32(gb.shard_view(gb.grad_flat, i)), grads[i], ("grad", gi, i))
+                    _cmp_f32(f32(gb.shard_view(gb.master_flat, i)), masters[i], ("master", gi, i))
+                o = seg[gi][0]
+                assert np.array_equal(u16(arena[o:o + plan.S]), O.pack(plan, masters))
+                full_in = u16(ag_b[gi]).reshape(n, plan.S)
+                for i, want in enumerate(O.unpack(plan, full_in)):
+                    assert np.array_equal(u16(gb.full_view(i)), want), ("full", gi, i)
+    capi.fsdp_adamw_groups(gset, step=4, **HP)
+    capi.fsdp_pack_allgather_groups(gset, arena)
+    for gi, ga in enumerate(A):
+        ga.adamw(4, **HP)
+        ga.pack(in_a[gi])
+    torch.cuda.synchronize()
+    for gi, (ga, gb) in enumerate(zip(A, B)):
+        assert torch.equal(ga.master_flat, gb.master_flat)
+        o = seg[gi][0]
+        assert torch.equal(arena[o:o + gb.S], in_a[gi])
+    capi.fsdp_group_set_destroy(gset)
+    for g in A + B:
+        g.close()
+
+
+def test_group_set_refuses_rebound_groups_and_overlapping_shards():
+    n, r = 4, 1
+    g1 = ShardedGroup([(64, 8), (9,)], n, r)
+    g2 = ShardedGroup([(33, 3)], n, r)
+    gset = capi.fsdp_group_set_create([g1.plan, g2.plan])
+    capi.fsdp_adamw_groups(gset, step=1, **HP)
+    spare = torch.zeros_like(g2.master_flat)
+    capi.fsdp_bind(g2.plan, master=g2._ptrs(spare))
+    with pytest.raises(capi.FsdpError) as ei:
+        capi.fsdp_adamw_groups(gset, step=2, **HP)
+    assert ei.value.status == capi.FSDP_E_STATE
+    capi.fsdp_bind(g2.plan, master=g2._ptrs(g2.master_flat))
+    capi.fsdp_adamw_groups(gset, step=2, **HP)
+    torch.cuda.synchronize()
+    capi.fsdp_group_set_destroy(gset)
+    # g3's m shards are g1's master: one launch would race on them
+    g3 = ShardedGroup([(64, 8), (9,)], n, r)
+    capi.fsdp_bind(g3.plan, exp_avg=g1._ptrs(g1.master_flat))
+    with pytest.raises(capi.FsdpError) as ei:
+        capi.fsdp_group_set_create([g1.plan, g3.plan])
+    assert ei.value.status == capi.FSDP_E_INVAL and "overlap" in str(ei.value)
+    for g in (g1, g2, g3):
+        g.close()
+
+
 def test_rejected_bind_keeps_the_previous_binding():
     """A bind that fails argument checks changes nothing: the plan stays bound
     to its previous tensors and the hot calls still produce the oracle's
