@@ -125,6 +125,9 @@ def parse():
                          "resharding kernel)")
     ap.add_argument("--no-next", action="store_true",
                     help="skip timing the reduce-scatter copy-in and fp32-contribution kernels")
+    ap.add_argument("--no-references", action="store_true",
+                    help="skip timing the AdamW and copy-in kernels beside torch's kernels of "
+                         "the same access pattern")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device-to-device copy of 2 GiB instead (the "
                          "reference for HBM byte counters and the copy ceiling)")
@@ -310,55 +313,141 @@ def measure_isolated(groups, kinds, n, rank, hp, rs_arena, ag_arena, fused, stre
     been flushed, so no input can come from the last-level cache: the
     per-kernel roofline protocol.  The flush writes 1 GiB and then reads
     another 1 GiB, so the cache holds only clean lines when the timed launch
-    starts (no write-back of the flush lands in it).  Sum of algorithmic
-    bytes / sum of event-timed launch durations over the launches."""
+    starts (no write-back of the flush lands in it).
+
+    A launch can end with up to 256 MB of its own writes still dirty in the
+    MALL, written back to HBM after its end event; for a short, write-heavy
+    launch that flatters its rate.  So each launch is also followed by a
+    1 GiB read sweep, which evicts those lines, and timed up to the sweep's
+    end, minus the same sweep's time on a clean cache: the launch's full
+    cost, write-backs included.  Reports sum of algorithmic bytes / sum of
+    durations over the launches, both ways."""
     import torch
     from sharded_shard_amd import capi
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=rs_arena[0].device)
-    sweep = torch.zeros(1 << 28, dtype=torch.int32, device=rs_arena[0].device)
+    dev = rs_arena[0].device
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    sweep = torch.zeros(1 << 28, dtype=torch.int32, device=dev)
+    evict = torch.zeros(1 << 28, dtype=torch.int32, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def clean(tag):
+        flush.fill_(tag & 0xFF)
+        sweep.max()                         # read-only pass over another 1 GiB
+
+    def timed(launch, tag):
+        """(launch alone, launch plus the write-backs it left) in ms."""
+        clean(tag)
+        a, b, c = ev(), ev(), ev()
+        a.record(stream)
+        launch()
+        b.record(stream)
+        evict.max()
+        c.record(stream)
+        clean(tag + 1)
+        a2, c2 = ev(), ev()
+        a2.record(stream)
+        evict.max()
+        c2.record(stream)
+        c2.synchronize()
+        return a.elapsed_time(b), a.elapsed_time(c) - a2.elapsed_time(c2)
+
     res = {}
     t = 10_000
     for k in kinds:
-        tot_b = tot_ms = 0.0
+        tot_b = tot_ms = tot_wb = 0.0
         if gset is not None and k in SET_KINDS:
             launch = {"adamw": lambda: capi.fsdp_adamw_groups(gset, step=t, stream=stream, **hp),
                       "pack": lambda: capi.fsdp_pack_allgather_groups(gset, arena, stream)}[k]
-            flush.fill_(1)
-            sweep.max()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            launch()
-            b.record(stream)
-            b.synchronize()
-            gbps = sum(algorithmic_bytes(g.S, g.V, g.F, n, fused)[k] for g in groups) \
-                / (a.elapsed_time(b) * 1e-3) / 1e9
+            tot_ms, tot_wb = timed(launch, t)
+            tot_b = sum(algorithmic_bytes(g.S, g.V, g.F, n, fused)[k] for g in groups)
             t += 1
-            res[k] = {"isolated_GBps": round(gbps, 1),
-                      "isolated_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
-            continue
-        for gi, g in enumerate(groups):
-            rs = rs_arena[gi & 1][:n * g.S]
-            ag_in = ag_arena[gi & 1][rank * g.S:(rank + 1) * g.S]
-            ag_out = ag_arena[gi & 1][:n * g.S]
-            launch = {"step": lambda: g.step(rs, ag_in, t, **hp, stream=stream),
-                      "reduce": lambda: g.reduce(rs, stream),
-                      "adamw": lambda: g.adamw(t, **hp, stream=stream),
-                      "pack": lambda: g.pack(ag_in, stream),
-                      "unpack": lambda: g.unpack(ag_out, stream)}[k]
-            flush.fill_(gi & 0xFF)
-            sweep.max()                     # read-only pass over another 1 GiB
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            launch()
-            b.record(stream)
-            b.synchronize()
-            tot_ms += a.elapsed_time(b)
-            tot_b += algorithmic_bytes(g.S, g.V, g.F, n, fused)[k]
-            t += 1
+        else:
+            for gi, g in enumerate(groups):
+                rs = rs_arena[gi & 1][:n * g.S]
+                ag_in = ag_arena[gi & 1][rank * g.S:(rank + 1) * g.S]
+                ag_out = ag_arena[gi & 1][:n * g.S]
+                launch = {"step": lambda: g.step(rs, ag_in, t, **hp, stream=stream),
+                          "reduce": lambda: g.reduce(rs, stream),
+                          "adamw": lambda: g.adamw(t, **hp, stream=stream),
+                          "pack": lambda: g.pack(ag_in, stream),
+                          "unpack": lambda: g.unpack(ag_out, stream)}[k]
+                ms, wb = timed(launch, gi)
+                tot_ms += ms
+                tot_wb += wb
+                tot_b += algorithmic_bytes(g.S, g.V, g.F, n, fused)[k]
+                t += 1
         gbps = tot_b / (tot_ms * 1e-3) / 1e9
-        res[k] = {"isolated_GBps": round(gbps, 1), "isolated_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
-    del flush, sweep
+        wb_gbps = tot_b / (tot_wb * 1e-3) / 1e9 if tot_wb > 0 else None
+        res[k] = {"isolated_GBps": round(gbps, 1), "isolated_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+                  "isolated_with_writeback_GBps": round(wb_gbps, 1) if wb_gbps else None,
+                  "isolated_with_writeback_hbm_frac":
+                      round(wb_gbps / HBM_PEAK_GBPS, 4) if wb_gbps else None}
+    del flush, sweep, evict
     return res
+
+
+def measure_pattern_references(dev, stream, n=1 << 28, reps=5):
+    """The library's AdamW and copy-in beside torch's own kernels with the
+    same access pattern, on the same n-element fp32 shards (4 GiB of p, g, m
+    and v: the launches stream from HBM): torch's fused AdamW reads p, g, m,
+    v and writes p, m, v (28 B per element, as fsdp_adamw_shard); torch's
+    fp32 -> bf16 cast reads 4 B and writes 2 B per element (as the copy-in).
+    Each rate is the best of `reps` event-timed launches; context for the
+    kernels' fractions of peak, not a target."""
+    import torch
+    from sharded_shard_amd import capi
+    from workloads import synth
+    p = synth.normal_f32(n, 0.02, ("ref-p",), device=dev)
+    g = synth.normal_f32(n, 1e-3, ("ref-g",), device=dev)
+    m, v = torch.zeros_like(p), torch.zeros_like(p)
+    out = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    plan = capi.fsdp_plan_create([n], [1], 1, 0, 1)
+    hp = dict(lr=3e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    step_t = torch.zeros((), dtype=torch.float32, device=dev)
+
+    def best(fn):
+        ms = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            ms.append(a.elapsed_time(b))
+        return min(ms)
+
+    def torch_adamw():
+        step_t.add_(1)      # a tiny launch of its own, before the timed region's main kernel
+        torch._fused_adamw_([p], [g], [m], [v], [], [step_t], lr=hp["lr"], beta1=hp["beta1"],
+                            beta2=hp["beta2"], weight_decay=hp["weight_decay"], eps=hp["eps"],
+                            amsgrad=False, maximize=False)
+
+    try:
+        capi.fsdp_bind(plan, [p], [g], [m], [v], None, stream)
+        t = [0]
+
+        def ours_adamw():
+            t[0] += 1
+            capi.fsdp_adamw_shard(plan, step=t[0], stream=stream, **hp)
+
+        res = {}
+        for name, fn, bpe in (("adamw_kernel", ours_adamw, 28),
+                              ("torch_fused_adamw", torch_adamw, 28),
+                              ("pack_kernel", lambda: capi.fsdp_pack_allgather(plan, out, stream), 6),
+                              ("torch_cast_f32_to_bf16", lambda: out.copy_(p), 6)):
+            fn()                                   # warm
+            ms = best(fn)
+            gbps = bpe * n / (ms * 1e-3) / 1e9
+            res[name] = {"ms": round(ms, 4), "GBps": round(gbps, 1),
+                         "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+        res["elements"] = n
+        res["note"] = ("same fp32 shards for all four; torch's AdamW timing includes its step "
+                       "counter's own small launch")
+        return res
+    finally:
+        capi.fsdp_plan_destroy(plan)
+        del p, g, m, v, out
+        torch.cuda.empty_cache()
 
 
 def measure_host_adamw(n=1 << 25, reps=3):
@@ -703,6 +792,8 @@ def main():
     }
     out.update(head)
     out["copy_ceiling"] = ceiling
+    if not args.no_references:
+        out["pattern_references"] = measure_pattern_references(dev, stream)
     also = []
     for c in args.also:
         also.append(run_workload(c, args, dev, copy_gbps))
