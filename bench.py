@@ -22,8 +22,9 @@ same workload.  The same record for each workload named by --also (the
 
 By default reduce, AdamW and pack run as one fused launch per group
 (fsdp_step_shard, bit-identical to the three calls); --unfused runs them as
-separate kernels through a group set: a reduce per group, then one AdamW and
-one copy-in launch over every group.
+three launches per group, and --group-set as separate kernels through a group
+set: a reduce per group, then one AdamW and one copy-in launch over every
+group.
 """
 from __future__ import annotations
 
@@ -112,8 +113,11 @@ def parse():
     ap.add_argument("--rank", type=int, default=None, help="simulated rank (default: the config's)")
     ap.add_argument("--align", type=int, default=1, choices=[1, 8])
     ap.add_argument("--unfused", action="store_true",
-                    help="run reduce (per group), adamw and pack (one launch each over every "
-                         "group) instead of the fused step")
+                    help="run reduce, adamw and pack as separate launches per group instead of "
+                         "the fused step")
+    ap.add_argument("--group-set", action="store_true",
+                    help="separate kernels through a group set: reduce per group, then one "
+                         "adamw and one copy-in launch over every group")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown-steps", type=int, default=3,
                     help="extra untimed steps per kernel kind, with events around its launches")
@@ -549,7 +553,7 @@ def run_workload(cfg_index, args, dev, copy_gbps):
     print("bench: state resident", file=sys.stderr, flush=True)
 
     V = sum(g.V for g in groups)
-    fused = not args.unfused
+    fused = not (args.unfused or args.group_set)
     kinds = ["step", "unpack"] if fused else ["reduce", "adamw", "pack", "unpack"]
     byts = {k: 0 for k in kinds}
     for g in groups:
@@ -567,13 +571,13 @@ def run_workload(cfg_index, args, dev, copy_gbps):
     # group, one AdamW and one copy-in launch over every group (into an arena
     # of every group's segment), a copy-out per group.
     gset = arena = None
-    if fused:
+    if not args.group_set:
         execute = capi.StepGroupsCall(
             [g.plan for g in groups],
             [rs_arena[gi & 1][:n * g.S] for gi, g in enumerate(groups)],
             [ag_arena[gi & 1][rank * g.S:(rank + 1) * g.S] for gi, g in enumerate(groups)],
             [ag_arena[gi & 1][:n * g.S] for gi, g in enumerate(groups)],
-            stream=stream, **hp)
+            flags=0 if fused else capi.FSDP_STEP_UNFUSED, stream=stream, **hp)
     else:
         gset = capi.fsdp_group_set_create([g.plan for g in groups], stream)
         arena = torch.empty(max(1, capi.fsdp_group_set_segment(gset, 0)[1]), dtype=torch.int16,
@@ -582,7 +586,7 @@ def run_workload(cfg_index, args, dev, copy_gbps):
             gset, [g.plan for g in groups],
             [rs_arena[gi & 1][:n * g.S] for gi, g in enumerate(groups)], arena,
             [ag_arena[gi & 1][:n * g.S] for gi, g in enumerate(groups)], stream=stream, **hp)
-    one_launch = set() if fused else set(SET_KINDS)
+    one_launch = set(SET_KINDS) if args.group_set else set()
 
     def launch_bytes(kind, gi):
         """Algorithmic bytes of the launch of `kind` timed by group gi's events."""
@@ -698,7 +702,8 @@ def run_workload(cfg_index, args, dev, copy_gbps):
                    "params_per_rank": V, "align_elems": args.align,
                    "step": ("per group: fused reduce+adamw+pack -> unpack" if fused else
                             "reduce per group -> one adamw launch over every group -> one "
-                            "copy-in launch over every group -> unpack per group"),
+                            "copy-in launch over every group -> unpack per group"
+                            if args.group_set else "per group: reduce -> adamw -> pack -> unpack"),
                    "io": "fp32 master/m/v shards, bf16 [N,S] grads and all-gather buffers"},
         "effective_GBps": eff_gbps,
         "hbm_frac": eff_gbps / HBM_PEAK_GBPS,

@@ -2,8 +2,9 @@
 
     python -m sharded_shard_amd.profiling <rocprof dir> <profiles dir>
 
-The rocprof directory holds, per workload tag (c1, c2, c3, c4, and c2u/c4u
-for the separate-kernel path), the output of
+The rocprof directory holds, per workload tag (c1, c2, c3, c4; c2u/c4u for
+the separate kernels per group and c2s/c4s for them through a group set),
+the output of
 
 * ``<tag>_trace``: ``rocprofv3 --kernel-trace --stats -T -f csv`` of bench.py
   (kernel durations, averaged per kernel name);
@@ -46,9 +47,11 @@ WORKLOADS = {   # tag: (config, label, file stem)
     "c3": (3, "ragged MoE, 2 groups, N=6, rank 5", "moe_ragged_n6"),
     "c4": (4, "70B-shaped, 81 groups, N=64, rank 0", "llama70b_n64"),
 }
-SEPARATE = {"c2u": "c2", "c4u": "c4"}
-# kernels the separate-kernel path launches once per step over every group
-# (a group set): one launch moves the bytes of all groups
+# separate-kernel traces: tag -> (workload tag, bench options, group set)
+SEPARATE = {"c2u": ("c2", "--unfused", False), "c4u": ("c4", "--unfused", False),
+            "c2s": ("c2", "--group-set", True), "c4s": ("c4", "--group-set", True)}
+# kernels a group set launches once per step over every group: one launch
+# moves the bytes of all groups
 SET_KERNELS = ("adamw_kernel", "pack_kernel")
 
 # kernel name -> algorithmic bytes of one launch for a group (S, V, F, N)
@@ -222,22 +225,25 @@ def summarize(prof, out_dir, sha):
                                    "traffic_bytes_per_launch": t2 if t2 is not None else t1,
                                    "traffic_fetch_write_bytes_per_launch": t1}
         traffic["workloads"][cfg.name] = wl
-        for sep_tag, of in SEPARATE.items():
-            if of != tag:
+        for sep_tag, (of, opt, is_set) in SEPARATE.items():
+            if of != tag or not glob.glob(f"{prof}/{sep_tag}_trace"):
                 continue
             sstats = kernel_stats(prof, sep_tag)
-            lines += ["", "## Separate-kernel path (--unfused)", "", "```",
-                      _trace_cmd(sep_tag, args + " --unfused"), "```", "",
-                      "A reduce and a copy-out per group; " + " and ".join(SET_KERNELS) +
-                      " run once per step over every group (a group set), so one launch "
-                      "moves the bytes of all groups.", "",
-                      "| kernel | calls | avg us | algorithmic bytes | GB/s | % of 8 TB/s |",
+            lines += ["", f"## Separate-kernel path ({opt})", "", "```",
+                      _trace_cmd(sep_tag, args + " " + opt), "```", ""]
+            lines += (["A reduce and a copy-out per group; " + " and ".join(SET_KERNELS) +
+                       " run once per step over every group (a group set), so one launch "
+                       "moves the bytes of all groups.", ""] if is_set else
+                      ["Reduce, AdamW, copy-in and copy-out per group, one group after the "
+                       "other.", ""])
+            lines += ["| kernel | calls | avg us | algorithmic bytes | GB/s | % of 8 TB/s |",
                       "|---|---|---|---|---|---|"]
             n_groups = len(group_sizes(ci)[1])
             for name, s in sorted(sstats.items(), key=lambda kv: -kv[1]["total_us"]):
                 if name not in ALG:
                     continue
-                alg = alg_bytes_per_launch(ci, name) * (n_groups if name in SET_KERNELS else 1)
+                alg = alg_bytes_per_launch(ci, name) * (
+                    n_groups if is_set and name in SET_KERNELS else 1)
                 gbps = alg / (s["avg_us"] * 1e-6) / 1e9
                 lines.append(f"| {name} | {s['calls']} | {s['avg_us']:.1f} | {alg:.4g} | "
                              f"{gbps:.0f} | {100 * gbps / HBM_PEAK_GBPS:.1f} |")
