@@ -274,7 +274,75 @@ def summarize(prof, out_dir, sha):
     path = os.path.join(out_dir, "pmc_traffic.json")
     json.dump(traffic, open(path, "w"), indent=1)
     files.append(path)
+    if glob.glob(f"{prof}/cal_LAT"):
+        files.append(memory_pressure(prof, out_dir, sha))
     return files
+
+
+LAT_COUNTERS = ["TCC_EA0_RDREQ_LEVEL_sum", "TCC_EA0_RDREQ_sum", "TCC_EA0_WRREQ_LEVEL_sum",
+                "TCC_EA0_WRREQ_sum"]
+STALL_COUNTERS = ["TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum", "TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum",
+                  "TCC_CYCLE_sum", "TCC_BUSY_sum"]
+# tag: (bench options, kernels to report)
+PRESSURE = {
+    "c2": ("--config 2", ["step_kernel_aligned", "unpack_kernel"]),
+    "c4": ("--config 4", ["step_kernel_wide", "unpack_kernel"]),
+    "c4s": ("--config 4 --group-set", ["adamw_kernel", "pack_kernel", "reduce_kernel"]),
+}
+
+
+def memory_pressure(prof, out_dir, sha):
+    """Average read and write latency at the L2's memory interface (requests
+    in flight summed per cycle / requests, Little's law), reads in flight per
+    L2 channel, and the share of L2 cycles the read or write interface was
+    out of credits for the memory fabric, per kernel against the calibration
+    copy.  The counters are summed over the 16 L2 channels."""
+    def copy_kernel(run):      # the 2 GiB copy: the runtime's copy kernel
+        cs = counters(prof, run)
+        return next(v for k, v in cs.items() if "copyBuffer" in k)
+
+    rows = [("copy (runtime, 2 GiB)", "--copy-calibration",
+             {**copy_kernel("cal_LAT"), **copy_kernel("cal_STALL")})]
+    for tag, (args, names) in PRESSURE.items():
+        lat, st = counters(prof, f"{tag}_LAT"), counters(prof, f"{tag}_STALL")
+        for name in names:
+            if name in lat and name in st:
+                rows.append((name, args, {**lat[name], **st[name]}))
+    lines = ["# Memory-side latency and back-pressure per kernel", "",
+             "REPO is the repository root on the GPU box.", "", "```"]
+    for run, cs in (("LAT", LAT_COUNTERS), ("STALL", STALL_COUNTERS)):
+        lines.append("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc " + " ".join(cs) +
+                     f" -T -f csv -d $REPO/gpurun_out/prof2/cal_{run} -o cal -- python3 "
+                     "$REPO/bench.py --copy-calibration")
+        for tag, (args, _) in PRESSURE.items():
+            lines.append("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc " + " ".join(cs) +
+                         f" -T -f csv -d $REPO/gpurun_out/prof2/{tag}_{run} -o {tag} -- python3 "
+                         f"$REPO/bench.py {args} --also none --steps 1 --warmup 1 "
+                         "--breakdown-steps 0 --no-isolated --no-copy-ceiling --no-cpu-baseline "
+                         "--no-references --no-next")
+    lines += ["```", "",
+              "Per dispatch, averaged over the kernel's dispatches: read (write) latency = "
+              "TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ (WRREQ), in L2 cycles; reads in flight per "
+              "L2 channel = TCC_EA0_RDREQ_LEVEL / TCC_CYCLE (both summed over the channels); "
+              "credit stalls = cycles the L2's read (write) interface was out of credits for "
+              "the memory fabric / TCC_CYCLE.", "",
+              "| kernel | run | read latency | write latency | reads in flight per channel | "
+              "read credit stall | write credit stall |",
+              "|---|---|---|---|---|---|---|"]
+    for name, args, c in rows:
+        cyc = c.get("TCC_CYCLE_sum", 0.0) or float("nan")
+        rd = c.get("TCC_EA0_RDREQ_sum", 0.0) or float("nan")
+        wr = c.get("TCC_EA0_WRREQ_sum", 0.0) or float("nan")
+        lines.append(
+            f"| {name} | {args} | {c.get('TCC_EA0_RDREQ_LEVEL_sum', 0.0) / rd:.0f} | "
+            f"{c.get('TCC_EA0_WRREQ_LEVEL_sum', 0.0) / wr:.0f} | "
+            f"{c.get('TCC_EA0_RDREQ_LEVEL_sum', 0.0) / cyc:.1f} | "
+            f"{100 * c.get('TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum', 0.0) / cyc:.1f}% | "
+            f"{100 * c.get('TCC_EA0_WRREQ_DRAM_CREDIT_STALL_sum', 0.0) / cyc:.1f}% |")
+    lines += ["", f"Kernel sources sha256 when measured: `{sha}`", ""]
+    path = os.path.join(out_dir, "memory_pressure.md")
+    open(path, "w").write("\n".join(lines))
+    return path
 
 
 if __name__ == "__main__":
