@@ -434,6 +434,11 @@ fsdp_status fsdp_group_set_create(fsdp_plan *const *plans, int32_t n_groups,
 /* Waits for the device and frees the set's tables; NULL is ignored. */
 void fsdp_group_set_destroy(fsdp_group_set *set);
 
+/* The number of groups of the set and the elements of its copy-in arena.
+ * Errors: FSDP_E_INVAL (null argument). */
+fsdp_status fsdp_group_set_info(const fsdp_group_set *set, int32_t *n_groups,
+                                int64_t *arena_elems);
+
 /* Group g's copy-in segment: elements [*offset, *offset + S_g) of the arena,
  * which holds *arena_elems elements in all.  Errors: FSDP_E_INVAL. */
 fsdp_status fsdp_group_set_segment(const fsdp_group_set *set, int32_t g,

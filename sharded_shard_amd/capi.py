@@ -130,6 +130,7 @@ _SIGS = {
                                 ctypes.c_uint32, _i32, _PP, _P]),
     "fsdp_group_set_create": (_i32, [_PP, _i32, _P, ctypes.POINTER(_P)]),
     "fsdp_group_set_destroy": (None, [_P]),
+    "fsdp_group_set_info": (_i32, [_P, ctypes.POINTER(_i32), ctypes.POINTER(_i64)]),
     "fsdp_group_set_segment": (_i32, [_P, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
     "fsdp_adamw_groups": (_i32, [_P, ctypes.POINTER(AdamwHparams), _i64, _P]),
     "fsdp_pack_allgather_groups": (_i32, [_P, _P, _P]),
@@ -500,6 +501,14 @@ def fsdp_group_set_destroy(gset) -> None:
     lib.fsdp_group_set_destroy(gset)
 
 
+def fsdp_group_set_info(gset):
+    """(n_groups, arena_elems) of a group set."""
+    n, tot = _i32(), _i64()
+    _check(lib.fsdp_group_set_info(gset, ctypes.byref(n), ctypes.byref(tot)),
+           "fsdp_group_set_info")
+    return n.value, tot.value
+
+
 def fsdp_group_set_segment(gset, g: int):
     """(offset, arena_elems): group g's copy-in segment starts at element offset
     of an arena of arena_elems bf16 elements."""
@@ -512,7 +521,7 @@ def fsdp_group_set_segment(gset, g: int):
 def _arena_elems(gset):
     if gset is None or getattr(gset, "value", 1) is None:
         return None
-    return fsdp_group_set_segment(gset, 0)[1]
+    return fsdp_group_set_info(gset)[1]
 
 
 def fsdp_adamw_groups(gset, lr: float, beta1: float, beta2: float, eps: float,
@@ -540,6 +549,8 @@ class StepGroupSetCall:
     def __init__(self, gset, plans, rs_in, arena, ag_out, lr, beta1, beta2, eps,
                  weight_decay, stream=None):
         n = len(plans)
+        if n != fsdp_group_set_info(gset)[0]:
+            raise ValueError(f"plans: {n} given, the set has {fsdp_group_set_info(gset)[0]} groups")
         if len(rs_in) != n or (ag_out is not None and len(ag_out) != n):
             raise ValueError("rs_in and ag_out must have one entry per group")
         self.n = n

@@ -999,6 +999,15 @@ void fsdp_group_set_destroy(fsdp_group_set *set) {
     delete set;
 }
 
+fsdp_status fsdp_group_set_info(const fsdp_group_set *set, int32_t *n_groups,
+                                int64_t *arena_elems) {
+    if (set == nullptr || n_groups == nullptr || arena_elems == nullptr)
+        return fail(FSDP_E_INVAL, "fsdp_group_set_info: null argument");
+    *n_groups = static_cast<int32_t>(set->plans.size());
+    *arena_elems = set->seg_off.back();
+    return FSDP_OK;
+}
+
 fsdp_status fsdp_group_set_segment(const fsdp_group_set *set, int32_t g, int64_t *offset,
                                    int64_t *arena_elems) {
     if (set == nullptr || offset == nullptr || arena_elems == nullptr)

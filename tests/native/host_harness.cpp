@@ -279,6 +279,12 @@ void group_sets(const Workload &w, Instance &a, Instance &b) {
           "%s: segments at %lld, %lld of %lld", w.name.c_str(), (long long)off[0],
           (long long)off[1], (long long)total);
     CHECK_STATUS(fsdp_group_set_segment(set, 2, &off[0], &total), FSDP_E_INVAL);
+    int32_t n_groups = 0;
+    int64_t t2 = 0;
+    CHECK_STATUS(fsdp_group_set_info(set, &n_groups, &t2), FSDP_OK);
+    CHECK(n_groups == 2 && t2 == total, "%s: info %d groups, %lld elements", w.name.c_str(),
+          n_groups, (long long)t2);
+    CHECK_STATUS(fsdp_group_set_info(set, nullptr, &t2), FSDP_E_INVAL);
     uint16_t *arena = alloc<uint16_t>(total);
 
     harness::spans.clear();

@@ -223,9 +223,11 @@ def test_group_set_rejects_bad_arguments_without_gpu():
         assert capi.lib.fsdp_pack_allgather_groups(None, 0x1000, None) == capi.FSDP_E_INVAL
         assert capi.lib.fsdp_step_group_set(None, None, 0x1000, None, capi.ctypes.byref(hp), 1,
                                             0, None, None) == capi.FSDP_E_INVAL
-        with pytest.raises(capi.FsdpError) as ei:
-            capi.fsdp_group_set_segment(None, 0)
-        assert ei.value.status == capi.FSDP_E_INVAL
+        for call in (lambda: capi.fsdp_group_set_segment(None, 0),
+                     lambda: capi.fsdp_group_set_info(None)):
+            with pytest.raises(capi.FsdpError) as ei:
+                call()
+            assert ei.value.status == capi.FSDP_E_INVAL
         capi.fsdp_group_set_destroy(None)
     finally:
         capi.fsdp_plan_destroy(p)
