@@ -42,16 +42,20 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "sharded-step params/sec per GPU + effective HBM GB/s (% of MI355X peak)"
 
 
-def algorithmic_bytes(S, V, F, N, fused):
+def algorithmic_bytes(S, V, F, N, fused, adamw_copy_in=False):
     """Bytes each kernel must move once per group.
 
     reduce: read N bf16 contributions (2NV) + write the fp32 grad (4V);
     adamw: read p, g, m, v (16V) + write p, m, v (12V); pack: read 4V fp32 +
     write 2S bf16; unpack: read 2F + write 2F.  The fused step reads 2NV + 12V
-    and writes 12V + 2S: the gradient never goes to HBM.
+    and writes 12V + 2S: the gradient never goes to HBM.  AdamW fused with the
+    copy-in (adamw_copy_in) reads 16V and writes 12V + 2S: the master is read
+    once for both.
     """
     if fused:
         return {"step": 2 * N * V + 24 * V + 2 * S, "unpack": 4 * F}
+    if adamw_copy_in:
+        return {"reduce": 2 * N * V + 4 * V, "adamw_pack": 28 * V + 2 * S, "unpack": 4 * F}
     return {"reduce": 2 * N * V + 4 * V, "adamw": 28 * V, "pack": 4 * V + 2 * S,
             "unpack": 4 * F}
 
@@ -95,10 +99,11 @@ TRAFFIC_SOURCE = ("HBM bytes per launch from the rocprofv3 memory-request counte
 
 KERNEL_NAMES = {"step": "step_kernel (fused reduce+adamw+pack)", "reduce": "reduce_kernel",
                 "adamw": "adamw_kernel", "pack": "pack_kernel (copy-in)",
-                "unpack": "unpack_kernel (copy-out)"}
-# kinds the separate-kernel path launches once per step over every group (a
-# group set); the others run once per group
-SET_KINDS = ("adamw", "pack")
+                "unpack": "unpack_kernel (copy-out)",
+                "adamw_pack": "adamw_pack_kernel (AdamW fused with the copy-in)"}
+# kinds a group set launches once per step over every group; the others run
+# once per group
+SET_KINDS = ("adamw", "pack", "adamw_pack")
 
 
 def parse():
@@ -118,6 +123,8 @@ def parse():
     ap.add_argument("--group-set", action="store_true",
                     help="separate kernels through a group set: reduce per group, then one "
                          "adamw and one copy-in launch over every group")
+    ap.add_argument("--group-set-fused", action="store_true",
+                    help="as --group-set, with AdamW and the copy-in fused in one launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown-steps", type=int, default=3,
                     help="extra untimed steps per kernel kind, with events around its launches")
@@ -138,6 +145,8 @@ def parse():
     args = ap.parse_args()
     if args.steps < 1 or args.warmup < 0:
         ap.error("--steps must be at least 1 and --warmup at least 0")
+    if args.group_set_fused:
+        args.group_set = True
     if args.also is None:
         args.also = "4" if args.config == 2 else "none"
     try:
@@ -311,7 +320,7 @@ def _pct(sorted_vals, q):
 
 
 def measure_isolated(groups, kinds, n, rank, hp, rs_arena, ag_arena, fused, stream,
-                     gset=None, arena=None):
+                     gset=None, arena=None, adamw_copy_in=False):
     """Each kernel kind launched alone per group (or, for the kinds a group
     set runs in one launch, alone over every group) after the 256 MB MALL has
     been flushed, so no input can come from the last-level cache: the
@@ -361,9 +370,12 @@ def measure_isolated(groups, kinds, n, rank, hp, rs_arena, ag_arena, fused, stre
         tot_b = tot_ms = tot_wb = 0.0
         if gset is not None and k in SET_KINDS:
             launch = {"adamw": lambda: capi.fsdp_adamw_groups(gset, step=t, stream=stream, **hp),
-                      "pack": lambda: capi.fsdp_pack_allgather_groups(gset, arena, stream)}[k]
+                      "pack": lambda: capi.fsdp_pack_allgather_groups(gset, arena, stream),
+                      "adamw_pack": lambda: capi.fsdp_adamw_pack_groups(
+                          gset, arena, step=t, stream=stream, **hp)}[k]
             tot_ms, tot_wb = timed(launch, t)
-            tot_b = sum(algorithmic_bytes(g.S, g.V, g.F, n, fused)[k] for g in groups)
+            tot_b = sum(algorithmic_bytes(g.S, g.V, g.F, n, fused, adamw_copy_in)[k]
+                        for g in groups)
             t += 1
         else:
             for gi, g in enumerate(groups):
@@ -378,7 +390,7 @@ def measure_isolated(groups, kinds, n, rank, hp, rs_arena, ag_arena, fused, stre
                 ms, wb = timed(launch, gi)
                 tot_ms += ms
                 tot_wb += wb
-                tot_b += algorithmic_bytes(g.S, g.V, g.F, n, fused)[k]
+                tot_b += algorithmic_bytes(g.S, g.V, g.F, n, fused, adamw_copy_in)[k]
                 t += 1
         gbps = tot_b / (tot_ms * 1e-3) / 1e9
         wb_gbps = tot_b / (tot_wb * 1e-3) / 1e9 if tot_wb > 0 else None
@@ -560,10 +572,11 @@ def run_workload(cfg_index, args, dev, copy_gbps):
 
     V = sum(g.V for g in groups)
     fused = not (args.unfused or args.group_set)
-    kinds = ["step", "unpack"] if fused else ["reduce", "adamw", "pack", "unpack"]
+    aci = args.group_set_fused
+    kinds = list(algorithmic_bytes(1, 1, 1, n, fused, aci))
     byts = {k: 0 for k in kinds}
     for g in groups:
-        for k, b in algorithmic_bytes(g.S, g.V, g.F, n, fused).items():
+        for k, b in algorithmic_bytes(g.S, g.V, g.F, n, fused, aci).items():
             byts[k] += b
     step_bytes = sum(byts.values())
     dominant = max(kinds, key=lambda k: byts[k])
@@ -591,17 +604,18 @@ def run_workload(cfg_index, args, dev, copy_gbps):
         execute = capi.StepGroupSetCall(
             gset, [g.plan for g in groups],
             [rs_arena[gi & 1][:n * g.S] for gi, g in enumerate(groups)], arena,
-            [ag_arena[gi & 1][:n * g.S] for gi, g in enumerate(groups)], stream=stream, **hp)
+            [ag_arena[gi & 1][:n * g.S] for gi, g in enumerate(groups)],
+            flags=capi.FSDP_SET_ADAMW_COPY_IN if aci else 0, stream=stream, **hp)
     one_launch = set(SET_KINDS) if args.group_set else set()
 
     def launch_bytes(kind, gi):
         """Algorithmic bytes of the launch of `kind` timed by group gi's events."""
         if kind in one_launch:
             return byts[kind]
-        return algorithmic_bytes(groups[gi].S, groups[gi].V, groups[gi].F, n, fused)[kind]
+        return algorithmic_bytes(groups[gi].S, groups[gi].V, groups[gi].F, n, fused, aci)[kind]
     kernel_id = {"step": capi.FSDP_KERNEL_STEP, "reduce": capi.FSDP_KERNEL_REDUCE,
                  "adamw": capi.FSDP_KERNEL_ADAMW, "pack": capi.FSDP_KERNEL_PACK,
-                 "unpack": capi.FSDP_KERNEL_UNPACK}
+                 "unpack": capi.FSDP_KERNEL_UNPACK, "adamw_pack": capi.FSDP_KERNEL_ADAMW_PACK}
 
     def new_events():
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(groups))]
@@ -663,7 +677,7 @@ def run_workload(cfg_index, args, dev, copy_gbps):
     per = {k: 0.0 for k in kinds}
     if args.breakdown_steps > 0:
         runs = {k: [new_events() for _ in range(args.breakdown_steps)] for k in kinds}
-        for k in one_launch:
+        for k in one_launch & set(kinds):
             runs[k] = [[e if i < 2 else None for i, e in enumerate(evs)] for evs in runs[k]]
         torch.cuda.synchronize()
         for k in kinds:
@@ -688,7 +702,7 @@ def run_workload(cfg_index, args, dev, copy_gbps):
                       "traffic_bytes_per_launch": measured_traffic(cfg.name, rank, args.align, k)}
     if args.isolated:
         iso = measure_isolated(groups, kinds, n, rank, hp, rs_arena, ag_arena, fused, stream,
-                               gset, arena)
+                               gset, arena, aci)
         for k in kinds:
             kernels[k].update(iso[k])
 
@@ -707,6 +721,8 @@ def run_workload(cfg_index, args, dev, copy_gbps):
         "config": {"workload": cfg.name, "world": n, "rank": rank, "groups": len(groups),
                    "params_per_rank": V, "align_elems": args.align,
                    "step": ("per group: fused reduce+adamw+pack -> unpack" if fused else
+                            "reduce per group -> one adamw+copy-in launch over every group -> "
+                            "unpack per group" if aci else
                             "reduce per group -> one adamw launch over every group -> one "
                             "copy-in launch over every group -> unpack per group"
                             if args.group_set else "per group: reduce -> adamw -> pack -> unpack"),
@@ -717,7 +733,9 @@ def run_workload(cfg_index, args, dev, copy_gbps):
         "step_algorithmic_bytes": step_bytes,
         "bytes_note": ("bytes the step's kernels must move once each (fused step "
                        "(2N+24)V+2S, copy-out 4F per group); hbm_frac = these / time / 8 TB/s"
-                       if fused else "bytes of the four separate kernels (reduce (2N+4)V, AdamW "
+                       if fused else "bytes of the separate kernels (reduce (2N+4)V, AdamW "
+                       "and copy-in fused 28V+2S, copy-out 4F per group) / time / 8 TB/s" if aci
+                       else "bytes of the four separate kernels (reduce (2N+4)V, AdamW "
                        "28V, copy-in 4V+2S, copy-out 4F per group) / time / 8 TB/s"),
         "wall_ms_per_step": wall * 1e3 / args.steps,
         "step_ms": {"median": _pct(step_ms, 50), "p10": _pct(step_ms, 10), "p90": _pct(step_ms, 90)},

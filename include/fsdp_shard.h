@@ -11,8 +11,9 @@
  *   update    fsdp_adamw_shard       AdamW on fp32 master, m and v shards
  *   fused     fsdp_step_shard        reduce -> AdamW -> copy-in in one pass
  *   executor  fsdp_step_groups       a whole step over many groups, one call
- *   sets      fsdp_adamw_groups, fsdp_pack_allgather_groups, fsdp_step_group_set
- *             AdamW and copy-in of many groups, one launch each
+ *   sets      fsdp_adamw_groups, fsdp_pack_allgather_groups,
+ *             fsdp_adamw_pack_groups, fsdp_step_group_set
+ *             AdamW and copy-in of many groups, one launch each or fused
  *
  * and around them: the reduce-scatter copy-in (fsdp_pack_reduce_scatter),
  * fp32 contributions (fsdp_reduce_shard_f32), the FP8 E4M3 all-gather
@@ -343,13 +344,15 @@ fsdp_status fsdp_adamw_shard(const fsdp_plan *plan,
 /* Flags of fsdp_step_shard and fsdp_step_groups. */
 enum { FSDP_STEP_WRITE_GRAD = 1, FSDP_STEP_UNFUSED = 2 };
 
-/* Kernel selectors for the timing hooks of fsdp_step_groups. */
+/* Kernel selectors for the timing hooks of fsdp_step_groups and
+ * fsdp_step_group_set. */
 enum {
     FSDP_KERNEL_STEP = 0,
     FSDP_KERNEL_REDUCE = 1,
     FSDP_KERNEL_ADAMW = 2,
     FSDP_KERNEL_PACK = 3,
-    FSDP_KERNEL_UNPACK = 4
+    FSDP_KERNEL_UNPACK = 4,
+    FSDP_KERNEL_ADAMW_PACK = 5
 };
 
 /* Fused sharded step: reduce -> AdamW -> copy-in in one pass over this
@@ -462,10 +465,28 @@ fsdp_status fsdp_adamw_groups(const fsdp_group_set *set,
 fsdp_status fsdp_pack_allgather_groups(const fsdp_group_set *set, uint16_t *arena,
                                        void *stream);
 
+/* fsdp_adamw_groups and fsdp_pack_allgather_groups in one launch: per
+ * element the AdamW update, then the bf16 cast of the new master into the
+ * group's arena segment (zeros in padding), so the master is read once for
+ * both.  The optimizer step that writes the next all-gather's input ([ST]
+ * fully_shard paragraph and "Mixed precision"; [MS] "Working Principle":
+ * the update, then the all-gather of the updated shards).  Results are
+ * bit-identical to the two calls.  Needs FSDP_ROLE_MASTER | GRAD | EXP_AVG |
+ * EXP_AVG_SQ on every group.
+ * Errors: as fsdp_adamw_groups and fsdp_pack_allgather_groups. */
+fsdp_status fsdp_adamw_pack_groups(const fsdp_group_set *set,
+                                   const fsdp_adamw_hparams_t *hp, int64_t step,
+                                   uint16_t *arena, void *stream);
+
+/* Flags of fsdp_step_group_set: AdamW and copy-in as one fused launch
+ * (fsdp_adamw_pack_groups) instead of two. */
+enum { FSDP_SET_ADAMW_COPY_IN = 1 };
+
 /* The unfused sharded step of a set, from native code on one stream:
  * fsdp_reduce_shard of every group in order (each group's reduce-scatter
- * output arrives on its own), then fsdp_adamw_groups, then
- * fsdp_pack_allgather_groups, then -- unless ag_out is NULL --
+ * output arrives on its own), then fsdp_adamw_groups and
+ * fsdp_pack_allgather_groups (with FSDP_SET_ADAMW_COPY_IN:
+ * fsdp_adamw_pack_groups), then -- unless ag_out is NULL --
  * fsdp_unpack_allgather of every group.  Master, grad, m, v, the arena
  * segments and the full tensors equal those of fsdp_step_groups with
  * FSDP_STEP_UNFUSED and ag_in[g] = the group's segment.
@@ -474,18 +495,20 @@ fsdp_status fsdp_pack_allgather_groups(const fsdp_group_set *set, uint16_t *aren
  *   timing_events  NULL, or 2*n_groups hipEvent_t: for the per-group
  *                  kernels (FSDP_KERNEL_REDUCE, FSDP_KERNEL_UNPACK) events
  *                  2g and 2g+1 bracket group g's launch; for the one-launch
- *                  kernels (FSDP_KERNEL_ADAMW, FSDP_KERNEL_PACK) events 0
- *                  and 1 bracket that launch.  A NULL pair is skipped; a
- *                  pair with one NULL is an error
+ *                  kernels (FSDP_KERNEL_ADAMW, FSDP_KERNEL_PACK, or with the
+ *                  flag FSDP_KERNEL_ADAMW_PACK) events 0 and 1 bracket that
+ *                  launch.  A NULL pair is skipped; a pair with one NULL is
+ *                  an error
  * Every argument is checked before anything is launched.  Errors: as the
- * calls it makes, plus FSDP_E_INVAL for a null rs_in array, an arena
- * overlapping an rs_in buffer or a timed kernel the call does not run. */
+ * calls it makes, plus FSDP_E_INVAL for a null rs_in array, an unknown
+ * flag, an arena overlapping an rs_in buffer or a timed kernel the call
+ * does not run. */
 fsdp_status fsdp_step_group_set(const fsdp_group_set *set,
                                 const uint16_t *const *rs_in, uint16_t *arena,
                                 const uint16_t *const *ag_out,
                                 const fsdp_adamw_hparams_t *hp, int64_t step,
-                                int32_t timed_kernel, void *const *timing_events,
-                                void *stream);
+                                uint32_t flags, int32_t timed_kernel,
+                                void *const *timing_events, void *stream);
 
 /* ---- CPU offload --------------------------------------------------------- */
 

@@ -44,6 +44,9 @@ FSDP_KERNEL_REDUCE = 1
 FSDP_KERNEL_ADAMW = 2
 FSDP_KERNEL_PACK = 3
 FSDP_KERNEL_UNPACK = 4
+FSDP_KERNEL_ADAMW_PACK = 5
+
+FSDP_SET_ADAMW_COPY_IN = 1
 
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
@@ -134,8 +137,9 @@ _SIGS = {
     "fsdp_group_set_segment": (_i32, [_P, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
     "fsdp_adamw_groups": (_i32, [_P, ctypes.POINTER(AdamwHparams), _i64, _P]),
     "fsdp_pack_allgather_groups": (_i32, [_P, _P, _P]),
-    "fsdp_step_group_set": (_i32, [_P, _PP, _P, _PP, ctypes.POINTER(AdamwHparams), _i64, _i32,
-                                   _PP, _P]),
+    "fsdp_adamw_pack_groups": (_i32, [_P, ctypes.POINTER(AdamwHparams), _i64, _P, _P]),
+    "fsdp_step_group_set": (_i32, [_P, _PP, _P, _PP, ctypes.POINTER(AdamwHparams), _i64,
+                                   ctypes.c_uint32, _i32, _PP, _P]),
     "fsdp_check_stream": (_i32, [_P]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -538,6 +542,15 @@ def fsdp_pack_allgather_groups(gset, arena, stream=None) -> None:
            "fsdp_pack_allgather_groups")
 
 
+def fsdp_adamw_pack_groups(gset, arena, lr: float, beta1: float, beta2: float, eps: float,
+                           weight_decay: float, step: int, stream=None) -> None:
+    n = _arena_elems(gset)
+    a = _dev(arena, 2 * n, "arena") if n is not None else addr(arena)
+    hp = AdamwHparams(lr, beta1, beta2, eps, weight_decay)
+    _check(lib.fsdp_adamw_pack_groups(gset, ctypes.byref(hp), step, a, stream_handle(stream)),
+           "fsdp_adamw_pack_groups")
+
+
 class StepGroupSetCall:
     """fsdp_step_group_set with its pointer arrays marshalled once.
 
@@ -547,7 +560,7 @@ class StepGroupSetCall:
     """
 
     def __init__(self, gset, plans, rs_in, arena, ag_out, lr, beta1, beta2, eps,
-                 weight_decay, stream=None):
+                 weight_decay, flags=0, stream=None):
         n = len(plans)
         if n != fsdp_group_set_info(gset)[0]:
             raise ValueError(f"plans: {n} given, the set has {fsdp_group_set_info(gset)[0]} groups")
@@ -566,6 +579,7 @@ class StepGroupSetCall:
         self._ag_out = _ptr_array(out_p) if ag_out is not None else None
         self._keep = (rs_in, arena, ag_out)
         self._hp = AdamwHparams(lr, beta1, beta2, eps, weight_decay)
+        self.flags = flags
         self._stream = stream_handle(stream)
 
     def __call__(self, step: int, timed_kernel: int = 0, events=None) -> None:
@@ -577,8 +591,8 @@ class StepGroupSetCall:
                 *[int(e.cuda_event) if e is not None else None for e in events])
             ev = ctypes.cast(ev, _PP)
         _check(lib.fsdp_step_group_set(self._set, self._rs, self._arena, self._ag_out,
-                                       ctypes.byref(self._hp), step, timed_kernel, ev,
-                                       self._stream), "fsdp_step_group_set")
+                                       ctypes.byref(self._hp), step, self.flags, timed_kernel,
+                                       ev, self._stream), "fsdp_step_group_set")
 
 
 def fsdp_check_stream(stream=None) -> None:

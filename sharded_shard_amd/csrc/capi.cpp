@@ -881,6 +881,21 @@ hipError_t do_pack_set(const fsdp_group_set *set, uint16_t *arena, hipStream_t s
         [&] { return fsdp::launch_pack(set->d_pack, set->n_pack, set->d_entries, arena, st); });
 }
 
+hipError_t do_adamw_pack_set(const fsdp_group_set *set, const float scal[8], uint16_t *arena,
+                             hipStream_t st) {
+    return guarded([&] {
+        return fsdp::launch_adamw_pack(set->d_pack, set->n_pack, set->d_entries, arena, scal, st);
+    });
+}
+
+fsdp_status check_arena(const fsdp_group_set *set, const uint16_t *arena, const char *call) {
+    if (arena == nullptr && set->seg_off.back() > 0)
+        return fail(FSDP_E_INVAL, std::string(call) + ": null arena");
+    if (misaligned(arena, 2))
+        return fail(FSDP_E_ALIGN, std::string(call) + ": arena not 2-byte aligned");
+    return FSDP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1034,18 +1049,27 @@ fsdp_status fsdp_pack_allgather_groups(const fsdp_group_set *set, uint16_t *aren
                                        void *stream) {
     const char *call = "fsdp_pack_allgather_groups";
     fsdp_status s = check_set(set, FSDP_ROLE_MASTER, call);
-    if (s != FSDP_OK) return s;
-    if (arena == nullptr && set->seg_off.back() > 0)
-        return fail(FSDP_E_INVAL, "fsdp_pack_allgather_groups: null arena");
-    if (misaligned(arena, 2))
-        return fail(FSDP_E_ALIGN, "fsdp_pack_allgather_groups: arena not 2-byte aligned");
+    if (s != FSDP_OK || (s = check_arena(set, arena, call)) != FSDP_OK) return s;
     return launched(do_pack_set(set, arena, static_cast<hipStream_t>(stream)),
                     "fsdp_pack_allgather_groups: launch");
 }
 
+fsdp_status fsdp_adamw_pack_groups(const fsdp_group_set *set, const fsdp_adamw_hparams_t *hp,
+                                   int64_t step, uint16_t *arena, void *stream) {
+    const char *call = "fsdp_adamw_pack_groups";
+    fsdp_status s = check_set(set, kAdamwRoles, call);
+    if (s != FSDP_OK || (s = check_hparams(hp, step, call)) != FSDP_OK ||
+        (s = check_arena(set, arena, call)) != FSDP_OK)
+        return s;
+    float scal[8];
+    adamw_scalars(hp, step, scal);
+    return launched(do_adamw_pack_set(set, scal, arena, static_cast<hipStream_t>(stream)),
+                    "fsdp_adamw_pack_groups: launch");
+}
+
 fsdp_status fsdp_step_group_set(const fsdp_group_set *set, const uint16_t *const *rs_in,
                                 uint16_t *arena, const uint16_t *const *ag_out,
-                                const fsdp_adamw_hparams_t *hp, int64_t step,
+                                const fsdp_adamw_hparams_t *hp, int64_t step, uint32_t flags,
                                 int32_t timed_kernel, void *const *timing_events,
                                 void *stream) {
     const char *call = "fsdp_step_group_set";
@@ -1053,14 +1077,17 @@ fsdp_status fsdp_step_group_set(const fsdp_group_set *set, const uint16_t *const
     if (s != FSDP_OK) return s;
     const int32_t n = static_cast<int32_t>(set->plans.size());
     if (rs_in == nullptr) return fail(FSDP_E_INVAL, "fsdp_step_group_set: null rs_in array");
-    if ((s = check_hparams(hp, step, call)) != FSDP_OK) return s;
-    if (arena == nullptr && set->seg_off.back() > 0)
-        return fail(FSDP_E_INVAL, "fsdp_step_group_set: null arena");
-    if (misaligned(arena, 2))
-        return fail(FSDP_E_ALIGN, "fsdp_step_group_set: arena not 2-byte aligned");
+    if ((flags & ~static_cast<uint32_t>(FSDP_SET_ADAMW_COPY_IN)) != 0)
+        return fail(FSDP_E_INVAL, "fsdp_step_group_set: unknown flag");
+    const bool fused = (flags & FSDP_SET_ADAMW_COPY_IN) != 0;
+    if ((s = check_hparams(hp, step, call)) != FSDP_OK ||
+        (s = check_arena(set, arena, call)) != FSDP_OK)
+        return s;
     if (timing_events != nullptr) {
-        const bool ok = timed_kernel == FSDP_KERNEL_REDUCE || timed_kernel == FSDP_KERNEL_ADAMW ||
-                        timed_kernel == FSDP_KERNEL_PACK ||
+        const bool ok = timed_kernel == FSDP_KERNEL_REDUCE ||
+                        (fused ? timed_kernel == FSDP_KERNEL_ADAMW_PACK
+                               : (timed_kernel == FSDP_KERNEL_ADAMW ||
+                                  timed_kernel == FSDP_KERNEL_PACK)) ||
                         (timed_kernel == FSDP_KERNEL_UNPACK && ag_out != nullptr);
         if (!ok) return fail(FSDP_E_INVAL, "fsdp_step_group_set: timed_kernel is not run by this call");
         for (int32_t g = 0; g < n; ++g)
@@ -1098,12 +1125,17 @@ fsdp_status fsdp_step_group_set(const fsdp_group_set *set, const uint16_t *const
         if (e != hipSuccess)
             return hip_fail(e, ("fsdp_step_group_set: reduce of group " + std::to_string(g)).c_str());
     }
-    if ((e = mark(0, FSDP_KERNEL_ADAMW, 0)) == hipSuccess &&
-        (e = do_adamw_set(set, scal, st)) == hipSuccess &&
-        (e = mark(0, FSDP_KERNEL_ADAMW, 1)) == hipSuccess &&
-        (e = mark(0, FSDP_KERNEL_PACK, 0)) == hipSuccess &&
-        (e = do_pack_set(set, arena, st)) == hipSuccess)
+    if (fused) {
+        if ((e = mark(0, FSDP_KERNEL_ADAMW_PACK, 0)) == hipSuccess &&
+            (e = do_adamw_pack_set(set, scal, arena, st)) == hipSuccess)
+            e = mark(0, FSDP_KERNEL_ADAMW_PACK, 1);
+    } else if ((e = mark(0, FSDP_KERNEL_ADAMW, 0)) == hipSuccess &&
+               (e = do_adamw_set(set, scal, st)) == hipSuccess &&
+               (e = mark(0, FSDP_KERNEL_ADAMW, 1)) == hipSuccess &&
+               (e = mark(0, FSDP_KERNEL_PACK, 0)) == hipSuccess &&
+               (e = do_pack_set(set, arena, st)) == hipSuccess) {
         e = mark(0, FSDP_KERNEL_PACK, 1);
+    }
     if (e != hipSuccess) return hip_fail(e, "fsdp_step_group_set: AdamW or copy-in");
     for (int32_t g = 0; ag_out != nullptr && g < n; ++g) {
         if ((e = mark(g, FSDP_KERNEL_UNPACK, 0)) == hipSuccess &&

@@ -27,6 +27,9 @@ hipError_t launch_reduce(const ReduceTile *tiles, int64_t n, const DevEntry *ent
 // 1-lr*wd, lr/(1-beta1^t), sqrt(1-beta2^t)
 hipError_t launch_adamw(const EwTile *tiles, int64_t n, const DevEntry *ents,
                         const float scal[8], hipStream_t st);
+// AdamW, then the bf16 copy-in of the new master, over the copy-in tiles
+hipError_t launch_adamw_pack(const PackTile *tiles, int64_t n, const DevEntry *ents,
+                             uint16_t *ag_in, const float scal[8], hipStream_t st);
 // fused reduce -> AdamW -> copy-in over the copy-in tiles
 hipError_t launch_step(const PackTile *tiles, int64_t n, const DevEntry *ents,
                        const uint16_t *rs_in, uint16_t *ag_in, int64_t S, int32_t N,

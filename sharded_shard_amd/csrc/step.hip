@@ -1,6 +1,7 @@
-// AdamW on the fp32 shards and the fused sharded step (reduce -> AdamW ->
-// copy-in in one pass), bit-identical to the separate kernels: the same
-// device functions in the same order, one fp32 rounding per operation.
+// AdamW on the fp32 shards, AdamW fused with the copy-in, and the fused
+// sharded step (reduce -> AdamW -> copy-in in one pass), bit-identical to the
+// separate kernels: the same device functions in the same order, one fp32
+// rounding per operation.
 #include "launch.hpp"
 #include "rows.hpp"
 
@@ -8,6 +9,14 @@
 // kernel itself but slowed the copy-in and copy-out after it by more)
 #ifndef FSDP_ADAMW_POL
 #define FSDP_ADAMW_POL 0
+#endif
+// AdamW fused with the copy-in: plain loads and stores, as AdamW; elements
+// per block
+#ifndef FSDP_ADAMW_PACK_POL
+#define FSDP_ADAMW_PACK_POL 0
+#endif
+#ifndef FSDP_ADAMW_PACK_SUB
+#define FSDP_ADAMW_PACK_SUB 4096
 #endif
 // shard policy of the wide fused step (plain: its lanes store two halves
 // of a 32-byte span, which non-temporal stores split into partial writes)
@@ -278,6 +287,102 @@ __device__ __forceinline__ void store8_at(uint16_t *p, uint32_t k, u32x2 w) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// AdamW fused with the copy-in: the optimizer step that also writes the next
+// all-gather's bf16 segment, with the gradient from the grad shards
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void adamw_pack_scalar_at(float *P, const float *G, float *M,
+                                                     float *Vv, uint16_t *dst, int64_t i,
+                                                     const AdamwScalars &c) {
+    float p = P[i], m = M[i], v = Vv[i];
+    adamw_elem(p, G[i], m, v, c);
+    P[i] = p;
+    M[i] = m;
+    Vv[i] = v;
+    dst[i] = static_cast<uint16_t>(bf16_rne(p));
+}
+
+// Valid elements [0, valid) of one run: AdamW exactly as adamw_run, then
+// the bf16 cast of the new master into dst as pack_run writes it; zeros in
+// dst from valid to len.  Four elements per lane and vector, two vectors a
+// block apart per iteration; the bf16 output stored by its own 8-byte phase.
+template <int POL>
+__device__ __forceinline__ void adamw_pack_run(float *P, const float *G, float *M, float *Vv,
+                                               uint16_t *dst, int64_t len, int64_t valid,
+                                               const AdamwScalars &c) {
+    constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
+    const int tid = threadIdx.x;
+    const uint32_t ap = lo32(P) & 15u;
+    const bool same = ap == (lo32(G) & 15u) && ap == (lo32(M) & 15u) && ap == (lo32(Vv) & 15u);
+    if (!same) {
+        for (int64_t i = tid; i < valid; i += kBlock) adamw_pack_scalar_at(P, G, M, Vv, dst, i, c);
+    } else {
+        int64_t head = ((16u - ap) & 15u) >> 2;
+        if (head > valid) head = valid;
+        if (tid < head) adamw_pack_scalar_at(P, G, M, Vv, dst, tid, c);
+        const int64_t nvec = (valid - head) >> 2;
+        f32x4 *pv = reinterpret_cast<f32x4 *>(P + head);
+        const f32x4 *gv = reinterpret_cast<const f32x4 *>(G + head);
+        f32x4 *mv = reinterpret_cast<f32x4 *>(M + head);
+        f32x4 *vv = reinterpret_cast<f32x4 *>(Vv + head);
+        uint16_t *d = dst + head;
+        const uint32_t k8 = lo32(d) & 7u;
+        int64_t i = tid;
+        for (; i + kBlock < nvec; i += 2 * kBlock) {
+            const int64_t i1 = i + kBlock;
+            f32x4 p0 = ldp<LN>(pv + i), m0 = ldp<LN>(mv + i), v0 = ldp<LN>(vv + i);
+            f32x4 p1 = ldp<LN>(pv + i1), m1 = ldp<LN>(mv + i1), v1 = ldp<LN>(vv + i1);
+            const f32x4 g0 = ldp<LN>(gv + i), g1 = ldp<LN>(gv + i1);
+            adamw_vec(p0, g0, m0, v0, c);
+            adamw_vec(p1, g1, m1, v1, c);
+            stp<SN>(pv + i, p0);
+            stp<SN>(mv + i, m0);
+            stp<SN>(vv + i, v0);
+            stp<SN>(pv + i1, p1);
+            stp<SN>(mv + i1, m1);
+            stp<SN>(vv + i1, v1);
+            store8_at<SN>(d + (i << 2), k8, u32x2{pack2(p0.x, p0.y), pack2(p0.z, p0.w)});
+            store8_at<SN>(d + (i1 << 2), k8, u32x2{pack2(p1.x, p1.y), pack2(p1.z, p1.w)});
+        }
+        if (i < nvec) {
+            f32x4 p0 = ldp<LN>(pv + i), m0 = ldp<LN>(mv + i), v0 = ldp<LN>(vv + i);
+            const f32x4 g0 = ldp<LN>(gv + i);
+            adamw_vec(p0, g0, m0, v0, c);
+            stp<SN>(pv + i, p0);
+            stp<SN>(mv + i, m0);
+            stp<SN>(vv + i, v0);
+            store8_at<SN>(d + (i << 2), k8, u32x2{pack2(p0.x, p0.y), pack2(p0.z, p0.w)});
+        }
+        const int64_t e = head + (nvec << 2) + tid;
+        if (e < valid) adamw_pack_scalar_at(P, G, M, Vv, dst, e, c);
+    }
+    zero_bf16<SN>(dst, valid, len);
+}
+
+// Over copy-in tiles: AdamW of the tile's valid elements and their bf16
+// copy into ag_in (the set's arena), zeros in the padding.
+template <int POL>
+__global__ __launch_bounds__(kBlock) void adamw_pack_kernel(
+    const PackTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
+    const DevEntry *__restrict__ ents, uint16_t *__restrict__ ag_in, AdamwScalars c) {
+    const int64_t L = sub;
+    const int64_t nvt = n_tiles * split;
+    for (int64_t vt = first_vt(); vt < nvt; vt += gridDim.x) {
+        int64_t t, b;
+        sub_range(vt, split, L, &t, &b);
+        const PackTile tl = tiles[t];
+        if (b >= tl.len) continue;
+        const int64_t len = tl.len - b < L ? tl.len - b : L;
+        int64_t valid = tl.valid - b;
+        valid = valid < 0 ? 0 : (valid > len ? len : valid);
+        const DevEntry en = ents[tl.entry];
+        const int64_t o = tl.src + b;
+        adamw_pack_run<POL>(en.master + o, en.grad + o, en.exp_avg + o, en.exp_avg_sq + o,
+                            ag_in + tl.dst + b, len, valid, c);
+    }
+}
+
 // The fused step, a quad per lane and pass: lane l of a wave takes quads
 // l + 64 h (h < QP) of the wave's 64 QP, so every load and store instruction
 // of the wave is contiguous (rows 512 bytes, shards 1 KB, the bf16 output 512
@@ -428,6 +533,15 @@ hipError_t launch_adamw(const EwTile *tiles, int64_t n, const DevEntry *ents,
     const int32_t sp = split_for(kTileAdamw, FSDP_ADAMW_SUB);
     adamw_kernel<FSDP_ADAMW_POL><<<grid_for(n, sp), kBlock, 0, st>>>(
         tiles, n, sp, kTileAdamw / sp, ents, to_scalars(scal));
+    return hipGetLastError();
+}
+
+hipError_t launch_adamw_pack(const PackTile *tiles, int64_t n, const DevEntry *ents,
+                             uint16_t *ag_in, const float scal[8], hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const int32_t sp = split_for(kTilePack, FSDP_ADAMW_PACK_SUB);
+    adamw_pack_kernel<FSDP_ADAMW_PACK_POL><<<grid_for(n, sp), kBlock, 0, st>>>(
+        tiles, n, sp, kTilePack / sp, ents, ag_in, to_scalars(scal));
     return hipGetLastError();
 }
 

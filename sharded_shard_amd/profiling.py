@@ -3,8 +3,8 @@
     python -m sharded_shard_amd.profiling <rocprof dir> <profiles dir>
 
 The rocprof directory holds, per workload tag (c1, c2, c3, c4; c2u/c4u for
-the separate kernels per group and c2s/c4s for them through a group set),
-the output of
+the separate kernels per group, c2s/c4s for them through a group set and
+c2f/c4f for a group set with AdamW and the copy-in fused), the output of
 
 * ``<tag>_trace``: ``rocprofv3 --kernel-trace --stats -T -f csv`` of bench.py
   (kernel durations, averaged per kernel name);
@@ -49,10 +49,11 @@ WORKLOADS = {   # tag: (config, label, file stem)
 }
 # separate-kernel traces: tag -> (workload tag, bench options, group set)
 SEPARATE = {"c2u": ("c2", "--unfused", False), "c4u": ("c4", "--unfused", False),
-            "c2s": ("c2", "--group-set", True), "c4s": ("c4", "--group-set", True)}
+            "c2s": ("c2", "--group-set", True), "c4s": ("c4", "--group-set", True),
+            "c2f": ("c2", "--group-set-fused", True), "c4f": ("c4", "--group-set-fused", True)}
 # kernels a group set launches once per step over every group: one launch
 # moves the bytes of all groups
-SET_KERNELS = ("adamw_kernel", "pack_kernel")
+SET_KERNELS = ("adamw_kernel", "pack_kernel", "adamw_pack_kernel")
 
 # kernel name -> algorithmic bytes of one launch for a group (S, V, F, N)
 ALG = {
@@ -62,6 +63,7 @@ ALG = {
     "unpack_kernel": lambda S, V, F, N: 4 * F,
     "reduce_kernel": lambda S, V, F, N: 2 * N * V + 4 * V,
     "adamw_kernel": lambda S, V, F, N: 28 * V,
+    "adamw_pack_kernel": lambda S, V, F, N: 28 * V + 2 * S,
     "pack_kernel": lambda S, V, F, N: 4 * V + 2 * S,
     "rspack_bf16_kernel": lambda S, V, F, N: 2 * F + 2 * N * S,
     "rspack_f32_kernel": lambda S, V, F, N: 2 * F + 4 * N * S,
@@ -231,7 +233,7 @@ def summarize(prof, out_dir, sha):
             sstats = kernel_stats(prof, sep_tag)
             lines += ["", f"## Separate-kernel path ({opt})", "", "```",
                       _trace_cmd(sep_tag, args + " " + opt), "```", ""]
-            lines += (["A reduce and a copy-out per group; " + " and ".join(SET_KERNELS) +
+            lines += (["A reduce and a copy-out per group; " + " / ".join(SET_KERNELS) +
                        " run once per step over every group (a group set), so one launch "
                        "moves the bytes of all groups.", ""] if is_set else
                       ["Reduce, AdamW, copy-in and copy-out per group, one group after the "

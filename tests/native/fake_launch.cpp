@@ -80,6 +80,21 @@ hipError_t launch_reduce(const ReduceTile *tiles, int64_t n, const DevEntry *ent
     return hipSuccess;
 }
 
+hipError_t launch_adamw_pack(const PackTile *tiles, int64_t n, const DevEntry *ents,
+                             uint16_t *ag_in, const float *, hipStream_t) {
+    ++harness::launches;
+    for (int64_t i = 0; i < n; ++i) {
+        const PackTile &t = tiles[i];
+        const DevEntry &e = ents[t.entry];
+        touch(e.grad, t.src, t.valid);
+        touch(e.exp_avg, t.src, t.valid);
+        touch(e.exp_avg_sq, t.src, t.valid);
+        wrote(e.master, t.src, t.valid, harness::kShard);
+        wrote(ag_in, t.dst, t.len, harness::kSegment);
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_adamw(const EwTile *tiles, int64_t n, const DevEntry *ents, const float *,
                         hipStream_t) {
     ++harness::launches;

@@ -318,7 +318,7 @@ void group_sets(const Workload &w, Instance &a, Instance &b) {
     const uint16_t *rs[2] = {a.rs, b.rs};
     const uint16_t *ag_out[2] = {a.ag, b.ag};
     harness::spans.clear();
-    CHECK_STATUS(fsdp_step_group_set(set, rs, arena, ag_out, &kHp, 2, 0, nullptr, nullptr),
+    CHECK_STATUS(fsdp_step_group_set(set, rs, arena, ag_out, &kHp, 2, 0, 0, nullptr, nullptr),
                  FSDP_OK);
     check_arena("set executor copy-in");
     for (Instance *in : {&a, &b}) {
@@ -329,21 +329,49 @@ void group_sets(const Workload &w, Instance &a, Instance &b) {
     int ev_storage[4];
     void *evs[4] = {&ev_storage[0], &ev_storage[1], &ev_storage[2], &ev_storage[3]};
     for (int32_t k : {FSDP_KERNEL_REDUCE, FSDP_KERNEL_ADAMW, FSDP_KERNEL_PACK, FSDP_KERNEL_UNPACK})
-        CHECK_STATUS(fsdp_step_group_set(set, rs, arena, ag_out, &kHp, 3, k, evs, nullptr),
+        CHECK_STATUS(fsdp_step_group_set(set, rs, arena, ag_out, &kHp, 3, 0, k, evs, nullptr),
                      FSDP_OK);
-    CHECK_STATUS(fsdp_step_group_set(set, rs, arena, ag_out, &kHp, 3, FSDP_KERNEL_STEP, evs,
+    CHECK_STATUS(fsdp_step_group_set(set, rs, arena, ag_out, &kHp, 3, 0, FSDP_KERNEL_STEP, evs,
                                      nullptr),
                  FSDP_E_INVAL);
-    CHECK_STATUS(fsdp_step_group_set(set, rs, arena, nullptr, &kHp, 3, FSDP_KERNEL_UNPACK, evs,
-                                     nullptr),
+    CHECK_STATUS(fsdp_step_group_set(set, rs, arena, ag_out, &kHp, 3, 0, FSDP_KERNEL_ADAMW_PACK,
+                                     evs, nullptr),
                  FSDP_E_INVAL);
+    CHECK_STATUS(fsdp_step_group_set(set, rs, arena, nullptr, &kHp, 3, 0, FSDP_KERNEL_UNPACK,
+                                     evs, nullptr),
+                 FSDP_E_INVAL);
+    // AdamW and copy-in fused: one launch, the same coverage
+    for (int32_t k : {FSDP_KERNEL_REDUCE, FSDP_KERNEL_ADAMW_PACK, FSDP_KERNEL_UNPACK}) {
+        harness::spans.clear();
+        const long l0 = harness::launches;
+        CHECK_STATUS(fsdp_step_group_set(set, rs, arena, ag_out, &kHp, 3, FSDP_SET_ADAMW_COPY_IN,
+                                         k, evs, nullptr),
+                     FSDP_OK);
+        CHECK(harness::launches == l0 + 5, "%s: %ld launches, wanted 5", w.name.c_str(),
+              harness::launches - l0);
+        check_arena("set executor, fused AdamW and copy-in");
+        for (Instance *in : {&a, &b}) {
+            check_shards(*in, in->grad, "set executor reduce", w.name);
+            check_shards(*in, in->master, "set executor fused AdamW", w.name);
+        }
+    }
+    CHECK_STATUS(fsdp_step_group_set(set, rs, arena, ag_out, &kHp, 3, FSDP_SET_ADAMW_COPY_IN,
+                                     FSDP_KERNEL_ADAMW, evs, nullptr),
+                 FSDP_E_INVAL);
+    CHECK_STATUS(fsdp_step_group_set(set, rs, arena, ag_out, &kHp, 3, 2u, 0, nullptr, nullptr),
+                 FSDP_E_INVAL);
+    harness::spans.clear();
+    CHECK_STATUS(fsdp_adamw_pack_groups(set, &kHp, 4, arena, nullptr), FSDP_OK);
+    check_arena("fused AdamW and copy-in");
+    for (Instance *in : {&a, &b}) check_shards(*in, in->master, "fused AdamW", w.name);
+    CHECK_STATUS(fsdp_adamw_pack_groups(set, nullptr, 4, arena, nullptr), FSDP_E_INVAL);
     evs[1] = nullptr;
-    CHECK_STATUS(fsdp_step_group_set(set, rs, arena, ag_out, &kHp, 3, FSDP_KERNEL_ADAMW, evs,
+    CHECK_STATUS(fsdp_step_group_set(set, rs, arena, ag_out, &kHp, 3, 0, FSDP_KERNEL_ADAMW, evs,
                                      nullptr),
                  FSDP_E_INVAL);
-    CHECK_STATUS(fsdp_step_group_set(set, nullptr, arena, ag_out, &kHp, 3, 0, nullptr, nullptr),
+    CHECK_STATUS(fsdp_step_group_set(set, nullptr, arena, ag_out, &kHp, 3, 0, 0, nullptr, nullptr),
                  FSDP_E_INVAL);
-    CHECK_STATUS(fsdp_step_group_set(set, rs, arena, ag_out, &kHp, 0, 0, nullptr, nullptr),
+    CHECK_STATUS(fsdp_step_group_set(set, rs, arena, ag_out, &kHp, 0, 0, 0, nullptr, nullptr),
                  FSDP_E_INVAL);
     if (S > 0) {
         CHECK_STATUS(fsdp_pack_allgather_groups(set, nullptr, nullptr), FSDP_E_INVAL);
@@ -353,7 +381,7 @@ void group_sets(const Workload &w, Instance &a, Instance &b) {
                      FSDP_E_ALIGN);
         // the arena may not cover a group's reduce-scatter input
         CHECK_STATUS(fsdp_step_group_set(set, rs, const_cast<uint16_t *>(b.rs), ag_out, &kHp, 3, 0,
-                                         nullptr, nullptr),
+                                         0, nullptr, nullptr),
                      FSDP_E_INVAL);
         setenv("FSDP_FAULT", "launch", 1);
         const long l0 = harness::launches;

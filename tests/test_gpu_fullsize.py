@@ -11,8 +11,9 @@ plans, tiles and grids).  Outputs are checked three ways:
   read back (first and last elements, tile edges, random picks), for the
   separate kernels and the single-group fused call;
 * whole workloads through a group set: the separate-kernel path (a reduce per
-  group, one AdamW and one copy-in launch over all 33 or 81 groups) equals the
-  fused executor bit for bit in every shard and copy-in segment;
+  group, one AdamW and one copy-in launch over all 33 or 81 groups, or the two
+  fused in one launch) equals the fused executor bit for bit in every shard
+  and copy-in segment;
 * exact properties over every element: unpack of every rank's pack of a full
   weight W gives bf16(W) back bit for bit, with torch's library cast as the
   reference; N equal gradient contributions reduce to exactly that gradient.
@@ -365,8 +366,9 @@ def test_step_groups_whole_groups_every_element(name, cfg_index, group_ids, rank
 # element of the grad, master, m and v shards and of every copy-in segment
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("fuse", [False, True], ids=["two-launches", "adamw-copy-in"])
 @pytest.mark.parametrize("cfg_index", [2, 4])
-def test_group_set_every_group_equals_fused_executor(cfg_index):
+def test_group_set_every_group_equals_fused_executor(cfg_index, fuse):
     cfg = configs.get(cfg_index)
     n, hp, rank = cfg.world, vars(cfg.hp), cfg.timing_rank
     shapes = [[p.shape for p in grp.params] for grp in cfg.groups]
@@ -391,11 +393,12 @@ def test_group_set_every_group_equals_fused_executor(cfg_index):
     gset = capi.fsdp_group_set_create([g.plan for g in B])
     offs = [capi.fsdp_group_set_segment(gset, gi)[0] for gi in range(len(B))]
     arena = torch.empty(capi.fsdp_group_set_segment(gset, 0)[1], dtype=torch.int16, device=DEV)
-    separate = capi.StepGroupSetCall(gset, [g.plan for g in B], rs, arena, None, **hp)
+    separate = capi.StepGroupSetCall(gset, [g.plan for g in B], rs, arena, None,
+                                     flags=capi.FSDP_SET_ADAMW_COPY_IN if fuse else 0, **hp)
     for t in (1, 2):
         for b in range(2):
             synth.fill_normal_bf16_bits_(rs_arena[b], cfg.grad_std, ("set-full-rs", cfg_index, b, t))
-        print(f"[fullsize] group set c{cfg_index} step {t}", flush=True)
+        print(f"[fullsize] group set c{cfg_index} fuse={fuse} step {t}", flush=True)
         fused(t)
         separate(t)
         torch.cuda.synchronize()

@@ -520,17 +520,18 @@ def _same_bf16_nan_ok(got, want, what):
     assert np.array_equal(got[~gn], want[~wn]), what
 
 
-@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+@pytest.mark.parametrize("fused", ["separate", "fused", "set"])
 @pytest.mark.parametrize("n,align", [(3, 1), (6, 1), (8, 8), (16, 8), (64, 8)])
 def test_step_special_values_match_oracle(n, align, fused):
     """Infinities, NaNs, overflowing sums, subnormals and signed zeros through
     reduce, AdamW and the copy-in for 3 steps, on the misaligned, aligned and
-    wide kernels: every output bit-exact with the oracle, NaNs matched as
-    NaNs."""
+    wide kernels, and with AdamW fused with the copy-in over a group set:
+    every output bit-exact with the oracle, NaNs matched as NaNs."""
     shapes = [(37, 5), (64,), (130, 3), (9, 129), (1024, 16)]
     r = n // 2
     plan = O.plan(shapes, n, r, align)
     g = ShardedGroup(shapes, n, r, align)
+    gset = capi.fsdp_group_set_create([g.plan]) if fused == "set" else None
     rng = np.random.default_rng(7000 + n)
     masters = []
     for i, e in enumerate(g.entries):
@@ -553,14 +554,18 @@ def test_step_special_values_match_oracle(n, align, fused):
         rs[:, cols[:2]] = 0x0001
         rs[:, cols[2:]] = 0x807F
         d_rs = torch.from_numpy(rs.reshape(-1).view(np.int16)).to(DEV)
-        ag = torch.zeros(plan.S, dtype=torch.int16, device=DEV)
-        if fused:
-            g.step(d_rs, ag, t, write_grad=True, **HP)
+        ag = torch.zeros((plan.S + 7) // 8 * 8, dtype=torch.int16, device=DEV)
+        if fused == "fused":
+            g.step(d_rs, ag[:plan.S], t, write_grad=True, **HP)
+        elif fused == "set":
+            g.reduce(d_rs)
+            capi.fsdp_adamw_pack_groups(gset, ag, step=t, **HP)
         else:
             g.reduce(d_rs)
             g.adamw(t, **HP)
-            g.pack(ag)
+            g.pack(ag[:plan.S])
         torch.cuda.synchronize()
+        ag = ag[:plan.S]
         with np.errstate(all="ignore"):
             grads = O.reduce(plan, rs)
             for x, gr, m, v in zip(masters, grads, ms, vs):
@@ -576,6 +581,8 @@ def test_step_special_values_match_oracle(n, align, fused):
             _same_f32_nan_ok(f32(g.shard_view(g.master_flat, i)), masters[i], ("p", n, t, i))
             _same_f32_nan_ok(f32(g.shard_view(g.m_flat, i)), ms[i], ("m", n, t, i))
             _same_f32_nan_ok(f32(g.shard_view(g.v_flat, i)), vs[i], ("v", n, t, i))
+    if gset is not None:
+        capi.fsdp_group_set_destroy(gset)
     g.close()
     assert seen == {"nan", "inf", "sub"}, seen     # the specials reached the reduction
 
@@ -616,6 +623,69 @@ def test_fused_step_mixed_alignment_shards():
             _cmp_f32(f32(views[2][i]), ms[i], ("m", t, i))
             _cmp_f32(f32(views[3][i]), vs[i], ("v", t, i))
     g.close()
+
+
+@pytest.mark.parametrize("arena_off", [0, 1, 2, 3])
+def test_set_adamw_copy_in_mixed_alignment_and_output_phase(arena_off):
+    """AdamW fused with the copy-in over a group set: shards whose pointers
+    differ modulo 16 take the element-wise path, equal ones the vector path,
+    and the bf16 output lands at every 2-byte phase; both against the oracle
+    and against fsdp_adamw_groups + fsdp_pack_allgather_groups."""
+    shapes, n, r = [(41, 9), (777,), (3, 5), (128, 8)], 3, 1
+    plan = O.plan(shapes, n, r)
+    g = ShardedGroup(shapes, n, r, bind=False)
+    h = ShardedGroup(shapes, n, r)                  # equal phases: the vector path
+    bufs = [torch.zeros(plan.V + 64, dtype=torch.float32, device=DEV) for _ in range(4)]
+    views = [[], [], [], []]
+    for role in range(4):
+        o = 1 + role
+        for e in g.entries:
+            views[role].append(bufs[role][o:o + e.valid_numel])
+            o += e.valid_numel + 5
+    host = []
+    for i, e in enumerate(g.entries):
+        p0 = synth.normal_f32(e.valid_numel, 0.02, ("sm", i))
+        g0 = synth.normal_f32(e.valid_numel, 1e-3, ("sg", i))
+        views[0][i].copy_(p0)
+        views[1][i].copy_(g0)
+        h.shard_view(h.master_flat, i).copy_(p0)
+        h.shard_view(h.grad_flat, i).copy_(g0)
+        host.append((p0.numpy().copy(), g0.numpy().copy()))
+    capi.fsdp_bind(g.plan, *[[v.data_ptr() for v in views[role]] for role in range(4)], None)
+    ref = ShardedGroup(shapes, n, r)                # h's twin through the two launches
+    ref.master_flat.copy_(h.master_flat)
+    ref.grad_flat.copy_(h.grad_flat)
+    sets = [capi.fsdp_group_set_create([x.plan]) for x in (g, h, ref)]
+    total = capi.fsdp_group_set_info(sets[0])[1]
+    arenas = [torch.full((total + 8,), 0x5A5A, dtype=torch.int16, device=DEV) for _ in range(3)]
+    ms = [np.zeros_like(p) for p, _ in host]
+    vs = [np.zeros_like(p) for p, _ in host]
+    ps = [p.copy() for p, _ in host]
+    for t in (1, 2):
+        a = [x[arena_off:arena_off + total] for x in arenas]
+        capi.fsdp_adamw_pack_groups(sets[0], a[0], step=t, **HP)
+        capi.fsdp_adamw_pack_groups(sets[1], a[1], step=t, **HP)
+        capi.fsdp_adamw_groups(sets[2], step=t, **HP)
+        capi.fsdp_pack_allgather_groups(sets[2], a[2])
+        torch.cuda.synchronize()
+        for x, (_, gr), m, v in zip(ps, host, ms, vs):
+            O.adamw(x, gr, m, v, t, **HP)
+        want = O.pack(plan, ps)
+        for k in range(3):
+            assert np.array_equal(u16(a[k])[:plan.S], want), (k, t)
+            assert (u16(arenas[k])[:arena_off] == 0x5A5A).all()
+            assert (u16(arenas[k])[arena_off + plan.S:] == 0x5A5A).all()
+        for i in range(len(shapes)):
+            _cmp_f32(f32(views[0][i]), ps[i], ("p", t, i))
+            _cmp_f32(f32(views[2][i]), ms[i], ("m", t, i))
+            _cmp_f32(f32(views[3][i]), vs[i], ("v", t, i))
+            for x in (h, ref):
+                _cmp_f32(f32(x.shard_view(x.master_flat, i)), ps[i], ("p vec", t, i))
+                _cmp_f32(f32(x.shard_view(x.m_flat, i)), ms[i], ("m vec", t, i))
+    for st in sets:
+        capi.fsdp_group_set_destroy(st)
+    for x in (g, h, ref):
+        x.close()
 
 
 def test_fused_step_rejects_unbound_and_bad_flags():
@@ -760,11 +830,13 @@ def _set_groups(kind):
     return groups, 8, 3
 
 
+@pytest.mark.parametrize("fuse", [False, True], ids=["two-launches", "adamw-copy-in"])
 @pytest.mark.parametrize("kind", ["n6", "n64", "many"])
-def test_group_set_equals_per_group_unfused_step_and_oracle(kind):
-    """fsdp_step_group_set (one AdamW and one copy-in launch over every group)
-    against fsdp_step_groups with FSDP_STEP_UNFUSED (per-group launches) over
-    3 steps, every tensor bit for bit, and the first step against the oracle."""
+def test_group_set_equals_per_group_unfused_step_and_oracle(kind, fuse):
+    """fsdp_step_group_set (one AdamW and one copy-in launch over every group,
+    or the two fused in one launch) against fsdp_step_groups with
+    FSDP_STEP_UNFUSED (per-group launches) over 3 steps, every tensor bit for
+    bit, and the first step against the oracle."""
     group_shapes, n, r = _set_groups(kind)
     A, B, rs_bufs, ag_a, ag_b, plans = [], [], [], [], [], []
     for gi, shapes in enumerate(group_shapes):
@@ -792,7 +864,8 @@ def test_group_set_equals_per_group_unfused_step_and_oracle(kind):
     in_a = [torch.zeros(g.S, dtype=torch.int16, device=DEV) for g in A]
     call_a = capi.StepGroupsCall([g.plan for g in A], rs_bufs, in_a, ag_a,
                                  flags=capi.FSDP_STEP_UNFUSED, **HP)
-    call_b = capi.StepGroupSetCall(gset, [g.plan for g in B], rs_bufs, arena, ag_b, **HP)
+    call_b = capi.StepGroupSetCall(gset, [g.plan for g in B], rs_bufs, arena, ag_b,
+                                   flags=capi.FSDP_SET_ADAMW_COPY_IN if fuse else 0, **HP)
     gap = torch.ones(total, dtype=torch.bool, device=DEV)
     for (o, _), g in zip(seg, B):
         gap[o:o + g.S] = False
@@ -801,8 +874,10 @@ def test_group_set_equals_per_group_unfused_step_and_oracle(kind):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(B))]
         for e in evs:
             e.record()
-        call_b(t, [capi.FSDP_KERNEL_REDUCE, capi.FSDP_KERNEL_ADAMW, capi.FSDP_KERNEL_PACK][t - 1],
-               evs)
+        kinds = ([capi.FSDP_KERNEL_REDUCE, capi.FSDP_KERNEL_ADAMW_PACK, capi.FSDP_KERNEL_UNPACK]
+                 if fuse else
+                 [capi.FSDP_KERNEL_REDUCE, capi.FSDP_KERNEL_ADAMW, capi.FSDP_KERNEL_PACK])
+        call_b(t, kinds[t - 1], evs)
         torch.cuda.synchronize()
         assert evs[0].elapsed_time(evs[1]) >= 0
         for gi, (ga, gb) in enumerate(zip(A, B)):
@@ -830,8 +905,11 @@ def test_group_set_equals_per_group_unfused_step_and_oracle(kind):
                 full_in = u16(ag_b[gi]).reshape(n, plan.S)
                 for i, want in enumerate(O.unpack(plan, full_in)):
                     assert np.array_equal(u16(gb.full_view(i)), want), ("full", gi, i)
-    capi.fsdp_adamw_groups(gset, step=4, **HP)
-    capi.fsdp_pack_allgather_groups(gset, arena)
+    if fuse:
+        capi.fsdp_adamw_pack_groups(gset, arena, step=4, **HP)
+    else:
+        capi.fsdp_adamw_groups(gset, step=4, **HP)
+        capi.fsdp_pack_allgather_groups(gset, arena)
     for gi, ga in enumerate(A):
         ga.adamw(4, **HP)
         ga.pack(in_a[gi])
