@@ -458,10 +458,11 @@ fsdp_status fsdp_adamw_groups(const fsdp_group_set *set,
 
 /* fsdp_pack_allgather of every group of the set into its segment of
  * `arena` (bf16, 2-byte aligned; 16-byte aligned for full-width stores), in
- * one launch; each segment equals the per-group copy-in.  Needs
+ * one launch; each segment equals the per-group copy-in.  The arena may not
+ * share a byte with any bound shard tensor of the set.  Needs
  * FSDP_ROLE_MASTER on every group.
- * Errors: FSDP_E_INVAL (null set, null arena), FSDP_E_ALIGN, FSDP_E_STATE,
- *         FSDP_E_HIP. */
+ * Errors: FSDP_E_INVAL (null set, null arena, arena overlapping a shard),
+ *         FSDP_E_ALIGN, FSDP_E_STATE, FSDP_E_HIP. */
 fsdp_status fsdp_pack_allgather_groups(const fsdp_group_set *set, uint16_t *arena,
                                        void *stream);
 

@@ -46,6 +46,7 @@ struct fsdp_group_set {
     std::vector<fsdp_plan *> plans;
     std::vector<int64_t> ent_off, seg_off;  // n_groups + 1 prefix offsets
     std::vector<fsdp::DevEntry> snapshot;   // concatenated entries at creation
+    std::vector<std::pair<uintptr_t, uintptr_t>> shard_bytes;  // union of the shard tensors
     int device = -1;
     char *dmem = nullptr;
     fsdp::DevEntry *d_entries = nullptr;
@@ -806,7 +807,7 @@ int64_t round8(int64_t n) { return (n + 7) & ~static_cast<int64_t>(7); }
 // No element of a written AdamW shard (master, exp_avg, exp_avg_sq) may
 // belong to any other bound shard of the set (those three or grad), in
 // this group or another: one launch updates them all at once.
-fsdp_status check_disjoint(const fsdp_group_set *set) {
+fsdp_status check_disjoint(fsdp_group_set *set) {
     struct Span {
         uintptr_t lo, hi;
         bool written;
@@ -830,6 +831,11 @@ fsdp_status check_disjoint(const fsdp_group_set *set) {
     }
     std::sort(spans.begin(), spans.end(),
               [](const Span &a, const Span &b) { return a.lo < b.lo; });
+    for (const Span &sp : spans)      // sorted, merged: a copy-in arena is checked against it
+        if (!set->shard_bytes.empty() && sp.lo <= set->shard_bytes.back().second)
+            set->shard_bytes.back().second = std::max(set->shard_bytes.back().second, sp.hi);
+        else
+            set->shard_bytes.emplace_back(sp.lo, sp.hi);
     // Every overlapping pair is seen when its later-starting span comes up:
     // it meets an earlier written span, or it is written and meets any.
     uintptr_t end_any = 0, end_written = 0;
@@ -888,11 +894,23 @@ hipError_t do_adamw_pack_set(const fsdp_group_set *set, const float scal[8], uin
     });
 }
 
+// The copy-in arena is written in the same launch that reads (and, fused,
+// writes) the shards: it must not share a byte with any of them.
 fsdp_status check_arena(const fsdp_group_set *set, const uint16_t *arena, const char *call) {
-    if (arena == nullptr && set->seg_off.back() > 0)
+    const int64_t elems = set->seg_off.back();
+    if (arena == nullptr && elems > 0)
         return fail(FSDP_E_INVAL, std::string(call) + ": null arena");
     if (misaligned(arena, 2))
         return fail(FSDP_E_ALIGN, std::string(call) + ": arena not 2-byte aligned");
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(arena);
+    const uintptr_t a1 = a0 + static_cast<uintptr_t>(elems) * 2;
+    // the first merged span ending after a0 is the only one that can overlap
+    auto it = std::upper_bound(set->shard_bytes.begin(), set->shard_bytes.end(), a0,
+                               [](uintptr_t v, const std::pair<uintptr_t, uintptr_t> &sp) {
+                                   return v < sp.second;
+                               });
+    if (elems > 0 && it != set->shard_bytes.end() && it->first < a1)
+        return fail(FSDP_E_INVAL, std::string(call) + ": arena overlaps a bound shard tensor");
     return FSDP_OK;
 }
 

@@ -379,6 +379,14 @@ void group_sets(const Workload &w, Instance &a, Instance &b) {
                                                          reinterpret_cast<char *>(arena) + 1),
                                                 nullptr),
                      FSDP_E_ALIGN);
+        // the arena may not cover a shard tensor of the set
+        uint16_t *in_master = nullptr;
+        for (size_t i = 0; i < a.ents.size() && in_master == nullptr; ++i)
+            if (a.ents[i].valid_numel > 0) in_master = reinterpret_cast<uint16_t *>(a.master[i]);
+        if (in_master != nullptr) {
+            CHECK_STATUS(fsdp_pack_allgather_groups(set, in_master - 3, nullptr), FSDP_E_INVAL);
+            CHECK_STATUS(fsdp_adamw_pack_groups(set, &kHp, 1, in_master, nullptr), FSDP_E_INVAL);
+        }
         // the arena may not cover a group's reduce-scatter input
         CHECK_STATUS(fsdp_step_group_set(set, rs, const_cast<uint16_t *>(b.rs), ag_out, &kHp, 3, 0,
                                          0, nullptr, nullptr),

@@ -936,7 +936,15 @@ def test_group_set_refuses_rebound_groups_and_overlapping_shards():
     assert ei.value.status == capi.FSDP_E_STATE
     capi.fsdp_bind(g2.plan, master=g2._ptrs(g2.master_flat))
     capi.fsdp_adamw_groups(gset, step=2, **HP)
+    # an arena over a shard tensor of the set is refused before any launch
+    before = g1.master_flat.clone()
+    for call in (lambda a: capi.fsdp_pack_allgather_groups(gset, a),
+                 lambda a: capi.fsdp_adamw_pack_groups(gset, a, step=3, **HP)):
+        with pytest.raises(capi.FsdpError) as ei:
+            call(g1.master_flat.data_ptr() + 8)
+        assert ei.value.status == capi.FSDP_E_INVAL and "overlaps" in str(ei.value)
     torch.cuda.synchronize()
+    assert torch.equal(before, g1.master_flat)
     capi.fsdp_group_set_destroy(gset)
     # g3's m shards are g1's master: one launch would race on them
     g3 = ShardedGroup([(64, 8), (9,)], n, r)
