@@ -2,9 +2,9 @@
 
 Each case draws a ragged group (1-6 parameters, 0-400 rows, 1-70 columns, some
 1-D), a world size of 1-13 (16-64 for every fourth case), a rank, the
-alignment option and element offsets of the [N, S] buffers, so layouts the
-fixed cases do not name (misaligned rows at every offset, partial row
-batches, empty chunks, tiny runs) are covered.
+alignment option and element offsets of the [N, S] buffers and of a group
+set's copy-in arena, so layouts the fixed cases do not name (misaligned rows
+at every offset, partial row batches, empty chunks, tiny runs) are covered.
 Bit-exact bars as in the fixed-case tests.
 """
 import numpy as np
@@ -106,6 +106,25 @@ def test_random_group_every_kernel(seed):
             _bits_equal(_f32(g.shard_view(g.m_flat, i)), host_m[i], ("m", seed, i, t))
             _bits_equal(_f32(g.shard_view(g.v_flat, i)), host_v[i], ("v", seed, i, t))
         assert np.array_equal(_u16(ag[r * S:(r + 1) * S]), O.pack(plan, host_p)), ("pack", seed, t)
+
+    # the optimizer step fused with the copy-in over a group set of this
+    # group (gradient: the last step's, still bound), into an arena at an
+    # element offset of its own
+    gset = capi.fsdp_group_set_create([g.plan])
+    total = capi.fsdp_group_set_info(gset)[1]
+    arena_buf = torch.full((total + 16,), 0x5A5A, dtype=torch.int16, device=DEV)
+    arena = arena_buf[o_b:o_b + total]
+    capi.fsdp_adamw_pack_groups(gset, arena, step=3, **HP)
+    torch.cuda.synchronize()
+    for i in range(len(shapes)):
+        O.adamw(host_p[i], grads[i], host_m[i], host_v[i], 3, **HP)
+        _bits_equal(_f32(g.shard_view(g.master_flat, i)), host_p[i], ("set master", seed, i))
+        _bits_equal(_f32(g.shard_view(g.m_flat, i)), host_m[i], ("set m", seed, i))
+        _bits_equal(_f32(g.shard_view(g.v_flat, i)), host_v[i], ("set v", seed, i))
+    assert np.array_equal(_u16(arena)[:S], O.pack(plan, host_p)), ("set pack", seed)
+    assert (_u16(arena_buf)[:o_b] == 0x5A5A).all() and (_u16(arena)[S:] == 0x5A5A).all()
+    assert (_u16(arena_buf)[o_b + total:] == 0x5A5A).all()
+    capi.fsdp_group_set_destroy(gset)
 
     # copy-out of a random [N, S] buffer (padding holds sentinels)
     rng = np.random.default_rng(synth.seed_for("rg-ag", seed) % (2**32))
