@@ -22,9 +22,10 @@ same workload.  The same record for each workload named by --also (the
 
 By default reduce, AdamW and pack run as one fused launch per group
 (fsdp_step_shard, bit-identical to the three calls); --unfused runs them as
-three launches per group, and --group-set as separate kernels through a group
-set: a reduce per group, then one AdamW and one copy-in launch over every
-group.
+three launches per group, --group-set as separate kernels through a group
+set (a reduce per group, then one AdamW and one copy-in launch over every
+group), and --group-set-fused as a group set with AdamW and the copy-in fused
+in one launch.
 """
 from __future__ import annotations
 
@@ -65,7 +66,7 @@ def algorithmic_bytes(S, V, F, N, fused, adamw_copy_in=False):
 KERNEL_SYMBOLS = {"step": ("step_kernel_wide", "step_kernel_aligned", "step_kernel"),
                   "reduce": ("reduce_kernel",),
                   "adamw": ("adamw_kernel",), "pack": ("pack_kernel",),
-                  "unpack": ("unpack_kernel",)}
+                  "unpack": ("unpack_kernel",), "adamw_pack": ("adamw_pack_kernel",)}
 
 
 def measured_traffic(workload, rank, align, kind):
@@ -84,7 +85,7 @@ def measured_traffic(workload, rank, align, kind):
     wl = rec.get("workloads", {}).get(workload)
     if not wl or wl.get("rank") != rank or wl.get("align_elems") != align:
         return None
-    for sym in KERNEL_SYMBOLS[kind]:
+    for sym in KERNEL_SYMBOLS.get(kind, ()):
         k = wl.get("kernels", {}).get(sym)
         if k is not None:
             return k["traffic_bytes_per_launch"]

@@ -74,3 +74,16 @@ def test_bad_also_is_rejected(args):
     r = _run(*args)
     assert r.returncode == 2
     assert "--also" in r.stderr
+
+
+def test_traffic_lookup_covers_every_kernel_kind():
+    """Every kernel kind the bench can time has a traffic lookup (a number
+    from the committed counters or None), for every path."""
+    kinds = set()
+    for fused, aci in ((True, False), (False, False), (False, True)):
+        kinds |= set(bench.algorithmic_bytes(8, 8, 8, 2, fused, aci))
+    for cfg in (configs.get(2), configs.get(4)):
+        for k in sorted(kinds):
+            got = bench.measured_traffic(cfg.name, cfg.timing_rank, 1, k)
+            assert got is None or got > 0, (cfg.name, k, got)
+            assert k in bench.KERNEL_NAMES
