@@ -137,6 +137,9 @@ def parse():
                          "resharding kernel)")
     ap.add_argument("--no-next", action="store_true",
                     help="skip timing the reduce-scatter copy-in and fp32-contribution kernels")
+    ap.add_argument("--no-next-group-set", action="store_true",
+                    help="skip timing the FP8 copy-in of every group in one launch (a kernel "
+                         "trace would merge it with the per-group launches)")
     ap.add_argument("--no-references", action="store_true",
                     help="skip timing the AdamW and copy-in kernels beside torch's kernels of "
                          "the same access pattern")
@@ -240,11 +243,14 @@ def cpu_baseline(cfg, rank, min_s=10.0, max_s=30.0):
     return out
 
 
-def measure_next(groups, n, rs_bf16, full_arena, stream, reps):
+def measure_next(groups, n, rs_bf16, full_arena, stream, reps, with_set=True):
     """Per-kernel rates of the kernels beyond the step, on the same groups:
-    the reduce-scatter copy-in (full bf16 grads -> [N, S] bf16, and widened
-    to fp32) and the reduction of fp32 contributions.  The full-parameter
-    arena stands in for the unsharded gradients."""
+    the reduce-scatter copy-ins (full bf16 grads -> [N, S] bf16, widened to
+    fp32, and from fp32 accumulators), the reduction of fp32 contributions,
+    accumulation, the FP8 copy-in (per group, and of every group in one
+    launch through a group set) and copy-out, and resharding of the first
+    group.  The full-parameter arena stands in for the unsharded
+    gradients."""
     import torch
     from sharded_shard_amd import capi
 
@@ -290,6 +296,20 @@ def measure_next(groups, n, rs_bf16, full_arena, stream, reps):
     kinds[f"reshard_f32_{n}_to_{n2}_first_group"] = (
         lambda g: capi.fsdp_reshard_execute(rplan, stream) if g is g0 else None,
         lambda g: 8 * dst_numel if g is g0 else 0)
+    # the FP8 copy-in of every group as one launch through a group set (a
+    # kernel trace would merge it with the per-group launches of the same
+    # kernel: profiled runs leave it out)
+    gset = capi.fsdp_group_set_create([g.plan for g in groups], stream) if with_set else None
+    set_scales = set_arena8 = None
+    if with_set:
+        _, n_params, set_elems = capi.fsdp_group_set_sizes(gset)
+        set_scales = torch.full((max(1, n_params),), 448.0 / 0.1, dtype=torch.float32,
+                                device=full_arena.device)
+        set_arena8 = torch.empty(max(1, set_elems), dtype=torch.uint8, device=full_arena.device)
+        kinds["fp8_copy_in_group_set"] = (
+            lambda g: capi.fsdp_pack_allgather_fp8_groups(gset, set_arena8, set_scales, stream)
+            if g is g0 else None,
+            lambda g: sum(4 * x.V + x.S for x in groups) if g is g0 else 0)
     res = {}
     for name, (fn, nbytes) in kinds.items():
         busy = [g for g in groups if nbytes(g) > 0]
@@ -309,7 +329,9 @@ def measure_next(groups, n, rs_bf16, full_arena, stream, reps):
         res[name] = {"ms_per_step": round(ms, 4), "algorithmic_GB_per_step": round(byts / 1e9, 4),
                      "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
     capi.fsdp_reshard_plan_destroy(rplan)
-    del rs_f32, dst, acc_arena, fp8_scales
+    if gset is not None:
+        capi.fsdp_group_set_destroy(gset)
+    del rs_f32, dst, acc_arena, fp8_scales, set_scales, set_arena8
     res["adamw_host_cpu_offload"] = measure_host_adamw()
     return res
 
@@ -770,7 +792,8 @@ def run_workload(cfg_index, args, dev, copy_gbps):
             "hbm_frac": (step_bytes + byts["unpack"]) / (t2 * 1e-3) / 1e9 / HBM_PEAK_GBPS}
     if not args.no_next:
         rec["next_kernels"] = measure_next(groups, n, rs_arena[0], full_arena, stream,
-                                           max(1, args.breakdown_steps))
+                                           max(1, args.breakdown_steps),
+                                           with_set=not args.no_next_group_set)
     if gset is not None:
         capi.fsdp_group_set_destroy(gset)
     for g in groups:

@@ -12,8 +12,9 @@
  *   fused     fsdp_step_shard        reduce -> AdamW -> copy-in in one pass
  *   executor  fsdp_step_groups       a whole step over many groups, one call
  *   sets      fsdp_adamw_groups, fsdp_pack_allgather_groups,
- *             fsdp_adamw_pack_groups, fsdp_step_group_set
- *             AdamW and copy-in of many groups, one launch each or fused
+ *             fsdp_adamw_pack_groups, fsdp_amax_groups,
+ *             fsdp_pack_allgather_fp8_groups, fsdp_step_group_set
+ *             AdamW, amax and copy-ins of many groups, one launch each
  *
  * and around them: the reduce-scatter copy-in (fsdp_pack_reduce_scatter),
  * fp32 contributions (fsdp_reduce_shard_f32), the FP8 E4M3 all-gather
@@ -437,10 +438,11 @@ fsdp_status fsdp_group_set_create(fsdp_plan *const *plans, int32_t n_groups,
 /* Waits for the device and frees the set's tables; NULL is ignored. */
 void fsdp_group_set_destroy(fsdp_group_set *set);
 
-/* The number of groups of the set and the elements of its copy-in arena.
- * Errors: FSDP_E_INVAL (null argument). */
+/* The number of groups and of parameters of the set (its parameters are
+ * numbered group by group, in each group's registration order) and the
+ * elements of its copy-in arena.  Errors: FSDP_E_INVAL (null argument). */
 fsdp_status fsdp_group_set_info(const fsdp_group_set *set, int32_t *n_groups,
-                                int64_t *arena_elems);
+                                int32_t *n_params, int64_t *arena_elems);
 
 /* Group g's copy-in segment: elements [*offset, *offset + S_g) of the arena,
  * which holds *arena_elems elements in all.  Errors: FSDP_E_INVAL. */
@@ -478,6 +480,24 @@ fsdp_status fsdp_pack_allgather_groups(const fsdp_group_set *set, uint16_t *aren
 fsdp_status fsdp_adamw_pack_groups(const fsdp_group_set *set,
                                    const fsdp_adamw_hparams_t *hp, int64_t step,
                                    uint16_t *arena, void *stream);
+
+/* fsdp_amax_shard of every group in one launch: amax[k] = the largest |x|
+ * of the set's parameter k (numbered as by fsdp_group_set_info) over this
+ * rank's master shard, NaN if it holds one, 0 if it is empty; amax holds
+ * n_params floats.  [AF] FP8 item (tensor-wise scales from the amax).
+ * Needs FSDP_ROLE_MASTER.  Errors: FSDP_E_INVAL (null set or amax),
+ * FSDP_E_ALIGN, FSDP_E_STATE, FSDP_E_HIP. */
+fsdp_status fsdp_amax_groups(const fsdp_group_set *set, float *amax, void *stream);
+
+/* fsdp_pack_allgather_fp8 of every group in one launch: group g's FP8 E4M3
+ * segment (S_g bytes) at byte offset fsdp_group_set_segment's offset of
+ * `arena`, scaled by scales[k] for the set's parameter k.  Each segment
+ * equals the per-group FP8 copy-in.  The arena may not share a byte with a
+ * bound shard tensor.  [AF] FP8 item; [ST] "Mixed precision".  Needs
+ * FSDP_ROLE_MASTER.  Errors: FSDP_E_INVAL (null set, arena or scales; arena
+ * overlapping a shard), FSDP_E_ALIGN, FSDP_E_STATE, FSDP_E_HIP. */
+fsdp_status fsdp_pack_allgather_fp8_groups(const fsdp_group_set *set, uint8_t *arena,
+                                           const float *scales, void *stream);
 
 /* Flags of fsdp_step_group_set: AdamW and copy-in as one fused launch
  * (fsdp_adamw_pack_groups) instead of two. */

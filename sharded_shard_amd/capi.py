@@ -133,7 +133,10 @@ _SIGS = {
                                 ctypes.c_uint32, _i32, _PP, _P]),
     "fsdp_group_set_create": (_i32, [_PP, _i32, _P, ctypes.POINTER(_P)]),
     "fsdp_group_set_destroy": (None, [_P]),
-    "fsdp_group_set_info": (_i32, [_P, ctypes.POINTER(_i32), ctypes.POINTER(_i64)]),
+    "fsdp_group_set_info": (_i32, [_P, ctypes.POINTER(_i32), ctypes.POINTER(_i32),
+                                   ctypes.POINTER(_i64)]),
+    "fsdp_amax_groups": (_i32, [_P, _P, _P]),
+    "fsdp_pack_allgather_fp8_groups": (_i32, [_P, _P, _P, _P]),
     "fsdp_group_set_segment": (_i32, [_P, _i32, ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
     "fsdp_adamw_groups": (_i32, [_P, ctypes.POINTER(AdamwHparams), _i64, _P]),
     "fsdp_pack_allgather_groups": (_i32, [_P, _P, _P]),
@@ -507,10 +510,16 @@ def fsdp_group_set_destroy(gset) -> None:
 
 def fsdp_group_set_info(gset):
     """(n_groups, arena_elems) of a group set."""
-    n, tot = _i32(), _i64()
-    _check(lib.fsdp_group_set_info(gset, ctypes.byref(n), ctypes.byref(tot)),
+    n, tot = fsdp_group_set_sizes(gset)[::2]
+    return n, tot
+
+
+def fsdp_group_set_sizes(gset):
+    """(n_groups, n_params, arena_elems) of a group set."""
+    n, np_, tot = _i32(), _i32(), _i64()
+    _check(lib.fsdp_group_set_info(gset, ctypes.byref(n), ctypes.byref(np_), ctypes.byref(tot)),
            "fsdp_group_set_info")
-    return n.value, tot.value
+    return n.value, np_.value, tot.value
 
 
 def fsdp_group_set_segment(gset, g: int):
@@ -549,6 +558,27 @@ def fsdp_adamw_pack_groups(gset, arena, lr: float, beta1: float, beta2: float, e
     hp = AdamwHparams(lr, beta1, beta2, eps, weight_decay)
     _check(lib.fsdp_adamw_pack_groups(gset, ctypes.byref(hp), step, a, stream_handle(stream)),
            "fsdp_adamw_pack_groups")
+
+
+def fsdp_amax_groups(gset, amax, stream=None) -> None:
+    """amax: n_params fp32 (the set's parameters in group order)."""
+    if gset is None or getattr(gset, "value", 1) is None:
+        a = addr(amax)
+    else:
+        a = _dev(amax, 4 * fsdp_group_set_sizes(gset)[1], "amax")
+    _check(lib.fsdp_amax_groups(gset, a, stream_handle(stream)), "fsdp_amax_groups")
+
+
+def fsdp_pack_allgather_fp8_groups(gset, arena, scales, stream=None) -> None:
+    """arena: one byte per element of the set's arena; scales: n_params fp32."""
+    if gset is None or getattr(gset, "value", 1) is None:
+        a, sc = addr(arena), addr(scales)
+    else:
+        _, np_, tot = fsdp_group_set_sizes(gset)
+        a = _dev(arena, tot, "arena")
+        sc = _dev(scales, 4 * np_, "scales")
+    _check(lib.fsdp_pack_allgather_fp8_groups(gset, a, sc, stream_handle(stream)),
+           "fsdp_pack_allgather_fp8_groups")
 
 
 class StepGroupSetCall:

@@ -896,14 +896,15 @@ hipError_t do_adamw_pack_set(const fsdp_group_set *set, const float scal[8], uin
 
 // The copy-in arena is written in the same launch that reads (and, fused,
 // writes) the shards: it must not share a byte with any of them.
-fsdp_status check_arena(const fsdp_group_set *set, const uint16_t *arena, const char *call) {
+fsdp_status check_arena(const fsdp_group_set *set, const void *arena, const char *call,
+                        uintptr_t elem_bytes = 2) {
     const int64_t elems = set->seg_off.back();
     if (arena == nullptr && elems > 0)
         return fail(FSDP_E_INVAL, std::string(call) + ": null arena");
-    if (misaligned(arena, 2))
-        return fail(FSDP_E_ALIGN, std::string(call) + ": arena not 2-byte aligned");
+    if (misaligned(arena, elem_bytes))
+        return fail(FSDP_E_ALIGN, std::string(call) + ": arena misaligned for its element type");
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(arena);
-    const uintptr_t a1 = a0 + static_cast<uintptr_t>(elems) * 2;
+    const uintptr_t a1 = a0 + static_cast<uintptr_t>(elems) * elem_bytes;
     // the first merged span ending after a0 is the only one that can overlap
     auto it = std::upper_bound(set->shard_bytes.begin(), set->shard_bytes.end(), a0,
                                [](uintptr_t v, const std::pair<uintptr_t, uintptr_t> &sp) {
@@ -1033,10 +1034,11 @@ void fsdp_group_set_destroy(fsdp_group_set *set) {
 }
 
 fsdp_status fsdp_group_set_info(const fsdp_group_set *set, int32_t *n_groups,
-                                int64_t *arena_elems) {
-    if (set == nullptr || n_groups == nullptr || arena_elems == nullptr)
+                                int32_t *n_params, int64_t *arena_elems) {
+    if (set == nullptr || n_groups == nullptr || n_params == nullptr || arena_elems == nullptr)
         return fail(FSDP_E_INVAL, "fsdp_group_set_info: null argument");
     *n_groups = static_cast<int32_t>(set->plans.size());
+    *n_params = static_cast<int32_t>(set->ent_off.back());
     *arena_elems = set->seg_off.back();
     return FSDP_OK;
 }
@@ -1083,6 +1085,38 @@ fsdp_status fsdp_adamw_pack_groups(const fsdp_group_set *set, const fsdp_adamw_h
     adamw_scalars(hp, step, scal);
     return launched(do_adamw_pack_set(set, scal, arena, static_cast<hipStream_t>(stream)),
                     "fsdp_adamw_pack_groups: launch");
+}
+
+fsdp_status fsdp_amax_groups(const fsdp_group_set *set, float *amax, void *stream) {
+    const char *call = "fsdp_amax_groups";
+    fsdp_status s = check_set(set, FSDP_ROLE_MASTER, call);
+    if (s != FSDP_OK) return s;
+    const int64_t np = set->ent_off.back();
+    if (amax == nullptr && np > 0) return fail(FSDP_E_INVAL, "fsdp_amax_groups: null amax");
+    if (misaligned(amax, 4)) return fail(FSDP_E_ALIGN, "fsdp_amax_groups: amax not 4-byte aligned");
+    return launched(guarded([&] {
+                        return fsdp::launch_amax(set->d_adamw, set->n_adamw, set->d_entries, amax,
+                                                 static_cast<int32_t>(np),
+                                                 static_cast<hipStream_t>(stream));
+                    }),
+                    "fsdp_amax_groups: launch");
+}
+
+fsdp_status fsdp_pack_allgather_fp8_groups(const fsdp_group_set *set, uint8_t *arena,
+                                           const float *scales, void *stream) {
+    const char *call = "fsdp_pack_allgather_fp8_groups";
+    fsdp_status s = check_set(set, FSDP_ROLE_MASTER, call);
+    if (s != FSDP_OK || (s = check_arena(set, arena, call, 1)) != FSDP_OK) return s;
+    if (scales == nullptr && set->ent_off.back() > 0)
+        return fail(FSDP_E_INVAL, "fsdp_pack_allgather_fp8_groups: null scales");
+    if (misaligned(scales, 4))
+        return fail(FSDP_E_ALIGN, "fsdp_pack_allgather_fp8_groups: scales not 4-byte aligned");
+    return launched(guarded([&] {
+                        return fsdp::launch_pack_fp8(set->d_pack, set->n_pack, set->d_entries,
+                                                     arena, scales,
+                                                     static_cast<hipStream_t>(stream));
+                    }),
+                    "fsdp_pack_allgather_fp8_groups: launch");
 }
 
 fsdp_status fsdp_step_group_set(const fsdp_group_set *set, const uint16_t *const *rs_in,

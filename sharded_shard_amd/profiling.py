@@ -155,14 +155,14 @@ def _trace_cmd(tag, args):
             f"-d $REPO/gpurun_out/prof2/{tag}_trace -o {tag} -- python3 $REPO/bench.py {args} "
             "--also none --steps 10 --warmup 2 --breakdown-steps 0 --no-isolated "
             "--no-copy-ceiling --no-cpu-baseline" + (" --no-next" if tag in SEPARATE else "") +
-            " --no-references")
+            " --no-references --no-next-group-set")
 
 
 def _pmc_cmd(tag, args, counters_):
     return ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc " + " ".join(counters_) +
             f" -T -f csv -d $REPO/gpurun_out/prof2/{tag}_<run> -o {tag} -- python3 $REPO/bench.py "
             f"{args} --also none --steps 1 --warmup 1 --breakdown-steps 0 --no-isolated "
-            "--no-copy-ceiling --no-cpu-baseline --no-references")
+            "--no-copy-ceiling --no-cpu-baseline --no-references --no-next-group-set")
 
 
 RD_COUNTERS = ["TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum",

@@ -187,7 +187,10 @@ hipError_t launch_amax(const EwTile *tiles, int64_t n, const DevEntry *ents, flo
                        int32_t n_params, hipStream_t) {
     ++harness::launches;
     wrote(amax, 0, n_params, harness::kSmall);
-    for (int64_t i = 0; i < n; ++i) touch(ents[tiles[i].entry].master, tiles[i].off, tiles[i].len);
+    for (int64_t i = 0; i < n; ++i) {
+        touch(amax, tiles[i].entry, 1);
+        touch(ents[tiles[i].entry].master, tiles[i].off, tiles[i].len);
+    }
     return hipSuccess;
 }
 

@@ -279,23 +279,25 @@ void group_sets(const Workload &w, Instance &a, Instance &b) {
           "%s: segments at %lld, %lld of %lld", w.name.c_str(), (long long)off[0],
           (long long)off[1], (long long)total);
     CHECK_STATUS(fsdp_group_set_segment(set, 2, &off[0], &total), FSDP_E_INVAL);
-    int32_t n_groups = 0;
+    int32_t n_groups = 0, n_params = 0;
     int64_t t2 = 0;
-    CHECK_STATUS(fsdp_group_set_info(set, &n_groups, &t2), FSDP_OK);
-    CHECK(n_groups == 2 && t2 == total, "%s: info %d groups, %lld elements", w.name.c_str(),
-          n_groups, (long long)t2);
-    CHECK_STATUS(fsdp_group_set_info(set, nullptr, &t2), FSDP_E_INVAL);
+    CHECK_STATUS(fsdp_group_set_info(set, &n_groups, &n_params, &t2), FSDP_OK);
+    CHECK(n_groups == 2 && t2 == total && n_params == int32_t(a.ents.size() + b.ents.size()),
+          "%s: info %d groups, %d params, %lld elements", w.name.c_str(), n_groups, n_params,
+          (long long)t2);
+    CHECK_STATUS(fsdp_group_set_info(set, nullptr, &n_params, &t2), FSDP_E_INVAL);
     uint16_t *arena = alloc<uint16_t>(total);
 
     harness::spans.clear();
     CHECK_STATUS(fsdp_adamw_groups(set, &kHp, 1, nullptr), FSDP_OK);
     for (Instance *in : {&a, &b}) check_shards(*in, in->master, "set AdamW", w.name);
 
-    auto check_arena = [&](const char *what) {
+    auto check_arena = [&](const char *what, const void *base = nullptr) {
+        if (base == nullptr) base = arena;
         std::vector<uint8_t> hits(static_cast<size_t>(total), 0);
         int64_t outside = 0, bad = 0;
         for (const harness::Span &sp : harness::spans) {
-            if (sp.base != arena || sp.kind != harness::kSegment) continue;
+            if (sp.base != base || sp.kind != harness::kSegment) continue;
             if (sp.off < 0 || sp.off + sp.len > total) {
                 ++outside;
                 continue;
@@ -314,6 +316,27 @@ void group_sets(const Workload &w, Instance &a, Instance &b) {
     harness::spans.clear();
     CHECK_STATUS(fsdp_pack_allgather_groups(set, arena, nullptr), FSDP_OK);
     check_arena("set copy-in");
+
+    // FP8: amax of every parameter and the FP8 copy-in of every group, one
+    // launch each (amax: a clear and a launch)
+    uint8_t *arena8 = alloc<uint8_t>(total);
+    float *amax = alloc<float>(n_params), *scales = alloc<float>(n_params);
+    harness::spans.clear();
+    long l8 = harness::launches;
+    CHECK_STATUS(fsdp_amax_groups(set, amax, nullptr), FSDP_OK);
+    if (n_params > 0) check_cover(amax, n_params, harness::kSmall, "set amax", w.name);
+    CHECK_STATUS(fsdp_pack_allgather_fp8_groups(set, arena8, scales, nullptr), FSDP_OK);
+    CHECK(harness::launches == l8 + 2 || n_params == 0, "%s: %ld FP8 set launches",
+          w.name.c_str(), harness::launches - l8);
+    check_arena("set FP8 copy-in", arena8);
+    if (n_params > 0) {
+        CHECK_STATUS(fsdp_amax_groups(set, nullptr, nullptr), FSDP_E_INVAL);
+        CHECK_STATUS(fsdp_pack_allgather_fp8_groups(set, arena8, nullptr, nullptr), FSDP_E_INVAL);
+        CHECK_STATUS(fsdp_amax_groups(set, reinterpret_cast<float *>(
+                                                reinterpret_cast<char *>(amax) + 2),
+                                      nullptr),
+                     FSDP_E_ALIGN);
+    }
 
     const uint16_t *rs[2] = {a.rs, b.rs};
     const uint16_t *ag_out[2] = {a.ag, b.ag};

@@ -225,6 +225,9 @@ def test_group_set_rejects_bad_arguments_without_gpu():
                                             0, 0, None, None) == capi.FSDP_E_INVAL
         assert capi.lib.fsdp_adamw_pack_groups(None, capi.ctypes.byref(hp), 1, 0x1000,
                                                None) == capi.FSDP_E_INVAL
+        assert capi.lib.fsdp_amax_groups(None, 0x1000, None) == capi.FSDP_E_INVAL
+        assert capi.lib.fsdp_pack_allgather_fp8_groups(None, 0x1000, 0x2000,
+                                                       None) == capi.FSDP_E_INVAL
         for call in (lambda: capi.fsdp_group_set_segment(None, 0),
                      lambda: capi.fsdp_group_set_info(None)):
             with pytest.raises(capi.FsdpError) as ei:

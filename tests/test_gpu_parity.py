@@ -923,6 +923,68 @@ def test_group_set_equals_per_group_unfused_step_and_oracle(kind, fuse):
         g.close()
 
 
+@pytest.mark.parametrize("kind", ["n6", "n64", "many"])
+def test_group_set_fp8_equals_per_group_and_oracle(kind):
+    """fsdp_amax_groups and fsdp_pack_allgather_fp8_groups (one launch each
+    over every group) against the per-group calls, bit for bit, and against
+    the oracle; special values (NaN, infinities, huge and subnormal masters)
+    in the first group, an FP8 arena at an odd byte offset."""
+    group_shapes, n, r = _set_groups(kind)
+    groups, plans, masters = [], [], []
+    rng = np.random.default_rng(synth.seed_for("set-fp8", kind) % (2**32))
+    for gi, shapes in enumerate(group_shapes):
+        g = ShardedGroup(shapes, n, r)
+        _fill_masters(g, ("set-fp8", kind, gi))
+        if gi == 0:
+            for i, e in enumerate(g.entries):
+                if e.valid_numel >= len(_F32_SPECIALS) and i % 2 == 0:
+                    x = f32(g.shard_view(g.master_flat, i))
+                    pos = rng.choice(x.size, size=len(_F32_SPECIALS), replace=False)
+                    x[pos] = np.array(_F32_SPECIALS, dtype=np.float32)
+                    g.shard_view(g.master_flat, i).copy_(torch.from_numpy(x))
+        groups.append(g)
+        plans.append(O.plan(shapes, n, r))
+        masters.append([f32(g.shard_view(g.master_flat, i)) for i in range(len(shapes))])
+    gset = capi.fsdp_group_set_create([g.plan for g in groups])
+    n_groups, n_params, total = capi.fsdp_group_set_sizes(gset)
+    assert n_groups == len(groups) and n_params == sum(len(s) for s in group_shapes)
+    amax = torch.full((max(1, n_params),), -1.0, dtype=torch.float32, device=DEV)
+    capi.fsdp_amax_groups(gset, amax)
+    per = []
+    for g in groups:
+        a = torch.full((max(1, len(g.shapes)),), -1.0, dtype=torch.float32, device=DEV)
+        g.amax(a)
+        per.append(a[:len(g.shapes)])
+    torch.cuda.synchronize()
+    per_cat = torch.cat(per) if n_params else amax[:0]
+    assert torch.equal(amax[:n_params].view(torch.int32), per_cat.view(torch.int32))
+    want_amax = np.concatenate([O.amax(ms) for ms in masters])
+    _same_f32_nan_ok(f32(amax[:n_params]), want_amax, "amax")
+    a_h = want_amax.astype(np.float64)
+    scales_h = np.where(np.isfinite(a_h) & (a_h > 0), 448.0 / np.where(a_h > 0, a_h, 1.0),
+                        1.0).astype(np.float32)
+    scales = torch.from_numpy(scales_h).to(DEV) if n_params else torch.ones(1, device=DEV)
+    buf = torch.full((total + 16,), 0x5A, dtype=torch.uint8, device=DEV)
+    arena = buf[3:3 + total]
+    capi.fsdp_pack_allgather_fp8_groups(gset, arena, scales)
+    k = 0
+    for gi, (g, plan) in enumerate(zip(groups, plans)):
+        seg = torch.zeros(max(1, g.S), dtype=torch.uint8, device=DEV)
+        np_g = len(g.shapes)
+        g.pack_fp8(seg[:g.S], scales[k:k + np_g] if np_g else scales)
+        torch.cuda.synchronize()
+        o = capi.fsdp_group_set_segment(gset, gi)[0]
+        assert torch.equal(arena[o:o + g.S], seg[:g.S]), ("segment", gi)
+        want = O.pack_fp8(plan, masters[gi], [float(x) for x in scales_h[k:k + np_g]])
+        assert np.array_equal(arena[o:o + g.S].cpu().numpy(), want), ("oracle", gi)
+        k += np_g
+    h = buf.cpu().numpy()
+    assert (h[:3] == 0x5A).all() and (h[3 + total:] == 0x5A).all()
+    capi.fsdp_group_set_destroy(gset)
+    for g in groups:
+        g.close()
+
+
 def test_group_set_refuses_rebound_groups_and_overlapping_shards():
     n, r = 4, 1
     g1 = ShardedGroup([(64, 8), (9,)], n, r)
