@@ -278,7 +278,54 @@ def summarize(prof, out_dir, sha):
     files.append(path)
     if glob.glob(f"{prof}/cal_LAT"):
         files.append(memory_pressure(prof, out_dir, sha))
+    if glob.glob(f"{prof}/default_trace"):
+        files.append(default_run(prof, out_dir, sha))
     return files
+
+
+def default_run(prof, out_dir, sha):
+    """The bench's default command under a kernel trace: every kernel's
+    average duration, and the headline roofline kernel's trace average beside
+    the average the same run's HIP events gave (its JSON line is the last
+    line of the run's stdout)."""
+    stats = kernel_stats(prof, "default")
+    rec = None
+    for line in reversed(open(f"{prof}/default_trace.log").read().splitlines()):
+        if line.startswith("{"):
+            rec = json.loads(line)
+            break
+    lines = ["# The bench's default command under a kernel trace", "",
+             "REPO is the repository root on the GPU box.", "", "```",
+             "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -T -f csv -d "
+             "$REPO/gpurun_out/prof2/default_trace -o default -- python3 $REPO/bench.py", "```",
+             "", "Both workloads of the default line (the 7B shape, then the 70B shape under "
+             "\"also\"), with their per-kernel event steps, isolated launches, next-row "
+             "kernels and pattern references; kernels of the same name from the two workloads "
+             "share a row.", "",
+             "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for name, st in sorted(stats.items(), key=lambda kv: -kv[1]["total_us"]):
+        lines.append(f"| {name} | {st['calls']} | {st['avg_us']:.1f} | {st['min_us']:.1f} | "
+                     f"{st['max_us']:.1f} |")
+    if rec is not None:
+        roof = rec["roofline"]
+        # the headline's dominant kernel on aligned rows at 8 ranks
+        trace = stats.get("step_kernel_aligned", {}).get("avg_us")
+        lines += ["", "## Headline roofline kernel: events against the trace", "",
+                  f"Workload: {rec['config']['workload']}; the line's roofline kernel: "
+                  f"{roof['kernel']}.", "",
+                  "| source | average launch (us) |", "|---|---|",
+                  f"| HIP events in the timed steps (roofline.avg_launch_ms) | "
+                  f"{1e3 * roof['avg_launch_ms']:.1f} |"]
+        if trace is not None:
+            lines.append(f"| rocprofv3, step_kernel_aligned, every launch of the run | "
+                         f"{trace:.1f} |")
+        lines += ["", f"The same run's line: {rec['ms_per_step']:.3f} ms per step, hbm_frac "
+                  f"{rec['hbm_frac']:.4f}, roofline.frac {roof['frac']:.4f} (under the "
+                  "profiler)."]
+    lines += ["", f"Kernel sources sha256 when measured: `{sha}`", ""]
+    path = os.path.join(out_dir, "bench_default_trace.md")
+    open(path, "w").write("\n".join(lines))
+    return path
 
 
 LAT_COUNTERS = ["TCC_EA0_RDREQ_LEVEL_sum", "TCC_EA0_RDREQ_sum", "TCC_EA0_WRREQ_LEVEL_sum",
