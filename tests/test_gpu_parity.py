@@ -1018,6 +1018,73 @@ def test_group_set_refuses_rebound_groups_and_overlapping_shards():
         g.close()
 
 
+@pytest.mark.parametrize("path", ["fused", "unfused", "set"])
+def test_step_captured_in_a_graph_replays_like_eager_calls(path):
+    """Hot calls only enqueue kernels (no allocation, no synchronization, no
+    memset), so a whole multi-group step can be captured in a HIP graph.
+    Three replays, with eager work and synchronizations between them, match
+    three eager calls of the same step on a twin state, bit for bit, every
+    replay."""
+    n, r = 6, 5
+    group_shapes = [CASES[1][1], [(70001,), (300, 33)], [(64, 8)]]
+    A, B, rs_bufs, ag_a, ag_b = [], [], [], [], []
+    for gi, shapes in enumerate(group_shapes):
+        ga, gb = ShardedGroup(shapes, n, r), ShardedGroup(shapes, n, r)
+        _fill_masters(ga, ("graph", gi))
+        gb.master_flat.copy_(ga.master_flat)
+        plan = O.plan(shapes, n, r)
+        rs_bufs.append(torch.from_numpy(_rs_input(plan, n, ("graph-rs", gi)).reshape(-1)
+                                        .view(np.int16)).to(DEV))
+        other = torch.from_numpy(_rand_ag(n, plan.S, ("graph-ag", gi)).reshape(-1)
+                                 .view(np.int16)).to(DEV)
+        ag_a.append(other.clone())
+        ag_b.append(other.clone())
+        A.append(ga)
+        B.append(gb)
+
+    def make(groups, ags, stream):
+        if path == "set":
+            gset = capi.fsdp_group_set_create([g.plan for g in groups])
+            arena = torch.zeros(capi.fsdp_group_set_info(gset)[1], dtype=torch.int16, device=DEV)
+            call = capi.StepGroupSetCall(gset, [g.plan for g in groups], rs_bufs, arena, ags,
+                                         flags=capi.FSDP_SET_ADAMW_COPY_IN, stream=stream, **HP)
+            return call, (gset, arena)
+        ins = [a[r * g.S:(r + 1) * g.S] for a, g in zip(ags, groups)]
+        flags = capi.FSDP_STEP_UNFUSED if path == "unfused" else capi.FSDP_STEP_WRITE_GRAD
+        return capi.StepGroupsCall([g.plan for g in groups], rs_bufs, ins, ags, flags=flags,
+                                   stream=stream, **HP), None
+
+    eager, keep_a = make(A, ag_a, torch.cuda.current_stream())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        captured, keep_b = make(B, ag_b, side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            captured(1)                 # the step index is baked into the graph
+    torch.cuda.synchronize()
+    for k in range(3):
+        eager(1)
+        graph.replay()
+        torch.cuda.synchronize()
+        for gi, (ga, gb) in enumerate(zip(A, B)):
+            for fl in ("master_flat", "grad_flat", "m_flat", "v_flat", "full_flat"):
+                x, y = getattr(ga, fl), getattr(gb, fl)
+                assert torch.equal(x.view(torch.int16), y.view(torch.int16)), (path, k, gi, fl)
+            assert torch.equal(ag_a[gi], ag_b[gi]), (path, k, gi)
+        if keep_a is not None:
+            assert torch.equal(keep_a[1], keep_b[1]), (path, k, "arena")
+        for x in (ag_a, ag_b):          # eager work between replays
+            x[0].add_(0)
+    for keep in (keep_a, keep_b):
+        if keep is not None:
+            capi.fsdp_group_set_destroy(keep[0])
+    del graph
+    for g in A + B:
+        g.close()
+
+
 def test_rejected_bind_keeps_the_previous_binding():
     """A bind that fails argument checks changes nothing: the plan stays bound
     to its previous tensors and the hot calls still produce the oracle's
