@@ -140,6 +140,8 @@ def parse():
     ap.add_argument("--no-next-group-set", action="store_true",
                     help="skip timing the FP8 copy-in of every group in one launch (a kernel "
                          "trace would merge it with the per-group launches)")
+    ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time the step captured in a HIP graph and replayed")
     ap.add_argument("--no-references", action="store_true",
                     help="skip timing the AdamW and copy-in kernels beside torch's kernels of "
                          "the same access pattern")
@@ -613,22 +615,26 @@ def run_workload(cfg_index, args, dev, copy_gbps):
     # group, one AdamW and one copy-in launch over every group (into an arena
     # of every group's segment), a copy-out per group.
     gset = arena = None
-    if not args.group_set:
-        execute = capi.StepGroupsCall(
-            [g.plan for g in groups],
-            [rs_arena[gi & 1][:n * g.S] for gi, g in enumerate(groups)],
-            [ag_arena[gi & 1][rank * g.S:(rank + 1) * g.S] for gi, g in enumerate(groups)],
-            [ag_arena[gi & 1][:n * g.S] for gi, g in enumerate(groups)],
-            flags=0 if fused else capi.FSDP_STEP_UNFUSED, stream=stream, **hp)
-    else:
+    if args.group_set:
         gset = capi.fsdp_group_set_create([g.plan for g in groups], stream)
         arena = torch.empty(max(1, capi.fsdp_group_set_segment(gset, 0)[1]), dtype=torch.int16,
                             device=dev)
-        execute = capi.StepGroupSetCall(
+
+    def make_execute(on_stream):
+        if not args.group_set:
+            return capi.StepGroupsCall(
+                [g.plan for g in groups],
+                [rs_arena[gi & 1][:n * g.S] for gi, g in enumerate(groups)],
+                [ag_arena[gi & 1][rank * g.S:(rank + 1) * g.S] for gi, g in enumerate(groups)],
+                [ag_arena[gi & 1][:n * g.S] for gi, g in enumerate(groups)],
+                flags=0 if fused else capi.FSDP_STEP_UNFUSED, stream=on_stream, **hp)
+        return capi.StepGroupSetCall(
             gset, [g.plan for g in groups],
             [rs_arena[gi & 1][:n * g.S] for gi, g in enumerate(groups)], arena,
             [ag_arena[gi & 1][:n * g.S] for gi, g in enumerate(groups)],
-            flags=capi.FSDP_SET_ADAMW_COPY_IN if aci else 0, stream=stream, **hp)
+            flags=capi.FSDP_SET_ADAMW_COPY_IN if aci else 0, stream=on_stream, **hp)
+
+    execute = make_execute(stream)
     one_launch = set(SET_KINDS) if args.group_set else set()
 
     def launch_bytes(kind, gi):
@@ -710,6 +716,34 @@ def run_workload(cfg_index, args, dev, copy_gbps):
         per = {k: sum(sum(ms for _, ms in elapsed_sampled(evs)) for evs in runs[k])
                / args.breakdown_steps for k in kinds}
 
+    # the same step captured once in a HIP graph and replayed: the launches
+    # without host work between them (step index fixed in the graph; the
+    # same kernels and bytes)
+    graph_rec = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            gcall = make_execute(side)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph, stream=side):
+                gcall(step_counter[0] + 1)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            graph.replay()
+        ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ga.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        gb.record(stream)
+        gb.synchronize()
+        g_ms = ga.elapsed_time(gb) / args.steps
+        graph_rec = {"ms_per_step": g_ms, "params_per_s": V / (g_ms * 1e-3), "steps": args.steps,
+                     "note": "one step captured in a HIP graph (its step index fixed) and "
+                             "replayed; the same kernels and bytes as the timed steps"}
+        del graph, gcall
+
     def frac(gbps, ref):
         return round(gbps / ref, 4) if gbps and ref else None
 
@@ -781,6 +815,8 @@ def run_workload(cfg_index, args, dev, copy_gbps):
                                " on the step's stream, inside the timed steps"},
         "kernels": kernels,
     }
+    if graph_rec is not None:
+        rec["graph_replay"] = graph_rec
     if per.get("unpack"):
         # derived, not timed: with reshard-after-forward a step all-gathers
         # every group twice (forward and backward), so one more copy-out per

@@ -155,14 +155,14 @@ def _trace_cmd(tag, args):
             f"-d $REPO/gpurun_out/prof2/{tag}_trace -o {tag} -- python3 $REPO/bench.py {args} "
             "--also none --steps 10 --warmup 2 --breakdown-steps 0 --no-isolated "
             "--no-copy-ceiling --no-cpu-baseline" + (" --no-next" if tag in SEPARATE else "") +
-            " --no-references --no-next-group-set")
+            " --no-references --no-next-group-set --no-graph")
 
 
 def _pmc_cmd(tag, args, counters_):
     return ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc " + " ".join(counters_) +
             f" -T -f csv -d $REPO/gpurun_out/prof2/{tag}_<run> -o {tag} -- python3 $REPO/bench.py "
             f"{args} --also none --steps 1 --warmup 1 --breakdown-steps 0 --no-isolated "
-            "--no-copy-ceiling --no-cpu-baseline --no-references --no-next-group-set")
+            "--no-copy-ceiling --no-cpu-baseline --no-references --no-next-group-set --no-graph")
 
 
 RD_COUNTERS = ["TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum",
@@ -368,7 +368,7 @@ def memory_pressure(prof, out_dir, sha):
                          f" -T -f csv -d $REPO/gpurun_out/prof2/{tag}_{run} -o {tag} -- python3 "
                          f"$REPO/bench.py {args} --also none --steps 1 --warmup 1 "
                          "--breakdown-steps 0 --no-isolated --no-copy-ceiling --no-cpu-baseline "
-                         "--no-references --no-next")
+                         "--no-references --no-next --no-graph")
     lines += ["```", "",
               "Per dispatch, averaged over the kernel's dispatches: read (write) latency = "
               "TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ (WRREQ), in L2 cycles; reads in flight per "
