@@ -152,7 +152,7 @@ def calibration(prof):
 
 def _trace_cmd(tag, args):
     return ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -T -f csv "
-            f"-d $REPO/gpurun_out/prof2/{tag}_trace -o {tag} -- python3 $REPO/bench.py {args} "
+            f"-d $OUT/{tag}_trace -o {tag} -- python3 $REPO/bench.py {args} "
             "--also none --steps 10 --warmup 2 --breakdown-steps 0 --no-isolated "
             "--no-copy-ceiling --no-cpu-baseline" + (" --no-next" if tag in SEPARATE else "") +
             " --no-references --no-next-group-set --no-graph")
@@ -160,7 +160,7 @@ def _trace_cmd(tag, args):
 
 def _pmc_cmd(tag, args, counters_):
     return ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc " + " ".join(counters_) +
-            f" -T -f csv -d $REPO/gpurun_out/prof2/{tag}_<run> -o {tag} -- python3 $REPO/bench.py "
+            f" -T -f csv -d $OUT/{tag}_<run> -o {tag} -- python3 $REPO/bench.py "
             f"{args} --also none --steps 1 --warmup 1 --breakdown-steps 0 --no-isolated "
             "--no-copy-ceiling --no-cpu-baseline --no-references --no-next-group-set --no-graph")
 
@@ -183,7 +183,8 @@ def summarize(prof, out_dir, sha):
         crd, cwr = counters(prof, f"{tag}_RD"), counters(prof, f"{tag}_WR")
         args = f"--config {ci}"
         lines = [f"# Kernels of the sharded step -- {cfg.name}, rank {cfg.timing_rank}", "",
-                 "REPO is the repository root on the GPU box.", "",
+                 "REPO is the repository root and OUT the rocprofv3 output directory (the one this "
+                 "summary was written from), on the machine with the GPU.", "",
                  "## Kernel trace", "", "```", _trace_cmd(tag, args), "```", "",
                  "Timed steps plus the next-row kernels; no per-kernel event steps, no "
                  "isolated launches.", "",
@@ -255,9 +256,10 @@ def summarize(prof, out_dir, sha):
         files.append(path)
     cal_lines = [
         "# HBM byte counters: calibration on a copy of known size", "",
-        "REPO is the repository root on the GPU box.", "", "```",
+        "REPO is the repository root and OUT the rocprofv3 output directory (the one this "
+                 "summary was written from), on the machine with the GPU.", "", "```",
         "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -T -f csv -d "
-        "$REPO/gpurun_out/prof2/cal_FETCH -o cal -- python3 $REPO/bench.py --copy-calibration",
+        "$OUT/cal_FETCH -o cal -- python3 $REPO/bench.py --copy-calibration",
         "(the same with --pmc WRITE_SIZE, --pmc " + " ".join(RD_COUNTERS) + ", --pmc "
         + " ".join(WR_COUNTERS) + ")", "```", "",
         "torch's copy kernel over 2 GiB: 2,147,483,648 bytes read and written per launch.", "",
@@ -295,9 +297,10 @@ def default_run(prof, out_dir, sha):
             rec = json.loads(line)
             break
     lines = ["# The bench's default command under a kernel trace", "",
-             "REPO is the repository root on the GPU box.", "", "```",
+             "REPO is the repository root and OUT the rocprofv3 output directory (the one this "
+                 "summary was written from), on the machine with the GPU.", "", "```",
              "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -T -f csv -d "
-             "$REPO/gpurun_out/prof2/default_trace -o default -- python3 $REPO/bench.py", "```",
+             "$OUT/default_trace -o default -- python3 $REPO/bench.py", "```",
              "", "Both workloads of the default line (the 7B shape, then the 70B shape under "
              "\"also\"), with their per-kernel event steps, isolated launches, next-row "
              "kernels and pattern references; kernels of the same name from the two workloads "
@@ -358,14 +361,15 @@ def memory_pressure(prof, out_dir, sha):
             if name in lat and name in st:
                 rows.append((name, args, {**lat[name], **st[name]}))
     lines = ["# Memory-side latency and back-pressure per kernel", "",
-             "REPO is the repository root on the GPU box.", "", "```"]
+             "REPO is the repository root and OUT the rocprofv3 output directory (the one this "
+                 "summary was written from), on the machine with the GPU.", "", "```"]
     for run, cs in (("LAT", LAT_COUNTERS), ("STALL", STALL_COUNTERS)):
         lines.append("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc " + " ".join(cs) +
-                     f" -T -f csv -d $REPO/gpurun_out/prof2/cal_{run} -o cal -- python3 "
+                     f" -T -f csv -d $OUT/cal_{run} -o cal -- python3 "
                      "$REPO/bench.py --copy-calibration")
         for tag, (args, _) in PRESSURE.items():
             lines.append("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc " + " ".join(cs) +
-                         f" -T -f csv -d $REPO/gpurun_out/prof2/{tag}_{run} -o {tag} -- python3 "
+                         f" -T -f csv -d $OUT/{tag}_{run} -o {tag} -- python3 "
                          f"$REPO/bench.py {args} --also none --steps 1 --warmup 1 "
                          "--breakdown-steps 0 --no-isolated --no-copy-ceiling --no-cpu-baseline "
                          "--no-references --no-next --no-graph")
