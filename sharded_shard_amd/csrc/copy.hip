@@ -209,7 +209,16 @@ __device__ __forceinline__ void widen_run(float *__restrict__ dst, const uint16_
     if ((k & 7u) == 0) {
         const int64_t nq = (valid - head) >> 2;
         const u32x2 *sv = reinterpret_cast<const u32x2 *>(s);
-        for (int64_t q = tid; q < nq; q += kBlock) {
+        // two loads a block apart before their stores (+1-2%; the fp32 copy
+        // from the accumulators measured 5% slower that way and keeps one)
+        int64_t q = tid;
+        for (; q + kBlock < nq; q += 2 * kBlock) {
+            const u32x2 w0 = ldp<LN>(sv + q), w1 = ldp<LN>(sv + q + kBlock);
+            stp<SN>(dv + q, f32x4{bf16_lo(w0.x), bf16_hi(w0.x), bf16_lo(w0.y), bf16_hi(w0.y)});
+            stp<SN>(dv + q + kBlock,
+                    f32x4{bf16_lo(w1.x), bf16_hi(w1.x), bf16_lo(w1.y), bf16_hi(w1.y)});
+        }
+        for (; q < nq; q += kBlock) {
             const u32x2 w = ldp<LN>(sv + q);
             stp<SN>(dv + q, f32x4{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)});
         }

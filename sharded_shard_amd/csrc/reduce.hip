@@ -148,7 +148,24 @@ __device__ __forceinline__ void accumulate_run(float *__restrict__ acc, const ui
     const int64_t nvec = (len - head) >> 2;
     f32x4 *av = reinterpret_cast<f32x4 *>(acc + head);
     const u32x2 *gv = reinterpret_cast<const u32x2 *>(g + head);
-    for (int64_t v = tid; v < nvec; v += kBlock) {
+    // two vectors a block apart per iteration, both loaded before either is
+    // stored (one per iteration measured 3-5% slower)
+    int64_t v = tid;
+    for (; v + kBlock < nvec; v += 2 * kBlock) {
+        const int64_t v1 = v + kBlock;
+        const u32x2 w0 = ldp<LN>(gv + v), w1 = ldp<LN>(gv + v1);
+        const f32x4 x0{bf16_lo(w0.x), bf16_hi(w0.x), bf16_lo(w0.y), bf16_hi(w0.y)};
+        const f32x4 x1{bf16_lo(w1.x), bf16_hi(w1.x), bf16_lo(w1.y), bf16_hi(w1.y)};
+        if (kReset) {
+            stp<SN>(av + v, x0);
+            stp<SN>(av + v1, x1);
+        } else {
+            const f32x4 a0 = ldp<LN>(av + v), a1 = ldp<LN>(av + v1);
+            stp<SN>(av + v, f32x4{a0.x + x0.x, a0.y + x0.y, a0.z + x0.z, a0.w + x0.w});
+            stp<SN>(av + v1, f32x4{a1.x + x1.x, a1.y + x1.y, a1.z + x1.z, a1.w + x1.w});
+        }
+    }
+    for (; v < nvec; v += kBlock) {
         const u32x2 w = ldp<LN>(gv + v);
         const f32x4 x{bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y)};
         if (kReset) {
