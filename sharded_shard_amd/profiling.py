@@ -171,6 +171,7 @@ WR_COUNTERS = ["TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum"]
 
 
 def summarize(prof, out_dir, sha):
+    os.makedirs(out_dir, exist_ok=True)
     cal = calibration(prof)
     traffic = {"kernels_source_sha256": sha, "fetch_scale": cal["fetch_scale"],
                "write_scale": cal["write_scale"], "calibration": cal, "workloads": {}}
