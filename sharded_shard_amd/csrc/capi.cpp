@@ -534,7 +534,7 @@ hipError_t do_reduce(const fsdp_plan *p, const uint16_t *rs_in, hipStream_t st) 
 hipError_t do_adamw(const fsdp_plan *p, const float scal[8], hipStream_t st) {
     return guarded([&] {
         return fsdp::launch_adamw(p->d_adamw, static_cast<int64_t>(p->L.adamw.size()),
-                                  p->d_entries, scal, st);
+                                  p->d_entries, scal, false, st);
     });
 }
 
@@ -878,7 +878,7 @@ fsdp_status check_set(const fsdp_group_set *set, int32_t roles, const char *call
 
 hipError_t do_adamw_set(const fsdp_group_set *set, const float scal[8], hipStream_t st) {
     return guarded([&] {
-        return fsdp::launch_adamw(set->d_adamw, set->n_adamw, set->d_entries, scal, st);
+        return fsdp::launch_adamw(set->d_adamw, set->n_adamw, set->d_entries, scal, true, st);
     });
 }
 

@@ -24,9 +24,11 @@ hipError_t launch_reduce(const ReduceTile *tiles, int64_t n, const DevEntry *ent
                          const uint16_t *rs_in, int64_t S, int32_t N, bool chunk_aligned,
                          hipStream_t st);
 // AdamW on the bound shards; scal: beta1, 1-beta1, beta2, 1-beta2, eps,
-// 1-lr*wd, lr/(1-beta1^t), sqrt(1-beta2^t)
+// 1-lr*wd, lr/(1-beta1^t), sqrt(1-beta2^t); one_launch: the tiles cover every
+// group of a step (a group set), so no later kernel reads what it leaves in
+// the caches
 hipError_t launch_adamw(const EwTile *tiles, int64_t n, const DevEntry *ents,
-                        const float scal[8], hipStream_t st);
+                        const float scal[8], bool one_launch, hipStream_t st);
 // AdamW, then the bf16 copy-in of the new master, over the copy-in tiles
 hipError_t launch_adamw_pack(const PackTile *tiles, int64_t n, const DevEntry *ents,
                              uint16_t *ag_in, const float scal[8], hipStream_t st);

@@ -5,16 +5,24 @@
 #include "launch.hpp"
 #include "rows.hpp"
 
-// AdamW: plain loads and stores (non-temporal ones measured faster for the
-// kernel itself but slowed the copy-in and copy-out after it by more)
+// AdamW per group: plain loads and stores (non-temporal ones make the
+// kernel faster but the step slower: on the Llama 70B shape, per group,
+// 73.4 against 72.3 ms, the next group's reduction losing 3%)
 #ifndef FSDP_ADAMW_POL
 #define FSDP_ADAMW_POL 0
 #endif
-// AdamW fused with the copy-in: plain loads and stores, as AdamW; elements
-// per block
-#ifndef FSDP_ADAMW_PACK_POL
-#define FSDP_ADAMW_PACK_POL 0
+// AdamW as one launch over every group, and AdamW fused with the copy-in
+// (also one launch over a group set): non-temporal loads and stores (the
+// AdamW launch 5.25 -> 5.55 TB/s on the Llama 7B shape, the step 14.71 ->
+// 14.57 ms; the fused launch's step 14.17 -> 14.04 ms, and 73.3 -> 73.05 ms
+// on the 70B shape)
+#ifndef FSDP_ADAMW_SET_POL
+#define FSDP_ADAMW_SET_POL 3
 #endif
+#ifndef FSDP_ADAMW_PACK_POL
+#define FSDP_ADAMW_PACK_POL 3
+#endif
+// elements per block of AdamW fused with the copy-in
 #ifndef FSDP_ADAMW_PACK_SUB
 #define FSDP_ADAMW_PACK_SUB 4096
 #endif
@@ -528,11 +536,15 @@ AdamwScalars to_scalars(const float s[8]) {
 // ---------------------------------------------------------------------------
 
 hipError_t launch_adamw(const EwTile *tiles, int64_t n, const DevEntry *ents,
-                        const float scal[8], hipStream_t st) {
+                        const float scal[8], bool one_launch, hipStream_t st) {
     if (n == 0) return hipSuccess;
     const int32_t sp = split_for(kTileAdamw, FSDP_ADAMW_SUB);
-    adamw_kernel<FSDP_ADAMW_POL><<<grid_for(n, sp), kBlock, 0, st>>>(
-        tiles, n, sp, kTileAdamw / sp, ents, to_scalars(scal));
+    if (one_launch)
+        adamw_kernel<FSDP_ADAMW_SET_POL><<<grid_for(n, sp), kBlock, 0, st>>>(
+            tiles, n, sp, kTileAdamw / sp, ents, to_scalars(scal));
+    else
+        adamw_kernel<FSDP_ADAMW_POL><<<grid_for(n, sp), kBlock, 0, st>>>(
+            tiles, n, sp, kTileAdamw / sp, ents, to_scalars(scal));
     return hipGetLastError();
 }
 

@@ -96,7 +96,7 @@ hipError_t launch_adamw_pack(const PackTile *tiles, int64_t n, const DevEntry *e
 }
 
 hipError_t launch_adamw(const EwTile *tiles, int64_t n, const DevEntry *ents, const float *,
-                        hipStream_t) {
+                        bool, hipStream_t) {
     ++harness::launches;
     for (int64_t i = 0; i < n; ++i) {
         const EwTile &t = tiles[i];
