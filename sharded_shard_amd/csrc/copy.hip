@@ -48,13 +48,6 @@ namespace fsdp {
 
 namespace {
 
-// Misaligned sources: the chunk after a wave's span, which lane 63 loads
-// for its funnel shift and another wave reads next, takes a temporal load
-// (with the non-temporal hint of the rest of the run it was often evicted
-// before that wave's read and fetched twice; measured on the ragged MoE
-// workload: fp32 reduce-scatter copy-in +1%, copy-out +1%).
-constexpr int kBoundaryNT = 0;
-
 // ---------------------------------------------------------------------------
 // copy-out: [N, S] bf16 -> full parameters
 // ---------------------------------------------------------------------------

@@ -215,7 +215,7 @@ __device__ __forceinline__ void sum_rows_quad_mis(const uint16_t *base, uint32_t
             for (int h = 0; h < 2; ++h) {
                 const uint32_t o = offb + 512u * h;
                 a[i][h] = bload8<NT>(al, o, n);
-                e[i][h] = bload8<NT>(al, last ? o + 8u : n, n);
+                e[i][h] = bload8<kBoundaryNT>(al, last ? o + 8u : n, n);
             }
         }
 #pragma unroll
