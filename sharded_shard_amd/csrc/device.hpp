@@ -299,20 +299,6 @@ inline int32_t split_rows(int64_t tile, int32_t N, int32_t extra_rows) {
     return split_for(tile, want);
 }
 
-// Misaligned rows: a wave covers 63 groups (504 elements), so sub-ranges are
-// cut in whole such waves; a power-of-two sub-range would leave one wave a
-// second pass through all N rows for a handful of groups.
-struct RowSplit {
-    int32_t split;
-    int64_t sub;
-};
-inline RowSplit row_split(int64_t tile, int32_t sp, bool aligned) {
-    const int64_t sub = tile / sp;
-    if (aligned) return RowSplit{sp, sub};
-    const int64_t msub = sub / 512 * 504;
-    return RowSplit{static_cast<int32_t>((tile + msub - 1) / msub), msub};
-}
-
 }  // namespace
 
 }  // namespace fsdp

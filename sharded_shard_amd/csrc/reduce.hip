@@ -4,28 +4,23 @@
 #include "launch.hpp"
 #include "rows.hpp"
 
-// the bf16 reduction's row-batch and wide variants: non-temporal loads
+// the bf16 reduction's wide variant: non-temporal loads
 #ifndef FSDP_REDUCE_POL
 #define FSDP_REDUCE_POL 1
 #endif
-// the bf16 reduction on aligned rows below the wide threshold: a quad per
-// lane, non-temporal loads and stores
+// the bf16 reduction below the wide threshold, aligned or misaligned rows:
+// a quad per lane, non-temporal loads and stores (on the ragged MoE rows
+// 5.0 TB/s, against 4.1 for 63 groups of 8 per wave)
 #ifndef FSDP_REDUCE_QUAD_POL
 #define FSDP_REDUCE_QUAD_POL 3
 #endif
-// Lanes of the fp32 reduction store two 16-byte halves of a 32-byte span per
-// group: non-temporal stores of that pattern cost extra HBM writes (measured
-// 1.1-1.7x the algorithmic bytes), plain stores do not.  The fp32 copy-ins
-// and the accumulation move four elements per lane, so every store
-// instruction of a wave writes 1 KB contiguously, and take non-temporal
-// loads and stores.
+// the fp32 reduction: a vector per lane, so every wave instruction is
+// contiguous (lanes storing two 16-byte halves of a 32-byte span, an earlier
+// layout, made non-temporal stores cost 1.1-1.7x the algorithmic bytes), and
+// non-temporal loads and stores (on the ragged MoE rows 6.2 TB/s, against
+// 5.5 for that layout with plain ones)
 #ifndef FSDP_REDUCE_F32_POL
-#define FSDP_REDUCE_F32_POL 0
-#endif
-// the fp32 reduction on aligned rows: a vector per lane, non-temporal loads
-// and stores
-#ifndef FSDP_REDUCE_F32_QUAD_POL
-#define FSDP_REDUCE_F32_QUAD_POL 3
+#define FSDP_REDUCE_F32_POL 3
 #endif
 // gradient accumulation: non-temporal loads and stores
 #ifndef FSDP_ACC_POL
@@ -49,10 +44,16 @@ namespace {
 // reduce: [N, S] bf16 contributions -> fp32 mean, this rank's pieces
 // ---------------------------------------------------------------------------
 
+// Valid elements [0, len) of one run.  One or two rows in flight per lane
+// (C == 1): a quad per lane and pass, two passes 64 quads apart, so every
+// wave instruction is contiguous and loads and stores take
+// FSDP_REDUCE_QUAD_POL; misaligned rows are funnel-shifted by their own
+// phase (sum_rows_quad_mis).  The wide variant (C > 1, 16-byte aligned rows
+// only) takes C groups of 8 per lane, row by row (sum_rows_wide).
 template <int POL, int C, bool kChunkAligned>
 __device__ __forceinline__ void reduce_run(float *__restrict__ dst, const uint16_t *__restrict__ src0,
                                            int64_t len, int64_t S, int32_t N, float fN) {
-    constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
+    static_assert(kChunkAligned || C == 1, "the wide variant needs aligned rows");
     const int tid = threadIdx.x;
     const uint32_t kS = static_cast<uint32_t>((S * 2) & 15);
     int64_t head = ((16u - (lo32(dst) & 15u)) & 15u) >> 2;
@@ -68,17 +69,19 @@ __device__ __forceinline__ void reduce_run(float *__restrict__ dst, const uint16
     if (tid < head) dst[tid] = sum_rows_scalar(src0, S, N, tid) / fN;
     const uint32_t dbytes = static_cast<uint32_t>(2 * (len - head));
     f32x4 *dv = reinterpret_cast<f32x4 *>(dst + head);
-    if constexpr (kChunkAligned && C == 1) {
-        // a quad per lane and pass, two passes 64 quads apart: every wave
-        // instruction contiguous, so the stores take FSDP_REDUCE_QUAD_POL
-        constexpr int QS = (FSDP_REDUCE_QUAD_POL >> 1) & 1;
+    if constexpr (C == 1) {
+        constexpr int QL = FSDP_REDUCE_QUAD_POL & 1, QS = (FSDP_REDUCE_QUAD_POL >> 1) & 1;
         const int64_t nq = (len - head) >> 2;
         const int64_t lane = tid & 63;
         const int64_t qstep = static_cast<int64_t>(blockDim.x >> 6) * 128;
         for (int64_t qb = (tid >> 6) * 128; qb < nq; qb += qstep) {
+            const uint32_t off = static_cast<uint32_t>(qb + lane) << 3;
             float acc[2][4];
-            sum_rows_quad<FSDP_REDUCE_QUAD_POL & 1, FSDP_REDUCE_ROW_BATCH, 2>(
-                s0, static_cast<uint32_t>(qb + lane) << 3, dbytes, S, N, acc);
+            if constexpr (kChunkAligned)
+                sum_rows_quad<QL, FSDP_REDUCE_ROW_BATCH, 2>(s0, off, dbytes, S, N, acc);
+            else
+                sum_rows_quad_mis<QL, FSDP_REDUCE_MIS_ROW_BATCH>(s0, off, dbytes, S, N, k0 & 7u,
+                                                                 kS & 7u, acc);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int64_t q = qb + lane + 64 * h;
@@ -90,26 +93,24 @@ __device__ __forceinline__ void reduce_run(float *__restrict__ dst, const uint16
         const int64_t done = head + (nq << 2);
         if (tid < len - done) dst[done + tid] = sum_rows_scalar(src0, S, N, done + tid) / fN;
         return;
-    }
-    const int64_t ngrp = (len - head) >> 3;
-    for (GroupWalk<kChunkAligned, C> w; w.more(ngrp); w.next()) {
-        float acc[C][8];
-        if constexpr (C == 1)
-            sum_rows8<LN, FSDP_REDUCE_ROW_BATCH, kChunkAligned>(
-                s0, static_cast<uint32_t>(w.g) << 4, dbytes, S, N, k0, kS, acc[0]);
-        else
+    } else {
+        constexpr int LN = POL & 1, SN = (POL >> 1) & 1;
+        const int64_t ngrp = (len - head) >> 3;
+        for (GroupWalk<C> w; w.more(ngrp); w.next()) {
+            float acc[C][8];
             sum_rows_wide<LN, C>(s0, static_cast<uint32_t>(w.g) << 4, dbytes, S, N, acc);
 #pragma unroll
-        for (int q = 0; q < C; ++q) {
-            if (!w.own(ngrp, q)) continue;
-            const int64_t g = w.at(q);
-            const float *a = acc[q];
-            stp<SN>(dv + 2 * g, f32x4{a[0] / fN, a[1] / fN, a[2] / fN, a[3] / fN});
-            stp<SN>(dv + 2 * g + 1, f32x4{a[4] / fN, a[5] / fN, a[6] / fN, a[7] / fN});
+            for (int q = 0; q < C; ++q) {
+                if (!w.own(ngrp, q)) continue;
+                const int64_t g = w.at(q);
+                const float *a = acc[q];
+                stp<SN>(dv + 2 * g, f32x4{a[0] / fN, a[1] / fN, a[2] / fN, a[3] / fN});
+                stp<SN>(dv + 2 * g + 1, f32x4{a[4] / fN, a[5] / fN, a[6] / fN, a[7] / fN});
+            }
         }
+        const int64_t done = head + (ngrp << 3);
+        if (tid < len - done) dst[done + tid] = sum_rows_scalar(src0, S, N, done + tid) / fN;
     }
-    const int64_t done = head + (ngrp << 3);
-    if (tid < len - done) dst[done + tid] = sum_rows_scalar(src0, S, N, done + tid) / fN;
 }
 
 template <int POL, int C, bool kChunkAligned>
@@ -208,64 +209,13 @@ __device__ __forceinline__ float sum_rows_scalar_f32(const float *src0, int64_t 
     return acc;
 }
 
-// Eight consecutive column sums of the N rows of [N, S] fp32 whose row 0
-// starts at base (uniform) plus this lane's byte offset offb (32 bytes per
-// group), added in rank order from row 0; q0 = dword index of base + offb
-// modulo 4, qS = S modulo 4.  Buffer ranges cover exactly the 16-byte chunks
-// holding each row's dbytes data bytes.  Same scheme as sum_rows8: with
-// kChunkAligned (q0 = qS = 0) each row is two aligned loads; otherwise a
-// lane's third chunk is the next lane's first (waves of 63 groups).
-template <int NT, int RB, bool kChunkAligned>
-__device__ __forceinline__ void sum_rows8f(const float *base, uint32_t offb, uint32_t dbytes,
-                                           int64_t S, int32_t N, uint32_t q0, uint32_t qS,
-                                           float (&acc)[8]) {
-    const char *r = reinterpret_cast<const char *>(base);
-    const int64_t Sb = S * 4;
-    for (int32_t j = 0; j < N; j += RB) {
-        f32x4 lo[RB], hi[RB];
-        if (kChunkAligned) {
-            const uint32_t nb = (dbytes + 15u) & ~15u;
-#pragma unroll
-            for (int i = 0; i < RB; ++i) {
-                const char *row = r + (j + i) * Sb;
-                const uint32_t n = j + i < N ? nb : 0u;
-                lo[i] = __builtin_bit_cast(f32x4, bload16<NT>(row, offb, n));
-                hi[i] = __builtin_bit_cast(f32x4, bload16<NT>(row, offb + 16, n));
-            }
-        } else {
-            uint32_t qq[RB];
-#pragma unroll
-            for (int i = 0; i < RB; ++i) {
-                qq[i] = (q0 + static_cast<uint32_t>(j + i) * qS) & 3u;
-                const char *al = r + (j + i) * Sb - 4 * qq[i];
-                const uint32_t n = j + i < N ? (4 * qq[i] + dbytes + 15u) & ~15u : 0u;
-                lo[i] = __builtin_bit_cast(f32x4, bload16<NT>(al, offb, n));
-                hi[i] = __builtin_bit_cast(f32x4, bload16<NT>(al, offb + 16, n));
-            }
-#pragma unroll
-            for (int i = 0; i < RB; ++i) {
-                const f32x4 c = __builtin_bit_cast(
-                    f32x4, next_lane16(__builtin_bit_cast(u32x4, lo[i])));
-                select8f(lo[i], hi[i], c, qq[i], lo[i], hi[i]);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < RB; ++i) {
-            if (j + i < N) {
-                const float x[8] = {lo[i].x, lo[i].y, lo[i].z, lo[i].w,
-                                    hi[i].x, hi[i].y, hi[i].z, hi[i].w};
-                if (j + i == 0) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[e] = x[e];
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc[e] = acc[e] + x[e];
-                }
-            }
-        }
-    }
-}
-
+// Valid elements [0, len) of one run: four elements (one vector) per lane
+// and pass, two passes 64 vectors apart, so every wave instruction is
+// contiguous and loads and stores take POL.  On misaligned rows (row j
+// starts q_j = (q0 + j qS) & 3 dwords past a 16-byte boundary) lane l loads
+// the aligned chunk holding its first element, takes the next chunk from
+// lane l + 1 (DPP; lane 63 loads its own) and shifts by q_j dwords, one row
+// at a time: every chunk of a row is read once.
 template <int POL, bool kChunkAligned>
 __device__ __forceinline__ void reduce_f32_run(float *__restrict__ dst,
                                                const float *__restrict__ src0, int64_t len,
@@ -286,28 +236,25 @@ __device__ __forceinline__ void reduce_f32_run(float *__restrict__ dst,
     if (tid < head) dst[tid] = sum_rows_scalar_f32(src0, S, N, tid) / fN;
     const uint32_t dbytes = static_cast<uint32_t>(4 * (len - head));
     f32x4 *dv = reinterpret_cast<f32x4 *>(dst + head);
-    if constexpr (kChunkAligned) {
-        // four elements (one vector) per lane and pass, two passes 64
-        // vectors apart: every wave instruction contiguous, so loads and
-        // stores take FSDP_REDUCE_F32_QUAD_POL
-        constexpr int QL = FSDP_REDUCE_F32_QUAD_POL & 1, QS = (FSDP_REDUCE_F32_QUAD_POL >> 1) & 1;
-        const char *r = reinterpret_cast<const char *>(s0);
-        const int64_t Sb = S * 4;
-        const uint32_t nb = (dbytes + 15u) & ~15u;
-        const int64_t nq = (len - head) >> 2;
-        const int64_t lane = tid & 63;
-        const int64_t qstep = static_cast<int64_t>(blockDim.x >> 6) * 128;
-        for (int64_t qb = (tid >> 6) * 128; qb < nq; qb += qstep) {
-            const uint32_t off = static_cast<uint32_t>(qb + lane) << 4;
-            f32x4 acc[2];
+    const char *r = reinterpret_cast<const char *>(s0);
+    const int64_t Sb = S * 4;
+    const int64_t nq = (len - head) >> 2;
+    const int64_t lane = tid & 63;
+    const bool last = lane == 63;
+    const int64_t qstep = static_cast<int64_t>(blockDim.x >> 6) * 128;
+    for (int64_t qb = (tid >> 6) * 128; qb < nq; qb += qstep) {
+        const uint32_t off = static_cast<uint32_t>(qb + lane) << 4;
+        f32x4 acc[2];
+        if constexpr (kChunkAligned) {
+            const uint32_t nb = (dbytes + 15u) & ~15u;
             for (int32_t j = 0; j < N; j += FSDP_REDUCE_ROW_BATCH) {
                 f32x4 x[FSDP_REDUCE_ROW_BATCH][2];
 #pragma unroll
                 for (int i = 0; i < FSDP_REDUCE_ROW_BATCH; ++i) {
                     const char *row = r + (j + i) * Sb;
                     const uint32_t n = j + i < N ? nb : 0u;
-                    x[i][0] = __builtin_bit_cast(f32x4, bload16<QL>(row, off, n));
-                    x[i][1] = __builtin_bit_cast(f32x4, bload16<QL>(row, off + 1024u, n));
+                    x[i][0] = __builtin_bit_cast(f32x4, bload16<LN>(row, off, n));
+                    x[i][1] = __builtin_bit_cast(f32x4, bload16<LN>(row, off + 1024u, n));
                 }
 #pragma unroll
                 for (int i = 0; i < FSDP_REDUCE_ROW_BATCH; ++i) {
@@ -321,30 +268,37 @@ __device__ __forceinline__ void reduce_f32_run(float *__restrict__ dst,
                     }
                 }
             }
+        } else {
+            for (int32_t j = 0; j < N; ++j) {
+                const uint32_t qq = (q0 + static_cast<uint32_t>(j) * qS) & 3u;
+                const char *al = r + j * Sb - 4 * qq;
+                const uint32_t n = (4 * qq + dbytes + 15u) & ~15u;
+                u32x4 a[2], e[2];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int64_t q = qb + lane + 64 * h;
-                if (q < nq)
-                    stp<QS>(dv + q, f32x4{acc[h].x / fN, acc[h].y / fN, acc[h].z / fN,
-                                          acc[h].w / fN});
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t o = off + 1024u * h;
+                    a[h] = bload16<LN>(al, o, n);
+                    e[h] = bload16<kBoundaryNT>(al, last ? o + 16u : n, n);
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    u32x4 b = next_lane16(a[h]);
+                    if (last) b = e[h];
+                    const f32x4 y = __builtin_bit_cast(f32x4, funnel(a[h], b, 4 * qq));
+                    acc[h] = j == 0 ? y
+                                    : f32x4{acc[h].x + y.x, acc[h].y + y.y, acc[h].z + y.z,
+                                            acc[h].w + y.w};
+                }
             }
         }
-        const int64_t done = head + (nq << 2);
-        if (tid < len - done) dst[done + tid] = sum_rows_scalar_f32(src0, S, N, done + tid) / fN;
-        return;
-    }
-    const int64_t ngrp = (len - head) >> 3;
-    for (GroupWalk<kChunkAligned> w; w.more(ngrp); w.next()) {
-        float acc[8];
-        sum_rows8f<LN, FSDP_REDUCE_ROW_BATCH, kChunkAligned>(
-            s0, static_cast<uint32_t>(w.g) << 5, dbytes, S, N, q0, qS, acc);
-        if (w.own(ngrp)) {
-            const int64_t g = w.g;
-            stp<SN>(dv + 2 * g, f32x4{acc[0] / fN, acc[1] / fN, acc[2] / fN, acc[3] / fN});
-            stp<SN>(dv + 2 * g + 1, f32x4{acc[4] / fN, acc[5] / fN, acc[6] / fN, acc[7] / fN});
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t q = qb + lane + 64 * h;
+            if (q < nq)
+                stp<SN>(dv + q, f32x4{acc[h].x / fN, acc[h].y / fN, acc[h].z / fN, acc[h].w / fN});
         }
     }
-    const int64_t done = head + (ngrp << 3);
+    const int64_t done = head + (nq << 2);
     if (tid < len - done) dst[done + tid] = sum_rows_scalar_f32(src0, S, N, done + tid) / fN;
 }
 
@@ -386,14 +340,14 @@ hipError_t launch_reduce(const ReduceTile *tiles, int64_t n, const DevEntry *ent
             <<<grid_for(n, wsp), 64, 0, st>>>(tiles, n, wsp, wsub, ents, rs_in, S, N, fN);
         return hipGetLastError();
     }
-    const RowSplit rsp = row_split(kTileReduce, split_rows(kTileReduce, N, 0), chunk_aligned);
-    const unsigned grid = grid_for(n, rsp.split);
+    const int32_t sp = split_rows(kTileReduce, N, 0);
+    const unsigned grid = grid_for(n, sp);
     if (chunk_aligned)
         reduce_kernel<FSDP_REDUCE_POL, 1, true>
-            <<<grid, kBlock, 0, st>>>(tiles, n, rsp.split, rsp.sub, ents, rs_in, S, N, fN);
+            <<<grid, kBlock, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
     else
         reduce_kernel<FSDP_REDUCE_POL, 1, false>
-            <<<grid, kBlock, 0, st>>>(tiles, n, rsp.split, rsp.sub, ents, rs_in, S, N, fN);
+            <<<grid, kBlock, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
     return hipGetLastError();
 }
 
@@ -415,14 +369,14 @@ hipError_t launch_reduce_f32(const ReduceTile *tiles, int64_t n, const DevEntry 
     if (n == 0) return hipSuccess;
     const float fN = static_cast<float>(N);
     // fp32 rows carry twice the bytes of bf16 rows per element
-    const RowSplit rsp = row_split(kTileReduce, split_rows(kTileReduce, 2 * N, 0), chunk_aligned);
-    const unsigned grid = grid_for(n, rsp.split);
+    const int32_t sp = split_rows(kTileReduce, 2 * N, 0);
+    const unsigned grid = grid_for(n, sp);
     if (chunk_aligned)
         reduce_f32_kernel<FSDP_REDUCE_F32_POL, true>
-            <<<grid, kBlock, 0, st>>>(tiles, n, rsp.split, rsp.sub, ents, rs_in, S, N, fN);
+            <<<grid, kBlock, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
     else
         reduce_f32_kernel<FSDP_REDUCE_F32_POL, false>
-            <<<grid, kBlock, 0, st>>>(tiles, n, rsp.split, rsp.sub, ents, rs_in, S, N, fN);
+            <<<grid, kBlock, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
     return hipGetLastError();
 }
 

@@ -6,10 +6,15 @@
 
 #include "device.hpp"
 
-// rows in flight per lane of the plain reductions (measured on MI355X: more
-// rows in flight per wave spread each wave over more DRAM pages)
+// rows in flight per lane of the plain reductions on aligned rows (measured
+// on MI355X: 1 ties at 8 ranks; 4 and 8 spread each wave over more DRAM
+// pages, 7-9% slower for fp32 rows at 64 ranks), and on misaligned rows (2
+// measured 2.5% slower than 1)
 #ifndef FSDP_REDUCE_ROW_BATCH
 #define FSDP_REDUCE_ROW_BATCH 2
+#endif
+#ifndef FSDP_REDUCE_MIS_ROW_BATCH
+#define FSDP_REDUCE_MIS_ROW_BATCH 1
 #endif
 
 namespace fsdp {
@@ -46,60 +51,14 @@ __device__ __forceinline__ void init8(float (&acc)[8], u32x4 x) {
     acc[7] = bf16_hi(x.w);
 }
 
-// Eight consecutive column sums of the N rows of [N, S] bf16 whose row 0
-// starts at base (uniform) plus this lane's byte offset offb, added in rank
-// order from row 0; k0 = (base + offb) & 15, kS = (2S) & 15.  Each row's
-// buffer range covers exactly the 16-byte chunks that hold its dbytes data
-// bytes, so a lane past the end of the data reads zeros and never touches
-// memory beyond the last chunk.  Rows are loaded RB at a time.
-//
-// kChunkAligned: every row starts 16-byte aligned here (k0 = 0, kS = 0), so
-// each row is one aligned 16-byte load.  Otherwise a row is read as aligned
-// 16-byte chunks and funnel-shifted; the caller gives the lanes of a wave
-// consecutive chunks (offb = 16 * (lane + const)), so a lane's second chunk
-// is the next lane's first, and lane 63's sums are not valid.
-template <int NT, int RB, bool kChunkAligned>
-__device__ __forceinline__ void sum_rows8(const uint16_t *base, uint32_t offb, uint32_t dbytes,
-                                          int64_t S, int32_t N, uint32_t k0, uint32_t kS,
-                                          float (&acc)[8]) {
-    const char *r = reinterpret_cast<const char *>(base);
-    const int64_t Sb = S * 2;
-    for (int32_t j = 0; j < N; j += RB) {
-        // rows past N get an empty range: their loads read zero and are
-        // never added
-        u32x4 x[RB];
-        if (kChunkAligned) {
-            const uint32_t nb = (dbytes + 15u) & ~15u;
-#pragma unroll
-            for (int i = 0; i < RB; ++i)
-                x[i] = bload16<NT>(r + (j + i) * Sb, offb, j + i < N ? nb : 0u);
-        } else {
-            uint32_t kk[RB];
-#pragma unroll
-            for (int i = 0; i < RB; ++i) {
-                kk[i] = (k0 + static_cast<uint32_t>(j + i) * kS) & 15u;
-                x[i] = bload16<NT>(r + (j + i) * Sb - kk[i], offb,
-                                   j + i < N ? (kk[i] + dbytes + 15u) & ~15u : 0u);
-            }
-#pragma unroll
-            for (int i = 0; i < RB; ++i) x[i] = funnel(x[i], next_lane16(x[i]), kk[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < RB; ++i) {
-            if (j + i < N) {
-                if (j + i == 0) init8(acc, x[i]);
-                else acc8(acc, x[i]);
-            }
-        }
-    }
-}
-
 // Aligned rows, C groups per lane: row by row from row 0, the C chunks of a
 // row in flight together, so a wave reads C KB of one row before it moves to
 // the next (at 64 ranks this keeps each wave on one DRAM region at a time:
 // measured 5.99 vs 5.31 TB/s for one chunk of four rows in flight).  Pass c
-// of this lane sits at byte offset offb + c * 1024; same buffer ranges as
-// sum_rows8.  kRoll (the fused step) reloads each chunk's register with the
+// of this lane sits at byte offset offb + c * 1024.  Each row's buffer range
+// covers exactly the 16-byte chunks holding its dbytes data bytes, so a lane
+// past the end of the data reads zeros and never touches memory beyond the
+// last chunk.  kRoll (the fused step) reloads each chunk's register with the
 // next row's chunk as soon as it has been added, so the wave never drains
 // its loads between rows: the 64-rank fused step 5.70 -> 5.93 TB/s on
 // MI355X; the plain reduction stays without (6.31 vs 6.19 TB/s).
@@ -160,7 +119,7 @@ __device__ __forceinline__ void sum_rows_wide(const uint16_t *base, uint32_t off
 // byte offsets offb + 512 h (h < QP) from row 0 at base (16-byte aligned
 // rows, uniform), over the N rows of [N, S] bf16, in rank order from row 0;
 // rows RB at a time, each row QP 8-byte loads per lane.  Buffer ranges as in
-// sum_rows8.
+// sum_rows_wide (8-byte granules).
 template <int NT, int RB, int QP>
 __device__ __forceinline__ void sum_rows_quad(const uint16_t *base, uint32_t offb, uint32_t dbytes,
                                               int64_t S, int32_t N, float (&acc)[QP][4]) {
@@ -240,31 +199,25 @@ __device__ __forceinline__ void sum_rows_quad_mis(const uint16_t *base, uint32_t
     }
 }
 
-// Group schedule of the row kernels: 8-element groups [0, ngrp), C per lane
-// per pass, a wave's lanes on consecutive groups.  Aligned rows: pass c of
-// lane l of wave w takes group (w*C + c)*64 + l, then all step by the block.
-// Misaligned rows (C = 1 only): a wave covers 63 groups and its lane 63 only
-// loads the chunk after lane 62's (see sum_rows8); every lane runs the same
-// number of iterations, and `own` says whether its group is to be written.
-template <bool kChunkAligned, int C = 1>
+// Group schedule of the wide row kernels (16-byte aligned rows): 8-element
+// groups [0, ngrp), C per lane per pass; pass c of lane l of wave w takes
+// group (w*C + c)*64 + l, then all step by the block.  Every lane runs the
+// same number of iterations, and `own` says whether its group exists.
+template <int C = 1>
 struct GroupWalk {
-    static_assert(kChunkAligned || C == 1, "several groups per lane need aligned rows");
-    static constexpr int64_t kPer = kChunkAligned ? 64 : 63;
     int64_t g, step;
     __device__ GroupWalk() {
         const int64_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-        g = wave * kPer * C + lane;
-        step = static_cast<int64_t>(blockDim.x >> 6) * kPer * C;
+        g = wave * 64 * C + lane;
+        step = static_cast<int64_t>(blockDim.x >> 6) * 64 * C;
     }
     // the wave still has work
     __device__ bool more(int64_t ngrp) const {
         return g - static_cast<int64_t>(threadIdx.x & 63) < ngrp;
     }
     // group of pass c
-    __device__ int64_t at(int c) const { return g + c * kPer; }
-    __device__ bool own(int64_t ngrp, int c = 0) const {
-        return at(c) < ngrp && (kChunkAligned || (threadIdx.x & 63) != 63);
-    }
+    __device__ int64_t at(int c) const { return g + c * 64; }
+    __device__ bool own(int64_t ngrp, int c = 0) const { return at(c) < ngrp; }
     __device__ void next() { g += step; }
 };
 

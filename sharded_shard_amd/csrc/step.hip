@@ -238,7 +238,7 @@ __device__ __forceinline__ void step_run_wide(const uint16_t *__restrict__ rs0, 
         const int64_t ngrp = (valid - head) >> 3;
         const uint32_t ka = lo32(dst + head) & 15u;
         const uint32_t dbytes = static_cast<uint32_t>(2 * (valid - head));
-        for (GroupWalk<true, C> w; w.more(ngrp); w.next()) {
+        for (GroupWalk<C> w; w.more(ngrp); w.next()) {
             float acc[C][8];
             sum_rows_wide<FSDP_STEP_ROW_NT, C, true>(rs0 + head, static_cast<uint32_t>(w.g) << 4,
                                                      dbytes, S, N, acc);
@@ -585,9 +585,8 @@ hipError_t launch_step(const PackTile *tiles, int64_t n, const DevEntry *ents,
     const AdamwScalars c = to_scalars(scal);
     // p, m, v read and written: six more streams per element besides the N rows;
     // both variants run whole waves of 128 quads, so sub-ranges are powers of two
-    const RowSplit rsp = row_split(kTilePack, split_rows(kTilePack, N, 6), true);
-    const int32_t sp = rsp.split;
-    const int64_t sub = rsp.sub;
+    const int32_t sp = split_rows(kTilePack, N, 6);
+    const int64_t sub = kTilePack / sp;
     const unsigned grid = grid_for(n, sp);
     const unsigned thr = kBlock;
     const bool aligned = chunk_aligned;
