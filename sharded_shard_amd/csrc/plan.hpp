@@ -21,8 +21,10 @@
 
 namespace fsdp {
 
-// Tile lengths in elements.  Multiples of 8 so every tile of a run starts at
-// the same offset modulo 16 bytes as the run itself.
+// Tile lengths in elements, multiples of every sub-range length.  Tiles of a
+// run follow its start, except the reduce-scatter copy-in's, which follow
+// its destination's cache lines (plan.cpp); kernels take each sub-range's
+// alignment from its addresses.
 #ifndef FSDP_TILE_PACK
 #define FSDP_TILE_PACK 16384
 #endif
