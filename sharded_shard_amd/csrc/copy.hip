@@ -93,6 +93,11 @@ __device__ __forceinline__ void copy_run_bf16(uint16_t *__restrict__ dst,
         // with a temporal hint and stays in L2 for that wave (kBoundaryNT).
         const char *al = reinterpret_cast<const char *>(s) - k;
         const uint32_t nb = (k + 2 * static_cast<uint32_t>(len - head) + 15u) & ~15u;
+        // stores through a buffer range of exactly the run's vectors: lanes
+        // past the end are dropped without a branch, which would let the
+        // compiler sink a boundary load under it (see next_or_own)
+        char *db = reinterpret_cast<char *>(dv);
+        const uint32_t dn = static_cast<uint32_t>(nvec) << 4;
         const uint32_t lane = tid & 63;
         const bool last = lane == 63;
         for (int64_t w0 = tid - lane; w0 < nvec; w0 += 2 * TB) {
@@ -101,13 +106,9 @@ __device__ __forceinline__ void copy_run_bf16(uint16_t *__restrict__ dst,
             const u32x4 a0 = bload16<LN>(al, o0, nb), a1 = bload16<LN>(al, o1, nb);
             const u32x4 h0 = bload16<kBoundaryNT>(al, last ? o0 + 16 : nb, nb);
             const u32x4 h1 = bload16<kBoundaryNT>(al, last ? o1 + 16 : nb, nb);
-            u32x4 b0 = next_lane16(a0), b1 = next_lane16(a1);
-            if (last) {
-                b0 = h0;
-                b1 = h1;
-            }
-            if (v0 < nvec) stp<SN>(dv + v0, funnel(a0, b0, k));
-            if (v1 < nvec) stp<SN>(dv + v1, funnel(a1, b1, k));
+            const u32x4 b0 = next_or_own(a0, h0), b1 = next_or_own(a1, h1);
+            bstore16<SN>(db, o0, dn, funnel(a0, b0, k));
+            bstore16<SN>(db, o1, dn, funnel(a1, b1, k));
         }
     }
     const int64_t done = head + (nvec << 3);
@@ -233,6 +234,8 @@ __device__ __forceinline__ void widen_run(float *__restrict__ dst, const uint16_
         const uint32_t lane = tid & 63;
         const bool last = lane == 63, s4 = k8 >= 4u;
         const uint32_t sh = k8 & 3u;
+        char *db = reinterpret_cast<char *>(dv);     // bounded stores, as in copy_run_bf16
+        const uint32_t dn = static_cast<uint32_t>(nq) << 4;
         // two words a block apart per lane, both loaded before either is
         // used (one per iteration measured 6% slower on the ragged MoE rows)
         for (int64_t w0 = tid - lane; w0 < nq; w0 += 2 * kBlock) {
@@ -245,16 +248,16 @@ __device__ __forceinline__ void widen_run(float *__restrict__ dst, const uint16_
             }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                const int64_t q = w0 + lane + u * kBlock;
-                u32x2 b{next_lane(a[u].x), next_lane(a[u].y)};
-                if (last) b = h[u];
+                const uint32_t q = static_cast<uint32_t>(w0 + lane + u * kBlock);
+                const u32x2 b = next_or_own(a[u], h[u]);
                 // bytes [k8, k8 + 8) of a:b
                 const uint32_t u0 = s4 ? a[u].y : a[u].x, u1 = s4 ? b.x : a[u].y;
                 const uint32_t u2 = s4 ? b.y : b.x;
                 const uint32_t r0 = __builtin_amdgcn_alignbyte(u1, u0, sh);
                 const uint32_t r1 = __builtin_amdgcn_alignbyte(u2, u1, sh);
-                if (q < nq)
-                    stp<SN>(dv + q, f32x4{bf16_lo(r0), bf16_hi(r0), bf16_lo(r1), bf16_hi(r1)});
+                bstore16<SN>(db, q << 4, dn,
+                             __builtin_bit_cast(u32x4, f32x4{bf16_lo(r0), bf16_hi(r0),
+                                                             bf16_lo(r1), bf16_hi(r1)}));
             }
         }
         done = head + (nq << 2);
@@ -302,16 +305,16 @@ __device__ __forceinline__ void copy_run_u8(uint8_t *__restrict__ dst, const uin
         for (int64_t v = tid; v < nvec; v += TB)
             stp<SN>(dv + v, bload16<LN>(al, static_cast<uint32_t>(v) << 4, nb));
     } else {
+        char *db = reinterpret_cast<char *>(dv);     // bounded stores, as in copy_run_bf16
+        const uint32_t dn = static_cast<uint32_t>(nvec) << 4;
         const uint32_t lane = tid & 63;
         const bool last = lane == 63;
         for (int64_t w0 = tid - lane; w0 < nvec; w0 += TB) {
-            const int64_t v = w0 + lane;
-            const uint32_t o = static_cast<uint32_t>(v) << 4;
+            const uint32_t o = static_cast<uint32_t>(w0 + lane) << 4;
             const u32x4 a = bload16<LN>(al, o, nb);
             const u32x4 h = bload16<kBoundaryNT>(al, last ? o + 16 : nb, nb);
-            u32x4 b = next_lane16(a);
-            if (last) b = h;
-            if (v < nvec) stp<SN>(dv + v, funnel(a, b, k));
+            const u32x4 b = next_or_own(a, h);
+            bstore16<SN>(db, o, dn, funnel(a, b, k));
         }
     }
     const int64_t done = head + (nvec << 4);
@@ -361,6 +364,8 @@ __device__ __forceinline__ void copy_f32_run(float *__restrict__ dst, const floa
         const char *al = reinterpret_cast<const char *>(s) - 4 * q;
         const int64_t nv = (valid - head) >> 2;
         const uint32_t nb = (4 * q + 4 * static_cast<uint32_t>(valid - head) + 15u) & ~15u;
+        char *db = reinterpret_cast<char *>(dv);     // bounded stores, as in copy_run_bf16
+        const uint32_t dn = static_cast<uint32_t>(nv) << 4;
         const uint32_t lane = tid & 63;
         const bool last = lane == 63;
         // two chunks a block apart per lane, as in widen_run (one per
@@ -375,10 +380,9 @@ __device__ __forceinline__ void copy_f32_run(float *__restrict__ dst, const floa
             }
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                const int64_t v = w0 + lane + u * kBlock;
-                u32x4 b = next_lane16(a[u]);
-                if (last) b = h[u];
-                if (v < nv) stp<SN>(dv + v, __builtin_bit_cast(f32x4, funnel(a[u], b, 4 * q)));
+                const uint32_t v = static_cast<uint32_t>(w0 + lane + u * kBlock);
+                const u32x4 b = next_or_own(a[u], h[u]);
+                bstore16<SN>(db, v << 4, dn, funnel(a[u], b, 4 * q));
             }
         }
         done = head + (nv << 2);

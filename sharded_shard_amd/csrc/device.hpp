@@ -153,6 +153,15 @@ __device__ __forceinline__ u32x2 bload8(const char *al, uint32_t voff, uint32_t 
     return __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, NT ? 2 : 0);
 }
 
+// Raw buffer store of 16 bytes at byte offset voff from a 16-byte aligned,
+// wave-uniform base; stores at or past nbytes are dropped, so a lane past
+// the end of a run needs no branch around its store.
+template <int NT>
+__device__ __forceinline__ void bstore16(char *al, uint32_t voff, uint32_t nbytes, u32x4 w) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(al, 0, nbytes, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, voff, 0, NT ? 2 : 0);
+}
+
 // The same register of the next lane of the wave (wave_shl:1 DPP); the last
 // lane gets 0.
 __device__ __forceinline__ uint32_t next_lane(uint32_t x) {
@@ -161,6 +170,24 @@ __device__ __forceinline__ uint32_t next_lane(uint32_t x) {
 
 __device__ __forceinline__ u32x4 next_lane16(u32x4 a) {
     return u32x4{next_lane(a.x), next_lane(a.y), next_lane(a.z), next_lane(a.w)};
+}
+
+// The next lane's register, lane 63 taking `own` instead (its load of the
+// chunk past the wave's span): the DPP move's old value, which a lane
+// without a source lane keeps.  Consumed by the move itself rather than by
+// a select on the lane index, the load cannot be sunk by the compiler under
+// a branch (a lane-63 select, or a guard on a later store or add), where it
+// left only after the wave's other loads had returned: one more memory
+// latency per iteration.
+__device__ __forceinline__ uint32_t next_lane_or(uint32_t x, uint32_t own) {
+    return __builtin_amdgcn_update_dpp(own, x, 0x130, 0xF, 0xF, false);
+}
+__device__ __forceinline__ u32x4 next_or_own(u32x4 a, u32x4 own) {
+    return u32x4{next_lane_or(a.x, own.x), next_lane_or(a.y, own.y), next_lane_or(a.z, own.z),
+                 next_lane_or(a.w, own.w)};
+}
+__device__ __forceinline__ u32x2 next_or_own(u32x2 a, u32x2 own) {
+    return u32x2{next_lane_or(a.x, own.x), next_lane_or(a.y, own.y)};
 }
 
 // Eight fp32 starting at p, whose dword index modulo 4 is q (wave-uniform).

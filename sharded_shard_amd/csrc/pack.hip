@@ -56,27 +56,33 @@ __device__ __forceinline__ void pack_vec(u32x4 *__restrict__ dv, const float *__
 // elements, takes the third from lane l + 1 (DPP; lane 63 loads its own with
 // a load whose other lanes read nothing) and selects: every chunk is read
 // once (a third load per lane instead measured 5% slower on the ragged MoE
-// rows).  Whole waves iterate together.
+// rows).  Whole waves iterate together.  The stores go through a buffer
+// range of exactly the nvec vectors: with a branch around them instead the
+// compiler issued the second load only after the first had returned, and
+// under the non-temporal hint the lines the two loads share were often
+// fetched twice (ragged MoE rows: reads 1.41x the algorithmic bytes by the
+// request counters, now 1.02x; the copy-in 4.23 -> 4.79 TB/s).
 template <int LN, int SN>
 __device__ __forceinline__ void pack_vec_mis(u32x4 *__restrict__ dv, const float *__restrict__ s,
                                              int64_t nvec, uint32_t q) {
     const char *al = reinterpret_cast<const char *>(s - q);
     const uint32_t nb = (4u * (q + 8u * static_cast<uint32_t>(nvec)) + 15u) & ~15u;
+    char *dst = reinterpret_cast<char *>(dv);
+    const uint32_t db = static_cast<uint32_t>(nvec) << 4;
     const uint32_t lane = threadIdx.x & 63;
     const bool last = lane == 63;
     for (int64_t w0 = threadIdx.x - lane; w0 < nvec; w0 += kBlock) {
-        const int64_t v = w0 + lane;
-        const uint32_t o = static_cast<uint32_t>(v) << 5;
+        const uint32_t v = static_cast<uint32_t>(w0 + lane);
+        const uint32_t o = v << 5;
         const f32x4 c0 = __builtin_bit_cast(f32x4, bload16<LN>(al, o, nb));
         const f32x4 c1 = __builtin_bit_cast(f32x4, bload16<LN>(al, o + 16u, nb));
         const u32x4 e = bload16<kBoundaryNT>(al, last ? o + 32u : nb, nb);
-        u32x4 c2 = next_lane16(__builtin_bit_cast(u32x4, c0));
-        if (last) c2 = e;
+        const u32x4 c2 = next_or_own(__builtin_bit_cast(u32x4, c0), e);
         f32x4 a0, a1;
         select8f(c0, c1, __builtin_bit_cast(f32x4, c2), q, a0, a1);
-        if (v < nvec)
-            stp<SN>(dv + v, u32x4{pack2(a0.x, a0.y), pack2(a0.z, a0.w), pack2(a1.x, a1.y),
-                                  pack2(a1.z, a1.w)});
+        bstore16<SN>(dst, v << 4, db,
+                     u32x4{pack2(a0.x, a0.y), pack2(a0.z, a0.w), pack2(a1.x, a1.y),
+                           pack2(a1.z, a1.w)});
     }
 }
 
@@ -92,13 +98,8 @@ __device__ __forceinline__ void pack_run(uint16_t *__restrict__ dst, const float
     u32x4 *dv = reinterpret_cast<u32x4 *>(dst + head);
     const float *s = src + head;
     const uint32_t q = (lo32(s) >> 2) & 3u;
-    // A misaligned source is read with temporal loads: under the
-    // non-temporal hint the lines its two half-line loads per lane share
-    // were fetched again (reads 1.41x the algorithmic bytes by the request
-    // counters on the ragged MoE rows, 1.00x with temporal loads; the
-    // separate-kernel step 1.433 -> 1.422 ms).
     if (q == 0) pack_vec<LN, SN>(dv, s, nvec);
-    else pack_vec_mis<0, SN>(dv, s, nvec, q);
+    else pack_vec_mis<LN, SN>(dv, s, nvec, q);
     const int64_t done = head + (nvec << 3);
     if (tid < valid - done) dst[done + tid] = static_cast<uint16_t>(bf16_rne(src[done + tid]));
     zero_bf16<SN>(dst, valid, len);

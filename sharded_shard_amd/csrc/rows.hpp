@@ -183,8 +183,7 @@ __device__ __forceinline__ void sum_rows_quad_mis(const uint16_t *base, uint32_t
             const uint32_t sh = kk[i] & 3u;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                u32x2 b{next_lane(a[i][h].x), next_lane(a[i][h].y)};
-                if (last) b = e[i][h];
+                const u32x2 b = next_or_own(a[i][h], e[i][h]);
                 // bytes [k, k + 8) of a:b
                 const uint32_t u0 = s4 ? a[i][h].y : a[i][h].x, u1 = s4 ? b.x : a[i][h].y;
                 const uint32_t u2 = s4 ? b.y : b.x;
