@@ -424,6 +424,10 @@ __device__ __forceinline__ void step_run_quad(const uint16_t *__restrict__ rs0, 
         const uint32_t dbytes = static_cast<uint32_t>(2 * (valid - head));
         const int64_t lane = tid & 63;
         const int64_t qstep = static_cast<int64_t>(blockDim.x >> 6) * 64 * QP;
+        char *pb = reinterpret_cast<char *>(P + head), *mb = reinterpret_cast<char *>(M + head);
+        char *vb = reinterpret_cast<char *>(Vv + head);
+        char *gb = kWriteGrad ? reinterpret_cast<char *>(G + head) : nullptr;
+        const uint32_t sb = static_cast<uint32_t>(nq) << 4;
         for (int64_t qb = (tid >> 6) * 64 * QP; qb < nq; qb += qstep) {
             float acc[QP][4];
             if constexpr (kMis)
@@ -433,22 +437,32 @@ __device__ __forceinline__ void step_run_quad(const uint16_t *__restrict__ rs0, 
             else
                 sum_rows_quad<FSDP_STEP_ROW_NT, RB, QP>(
                     rs0 + head, static_cast<uint32_t>(qb + lane) << 3, dbytes, S, N, acc);
+            // p, m and v of every quad of the pass through buffer ranges of
+            // the run's vectors: all loads leave before the first wait (with
+            // a guard per quad they went one quad at a time), and lanes past
+            // the end read zeros and have their stores dropped
+            f32x4 pq[QP], mq[QP], vq[QP];
 #pragma unroll
             for (int h = 0; h < QP; ++h) {
-                const int64_t q = qb + lane + 64 * h;
-                if (q >= nq) continue;
-                const int64_t e0 = head + (q << 2);
-                f32x4 *pv = reinterpret_cast<f32x4 *>(P + e0);
-                f32x4 *mv = reinterpret_cast<f32x4 *>(M + e0);
-                f32x4 *vv = reinterpret_cast<f32x4 *>(Vv + e0);
-                f32x4 pq = ldp<LN>(pv), mq = ldp<LN>(mv), vq = ldp<LN>(vv);
+                const uint32_t o = static_cast<uint32_t>(qb + lane + 64 * h) << 4;
+                pq[h] = __builtin_bit_cast(f32x4, bload16<LN>(pb, o, sb));
+                mq[h] = __builtin_bit_cast(f32x4, bload16<LN>(mb, o, sb));
+                vq[h] = __builtin_bit_cast(f32x4, bload16<LN>(vb, o, sb));
+            }
+#pragma unroll
+            for (int h = 0; h < QP; ++h) {
+                const uint32_t o = static_cast<uint32_t>(qb + lane + 64 * h) << 4;
                 const f32x4 g{acc[h][0] / fN, acc[h][1] / fN, acc[h][2] / fN, acc[h][3] / fN};
-                if (kWriteGrad) stp<SN>(reinterpret_cast<f32x4 *>(G + e0), g);
-                adamw_vec(pq, g, mq, vq, c);
-                stp<SN>(pv, pq);
-                stp<SN>(mv, mq);
-                stp<SN>(vv, vq);
-                store8_at<FSDP_STEP_OUT_NT>(dst + e0, k8, u32x2{pack2(pq.x, pq.y), pack2(pq.z, pq.w)});
+                if (kWriteGrad) bstore16<SN>(gb, o, sb, __builtin_bit_cast(u32x4, g));
+                adamw_vec(pq[h], g, mq[h], vq[h], c);
+                bstore16<SN>(pb, o, sb, __builtin_bit_cast(u32x4, pq[h]));
+                bstore16<SN>(mb, o, sb, __builtin_bit_cast(u32x4, mq[h]));
+                bstore16<SN>(vb, o, sb, __builtin_bit_cast(u32x4, vq[h]));
+                const int64_t q = qb + lane + 64 * h;
+                if (q < nq)
+                    store8_at<FSDP_STEP_OUT_NT>(
+                        dst + head + (q << 2), k8,
+                        u32x2{pack2(pq[h].x, pq[h].y), pack2(pq[h].z, pq[h].w)});
             }
         }
         const int64_t done = head + (nq << 2);
