@@ -24,9 +24,13 @@
 #endif
 // rows in flight per lane of the fp32 reduction on misaligned rows (2:
 // 6.34-6.42 TB/s on the ragged MoE rows against 5.77-6.13 with 1; the bf16
-// reduction there keeps 1, 2 measured 2% slower)
+// reduction there keeps 1, 2 measured 2% slower) and on aligned rows (1:
+// 2 and 4 measured 1% and 0.5% slower at 8 ranks, 4% and 8% at 64)
 #ifndef FSDP_REDUCE_F32_MIS_ROW_BATCH
 #define FSDP_REDUCE_F32_MIS_ROW_BATCH 2
+#endif
+#ifndef FSDP_REDUCE_F32_ROW_BATCH
+#define FSDP_REDUCE_F32_ROW_BATCH 1
 #endif
 // gradient accumulation: non-temporal loads and stores
 #ifndef FSDP_ACC_POL
@@ -253,19 +257,20 @@ __device__ __forceinline__ void reduce_f32_run(float *__restrict__ dst,
         const uint32_t off = static_cast<uint32_t>(qb + lane) << 4;
         f32x4 acc[2];
         if constexpr (kChunkAligned) {
+            // whole batches, then the rest one row at a time (as sum_rows_quad)
+            constexpr int RB = FSDP_REDUCE_F32_ROW_BATCH;
             const uint32_t nb = (dbytes + 15u) & ~15u;
-            for (int32_t j = 0; j < N; j += FSDP_REDUCE_ROW_BATCH) {
-                f32x4 x[FSDP_REDUCE_ROW_BATCH][2];
+            int32_t j = 0;
+            for (; j + RB <= N; j += RB) {
+                f32x4 x[RB][2];
 #pragma unroll
-                for (int i = 0; i < FSDP_REDUCE_ROW_BATCH; ++i) {
-                    const char *row = r + (j + i) * Sb;
-                    const uint32_t n = j + i < N ? nb : 0u;
-                    x[i][0] = __builtin_bit_cast(f32x4, bload16<LN>(row, off, n));
-                    x[i][1] = __builtin_bit_cast(f32x4, bload16<LN>(row, off + 1024u, n));
-                }
+                for (int i = 0; i < RB; ++i)
 #pragma unroll
-                for (int i = 0; i < FSDP_REDUCE_ROW_BATCH; ++i) {
-                    if (j + i >= N) continue;
+                    for (int h = 0; h < 2; ++h)
+                        x[i][h] = __builtin_bit_cast(
+                            f32x4, bload16<LN>(r + (j + i) * Sb, off + 1024u * h, nb));
+#pragma unroll
+                for (int i = 0; i < RB; ++i)
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         const f32x4 y = x[i][h];
@@ -273,6 +278,15 @@ __device__ __forceinline__ void reduce_f32_run(float *__restrict__ dst,
                                             : f32x4{acc[h].x + y.x, acc[h].y + y.y,
                                                     acc[h].z + y.z, acc[h].w + y.w};
                     }
+            }
+            for (; j < N; ++j) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const f32x4 y = __builtin_bit_cast(
+                        f32x4, bload16<LN>(r + j * Sb, off + 1024u * h, nb));
+                    acc[h] = j == 0 ? y
+                                    : f32x4{acc[h].x + y.x, acc[h].y + y.y, acc[h].z + y.z,
+                                            acc[h].w + y.w};
                 }
             }
         } else {

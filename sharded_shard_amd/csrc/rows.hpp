@@ -6,9 +6,9 @@
 
 #include "device.hpp"
 
-// rows in flight per lane of the plain reductions on aligned rows (measured
-// on MI355X: 1 ties at 8 ranks; 4 and 8 spread each wave over more DRAM
-// pages, 7-9% slower for fp32 rows at 64 ranks), and on misaligned rows (2
+// rows in flight per lane of the bf16 reduction on aligned rows (2: 0.4%
+// ahead of 1 at 8 ranks with both rows' loads issued together; more rows
+// spread each wave over more DRAM pages), and on misaligned rows (2
 // measured 2.5% slower than 1)
 #ifndef FSDP_REDUCE_ROW_BATCH
 #define FSDP_REDUCE_ROW_BATCH 2
@@ -119,25 +119,27 @@ __device__ __forceinline__ void sum_rows_wide(const uint16_t *base, uint32_t off
 // byte offsets offb + 512 h (h < QP) from row 0 at base (16-byte aligned
 // rows, uniform), over the N rows of [N, S] bf16, in rank order from row 0;
 // rows RB at a time, each row QP 8-byte loads per lane.  Buffer ranges as in
-// sum_rows_wide (8-byte granules).
+// sum_rows_wide (8-byte granules).  Lanes past the data read zeros.
 template <int NT, int RB, int QP>
 __device__ __forceinline__ void sum_rows_quad(const uint16_t *base, uint32_t offb, uint32_t dbytes,
                                               int64_t S, int32_t N, float (&acc)[QP][4]) {
     const char *r = reinterpret_cast<const char *>(base);
     const int64_t Sb = S * 2;
     const uint32_t nb = (dbytes + 7u) & ~7u;
-    for (int32_t j = 0; j < N; j += RB) {
+    // whole batches of RB rows, then the last N mod RB rows one at a time:
+    // no guard sits between a batch's loads and its adds (a guard per row let
+    // the compiler issue each row's loads only after the previous row's had
+    // returned, so a batch of 2 ran as 1)
+    int32_t j = 0;
+    for (; j + RB <= N; j += RB) {
         u32x2 x[RB][QP];
 #pragma unroll
-        for (int i = 0; i < RB; ++i) {
-            const char *row = r + (j + i) * Sb;
-            const uint32_t n = j + i < N ? nb : 0u;
+        for (int i = 0; i < RB; ++i)
 #pragma unroll
-            for (int h = 0; h < QP; ++h) x[i][h] = bload8<NT>(row, offb + 512u * h, n);
-        }
+            for (int h = 0; h < QP; ++h)
+                x[i][h] = bload8<NT>(r + (j + i) * Sb, offb + 512u * h, nb);
 #pragma unroll
-        for (int i = 0; i < RB; ++i) {
-            if (j + i >= N) continue;
+        for (int i = 0; i < RB; ++i)
 #pragma unroll
             for (int h = 0; h < QP; ++h) {
                 const float y[4] = {bf16_lo(x[i][h].x), bf16_hi(x[i][h].x), bf16_lo(x[i][h].y),
@@ -145,6 +147,16 @@ __device__ __forceinline__ void sum_rows_quad(const uint16_t *base, uint32_t off
 #pragma unroll
                 for (int e = 0; e < 4; ++e) acc[h][e] = j + i == 0 ? y[e] : acc[h][e] + y[e];
             }
+    }
+    for (; j < N; ++j) {
+        u32x2 x[QP];
+#pragma unroll
+        for (int h = 0; h < QP; ++h) x[h] = bload8<NT>(r + j * Sb, offb + 512u * h, nb);
+#pragma unroll
+        for (int h = 0; h < QP; ++h) {
+            const float y[4] = {bf16_lo(x[h].x), bf16_hi(x[h].x), bf16_lo(x[h].y), bf16_hi(x[h].y)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[h][e] = j == 0 ? y[e] : acc[h][e] + y[e];
         }
     }
 }
