@@ -47,9 +47,7 @@
 
 // Elements per block of the kernels that read all N rows per element (the
 // reductions and the narrow fused step): about FSDP_ROWS_BUDGET
-// row-elements per block, at least FSDP_MIN_SUB elements (2048 elements at
-// 8 ranks; half or twice the budget measured 0.8% and 4.6% slower per 7B
-// step, 1.2% and 6% on the ragged MoE rows).
+// row-elements per block, at least FSDP_MIN_SUB elements.
 #ifndef FSDP_ROWS_BUDGET
 #define FSDP_ROWS_BUDGET 32768
 #endif
