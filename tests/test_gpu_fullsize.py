@@ -67,7 +67,10 @@ def _col_plan(world, k):
     return O.Plan(world=world, rank=0, align=1, entries=[e], S=k)
 
 
-CASES = [(2, "block"), (2, "root"), (4, "block"), (4, "root")]
+# 7B and 70B block and root groups (aligned rows), and the ragged MoE
+# workload's two groups at rank 5 (odd segments: every row of [N, S] and
+# most shard and piece offsets misaligned)
+CASES = [(2, "block"), (2, "root"), (3, "block"), (3, "root"), (4, "block"), (4, "root")]
 
 
 @pytest.mark.parametrize("cfg_index,which", CASES, ids=[f"c{c}-{w}" for c, w in CASES])
@@ -200,11 +203,12 @@ def test_reduce_all_equal_every_element(cfg_index):
     g.close()
 
 
-@pytest.mark.parametrize("cfg_index", [2, 4])
+@pytest.mark.parametrize("cfg_index", [2, 3, 4])
 def test_next_rows_full_block_group(cfg_index):
     """The reduce-scatter copy-ins (bf16 and fp32), the fp32 reduction and
-    gradient accumulation on a full block group, in the bench's launch
-    configuration.  Every element against constructions from torch's own
+    gradient accumulation on a full group (a 7B or 70B block group; the
+    ragged MoE group at rank 5, whose odd segment misaligns every row of
+    [N, S]), in the bench's launch configuration.  Every element against constructions from torch's own
     ops (chunk, zero padding, exact widening, fp32 add); the fp32 reduction
     against the oracle on sampled columns and, over every element, against
     the bf16 reduction of the same values."""
