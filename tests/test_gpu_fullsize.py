@@ -288,10 +288,12 @@ def test_next_rows_full_block_group(cfg_index):
 # paragraph) through the multi-group executor the bench times, 3 AdamW steps,
 # every element of every output against the oracle, bit for bit.  The groups:
 # the one-block Llama group (= a block of the 7B shape, N = 8, the aligned
-# fused kernel), the ragged MoE workload's two groups at ranks 5 and 0 (N = 6,
-# odd segment, misaligned fused kernel), and the 70B shape's first and last
-# block and its root group (N = 64, the wide fused kernel).
+# fused kernel), the 7B shape's root group (embedding, final norm, head), the
+# ragged MoE workload's two groups at ranks 5 and 0 (N = 6, odd segment,
+# misaligned fused kernel), and the 70B shape's first and last block and its
+# root group (N = 64, the wide fused kernel).
 WHOLE = [("llama-block-r0", 1, (0,), 0),
+         ("llama7b-root-r0", 2, (32,), 0),
          ("moe-r5", 3, (0, 1), 5),
          ("moe-r0", 3, (0, 1), 0),
          ("llama70b-r0", 4, (0, 79, 80), 0)]
