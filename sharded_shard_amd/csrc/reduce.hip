@@ -159,7 +159,8 @@ __device__ __forceinline__ void accumulate_run(float *__restrict__ acc, const ui
     const int64_t nvec = (len - head) >> 2;
     f32x4 *av = reinterpret_cast<f32x4 *>(acc + head);
     const u32x2 *gv = reinterpret_cast<const u32x2 *>(g + head);
-    // two vectors a block apart per iteration, both loaded before either is
+    // one vector per lane in a sub-range of FSDP_ADAMW_SUB elements; longer
+    // ones take two a block apart per iteration, both loaded before either is
     // stored (one per iteration measured 3-5% slower)
     int64_t v = tid;
     for (; v + kBlock < nvec; v += 2 * kBlock) {

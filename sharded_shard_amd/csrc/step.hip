@@ -22,9 +22,11 @@
 #ifndef FSDP_ADAMW_PACK_POL
 #define FSDP_ADAMW_PACK_POL 3
 #endif
-// elements per block of AdamW fused with the copy-in
+// elements per block of AdamW fused with the copy-in: one vector per lane
+// and array, as AdamW (against 4096: 5.3-5.4 -> 5.5-5.8 TB/s; 2048 in
+// between)
 #ifndef FSDP_ADAMW_PACK_SUB
-#define FSDP_ADAMW_PACK_SUB 4096
+#define FSDP_ADAMW_PACK_SUB 1024
 #endif
 // shard policy of the wide fused step (plain: its lanes store two halves
 // of a 32-byte span, which non-temporal stores split into partial writes)
@@ -314,8 +316,9 @@ __device__ __forceinline__ void adamw_pack_scalar_at(float *P, const float *G, f
 
 // Valid elements [0, valid) of one run: AdamW exactly as adamw_run, then
 // the bf16 cast of the new master into dst as pack_run writes it; zeros in
-// dst from valid to len.  Four elements per lane and vector, two vectors a
-// block apart per iteration; the bf16 output stored by its own 8-byte phase.
+// dst from valid to len.  Four elements per lane and vector (one vector per
+// lane in a sub-range of FSDP_ADAMW_PACK_SUB elements, longer ones two a
+// block apart per iteration); the bf16 output stored by its own 8-byte phase.
 template <int POL>
 __device__ __forceinline__ void adamw_pack_run(float *P, const float *G, float *M, float *Vv,
                                                uint16_t *dst, int64_t len, int64_t valid,
