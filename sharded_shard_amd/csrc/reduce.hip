@@ -32,6 +32,14 @@
 #ifndef FSDP_REDUCE_F32_ROW_BATCH
 #define FSDP_REDUCE_F32_ROW_BATCH 1
 #endif
+// the fp32 reduction on aligned rows below this many ranks: one vector per
+// lane over half its rows budget (1024 elements per block at 8 ranks, 3.5-5%
+// faster than two vectors per lane over 2048); from it on, and on misaligned
+// rows, two vectors per lane (at 64 ranks 1.3% faster than one, on the ragged
+// MoE rows 8%)
+#ifndef FSDP_REDUCE_F32_PAIR_MIN_N
+#define FSDP_REDUCE_F32_PAIR_MIN_N 16
+#endif
 // gradient accumulation: non-temporal loads and stores
 #ifndef FSDP_ACC_POL
 #define FSDP_ACC_POL 3
@@ -221,14 +229,14 @@ __device__ __forceinline__ float sum_rows_scalar_f32(const float *src0, int64_t 
 }
 
 // Valid elements [0, len) of one run: four elements (one vector) per lane
-// and pass, two passes 64 vectors apart, so every wave instruction is
+// and pass, H passes 64 vectors apart, so every wave instruction is
 // contiguous and loads and stores take POL.  On misaligned rows (row j
 // starts q_j = (q0 + j qS) & 3 dwords past a 16-byte boundary) lane l loads
 // the aligned chunk holding its first element, takes the next chunk from
 // lane l + 1 (DPP; lane 63 loads its own) and shifts by q_j dwords,
 // FSDP_REDUCE_F32_MIS_ROW_BATCH rows at a time: every chunk of a row is
 // read once.
-template <int POL, bool kChunkAligned>
+template <int POL, bool kChunkAligned, int H>
 __device__ __forceinline__ void reduce_f32_run(float *__restrict__ dst,
                                                const float *__restrict__ src0, int64_t len,
                                                int64_t S, int32_t N, float fN) {
@@ -253,27 +261,27 @@ __device__ __forceinline__ void reduce_f32_run(float *__restrict__ dst,
     const int64_t nq = (len - head) >> 2;
     const int64_t lane = tid & 63;
     const bool last = lane == 63;
-    const int64_t qstep = static_cast<int64_t>(blockDim.x >> 6) * 128;
-    for (int64_t qb = (tid >> 6) * 128; qb < nq; qb += qstep) {
+    const int64_t qstep = static_cast<int64_t>(blockDim.x >> 6) * 64 * H;
+    for (int64_t qb = (tid >> 6) * 64 * H; qb < nq; qb += qstep) {
         const uint32_t off = static_cast<uint32_t>(qb + lane) << 4;
-        f32x4 acc[2];
+        f32x4 acc[H];
         if constexpr (kChunkAligned) {
             // whole batches, then the rest one row at a time (as sum_rows_quad)
             constexpr int RB = FSDP_REDUCE_F32_ROW_BATCH;
             const uint32_t nb = (dbytes + 15u) & ~15u;
             int32_t j = 0;
             for (; j + RB <= N; j += RB) {
-                f32x4 x[RB][2];
+                f32x4 x[RB][H];
 #pragma unroll
                 for (int i = 0; i < RB; ++i)
 #pragma unroll
-                    for (int h = 0; h < 2; ++h)
+                    for (int h = 0; h < H; ++h)
                         x[i][h] = __builtin_bit_cast(
                             f32x4, bload16<LN>(r + (j + i) * Sb, off + 1024u * h, nb));
 #pragma unroll
                 for (int i = 0; i < RB; ++i)
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
+                    for (int h = 0; h < H; ++h) {
                         const f32x4 y = x[i][h];
                         acc[h] = j + i == 0 ? y
                                             : f32x4{acc[h].x + y.x, acc[h].y + y.y,
@@ -282,7 +290,7 @@ __device__ __forceinline__ void reduce_f32_run(float *__restrict__ dst,
             }
             for (; j < N; ++j) {
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
+                for (int h = 0; h < H; ++h) {
                     const f32x4 y = __builtin_bit_cast(
                         f32x4, bload16<LN>(r + j * Sb, off + 1024u * h, nb));
                     acc[h] = j == 0 ? y
@@ -293,7 +301,7 @@ __device__ __forceinline__ void reduce_f32_run(float *__restrict__ dst,
         } else {
             constexpr int RB = FSDP_REDUCE_F32_MIS_ROW_BATCH;
             for (int32_t j = 0; j < N; j += RB) {
-                u32x4 a[RB][2], e[RB][2];
+                u32x4 a[RB][H], e[RB][H];
                 uint32_t qq[RB];
 #pragma unroll
                 for (int i = 0; i < RB; ++i) {
@@ -302,7 +310,7 @@ __device__ __forceinline__ void reduce_f32_run(float *__restrict__ dst,
                     const char *al = r + (j + i) * Sb - 4 * qq[i];
                     const uint32_t n = j + i < N ? (4 * qq[i] + dbytes + 15u) & ~15u : 0u;
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
+                    for (int h = 0; h < H; ++h) {
                         const uint32_t o = off + 1024u * h;
                         a[i][h] = bload16<LN>(al, o, n);
                         e[i][h] = bload16<kBoundaryNT>(al, last ? o + 16u : n, n);
@@ -311,7 +319,7 @@ __device__ __forceinline__ void reduce_f32_run(float *__restrict__ dst,
 #pragma unroll
                 for (int i = 0; i < RB; ++i) {
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
+                    for (int h = 0; h < H; ++h) {
                         const u32x4 b = next_or_own(a[i][h], e[i][h]);
                         const f32x4 y = __builtin_bit_cast(f32x4, funnel(a[i][h], b, 4 * qq[i]));
                         if (j + i >= N) continue;
@@ -323,7 +331,7 @@ __device__ __forceinline__ void reduce_f32_run(float *__restrict__ dst,
             }
         }
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < H; ++h) {
             const int64_t q = qb + lane + 64 * h;
             if (q < nq)
                 stp<SN>(dv + q, f32x4{acc[h].x / fN, acc[h].y / fN, acc[h].z / fN, acc[h].w / fN});
@@ -333,7 +341,7 @@ __device__ __forceinline__ void reduce_f32_run(float *__restrict__ dst,
     if (tid < len - done) dst[done + tid] = sum_rows_scalar_f32(src0, S, N, done + tid) / fN;
 }
 
-template <int POL, bool kChunkAligned>
+template <int POL, bool kChunkAligned, int H>
 __global__ __launch_bounds__(kBlock) void reduce_f32_kernel(
     const ReduceTile *__restrict__ tiles, int64_t n_tiles, int32_t split, int64_t sub,
     const DevEntry *__restrict__ ents, const float *__restrict__ rs_in, int64_t S, int32_t N,
@@ -346,7 +354,7 @@ __global__ __launch_bounds__(kBlock) void reduce_f32_kernel(
         const ReduceTile tl = tiles[t];
         if (b >= tl.len) continue;
         const int64_t len = tl.len - b < L ? tl.len - b : L;
-        reduce_f32_run<POL, kChunkAligned>(ents[tl.entry].grad + tl.dst + b, rs_in + tl.src + b,
+        reduce_f32_run<POL, kChunkAligned, H>(ents[tl.entry].grad + tl.dst + b, rs_in + tl.src + b,
                                           len, S, N, fN);
     }
 }
@@ -371,7 +379,10 @@ hipError_t launch_reduce(const ReduceTile *tiles, int64_t n, const DevEntry *ent
             <<<grid_for(n, wsp), 64, 0, st>>>(tiles, n, wsp, wsub, ents, rs_in, S, N, fN);
         return hipGetLastError();
     }
-    const int32_t sp = split_rows(kTileReduce, N, 0);
+    // half the rows budget: one pass of two quads per lane at 8 ranks (2048
+    // elements per block; the full budget measured 4% slower there and 7% on
+    // the ragged MoE rows, a quarter 1-2%)
+    const int32_t sp = split_rows(kTileReduce, 2 * N, 0);
     const unsigned grid = grid_for(n, sp);
     if (chunk_aligned)
         reduce_kernel<FSDP_REDUCE_POL, 1, true>
@@ -399,14 +410,19 @@ hipError_t launch_reduce_f32(const ReduceTile *tiles, int64_t n, const DevEntry 
                              hipStream_t st) {
     if (n == 0) return hipSuccess;
     const float fN = static_cast<float>(N);
-    // fp32 rows carry twice the bytes of bf16 rows per element
-    const int32_t sp = split_rows(kTileReduce, 2 * N, 0);
+    // fp32 rows carry twice the bytes of bf16 rows per element; one vector
+    // per lane takes half that budget again
+    const bool one = chunk_aligned && N < FSDP_REDUCE_F32_PAIR_MIN_N;
+    const int32_t sp = split_rows(kTileReduce, (one ? 4 : 2) * N, 0);
     const unsigned grid = grid_for(n, sp);
-    if (chunk_aligned)
-        reduce_f32_kernel<FSDP_REDUCE_F32_POL, true>
+    if (one)
+        reduce_f32_kernel<FSDP_REDUCE_F32_POL, true, 1>
+            <<<grid, kBlock, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
+    else if (chunk_aligned)
+        reduce_f32_kernel<FSDP_REDUCE_F32_POL, true, 2>
             <<<grid, kBlock, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
     else
-        reduce_f32_kernel<FSDP_REDUCE_F32_POL, false>
+        reduce_f32_kernel<FSDP_REDUCE_F32_POL, false, 2>
             <<<grid, kBlock, 0, st>>>(tiles, n, sp, kTileReduce / sp, ents, rs_in, S, N, fN);
     return hipGetLastError();
 }
