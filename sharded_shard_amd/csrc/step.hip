@@ -71,14 +71,34 @@
 #ifndef FSDP_WIDE_OUT_NT
 #define FSDP_WIDE_OUT_NT 0
 #endif
-// occupancy target of the wide fused step (waves per SIMD)
+// register budget of the wide fused step: at least this many waves per SIMD
+// (amdgpu_waves_per_eu; capping it at 3 with an LDS reservation, below,
+// measured 1.6% slower per 70B step)
 #ifndef FSDP_STEP_WIDE_WAVES
 #define FSDP_STEP_WIDE_WAVES 4
 #endif
-// occupancy target of the aligned fused step, waves per SIMD (6 measured
-// ahead of 7 and 8)
+// register budget of the aligned fused step: at least this many waves per
+// SIMD (amdgpu_waves_per_eu; 6 measured ahead of 7 and 8)
 #ifndef FSDP_STEP_WAVES
 #define FSDP_STEP_WAVES 6
+#endif
+// Occupancy caps.  A block that reserves LDS it never touches limits how many
+// blocks share a CU (160 KB of LDS per CU).  The aligned fused step reserves
+// 28 KB, so 5 of its 256-thread blocks (5 waves per SIMD) share a CU: 7B step
+// 11.63-11.65 -> 11.54-11.55 ms and one block 0.3585-0.3596 -> 0.3556 ms at 8
+// ranks (24 KB, 6 blocks, measured no change; 36 KB, 4 blocks, 0.3% slower;
+// the misaligned fused step measured no gain at 6 or 5 blocks and 1.7% loss
+// at 4).  AdamW as one launch over a group set and AdamW fused with the
+// copy-in reserve 48 KB, 3 blocks per CU: AdamW 6.0 -> 6.1 TB/s on the 7B
+// shape and 5.7 -> 6.2 on the 70B shape, the fused AdamW + copy-in 5.8 -> 6.1
+// and 5.5 -> 6.2 (group-set steps 0.4-2% faster; 64 KB, 2 blocks, slower).
+// Per group, AdamW keeps no cap: 48 KB measured 1.3% faster per 7B step but
+// 0.4% slower per 70B step, whose per-group launches are short.
+#ifndef FSDP_STEP_LDS
+#define FSDP_STEP_LDS 28672
+#endif
+#ifndef FSDP_ADAMW_SET_LDS
+#define FSDP_ADAMW_SET_LDS 49152
 #endif
 // the fused step reads its N gradient rows with non-temporal loads
 #ifndef FSDP_STEP_ROW_NT
@@ -558,7 +578,7 @@ hipError_t launch_adamw(const EwTile *tiles, int64_t n, const DevEntry *ents,
     if (n == 0) return hipSuccess;
     const int32_t sp = split_for(kTileAdamw, FSDP_ADAMW_SUB);
     if (one_launch)
-        adamw_kernel<FSDP_ADAMW_SET_POL><<<grid_for(n, sp), kBlock, 0, st>>>(
+        adamw_kernel<FSDP_ADAMW_SET_POL><<<grid_for(n, sp), kBlock, FSDP_ADAMW_SET_LDS, st>>>(
             tiles, n, sp, kTileAdamw / sp, ents, to_scalars(scal));
     else
         adamw_kernel<FSDP_ADAMW_POL><<<grid_for(n, sp), kBlock, 0, st>>>(
@@ -570,7 +590,7 @@ hipError_t launch_adamw_pack(const PackTile *tiles, int64_t n, const DevEntry *e
                              uint16_t *ag_in, const float scal[8], hipStream_t st) {
     if (n == 0) return hipSuccess;
     const int32_t sp = split_for(kTilePack, FSDP_ADAMW_PACK_SUB);
-    adamw_pack_kernel<FSDP_ADAMW_PACK_POL><<<grid_for(n, sp), kBlock, 0, st>>>(
+    adamw_pack_kernel<FSDP_ADAMW_PACK_POL><<<grid_for(n, sp), kBlock, FSDP_ADAMW_SET_LDS, st>>>(
         tiles, n, sp, kTilePack / sp, ents, ag_in, to_scalars(scal));
     return hipGetLastError();
 }
@@ -581,11 +601,11 @@ void launch_step_rb(bool aligned, bool write_grad, unsigned grid, unsigned thr, 
                     const uint16_t *rs_in, uint16_t *ag_in, int64_t S, int32_t N, float fN,
                     const AdamwScalars &c) {
     if (aligned && write_grad)
-        step_kernel_aligned<RB, true><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in,
-                                                           S, N, fN, c);
+        step_kernel_aligned<RB, true><<<grid, thr, FSDP_STEP_LDS, st>>>(
+            tiles, n, sp, sub, ents, rs_in, ag_in, S, N, fN, c);
     else if (aligned)
-        step_kernel_aligned<RB, false><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in,
-                                                            ag_in, S, N, fN, c);
+        step_kernel_aligned<RB, false><<<grid, thr, FSDP_STEP_LDS, st>>>(
+            tiles, n, sp, sub, ents, rs_in, ag_in, S, N, fN, c);
     else if (write_grad)
         step_kernel<RBG, true><<<grid, thr, 0, st>>>(tiles, n, sp, sub, ents, rs_in, ag_in, S, N,
                                                     fN, c);
