@@ -43,6 +43,14 @@
 #ifndef FSDP_RSPACK_ACC_POL
 #define FSDP_RSPACK_ACC_POL 3
 #endif
+// LDS the copy-in from the accumulators reserves and never touches, so that
+// 6 of its 256-thread blocks share a CU (160 KB of LDS per CU): 6.07 -> 6.37
+// TB/s on the 70B shape, +1.5% on the 7B shape and +1.8% on the ragged MoE
+// rows.  The reductions, the accumulation, the other copy-ins and the FP8
+// copy-in measured slower at 6, 5, 4 or 3 blocks per CU.
+#ifndef FSDP_RSPACK_ACC_LDS
+#define FSDP_RSPACK_ACC_LDS 24576
+#endif
 
 namespace fsdp {
 
@@ -464,10 +472,10 @@ hipError_t launch_rspack_acc(const PackTile *tiles, int64_t n, const DevEntry *e
     if (n == 0) return hipSuccess;
     const int32_t sp = split_for(kTileUnpack, FSDP_UNPACK_SUB);
     if (chunk_aligned)
-        rspack_acc_kernel<FSDP_RSPACK_ACC_POL, false><<<grid_for(n, sp), kBlock, 0, st>>>(
+        rspack_acc_kernel<FSDP_RSPACK_ACC_POL, false><<<grid_for(n, sp), kBlock, FSDP_RSPACK_ACC_LDS, st>>>(
             tiles, n, sp, kTileUnpack / sp, ents, out);
     else
-        rspack_acc_kernel<FSDP_RSPACK_ACC_POL, true><<<grid_for(n, sp), kBlock, 0, st>>>(
+        rspack_acc_kernel<FSDP_RSPACK_ACC_POL, true><<<grid_for(n, sp), kBlock, FSDP_RSPACK_ACC_LDS, st>>>(
             tiles, n, sp, kTileUnpack / sp, ents, out);
     return hipGetLastError();
 }
