@@ -30,6 +30,16 @@
 #ifndef FSDP_UNPACK_MIS_THREADS
 #define FSDP_UNPACK_MIS_THREADS 256
 #endif
+// LDS the copy-out and the bf16 reduce-scatter copy-in reserve, and never
+// touch, on misaligned rows, so that 6 of their 256-thread blocks share a CU
+// (160 KB of LDS per CU): on the ragged MoE rows the copy-out 6.09-6.14 ->
+// 6.24-6.29 TB/s, the copy-in 6.00-6.03 -> 6.13-6.19 and the step
+// 1.072-1.077 -> 1.062-1.070 ms (7 blocks alike, 5 in between; on aligned
+// rows the 128-thread copies gained nothing at 6 waves per SIMD and the FP8
+// copy-out lost 3.5%)
+#ifndef FSDP_COPY_MIS_LDS
+#define FSDP_COPY_MIS_LDS 24576
+#endif
 // 16-byte chunks each lane of an aligned copy loads before storing them (4
 // or 8 with correspondingly larger blocks measured 9-16% slower)
 #ifndef FSDP_UNPACK_UNROLL
@@ -437,8 +447,8 @@ hipError_t launch_unpack(const UnpackTile *tiles, int64_t n, const DevEntry *ent
     } else {
         const int32_t sp = split_for(kTileUnpack, FSDP_UNPACK_MIS_SUB);
         unpack_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_MIS_THREADS, true>
-            <<<grid_for(n, sp), FSDP_UNPACK_MIS_THREADS, 0, st>>>(tiles, n, sp, kTileUnpack / sp,
-                                                                  ents, ag_out);
+            <<<grid_for(n, sp), FSDP_UNPACK_MIS_THREADS, FSDP_COPY_MIS_LDS, st>>>(
+                tiles, n, sp, kTileUnpack / sp, ents, ag_out);
     }
     return hipGetLastError();
 }
@@ -499,8 +509,8 @@ hipError_t launch_rspack(const PackTile *tiles, int64_t n, const DevEntry *ents,
                                                    static_cast<uint16_t *>(out));
     else
         rspack_bf16_kernel<FSDP_UNPACK_POL, FSDP_UNPACK_MIS_THREADS, true>
-            <<<grid, FSDP_UNPACK_MIS_THREADS, 0, st>>>(tiles, n, sp, kTileUnpack / sp, ents,
-                                                       static_cast<uint16_t *>(out));
+            <<<grid, FSDP_UNPACK_MIS_THREADS, FSDP_COPY_MIS_LDS, st>>>(
+                tiles, n, sp, kTileUnpack / sp, ents, static_cast<uint16_t *>(out));
     return hipGetLastError();
 }
 
